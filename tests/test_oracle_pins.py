@@ -1,0 +1,304 @@
+"""Pins of the fp64 oracle to facts fixed outside it: hand-worked fixtures, closed forms,
+brute force on tiny inputs and special cases that reduce to plain linear algebra.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped bias term, a wrong
+group or nibble index, a transposed operand, a sign error, a wrong tie rule) fails it."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+from golden_io import read_fixture
+from moe_synth import CONFIGS, Synth
+
+RNG = np.random.default_rng(1234)
+
+
+def _fixture_row(name):
+    fx = read_fixture(name)
+    bits = int(fx["bits"][0][0])
+    group = int(fx["group"][0][0])
+    words = np.array([[int(w, 16) for w in fx["words"][0]]], dtype=np.uint32)
+    codes = np.array([int(c) for c in fx["codes"][0]])
+    s = np.array([[float(fx["scale"][0][0])]], dtype=np.float16)
+    b = np.array([[float(fx["bias"][0][0])]], dtype=np.float16)
+    return fx, bits, group, words, codes, s, b
+
+
+@pytest.mark.parametrize("name", ["dequant_int4_hand_packed.txt", "dequant_int2_hand_packed.txt"])
+def test_hand_packed_dequant(name):
+    fx, bits, group, words, codes, s, b = _fixture_row(name)
+    assert (O.codes(words, bits)[0] == codes).all()
+    W = O.dequant(words, s, b, bits, group)
+    head = [float(v) for v in fx["weights_head"][0]]
+    assert W[0, : len(head)].tolist() == head
+    # x = e_j returns column j exactly; x = ones returns the hand-computed sum
+    for j in (0, 5, 17, 63):
+        e = np.zeros(64)
+        e[j] = 1.0
+        assert (W @ e)[0] == W[0, j]
+    assert (W @ np.ones(64))[0] == float(fx["dot_ones"][0][0])
+
+
+def test_group_index_along_input_dim():
+    # two groups of 32 columns: codes all 1; group 0 -> 1*1+0, group 1 -> 1*2+10
+    words = np.full((1, 8), 0x11111111, dtype=np.uint32)
+    s = np.array([[1.0, 2.0]], dtype=np.float16)
+    b = np.array([[0.0, 10.0]], dtype=np.float16)
+    W = O.dequant(words, s, b, 4, 32)
+    assert W[0, :32].tolist() == [1.0] * 32 and W[0, 32:].tolist() == [12.0] * 32
+
+
+def _bytewise_codes(words, bits):
+    """Independent unpack: walk the little-endian bytes, low bit-field first."""
+    out = []
+    for row in words:
+        vals = []
+        for byte in row.astype("<u4").tobytes():
+            for f in range(8 // bits):
+                vals.append((byte >> (bits * f)) & ((1 << bits) - 1))
+        out.append(vals)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 64), (4, 128), (2, 32), (2, 64), (2, 128)])
+def test_dequant_matvec_vs_fma_grouped_form(bits, group):
+    """sum_j (q_j s + b) x_j == s * sum_j q_j x_j + b * sum_j x_j per group (the FMA rewrite of
+    the Metal listing), with codes unpacked by an independent byte walk."""
+    rows, cols = 3, 256
+    words = RNG.integers(0, 2 ** 32, size=(rows, cols * bits // 32), dtype=np.uint64).astype(np.uint32)
+    s = RNG.uniform(0.005, 0.02, size=(rows, cols // group)).astype(np.float16)
+    b = (-(2 ** (bits - 1)) * s.astype(np.float64) + RNG.normal(0, 1e-3, s.shape)).astype(np.float16)
+    x = RNG.normal(size=cols)
+    q = _bytewise_codes(words, bits)
+    assert (q == O.codes(words, bits)).all()
+    ref = np.zeros(rows)
+    for o in range(rows):
+        for gi in range(cols // group):
+            sl = slice(gi * group, (gi + 1) * group)
+            sx = float(s[o, gi]) * x[sl]
+            bx = float(b[o, gi]) * x[sl]
+            ref[o] += np.sum(q[o, sl] * sx + bx)
+    got = O.dequant(words, s, b, bits, group) @ x
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_activation_closed_forms():
+    fx = read_fixture("activations.txt")
+    for v, want in fx["silu"]:
+        assert O.silu(np.array([float(v)]))[0] == pytest.approx(float(want), abs=1e-15)
+    for v, want in fx["gelu"]:
+        assert O.gelu_erf(np.array([float(v)]))[0] == pytest.approx(float(want), abs=1e-15)
+
+
+def test_rmsnorm_closed_form():
+    h = np.full(64, 3.0)
+    assert O.rmsnorm(h)[0] == pytest.approx(3.0 / math.sqrt(9.0 + 1e-6), rel=1e-15)
+    h = np.array([3.0, -4.0])
+    assert O.rmsnorm(h).tolist() == pytest.approx([3 / math.sqrt(12.5 + 1e-6), -4 / math.sqrt(12.5 + 1e-6)])
+
+
+# ------------------------------------------------------------------------------- top-K
+def test_topk_crafted_ties():
+    assert O.topk_indices(np.zeros(16), 4) == [0, 1, 2, 3]
+    assert O.topk_indices(np.array([1.0, 3.0, 3.0, 2.0]), 2) == [1, 2]
+    assert O.topk_indices(np.array([1.0, 3.0, 3.0, 2.0]), 3) == [1, 2, 3]
+    assert O.topk_indices(np.array([-1.0, -0.0, 0.0, -2.0]), 2) == [1, 2]
+
+
+def test_topk_vs_lexsort_and_invariants():
+    for E, K in [(16, 2), (256, 4), (256, 8), (512, 4), (64, 64)]:
+        for _ in range(5):
+            lg = np.round(RNG.normal(size=E), 1)    # many exact ties
+            idx = O.topk_indices(lg, K)
+            ref = list(np.lexsort((np.arange(E), -lg))[:K])
+            assert idx == ref
+            assert len(set(idx)) == K and all(0 <= e < E for e in idx)
+            vals = lg[idx]
+            assert (np.diff(vals) <= 0).all()
+            w = O.topk_weights(lg, idx, True)
+            assert w.sum() == pytest.approx(1.0, abs=1e-12)
+            for i in range(K):
+                for j in range(K):
+                    assert w[i] / w[j] == pytest.approx(math.exp(vals[i] - vals[j]), rel=1e-12)
+            wf = O.topk_weights(lg, idx, False)
+            full = scipy.special.softmax(lg)
+            np.testing.assert_allclose(wf, full[idx], rtol=1e-12)
+
+
+# ------------------------------------------------------------------------------- experts
+def _tiny_layer(seed=0):
+    cfg = CONFIGS["tiny"]
+    syn = Synth(cfg, seed)
+    experts = {}
+    for mat in ("gate", "up", "down"):
+        q, s, b = syn.expert_mat(0, list(range(cfg.E)), mat)
+        experts[mat] = (q.numpy(), s.numpy(), b.numpy())
+    get = lambda e: tuple((experts[m][0][e], experts[m][1][e], experts[m][2][e]) for m in ("gate", "up", "down"))
+    return cfg, syn, get
+
+
+def test_k_equals_e_dense_equivalence():
+    """K = E: the top-K layer equals the dense mixture r + sum_e softmax(l)_e FFN_e(x),
+    computed here with no top-K code at all."""
+    cfg, syn, get = _tiny_layer()
+    x = syn.hidden(7, 1)[0].numpy()
+    wr = syn.router(0).numpy()
+    lg = O.router_logits(wr, x)
+    p = scipy.special.softmax(lg)
+    dense = O.f64(x).copy()
+    for e in range(cfg.E):
+        dense += p[e] * O.expert_ffn_packed(x, *get(e), cfg.bits, cfg.group)
+    for renorm in (True, False):
+        idx, w = O.route_topk(lg[None], cfg.E, renorm)
+        y = O.moe_layer(x, x, idx, w, get, cfg.bits, cfg.group)
+        np.testing.assert_allclose(y[0], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_one_hot_routing_is_single_expert():
+    cfg, syn, get = _tiny_layer()
+    x = syn.hidden(3, 1)[0].numpy()
+    j = 11
+    lg = np.zeros(cfg.E)
+    lg[j] = 100.0
+    idx, w = O.route_topk(lg[None], 1)
+    assert idx[0].tolist() == [j] and w[0].tolist() == [1.0]
+    y = O.moe_layer(x, x, idx, w, get, cfg.bits, cfg.group)
+    single = O.f64(x) + O.expert_ffn_packed(x, *get(j), cfg.bits, cfg.group)
+    np.testing.assert_array_equal(y[0], single)
+    idx2, w2 = O.route_topk(lg[None], 2)
+    assert idx2[0].tolist() == [j, 0]
+    assert w2[0, 1] == pytest.approx(math.exp(-100.0) / (1 + math.exp(-100.0)), rel=1e-12)
+
+
+def test_scalar_ffn_by_hand():
+    Wg, Wu, Wd = np.array([[2.0]]), np.array([[3.0]]), np.array([[0.5]])
+    o = O.expert_ffn(np.array([1.0]), Wg, Wu, Wd)
+    silu2 = 2.0 / (1.0 + math.exp(-2.0))
+    assert o[0] == pytest.approx(0.5 * silu2 * 3.0, rel=1e-15)
+    # SiLU on the gate branch, not the up branch
+    assert o[0] != pytest.approx(0.5 * 2.0 * (3.0 / (1.0 + math.exp(-3.0))), rel=1e-6)
+
+
+def test_expert_ffn_matches_explicit_loops():
+    """Small random expert, every product written as a Python loop (catches a transposed
+    operand or a swapped gate/up)."""
+    d, I = 8, 5
+    Wg, Wu, Wd = RNG.normal(size=(I, d)), RNG.normal(size=(I, d)), RNG.normal(size=(d, I))
+    x = RNG.normal(size=d)
+    a = []
+    for i in range(I):
+        g = sum(Wg[i, c] * x[c] for c in range(d))
+        u = sum(Wu[i, c] * x[c] for c in range(d))
+        a.append(g / (1 + math.exp(-g)) * u)
+    ref = [sum(Wd[j, i] * a[i] for i in range(I)) for j in range(d)]
+    np.testing.assert_allclose(O.expert_ffn(x, Wg, Wu, Wd), ref, rtol=1e-12)
+
+
+def test_combine_by_hand():
+    o = np.array([[1.0, 2.0], [10.0, 20.0]])
+    w = np.array([0.25, 0.75])
+    r = np.array([100.0, 200.0])
+    assert O.combine(o, w, r).tolist() == [100 + 0.25 + 7.5, 200 + 0.5 + 15.0]
+    assert O.combine(o, w, r, shared=np.array([1.0, -1.0])).tolist() == [108.75, 214.5]
+
+
+# ------------------------------------------------------------------------------- LoRA
+def test_lora_zero_b_is_base_and_merge_identity():
+    d, I, r, alpha = 64, 32, 4, 8.0
+    Wg, Wu, Wd = RNG.normal(size=(I, d)), RNG.normal(size=(I, d)), RNG.normal(size=(d, I))
+    x = RNG.normal(size=d)
+    lora = {m: (RNG.normal(0, 0.02, (r, c)), RNG.normal(0, 0.02, (rw, r)))
+            for m, (rw, c) in (("gate", (I, d)), ("up", (I, d)), ("down", (d, I)))}
+    lora["alpha"] = alpha
+    zero = {m: (lora[m][0], np.zeros_like(lora[m][1])) for m in ("gate", "up", "down")}
+    zero["alpha"] = alpha
+    np.testing.assert_array_equal(O.expert_ffn(x, Wg, Wu, Wd, zero), O.expert_ffn(x, Wg, Wu, Wd))
+    merged = [W + (alpha / r) * lora[m][1] @ lora[m][0] for W, m in ((Wg, "gate"), (Wu, "up"), (Wd, "down"))]
+    np.testing.assert_allclose(O.expert_ffn(x, Wg, Wu, Wd, lora), O.expert_ffn(x, *merged), rtol=1e-10, atol=1e-12)
+    # the delta is scaled by alpha / rank (= 2 for rank 16, alpha 32)
+    A, B = lora["gate"]
+    assert np.allclose(O.lora_delta(A, B, alpha, x), 2.0 * (B @ (A @ x)))
+
+
+# ------------------------------------------------------------------------------- prerouter
+def _rand_head(d, E, H):
+    return {"fc1_x": RNG.normal(size=(H, d)), "fc1_r": RNG.normal(size=(2 * E, H)),
+            "fc1_b": RNG.normal(size=H), "fc2": RNG.normal(size=(E, H)), "fc2_b": RNG.normal(size=E),
+            "lin_x": RNG.normal(size=(E, d)), "lin_r": RNG.normal(size=(2 * E, E)), "lin_b": RNG.normal(size=E)}
+
+
+def test_prerouter_reduces_to_router():
+    d, E, H, K = 32, 16, 8, 2
+    pw = _rand_head(d, E, H)
+    pw.update(fc2=np.zeros((E, H)), fc2_b=None, lin_r=np.zeros((2 * E, E)), lin_b=None)
+    x = RNG.normal(size=d)
+    got = O.prerouter_logits(x, [3, 5], [1, 2], pw, E)
+    np.testing.assert_allclose(got, O.router_logits(pw["lin_x"], x), rtol=1e-13)
+
+
+def test_prerouter_khot_gather_exact():
+    """fc1_x = 0 and fc1 routing rows set to distinct constants: the pre-activation is the exact
+    sum of the selected rows (cur rows m, prev rows E + m), read out through fc2 = I."""
+    d, E, K = 16, 8, 3
+    H = E
+    fc1_r = np.array([[m + 1.0] * H for m in range(2 * E)])
+    pw = {"fc1_x": np.zeros((H, d)), "fc1_r": fc1_r, "fc1_b": None, "fc2": np.eye(E), "fc2_b": None,
+          "lin_x": np.zeros((E, d)), "lin_r": np.zeros((2 * E, E)), "lin_b": None}
+    cur, prev = [6, 1, 3], [0, 7, 2]
+    a = sum(m + 1.0 for m in cur) + sum(E + m + 1.0 for m in prev)
+    got = O.prerouter_logits(RNG.normal(size=d), cur, prev, pw, E)
+    np.testing.assert_allclose(got, [a * 0.5 * (1 + math.erf(a / math.sqrt(2)))] * E, rtol=1e-15)
+    a0 = sum(m + 1.0 for m in cur)        # no previous token -> zero vector
+    got0 = O.prerouter_logits(RNG.normal(size=d), cur, None, pw, E)
+    np.testing.assert_allclose(got0, [a0 * 0.5 * (1 + math.erf(a0 / math.sqrt(2)))] * E, rtol=1e-15)
+
+
+def test_prerouter_by_hand():
+    """d=2, E=2, K=1, H=1 worked out by hand: z = [x0, x1, cur0, cur1, prev0, prev1]."""
+    x = np.array([1.0, -2.0])
+    pw = {"fc1_x": np.array([[0.5, 0.25]]), "fc1_r": np.array([[1.0], [2.0], [3.0], [4.0]]),
+          "fc1_b": np.array([0.1]), "fc2": np.array([[2.0], [-1.0]]), "fc2_b": np.array([0.0, 1.0]),
+          "lin_x": np.array([[1.0, 0.0], [0.0, 1.0]]),
+          "lin_r": np.array([[1.0, 0.0], [0.0, 1.0], [5.0, 6.0], [7.0, 8.0]]), "lin_b": np.array([0.5, 0.0])}
+    # cur = [1] -> z[3] = 1 ; prev = [0] -> z[4] = 1
+    a = 0.5 * 1 + 0.25 * -2 + 2.0 + 3.0 + 0.1          # = 5.1
+    g = 0.5 * a * (1 + math.erf(a / math.sqrt(2)))
+    want = [2 * g + 0 + (1.0 + 0.0 + 5.0) + 0.5, -g + 1 + (-2.0 + 1.0 + 6.0)]
+    np.testing.assert_allclose(O.prerouter_logits(x, [1], [0], pw, 2), want, rtol=1e-15)
+
+
+# ------------------------------------------------------------------------------- grouping
+def test_group_by_expert_brute_force():
+    for T, K, E in [(256, 4, 256), (7, 2, 16), (1, 1, 4)]:
+        idx = np.array([RNG.choice(E, size=K, replace=False) for _ in range(T)])
+        counts, off, perm = O.group_by_expert(idx, E)
+        ref = [p for _, p in sorted((int(e), p) for p, e in enumerate(idx.reshape(-1)))]
+        assert perm.tolist() == ref
+        assert off[-1] == T * K and (np.diff(off) == counts).all()
+        assert counts.tolist() == np.bincount(idx.reshape(-1), minlength=E).tolist()
+
+
+# ------------------------------------------------------------------------------- bytes
+def test_expert_byte_accounting():
+    fx = read_fixture("byte_accounting.txt")
+    for name, v in fx.items():
+        assert CONFIGS[name].expert_bytes() == int(v[0][0])
+    assert CONFIGS["large-int4"].expert_bytes() == 6.75 * 2 ** 20
+
+
+# ------------------------------------------------------------------------------- chain
+def test_chain_single_layer_is_routed_layer():
+    cfg, syn, get = _tiny_layer()
+    h = syn.hidden(11, 1)[0].numpy()
+    st = O.ChainState(1)
+    hL, st2, tr = O.chain_token(h, st, E=cfg.E, K=cfg.K, bits=cfg.bits, group=cfg.group,
+                                router_get=lambda l: syn.router(l).numpy(), head_get=lambda l: None,
+                                expert_get=lambda l, e: get(e))
+    x = O.rmsnorm(h)
+    idx, w = O.route_topk(O.router_logits(syn.router(0).numpy(), x)[None], cfg.K)
+    y = O.moe_layer(x, h, idx, w, get, cfg.bits, cfg.group)
+    np.testing.assert_array_equal(hL, O.to_f16_f64(y[0]))
+    assert st2.prev[0].tolist() == idx[0].tolist()
