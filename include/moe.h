@@ -1,0 +1,164 @@
+/*
+ * moe.h -- C ABI of the decode-time fine-grained MoE layer with low-bit experts,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, per token (pages cited by title and section):
+ *   1. router logits l = W_r x, or the prerouter head's logits
+ *        ("La otra mitad del muro de la memoria: Servir MoEs de 35B desde SSD con prediccion
+ *         de enrutamiento entrenada", section "Arquitectura del cabezal Prerouter");
+ *   2. softmax top-K selection of experts
+ *        ("Arquitecturas nativas para device: MoE de grano fino y pre-attention router",
+ *         section "Dos niveles de sparsity");
+ *   3. affine group-quantised 4-bit / 2-bit dequantise-and-matvec for each selected
+ *      expert's gate, up and down projections, 4. fused SwiGLU, and 5. weighted expert
+ *      combine plus residual
+ *        ("Inferencia de LLM MoE en MacBook Pro: Streaming de Expertos desde SSD con Metal",
+ *         section "Arquitectura del Sistema" and its Metal dequant listing);
+ *   plus the unmerged low-rank adapter on the shared path, y = W_int4 x + (alpha/r) B A x
+ *        (Edge0 reading guide, section "Ejecucion del adaptador no fusionado").
+ *
+ * Conventions for every call
+ *   - Array pointers are DEVICE pointers owned by the caller; float16 values travel as their
+ *     uint16_t bit patterns.  The library never allocates and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks its arguments on the
+ *     host, then enqueues kernels on `stream` and returns without synchronising.  Calls are
+ *     safe to record into a HIP graph (no memset or host round trip inside).
+ *   - On an argument error nothing is enqueued and MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED is
+ *     returned.  A launch failure reported by the runtime returns MOE_ERR_HIP.  Faults inside a
+ *     kernel surface at the caller's next synchronisation, as for any HIP call.
+ *   - Device-side expert indices must lie in [0, E) and a row of them must hold distinct
+ *     experts.  A kernel that meets an index outside [0, E) reads no weights for it and writes
+ *     NaN where that expert's contribution would go.
+ *   - No C++ exception crosses this boundary.
+ *
+ * Quantised matrix layout (one "stack" = the same projection of all E experts)
+ *   q      : uint32 [E][rows][cols*bits/32], little-endian words; column j of a row is held in
+ *            word j/(32/bits) at bit offset bits*(j%(32/bits)), lowest bits = lowest column.
+ *   scales : float16 [E][rows][cols/group]; biases: float16 [E][rows][cols/group].
+ *   weight[e][o][j] = code * scales[e][o][j/group] + biases[e][o][j/group].
+ *   gate and up have rows = d_ff, cols = d_model; down has rows = d_model, cols = d_ff.
+ *   q must be 16-byte aligned; rows must be a whole number of 16-byte segments
+ *   (cols*bits % 128 == 0).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad size, K > E, misalignment ...     */
+  MOE_ERR_UNSUPPORTED = 2, /* bits not in {2,4}, group not in {32,64,128}, shape off-grid   */
+  MOE_ERR_HIP = 3          /* the HIP runtime rejected a launch                              */
+} moe_status;
+
+/* flags */
+#define MOE_TOPK_RENORM 0x1u   /* top-K weights = softmax over the K selected logits; without
+                                  it, the full softmax over all E logits read at the K experts */
+#define MOE_INPUT_RMSNORM 0x2u /* consume x := x / sqrt(mean(x^2) + 1e-6) (weightless RMS norm,
+                                  the glue between chained layers), computed in float32       */
+
+/* Limits checked by every call. */
+#define MOE_MAX_E 1024
+#define MOE_MAX_K 16
+#define MOE_MAX_D 8192
+
+typedef struct {
+  const uint32_t* q;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} moe_qmat;
+
+typedef struct {
+  int32_t n_experts; /* E (1 for a shared expert)   */
+  int32_t d_model;   /* d                            */
+  int32_t d_ff;      /* expert intermediate size I   */
+  int32_t bits;      /* 4 or 2                       */
+  int32_t group;     /* 32, 64 or 128                */
+  moe_qmat gate, up, down;
+} moe_experts;
+
+/* Unmerged low-rank adapter of one projection: delta = (alpha/rank) * B (A v).
+   A: float16 [rank][in], B: float16 [out][rank]; rank in 1..64. */
+typedef struct {
+  const uint16_t* A;
+  const uint16_t* B;
+  int32_t rank;
+  float alpha;
+} moe_lora;
+
+/* Prerouter head weights in split layout.  The head reads z = [x; khot(idx_cur); khot(idx_prev)]
+   of length d + 2E; fc1 = [fc1_x | fc1_r^T] and l = [lin_x | lin_r^T] (row j of fc1_r / lin_r is
+   column d + j of the dense matrix), so the K-hot columns are gathered as K rows.
+   logits = fc2 * gelu_erf(fc1 z + fc1_b) + fc2_b + l z + lin_b.  Biases may be NULL. */
+typedef struct {
+  int32_t d_hidden;       /* H */
+  const uint16_t* fc1_x;  /* [H][d]   */
+  const uint16_t* fc1_r;  /* [2E][H]  */
+  const uint16_t* fc1_b;  /* [H] or NULL */
+  const uint16_t* fc2;    /* [E][H]   */
+  const uint16_t* fc2_b;  /* [E] or NULL */
+  const uint16_t* lin_x;  /* [E][d]   */
+  const uint16_t* lin_r;  /* [2E][E]  */
+  const uint16_t* lin_b;  /* [E] or NULL */
+} moe_prerouter_w;
+
+/* S1a + S2: router and softmax top-K.
+   If w_router != NULL: logits[T][E] (float32, out) = W_r[E][d] x[T][d] (x optionally RMS-normed),
+   then top-K.  If w_router == NULL: `logits` is the input and x is ignored.
+   idx[T][K] (int32, out): experts by descending logit, equal logits -> lower index first.
+   w[T][K] (float32, out): softmax weights (MOE_TOPK_RENORM: over the K selected).
+   Limits: 1 <= T, 1 <= K <= min(E, 16), 1 <= E <= 1024, d % 8 == 0, d <= 8192. */
+moe_status moe_route_topk(void* stream, int32_t T, int32_t d, int32_t E, int32_t K, uint32_t flags,
+                          const uint16_t* x, const uint16_t* w_router, float* logits, int32_t* idx,
+                          float* w);
+
+/* Bytes of device workspace moe_prerouter needs for T tokens (float32 [T][H] + [T][E]). */
+size_t moe_prerouter_workspace_size(int32_t T, int32_t E, int32_t d_hidden);
+
+/* S1b: prerouter head of layer N; its logits route layer N+1 at the next token (feed them to
+   moe_route_topk with w_router == NULL).  idx_cur[T][K]: this layer's routing at this token;
+   idx_prev[T][K] or NULL: this layer's routing at the previous token (NULL = zero vector).
+   logits[T][E] float32 out.  Limits as moe_route_topk, plus 1 <= H <= 8192, H % 8 == 0. */
+moe_status moe_prerouter(void* stream, int32_t T, int32_t d, int32_t E, int32_t K, uint32_t flags,
+                         const uint16_t* x, const int32_t* idx_cur, const int32_t* idx_prev,
+                         const moe_prerouter_w* pw, float* logits, void* workspace,
+                         size_t workspace_bytes);
+
+/* Bytes of device workspace moe_expert_ffn_q4 needs for T tokens with K experts each. */
+size_t moe_expert_ffn_workspace_size(int32_t T, int32_t K, const moe_experts* ex);
+
+/* S3-S6: for each token t and slot k, expert e = idx[t][k]:
+     a = silu(gate_e x_t) * (up_e x_t),  o_tk = down_e a   (float32 accumulation)
+   With lora3 (only when ex->n_experts == 1): lora3[0], [1], [2] add their deltas to the gate,
+   up and down projections.
+   Outputs: out[T][K][d] float32 = unweighted o_tk (may be NULL), and/or the fused combine
+     y[T][d] float16 = r[t] + sum_k w[t][k] o_tk  (w_fuse, r_fuse, y_fuse all set, or all NULL).
+   Small T runs the batch-1 decode kernels; large T sorts the (token, slot) pairs by expert
+   and runs an MFMA grouped GEMM.  workspace: moe_expert_ffn_workspace_size bytes, 256-byte
+   aligned.  Limits: d, d_ff <= 8192; d, d_ff multiples of group; rows whole 16-byte segments. */
+moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                             const int32_t* idx, const moe_experts* ex, const moe_lora* lora3,
+                             float* out, const float* w_fuse, const uint16_t* r_fuse,
+                             uint16_t* y_fuse, void* workspace, size_t workspace_bytes);
+
+/* S6: y[T][d] float16 = r + sum_k w[t][k] o[t][k] (+ shared[t], weight 1), accumulated in
+   float32 in ascending k, rounded to nearest even. */
+moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,
+                       const uint16_t* r, const float* shared, uint16_t* y);
+
+const char* moe_status_string(moe_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

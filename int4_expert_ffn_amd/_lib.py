@@ -1,0 +1,217 @@
+"""ctypes binding of libmoe.so (include/moe.h).  Argument marshalling only: every step of the
+layer runs in the library's HIP kernels.  Functions take torch tensors (device memory) or raw
+integer device addresses, check dtype / device / contiguity, and raise MoEError on a non-OK
+status.  The stream defaults to torch's current stream on the tensors' device.
+
+Loading fails loudly (ImportError) when the library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
+MOE_TOPK_RENORM = 0x1
+MOE_INPUT_RMSNORM = 0x2
+MOE_MAX_E, MOE_MAX_K, MOE_MAX_D = 1024, 16, 8192
+
+# every symbol include/moe.h declares
+EXPORTS = (
+    "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine",
+    "moe_status_string", "moe_version",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_lib.moe_status_string(status).decode()}")
+
+
+class moe_qmat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class moe_experts(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat)]
+
+
+class moe_lora(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("rank", ctypes.c_int32), ("alpha", ctypes.c_float)]
+
+
+class moe_prerouter_w(ctypes.Structure):
+    _fields_ = [("d_hidden", ctypes.c_int32),
+                ("fc1_x", ctypes.c_void_p), ("fc1_r", ctypes.c_void_p), ("fc1_b", ctypes.c_void_p),
+                ("fc2", ctypes.c_void_p), ("fc2_b", ctypes.c_void_p),
+                ("lin_x", ctypes.c_void_p), ("lin_r", ctypes.c_void_p), ("lin_b", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int4_expert_ffn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "moe_route_topk": (st, [vp, i32, i32, i32, i32, u32, vp, vp, vp, vp, vp]),
+        "moe_prerouter_workspace_size": (sz, [i32, i32, i32]),
+        "moe_prerouter": (st, [vp, i32, i32, i32, i32, u32, vp, vp, vp, ctypes.POINTER(moe_prerouter_w), vp, vp, sz]),
+        "moe_expert_ffn_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
+        "moe_expert_ffn_q4": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora),
+                                   vp, vp, vp, vp, vp, sz]),
+        "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "moe_status_string": (ctypes.c_char_p, [st]),
+        "moe_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+# ----------------------------------------------------------------------------------------------
+def _ptr(t, dtype=None, name="tensor") -> Optional[int]:
+    """Device address of a tensor (checked), a raw int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    for t in tensors:
+        if t is not None and not isinstance(t, int):
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _check(status: int, call: str):
+    if status != MOE_OK:
+        raise MoEError(status, call)
+
+
+def _f16():
+    import torch
+    return torch.float16
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _qw():
+    import torch
+    return (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+class Experts:
+    """A stack of E quantised experts (tensors kept alive here) and its C descriptor."""
+
+    def __init__(self, gate, up, down, bits: int, group: int):
+        self.tensors = (gate, up, down)
+        q = gate[0]
+        E, I, _ = q.shape
+        d = down[0].shape[1]
+        mats = [moe_qmat(_ptr(m[0], _qw(), "q"), _ptr(m[1], _f16(), "scales"), _ptr(m[2], _f16(), "biases"))
+                for m in (gate, up, down)]
+        self.desc = moe_experts(E, d, I, bits, group, *mats)
+        self.E, self.d, self.I, self.bits, self.group = E, d, I, bits, group
+
+
+class Lora3:
+    """Adapters of gate, up and down: sequence of three (A, B) float16 tensor pairs."""
+
+    def __init__(self, pairs: Sequence, alpha: float):
+        self.tensors = tuple(pairs)
+        arr = (moe_lora * 3)()
+        for i, (A, B) in enumerate(pairs):
+            arr[i] = moe_lora(_ptr(A, _f16(), "lora A"), _ptr(B, _f16(), "lora B"), A.shape[0], float(alpha))
+        self.desc = arr
+
+
+class PrerouterWeights:
+    def __init__(self, w: dict):
+        self.tensors = dict(w)
+        g = lambda k: _ptr(w.get(k), _f16(), k)
+        self.desc = moe_prerouter_w(w["fc1_x"].shape[0], g("fc1_x"), g("fc1_r"), g("fc1_b"), g("fc2"), g("fc2_b"),
+                                    g("lin_x"), g("lin_r"), g("lin_b"))
+        self.H = w["fc1_x"].shape[0]
+
+
+# ---------------------------------------------------------------------------------------------- calls
+def moe_route_topk(T, d, E, K, flags, x, w_router, logits, idx, w, stream=None):
+    st = _lib.moe_route_topk(_stream(stream, logits, idx), T, d, E, K, flags,
+                             _ptr(x, _f16(), "x"), _ptr(w_router, _f16(), "w_router"),
+                             _ptr(logits, _f32(), "logits"), _ptr(idx, _i32(), "idx"), _ptr(w, _f32(), "w"))
+    _check(st, "moe_route_topk")
+
+
+def moe_prerouter_workspace_size(T, E, d_hidden) -> int:
+    return _lib.moe_prerouter_workspace_size(T, E, d_hidden)
+
+
+def moe_prerouter(T, d, E, K, flags, x, idx_cur, idx_prev, pw: PrerouterWeights, logits, workspace,
+                  workspace_bytes=None, stream=None):
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_prerouter(_stream(stream, logits), T, d, E, K, flags, _ptr(x, _f16(), "x"),
+                            _ptr(idx_cur, _i32(), "idx_cur"), _ptr(idx_prev, _i32(), "idx_prev"),
+                            ctypes.byref(pw.desc), _ptr(logits, _f32(), "logits"), _ptr(workspace, None, "workspace"),
+                            nbytes)
+    _check(st, "moe_prerouter")
+
+
+def moe_expert_ffn_workspace_size(T, K, ex: Experts) -> int:
+    return _lib.moe_expert_ffn_workspace_size(T, K, ctypes.byref(ex.desc))
+
+
+def moe_expert_ffn_q4(T, K, flags, x, idx, ex: Experts, lora3: Optional[Lora3], out, w_fuse, r_fuse, y_fuse,
+                      workspace, workspace_bytes=None, stream=None):
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_expert_ffn_q4(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"), _ptr(idx, _i32(), "idx"),
+                                ctypes.byref(ex.desc), ctypes.cast(lora3.desc, ctypes.POINTER(moe_lora)) if lora3 is not None else None,
+                                _ptr(out, _f32(), "out"), _ptr(w_fuse, _f32(), "w_fuse"), _ptr(r_fuse, _f16(), "r_fuse"),
+                                _ptr(y_fuse, _f16(), "y_fuse"), _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_expert_ffn_q4")
+
+
+def moe_combine(T, K, d, o, w, r, shared, y, stream=None):
+    st = _lib.moe_combine(_stream(stream, o, y), T, K, d, _ptr(o, _f32(), "o"), _ptr(w, _f32(), "w"),
+                          _ptr(r, _f16(), "r"), _ptr(shared, _f32(), "shared"), _ptr(y, _f16(), "y"))
+    _check(st, "moe_combine")
+
+
+def moe_version() -> int:
+    return _lib.moe_version()
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()

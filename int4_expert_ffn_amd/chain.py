@@ -1,0 +1,76 @@
+"""Host-side schedule of a prerouted decode stack: L MoE layers resident on one GPU.
+
+Per token t and layer l (all calls asynchronous on one stream, routing never leaves the device):
+  * layer 0, and every layer at the first token, runs its own router + softmax top-K;
+    any other layer uses the set and weights the head of layer l-1 predicted at token t-1
+    (the prediction is the routing: "La otra mitad del muro de la memoria: Servir MoEs de 35B
+    desde SSD ...", section "Ideas clave");
+  * the head of layer l (l < L-1) reads the layer input with the K-hot routing of layer l at
+    tokens t and t-1 and predicts layer l+1's routing for token t+1 (section "Arquitectura del
+    cabezal Prerouter");
+  * the expert FFN with the fused weighted combine + residual produces the next layer's input.
+Layer inputs are consumed through the weightless RMS norm (MOE_INPUT_RMSNORM); the residual is
+the un-normalised float16 hidden state.
+
+Routing buffers rotate over three token slots, so the head writing token t+1's routing never
+overwrites what token t still reads (slot t%3) or the previous-token vector (slot (t-1)%3).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerWeights:
+    experts: L.Experts
+    router: torch.Tensor                      # [E][d] float16
+    head: Optional[L.PrerouterWeights] = None  # predicts the next layer; None on the last layer
+
+
+class DecodeStack:
+    def __init__(self, layers: List[LayerWeights], K: int, device, renorm: bool = True):
+        ex0 = layers[0].experts
+        self.layers = layers
+        self.L = len(layers)
+        self.E, self.d, self.K = ex0.E, ex0.d, K
+        self.device = torch.device(device)
+        self.topk_flags = L.MOE_TOPK_RENORM if renorm else 0
+        dev = self.device
+        E, d = self.E, self.d
+        self.route_idx = torch.zeros((3, self.L, K), dtype=torch.int32, device=dev)
+        self.route_w = torch.zeros((3, self.L, K), dtype=torch.float32, device=dev)
+        self.logits = torch.zeros((self.L, E), dtype=torch.float32, device=dev)
+        self.head_logits = torch.zeros((self.L, E), dtype=torch.float32, device=dev)
+        self.h = torch.zeros((self.L + 1, d), dtype=torch.float16, device=dev)   # per-layer inputs/outputs
+        ffn_ws = max(L.moe_expert_ffn_workspace_size(1, K, lw.experts) for lw in layers)
+        H = max([lw.head.H for lw in layers if lw.head is not None] or [8])
+        head_ws = L.moe_prerouter_workspace_size(1, E, H)
+        self.ffn_ws = torch.empty(ffn_ws, dtype=torch.uint8, device=dev)
+        self.head_ws = torch.empty(head_ws, dtype=torch.uint8, device=dev)
+
+    def token(self, t: int, h_in: Optional[torch.Tensor] = None, record_routing: bool = False):
+        """Enqueue token t.  h_in [d] float16 is copied into the stack input unless None (then the
+        caller has already written self.h[0]).  Returns the output view self.h[L]."""
+        if h_in is not None:
+            self.h[0].copy_(h_in)
+        s, sp, sn = t % 3, (t - 1) % 3, (t + 1) % 3
+        RMS = L.MOE_INPUT_RMSNORM
+        for l, lw in enumerate(self.layers):
+            x = self.h[l]
+            idx, w = self.route_idx[s, l], self.route_w[s, l]
+            if l == 0 or t == 0:
+                L.moe_route_topk(1, self.d, self.E, self.K, self.topk_flags | RMS, x, lw.router,
+                                 self.logits[l], idx, w)
+            if lw.head is not None and l + 1 < self.L:
+                L.moe_prerouter(1, self.d, self.E, self.K, RMS, x, idx, self.route_idx[sp, l] if t > 0 else None,
+                                lw.head, self.head_logits[l], self.head_ws)
+                L.moe_route_topk(1, self.d, self.E, self.K, self.topk_flags, None, None, self.head_logits[l],
+                                 self.route_idx[sn, l + 1], self.route_w[sn, l + 1])
+            L.moe_expert_ffn_q4(1, self.K, RMS, x, idx, lw.experts, None, None, w, x, self.h[l + 1],
+                                self.ffn_ws)
+        return self.h[self.L]

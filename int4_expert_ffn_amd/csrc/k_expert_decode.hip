@@ -1,0 +1,347 @@
+// Batch-1 (small T) decode path of the expert FFN on gfx950: dequantise-and-matvec of the K
+// selected experts' gate / up projections with SwiGLU in the epilogue, then the down projection
+// with the weighted combine + residual in the epilogue.
+//
+// Steps follow "Inferencia de LLM MoE en MacBook Pro: Streaming de Expertos desde SSD con
+// Metal", section "Arquitectura del Sistema" (4/2-bit dequantised matvec, fused SwiGLU, expert
+// combine fused with the residual) and, for the shared-path adapter, the unmerged LoRA equation
+// of the Edge0 reading guide ("Ejecucion del adaptador no fusionado").
+//
+// Mapping.  A packed row is S 16-byte segments.  A "row slot" of L lanes (the power of two at or
+// above S, at most 64; lanes at or past S idle) owns one row; a lane owns P = ceil(S / L) <= 4
+// segments and always the same columns, so it builds
+// its permuted activation pairs once and reuses them for every row it visits.  A wave runs
+// 64 / L row slots side by side and NB rows per slot, with all NB*P 128-bit weight loads issued
+// before any arithmetic.  Row sums are xor-butterfly reductions inside the slot.  Every sum runs
+// in a fixed order, so results are bit-reproducible run to run.
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+namespace {
+
+struct LoraRef {
+  const uint16_t* B;  // [rows][rank]
+  const float* u;     // [T][rank]   (A v, already in float32)
+  int rank;
+  float scale;        // alpha / rank
+};
+
+__device__ __forceinline__ float lora_row(const LoraRef& lr, int t, int row) {
+  const uint16_t* b = lr.B + (size_t)row * lr.rank;
+  const float* u = lr.u + (size_t)t * lr.rank;
+  float acc = 0.f;
+  for (int r = 0; r < lr.rank; ++r) acc = fmaf(h2f(b[r]), u[r], acc);
+  return lr.scale * acc;
+}
+
+// u[t][r] = s_t * sum_i A[r][i] v_t[i]; one wave per (t, r).  s_t is the RMS-norm factor of v_t
+// when `rmsnorm`, else 1.
+__global__ void __launch_bounds__(256) k_lora_a(int T, int n_in, int rank, int rmsnorm,
+                                                const uint16_t* __restrict__ v, size_t v_stride,
+                                                const uint16_t* __restrict__ A, float* __restrict__ u) {
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
+  const int lane = threadIdx.x % WAVE;
+  if (wave >= T * rank) return;
+  const int t = wave / rank, r = wave % rank;
+  const uint16_t* vr = v + (size_t)t * v_stride;
+  const uint16_t* ar = A + (size_t)r * n_in;
+  float acc = 0.f, sq = 0.f;
+  for (int c = lane * 8; c < n_in; c += WAVE * 8) {
+    uint4 va = *reinterpret_cast<const uint4*>(vr + c);
+    uint4 aa = *reinterpret_cast<const uint4*>(ar + c);
+    const uint32_t vv[4] = {va.x, va.y, va.z, va.w}, av[4] = {aa.x, aa.y, aa.z, aa.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_amdgcn_fdot2(as_h2(vv[i]), as_h2(av[i]), acc, false);
+      sq = __builtin_amdgcn_fdot2(as_h2(vv[i]), as_h2(vv[i]), sq, false);
+    }
+  }
+  acc = group_sum(acc, WAVE);
+  sq = group_sum(sq, WAVE);
+  const float s = rmsnorm ? 1.f / sqrtf(sq / (float)n_in + RMS_EPS) : 1.f;
+  if (lane == 0) u[(size_t)t * rank + r] = acc * s;
+}
+
+// gate/up + SwiGLU.  Items are (k, i) pairs of token t = blockIdx.y, item = k * I + i.
+template <int BITS, int P, bool SPLIT, int NB>
+__global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I, int lg2g, int L,
+                                               uint32_t flags, const uint16_t* __restrict__ x,
+                                               const int32_t* __restrict__ idx, moe_qmat gate,
+                                               moe_qmat up, uint16_t* __restrict__ act, LoraRef lg,
+                                               LoraRef lu) {
+  using G = SegT<BITS>;
+  const int lane = threadIdx.x;
+  const int t = blockIdx.y;
+  const int RPI = WAVE / L;
+  const int slot = lane / L, ls = lane % L;
+  const int wpr = d * BITS / 32;
+  const int ngr = d >> lg2g;
+  const int items = K * I;
+  const int base = blockIdx.x * RPI * NB;
+  if (base >= items) return;
+
+  const int S = d * BITS / 128;
+  uint32_t xp[P][G::PAIRS];
+  float sx[P][2];
+  float sq = 0.f;
+  const uint16_t* xt = x + (size_t)t * d;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (ls + p * L < S) load_xpairs<BITS>(xt + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
+  }
+  float scale = 1.f;
+  if (flags & MOE_INPUT_RMSNORM) scale = 1.f / sqrtf(group_sum(sq, L) / (float)d + RMS_EPS);
+
+  // issue every weight load of this wave first
+  uint4 qg[NB][P], qu[NB][P];
+  size_t row[NB];
+  bool valid[NB], bad[NB];
+  int kk[NB], ii[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int item = base + nb * RPI + slot;
+    valid[nb] = item < items;
+    const int k = valid[nb] ? item / I : 0;
+    const int i = valid[nb] ? item - k * I : 0;
+    int e = idx[(size_t)t * K + k];
+    bad[nb] = (unsigned)e >= (unsigned)E;
+    if (bad[nb]) e = 0;
+    kk[nb] = k;
+    ii[nb] = i;
+    row[nb] = (size_t)e * I + i;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (ls + p * L < S) {
+        const size_t wo = row[nb] * wpr + (size_t)(ls + p * L) * 4;
+        qg[nb][p] = *reinterpret_cast<const uint4*>(gate.q + wo);
+        qu[nb][p] = *reinterpret_cast<const uint4*>(up.q + wo);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float pg = 0.f, pu = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (ls + p * L >= S) continue;
+      const int c0 = (ls + p * L) * G::COLS;
+      const size_t ga = row[nb] * ngr + (c0 >> lg2g);
+      const size_t gb = SPLIT ? row[nb] * ngr + ((c0 + G::COLS / 2) >> lg2g) : ga;
+      float d0, d1;
+      d0 = d1 = 0.f;
+      dot_segment<BITS>(qg[nb][p], xp[p], d0, d1);
+      pg += h2f(gate.scales[ga]) * d0 + h2f(gate.biases[ga]) * sx[p][0] + h2f(gate.scales[gb]) * d1 +
+            h2f(gate.biases[gb]) * sx[p][1];
+      d0 = d1 = 0.f;
+      dot_segment<BITS>(qu[nb][p], xp[p], d0, d1);
+      pu += h2f(up.scales[ga]) * d0 + h2f(up.biases[ga]) * sx[p][0] + h2f(up.scales[gb]) * d1 +
+            h2f(up.biases[gb]) * sx[p][1];
+    }
+    pg = group_sum(pg, L) * scale;
+    pu = group_sum(pu, L) * scale;
+    if (ls == 0 && valid[nb]) {
+      if (lg.B) pg += lora_row(lg, t, ii[nb]);
+      if (lu.B) pu += lora_row(lu, t, ii[nb]);
+      float a = pg / (1.f + expf(-pg)) * pu;
+      if (bad[nb]) a = quiet_nan();
+      act[((size_t)t * K + kk[nb]) * I + ii[nb]] = f2h(a);
+    }
+  }
+}
+
+// down projection (+ weighted combine + residual).  Items are output rows j of token t.
+template <int BITS, int P, bool SPLIT, int NB>
+__global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, int lg2g, int L,
+                                             const uint16_t* __restrict__ act,
+                                             const int32_t* __restrict__ idx, moe_qmat down,
+                                             float* __restrict__ out, const float* __restrict__ wf,
+                                             const uint16_t* __restrict__ rf, uint16_t* __restrict__ yf,
+                                             LoraRef ldn) {
+  using G = SegT<BITS>;
+  const int lane = threadIdx.x;
+  const int t = blockIdx.y;
+  const int RPI = WAVE / L;
+  const int slot = lane / L, ls = lane % L;
+  const int wpr = I * BITS / 32;
+  const int ngr = I >> lg2g;
+  const int base = blockIdx.x * RPI * NB;
+  if (base >= d) return;
+  const int S = I * BITS / 128;
+
+  float acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = 0.f;
+
+  for (int k = 0; k < K; ++k) {
+    int e = idx[(size_t)t * K + k];
+    const bool bad = (unsigned)e >= (unsigned)E;
+    if (bad) e = 0;
+    uint4 q[NB][P];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j = base + nb * RPI + slot;
+      const size_t rw = (size_t)e * d + (j < d ? j : 0);
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (ls + p * L < S) q[nb][p] = *reinterpret_cast<const uint4*>(down.q + rw * wpr + (size_t)(ls + p * L) * 4);
+    }
+    uint32_t xp[P][G::PAIRS];
+    float sx[P][2];
+    float sq = 0.f;
+    const uint16_t* at = act + ((size_t)t * K + k) * I;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (ls + p * L < S) load_xpairs<BITS>(at + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
+    const float wk = wf ? wf[(size_t)t * K + k] : 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j = base + nb * RPI + slot;
+      const size_t rw = (size_t)e * d + (j < d ? j : 0);
+      float po = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (ls + p * L >= S) continue;
+        const int c0 = (ls + p * L) * G::COLS;
+        const size_t ga = rw * ngr + (c0 >> lg2g);
+        const size_t gb = SPLIT ? rw * ngr + ((c0 + G::COLS / 2) >> lg2g) : ga;
+        float d0 = 0.f, d1 = 0.f;
+        dot_segment<BITS>(q[nb][p], xp[p], d0, d1);
+        po += h2f(down.scales[ga]) * d0 + h2f(down.biases[ga]) * sx[p][0] + h2f(down.scales[gb]) * d1 +
+              h2f(down.biases[gb]) * sx[p][1];
+      }
+      po = group_sum(po, L);
+      if (ls == 0 && j < d) {
+        if (ldn.B) po += lora_row(ldn, t, j);
+        if (bad) po = quiet_nan();
+        if (out) out[((size_t)t * K + k) * d + j] = po;
+        acc[nb] = fmaf(wk, po, acc[nb]);
+      }
+    }
+  }
+  if (yf) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j = base + nb * RPI + slot;
+      if (ls == 0 && j < d) yf[(size_t)t * d + j] = f2h(h2f(rf[(size_t)t * d + j]) + acc[nb]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_combine(int T, int K, int d, const float* __restrict__ o,
+                                                 const float* __restrict__ w,
+                                                 const uint16_t* __restrict__ r,
+                                                 const float* __restrict__ shared,
+                                                 uint16_t* __restrict__ y) {
+  const size_t n = (size_t)T * d;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / d, j = i - t * d;
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) acc = fmaf(w[t * K + k], o[(t * K + k) * d + j], acc);
+    if (shared) acc += shared[i];
+    y[i] = f2h(h2f(r[i]) + acc);
+  }
+}
+
+// geometry of a packed row with `cols` columns: S segments, row slots of L lanes (a power of two,
+// lanes at or past S idle), P segments per lane.
+struct RowGeo {
+  int S, L, P;
+  bool ok;
+};
+RowGeo row_geo(int bits, int cols) {
+  RowGeo g{};
+  g.S = cols * bits / 128;
+  if (g.S <= 0 || (cols * bits) % 128) return g;
+  g.L = 1;
+  while (g.L < g.S && g.L < WAVE) g.L <<= 1;
+  g.P = (g.S + g.L - 1) / g.L;
+  g.ok = g.P <= 4;
+  return g;
+}
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+constexpr int NB_GATEUP = 2;
+constexpr int NB_DOWN = 2;
+
+template <int BITS, int P, bool SPLIT>
+void launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
+                 LoraRef lu, LoraRef ldn, int which) {
+  const int lg2g = ilog2(a.group);
+  if (which == 0) {
+    const int rpw = (WAVE / gu.L) * NB_GATEUP;
+    dim3 grid((a.K * a.I + rpw - 1) / rpw, a.T);
+    hipLaunchKernelGGL((k_gateup<BITS, P, SPLIT, NB_GATEUP>), grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d,
+                       a.I, lg2g, gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, a.act, lg, lu);
+  } else {
+    const int rpw = (WAVE / gd.L) * NB_DOWN;
+    dim3 grid((a.d + rpw - 1) / rpw, a.T);
+    hipLaunchKernelGGL((k_down<BITS, P, SPLIT, NB_DOWN>), grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I,
+                       lg2g, gd.L, a.act, a.idx, a.ex.down, a.out, a.w_fuse, a.r_fuse, a.y_fuse, ldn);
+  }
+}
+
+template <int BITS, bool SPLIT>
+void launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
+              LoraRef lu, LoraRef ldn, int which) {
+  switch (which == 0 ? gu.P : gd.P) {
+    case 1: launch_pair<BITS, 1, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
+    case 2: launch_pair<BITS, 2, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
+    case 3: launch_pair<BITS, 3, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
+    default: launch_pair<BITS, 4, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
+  }
+}
+
+}  // namespace
+
+bool decode_shape_supported(int bits, int group, int d, int I) {
+  return row_geo(bits, d).ok && row_geo(bits, I).ok && group >= 32;
+}
+
+hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a) {
+  const RowGeo gu = row_geo(a.bits, a.d), gd = row_geo(a.bits, a.I);
+  LoraRef lg{}, lu{}, ldn{};
+  if (a.lora3) {
+    const moe_lora* L3 = a.lora3;
+    const int waves = a.T * L3[0].rank, waves_u = a.T * L3[1].rank;
+    hipLaunchKernelGGL(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[0].rank,
+                       (int)((a.flags & MOE_INPUT_RMSNORM) != 0), a.x, (size_t)a.d, L3[0].A, a.u_gate);
+    hipLaunchKernelGGL(k_lora_a, dim3((waves_u + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[1].rank,
+                       (int)((a.flags & MOE_INPUT_RMSNORM) != 0), a.x, (size_t)a.d, L3[1].A, a.u_up);
+    lg = LoraRef{L3[0].B, a.u_gate, L3[0].rank, L3[0].alpha / (float)L3[0].rank};
+    lu = LoraRef{L3[1].B, a.u_up, L3[1].rank, L3[1].alpha / (float)L3[1].rank};
+    ldn = LoraRef{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank};
+  }
+  const bool split = a.bits == 2 && a.group < SegT<2>::COLS;
+  for (int which = 0; which < 2; ++which) {
+    if (which == 1 && a.lora3) {
+      const int waves = a.T * a.lora3[2].rank;
+      hipLaunchKernelGGL(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, a.T, a.I, a.lora3[2].rank, 0,
+                         a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down);
+    }
+    if (a.bits == 4)
+      launch_p<4, false>(s, a, gu, gd, lg, lu, ldn, which);
+    else if (split)
+      launch_p<2, true>(s, a, gu, gd, lg, lu, ldn, which);
+    else
+      launch_p<2, false>(s, a, gu, gd, lg, lu, ldn, which);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,
+                          const uint16_t* r, const float* shared, uint16_t* y) {
+  const size_t n = (size_t)T * d;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s, T, K, d, o, w, r, shared, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

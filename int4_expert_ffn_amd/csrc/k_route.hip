@@ -1,0 +1,317 @@
+// Routing on gfx950: float16 router / prerouter-head matvecs and the wave64 softmax top-K.
+//
+// Router logits and top-K: each token goes to the K experts with the largest router logits
+// ("Arquitecturas nativas para device: MoE de grano fino y pre-attention router", section "Dos
+// niveles de sparsity").  Prerouter head: head(z) = fc2(gelu_erf(fc1 z)) + l(z) over
+// z = [x; K-hot of this layer's routing at t; K-hot at t-1], length d + 2E ("La otra mitad del
+// muro de la memoria: Servir MoEs de 35B desde SSD ...", section "Arquitectura del cabezal
+// Prerouter", both equations).  The K-hot columns of fc1 and l are stored as rows (split
+// layout), so the head reads only the 2K selected rows instead of 2E dense columns.
+//
+// Matvecs: one wave per output row; the row is held in registers as 128-bit segments and reused
+// across the wave's tokens; products of float16 pairs are exact in float32 (v_dot2_f32_f16).
+// The RMS-norm option scales the finished dot product (linearity), so x is never rounded.
+//
+// Top-K: one wave per token, up to 16 logits per lane.  A logit becomes a 64-bit key
+// (order-preserving bits of the float, then the complemented expert index), so one unsigned
+// max picks the largest logit and, among equal logits, the lowest index.  K rounds of a
+// wave-wide max pick the experts in order.
+#include <math.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+namespace {
+
+// Dot products of one float16 row (held in registers) with TPW tokens' float16 activations.
+template <int NSEG>
+__device__ __forceinline__ void row_dot_tokens(const uint4* wr, int nseg, const uint16_t* __restrict__ x,
+                                               int d, int t, int lane, float& acc, float& sq) {
+  acc = 0.f;
+  sq = 0.f;
+  const uint16_t* xt = x + (size_t)t * d;
+#pragma unroll
+  for (int p = 0; p < NSEG; ++p) {
+    const int sgi = lane + p * WAVE;
+    if (sgi < nseg) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xt + (size_t)sgi * 8);
+      const uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t wa[4] = {wr[p].x, wr[p].y, wr[p].z, wr[p].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_amdgcn_fdot2(as_h2(wa[i]), as_h2(xa[i]), acc, false);
+        sq = __builtin_amdgcn_fdot2(as_h2(xa[i]), as_h2(xa[i]), sq, false);
+      }
+    }
+  }
+  acc = group_sum(acc, WAVE);
+  sq = group_sum(sq, WAVE);
+}
+
+template <int NSEG>
+__device__ __forceinline__ void load_row(uint4* wr, const uint16_t* __restrict__ row, int nseg, int lane) {
+#pragma unroll
+  for (int p = 0; p < NSEG; ++p) {
+    const int sgi = lane + p * WAVE;
+    wr[p] = sgi < nseg ? *reinterpret_cast<const uint4*>(row + (size_t)sgi * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// logits[t][e] = s_t * W[e] . x_t ; grid (E, ceil(T / tpw)), one wave per block.
+template <int NSEG>
+__global__ void __launch_bounds__(64) k_router(int T, int d, int E, uint32_t flags, int tpw,
+                                               const uint16_t* __restrict__ x,
+                                               const uint16_t* __restrict__ W, float* __restrict__ logits) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int nseg = d / 8;
+  uint4 wr[NSEG];
+  load_row<NSEG>(wr, W + (size_t)e * d, nseg, lane);
+  const int t1 = min(T, (int)(blockIdx.y + 1) * tpw);
+  for (int t = blockIdx.y * tpw; t < t1; ++t) {
+    float acc, sq;
+    row_dot_tokens<NSEG>(wr, nseg, x, d, t, lane, acc, sq);
+    const float s = (flags & MOE_INPUT_RMSNORM) ? 1.f / sqrtf(sq / (float)d + RMS_EPS) : 1.f;
+    if (lane == 0) logits[(size_t)t * E + e] = acc * s;
+  }
+}
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0;  // -0 ranks as +0 (equal logits tie to the lower index)
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_order_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+constexpr int TOPK_VPL = MOE_MAX_E / WAVE;  // logits per lane
+
+__global__ void __launch_bounds__(64) k_topk(int T, int E, int K, uint32_t flags,
+                                             const float* __restrict__ logits, int32_t* __restrict__ idx,
+                                             float* __restrict__ w) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float* lt = logits + (size_t)t * E;
+  uint64_t key[TOPK_VPL];
+  float val[TOPK_VPL];
+#pragma unroll
+  for (int j = 0; j < TOPK_VPL; ++j) {
+    const int e = lane + j * WAVE;
+    val[j] = e < E ? lt[e] : 0.f;
+    key[j] = e < E ? ((uint64_t)order_bits(val[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  int sel_e[MOE_MAX_K];
+  float sel_v[MOE_MAX_K];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_K; ++k) {
+    sel_e[k] = 0;
+    sel_v[k] = 0.f;
+    if (k < K) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < TOPK_VPL; ++j) best = key[j] > best ? key[j] : best;
+      for (int m = WAVE / 2; m > 0; m >>= 1) {
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), m, WAVE);
+        const uint32_t lo = __shfl_xor((uint32_t)best, m, WAVE);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+      }
+      const int eb = (int)(0xFFFFFFFFu - (uint32_t)best);
+#pragma unroll
+      for (int j = 0; j < TOPK_VPL; ++j)
+        if (key[j] == best) key[j] = 0;
+      sel_e[k] = eb;
+      sel_v[k] = from_order_bits((uint32_t)(best >> 32));
+    }
+  }
+  // softmax weights, float32
+  float den = 0.f;
+  if (flags & MOE_TOPK_RENORM) {
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+      if (k < K) den += expf(sel_v[k] - sel_v[0]);
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < TOPK_VPL; ++j)
+      if (lane + j * WAVE < E) part += expf(val[j] - sel_v[0]);
+    den = group_sum(part, WAVE);
+  }
+  if (lane < K) {
+    float v = 0.f;
+    int e = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+      if (k == lane) {
+        v = sel_v[k];
+        e = sel_e[k];
+      }
+    idx[(size_t)t * K + lane] = e;
+    w[(size_t)t * K + lane] = expf(v - sel_v[0]) / den;
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
+// prerouter head
+struct HeadArgs {
+  int T, d, E, K, H;
+  uint32_t flags;
+  const uint16_t* x;
+  const int32_t* cur;
+  const int32_t* prev;
+  moe_prerouter_w pw;
+  float* g;    // [T][H] gelu(fc1 z + b1)
+  float* lin;  // [T][E] l z + b_l
+};
+
+__device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
+
+// Sum of the rows of `rtab` ([2E][ncol] float16) selected by the K-hot vectors, column c.
+__device__ __forceinline__ float khot_gather(const uint16_t* __restrict__ rtab, int ncol, int c, int E, int K,
+                                             const int32_t* cur, const int32_t* prev, bool& bad) {
+  float s = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int e = cur[k];
+    if ((unsigned)e >= (unsigned)E) {
+      bad = true;
+      continue;
+    }
+    s += h2f(rtab[(size_t)e * ncol + c]);
+  }
+  if (prev) {
+    for (int k = 0; k < K; ++k) {
+      const int e = prev[k];
+      if ((unsigned)e >= (unsigned)E) {
+        bad = true;
+        continue;
+      }
+      s += h2f(rtab[(size_t)(E + e) * ncol + c]);
+    }
+  }
+  return s;
+}
+
+// fc1 rows (blockIdx.x < H) and l rows (blockIdx.x >= H) against x; grid (H + E, ceil(T / tpw)).
+template <int NSEG>
+__global__ void __launch_bounds__(64) k_head_in(HeadArgs a, int tpw) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const bool is_fc1 = r < a.H;
+  const int c = is_fc1 ? r : r - a.H;
+  const uint16_t* W = is_fc1 ? a.pw.fc1_x + (size_t)c * a.d : a.pw.lin_x + (size_t)c * a.d;
+  const int nseg = a.d / 8;
+  uint4 wr[NSEG];
+  load_row<NSEG>(wr, W, nseg, lane);
+  const int t1 = min(a.T, (int)(blockIdx.y + 1) * tpw);
+  for (int t = blockIdx.y * tpw; t < t1; ++t) {
+    float acc, sq;
+    row_dot_tokens<NSEG>(wr, nseg, a.x, a.d, t, lane, acc, sq);
+    if (lane == 0) {
+      const float s = (a.flags & MOE_INPUT_RMSNORM) ? 1.f / sqrtf(sq / (float)a.d + RMS_EPS) : 1.f;
+      bool bad = false;
+      const int32_t* cur = a.cur + (size_t)t * a.K;
+      const int32_t* prev = a.prev ? a.prev + (size_t)t * a.K : nullptr;
+      if (is_fc1) {
+        float v = acc * s + khot_gather(a.pw.fc1_r, a.H, c, a.E, a.K, cur, prev, bad);
+        if (a.pw.fc1_b) v += h2f(a.pw.fc1_b[c]);
+        v = gelu_erf(v);
+        a.g[(size_t)t * a.H + c] = bad ? quiet_nan() : v;
+      } else {
+        float v = acc * s + khot_gather(a.pw.lin_r, a.E, c, a.E, a.K, cur, prev, bad);
+        if (a.pw.lin_b) v += h2f(a.pw.lin_b[c]);
+        a.lin[(size_t)t * a.E + c] = bad ? quiet_nan() : v;
+      }
+    }
+  }
+}
+
+// logits[t][e] = fc2[e] . g_t + fc2_b[e] + lin[t][e]; grid (E, ceil(T / tpw)).
+template <int NSEG>
+__global__ void __launch_bounds__(64) k_head_out(HeadArgs a, int tpw, float* __restrict__ logits) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int nseg = a.H / 8;
+  uint4 wr[NSEG];
+  load_row<NSEG>(wr, a.pw.fc2 + (size_t)e * a.H, nseg, lane);
+  const int t1 = min(a.T, (int)(blockIdx.y + 1) * tpw);
+  for (int t = blockIdx.y * tpw; t < t1; ++t) {
+    const float* gt = a.g + (size_t)t * a.H;
+    float acc = 0.f;
+#pragma unroll
+    for (int p = 0; p < NSEG; ++p) {
+      const int sgi = lane + p * WAVE;
+      if (sgi < nseg) {
+        const float4 g0 = *reinterpret_cast<const float4*>(gt + (size_t)sgi * 8);
+        const float4 g1 = *reinterpret_cast<const float4*>(gt + (size_t)sgi * 8 + 4);
+        const half2_t w0 = as_h2(wr[p].x), w1 = as_h2(wr[p].y), w2 = as_h2(wr[p].z), w3 = as_h2(wr[p].w);
+        acc = fmaf((float)w0.x, g0.x, acc);
+        acc = fmaf((float)w0.y, g0.y, acc);
+        acc = fmaf((float)w1.x, g0.z, acc);
+        acc = fmaf((float)w1.y, g0.w, acc);
+        acc = fmaf((float)w2.x, g1.x, acc);
+        acc = fmaf((float)w2.y, g1.y, acc);
+        acc = fmaf((float)w3.x, g1.z, acc);
+        acc = fmaf((float)w3.y, g1.w, acc);
+      }
+    }
+    acc = group_sum(acc, WAVE);
+    if (lane == 0) {
+      float v = acc + a.lin[(size_t)t * a.E + e];
+      if (a.pw.fc2_b) v += h2f(a.pw.fc2_b[e]);
+      logits[(size_t)t * a.E + e] = v;
+    }
+  }
+}
+
+int nseg_for(int cols) {  // 128-bit segments per lane, rounded up to a power of two
+  const int per_lane = (cols / 8 + WAVE - 1) / WAVE;
+  int n = 1;
+  while (n < per_lane) n <<= 1;
+  return n;
+}
+
+constexpr int TPW = 16;  // tokens per wave in the matvecs
+
+}  // namespace
+
+hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags, const uint16_t* x,
+                              const uint16_t* w, float* logits) {
+  const dim3 grid(E, (T + TPW - 1) / TPW);
+  switch (nseg_for(d)) {
+    case 1: hipLaunchKernelGGL(k_router<1>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+    case 2: hipLaunchKernelGGL(k_router<2>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+    case 4: hipLaunchKernelGGL(k_router<4>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+    case 8: hipLaunchKernelGGL(k_router<8>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+    default: hipLaunchKernelGGL(k_router<16>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(hipStream_t s, int T, int E, int K, uint32_t flags, const float* logits, int32_t* idx,
+                       float* w) {
+  hipLaunchKernelGGL(k_topk, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_prerouter(hipStream_t s, int T, int d, int E, int K, uint32_t flags, const uint16_t* x,
+                            const int32_t* idx_cur, const int32_t* idx_prev, const moe_prerouter_w& pw,
+                            float* logits, float* ws_g, float* ws_lin) {
+  HeadArgs a{T, d, E, K, pw.d_hidden, flags, x, idx_cur, idx_prev, pw, ws_g, ws_lin};
+  const int ty = (T + TPW - 1) / TPW;
+  const dim3 g1(a.H + E, ty), g2(E, ty);
+  switch (nseg_for(d)) {
+    case 1: hipLaunchKernelGGL(k_head_in<1>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 2: hipLaunchKernelGGL(k_head_in<2>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 4: hipLaunchKernelGGL(k_head_in<4>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 8: hipLaunchKernelGGL(k_head_in<8>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    default: hipLaunchKernelGGL(k_head_in<16>, g1, dim3(WAVE), 0, s, a, TPW); break;
+  }
+  switch (nseg_for(a.H)) {
+    case 1: hipLaunchKernelGGL(k_head_out<1>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 2: hipLaunchKernelGGL(k_head_out<2>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 4: hipLaunchKernelGGL(k_head_out<4>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 8: hipLaunchKernelGGL(k_head_out<8>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    default: hipLaunchKernelGGL(k_head_out<16>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

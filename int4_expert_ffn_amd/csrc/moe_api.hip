@@ -1,0 +1,188 @@
+// C ABI of the MoE layer library: host-side argument checks, workspace sizing and dispatch to
+// the gfx950 kernels.  Nothing is enqueued when a check fails; no call allocates or keeps state.
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_RANK = 64;
+constexpr int GROUPED_MIN_T = 32;  // token count from which the grouped MFMA path runs
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool known_flags(uint32_t f) { return (f & ~(MOE_TOPK_RENORM | MOE_INPUT_RMSNORM)) == 0; }
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool routing_dims_ok(int32_t T, int32_t E, int32_t K) {
+  return T >= 1 && E >= 1 && E <= MOE_MAX_E && K >= 1 && K <= MOE_MAX_K && K <= E;
+}
+
+// workspace layout of moe_expert_ffn_q4
+struct FfnWs {
+  size_t act, u_gate, u_up, u_down, grouped, total;
+};
+FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex) {
+  FfnWs w{};
+  w.act = 0;
+  w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(uint16_t));
+  w.u_up = w.u_gate + align_up((size_t)T * MAX_RANK * sizeof(float));
+  w.u_down = w.u_up + align_up((size_t)T * MAX_RANK * sizeof(float));
+  w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * sizeof(float));
+  w.total = w.grouped + (T >= GROUPED_MIN_T ? grouped_workspace_extra(T, K, ex->n_experts, ex->d_model) : 0);
+  return w;
+}
+
+moe_status check_qmat(const moe_qmat& m) {
+  if (!m.q || !m.scales || !m.biases) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(m.q)) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)m.scales & 1u) || ((uintptr_t)m.biases & 1u)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status check_experts(const moe_experts* ex) {
+  if (!ex) return MOE_ERR_INVALID_ARG;
+  if (ex->n_experts < 1 || ex->n_experts > MOE_MAX_E) return MOE_ERR_INVALID_ARG;
+  if (ex->bits != 4 && ex->bits != 2) return MOE_ERR_UNSUPPORTED;
+  if (ex->group != 32 && ex->group != 64 && ex->group != 128) return MOE_ERR_UNSUPPORTED;
+  const int d = ex->d_model, I = ex->d_ff;
+  if (d < 1 || I < 1 || d > MOE_MAX_D || I > MOE_MAX_D) return MOE_ERR_INVALID_ARG;
+  if (d % ex->group || I % ex->group) return MOE_ERR_INVALID_ARG;
+  if ((d * ex->bits) % 128 || (I * ex->bits) % 128) return MOE_ERR_INVALID_ARG;
+  if (!decode_shape_supported(ex->bits, ex->group, d, I)) return MOE_ERR_UNSUPPORTED;
+  moe_status s;
+  if ((s = check_qmat(ex->gate)) != MOE_OK) return s;
+  if ((s = check_qmat(ex->up)) != MOE_OK) return s;
+  if ((s = check_qmat(ex->down)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported bits, group or shape";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown moe_status";
+}
+
+int32_t moe_version(void) { return 100; }
+
+moe_status moe_route_topk(void* stream, int32_t T, int32_t d, int32_t E, int32_t K, uint32_t flags,
+                          const uint16_t* x, const uint16_t* w_router, float* logits, int32_t* idx, float* w) {
+  if (!routing_dims_ok(T, E, K) || !known_flags(flags)) return MOE_ERR_INVALID_ARG;
+  if (!logits || !idx || !w) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (w_router) {
+    if (!x || d < 8 || d % 8 || d > MOE_MAX_D) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (launch_router_gemv(s, T, d, E, flags, x, w_router, logits) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return from_hip(launch_topk(s, T, E, K, flags, logits, idx, w));
+}
+
+size_t moe_prerouter_workspace_size(int32_t T, int32_t E, int32_t d_hidden) {
+  if (T < 1 || E < 1 || d_hidden < 1) return 0;
+  return align_up((size_t)T * d_hidden * sizeof(float)) + align_up((size_t)T * E * sizeof(float));
+}
+
+moe_status moe_prerouter(void* stream, int32_t T, int32_t d, int32_t E, int32_t K, uint32_t flags,
+                         const uint16_t* x, const int32_t* idx_cur, const int32_t* idx_prev,
+                         const moe_prerouter_w* pw, float* logits, void* workspace, size_t workspace_bytes) {
+  if (!routing_dims_ok(T, E, K) || !known_flags(flags)) return MOE_ERR_INVALID_ARG;
+  if (!x || !idx_cur || !pw || !logits || !workspace) return MOE_ERR_INVALID_ARG;
+  if (d < 8 || d % 8 || d > MOE_MAX_D) return MOE_ERR_INVALID_ARG;
+  const int H = pw->d_hidden;
+  if (H < 8 || H % 8 || H > MOE_MAX_D) return MOE_ERR_INVALID_ARG;
+  if (!pw->fc1_x || !pw->fc1_r || !pw->fc2 || !pw->lin_x || !pw->lin_r) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(pw->fc1_x) || !aligned16(pw->fc2) || !aligned16(pw->lin_x) ||
+      !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe_prerouter_workspace_size(T, E, H)) return MOE_ERR_INVALID_ARG;
+  float* g = (float*)workspace;
+  float* lin = (float*)((char*)workspace + align_up((size_t)T * H * sizeof(float)));
+  return from_hip(launch_prerouter((hipStream_t)stream, T, d, E, K, flags, x, idx_cur, idx_prev, *pw, logits, g, lin));
+}
+
+size_t moe_expert_ffn_workspace_size(int32_t T, int32_t K, const moe_experts* ex) {
+  if (!ex || T < 1 || K < 1 || ex->d_ff < 1 || ex->d_model < 1) return 0;
+  return ffn_ws(T, K, ex).total;
+}
+
+moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                             const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
+                             const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace,
+                             size_t workspace_bytes) {
+  moe_status st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  if (!routing_dims_ok(T, ex->n_experts, K) || !known_flags(flags)) return MOE_ERR_INVALID_ARG;
+  if (!x || !idx || !workspace || !aligned16(x) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  const bool fuse = w_fuse || r_fuse || y_fuse;
+  if (fuse && !(w_fuse && r_fuse && y_fuse)) return MOE_ERR_INVALID_ARG;
+  if (!out && !fuse) return MOE_ERR_INVALID_ARG;
+  if (lora3) {
+    if (ex->n_experts != 1) return MOE_ERR_INVALID_ARG;
+    for (int m = 0; m < 3; ++m) {
+      if (!lora3[m].A || !lora3[m].B || lora3[m].rank < 1 || lora3[m].rank > MAX_RANK) return MOE_ERR_INVALID_ARG;
+      if (!aligned16(lora3[m].A)) return MOE_ERR_INVALID_ARG;
+    }
+  }
+  const FfnWs ws = ffn_ws(T, K, ex);
+  if (workspace_bytes < ws.total) return MOE_ERR_INVALID_ARG;
+  char* base = (char*)workspace;
+  DecodeArgs a{};
+  a.T = T;
+  a.K = K;
+  a.E = ex->n_experts;
+  a.d = ex->d_model;
+  a.I = ex->d_ff;
+  a.bits = ex->bits;
+  a.group = ex->group;
+  a.flags = flags;
+  a.x = x;
+  a.idx = idx;
+  a.ex = *ex;
+  a.lora3 = lora3;
+  a.out = out;
+  a.w_fuse = w_fuse;
+  a.r_fuse = r_fuse;
+  a.y_fuse = y_fuse;
+  a.act = (uint16_t*)(base + ws.act);
+  a.u_gate = (float*)(base + ws.u_gate);
+  a.u_up = (float*)(base + ws.u_up);
+  a.u_down = (float*)(base + ws.u_down);
+  hipStream_t s = (hipStream_t)stream;
+  if (T >= GROUPED_MIN_T) {
+    GroupedArgs g{};
+    g.base = a;
+    char* gb = base + ws.grouped;
+    const size_t o_counts = 0;
+    const size_t o_offsets = o_counts + align_up((size_t)ex->n_experts * sizeof(int32_t));
+    const size_t o_perm = o_offsets + align_up((size_t)(ex->n_experts + 1) * sizeof(int32_t));
+    const size_t o_osorted = o_perm + align_up((size_t)T * K * sizeof(int32_t));
+    g.counts = (int32_t*)(gb + o_counts);
+    g.offsets = (int32_t*)(gb + o_offsets);
+    g.perm = (int32_t*)(gb + o_perm);
+    g.o_sorted = (float*)(gb + o_osorted);
+    return from_hip(launch_expert_grouped(s, g));
+  }
+  return from_hip(launch_expert_decode(s, a));
+}
+
+moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,
+                       const uint16_t* r, const float* shared, uint16_t* y) {
+  if (T < 1 || K < 1 || K > MOE_MAX_K || d < 1 || d > MOE_MAX_D) return MOE_ERR_INVALID_ARG;
+  if (!o || !w || !r || !y) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_combine((hipStream_t)stream, T, K, d, o, w, r, shared, y));
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels: float16 bit conversions, wave64 reductions and
+// the 16-byte dequantise-and-dot step.
+//
+// A "segment" is 16 bytes of one packed row: 4 little-endian uint32 words holding 32 4-bit or
+// 64 2-bit codes.  One lane loads one segment with a single 128-bit load.  The codes are turned
+// into float16 pairs with the exponent trick: (word >> s) & 0x000F000F | 0x64006400 is the
+// float16 pair (1024 + c_lo, 1024 + c_hi), exact; subtracting 1024 leaves the codes as exact
+// float16, and v_dot2_f32_f16 multiplies them by an activation pair with float32 accumulation.
+// The activation pairs are pre-permuted to match: for 4-bit, word w pairs columns (8w+j, 8w+j+4),
+// j = 0..3; for 2-bit, (16w+j, 16w+j+8), j = 0..7.
+//
+// Per group the dot product is regrouped as  sum_j (c_j s + b) x_j = s sum_j c_j x_j + b sum_j x_j
+// (the FMA rewrite of "nibble * scale + bias" in the Metal dequant listing of "Inferencia de LLM
+// MoE en MacBook Pro: Streaming de Expertos desde SSD con Metal", section "Arquitectura del
+// Sistema"), so scale and bias cost two FMAs per half segment instead of one per weight.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr float RMS_EPS = 1e-6f;
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// xor-butterfly sum over aligned groups of `width` lanes (power of two <= 64); every lane of a
+// group ends with the group's sum, always added in the same order.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = width >> 1; m > 0; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
+
+// ---------------------------------------------------------------------------------------------
+// Segment geometry per code width.
+template <int BITS>
+struct SegT;
+template <>
+struct SegT<4> {
+  static constexpr int COLS = 32;    // columns per 16-byte segment
+  static constexpr int PAIRS = 16;   // activation pairs per segment
+  static constexpr int PAIRS_PER_WORD = 4;
+};
+template <>
+struct SegT<2> {
+  static constexpr int COLS = 64;
+  static constexpr int PAIRS = 32;
+  static constexpr int PAIRS_PER_WORD = 8;
+};
+
+// Build the permuted activation pairs of one segment from a float16 row (32 or 64 columns
+// starting at `xs`, 16-byte aligned).  Also returns sum x over each half segment and sum x^2.
+template <int BITS>
+__device__ __forceinline__ void load_xpairs(const uint16_t* __restrict__ xs, uint32_t* xp, float* sx,
+                                            float& sq) {
+  const uint4* p = reinterpret_cast<const uint4*>(xs);
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // word w: columns 8w..8w+7 = one uint4 of halves
+      uint4 u = p[w];
+      xp[w * 4 + 0] = (u.x & 0xFFFFu) | (u.z << 16);
+      xp[w * 4 + 1] = (u.x >> 16) | (u.z & 0xFFFF0000u);
+      xp[w * 4 + 2] = (u.y & 0xFFFFu) | (u.w << 16);
+      xp[w * 4 + 3] = (u.y >> 16) | (u.w & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // word w: columns 16w..16w+15 = two uint4 of halves
+      uint4 a = p[2 * w], b = p[2 * w + 1];
+      uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t lo = (j & 1) ? (av[j >> 1] >> 16) : (av[j >> 1] & 0xFFFFu);
+        uint32_t hi = (j & 1) ? (bv[j >> 1] & 0xFFFF0000u) : (bv[j >> 1] << 16);
+        xp[w * 8 + j] = lo | hi;
+      }
+    }
+  }
+  const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+  float s0 = 0.f, s1 = 0.f, q = 0.f;
+  constexpr int HP = SegT<BITS>::PAIRS / 2;
+#pragma unroll
+  for (int i = 0; i < SegT<BITS>::PAIRS; ++i) {
+    half2_t v = as_h2(xp[i]);
+    if (i < HP)
+      s0 = __builtin_amdgcn_fdot2(v, one, s0, false);
+    else
+      s1 = __builtin_amdgcn_fdot2(v, one, s1, false);
+    q = __builtin_amdgcn_fdot2(v, v, q, false);
+  }
+  sx[0] = s0;
+  sx[1] = s1;
+  sq += q;
+}
+
+// sum_j c_j x_j over the two half segments (words 0-1 and words 2-3) of one 16-byte segment.
+template <int BITS>
+__device__ __forceinline__ void dot_segment(uint4 q, const uint32_t* xp, float& d0, float& d1) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      uint32_t t = ((w[i] >> (BITS * j)) & MASK) | 0x64006400u;
+      half2_t c = as_h2(t) - k1024;
+      if (i < 2)
+        d0 = __builtin_amdgcn_fdot2(c, as_h2(xp[i * PPW + j]), d0, false);
+      else
+        d1 = __builtin_amdgcn_fdot2(c, as_h2(xp[i * PPW + j]), d1, false);
+    }
+  }
+}
+
+}  // namespace moe

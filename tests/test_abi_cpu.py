@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before anything is enqueued (so no call here reaches the
+HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+lib_mod = pytest.importorskip("int4_expert_ffn_amd._lib", reason="libmoe.so not built")
+torch = pytest.importorskip("torch")
+if torch.cuda.device_count() > 0:   # the fake addresses below must never reach a real device
+    pytest.skip("host-only argument checks; skipped where a GPU is visible", allow_module_level=True)
+L = lib_mod._lib
+OK, INVALID, UNSUP = 0, 1, 2
+
+FAKE = 0x7F0000000000   # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 8
+    assert sorted(lib_mod.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n)
+    assert L.moe_version() == 100
+    for s in (0, 1, 2, 3):
+        assert L.moe_status_string(s).startswith(b"MOE_")
+
+
+def _ex(E=16, d=256, I=128, bits=4, group=32, q=FAKE):
+    m = lambda: lib_mod.moe_qmat(q, FAKE, FAKE)
+    return lib_mod.moe_experts(E, d, I, bits, group, m(), m(), m())
+
+
+def _ffn(ex, T=1, K=2, flags=0, x=FAKE, idx=FAKE, lora=None, out=FAKE, wf=None, rf=None, yf=None,
+         ws=FAKE, wsb=1 << 40):
+    st = L.moe_expert_ffn_q4(None, T, K, flags, x, idx, ctypes.byref(ex), lora, out, wf, rf, yf, ws, wsb)
+    assert st in (INVALID, UNSUP), "a call with fake pointers must never pass validation"
+    return st
+
+
+def test_route_topk_rejects():
+    r = lambda *a: L.moe_route_topk(None, *a)
+    assert r(0, 256, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID       # T < 1
+    assert r(1, 256, 16, 17, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID      # K > E
+    assert r(1, 256, 64, 17, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID      # K > 16
+    assert r(1, 256, 1025, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID     # E > 1024
+    assert r(1, 256, 16, 2, 0, FAKE, FAKE, FAKE, None, FAKE) == INVALID       # idx NULL
+    assert r(1, 256, 16, 2, 0x8, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID     # unknown flag
+    assert r(1, 250, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID       # d % 8
+    assert r(1, 16384, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID     # d > 8192
+    assert r(1, 256, 16, 2, 0, FAKE + 2, FAKE, FAKE, FAKE, FAKE) == INVALID   # misaligned x
+    assert r(1, 256, 16, 2, 0, None, FAKE, FAKE, FAKE, FAKE) == INVALID       # router without x
+
+
+def test_expert_ffn_rejects():
+    assert _ffn(_ex(bits=3)) == UNSUP
+    assert _ffn(_ex(bits=8)) == UNSUP
+    assert _ffn(_ex(group=16)) == UNSUP
+    assert _ffn(_ex(group=256)) == UNSUP
+    assert _ffn(_ex(d=240)) == INVALID                        # d % group
+    assert _ffn(_ex(d=16384, group=64)) == INVALID            # d > 8192
+    assert _ffn(_ex(bits=2, d=288, group=32)) == INVALID      # 2-bit row not whole 16-byte segments
+    assert _ffn(_ex(q=FAKE + 4)) == INVALID                   # misaligned q
+    assert _ffn(_ex(E=0)) == INVALID
+    assert _ffn(_ex(E=2), K=3) == INVALID                     # K > E
+    assert _ffn(_ex(), T=0) == INVALID
+    assert _ffn(_ex(), x=None) == INVALID
+    assert _ffn(_ex(), out=None) == INVALID                   # no output at all
+    assert _ffn(_ex(), out=None, wf=FAKE, rf=FAKE) == INVALID  # partial fuse triple
+    assert _ffn(_ex(), wsb=16) == INVALID                     # workspace too small
+    assert _ffn(_ex(), ws=FAKE + 8) == INVALID                # misaligned workspace
+    lora = (lib_mod.moe_lora * 3)(*[lib_mod.moe_lora(FAKE, FAKE, 16, 32.0)] * 3)
+    assert _ffn(_ex(E=16), lora=lora) == INVALID              # LoRA only on a single shared expert
+    bad_rank = (lib_mod.moe_lora * 3)(*[lib_mod.moe_lora(FAKE, FAKE, 65, 32.0)] * 3)
+    assert _ffn(_ex(E=1), K=1, lora=bad_rank) == INVALID
+
+
+def test_prerouter_and_combine_reject():
+    pw = lib_mod.moe_prerouter_w(1024, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None)
+    p = lambda *a, **k: L.moe_prerouter(None, *a)
+    assert p(1, 2048, 256, 4, 0, FAKE, FAKE, None, ctypes.byref(pw), FAKE, FAKE, 16) == INVALID   # workspace
+    assert p(1, 2048, 256, 4, 0, FAKE, None, None, ctypes.byref(pw), FAKE, FAKE, 1 << 30) == INVALID  # idx_cur
+    pw0 = lib_mod.moe_prerouter_w(1020, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None)
+    assert p(1, 2048, 256, 4, 0, FAKE, FAKE, None, ctypes.byref(pw0), FAKE, FAKE, 1 << 30) == INVALID  # H % 8
+    pw1 = lib_mod.moe_prerouter_w(1024, FAKE, None, None, FAKE, None, FAKE, FAKE, None)
+    assert p(1, 2048, 256, 4, 0, FAKE, FAKE, None, ctypes.byref(pw1), FAKE, FAKE, 1 << 30) == INVALID  # fc1_r
+    c = lambda *a: L.moe_combine(None, *a)
+    assert c(0, 4, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
+    assert c(1, 17, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
+    assert c(1, 4, 2048, None, FAKE, FAKE, None, FAKE) == INVALID
+    assert c(1, 4, 2048, FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_workspace_sizes_closed_form():
+    al = lambda v: (v + 255) // 256 * 256
+    assert L.moe_prerouter_workspace_size(1, 256, 1024) == al(4096) + al(1024)
+    assert L.moe_prerouter_workspace_size(0, 256, 1024) == 0
+    ex = _ex(E=256, d=2048, I=512, group=64)
+    want = al(1 * 4 * 512 * 2) + 3 * al(64 * 4)
+    assert L.moe_expert_ffn_workspace_size(1, 4, ctypes.byref(ex)) == want
+    assert L.moe_expert_ffn_workspace_size(256, 4, ctypes.byref(ex)) > want
+
+
+def test_binding_checks_tensors_on_host():
+    with pytest.raises(ValueError):
+        lib_mod._ptr(torch.zeros(4), None, "x")      # a host tensor is refused before any call
