@@ -57,6 +57,9 @@ class moe_prerouter_w(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int4_expert_ffn_amd.build`")
+    # torch first: its HIP runtime must be the one libmoe.so binds to.  Loaded the other way round,
+    # the process ends up with two runtimes and torch's streams are foreign to the library's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
     st = ctypes.c_int

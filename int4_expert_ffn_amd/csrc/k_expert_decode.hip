@@ -63,7 +63,31 @@ __global__ void __launch_bounds__(256) k_lora_a(int T, int n_in, int rank, int r
   if (lane == 0) u[(size_t)t * rank + r] = acc * s;
 }
 
+// scale and bias of the one or two groups a segment touches (SPLIT: a 2-bit segment spanning two
+// 32-column groups)
+template <int BITS, bool SPLIT>
+struct SegSB {
+  uint16_t sa, ba, sb, bb;
+  __device__ __forceinline__ void load(const moe_qmat& m, size_t row, int ngr, int lg2g, int seg) {
+    const int c0 = seg * SegT<BITS>::COLS;
+    const size_t ga = row * ngr + (c0 >> lg2g);
+    sa = m.scales[ga];
+    ba = m.biases[ga];
+    if (SPLIT) {
+      const size_t gb = row * ngr + ((c0 + SegT<BITS>::COLS / 2) >> lg2g);
+      sb = m.scales[gb];
+      bb = m.biases[gb];
+    }
+  }
+  // scale * sum(q x) + bias * sum(x) over the segment
+  __device__ __forceinline__ float apply(float d0, float d1, const float* sx) const {
+    if (SPLIT) return h2f(sa) * d0 + h2f(ba) * sx[0] + h2f(sb) * d1 + h2f(bb) * sx[1];
+    return h2f(sa) * (d0 + d1) + h2f(ba) * (sx[0] + sx[1]);
+  }
+};
+
 // gate/up + SwiGLU.  Items are (k, i) pairs of token t = blockIdx.y, item = k * I + i.
+// Loads go out in the order weights, scales/biases, activations, so one wait covers them all.
 template <int BITS, int P, bool SPLIT, int NB>
 __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I, int lg2g, int L,
                                                uint32_t flags, const uint16_t* __restrict__ x,
@@ -77,24 +101,13 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
   const int slot = lane / L, ls = lane % L;
   const int wpr = d * BITS / 32;
   const int ngr = d >> lg2g;
+  const int S = d * BITS / 128;
   const int items = K * I;
   const int base = blockIdx.x * RPI * NB;
   if (base >= items) return;
 
-  const int S = d * BITS / 128;
-  uint32_t xp[P][G::PAIRS];
-  float sx[P][2];
-  float sq = 0.f;
-  const uint16_t* xt = x + (size_t)t * d;
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    if (ls + p * L < S) load_xpairs<BITS>(xt + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
-  }
-  float scale = 1.f;
-  if (flags & MOE_INPUT_RMSNORM) scale = 1.f / sqrtf(group_sum(sq, L) / (float)d + RMS_EPS);
-
-  // issue every weight load of this wave first
   uint4 qg[NB][P], qu[NB][P];
+  SegSB<BITS, SPLIT> sg[NB][P], su[NB][P];
   size_t row[NB];
   bool valid[NB], bad[NB];
   int kk[NB], ii[NB];
@@ -110,15 +123,34 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
     kk[nb] = k;
     ii[nb] = i;
     row[nb] = (size_t)e * I + i;
+  }
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
       if (ls + p * L < S) {
         const size_t wo = row[nb] * wpr + (size_t)(ls + p * L) * 4;
         qg[nb][p] = *reinterpret_cast<const uint4*>(gate.q + wo);
         qu[nb][p] = *reinterpret_cast<const uint4*>(up.q + wo);
       }
-    }
-  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (ls + p * L < S) {
+        sg[nb][p].load(gate, row[nb], ngr, lg2g, ls + p * L);
+        su[nb][p].load(up, row[nb], ngr, lg2g, ls + p * L);
+      }
+
+  uint32_t xp[P][G::PAIRS];
+  float sx[P][2];
+  float sq = 0.f;
+  const uint16_t* xt = x + (size_t)t * d;
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (ls + p * L < S) load_xpairs<BITS>(xt + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
+  float scale = 1.f;
+  if (flags & MOE_INPUT_RMSNORM) scale = 1.f / sqrtf(group_sum(sq, L) / (float)d + RMS_EPS);
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -126,18 +158,12 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       if (ls + p * L >= S) continue;
-      const int c0 = (ls + p * L) * G::COLS;
-      const size_t ga = row[nb] * ngr + (c0 >> lg2g);
-      const size_t gb = SPLIT ? row[nb] * ngr + ((c0 + G::COLS / 2) >> lg2g) : ga;
-      float d0, d1;
-      d0 = d1 = 0.f;
+      float d0 = 0.f, d1 = 0.f;
       dot_segment<BITS>(qg[nb][p], xp[p], d0, d1);
-      pg += h2f(gate.scales[ga]) * d0 + h2f(gate.biases[ga]) * sx[p][0] + h2f(gate.scales[gb]) * d1 +
-            h2f(gate.biases[gb]) * sx[p][1];
+      pg += sg[nb][p].apply(d0, d1, sx[p]);
       d0 = d1 = 0.f;
       dot_segment<BITS>(qu[nb][p], xp[p], d0, d1);
-      pu += h2f(up.scales[ga]) * d0 + h2f(up.biases[ga]) * sx[p][0] + h2f(up.scales[gb]) * d1 +
-            h2f(up.biases[gb]) * sx[p][1];
+      pu += su[nb][p].apply(d0, d1, sx[p]);
     }
     pg = group_sum(pg, L) * scale;
     pu = group_sum(pu, L) * scale;
@@ -151,8 +177,9 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
   }
 }
 
-// down projection (+ weighted combine + residual).  Items are output rows j of token t.
-template <int BITS, int P, bool SPLIT, int NB>
+// down projection (+ weighted combine + residual).  Items are output rows j of token t; the wave
+// walks the token's K experts in chunks of KC, issuing every weight load of a chunk first.
+template <int BITS, int P, bool SPLIT, int NB, int KC>
 __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, int lg2g, int L,
                                              const uint16_t* __restrict__ act,
                                              const int32_t* __restrict__ idx, moe_qmat down,
@@ -166,64 +193,80 @@ __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, 
   const int slot = lane / L, ls = lane % L;
   const int wpr = I * BITS / 32;
   const int ngr = I >> lg2g;
+  const int S = I * BITS / 128;
   const int base = blockIdx.x * RPI * NB;
   if (base >= d) return;
-  const int S = I * BITS / 128;
 
+  int jj[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) jj[nb] = base + nb * RPI + slot;
   float acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = 0.f;
 
-  for (int k = 0; k < K; ++k) {
-    int e = idx[(size_t)t * K + k];
-    const bool bad = (unsigned)e >= (unsigned)E;
-    if (bad) e = 0;
-    uint4 q[NB][P];
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    uint4 q[KC][NB][P];
+    SegSB<BITS, SPLIT> sb[KC][NB][P];
+    bool bad[KC];
+    float wk[KC];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int j = base + nb * RPI + slot;
-      const size_t rw = (size_t)e * d + (j < d ? j : 0);
+    for (int kc = 0; kc < KC; ++kc) {
+      const int k = k0 + kc;
+      bad[kc] = true;
+      wk[kc] = 0.f;
+      if (k < K) {
+        int e = idx[(size_t)t * K + k];
+        bad[kc] = (unsigned)e >= (unsigned)E;
+        if (bad[kc]) e = 0;
+        wk[kc] = wf ? wf[(size_t)t * K + k] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const size_t rw = (size_t)e * d + (jj[nb] < d ? jj[nb] : 0);
+#pragma unroll
+          for (int p = 0; p < P; ++p)
+            if (ls + p * L < S) {
+              q[kc][nb][p] = *reinterpret_cast<const uint4*>(down.q + rw * wpr + (size_t)(ls + p * L) * 4);
+              sb[kc][nb][p].load(down, rw, ngr, lg2g, ls + p * L);
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int k = k0 + kc;
+      if (k >= K) break;
+      uint32_t xp[P][G::PAIRS];
+      float sx[P][2];
+      float sq = 0.f;
+      const uint16_t* at = act + ((size_t)t * K + k) * I;
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        if (ls + p * L < S) q[nb][p] = *reinterpret_cast<const uint4*>(down.q + rw * wpr + (size_t)(ls + p * L) * 4);
-    }
-    uint32_t xp[P][G::PAIRS];
-    float sx[P][2];
-    float sq = 0.f;
-    const uint16_t* at = act + ((size_t)t * K + k) * I;
+        if (ls + p * L < S) load_xpairs<BITS>(at + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      if (ls + p * L < S) load_xpairs<BITS>(at + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
-    const float wk = wf ? wf[(size_t)t * K + k] : 0.f;
+      for (int nb = 0; nb < NB; ++nb) {
+        float po = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int j = base + nb * RPI + slot;
-      const size_t rw = (size_t)e * d + (j < d ? j : 0);
-      float po = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (ls + p * L >= S) continue;
-        const int c0 = (ls + p * L) * G::COLS;
-        const size_t ga = rw * ngr + (c0 >> lg2g);
-        const size_t gb = SPLIT ? rw * ngr + ((c0 + G::COLS / 2) >> lg2g) : ga;
-        float d0 = 0.f, d1 = 0.f;
-        dot_segment<BITS>(q[nb][p], xp[p], d0, d1);
-        po += h2f(down.scales[ga]) * d0 + h2f(down.biases[ga]) * sx[p][0] + h2f(down.scales[gb]) * d1 +
-              h2f(down.biases[gb]) * sx[p][1];
-      }
-      po = group_sum(po, L);
-      if (ls == 0 && j < d) {
-        if (ldn.B) po += lora_row(ldn, t, j);
-        if (bad) po = quiet_nan();
-        if (out) out[((size_t)t * K + k) * d + j] = po;
-        acc[nb] = fmaf(wk, po, acc[nb]);
+        for (int p = 0; p < P; ++p) {
+          if (ls + p * L >= S) continue;
+          float d0 = 0.f, d1 = 0.f;
+          dot_segment<BITS>(q[kc][nb][p], xp[p], d0, d1);
+          po += sb[kc][nb][p].apply(d0, d1, sx[p]);
+        }
+        po = group_sum(po, L);
+        const int j = jj[nb];
+        if (ls == 0 && j < d) {
+          if (ldn.B) po += lora_row(ldn, t, j);
+          if (bad[kc]) po = quiet_nan();
+          if (out) out[((size_t)t * K + k) * d + j] = po;
+          acc[nb] = fmaf(wk[kc], po, acc[nb]);
+        }
       }
     }
   }
   if (yf) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int j = base + nb * RPI + slot;
+      const int j = jj[nb];
       if (ls == 0 && j < d) yf[(size_t)t * d + j] = f2h(h2f(rf[(size_t)t * d + j]) + acc[nb]);
     }
   }
@@ -268,33 +311,37 @@ int ilog2(int v) {
 }
 
 constexpr int NB_GATEUP = 2;
-constexpr int NB_DOWN = 2;
+constexpr int NB_DOWN = 1;
 
 template <int BITS, int P, bool SPLIT>
-void launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
+hipError_t launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
                  LoraRef lu, LoraRef ldn, int which) {
   const int lg2g = ilog2(a.group);
   if (which == 0) {
     const int rpw = (WAVE / gu.L) * NB_GATEUP;
     dim3 grid((a.K * a.I + rpw - 1) / rpw, a.T);
-    hipLaunchKernelGGL((k_gateup<BITS, P, SPLIT, NB_GATEUP>), grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d,
-                       a.I, lg2g, gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, a.act, lg, lu);
-  } else {
-    const int rpw = (WAVE / gd.L) * NB_DOWN;
-    dim3 grid((a.d + rpw - 1) / rpw, a.T);
-    hipLaunchKernelGGL((k_down<BITS, P, SPLIT, NB_DOWN>), grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I,
-                       lg2g, gd.L, a.act, a.idx, a.ex.down, a.out, a.w_fuse, a.r_fuse, a.y_fuse, ldn);
+    return launch(k_gateup<BITS, P, SPLIT, NB_GATEUP>, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g,
+                  gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, a.act, lg, lu);
   }
+  const int rpw = (WAVE / gd.L) * NB_DOWN;
+  dim3 grid((a.d + rpw - 1) / rpw, a.T);
+  auto go = [&](auto kern) {
+    return launch(kern, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g, gd.L, (const uint16_t*)a.act,
+                  a.idx, a.ex.down, a.out, a.w_fuse, a.r_fuse, a.y_fuse, ldn);
+  };
+  if (a.K <= 2) return go(k_down<BITS, P, SPLIT, NB_DOWN, 2>);
+  if (a.K <= 4) return go(k_down<BITS, P, SPLIT, NB_DOWN, 4>);
+  return go(k_down<BITS, P, SPLIT, NB_DOWN, 8>);
 }
 
 template <int BITS, bool SPLIT>
-void launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
+hipError_t launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const RowGeo& gd, LoraRef lg,
               LoraRef lu, LoraRef ldn, int which) {
   switch (which == 0 ? gu.P : gd.P) {
-    case 1: launch_pair<BITS, 1, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
-    case 2: launch_pair<BITS, 2, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
-    case 3: launch_pair<BITS, 3, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
-    default: launch_pair<BITS, 4, SPLIT>(s, a, gu, gd, lg, lu, ldn, which); break;
+    case 1: return launch_pair<BITS, 1, SPLIT>(s, a, gu, gd, lg, lu, ldn, which);
+    case 2: return launch_pair<BITS, 2, SPLIT>(s, a, gu, gd, lg, lu, ldn, which);
+    case 3: return launch_pair<BITS, 3, SPLIT>(s, a, gu, gd, lg, lu, ldn, which);
+    default: return launch_pair<BITS, 4, SPLIT>(s, a, gu, gd, lg, lu, ldn, which);
   }
 }
 
@@ -307,32 +354,34 @@ bool decode_shape_supported(int bits, int group, int d, int I) {
 hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a) {
   const RowGeo gu = row_geo(a.bits, a.d), gd = row_geo(a.bits, a.I);
   LoraRef lg{}, lu{}, ldn{};
+  const int rms = (a.flags & MOE_INPUT_RMSNORM) != 0;
+  hipError_t err = hipSuccess;
   if (a.lora3) {
     const moe_lora* L3 = a.lora3;
-    const int waves = a.T * L3[0].rank, waves_u = a.T * L3[1].rank;
-    hipLaunchKernelGGL(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[0].rank,
-                       (int)((a.flags & MOE_INPUT_RMSNORM) != 0), a.x, (size_t)a.d, L3[0].A, a.u_gate);
-    hipLaunchKernelGGL(k_lora_a, dim3((waves_u + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[1].rank,
-                       (int)((a.flags & MOE_INPUT_RMSNORM) != 0), a.x, (size_t)a.d, L3[1].A, a.u_up);
+    const int wg = a.T * L3[0].rank, wu = a.T * L3[1].rank;
+    err = first_error(err, launch(k_lora_a, dim3((wg + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[0].rank, rms, a.x,
+                                  (size_t)a.d, L3[0].A, a.u_gate));
+    err = first_error(err, launch(k_lora_a, dim3((wu + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[1].rank, rms, a.x,
+                                  (size_t)a.d, L3[1].A, a.u_up));
     lg = LoraRef{L3[0].B, a.u_gate, L3[0].rank, L3[0].alpha / (float)L3[0].rank};
     lu = LoraRef{L3[1].B, a.u_up, L3[1].rank, L3[1].alpha / (float)L3[1].rank};
     ldn = LoraRef{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank};
   }
   const bool split = a.bits == 2 && a.group < SegT<2>::COLS;
-  for (int which = 0; which < 2; ++which) {
+  for (int which = 0; which < 2 && err == hipSuccess; ++which) {
     if (which == 1 && a.lora3) {
-      const int waves = a.T * a.lora3[2].rank;
-      hipLaunchKernelGGL(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, a.T, a.I, a.lora3[2].rank, 0,
-                         a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down);
+      const int wd = a.T * a.lora3[2].rank;
+      err = first_error(err, launch(k_lora_a, dim3((wd + 3) / 4), dim3(256), 0, s, a.T, a.I, a.lora3[2].rank, 0,
+                                    (const uint16_t*)a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down));
     }
     if (a.bits == 4)
-      launch_p<4, false>(s, a, gu, gd, lg, lu, ldn, which);
+      err = first_error(err, launch_p<4, false>(s, a, gu, gd, lg, lu, ldn, which));
     else if (split)
-      launch_p<2, true>(s, a, gu, gd, lg, lu, ldn, which);
+      err = first_error(err, launch_p<2, true>(s, a, gu, gd, lg, lu, ldn, which));
     else
-      launch_p<2, false>(s, a, gu, gd, lg, lu, ldn, which);
+      err = first_error(err, launch_p<2, false>(s, a, gu, gd, lg, lu, ldn, which));
   }
-  return hipGetLastError();
+  return err;
 }
 
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,
@@ -340,8 +389,7 @@ hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, co
   const size_t n = (size_t)T * d;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s, T, K, d, o, w, r, shared, y);
-  return hipGetLastError();
+  return launch(k_combine, dim3(blocks), dim3(256), 0, s, T, K, d, o, w, r, shared, y);
 }
 
 }  // namespace moe

@@ -110,18 +110,16 @@ __global__ void __launch_bounds__(64) k_topk(int T, int E, int K, uint32_t flags
       uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < TOPK_VPL; ++j) best = key[j] > best ? key[j] : best;
-      for (int m = WAVE / 2; m > 0; m >>= 1) {
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), m, WAVE);
-        const uint32_t lo = __shfl_xor((uint32_t)best, m, WAVE);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-      }
-      const int eb = (int)(0xFFFFFFFFu - (uint32_t)best);
+      // wave max of the 64-bit keys: largest order bits first, then among those lanes the
+      // largest complemented index (= the lowest expert index)
+      const uint32_t hi = wave_max_u32((uint32_t)(best >> 32));
+      const uint32_t lo = wave_max_u32((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
+      const uint64_t top = ((uint64_t)hi << 32) | lo;
 #pragma unroll
       for (int j = 0; j < TOPK_VPL; ++j)
-        if (key[j] == best) key[j] = 0;
-      sel_e[k] = eb;
-      sel_v[k] = from_order_bits((uint32_t)(best >> 32));
+        if (key[j] == top) key[j] = 0;
+      sel_e[k] = (int)(0xFFFFFFFFu - lo);
+      sel_v[k] = from_order_bits(hi);
     }
   }
   // softmax weights, float32
@@ -166,29 +164,15 @@ struct HeadArgs {
 
 __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
 
-// Sum of the rows of `rtab` ([2E][ncol] float16) selected by the K-hot vectors, column c.
-__device__ __forceinline__ float khot_gather(const uint16_t* __restrict__ rtab, int ncol, int c, int E, int K,
-                                             const int32_t* cur, const int32_t* prev, bool& bad) {
-  float s = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int e = cur[k];
-    if ((unsigned)e >= (unsigned)E) {
-      bad = true;
-      continue;
-    }
-    s += h2f(rtab[(size_t)e * ncol + c]);
-  }
-  if (prev) {
-    for (int k = 0; k < K; ++k) {
-      const int e = prev[k];
-      if ((unsigned)e >= (unsigned)E) {
-        bad = true;
-        continue;
-      }
-      s += h2f(rtab[(size_t)(E + e) * ncol + c]);
-    }
-  }
-  return s;
+// One term of the K-hot gather, spread over lanes: lane j < K reads row cur[j] of `rtab`
+// ([2E][ncol] float16), lane K <= j < 2K reads row E + prev[j - K]; other lanes give 0.  A row
+// index outside [0, E) yields NaN.
+__device__ __forceinline__ float khot_term(const uint16_t* __restrict__ rtab, int ncol, int c, int E, int K,
+                                           const int32_t* cur, const int32_t* prev, int lane) {
+  if (lane >= 2 * K || (lane >= K && !prev)) return 0.f;
+  const int e = lane < K ? cur[lane] : prev[lane - K];
+  if ((unsigned)e >= (unsigned)E) return quiet_nan();
+  return h2f(rtab[(size_t)(lane < K ? e : E + e) * ncol + c]);
 }
 
 // fc1 rows (blockIdx.x < H) and l rows (blockIdx.x >= H) against x; grid (H + E, ceil(T / tpw)).
@@ -198,28 +182,31 @@ __global__ void __launch_bounds__(64) k_head_in(HeadArgs a, int tpw) {
   const bool is_fc1 = r < a.H;
   const int c = is_fc1 ? r : r - a.H;
   const uint16_t* W = is_fc1 ? a.pw.fc1_x + (size_t)c * a.d : a.pw.lin_x + (size_t)c * a.d;
+  const uint16_t* rtab = is_fc1 ? a.pw.fc1_r : a.pw.lin_r;
+  const int ncol = is_fc1 ? a.H : a.E;
+  const uint16_t* bias = is_fc1 ? a.pw.fc1_b : a.pw.lin_b;
   const int nseg = a.d / 8;
+  const int t0 = blockIdx.y * tpw, t1 = min(a.T, t0 + tpw);
+  // the gather of the first token goes out before the row loads
+  float kh = khot_term(rtab, ncol, c, a.E, a.K, a.cur + (size_t)t0 * a.K,
+                       a.prev ? a.prev + (size_t)t0 * a.K : nullptr, lane);
   uint4 wr[NSEG];
   load_row<NSEG>(wr, W, nseg, lane);
-  const int t1 = min(a.T, (int)(blockIdx.y + 1) * tpw);
-  for (int t = blockIdx.y * tpw; t < t1; ++t) {
+  const float b = bias ? h2f(bias[c]) : 0.f;
+  for (int t = t0; t < t1; ++t) {
+    if (t > t0)
+      kh = khot_term(rtab, ncol, c, a.E, a.K, a.cur + (size_t)t * a.K, a.prev ? a.prev + (size_t)t * a.K : nullptr,
+                     lane);
     float acc, sq;
     row_dot_tokens<NSEG>(wr, nseg, a.x, a.d, t, lane, acc, sq);
+    const float g = group_sum(kh, 32);   // at most 2K <= 32 lanes hold terms
     if (lane == 0) {
       const float s = (a.flags & MOE_INPUT_RMSNORM) ? 1.f / sqrtf(sq / (float)a.d + RMS_EPS) : 1.f;
-      bool bad = false;
-      const int32_t* cur = a.cur + (size_t)t * a.K;
-      const int32_t* prev = a.prev ? a.prev + (size_t)t * a.K : nullptr;
-      if (is_fc1) {
-        float v = acc * s + khot_gather(a.pw.fc1_r, a.H, c, a.E, a.K, cur, prev, bad);
-        if (a.pw.fc1_b) v += h2f(a.pw.fc1_b[c]);
-        v = gelu_erf(v);
-        a.g[(size_t)t * a.H + c] = bad ? quiet_nan() : v;
-      } else {
-        float v = acc * s + khot_gather(a.pw.lin_r, a.E, c, a.E, a.K, cur, prev, bad);
-        if (a.pw.lin_b) v += h2f(a.pw.lin_b[c]);
-        a.lin[(size_t)t * a.E + c] = bad ? quiet_nan() : v;
-      }
+      const float v = acc * s + g + b;
+      if (is_fc1)
+        a.g[(size_t)t * a.H + c] = gelu_erf(v);
+      else
+        a.lin[(size_t)t * a.E + c] = v;
     }
   }
 }
@@ -276,19 +263,17 @@ hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags
                               const uint16_t* w, float* logits) {
   const dim3 grid(E, (T + TPW - 1) / TPW);
   switch (nseg_for(d)) {
-    case 1: hipLaunchKernelGGL(k_router<1>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
-    case 2: hipLaunchKernelGGL(k_router<2>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
-    case 4: hipLaunchKernelGGL(k_router<4>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
-    case 8: hipLaunchKernelGGL(k_router<8>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
-    default: hipLaunchKernelGGL(k_router<16>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits); break;
+    case 1: return launch(k_router<1>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
+    case 2: return launch(k_router<2>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
+    case 4: return launch(k_router<4>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
+    case 8: return launch(k_router<8>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
+    default: return launch(k_router<16>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_topk(hipStream_t s, int T, int E, int K, uint32_t flags, const float* logits, int32_t* idx,
                        float* w) {
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
-  return hipGetLastError();
+  return launch(k_topk, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
 }
 
 hipError_t launch_prerouter(hipStream_t s, int T, int d, int E, int K, uint32_t flags, const uint16_t* x,
@@ -297,21 +282,23 @@ hipError_t launch_prerouter(hipStream_t s, int T, int d, int E, int K, uint32_t 
   HeadArgs a{T, d, E, K, pw.d_hidden, flags, x, idx_cur, idx_prev, pw, ws_g, ws_lin};
   const int ty = (T + TPW - 1) / TPW;
   const dim3 g1(a.H + E, ty), g2(E, ty);
+  hipError_t e1, e2;
   switch (nseg_for(d)) {
-    case 1: hipLaunchKernelGGL(k_head_in<1>, g1, dim3(WAVE), 0, s, a, TPW); break;
-    case 2: hipLaunchKernelGGL(k_head_in<2>, g1, dim3(WAVE), 0, s, a, TPW); break;
-    case 4: hipLaunchKernelGGL(k_head_in<4>, g1, dim3(WAVE), 0, s, a, TPW); break;
-    case 8: hipLaunchKernelGGL(k_head_in<8>, g1, dim3(WAVE), 0, s, a, TPW); break;
-    default: hipLaunchKernelGGL(k_head_in<16>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 1: e1 = launch(k_head_in<1>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 2: e1 = launch(k_head_in<2>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 4: e1 = launch(k_head_in<4>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    case 8: e1 = launch(k_head_in<8>, g1, dim3(WAVE), 0, s, a, TPW); break;
+    default: e1 = launch(k_head_in<16>, g1, dim3(WAVE), 0, s, a, TPW); break;
   }
+  if (e1 != hipSuccess) return e1;
   switch (nseg_for(a.H)) {
-    case 1: hipLaunchKernelGGL(k_head_out<1>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
-    case 2: hipLaunchKernelGGL(k_head_out<2>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
-    case 4: hipLaunchKernelGGL(k_head_out<4>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
-    case 8: hipLaunchKernelGGL(k_head_out<8>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
-    default: hipLaunchKernelGGL(k_head_out<16>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 1: e2 = launch(k_head_out<1>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 2: e2 = launch(k_head_out<2>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 4: e2 = launch(k_head_out<4>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    case 8: e2 = launch(k_head_out<8>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
+    default: e2 = launch(k_head_out<16>, g2, dim3(WAVE), 0, s, a, TPW, logits); break;
   }
-  return hipGetLastError();
+  return e2;
 }
 
 }  // namespace moe

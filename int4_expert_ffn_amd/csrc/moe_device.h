@@ -18,7 +18,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace moe {
+
+// Enqueue kernel `k` and return the status of this launch alone.  (hipGetLastError would also
+// report errors other runtime users left behind, such as hipErrorNotReady from event queries.)
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                         Args&&... args) {
+  std::tuple<KArgs...> held(std::forward<Args>(args)...);
+  void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&argv](auto&... a) {
+    int i = 0;
+    ((argv[i++] = (void*)&a), ...);
+  }, held);
+  return hipLaunchKernel((const void*)k, grid, block, argv, shmem, s);
+}
+
+inline hipError_t first_error(hipError_t a, hipError_t b) { return a != hipSuccess ? a : b; }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -39,6 +58,25 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 }
 
 __device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
+
+// Unsigned max over the 64 lanes of a wave with DPP moves (no LDS round trip): prefix max inside
+// each row of 16 lanes (row_shr 1, 2, 4, 8), then row_bcast15 / row_bcast31 carry it across
+// rows; lane 63 ends with the wave max, which readlane broadcasts.  Lanes whose DPP source is
+// out of range keep their own value (the `old` operand), which is neutral for max.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t x) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xf, false);
+  return o > x ? o : x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 
 // ---------------------------------------------------------------------------------------------
 // Segment geometry per code width.
