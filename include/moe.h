@@ -147,6 +147,14 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
                              float* out, const float* w_fuse, const uint16_t* r_fuse,
                              uint16_t* y_fuse, void* workspace, size_t workspace_bytes);
 
+/* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
+   (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose
+   index lies outside [0, E); perm[T*K] (int32, out) lists flat pair indices t*K + k grouped by
+   expert, ascending inside each expert; offsets[e] is the first position of expert e.
+   Limits: 1 <= T*K <= 2^24, 1 <= E <= 1024. */
+moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx,
+                              int32_t* counts, int32_t* offsets, int32_t* perm);
+
 /* S6: y[T][d] float16 = r + sum_k w[t][k] o[t][k] (+ shared[t], weight 1), accumulated in
    float32 in ascending k, rounded to nearest even. */
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,

@@ -22,7 +22,7 @@ MOE_MAX_E, MOE_MAX_K, MOE_MAX_D = 1024, 16, 8192
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_sort_by_expert",
     "moe_status_string", "moe_version",
 )
 
@@ -71,6 +71,7 @@ def _load():
         "moe_expert_ffn_q4": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora),
                                    vp, vp, vp, vp, vp, sz]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_version": (i32, []),
     }
@@ -210,6 +211,12 @@ def moe_combine(T, K, d, o, w, r, shared, y, stream=None):
     st = _lib.moe_combine(_stream(stream, o, y), T, K, d, _ptr(o, _f32(), "o"), _ptr(w, _f32(), "w"),
                           _ptr(r, _f16(), "r"), _ptr(shared, _f32(), "shared"), _ptr(y, _f16(), "y"))
     _check(st, "moe_combine")
+
+
+def moe_sort_by_expert(T, K, E, idx, counts, offsets, perm, stream=None):
+    st = _lib.moe_sort_by_expert(_stream(stream, idx), T, K, E, _ptr(idx, _i32(), "idx"), _ptr(counts, _i32(), "counts"),
+                                 _ptr(offsets, _i32(), "offsets"), _ptr(perm, _i32(), "perm"))
+    _check(st, "moe_sort_by_expert")
 
 
 def moe_version() -> int:

@@ -1,6 +1,8 @@
 """Build libmoe.so (the HIP library behind include/moe.h) in-tree with hipcc for gfx950.
 
-    python -m int4_expert_ffn_amd.build        (or import and call build())
+    python int4_expert_ffn_amd/build.py
+
+Run it by path (or through __graft_entry__.build()): importing the package loads the library.
 """
 import glob
 import os

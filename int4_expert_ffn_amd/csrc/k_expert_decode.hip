@@ -347,6 +347,11 @@ hipError_t launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const 
 
 }  // namespace
 
+hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,
+                         size_t v_stride, const uint16_t* A, float* u) {
+  return launch(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, T, n_in, rank, rmsnorm, v, v_stride, A, u);
+}
+
 bool decode_shape_supported(int bits, int group, int d, int I) {
   return row_geo(bits, d).ok && row_geo(bits, I).ok && group >= 32;
 }

@@ -166,16 +166,25 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
     g.base = a;
     char* gb = base + ws.grouped;
     const size_t o_counts = 0;
-    const size_t o_offsets = o_counts + align_up((size_t)ex->n_experts * sizeof(int32_t));
-    const size_t o_perm = o_offsets + align_up((size_t)(ex->n_experts + 1) * sizeof(int32_t));
-    const size_t o_osorted = o_perm + align_up((size_t)T * K * sizeof(int32_t));
+    const size_t o_offsets = o_counts + align_up((size_t)(ex->n_experts + 1) * sizeof(int32_t));
+    const size_t o_perm = o_offsets + align_up((size_t)(ex->n_experts + 2) * sizeof(int32_t));
+    const size_t o_rowscale = o_perm + align_up((size_t)T * K * sizeof(int32_t));
+    const size_t o_osorted = o_rowscale + align_up((size_t)T * sizeof(float));
     g.counts = (int32_t*)(gb + o_counts);
     g.offsets = (int32_t*)(gb + o_offsets);
     g.perm = (int32_t*)(gb + o_perm);
+    g.rowscale = (float*)(gb + o_rowscale);
     g.o_sorted = (float*)(gb + o_osorted);
     return from_hip(launch_expert_grouped(s, g));
   }
   return from_hip(launch_expert_decode(s, a));
+}
+
+moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,
+                              int32_t* offsets, int32_t* perm) {
+  if (T < 1 || K < 1 || E < 1 || E > MOE_MAX_E || (int64_t)T * K > (1 << 24)) return MOE_ERR_INVALID_ARG;
+  if (!idx || !counts || !offsets || !perm) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_sort((hipStream_t)stream, T * K, E, idx, counts, offsets, perm));
 }
 
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,

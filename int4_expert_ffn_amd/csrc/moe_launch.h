@@ -40,16 +40,22 @@ struct DecodeArgs {
 };
 hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a);
 bool decode_shape_supported(int bits, int group, int d, int I);
+// u[t][r] = s_t * A[r] . v_t for `waves` = T * rank waves (s_t = RMS-norm factor when rmsnorm)
+hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,
+                         size_t v_stride, const uint16_t* A, float* u);
 
 // batched (grouped GEMM) expert FFN ------------------------------------------------------------
 struct GroupedArgs {
-  DecodeArgs base;
-  int32_t* counts;    // workspace [E]
-  int32_t* offsets;   // workspace [E+1]
+  DecodeArgs base;    // base.act holds the expert-sorted activations [T*K][I]
+  int32_t* counts;    // workspace [E+1] (bucket E: indices outside [0, E))
+  int32_t* offsets;   // workspace [E+2]
   int32_t* perm;      // workspace [T*K]
+  float* rowscale;    // workspace [T]
   float* o_sorted;    // workspace [T*K][d] float32 (used when out == nullptr)
 };
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& a);
+hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm);
 size_t grouped_workspace_extra(int T, int K, int E, int d);
 
 // combine -------------------------------------------------------------------------------------

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -95,6 +95,11 @@ def test_prerouter_and_combine_reject():
     assert p(1, 2048, 256, 4, 0, FAKE, FAKE, None, ctypes.byref(pw0), FAKE, FAKE, 1 << 30) == INVALID  # H % 8
     pw1 = lib_mod.moe_prerouter_w(1024, FAKE, None, None, FAKE, None, FAKE, FAKE, None)
     assert p(1, 2048, 256, 4, 0, FAKE, FAKE, None, ctypes.byref(pw1), FAKE, FAKE, 1 << 30) == INVALID  # fc1_r
+    so = lambda *a: L.moe_sort_by_expert(None, *a)
+    assert so(0, 4, 256, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert so(1, 4, 2000, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert so(1 << 22, 16, 256, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert so(4, 4, 256, FAKE, None, FAKE, FAKE) == INVALID
     c = lambda *a: L.moe_combine(None, *a)
     assert c(0, 4, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
     assert c(1, 17, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
