@@ -156,10 +156,11 @@ def _shared(M, cfg, syn, layer=0):
     se = syn.shared_expert_id()
     mats = [syn.expert_mat(layer, [se], m, DEV) for m in S.MATS]
     ex = M.Experts(*mats, cfg.bits, cfg.group)
-    cpu = tuple(tuple(a[0].cpu().numpy() for a in m) for m in mats)
+    cpu = tuple(tuple(a[0].numpy() for a in syn.expert_mat(layer, [se], m, "cpu")) for m in S.MATS)
     lw = syn.lora(layer, DEV)
     lora = M.Lora3([lw[m] for m in S.MATS], cfg.lora_alpha)
-    lora_cpu = {m: (lw[m][0].cpu().numpy(), lw[m][1].cpu().numpy()) for m in S.MATS}
+    lw_cpu = syn.lora(layer, "cpu")      # the oracle's copy, drawn on the host
+    lora_cpu = {m: (lw_cpu[m][0].numpy(), lw_cpu[m][1].numpy()) for m in S.MATS}
     lora_cpu["alpha"] = cfg.lora_alpha
     return ex, cpu, lora, lora_cpu, lw
 

@@ -193,7 +193,7 @@ def test_prerouter_head(M):
     syn = S.Synth(cfg)
     T, E, K = 4, cfg.E, cfg.K
     hw = syn.head(0, DEV)
-    hc = {k: v.cpu().numpy() for k, v in hw.items()}
+    hc = {k: v.numpy() for k, v in syn.head(0, "cpu").items()}
     pw = M.PrerouterWeights(hw)
     h = syn.hidden(42, T)
     cur, _ = O.route_topk(syn.logits(1, T).numpy(), K)
@@ -234,8 +234,8 @@ def test_prerouted_chain(M):
         if l < cfg.L - 1:
             hw = syn.head(l, DEV)
             head = M.PrerouterWeights(hw)
-            heads_cpu.append({k: v.cpu().numpy() for k, v in hw.items()})
-        routers_cpu.append(router.cpu().numpy())
+            heads_cpu.append({k: v.numpy() for k, v in syn.head(l, "cpu").items()})
+        routers_cpu.append(syn.router(l, "cpu").numpy())
         layers.append(LayerWeights(ex, router, head))
     stack = DecodeStack(layers, cfg.K, DEV)
     caches = [ExpertCache(syn, l) for l in range(cfg.L)]
