@@ -160,6 +160,53 @@ moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, con
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,
                        const uint16_t* r, const float* shared, uint16_t* y);
 
+/* ---------------------------------------------------------------------------------------------
+   Whole-token decode of a resident prerouted stack in one persistent kernel.
+
+   One call runs token `token` through all L layers with the per-layer semantics of the calls
+   above (MOE_INPUT_RMSNORM on every layer input, the residual is the un-normalised input):
+     - layer 0, every layer whose predecessor has no head, and every layer at token 0 run their
+       own router + top-K;
+     - any other layer uses the experts and weights the head of the layer before it predicted
+       at the previous token (the prediction is the routing: Edge0 reading guide, section
+       "Ideas clave"); the head of layer l reads its layer input with the K-hot routing of layer
+       l at this token and at the previous one (none at token 0) and writes layer l+1's routing
+       for the next token ("Arquitectura del cabezal Prerouter").
+   Routing state lives in route_idx / route_w [3][L][K], slot token % 3 (this token), slot
+   (token + 2) % 3 (previous token), slot (token + 1) % 3 (written: next token).  Tokens must be
+   issued in order 0, 1, 2, ...; a graph captured for token t replays correctly for any t' >= 1
+   with t' % 3 == t % 3.
+
+   One workgroup per compute unit stays resident for the whole token; workgroups hand vectors to
+   each other through tagged words in the workspace.  The workspace must be zeroed once before
+   the first call and then passed unchanged to every later call of the same stack; calls on one
+   workspace must not overlap.  Its first 4 bytes hold a token counter, the next 4 an error
+   word: nonzero means a wait inside the kernel exceeded its bound and that call's outputs are
+   invalid (check it after synchronising when in doubt).
+   Supported shapes: d_model 2048 or 4096 with d_model*bits/128 a multiple of 64 (at most 128),
+   d_ff*bits/128 <= 64, K <= 8, K*d_ff <= 4096, E <= 4 * compute units, head width H a multiple
+   of 512 up to 2048 (or no heads), 2-bit only with group >= 64; others return
+   MOE_ERR_UNSUPPORTED (use the per-layer calls).  Device-side descriptors must match `st`. */
+typedef struct {
+  moe_experts experts;   /* this layer's routed experts (E, d_model, d_ff, bits, group as in the stack) */
+  const uint16_t* router; /* [E][d]: needed by self-routed layers (layer 0, token 0, no predecessor head) */
+  moe_prerouter_w head;  /* head predicting layer l+1 (d_hidden == stack d_hidden); fc1_x == NULL: none */
+} moe_decode_layer;
+
+typedef struct {
+  int32_t L, E, K, d_model, d_ff, bits, group, d_hidden; /* d_hidden 0 when no layer has a head */
+  const moe_decode_layer* layers; /* DEVICE array of L descriptors */
+  int32_t* route_idx;             /* DEVICE [3][L][K] */
+  float* route_w;                 /* DEVICE [3][L][K] */
+} moe_decode_stack;
+
+size_t moe_decode_workspace_size(const moe_decode_stack* st);
+
+/* h_in[d] float16 (device): the token's input hidden state; h_out[d] float16 (device): the output
+   of layer L-1.  flags: MOE_TOPK_RENORM or 0 (applies to every top-K). */
+moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
+                           const uint16_t* h_in, uint16_t* h_out, void* workspace, size_t workspace_bytes);
+
 const char* moe_status_string(moe_status s);
 
 /* Library version (major*10000 + minor*100 + patch). */

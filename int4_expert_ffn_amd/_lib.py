@@ -23,7 +23,7 @@ MOE_MAX_E, MOE_MAX_K, MOE_MAX_D = 1024, 16, 8192
 EXPORTS = (
     "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_sort_by_expert",
-    "moe_status_string", "moe_version",
+    "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
 )
 
 
@@ -54,6 +54,17 @@ class moe_prerouter_w(ctypes.Structure):
                 ("lin_x", ctypes.c_void_p), ("lin_r", ctypes.c_void_p), ("lin_b", ctypes.c_void_p)]
 
 
+class moe_decode_layer(ctypes.Structure):
+    _fields_ = [("experts", moe_experts), ("router", ctypes.c_void_p), ("head", moe_prerouter_w)]
+
+
+class moe_decode_stack(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("d_hidden", ctypes.c_int32), ("layers", ctypes.c_void_p), ("route_idx", ctypes.c_void_p),
+                ("route_w", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m int4_expert_ffn_amd.build`")
@@ -73,6 +84,8 @@ def _load():
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [st]),
+        "moe_decode_workspace_size": (sz, [ctypes.POINTER(moe_decode_stack)]),
+        "moe_decode_step": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, sz]),
         "moe_version": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -217,6 +230,18 @@ def moe_sort_by_expert(T, K, E, idx, counts, offsets, perm, stream=None):
     st = _lib.moe_sort_by_expert(_stream(stream, idx), T, K, E, _ptr(idx, _i32(), "idx"), _ptr(counts, _i32(), "counts"),
                                  _ptr(offsets, _i32(), "offsets"), _ptr(perm, _i32(), "perm"))
     _check(st, "moe_sort_by_expert")
+
+
+def moe_decode_workspace_size(stack: "moe_decode_stack") -> int:
+    return _lib.moe_decode_workspace_size(ctypes.byref(stack))
+
+
+def moe_decode_step(stack: "moe_decode_stack", token, flags, h_in, h_out, workspace, workspace_bytes=None,
+                    stream=None):
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_decode_step(_stream(stream, h_in, h_out), ctypes.byref(stack), token, flags, _ptr(h_in, _f16(), "h_in"),
+                              _ptr(h_out, _f16(), "h_out"), _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_decode_step")
 
 
 def moe_version() -> int:

@@ -14,6 +14,10 @@ the un-normalised float16 hidden state.
 
 Routing buffers rotate over three token slots, so the head writing token t+1's routing never
 overwrites what token t still reads (slot t%3) or the previous-token vector (slot (t-1)%3).
+
+Two ways to run a token: `token()` issues the per-layer C-ABI calls (5 launches per layer);
+`step()` issues one moe_decode_step launch, the persistent kernel that runs the same schedule
+with all layers in one kernel.  Both share the routing state, so they can be mixed token by token.
 """
 from __future__ import annotations
 
@@ -52,6 +56,43 @@ class DecodeStack:
         head_ws = L.moe_prerouter_workspace_size(1, E, H)
         self.ffn_ws = torch.empty(ffn_ws, dtype=torch.uint8, device=dev)
         self.head_ws = torch.empty(head_ws, dtype=torch.uint8, device=dev)
+        self._step = None
+
+    # ------------------------------------------------------------------ persistent whole-token kernel
+    def _step_state(self):
+        """Device array of layer descriptors, the stack descriptor and the zeroed step workspace."""
+        if self._step is None:
+            import ctypes
+            L_ = self.L
+            arr = (L.moe_decode_layer * L_)()
+            H = 0
+            for l, lw in enumerate(self.layers):
+                arr[l].experts = lw.experts.desc
+                arr[l].router = lw.router.data_ptr()
+                if lw.head is not None and l + 1 < L_:
+                    arr[l].head = lw.head.desc
+                    H = lw.head.H
+            raw = bytes(arr)
+            desc = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+            ex0 = self.layers[0].experts
+            st = L.moe_decode_stack(L_, self.E, self.K, self.d, ex0.I, ex0.bits, ex0.group, H, desc.data_ptr(),
+                                    self.route_idx.data_ptr(), self.route_w.data_ptr())
+            ws = torch.zeros(L.moe_decode_workspace_size(st), dtype=torch.uint8, device=self.device)
+            self._step = (desc, st, ws)
+        return self._step
+
+    def step(self, t: int, h_in: torch.Tensor, h_out: Optional[torch.Tensor] = None):
+        """Enqueue token t as one persistent-kernel launch reading h_in [d] and writing h_out
+        (default: self.h[L]).  Returns h_out."""
+        desc, st, ws = self._step_state()
+        out = self.h[self.L] if h_out is None else h_out
+        L.moe_decode_step(st, t, self.topk_flags, h_in, out, ws)
+        return out
+
+    def step_error_word(self) -> int:
+        """Nonzero if a wait inside a persistent-kernel step exceeded its bound (read after sync)."""
+        _, _, ws = self._step_state()
+        return int(ws[4:8].view(torch.int32).item())
 
     def token(self, t: int, h_in: Optional[torch.Tensor] = None, record_routing: bool = False):
         """Enqueue token t.  h_in [d] float16 is copied into the stack input unless None (then the

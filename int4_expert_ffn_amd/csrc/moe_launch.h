@@ -58,6 +58,12 @@ hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t
                        int32_t* perm);
 size_t grouped_workspace_extra(int T, int K, int E, int d);
 
+// whole-token persistent decode -----------------------------------------------------------------
+bool decode_step_supported(const moe_decode_stack& st);
+size_t decode_step_workspace(const moe_decode_stack& st);
+hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
+                              const uint16_t* h_in, uint16_t* h_out, void* ws);
+
 // combine -------------------------------------------------------------------------------------
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,
                           const uint16_t* r, const float* shared, uint16_t* y);

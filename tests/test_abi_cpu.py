@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -100,6 +100,20 @@ def test_prerouter_and_combine_reject():
     assert so(1, 4, 2000, FAKE, FAKE, FAKE, FAKE) == INVALID
     assert so(1 << 22, 16, 256, FAKE, FAKE, FAKE, FAKE) == INVALID
     assert so(4, 4, 256, FAKE, None, FAKE, FAKE) == INVALID
+    st = lib_mod.moe_decode_stack(40, 256, 4, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
+    ds = lambda stk, tok=1, flags=1, ws=FAKE, wsb=1 << 40: L.moe_decode_step(None, ctypes.byref(stk), tok, flags, FAKE,
+                                                                           FAKE, ws, wsb)
+    assert ds(st, tok=-1) == INVALID
+    assert ds(st, flags=2) == INVALID
+    assert ds(st, wsb=64) == INVALID
+    assert ds(st, ws=FAKE + 16) == INVALID
+    bad = lib_mod.moe_decode_stack(40, 256, 9, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
+    assert ds(bad) == UNSUP                     # K > 8 is not a persistent-kernel shape
+    tiny = lib_mod.moe_decode_stack(1, 16, 2, 256, 128, 4, 32, 0, FAKE, FAKE, FAKE)
+    assert ds(tiny) == UNSUP                    # d_model 256: per-layer calls only
+    nolayers = lib_mod.moe_decode_stack(40, 256, 4, 2048, 512, 4, 64, 1024, None, FAKE, FAKE)
+    assert ds(nolayers) == INVALID
+    assert L.moe_decode_workspace_size(ctypes.byref(st)) > 40 * 1024 * 8
     c = lambda *a: L.moe_combine(None, *a)
     assert c(0, 4, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
     assert c(1, 17, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
