@@ -5,11 +5,13 @@ Workload (one step = one token through the whole stack): the 35B-shaped decode l
 d_model 2048, 256 experts, top-4, expert intermediate 512, int4 affine group 64, 40 layers
 resident in HBM, prerouter heads (fc1 2560->1024, erf-GELU, fc2 1024->256, linear 2560->256) on
 layers 0..38, layer 0 routed by its own router -- batch 1, synthetic seeded weights and hidden
-states (a fresh draw per token).  Each token is one HIP-graph replay of every C-ABI call of the 40
-layers; inputs are resident in HBM before the timed region.
+states (a fresh draw per token).  Each token is one HIP-graph replay holding one moe_decode_step
+launch (the persistent kernel that runs all 40 layers); inputs are resident in HBM before the
+timed region.  The same schedule issued as per-layer C-ABI calls is timed beside it for context.
 
-Prints one JSON line: tokens/s, the roofline of the dominant step (the expert FFN of one layer,
-timed with HIP events on its own stream) and the CPU oracle timed on a bounded sample.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (k_decode_step, timed with
+HIP events on its stream: algorithmic bytes per token / time per token) and the CPU oracle timed
+on a bounded sample.
 """
 import argparse
 import json
@@ -115,81 +117,76 @@ def main():
     log(f"stack resident: {cfg.L} layers, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.1f} s")
 
     from int4_expert_ffn_amd.chain import DecodeStack
-    stack = DecodeStack(layers, cfg.K, dev)
     n_pool = 3 * 64
     pool = syn.hidden(7, n_pool, dev)
     ring = torch.empty((3, cfg.d), dtype=torch.float16, device=dev)
-
     stream = torch.cuda.Stream(device=dev)
-    with torch.cuda.stream(stream):
-        stack.token(0, pool[0])                 # bootstrap token: every layer routes itself
-        ring.copy_(pool[0:3])
-    stream.synchronize()
-    graphs = []
-    for j in range(3):                          # tokens 1, 2, 3 -> routing slots 1, 2, 0
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            stack.token(j + 1, ring[(j + 1) % 3])
-        graphs.append(g)
-    torch.cuda.synchronize()
 
-    def run(n, start):
+    def capture(stack, use_step):
+        """Three graphs, one per routing slot (tokens 1, 2, 3), each reading its ring slot."""
+        with torch.cuda.stream(stream):
+            if use_step:
+                stack.step(0, pool[0])          # token 0: every layer routes itself
+            else:
+                stack.token(0, pool[0])
+            ring.copy_(pool[0:3])
+        stream.synchronize()
+        graphs = []
+        for j in range(3):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                if use_step:
+                    stack.step(j + 1, ring[(j + 1) % 3])
+                else:
+                    stack.token(j + 1, ring[(j + 1) % 3])
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def run(graphs, n, start):
         for i in range(n):
             t = start + i
-            slot = t % 3
-            if slot == 1:                       # refill the three inputs of tokens t, t+1, t+2
+            if t % 3 == 1:                       # refill the inputs of tokens t, t+1, t+2
                 p = (t // 3 * 3) % n_pool
                 ring.copy_(pool[p:p + 3])
             graphs[(t - 1) % 3].replay()
 
-    args.warmup = -(-args.warmup // 3) * 3      # whole routing-slot rotations keep tokens consecutive
-    with torch.cuda.stream(stream):
-        run(args.warmup, 1)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start = 1 + args.warmup
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        ev0.record(stream)
-        run(args.steps, start)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        w1 = time.perf_counter()
-    wall = w1 - w0
-    ev_ms = ev0.elapsed_time(ev1)
-    tok_s = args.steps / wall
-    total_bytes, ffn_bytes = algorithmic_bytes(cfg)
-    h_out = stack.h[cfg.L].float()
-    assert torch.isfinite(h_out).all(), "non-finite decode output"
-
-    # dominant step: the expert FFN of one layer (gate/up + SwiGLU kernel, down + combine kernel),
-    # timed with HIP events on its stream over graph replays of all 40 layers' FFN calls.  Three
-    # graphs use the three routing sets left by the decode run (480 distinct experts, 850 MB), so
-    # the 256 MB last-level cache cannot hold a replay's weights.
-    ffn_graphs = []
-    fixed = [(stack.route_idx[s].clone(), stack.route_w[s].clone()) for s in range(3)]
-    for idx_fixed, w_fixed in fixed:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for l, lw in enumerate(layers):
-                x = stack.h[l]
-                M.moe_expert_ffn_q4(1, cfg.K, M.MOE_INPUT_RMSNORM, x, idx_fixed[l], lw.experts, None, None,
-                                    w_fixed[l], x, stack.h[l + 1], stack.ffn_ws)
-        ffn_graphs.append(g)
-    reps = 60
-    with torch.cuda.stream(stream):
-        for g in ffn_graphs:
-            g.replay()
+    def timed(graphs, steps, warmup):
+        warmup = -(-warmup // 3) * 3             # whole slot rotations keep tokens consecutive
+        with torch.cuda.stream(stream):
+            run(graphs, warmup, 1)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            ffn_graphs[i % 3].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ffn_us = e0.elapsed_time(e1) * 1e3 / (reps * cfg.L)
-    achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            e0.record(stream)
+            run(graphs, steps, 1 + warmup)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            w1 = time.perf_counter()
+        return w1 - w0, e0.elapsed_time(e1), warmup
+
+    # the timed step: one persistent-kernel launch (moe_decode_step) per token
+    stack = DecodeStack(layers, cfg.K, dev)
+    graphs = capture(stack, True)
+    wall, ev_ms, args.warmup = timed(graphs, args.steps, args.warmup)
+    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
+    h_out = stack.h[cfg.L].float()
+    assert torch.isfinite(h_out).all(), "non-finite decode output"
+    tok_s = args.steps / wall
+    total_bytes, ffn_bytes = algorithmic_bytes(cfg)
+    step_us = ev_ms * 1e3 / args.steps                 # HIP-event time per token on the stream
+    achieved = total_bytes / (step_us * 1e-6) / 1e9
+
+    # context: the same schedule as per-layer C-ABI calls (5 launches per layer)
+    del graphs
+    stack2 = DecodeStack(layers, cfg.K, dev)
+    graphs2 = capture(stack2, False)
+    n2 = max(30, args.steps // 4)
+    wall2, ev2, _ = timed(graphs2, n2, 30)
+    per_layer_tok_s = n2 / wall2
+    del graphs2
 
     rec = {
         "metric": "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)",
@@ -214,19 +211,20 @@ def main():
             "algorithmic_bytes_per_token": total_bytes,
             "achieved_GBps": round(total_bytes * tok_s / 1e9, 1),
             "frac_of_peak": round(total_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
-            "event_ms_per_step": round(ev_ms / args.steps, 4),
         },
         "roofline": {
-            "kernel": "expert FFN of one layer (k_gateup + k_down)",
+            "kernel": "k_decode_step (moe_decode_step: all 40 layers of one token in one launch)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None,
-            "bytes_per_launch": ffn_bytes,
-            "avg_us": round(ffn_us, 3),
+            "bytes_per_launch": total_bytes,
+            "avg_us": round(step_us, 2),
         },
+        "per_layer_calls": {"tokens_per_s": round(per_layer_tok_s, 2), "launches_per_token": 5 * cfg.L - 2,
+                            "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

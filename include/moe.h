@@ -184,7 +184,7 @@ moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const floa
    word: nonzero means a wait inside the kernel exceeded its bound and that call's outputs are
    invalid (check it after synchronising when in doubt).
    Supported shapes: d_model 2048 or 4096 with d_model*bits/128 a multiple of 64 (at most 128),
-   d_ff*bits/128 <= 64, K <= 8, K*d_ff <= 4096, E <= 4 * compute units, head width H a multiple
+   d_ff*bits/128 <= 64, K <= 8, K*d_ff <= 4096, L*K <= 512, E <= 4 * compute units, head width H a multiple
    of 512 up to 2048 (or no heads), 2-bit only with group >= 64; others return
    MOE_ERR_UNSUPPORTED (use the per-layer calls).  Device-side descriptors must match `st`. */
 typedef struct {

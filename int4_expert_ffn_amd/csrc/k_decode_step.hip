@@ -10,6 +10,7 @@
 //   * Work is split statically: every workgroup owns a slice of the gate/up row pairs, of the
 //     head's fc1 / linear rows, of the down rows (all K experts of a row live in one workgroup,
 //     so the weighted combine stays local and in fixed order) and of the fc2 rows.
+//   * The SwiGLU output travels in float32 and meets the down weights as a float16 hi + lo pair.
 //   * Data moves between workgroups as tagged 8-byte words (32-bit payload, 32-bit tag naming
 //     the token epoch and the phase), written and read with agent-scope relaxed atomics; a
 //     reader polls until every tag matches, so no flag/data ordering is needed.
@@ -17,7 +18,9 @@
 //     LDS); waves 1..4 compute.  Their weight loads for a phase are issued one phase early, and
 //     workgroup barriers fence LDS only, so those loads stay in flight while the phase waits.
 //   * The heads (off the critical path: their output routes the next token) ride in the same
-//     phases; the top-K of head l runs in one workgroup during layer l+1.
+//     phases; their top-Ks run after the last layer, spread over the workgroups.
+//   * The whole token's routing state is staged in LDS at the start, so issuing a phase's weight
+//     loads never waits on a global read of the expert indices.
 //
 // Phases per layer l: [R_l: own router + top-K, only for layer 0, layers with no prediction and
 // the first token] -> A_l: gate/up + SwiGLU, head fc1 (+GELU) and linear rows -> B_l: down +
@@ -34,7 +37,7 @@ constexpr int NTHREADS = (MW + 1) * WAVE;
 constexpr int GU_MAX = 4;                    // gate/up row pairs per compute wave
 constexpr int NH_MAX = 2;                    // head fc1/linear rows per compute wave
 constexpr int PD_MAX = 8;                    // (expert, row-group) down items per compute wave
-constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART = 512;
+constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART = 512, LDS_LK = 512;
 constexpr int POLL_MAX = 16;                 // words per lane per polling pass (1024 per wave)
 constexpr uint32_t TAG_SALT = 0x5A5A5A5Au;
 constexpr uint64_t WAIT_TICKS = 20000000;       // 0.2 s of the 100 MHz real-time counter
@@ -288,14 +291,15 @@ __device__ __forceinline__ void issue_B(const StepParams& p, int l, const int* r
 
 struct StepShared {
   uint16_t h[2][LDS_D];
-  uint16_t act[LDS_ACT];
+  float act[LDS_ACT];
   float g[LDS_H];
   float lin[LDS_E];
   float logit[LDS_E];
   float part[LDS_PART];
   float scale[2];
-  int route_e[2][8];    // routing of layer l in slot l & 1 (experts, weights)
-  float route_w[2][8];
+  int route_e[LDS_LK];  // this token's routing of every layer: [l * K + k]
+  float route_w[LDS_LK];
+  int prev_e[LDS_LK];   // the previous token's routing (K-hot "previous" input of the heads)
 };
 
 struct StepCtx {
@@ -333,18 +337,6 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     }
     sq = wave_sum(sq);
     if (lane == 0) sm.scale[hb] = 1.f / sqrtf(sq / (float)p.d + RMS_EPS);
-    // top-K of head l-1: layer l's routing for the next token (one workgroup per head)
-    if (l >= 1 && has_head(p, l - 1) && c.wg == (l - 1) % p.G) {
-      ll_wait(p.ll_hlog + (size_t)(l - 1) * p.E, p.E, c.tag(3 * (l - 1) + 2), p.err, failed,
-              [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
-      int e;
-      float w;
-      wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
-      if (lane < p.K) {
-        c.nxt_i[l * p.K + lane] = e;
-        c.nxt_w[l * p.K + lane] = w;
-      }
-    }
     lds_barrier();  // B1: h_l ready
     if (self_routed(p, l)) {
       ll_wait(p.ll_logits, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
@@ -352,8 +344,8 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       float w;
       wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
       if (lane < p.K) {
-        sm.route_e[l & 1][lane] = e;
-        sm.route_w[l & 1][lane] = w;
+        sm.route_e[l * p.K + lane] = e;
+        sm.route_w[l * p.K + lane] = w;
         if (c.wg == 0) {
           c.cur_i[l * p.K + lane] = e;
           c.cur_w[l * p.K + lane] = w;
@@ -362,14 +354,27 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       lds_barrier();  // B2: routing of layer l ready
     }
     const uint32_t tA = c.tag(3 * l + 1);
-    uint32_t* aw = reinterpret_cast<uint32_t*>(sm.act);
-    ll_wait(p.ll_act, p.K * p.I / 2, tA, p.err, failed, [&](int i, uint32_t v) { aw[i] = v; });
+    ll_wait(p.ll_act, p.K * p.I, tA, p.err, failed, [&](int i, uint32_t v) { sm.act[i] = __uint_as_float(v); });
     if (has_head(p, l)) {
       ll_wait(p.ll_g, p.H, tA, p.err, failed, [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
       ll_wait(p.ll_lin, p.E, tA, p.err, failed, [&](int i, uint32_t v) { sm.lin[i] = __uint_as_float(v); });
     }
     lds_barrier();  // B3: act (and head fc1 / linear outputs) ready
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
+  }
+  // Top-K of every head, off the token's critical path: head l predicts layer l+1's routing for
+  // the next token; workgroup l % G handles head l.
+  for (int l = c.wg; l + 1 < p.L; l += p.G) {
+    if (!has_head(p, l)) continue;
+    ll_wait(p.ll_hlog + (size_t)l * p.E, p.E, c.tag(3 * l + 2), p.err, failed,
+            [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
+    int e;
+    float w;
+    wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
+    if (lane < p.K) {
+      c.nxt_i[(l + 1) * p.K + lane] = e;
+      c.nxt_w[(l + 1) * p.K + lane] = w;
+    }
   }
 }
 
@@ -385,13 +390,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     const bool self = self_routed(p, l);
     const bool head = has_head(p, l);
     const int hb = l & 1;
-    const int* prev_l = c.prev_i ? c.prev_i + l * p.K : nullptr;
-    if (l == 0 && !self) {  // (layer 0 always routes itself; kept so the slot rule holds for any l)
-      if (cw == 0 && lane < p.K) {
-        sm.route_e[0][lane] = c.cur_i[lane];
-        sm.route_w[0][lane] = c.cur_w[lane];
-      }
-    }
+    const int* prev_l = c.prev_i ? sm.prev_e + l * p.K : nullptr;
     lds_barrier();  // B1
     const float scale = sm.scale[hb];
     const uint16_t* hl = sm.h[hb];
@@ -414,8 +413,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         if (lane == 0) ll_store(p.ll_logits + r, __float_as_uint(acc), c.tag(3 * l));
       }
       lds_barrier();  // B2
-      issue_A<BITS, PG, NSH, GUM>(p, l, sm.route_e[l & 1], prev_l, gw, lane, A);
-      issue_B<BITS, NSF, PDM>(p, l, sm.route_e[l & 1], wg, cw, lane, B);
+      issue_A<BITS, PG, NSH, GUM>(p, l, sm.route_e + l * p.K, prev_l, gw, lane, A);
+      issue_B<BITS, NSF, PDM>(p, l, sm.route_e + l * p.K, wg, cw, lane, B);
     }
 
     // ---- A_l: gate/up + SwiGLU, head fc1 (+GELU) and linear rows ----
@@ -425,7 +424,6 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       float sx[PG][2], sq = 0.f;
 #pragma unroll
       for (int q = 0; q < PG; ++q) load_xpairs<BITS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
-      uint32_t packed = 0;
 #pragma unroll
       for (int u = 0; u < GUM; ++u) {
         const int item = gw * p.GU + u;
@@ -444,13 +442,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           pu = wave_sum(pu) * scale;
           float a = pg / (1.f + expf(-pg)) * pu;
           if (A.bad[u]) a = quiet_nan();
-          const uint32_t hbits = f2h(a);
-          if ((item & 1) == 0) {
-            packed = hbits;
-          } else {
-            packed |= hbits << 16;
-            if (lane == 0) ll_store(p.ll_act + item / 2, packed, tA);
-          }
+          if (lane == 0) ll_store(p.ll_act + item, __float_as_uint(a), tA);
         }
       }
       if (head) {
@@ -484,8 +476,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       }
     }
     if (l + 1 < p.L && !self_routed(p, l + 1))  // weights of A_{l+1}, one phase early
-      issue_A<BITS, PG, NSH, GUM>(p, l + 1, c.cur_i + (l + 1) * p.K,
-                                  c.prev_i ? c.prev_i + (l + 1) * p.K : nullptr, gw, lane, A);
+      issue_A<BITS, PG, NSH, GUM>(p, l + 1, sm.route_e + (l + 1) * p.K,
+                                  c.prev_i ? sm.prev_e + (l + 1) * p.K : nullptr, gw, lane, A);
     lds_barrier();  // B3
 
     // ---- B_l: down partials of this workgroup's rows, head fc2 rows ----
@@ -499,11 +491,11 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           const int k = B.k[u], q = pk - k * p.DI;
           float po = 0.f;
           if (ls < S) {
-            uint32_t xp[GS::PAIRS];
-            float sx[2], sq = 0.f;
-            load_xpairs<BITS>(sm.act + (size_t)k * p.I + (size_t)ls * GS::COLS, xp, sx, sq);
+            uint32_t xh[GS::PAIRS], xl[GS::PAIRS];
+            float sx[2];
+            load_xpairs_f32<BITS>(sm.act + (size_t)k * p.I + (size_t)ls * GS::COLS, xh, xl, sx);
             float d0 = 0.f, d1 = 0.f;
-            dot_segment<BITS>(B.q[u], xp, d0, d1);
+            dot_segment_split<BITS>(B.q[u], xh, xl, d0, d1);
             po = h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * (sx[0] + sx[1]);
           }
           po = group_sum_last(po, p.Ldn);
@@ -536,13 +528,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         }
       }
     }
-    if (l + 1 < p.L && !self_routed(p, l + 1)) {  // weights of B_{l+1}, one phase early
-      issue_B<BITS, NSF, PDM>(p, l + 1, c.cur_i + (l + 1) * p.K, wg, cw, lane, B);
-      if (cw == 0 && lane < p.K) {  // its combine weights, read after the next barriers
-        sm.route_e[(l + 1) & 1][lane] = c.cur_i[(l + 1) * p.K + lane];
-        sm.route_w[(l + 1) & 1][lane] = c.cur_w[(l + 1) * p.K + lane];
-      }
-    }
+    if (l + 1 < p.L && !self_routed(p, l + 1))  // weights of B_{l+1}, one phase early
+      issue_B<BITS, NSF, PDM>(p, l + 1, sm.route_e + (l + 1) * p.K, wg, cw, lane, B);
     lds_barrier();  // B4
     // ---- combine + residual of this workgroup's rows -> h_{l+1} ----
     if (cw == 0) {
@@ -550,7 +537,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       float y = 0.f;
       if (jr < p.DR && j < p.d) {
         float acc = 0.f;
-        for (int k = 0; k < p.K; ++k) acc = fmaf(sm.route_w[hb][k], sm.part[k * p.DR + jr], acc);
+        for (int k = 0; k < p.K; ++k) acc = fmaf(sm.route_w[l * p.K + k], sm.part[k * p.DR + jr], acc);
         y = h2f(hl[j]) + acc;
       }
       const uint32_t yb = f2h(y);
@@ -581,6 +568,13 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   c.prev_i = p.bootstrap ? nullptr : p.ridx + (size_t)((p.slot + 2) % 3) * LK;
   c.nxt_i = p.ridx + (size_t)((p.slot + 1) % 3) * LK;
   c.nxt_w = p.rw + (size_t)((p.slot + 1) % 3) * LK;
+  if (wave > 0) {  // routing state of the whole token into LDS (read before the first barrier's use)
+    for (int i = threadIdx.x - WAVE; i < LK; i += MW * WAVE) {
+      sm.route_e[i] = c.cur_i[i];
+      sm.route_w[i] = c.cur_w[i];
+      sm.prev_e[i] = c.prev_i ? c.prev_i[i] : 0;
+    }
+  }
   if (wave == 0)
     sync_role(p, c, sm);
   else
@@ -610,9 +604,8 @@ static StepPlan plan_step(const moe_decode_stack& st, int G) {
   pl.Ldn = 1;
   while (pl.Ldn < SI) pl.Ldn <<= 1;
   const int RPI = WAVE / pl.Ldn;
-  if (K > 8 || K * I > LDS_ACT || (K * I) % 2 || E > LDS_E) return pl;
+  if (K > 8 || K * I > LDS_ACT || E > LDS_E || st.L * K > LDS_LK) return pl;
   pl.GU = (K * I + GW - 1) / GW;
-  pl.GU += pl.GU & 1;
   if (pl.GU > GU_MAX) return pl;
   pl.NR = (E + GW - 1) / GW;
   if (pl.NR > 1) return pl;
@@ -650,7 +643,7 @@ static StepWs step_ws(const moe_decode_stack& st) {
   w.err = 4;
   w.logits = 256;
   w.act = w.logits + al((size_t)st.E * 8);
-  w.g = w.act + al((size_t)st.K * st.d_ff / 2 * 8);
+  w.g = w.act + al((size_t)st.K * st.d_ff * 8);
   w.lin = w.g + al((size_t)(st.d_hidden > 0 ? st.d_hidden : 1) * 8);
   w.hlog = w.lin + al((size_t)st.E * 8);
   w.h = w.hlog + al((size_t)st.L * st.E * 8);

@@ -7,6 +7,10 @@
 // combine fused with the residual) and, for the shared-path adapter, the unmerged LoRA equation
 // of the Edge0 reading guide ("Ejecucion del adaptador no fusionado").
 //
+// The SwiGLU output stays in float32 between the two kernels; the down projection meets it as a
+// float16 hi + lo pair (two dot2 per code pair), so chained layers do not add a float16 rounding
+// of the activation to the error they pass on.
+//
 // Mapping.  A packed row is S 16-byte segments.  A "row slot" of L lanes (the power of two at or
 // above S, at most 64; lanes at or past S idle) owns one row; a lane owns P = ceil(S / L) <= 4
 // segments and always the same columns, so it builds
@@ -86,13 +90,29 @@ struct SegSB {
   }
 };
 
+// u[t][r] = A[r] . v_t with float32 v (the SwiGLU output feeding the down projection's adapter).
+__global__ void __launch_bounds__(256) k_lora_a_f32(int T, int n_in, int rank, const float* __restrict__ v,
+                                                    size_t v_stride, const uint16_t* __restrict__ A,
+                                                    float* __restrict__ u) {
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
+  const int lane = threadIdx.x % WAVE;
+  if (wave >= T * rank) return;
+  const int t = wave / rank, r = wave % rank;
+  const float* vr = v + (size_t)t * v_stride;
+  const uint16_t* ar = A + (size_t)r * n_in;
+  float acc = 0.f;
+  for (int c = lane; c < n_in; c += WAVE) acc = fmaf(h2f(ar[c]), vr[c], acc);
+  acc = group_sum(acc, WAVE);
+  if (lane == 0) u[(size_t)t * rank + r] = acc;
+}
+
 // gate/up + SwiGLU.  Items are (k, i) pairs of token t = blockIdx.y, item = k * I + i.
 // Loads go out in the order weights, scales/biases, activations, so one wait covers them all.
 template <int BITS, int P, bool SPLIT, int NB>
 __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I, int lg2g, int L,
                                                uint32_t flags, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ idx, moe_qmat gate,
-                                               moe_qmat up, uint16_t* __restrict__ act, LoraRef lg,
+                                               moe_qmat up, float* __restrict__ act, LoraRef lg,
                                                LoraRef lu) {
   using G = SegT<BITS>;
   const int lane = threadIdx.x;
@@ -172,7 +192,7 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
       if (lu.B) pu += lora_row(lu, t, ii[nb]);
       float a = pg / (1.f + expf(-pg)) * pu;
       if (bad[nb]) a = quiet_nan();
-      act[((size_t)t * K + kk[nb]) * I + ii[nb]] = f2h(a);
+      act[((size_t)t * K + kk[nb]) * I + ii[nb]] = a;
     }
   }
 }
@@ -181,7 +201,7 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
 // walks the token's K experts in chunks of KC, issuing every weight load of a chunk first.
 template <int BITS, int P, bool SPLIT, int NB, int KC>
 __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, int lg2g, int L,
-                                             const uint16_t* __restrict__ act,
+                                             const float* __restrict__ act,
                                              const int32_t* __restrict__ idx, moe_qmat down,
                                              float* __restrict__ out, const float* __restrict__ wf,
                                              const uint16_t* __restrict__ rf, uint16_t* __restrict__ yf,
@@ -235,13 +255,12 @@ __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, 
     for (int kc = 0; kc < KC; ++kc) {
       const int k = k0 + kc;
       if (k >= K) break;
-      uint32_t xp[P][G::PAIRS];
+      uint32_t xh[P][G::PAIRS], xl[P][G::PAIRS];
       float sx[P][2];
-      float sq = 0.f;
-      const uint16_t* at = act + ((size_t)t * K + k) * I;
+      const float* at = act + ((size_t)t * K + k) * I;
 #pragma unroll
       for (int p = 0; p < P; ++p)
-        if (ls + p * L < S) load_xpairs<BITS>(at + (size_t)(ls + p * L) * G::COLS, xp[p], sx[p], sq);
+        if (ls + p * L < S) load_xpairs_f32<BITS>(at + (size_t)(ls + p * L) * G::COLS, xh[p], xl[p], sx[p]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float po = 0.f;
@@ -249,7 +268,7 @@ __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, 
         for (int p = 0; p < P; ++p) {
           if (ls + p * L >= S) continue;
           float d0 = 0.f, d1 = 0.f;
-          dot_segment<BITS>(q[kc][nb][p], xp[p], d0, d1);
+          dot_segment_split<BITS>(q[kc][nb][p], xh[p], xl[p], d0, d1);
           po += sb[kc][nb][p].apply(d0, d1, sx[p]);
         }
         po = group_sum(po, L);
@@ -321,12 +340,12 @@ hipError_t launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, con
     const int rpw = (WAVE / gu.L) * NB_GATEUP;
     dim3 grid((a.K * a.I + rpw - 1) / rpw, a.T);
     return launch(k_gateup<BITS, P, SPLIT, NB_GATEUP>, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g,
-                  gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, a.act, lg, lu);
+                  gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, (float*)a.act, lg, lu);
   }
   const int rpw = (WAVE / gd.L) * NB_DOWN;
   dim3 grid((a.d + rpw - 1) / rpw, a.T);
   auto go = [&](auto kern) {
-    return launch(kern, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g, gd.L, (const uint16_t*)a.act,
+    return launch(kern, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g, gd.L, (const float*)a.act,
                   a.idx, a.ex.down, a.out, a.w_fuse, a.r_fuse, a.y_fuse, ldn);
   };
   if (a.K <= 2) return go(k_down<BITS, P, SPLIT, NB_DOWN, 2>);
@@ -376,8 +395,8 @@ hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a) {
   for (int which = 0; which < 2 && err == hipSuccess; ++which) {
     if (which == 1 && a.lora3) {
       const int wd = a.T * a.lora3[2].rank;
-      err = first_error(err, launch(k_lora_a, dim3((wd + 3) / 4), dim3(256), 0, s, a.T, a.I, a.lora3[2].rank, 0,
-                                    (const uint16_t*)a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down));
+      err = first_error(err, launch(k_lora_a_f32, dim3((wd + 3) / 4), dim3(256), 0, s, a.T, a.I, a.lora3[2].rank,
+                                    (const float*)a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down));
     }
     if (a.bits == 4)
       err = first_error(err, launch_p<4, false>(s, a, gu, gd, lg, lu, ldn, which));

@@ -336,11 +336,12 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   const int rows_per_block = 16 * GT_WAVES;
   hipError_t err = launch(k_grouped_gateup<BITS, SPLIT>, dim3(a.E, (a.I + rows_per_block - 1) / rows_per_block),
                           dim3(WAVE * GT_WAVES), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x, (const int32_t*)g.offsets,
-                          (const int32_t*)g.perm, rowscale, a.ex.gate, a.ex.up, a.act, lg, lu);
+                          (const int32_t*)g.perm, rowscale, a.ex.gate, a.ex.up, (uint16_t*)a.act, lg, lu);
   if (err != hipSuccess) return err;
   if (a.lora3) {
     const int wd = a.T * a.lora3[2].rank;
-    err = launch_lora_a(s, wd, a.T, a.I, a.lora3[2].rank, 0, a.act, (size_t)a.K * a.I, a.lora3[2].A, a.u_down);
+    err = launch_lora_a(s, wd, a.T, a.I, a.lora3[2].rank, 0, (const uint16_t*)a.act, (size_t)a.K * a.I,
+                        a.lora3[2].A, a.u_down);
     if (err != hipSuccess) return err;
   }
   return launch(k_grouped_down<BITS, SPLIT>, dim3(a.E + 1, (a.d + rows_per_block - 1) / rows_per_block),

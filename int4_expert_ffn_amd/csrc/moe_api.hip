@@ -29,7 +29,7 @@ struct FfnWs {
 FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex) {
   FfnWs w{};
   w.act = 0;
-  w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(uint16_t));
+  w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(float));
   w.u_up = w.u_gate + align_up((size_t)T * MAX_RANK * sizeof(float));
   w.u_down = w.u_up + align_up((size_t)T * MAX_RANK * sizeof(float));
   w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * sizeof(float));
@@ -156,7 +156,7 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
   a.w_fuse = w_fuse;
   a.r_fuse = r_fuse;
   a.y_fuse = y_fuse;
-  a.act = (uint16_t*)(base + ws.act);
+  a.act = base + ws.act;
   a.u_gate = (float*)(base + ws.u_gate);
   a.u_up = (float*)(base + ws.u_up);
   a.u_down = (float*)(base + ws.u_down);

@@ -161,4 +161,59 @@ __device__ __forceinline__ void dot_segment(uint4 q, const uint32_t* xp, float& 
   }
 }
 
+// Float32 activations as two float16 parts, hi = fp16(x) and lo = fp16(x - hi) (x ~ hi + lo to
+// about 22 significant bits), in the same permuted pair order as load_xpairs.  sx gets the float32
+// sum of each half segment.
+template <int BITS>
+__device__ __forceinline__ void load_xpairs_f32(const float* __restrict__ xs, uint32_t* hp, uint32_t* lp, float* sx) {
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  constexpr int CPW = 32 / BITS;  // columns per word
+  float s[2] = {0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float v[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; c += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(xs + w * CPW + c);
+      v[c] = f.x;
+      v[c + 1] = f.y;
+      v[c + 2] = f.z;
+      v[c + 3] = f.w;
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const float a = v[j], b = v[j + PPW];
+      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+      const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
+      hp[w * PPW + j] = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+      lp[w * PPW + j] = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+    }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) s[w >> 1] += v[c];
+  }
+  sx[0] = s[0];
+  sx[1] = s[1];
+}
+
+// sum_j c_j (hi_j + lo_j) over the two half segments: the code pairs are decoded once and meet
+// both activation parts.
+template <int BITS>
+__device__ __forceinline__ void dot_segment_split(uint4 q, const uint32_t* hp, const uint32_t* lp, float& d0,
+                                                  float& d1) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const half2_t c = as_h2(((w[i] >> (BITS * j)) & MASK) | 0x64006400u) - k1024;
+      float& d = i < 2 ? d0 : d1;
+      d = __builtin_amdgcn_fdot2(c, as_h2(hp[i * PPW + j]), d, false);
+      d = __builtin_amdgcn_fdot2(c, as_h2(lp[i * PPW + j]), d, false);
+    }
+  }
+}
+
 }  // namespace moe

@@ -33,7 +33,7 @@ struct DecodeArgs {
   const float* w_fuse;     // [T][K] or nullptr
   const uint16_t* r_fuse;  // [T][d] or nullptr
   uint16_t* y_fuse;        // [T][d] or nullptr
-  uint16_t* act;           // workspace [T][K][I] float16
+  void* act;               // workspace: decode [T][K][I] float32; batched [T*K][I] float16 (expert-sorted)
   float* u_gate;           // workspace [T][rank] (LoRA)
   float* u_up;
   float* u_down;

@@ -126,7 +126,7 @@ def test_workspace_sizes_closed_form():
     assert L.moe_prerouter_workspace_size(1, 256, 1024) == al(4096) + al(1024)
     assert L.moe_prerouter_workspace_size(0, 256, 1024) == 0
     ex = _ex(E=256, d=2048, I=512, group=64)
-    want = al(1 * 4 * 512 * 2) + 3 * al(64 * 4)
+    want = al(1 * 4 * 512 * 4) + 3 * al(64 * 4)
     assert L.moe_expert_ffn_workspace_size(1, 4, ctypes.byref(ex)) == want
     assert L.moe_expert_ffn_workspace_size(256, 4, ctypes.byref(ex)) > want
 
