@@ -34,11 +34,10 @@ namespace {
 
 constexpr int MW = 4;                        // compute waves per workgroup
 constexpr int NTHREADS = (MW + 1) * WAVE;
-constexpr int GU_MAX = 4;                    // gate/up row pairs per compute wave
 constexpr int NH_MAX = 2;                    // head fc1/linear rows per compute wave
-constexpr int PD_MAX = 8;                    // (expert, row-group) down items per compute wave
 constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART = 512, LDS_LK = 512;
-constexpr int POLL_MAX = 16;                 // words per lane per polling pass (1024 per wave)
+constexpr int POLL_MAX = 16;                 // words per lane per polling pass (1024 per wave), <= 64
+static_assert(POLL_MAX >= 1 && POLL_MAX <= 64, "one done bit per polled word");
 constexpr uint32_t TAG_SALT = 0x5A5A5A5Au;
 constexpr uint64_t WAIT_TICKS = 20000000;       // 0.2 s of the 100 MHz real-time counter
 
@@ -55,6 +54,9 @@ struct StepParams {
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_lin, *ll_hlog, *ll_h;
   uint32_t* epoch;
   int* err;
+  const uint16_t* zero16;  // a float16 zero (stands in for an absent bias)
+  const void* ws;          // the workspace (base of the tagged-word buffers)
+  uint32_t ws_bytes;
 };
 
 __device__ __forceinline__ void lds_barrier() {
@@ -63,39 +65,60 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ void ll_store(uint64_t* p, uint32_t payload, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Writers store a tagged word from ONE lane, without a branch: a buffer store whose other lanes
+// carry an offset past the buffer's end, which the hardware range check drops.  (A branch around
+// the store would blur the compiler's count of outstanding loads; 64 lanes storing the same word
+// serialise in the memory system.)  The sc1 bit makes the 8-byte store visible device-wide, as a
+// relaxed agent-scope atomic store is.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t OFF_NONE = 0x80000000u;  // past every buffer this kernel addresses
+constexpr int CPOL_SC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* word, bool on,
+                                       uint32_t payload, uint32_t tag) {
+  u32x2 v;
+  v.x = payload;
+  v.y = tag;
+  const uint32_t off = (uint32_t)((const char*)word - (const char*)p.ws);
+  __builtin_amdgcn_raw_buffer_store_b64(v, ws, on ? off : OFF_NONE, 0, CPOL_SC1);
 }
 __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Poll n tagged words until all carry `tag`; sink(i, payload) receives each word once.
-// Whole wave, POLL_MAX words per lane per pass.  A wait is bounded in wall-clock time: past
-// WAIT_TICKS it raises the error word, sets `failed`, and every later wait of this wave returns
-// at once, so a grid that cannot make progress still finishes quickly (with invalid results).
+// Whole wave, POLL_MAX words per lane per pass, chunk after chunk: wider passes were measured
+// slower, as more readers hammer the same lines at once.  A wait is bounded in wall-clock
+// time: past WAIT_TICKS it raises the error word, sets `failed`, and every later wait of this
+// wave returns at once, so a grid that cannot make progress still finishes quickly (with
+// invalid results).
 template <class Sink>
 __device__ __forceinline__ void ll_wait(const uint64_t* src, int n, uint32_t tag, int* err, bool& failed, Sink sink) {
   if (failed) return;
   const int lane = threadIdx.x % WAVE;
+  constexpr uint64_t ALL = POLL_MAX == 64 ? ~0ull : (1ull << POLL_MAX) - 1;  // one bit per word slot of a lane
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (int base = 0; base < n; base += POLL_MAX * WAVE) {
-    uint32_t done = 0;
+    uint64_t done = 0;
 #pragma unroll
     for (int j = 0; j < POLL_MAX; ++j)
-      if (base + lane + j * WAVE >= n) done |= 1u << j;
+      if (base + lane + j * WAVE >= n) done |= 1ull << j;
     while (true) {
+      const uint64_t* q = src + base + lane;
       uint64_t v[POLL_MAX];
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
-        if (!((done >> j) & 1u)) v[j] = ll_load(src + base + lane + j * WAVE);
+        if (!((done >> j) & 1u)) v[j] = ll_load(q + j * WAVE);
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
         if (!((done >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
           sink(base + lane + j * WAVE, (uint32_t)v[j]);
-          done |= 1u << j;
+          done |= 1ull << j;
         }
-      if (__all(done == (1u << POLL_MAX) - 1u)) break;
+      if (__all(done == ALL)) break;
       if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
         if (lane == 0) atomicAdd(err, 1);
         failed = true;
@@ -177,115 +200,158 @@ __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.f + er
 
 // ------------------------------------------------------------------------------------------
 // Per-layer weight loads held in registers between phases.
-template <int BITS, int PG, int NSH, int GUM>
-struct ABuf {  // gate/up row pairs + head fc1/linear rows (+ their K-hot gather terms)
-  uint4 qg[GUM][PG], qu[GUM][PG];
-  uint16_t sg[GUM][PG], bg[GUM][PG], su[GUM][PG], bu[GUM][PG];
-  bool bad[GUM];
-  uint4 hr[NH_MAX][NSH];
-  float kh[NH_MAX];
+//
+// The compute waves issue a phase's loads one phase early and consume them after the next
+// barriers.  The hardware counter that orders those waits retires memory operations in issue
+// order, so a vector load whose value is needed at once would also wait for every prefetch
+// before it.  Hence: descriptor fields are read through the constant address space (scalar
+// loads, counted apart), per-row biases travel with the prefetched weights, and the gate/up and
+// down loads are unconditional (an item past the end re-reads the last item, and its result is
+// not stored).  Head, fc2 and router rows go one per wave in the order (wave, workgroup), so the
+// rows past the first G*MW land one per workgroup; a wave without such a row skips it (a
+// branch uniform over the wave).
+typedef const __attribute__((address_space(4))) moe_decode_layer* layer_cptr;
+
+struct LayerView {  // the descriptor fields a compute wave needs
+  moe_qmat gate, up, down;
+  const uint16_t *router, *fc1_x, *fc1_r, *fc1_b, *fc2, *fc2_b, *lin_x, *lin_r, *lin_b;
+  bool head;
 };
-template <int BITS, int NSF, int PDM>
-struct BBuf {  // down (expert, row group) items + fc2 rows
-  uint4 q[PDM];
-  uint16_t s[PDM], b[PDM];
-  int k[PDM];
-  bool bad[PDM];
+
+__device__ __forceinline__ layer_cptr layer_at(const StepParams& p, int l) { return (layer_cptr)(p.layers + l); }
+
+__device__ __forceinline__ LayerView layer_view(const StepParams& p, int l) {
+  const layer_cptr D = layer_at(p, l);
+  LayerView v;
+  v.gate = {D->experts.gate.q, D->experts.gate.scales, D->experts.gate.biases};
+  v.up = {D->experts.up.q, D->experts.up.scales, D->experts.up.biases};
+  v.down = {D->experts.down.q, D->experts.down.scales, D->experts.down.biases};
+  v.router = D->router;
+  v.fc1_x = D->head.fc1_x;
+  v.fc1_r = D->head.fc1_r;
+  v.fc1_b = D->head.fc1_b;
+  v.fc2 = D->head.fc2;
+  v.fc2_b = D->head.fc2_b;
+  v.lin_x = D->head.lin_x;
+  v.lin_r = D->head.lin_r;
+  v.lin_b = D->head.lin_b;
+  v.head = l + 1 < p.L && v.fc1_x != nullptr;
+  return v;
+}
+
+template <int BITS, int PG, int NSH, int GU, int NH>
+struct ABuf {  // gate/up row pairs + head fc1/linear rows (+ K-hot gather terms and biases)
+  uint4 qg[GU][PG], qu[GU][PG];
+  uint16_t sg[GU][PG], bg[GU][PG], su[GU][PG], bu[GU][PG];
+  int item[GU];
+  bool bad[GU];
+  bool ok[GU];               // false: a repeat of the last item, not stored
+  uint4 hr[NH][NSH];
+  uint16_t kh[NH], hb[NH];  // raw float16: converted where used, so the loads stay in flight
+  int khm;                  // K-hot term of this lane: 0 none, 1 the table value, 2 NaN (bad index)
+};
+template <int BITS, int NSF, int PD>
+struct BBuf {  // down (expert, row group) items + one fc2 row
+  uint4 q[PD];
+  uint16_t s[PD], b[PD];
+  int k[PD], jr[PD];
+  bool bad[PD];
+  bool ok[PD];
   uint4 fr[NSF];
+  uint16_t fb;
 };
 
-__device__ __forceinline__ const moe_decode_layer& layer_desc(const StepParams& p, int l) { return p.layers[l]; }
+// Row r (r < NH) of this wave's head rows (fc1 rows, then linear rows), and its fc2 / router row.
+__device__ __forceinline__ int head_row(const StepParams& p, int r, int wg, int cw) { return (r * MW + cw) * p.G + wg; }
+__device__ __forceinline__ int e_row(const StepParams& p, int wg, int cw) { return cw * p.G + wg; }
 
-template <int BITS, int PG, int NSH, int GUM>
-__device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* re, const int* prev, int gw, int lane,
-                        ABuf<BITS, PG, NSH, GUM>& a) {
-  const moe_decode_layer& D = layer_desc(p, l);
+template <int BITS, int PG, int NSH, int GU, int NH>
+__device__ __forceinline__ void issue_A(const StepParams& p, const LayerView& v, const int* re, const int* prev,
+                                        int wg, int cw, int lane, ABuf<BITS, PG, NSH, GU, NH>& a) {
+  const int gw = wg * MW + cw;
   const int wpr = p.d * BITS / 32, ngr = p.d >> p.lg2g;
   const int items = p.K * p.I;
 #pragma unroll
-  for (int u = 0; u < GUM; ++u) {
-    const int item = gw * p.GU + u;
-    a.bad[u] = false;
-    if (u < p.GU && item < items) {
-      const int k = item / p.I, i = item - k * p.I;
-      int e = re[k];
-      a.bad[u] = (unsigned)e >= (unsigned)p.E;
-      if (a.bad[u]) e = 0;
-      const size_t row = (size_t)e * p.I + i;
+  for (int u = 0; u < GU; ++u) {
+    a.ok[u] = gw * GU + u < items;
+    const int item = min(gw * GU + u, items - 1);
+    const int k = item / p.I, i = item - k * p.I;
+    int e = re[k];
+    a.bad[u] = (unsigned)e >= (unsigned)p.E;
+    e = a.bad[u] ? 0 : e;
+    a.item[u] = item;
+    const size_t row = (size_t)e * p.I + i;
 #pragma unroll
-      for (int q = 0; q < PG; ++q) {
-        const int seg = lane + q * WAVE;
-        const size_t wo = row * wpr + (size_t)seg * 4;
-        a.qg[u][q] = *reinterpret_cast<const uint4*>(D.experts.gate.q + wo);
-        a.qu[u][q] = *reinterpret_cast<const uint4*>(D.experts.up.q + wo);
-        const size_t go = row * ngr + ((seg * SegT<BITS>::COLS) >> p.lg2g);
-        a.sg[u][q] = D.experts.gate.scales[go];
-        a.bg[u][q] = D.experts.gate.biases[go];
-        a.su[u][q] = D.experts.up.scales[go];
-        a.bu[u][q] = D.experts.up.biases[go];
-      }
+    for (int q = 0; q < PG; ++q) {
+      const int seg = lane + q * WAVE;
+      const size_t wo = row * wpr + (size_t)seg * 4;
+      a.qg[u][q] = *reinterpret_cast<const uint4*>(v.gate.q + wo);
+      a.qu[u][q] = *reinterpret_cast<const uint4*>(v.up.q + wo);
+      const size_t go = row * ngr + ((seg * SegT<BITS>::COLS) >> p.lg2g);
+      a.sg[u][q] = v.gate.scales[go];
+      a.bg[u][q] = v.gate.biases[go];
+      a.su[u][q] = v.up.scales[go];
+      a.bu[u][q] = v.up.biases[go];
     }
   }
-  const bool head = l + 1 < p.L && D.head.fc1_x != nullptr;
+  if (v.head) {
+    // K-hot gather: lane j < K reads row cur[j] of the routing table, lane K <= j < 2K row
+    // E + prev[j - K] (none at the first token); other lanes re-read row cur[0] and add 0.
+    const int j = lane < 2 * p.K ? lane : 0;
+    const bool is_prev = j >= p.K;
+    const bool use = lane < 2 * p.K && (!is_prev || prev != nullptr);
+    int e = is_prev ? (prev ? prev[j - p.K] : 0) : re[j];
+    const bool bad = (unsigned)e >= (unsigned)p.E;
+    e = bad ? 0 : e;
+    const int trow = is_prev && prev ? p.E + e : e;
+    a.khm = use ? (bad ? 2 : 1) : 0;
 #pragma unroll
-  for (int r = 0; r < NH_MAX; ++r) {
-    a.kh[r] = 0.f;
-    const int row = gw * p.NH + r;
-    if (head && r < p.NH && row < p.H + p.E) {
+    for (int r = 0; r < NH; ++r) {
+      const int row = head_row(p, r, wg, cw);
+      if (row >= p.H + p.E) break;  // uniform over the wave
       const bool fc1 = row < p.H;
       const int c = fc1 ? row : row - p.H;
-      const uint16_t* W = fc1 ? D.head.fc1_x + (size_t)c * p.d : D.head.lin_x + (size_t)c * p.d;
+      const uint16_t* W = (fc1 ? v.fc1_x : v.lin_x) + (size_t)c * p.d;
 #pragma unroll
-      for (int s = 0; s < NSH; ++s) a.hr[r][s] = *reinterpret_cast<const uint4*>(W + (size_t)(lane + s * WAVE) * 8);
-      const uint16_t* rtab = fc1 ? D.head.fc1_r : D.head.lin_r;
-      const int ncol = fc1 ? p.H : p.E;
-      if (lane < p.K) {
-        const int e = re[lane];
-        a.kh[r] = (unsigned)e < (unsigned)p.E ? h2f(rtab[(size_t)e * ncol + c]) : quiet_nan();
-      } else if (prev && lane < 2 * p.K) {
-        const int e = prev[lane - p.K];
-        a.kh[r] = (unsigned)e < (unsigned)p.E ? h2f(rtab[(size_t)(p.E + e) * ncol + c]) : quiet_nan();
-      }
+      for (int sg = 0; sg < NSH; ++sg) a.hr[r][sg] = *reinterpret_cast<const uint4*>(W + (size_t)(lane + sg * WAVE) * 8);
+      const uint16_t* rtab = fc1 ? v.fc1_r : v.lin_r;
+      a.kh[r] = rtab[(size_t)trow * (fc1 ? p.H : p.E) + c];
+      const uint16_t* bias = fc1 ? v.fc1_b : v.lin_b;
+      a.hb[r] = bias ? bias[c] : *p.zero16;
     }
   }
 }
 
-template <int BITS, int NSF, int PDM>
-__device__ __forceinline__ void issue_B(const StepParams& p, int l, const int* re, int wg, int cw, int lane,
-                        BBuf<BITS, NSF, PDM>& b) {
-  const moe_decode_layer& D = layer_desc(p, l);
+template <int BITS, int NSF, int PD>
+__device__ __forceinline__ void issue_B(const StepParams& p, const LayerView& v, const int* re, int wg, int cw, int lane,
+                                        BBuf<BITS, NSF, PD>& b) {
   const int wpr = p.I * BITS / 32, ngr = p.I >> p.lg2g;
-  const int RPI = WAVE / p.Ldn, slot = lane / p.Ldn, ls = lane % p.Ldn;
-  const int S = p.I * BITS / 128;
+  const int RPI = WAVE / p.Ldn, slot = lane / p.Ldn;
+  const int ls = min(lane % p.Ldn, p.I * BITS / 128 - 1);
   const int npairs = p.K * p.DI;
 #pragma unroll
-  for (int u = 0; u < PDM; ++u) {
-    const int pk = cw + u * MW;
-    b.k[u] = 0;
-    b.bad[u] = false;
-    if (u < p.PD && pk < npairs) {
-      const int k = pk / p.DI, q = pk - k * p.DI;
-      int e = re[k];
-      b.bad[u] = (unsigned)e >= (unsigned)p.E;
-      if (b.bad[u]) e = 0;
-      b.k[u] = k;
-      int j = wg * p.DR + q * RPI + slot;
-      if (j >= p.d) j = p.d - 1;
-      const size_t row = (size_t)e * p.d + j;
-      if (ls < S) {
-        b.q[u] = *reinterpret_cast<const uint4*>(D.experts.down.q + row * wpr + (size_t)ls * 4);
-        const size_t go = row * ngr + ((ls * SegT<BITS>::COLS) >> p.lg2g);
-        b.s[u] = D.experts.down.scales[go];
-        b.b[u] = D.experts.down.biases[go];
-      }
-    }
+  for (int u = 0; u < PD; ++u) {
+    const int pk = min(cw + u * MW, npairs - 1);
+    const int k = pk / p.DI, q = pk - k * p.DI;
+    int e = re[k];
+    b.bad[u] = (unsigned)e >= (unsigned)p.E;
+    e = b.bad[u] ? 0 : e;
+    b.ok[u] = cw + u * MW < npairs;
+    b.k[u] = k;
+    b.jr[u] = q * RPI + slot;
+    const int j = min(wg * p.DR + b.jr[u], p.d - 1);
+    const size_t row = (size_t)e * p.d + j;
+    b.q[u] = *reinterpret_cast<const uint4*>(v.down.q + row * wpr + (size_t)ls * 4);
+    const size_t go = row * ngr + ((ls * SegT<BITS>::COLS) >> p.lg2g);
+    b.s[u] = v.down.scales[go];
+    b.b[u] = v.down.biases[go];
   }
-  const bool head = l + 1 < p.L && D.head.fc1_x != nullptr;
-  const int row = wg * MW + cw;  // one fc2 row per compute wave (NO == 1)
-  if (head && row < p.E) {
+  const int row = e_row(p, wg, cw);
+  if (v.head && row < p.E) {  // uniform over the wave
 #pragma unroll
-    for (int s = 0; s < NSF; ++s)
-      b.fr[s] = *reinterpret_cast<const uint4*>(D.head.fc2 + (size_t)row * p.H + (size_t)(lane + s * WAVE) * 8);
+    for (int sg = 0; sg < NSF; ++sg)
+      b.fr[sg] = *reinterpret_cast<const uint4*>(v.fc2 + (size_t)row * p.H + (size_t)(lane + sg * WAVE) * 8);
+    b.fb = v.fc2_b ? v.fc2_b[row] : *p.zero16;
   }
 }
 
@@ -311,11 +377,11 @@ struct StepCtx {
   __device__ uint32_t tag(int ph) const { return ((epoch << 10) | (uint32_t)ph) ^ TAG_SALT; }
 };
 
-__device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
-  return p.bootstrap || l == 0 || p.layers[l - 1].head.fc1_x == nullptr;
-}
 __device__ __forceinline__ bool has_head(const StepParams& p, int l) {
-  return l + 1 < p.L && p.layers[l].head.fc1_x != nullptr;
+  return l + 1 < p.L && layer_at(p, l)->head.fc1_x != nullptr;
+}
+__device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
+  return p.bootstrap || l == 0 || !has_head(p, l - 1);
 }
 
 // Wave 0 of every workgroup: waits for the vectors each phase needs and unpacks them into LDS.
@@ -379,25 +445,35 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
 }
 
 // Waves 1..MW: the arithmetic, with each phase's weight loads issued one phase early.
-template <int BITS, int PG, int NSH, int NSF, int GUM, int PDM>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
 __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   using GS = SegT<BITS>;
-  const int lane = c.lane, cw = c.cw, gw = c.gw, wg = c.wg, dh = p.d / 2;
-  ABuf<BITS, PG, NSH, GUM> A;
-  BBuf<BITS, NSF, PDM> B;
+  constexpr int NH = NH_MAX;
+  const int lane = c.lane, cw = c.cw, gw = c.gw, wg = c.wg, dh = p.d / 2, K = p.K;
+  const __amdgpu_buffer_rsrc_t ws = buffer_of(p.ws, p.ws_bytes);
+  const __amdgpu_buffer_rsrc_t hout = buffer_of(p.h_out, (uint32_t)p.d * 2);
+  const bool lead = lane == 0;
+  ABuf<BITS, PG, NSH, GU, NH> A;
+  BBuf<BITS, NSF, PD> B;
+  LayerView vn = layer_view(p, 0);
+  bool self_n = true;
   for (int l = 0; l < p.L; ++l) {
-    const moe_decode_layer& D = p.layers[l];
-    const bool self = self_routed(p, l);
-    const bool head = has_head(p, l);
+    const LayerView v = vn;
+    const bool self = self_n;
+    if (l + 1 < p.L) {
+      vn = layer_view(p, l + 1);
+      self_n = p.bootstrap || !v.head;
+    }
+    const bool prefetch = l + 1 < p.L && !self_n;
     const int hb = l & 1;
-    const int* prev_l = c.prev_i ? sm.prev_e + l * p.K : nullptr;
     lds_barrier();  // B1
     const float scale = sm.scale[hb];
     const uint16_t* hl = sm.h[hb];
     if (self) {
-      // R_l: this wave's router rows -> tagged logits
-      for (int r = gw * p.NR; r < min(p.E, gw * p.NR + p.NR); ++r) {
-        const uint16_t* W = D.router + (size_t)r * p.d;
+      // R_l: at most one router row per wave -> tagged logit
+      const int r = e_row(p, wg, cw);
+      if (r < p.E) {  // uniform over the wave
+        const uint16_t* W = v.router + (size_t)r * p.d;
         float acc = 0.f;
 #pragma unroll
         for (int sg = 0; sg < NSH; ++sg) {
@@ -410,11 +486,11 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           acc = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), acc, false);
         }
         acc = wave_sum(acc) * scale;
-        if (lane == 0) ll_store(p.ll_logits + r, __float_as_uint(acc), c.tag(3 * l));
+        ll_put(ws, p, p.ll_logits + r, lead, __float_as_uint(acc), c.tag(3 * l));
       }
       lds_barrier();  // B2
-      issue_A<BITS, PG, NSH, GUM>(p, l, sm.route_e + l * p.K, prev_l, gw, lane, A);
-      issue_B<BITS, NSF, PDM>(p, l, sm.route_e + l * p.K, wg, cw, lane, B);
+      issue_A<BITS, PG, NSH, GU, NH>(p, v, sm.route_e + l * K, c.prev_i ? sm.prev_e + l * K : nullptr, wg, cw, lane, A);
+      issue_B<BITS, NSF, PD>(p, v, sm.route_e + l * K, wg, cw, lane, B);
     }
 
     // ---- A_l: gate/up + SwiGLU, head fc1 (+GELU) and linear rows ----
@@ -425,140 +501,117 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
 #pragma unroll
       for (int q = 0; q < PG; ++q) load_xpairs<BITS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
 #pragma unroll
-      for (int u = 0; u < GUM; ++u) {
-        const int item = gw * p.GU + u;
-        if (u < p.GU && item < p.K * p.I) {
-          float pg = 0.f, pu = 0.f;
+      for (int u = 0; u < GU; ++u) {
+        float pg = 0.f, pu = 0.f;
 #pragma unroll
-          for (int q = 0; q < PG; ++q) {
-            float d0 = 0.f, d1 = 0.f;
-            dot_segment<BITS>(A.qg[u][q], xp[q], d0, d1);
-            pg += h2f(A.sg[u][q]) * (d0 + d1) + h2f(A.bg[u][q]) * (sx[q][0] + sx[q][1]);
-            d0 = d1 = 0.f;
-            dot_segment<BITS>(A.qu[u][q], xp[q], d0, d1);
-            pu += h2f(A.su[u][q]) * (d0 + d1) + h2f(A.bu[u][q]) * (sx[q][0] + sx[q][1]);
-          }
-          pg = wave_sum(pg) * scale;
-          pu = wave_sum(pu) * scale;
-          float a = pg / (1.f + expf(-pg)) * pu;
-          if (A.bad[u]) a = quiet_nan();
-          if (lane == 0) ll_store(p.ll_act + item, __float_as_uint(a), tA);
+        for (int q = 0; q < PG; ++q) {
+          float d0 = 0.f, d1 = 0.f;
+          dot_segment<BITS>(A.qg[u][q], xp[q], d0, d1);
+          pg += h2f(A.sg[u][q]) * (d0 + d1) + h2f(A.bg[u][q]) * (sx[q][0] + sx[q][1]);
+          d0 = d1 = 0.f;
+          dot_segment<BITS>(A.qu[u][q], xp[q], d0, d1);
+          pu += h2f(A.su[u][q]) * (d0 + d1) + h2f(A.bu[u][q]) * (sx[q][0] + sx[q][1]);
         }
+        pg = wave_sum(pg) * scale;
+        pu = wave_sum(pu) * scale;
+        const float a = pg / (1.f + expf(-pg)) * pu;
+        ll_put(ws, p, p.ll_act + A.item[u], lead && A.ok[u], __float_as_uint(A.bad[u] ? quiet_nan() : a), tA);
       }
-      if (head) {
+      if (v.head) {
 #pragma unroll
-        for (int r = 0; r < NH_MAX; ++r) {
-          const int row = gw * p.NH + r;
-          if (r < p.NH && row < p.H + p.E) {
-            float acc = 0.f;
+        for (int r = 0; r < NH; ++r) {
+          const int row = head_row(p, r, wg, cw);
+          if (row >= p.H + p.E) break;  // uniform over the wave
+          float acc = 0.f;
 #pragma unroll
-            for (int sg = 0; sg < NSH; ++sg) {
-              const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)(lane + sg * WAVE) * 8);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
-            }
-            acc = wave_sum(acc) * scale;
-            const float gsum = wave_sum(A.kh[r]);
-            if (lane == 0) {
-              if (row < p.H) {
-                const float v = acc + gsum + (D.head.fc1_b ? h2f(D.head.fc1_b[row]) : 0.f);
-                ll_store(p.ll_g + row, __float_as_uint(gelu_erf(v)), tA);
-              } else {
-                const int col = row - p.H;
-                const float v = acc + gsum + (D.head.lin_b ? h2f(D.head.lin_b[col]) : 0.f);
-                ll_store(p.ll_lin + col, __float_as_uint(v), tA);
-              }
-            }
+          for (int sg = 0; sg < NSH; ++sg) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)(lane + sg * WAVE) * 8);
+            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
+            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
+            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
+            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
           }
+          const float kh = A.khm == 1 ? h2f(A.kh[r]) : (A.khm == 2 ? quiet_nan() : 0.f);
+          const float val = wave_sum(acc) * scale + wave_sum(kh) + h2f(A.hb[r]);
+          const bool fc1 = row < p.H;
+          ll_put(ws, p, fc1 ? p.ll_g + row : p.ll_lin + (row - p.H), lead, __float_as_uint(fc1 ? gelu_erf(val) : val), tA);
         }
       }
     }
-    if (l + 1 < p.L && !self_routed(p, l + 1))  // weights of A_{l+1}, one phase early
-      issue_A<BITS, PG, NSH, GUM>(p, l + 1, sm.route_e + (l + 1) * p.K,
-                                  c.prev_i ? sm.prev_e + (l + 1) * p.K : nullptr, gw, lane, A);
+    if (prefetch)  // weights of A_{l+1}, one phase early
+      issue_A<BITS, PG, NSH, GU, NH>(p, vn, sm.route_e + (l + 1) * K, c.prev_i ? sm.prev_e + (l + 1) * K : nullptr,
+                                     wg, cw, lane, A);
     lds_barrier();  // B3
 
     // ---- B_l: down partials of this workgroup's rows, head fc2 rows ----
     {
-      const int RPI = WAVE / p.Ldn, slot = lane / p.Ldn, ls = lane % p.Ldn;
       const int S = p.I * BITS / 128;
+      const int ls = lane % p.Ldn;
+      const int lsc = min(ls, S - 1);
 #pragma unroll
-      for (int u = 0; u < PDM; ++u) {
-        const int pk = cw + u * MW;
-        if (u < p.PD && pk < p.K * p.DI) {
-          const int k = B.k[u], q = pk - k * p.DI;
-          float po = 0.f;
-          if (ls < S) {
-            uint32_t xh[GS::PAIRS], xl[GS::PAIRS];
-            float sx[2];
-            load_xpairs_f32<BITS>(sm.act + (size_t)k * p.I + (size_t)ls * GS::COLS, xh, xl, sx);
-            float d0 = 0.f, d1 = 0.f;
-            dot_segment_split<BITS>(B.q[u], xh, xl, d0, d1);
-            po = h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * (sx[0] + sx[1]);
-          }
-          po = group_sum_last(po, p.Ldn);
-          if (ls == p.Ldn - 1) sm.part[k * p.DR + q * RPI + slot] = B.bad[u] ? quiet_nan() : po;
-        }
+      for (int u = 0; u < PD; ++u) {
+        uint32_t xh[GS::PAIRS], xl[GS::PAIRS];
+        float sx[2];
+        load_xpairs_f32<BITS>(sm.act + (size_t)B.k[u] * p.I + (size_t)lsc * GS::COLS, xh, xl, sx);
+        float d0 = 0.f, d1 = 0.f;
+        dot_segment_split<BITS>(B.q[u], xh, xl, d0, d1);
+        float po = ls < S ? h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * (sx[0] + sx[1]) : 0.f;
+        po = group_sum_last(po, p.Ldn);
+        if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
       }
-      if (head) {
-        const int row = wg * MW + cw;
-        if (row < p.E) {
-          float acc = 0.f;
+      const int row = e_row(p, wg, cw);
+      if (v.head && row < p.E) {  // uniform over the wave
+        float acc = 0.f;
 #pragma unroll
-          for (int sg = 0; sg < NSF; ++sg) {
-            const float* gp = sm.g + (size_t)(lane + sg * WAVE) * 8;
-            const half2_t w0 = as_h2(B.fr[sg].x), w1 = as_h2(B.fr[sg].y), w2 = as_h2(B.fr[sg].z),
-                          w3 = as_h2(B.fr[sg].w);
-            acc = fmaf((float)w0.x, gp[0], acc);
-            acc = fmaf((float)w0.y, gp[1], acc);
-            acc = fmaf((float)w1.x, gp[2], acc);
-            acc = fmaf((float)w1.y, gp[3], acc);
-            acc = fmaf((float)w2.x, gp[4], acc);
-            acc = fmaf((float)w2.y, gp[5], acc);
-            acc = fmaf((float)w3.x, gp[6], acc);
-            acc = fmaf((float)w3.y, gp[7], acc);
-          }
-          acc = wave_sum(acc);
-          if (lane == 0) {
-            const float v = acc + sm.lin[row] + (D.head.fc2_b ? h2f(D.head.fc2_b[row]) : 0.f);
-            ll_store(p.ll_hlog + (size_t)l * p.E + row, __float_as_uint(v), c.tag(3 * l + 2));
-          }
+        for (int sg = 0; sg < NSF; ++sg) {
+          const float* gp = sm.g + (size_t)(lane + sg * WAVE) * 8;
+          const half2_t w0 = as_h2(B.fr[sg].x), w1 = as_h2(B.fr[sg].y), w2 = as_h2(B.fr[sg].z),
+                        w3 = as_h2(B.fr[sg].w);
+          acc = fmaf((float)w0.x, gp[0], acc);
+          acc = fmaf((float)w0.y, gp[1], acc);
+          acc = fmaf((float)w1.x, gp[2], acc);
+          acc = fmaf((float)w1.y, gp[3], acc);
+          acc = fmaf((float)w2.x, gp[4], acc);
+          acc = fmaf((float)w2.y, gp[5], acc);
+          acc = fmaf((float)w3.x, gp[6], acc);
+          acc = fmaf((float)w3.y, gp[7], acc);
         }
+        const float val = wave_sum(acc) + sm.lin[row] + h2f(B.fb);
+        ll_put(ws, p, p.ll_hlog + (size_t)l * p.E + row, lead, __float_as_uint(val), c.tag(3 * l + 2));
       }
     }
-    if (l + 1 < p.L && !self_routed(p, l + 1))  // weights of B_{l+1}, one phase early
-      issue_B<BITS, NSF, PDM>(p, l + 1, sm.route_e + (l + 1) * p.K, wg, cw, lane, B);
+    if (prefetch)  // weights of B_{l+1}, one phase early
+      issue_B<BITS, NSF, PD>(p, vn, sm.route_e + (l + 1) * K, wg, cw, lane, B);
     lds_barrier();  // B4
-    // ---- combine + residual of this workgroup's rows -> h_{l+1} ----
+    // ---- combine + residual of this workgroup's rows -> h_{l+1} (wave 1; lane = row) ----
     if (cw == 0) {
-      const int jr = lane, j = wg * p.DR + jr;
-      float y = 0.f;
-      if (jr < p.DR && j < p.d) {
-        float acc = 0.f;
-        for (int k = 0; k < p.K; ++k) acc = fmaf(sm.route_w[l * p.K + k], sm.part[k * p.DR + jr], acc);
-        y = h2f(hl[j]) + acc;
-      }
-      const uint32_t yb = f2h(y);
-      const uint32_t nb = __shfl_down(yb, 1, WAVE);
-      if (jr < p.DR && j < p.d) {
-        if (l + 1 == p.L)
-          p.h_out[j] = (uint16_t)yb;
-        else if ((jr & 1) == 0)
-          ll_store(p.ll_h + (size_t)(l + 1) * dh + j / 2, yb | (nb << 16), c.tag(3 * l + 2));
+      const int nrows = min(p.DR, p.d - wg * p.DR);  // >= 2 and even: the last workgroup may hold fewer
+      const int jr = min(lane, nrows - 1);
+      const int j = wg * p.DR + jr;
+      const bool mine = lane < nrows;
+      float acc = 0.f;
+      for (int k = 0; k < K; ++k) acc = fmaf(sm.route_w[l * K + k], sm.part[k * p.DR + jr], acc);
+      const uint32_t yb = f2h(h2f(hl[j]) + acc);
+      if (l + 1 == p.L) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)yb, hout, mine ? (uint32_t)j * 2 : OFF_NONE, 0, 0);
+      } else {
+        // lane m sends word m (rows 2m, 2m+1)
+        const int m = min(lane, nrows / 2 - 1);
+        const uint32_t lo = __shfl(yb, 2 * m, WAVE), hi = __shfl(yb, 2 * m + 1, WAVE);
+        ll_put(ws, p, p.ll_h + (size_t)(l + 1) * dh + wg * (p.DR / 2) + m, lane < nrows / 2, lo | (hi << 16),
+               c.tag(3 * l + 2));
       }
     }
   }
 }
 
-template <int BITS, int PG, int NSH, int NSF, int GUM, int PDM>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
 __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   __shared__ __attribute__((aligned(16))) StepShared sm;
   StepCtx c;
   c.wg = blockIdx.x;
   c.lane = threadIdx.x % WAVE;
-  const int wave = threadIdx.x / WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   c.cw = wave - 1;
   c.gw = c.wg * MW + c.cw;
   c.epoch = *p.epoch;
@@ -575,10 +628,13 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
       sm.prev_e[i] = c.prev_i ? c.prev_i[i] : 0;
     }
   }
-  if (wave == 0)
+  if (wave == 0) {
     sync_role(p, c, sm);
-  else
-    compute_role<BITS, PG, NSH, NSF, GUM, PDM>(p, c, sm);
+  } else {
+    // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
+    __builtin_amdgcn_s_setprio(2);
+    compute_role<BITS, PG, NSH, NSF, GU, PD>(p, c, sm);
+  }
   if (c.wg == 0 && threadIdx.x == 0) *p.epoch = c.epoch + 1;
 }
 
@@ -590,57 +646,57 @@ struct StepPlan {
   int G, GU, NH, NR, NO, DR, DI, PD, Ldn, PG, NSH, NSF;
 };
 
-static StepPlan plan_step(const moe_decode_stack& st, int G) {
+static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD);
+
+static StepPlan plan_step(const moe_decode_stack& st, int cus) {
   StepPlan pl{};
   const int d = st.d_model, I = st.d_ff, E = st.E, K = st.K, H = st.d_hidden, bits = st.bits;
-  const int GW = G * MW;
-  if (G < 1 || d % 512 || d > LDS_D || (d * bits / 128) % WAVE) return pl;
+  if (cus < 1 || d % 512 || d > LDS_D || (d * bits / 128) % WAVE) return pl;
   pl.PG = d * bits / 128 / WAVE;
   pl.NSH = d / 512;
-  if (pl.PG > 2 || (pl.NSH != 4 && pl.NSH != 8)) return pl;
   const int SI = I * bits / 128;
   if (SI < 1 || SI > WAVE || (I * bits) % 128) return pl;
   if (bits == 2 && st.group < 64) return pl;  // a 2-bit segment must sit inside one group
+  if (K > 8 || K * I > LDS_ACT || E > LDS_E || st.L * K > LDS_LK) return pl;
   pl.Ldn = 1;
   while (pl.Ldn < SI) pl.Ldn <<= 1;
   const int RPI = WAVE / pl.Ldn;
-  if (K > 8 || K * I > LDS_ACT || E > LDS_E || st.L * K > LDS_LK) return pl;
-  pl.GU = (K * I + GW - 1) / GW;
-  if (pl.GU > GU_MAX) return pl;
-  pl.NR = (E + GW - 1) / GW;
-  if (pl.NR > 1) return pl;
-  pl.NO = 1;
-  if (E > GW) return pl;
-  pl.DR = (d + G - 1) / G;
+  // down rows per workgroup: a multiple of the rows one wave covers at once, and even (h travels
+  // as float16 pairs); then as many workgroups as it takes to cover d, each owning >= 2 rows
+  pl.DR = (d + cus - 1) / cus;
   pl.DR = (pl.DR + RPI - 1) / RPI * RPI;
   pl.DR += pl.DR & 1;
   if (pl.DR > WAVE || K * pl.DR > LDS_PART) return pl;
+  pl.G = (d + pl.DR - 1) / pl.DR;
+  const int GW = pl.G * MW;
   pl.DI = (pl.DR + RPI - 1) / RPI;
   pl.PD = (K * pl.DI + MW - 1) / MW;
-  if (pl.PD > PD_MAX) return pl;
+  pl.GU = (K * I + GW - 1) / GW;
+  pl.NR = (E + GW - 1) / GW;
+  pl.NO = (E + GW - 1) / GW;
+  if (pl.NR > 1 || pl.NO > 1) return pl;  // one router row and one fc2 row per compute wave
   if (H > 0) {
     if (H % 512 || H > LDS_H) return pl;
     pl.NSF = H / 512;
-    if (pl.NSF != 1 && pl.NSF != 2 && pl.NSF != 4) return pl;
     pl.NH = (H + E + GW - 1) / GW;
     if (pl.NH > NH_MAX) return pl;
   } else {
     pl.NSF = 1;
     pl.NH = 0;
   }
-  pl.G = G;
-  pl.ok = true;
+  pl.ok = has_variant(bits, pl.PG, pl.NSH, pl.NSF, pl.GU, pl.PD);
   return pl;
 }
 
 struct StepWs {
-  size_t epoch, err, logits, act, g, lin, hlog, h, total;
+  size_t epoch, err, zero, logits, act, g, lin, hlog, h, total;
 };
 static StepWs step_ws(const moe_decode_stack& st) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   StepWs w{};
   w.epoch = 0;
   w.err = 4;
+  w.zero = 8;  // 8 bytes that stay zero
   w.logits = 256;
   w.act = w.logits + al((size_t)st.E * 8);
   w.g = w.act + al((size_t)st.K * st.d_ff * 8);
@@ -658,32 +714,38 @@ static int device_cus() {
   return cus;
 }
 
-template <int BITS, int PG, int NSH, int NSF, int GUM, int PDM>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
 static hipError_t go(hipStream_t s, const StepParams& p) {
   int occ = 0;
-  auto k = k_decode_step<BITS, PG, NSH, NSF, GUM, PDM>;
+  auto k = k_decode_step<BITS, PG, NSH, NSF, GU, PD>;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, NTHREADS, 0);
   if (e != hipSuccess) return e;
   if (occ < 1) return hipErrorInvalidConfiguration;  // every workgroup must be resident at once
   return launch(k, dim3(p.G), dim3(NTHREADS), 0, s, p);
 }
 
-// Instantiated shapes (bits, gate/up segments per lane, fp16 segments per lane for d and H,
-// gate/up pairs and down items per wave): the decode configurations, then general fallbacks.
+// Instantiated shapes: (bits, gate/up segments per lane, fp16 segments per lane of a d-row and of
+// an H-row, gate/up pairs per wave, down items per wave).  The counts are exact, so every compute
+// wave issues the same loads.
+#define MOE_STEP_VARIANTS(X)                                                                       \
+  X(4, 1, 4, 2, 2, 2) /* d 2048, I 512, K 4, E 256, head hidden 1024 */                            \
+  X(4, 1, 4, 1, 4, 4) /* d 2048, I 512, K 8, E 256, no heads */                                    \
+  X(4, 2, 8, 1, 4, 8) /* d 4096, I 1024, K 4, E 512, int4, no heads */                             \
+  X(2, 1, 8, 1, 4, 4) /* d 4096, I 1024, K 4, E 512, int2, no heads */
+
+static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD) {
+#define MOE_STEP_HAS(B_, PG_, NSH_, NSF_, GU_, PD_) \
+  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && GU == GU_ && PD == PD_) return true;
+  MOE_STEP_VARIANTS(MOE_STEP_HAS)
+#undef MOE_STEP_HAS
+  return false;
+}
+
 static hipError_t dispatch(hipStream_t s, const StepParams& p, int bits, int PG, int NSH, int NSF) {
-  const int gum = p.GU <= 2 ? 2 : 4, pdm = p.PD <= 2 ? 2 : (p.PD <= 4 ? 4 : 8);
-#define MOE_STEP_CASE(B_, PG_, NSH_, NSF_, GUM_, PDM_)                                                  \
-  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF <= NSF_ && gum <= GUM_ && pdm <= PDM_)           \
-    return go<B_, PG_, NSH_, NSF_, GUM_, PDM_>(s, p);
-  MOE_STEP_CASE(4, 1, 4, 2, 2, 2)   // d 2048, I 512, K 4, H 1024
-  MOE_STEP_CASE(4, 1, 4, 2, 4, 4)   // d 2048, I 512, K 8
-  MOE_STEP_CASE(4, 2, 8, 1, 4, 8)   // d 4096, I 1024, int4
-  MOE_STEP_CASE(2, 1, 8, 1, 4, 4)   // d 4096, I 1024, int2
-  MOE_STEP_CASE(4, 1, 4, 4, 4, 8)
-  MOE_STEP_CASE(4, 2, 8, 4, 4, 8)
-  MOE_STEP_CASE(2, 1, 8, 4, 4, 8)
-  MOE_STEP_CASE(2, 2, 8, 4, 4, 8)
-#undef MOE_STEP_CASE
+#define MOE_STEP_GO(B_, PG_, NSH_, NSF_, GU_, PD_) \
+  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && p.GU == GU_ && p.PD == PD_) return go<B_, PG_, NSH_, NSF_, GU_, PD_>(s, p);
+  MOE_STEP_VARIANTS(MOE_STEP_GO)
+#undef MOE_STEP_GO
   return hipErrorInvalidValue;
 }
 
@@ -697,6 +759,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   const StepPlan pl = plan_step(st, G);
   if (!pl.ok) return hipErrorInvalidValue;
   const StepWs w = step_ws(st);
+  if (w.total >= OFF_NONE) return hipErrorInvalidValue;
   char* b = (char*)ws;
   StepParams p{};
   p.L = st.L;
@@ -733,6 +796,9 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.ll_h = (uint64_t*)(b + w.h);
   p.epoch = (uint32_t*)(b + w.epoch);
   p.err = (int*)(b + w.err);
+  p.zero16 = (const uint16_t*)(b + w.zero);
+  p.ws = ws;
+  p.ws_bytes = (uint32_t)w.total;
   return dispatch(s, p, st.bits, pl.PG, pl.NSH, pl.NSF);
 }
 
