@@ -12,27 +12,31 @@
 //     so the weighted combine stays local and in fixed order) and of the fc2 rows.
 //   * The SwiGLU output travels in float32 and meets the down weights as a float16 hi + lo pair.
 //   * Data moves between workgroups as tagged 8-byte words (32-bit payload, 32-bit tag naming
-//     the token epoch and the phase), written and read with agent-scope relaxed atomics; a
-//     reader polls until every tag matches, so no flag/data ordering is needed.
+//     the token epoch and the phase), written by one lane with device-coherent stores and read
+//     with agent-scope relaxed atomic loads; a reader polls until every tag matches, so no
+//     flag/data ordering is needed.
 //   * Per workgroup, wave 0 only waits for and unpacks the vector the next phase needs (into
 //     LDS); waves 1..4 compute.  Their weight loads for a phase are issued one phase early, and
 //     workgroup barriers fence LDS only, so those loads stay in flight while the phase waits.
-//   * The heads (off the critical path: their output routes the next token) ride in the same
-//     phases; their top-Ks run after the last layer, spread over the workgroups.
+//   * The heads are off the critical path (their output routes the next token).  The linear and
+//     fc1 rows of head l run in phase A of layer l; the wave that computes linear row e keeps it
+//     and adds it to fc2 row e, which runs in phase A of layer l+1, after the head's hidden vector
+//     g_l has been fetched while the grid waited for h_{l+1}.  So the act exchange carries only
+//     the SwiGLU outputs.  The top-Ks run after the last layer, spread over the workgroups.
 //   * The whole token's routing state is staged in LDS at the start, so issuing a phase's weight
 //     loads never waits on a global read of the expert indices.
 //
 // Phases per layer l: [R_l: own router + top-K, only for layer 0, layers with no prediction and
-// the first token] -> A_l: gate/up + SwiGLU, head fc1 (+GELU) and linear rows -> B_l: down +
-// combine + residual, head fc2 rows.  Every wait is bounded in time: one that runs out sets the
-// error word and lets the kernel finish (its results are then invalid).
+// the first token] -> A_l: gate/up + SwiGLU, fc2 rows of head l-1, linear and fc1 (+GELU) rows of
+// head l -> B_l: down + combine + residual.  Every wait is bounded in time: one that runs out
+// sets the error word and lets the kernel finish (its results are then invalid).
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int MW = 4;                        // compute waves per workgroup
+constexpr int MW = 8;                        // compute waves per workgroup (two per SIMD)
 constexpr int NTHREADS = (MW + 1) * WAVE;
 constexpr int NH_MAX = 2;                    // head fc1/linear rows per compute wave
 constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART = 512, LDS_LK = 512;
@@ -51,7 +55,7 @@ struct StepParams {
   float* rw;
   int slot, bootstrap;
   uint32_t topk_flags;
-  uint64_t *ll_logits, *ll_act, *ll_g, *ll_lin, *ll_hlog, *ll_h;
+  uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
   uint32_t* epoch;
   int* err;
   const uint16_t* zero16;  // a float16 zero (stands in for an absent bias)
@@ -65,6 +69,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Tagged-word vectors are plain arrays of 8-byte words; each lives in its own 256-byte-aligned
+// region of the workspace.  (Spreading their 64-byte lines over memory pages was measured slower.)
+__host__ __device__ constexpr size_t ll_bytes(size_t words) { return (words * 8 + 255) / 256 * 256; }
+__device__ __forceinline__ const uint64_t* ll_at(const uint64_t* base, size_t i) { return base + i; }
+
 // Writers store a tagged word from ONE lane, without a branch: a buffer store whose other lanes
 // carry an offset past the buffer's end, which the hardware range check drops.  (A branch around
 // the store would blur the compiler's count of outstanding loads; 64 lanes storing the same word
@@ -77,12 +86,12 @@ constexpr int CPOL_SC1 = 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* word, bool on,
-                                       uint32_t payload, uint32_t tag) {
+__device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* vec, size_t i,
+                                       bool on, uint32_t payload, uint32_t tag) {
   u32x2 v;
   v.x = payload;
   v.y = tag;
-  const uint32_t off = (uint32_t)((const char*)word - (const char*)p.ws);
+  const uint32_t off = (uint32_t)((const char*)ll_at(vec, i) - (const char*)p.ws);
   __builtin_amdgcn_raw_buffer_store_b64(v, ws, on ? off : OFF_NONE, 0, CPOL_SC1);
 }
 __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
@@ -96,7 +105,8 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 // wave returns at once, so a grid that cannot make progress still finishes quickly (with
 // invalid results).
 template <class Sink>
-__device__ __forceinline__ void ll_wait(const uint64_t* src, int n, uint32_t tag, int* err, bool& failed, Sink sink) {
+__device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n, uint32_t tag, int* err, bool& failed,
+                                        Sink sink) {
   if (failed) return;
   const int lane = threadIdx.x % WAVE;
   constexpr uint64_t ALL = POLL_MAX == 64 ? ~0ull : (1ull << POLL_MAX) - 1;  // one bit per word slot of a lane
@@ -107,11 +117,11 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, int n, uint32_t tag
     for (int j = 0; j < POLL_MAX; ++j)
       if (base + lane + j * WAVE >= n) done |= 1ull << j;
     while (true) {
-      const uint64_t* q = src + base + lane;
+      const size_t q = start + base + lane;
       uint64_t v[POLL_MAX];
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
-        if (!((done >> j) & 1u)) v[j] = ll_load(q + j * WAVE);
+        if (!((done >> j) & 1u)) v[j] = ll_load(ll_at(src, q + j * WAVE));
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
         if (!((done >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
@@ -145,6 +155,25 @@ __device__ __forceinline__ float group_sum_last(float v, int G) {
 }
 __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_sum_last(v, 64)), 63));
+}
+// N independent wave sums, step by step in lockstep so that consecutive DPP operations never
+// depend on each other; every lane receives every sum.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x111, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x112, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x114, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x118, 0xf>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x142, 0xa>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x143, 0xc>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
 }
 
 __device__ __forceinline__ uint32_t order_bits(float v) {
@@ -212,35 +241,15 @@ __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.f + er
 // branch uniform over the wave).
 typedef const __attribute__((address_space(4))) moe_decode_layer* layer_cptr;
 
-struct LayerView {  // the descriptor fields a compute wave needs
-  moe_qmat gate, up, down;
-  const uint16_t *router, *fc1_x, *fc1_r, *fc1_b, *fc2, *fc2_b, *lin_x, *lin_r, *lin_b;
-  bool head;
-};
-
 __device__ __forceinline__ layer_cptr layer_at(const StepParams& p, int l) { return (layer_cptr)(p.layers + l); }
 
-__device__ __forceinline__ LayerView layer_view(const StepParams& p, int l) {
-  const layer_cptr D = layer_at(p, l);
-  LayerView v;
-  v.gate = {D->experts.gate.q, D->experts.gate.scales, D->experts.gate.biases};
-  v.up = {D->experts.up.q, D->experts.up.scales, D->experts.up.biases};
-  v.down = {D->experts.down.q, D->experts.down.scales, D->experts.down.biases};
-  v.router = D->router;
-  v.fc1_x = D->head.fc1_x;
-  v.fc1_r = D->head.fc1_r;
-  v.fc1_b = D->head.fc1_b;
-  v.fc2 = D->head.fc2;
-  v.fc2_b = D->head.fc2_b;
-  v.lin_x = D->head.lin_x;
-  v.lin_r = D->head.lin_r;
-  v.lin_b = D->head.lin_b;
-  v.head = l + 1 < p.L && v.fc1_x != nullptr;
-  return v;
+// Whether layer l carries a head that predicts layer l+1.
+__device__ __forceinline__ bool has_head(const StepParams& p, int l) {
+  return l + 1 < p.L && layer_at(p, l)->head.fc1_x != nullptr;
 }
 
-template <int BITS, int PG, int NSH, int GU, int NH>
-struct ABuf {  // gate/up row pairs + head fc1/linear rows (+ K-hot gather terms and biases)
+template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
+struct ABuf {  // gate/up row pairs, head linear/fc1 rows (+ K-hot terms, biases), previous head's fc2 row
   uint4 qg[GU][PG], qu[GU][PG];
   uint16_t sg[GU][PG], bg[GU][PG], su[GU][PG], bu[GU][PG];
   int item[GU];
@@ -249,25 +258,40 @@ struct ABuf {  // gate/up row pairs + head fc1/linear rows (+ K-hot gather terms
   uint4 hr[NH][NSH];
   uint16_t kh[NH], hb[NH];  // raw float16: converted where used, so the loads stay in flight
   int khm;                  // K-hot term of this lane: 0 none, 1 the table value, 2 NaN (bad index)
+  uint4 fr[NSF];            // fc2 row of the previous layer's head
+  uint16_t fb;
 };
 template <int BITS, int NSF, int PD>
-struct BBuf {  // down (expert, row group) items + one fc2 row
+struct BBuf {  // down (expert, row group) items
   uint4 q[PD];
   uint16_t s[PD], b[PD];
   int k[PD], jr[PD];
   bool bad[PD];
   bool ok[PD];
-  uint4 fr[NSF];
-  uint16_t fb;
 };
 
-// Row r (r < NH) of this wave's head rows (fc1 rows, then linear rows), and its fc2 / router row.
+// Head rows are numbered fc1 rows first (0..H-1), then linear rows (H..H+E-1); row r (r < NH) of
+// a wave's head rows is head_row(r).  The wave that computes linear row e also computes fc2 row e
+// (lin_row), so the linear output never leaves its registers; with H a multiple of the workgroup
+// count those waves are the ones without an fc1 row.  e_row: the wave's router row.
 __device__ __forceinline__ int head_row(const StepParams& p, int r, int wg, int cw) { return (r * MW + cw) * p.G + wg; }
 __device__ __forceinline__ int e_row(const StepParams& p, int wg, int cw) { return cw * p.G + wg; }
+template <int NH>
+__device__ __forceinline__ int lin_row(const StepParams& p, int wg, int cw) {
+#pragma unroll
+  for (int r = 0; r < NH; ++r) {
+    const int j = head_row(p, r, wg, cw);
+    if (j >= p.H && j < p.H + p.E) return j - p.H;
+  }
+  return -1;
+}
 
-template <int BITS, int PG, int NSH, int GU, int NH>
-__device__ __forceinline__ void issue_A(const StepParams& p, const LayerView& v, const int* re, const int* prev,
-                                        int wg, int cw, int lane, ABuf<BITS, PG, NSH, GU, NH>& a) {
+// Loads of phase A of layer l, and the fc2 row of the head of layer l-1 when fc2_of_prev (the
+// second half of that head runs in this phase).  Descriptor fields are scalar loads.
+template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
+__device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* re, const int* prev, bool fc2_of_prev,
+                                        int wg, int cw, int lane, ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
+  const layer_cptr D = layer_at(p, l);
   const int gw = wg * MW + cw;
   const int wpr = p.d * BITS / 32, ngr = p.d >> p.lg2g;
   const int items = p.K * p.I;
@@ -285,16 +309,16 @@ __device__ __forceinline__ void issue_A(const StepParams& p, const LayerView& v,
     for (int q = 0; q < PG; ++q) {
       const int seg = lane + q * WAVE;
       const size_t wo = row * wpr + (size_t)seg * 4;
-      a.qg[u][q] = *reinterpret_cast<const uint4*>(v.gate.q + wo);
-      a.qu[u][q] = *reinterpret_cast<const uint4*>(v.up.q + wo);
+      a.qg[u][q] = *reinterpret_cast<const uint4*>(D->experts.gate.q + wo);
+      a.qu[u][q] = *reinterpret_cast<const uint4*>(D->experts.up.q + wo);
       const size_t go = row * ngr + ((seg * SegT<BITS>::COLS) >> p.lg2g);
-      a.sg[u][q] = v.gate.scales[go];
-      a.bg[u][q] = v.gate.biases[go];
-      a.su[u][q] = v.up.scales[go];
-      a.bu[u][q] = v.up.biases[go];
+      a.sg[u][q] = D->experts.gate.scales[go];
+      a.bg[u][q] = D->experts.gate.biases[go];
+      a.su[u][q] = D->experts.up.scales[go];
+      a.bu[u][q] = D->experts.up.biases[go];
     }
   }
-  if (v.head) {
+  if (has_head(p, l)) {
     // K-hot gather: lane j < K reads row cur[j] of the routing table, lane K <= j < 2K row
     // E + prev[j - K] (none at the first token); other lanes re-read row cur[0] and add 0.
     const int j = lane < 2 * p.K ? lane : 0;
@@ -311,20 +335,30 @@ __device__ __forceinline__ void issue_A(const StepParams& p, const LayerView& v,
       if (row >= p.H + p.E) break;  // uniform over the wave
       const bool fc1 = row < p.H;
       const int c = fc1 ? row : row - p.H;
-      const uint16_t* W = (fc1 ? v.fc1_x : v.lin_x) + (size_t)c * p.d;
+      const uint16_t* W = (fc1 ? D->head.fc1_x : D->head.lin_x) + (size_t)c * p.d;
 #pragma unroll
       for (int sg = 0; sg < NSH; ++sg) a.hr[r][sg] = *reinterpret_cast<const uint4*>(W + (size_t)(lane + sg * WAVE) * 8);
-      const uint16_t* rtab = fc1 ? v.fc1_r : v.lin_r;
+      const uint16_t* rtab = fc1 ? D->head.fc1_r : D->head.lin_r;
       a.kh[r] = rtab[(size_t)trow * (fc1 ? p.H : p.E) + c];
-      const uint16_t* bias = fc1 ? v.fc1_b : v.lin_b;
+      const uint16_t* bias = fc1 ? D->head.fc1_b : D->head.lin_b;
       a.hb[r] = bias ? bias[c] : *p.zero16;
     }
+  }
+  const int row = lin_row<NH>(p, wg, cw);
+  if (fc2_of_prev && row >= 0) {  // uniform over the wave
+    const uint16_t* fc2 = layer_at(p, l - 1)->head.fc2;
+    const uint16_t* fc2_b = layer_at(p, l - 1)->head.fc2_b;
+#pragma unroll
+    for (int sg = 0; sg < NSF; ++sg)
+      a.fr[sg] = *reinterpret_cast<const uint4*>(fc2 + (size_t)row * p.H + (size_t)(lane + sg * WAVE) * 8);
+    a.fb = fc2_b ? fc2_b[row] : *p.zero16;
   }
 }
 
 template <int BITS, int NSF, int PD>
-__device__ __forceinline__ void issue_B(const StepParams& p, const LayerView& v, const int* re, int wg, int cw, int lane,
+__device__ __forceinline__ void issue_B(const StepParams& p, int l, const int* re, int wg, int cw, int lane,
                                         BBuf<BITS, NSF, PD>& b) {
+  const layer_cptr D = layer_at(p, l);
   const int wpr = p.I * BITS / 32, ngr = p.I >> p.lg2g;
   const int RPI = WAVE / p.Ldn, slot = lane / p.Ldn;
   const int ls = min(lane % p.Ldn, p.I * BITS / 128 - 1);
@@ -341,17 +375,10 @@ __device__ __forceinline__ void issue_B(const StepParams& p, const LayerView& v,
     b.jr[u] = q * RPI + slot;
     const int j = min(wg * p.DR + b.jr[u], p.d - 1);
     const size_t row = (size_t)e * p.d + j;
-    b.q[u] = *reinterpret_cast<const uint4*>(v.down.q + row * wpr + (size_t)ls * 4);
+    b.q[u] = *reinterpret_cast<const uint4*>(D->experts.down.q + row * wpr + (size_t)ls * 4);
     const size_t go = row * ngr + ((ls * SegT<BITS>::COLS) >> p.lg2g);
-    b.s[u] = v.down.scales[go];
-    b.b[u] = v.down.biases[go];
-  }
-  const int row = e_row(p, wg, cw);
-  if (v.head && row < p.E) {  // uniform over the wave
-#pragma unroll
-    for (int sg = 0; sg < NSF; ++sg)
-      b.fr[sg] = *reinterpret_cast<const uint4*>(v.fc2 + (size_t)row * p.H + (size_t)(lane + sg * WAVE) * 8);
-    b.fb = v.fc2_b ? v.fc2_b[row] : *p.zero16;
+    b.s[u] = D->experts.down.scales[go];
+    b.b[u] = D->experts.down.biases[go];
   }
 }
 
@@ -359,9 +386,9 @@ struct StepShared {
   uint16_t h[2][LDS_D];
   float act[LDS_ACT];
   float g[LDS_H];
-  float lin[LDS_E];
   float logit[LDS_E];
   float part[LDS_PART];
+  float aout[MW * 4];   // this workgroup's SwiGLU outputs of the phase, gathered for one store
   float scale[2];
   int route_e[LDS_LK];  // this token's routing of every layer: [l * K + k]
   float route_w[LDS_LK];
@@ -377,9 +404,6 @@ struct StepCtx {
   __device__ uint32_t tag(int ph) const { return ((epoch << 10) | (uint32_t)ph) ^ TAG_SALT; }
 };
 
-__device__ __forceinline__ bool has_head(const StepParams& p, int l) {
-  return l + 1 < p.L && layer_at(p, l)->head.fc1_x != nullptr;
-}
 __device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
   return p.bootstrap || l == 0 || !has_head(p, l - 1);
 }
@@ -394,7 +418,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     if (l == 0) {
       for (int m = lane; m < dh; m += WAVE) hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
     } else {
-      ll_wait(p.ll_h + (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) { hw[i] = v; });
+      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) { hw[i] = v; });
     }
     float sq = 0.f;
     for (int m = lane; m < dh; m += WAVE) {
@@ -405,7 +429,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     if (lane == 0) sm.scale[hb] = 1.f / sqrtf(sq / (float)p.d + RMS_EPS);
     lds_barrier();  // B1: h_l ready
     if (self_routed(p, l)) {
-      ll_wait(p.ll_logits, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
+      ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
       int e;
       float w;
       wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
@@ -420,19 +444,20 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       lds_barrier();  // B2: routing of layer l ready
     }
     const uint32_t tA = c.tag(3 * l + 1);
-    ll_wait(p.ll_act, p.K * p.I, tA, p.err, failed, [&](int i, uint32_t v) { sm.act[i] = __uint_as_float(v); });
-    if (has_head(p, l)) {
-      ll_wait(p.ll_g, p.H, tA, p.err, failed, [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
-      ll_wait(p.ll_lin, p.E, tA, p.err, failed, [&](int i, uint32_t v) { sm.lin[i] = __uint_as_float(v); });
-    }
-    lds_barrier();  // B3: act (and head fc1 / linear outputs) ready
+    lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
+    ll_wait(p.ll_act, 0, p.K * p.I, tA, p.err, failed, [&](int i, uint32_t v) { sm.act[i] = __uint_as_float(v); });
+    lds_barrier();  // B3: act ready
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
+    // The head's hidden vector g_l feeds its fc2 rows in phase A of layer l+1; fetching it here
+    // overlaps the wait for h_{l+1} instead of lengthening the act exchange.
+    if (has_head(p, l))
+      ll_wait(p.ll_g, 0, p.H, tA, p.err, failed, [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
   }
   // Top-K of every head, off the token's critical path: head l predicts layer l+1's routing for
   // the next token; workgroup l % G handles head l.
   for (int l = c.wg; l + 1 < p.L; l += p.G) {
     if (!has_head(p, l)) continue;
-    ll_wait(p.ll_hlog + (size_t)l * p.E, p.E, c.tag(3 * l + 2), p.err, failed,
+    ll_wait(p.ll_hlog, (size_t)l * p.E, p.E, c.tag(3 * l + 2), p.err, failed,
             [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
     int e;
     float w;
@@ -445,26 +470,21 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
 }
 
 // Waves 1..MW: the arithmetic, with each phase's weight loads issued one phase early.
-template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
 __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   using GS = SegT<BITS>;
-  constexpr int NH = NH_MAX;
-  const int lane = c.lane, cw = c.cw, gw = c.gw, wg = c.wg, dh = p.d / 2, K = p.K;
+  const int lane = c.lane, cw = c.cw, wg = c.wg, dh = p.d / 2, K = p.K;
   const __amdgpu_buffer_rsrc_t ws = buffer_of(p.ws, p.ws_bytes);
   const __amdgpu_buffer_rsrc_t hout = buffer_of(p.h_out, (uint32_t)p.d * 2);
   const bool lead = lane == 0;
-  ABuf<BITS, PG, NSH, GU, NH> A;
+  ABuf<BITS, PG, NSH, NSF, GU, NH> A;
   BBuf<BITS, NSF, PD> B;
-  LayerView vn = layer_view(p, 0);
-  bool self_n = true;
+  float lin_keep = 0.f, lin_keep_next = 0.f;  // this wave's linear-row output of heads l-1 and l
   for (int l = 0; l < p.L; ++l) {
-    const LayerView v = vn;
-    const bool self = self_n;
-    if (l + 1 < p.L) {
-      vn = layer_view(p, l + 1);
-      self_n = p.bootstrap || !v.head;
-    }
-    const bool prefetch = l + 1 < p.L && !self_n;
+    const bool self = self_routed(p, l);
+    const bool head = has_head(p, l);
+    const bool fc2_now = l > 0 && has_head(p, l - 1);  // fc2 of head l-1 runs in this layer
+    const bool prefetch = l + 1 < p.L && !self_routed(p, l + 1);
     const int hb = l & 1;
     lds_barrier();  // B1
     const float scale = sm.scale[hb];
@@ -473,7 +493,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       // R_l: at most one router row per wave -> tagged logit
       const int r = e_row(p, wg, cw);
       if (r < p.E) {  // uniform over the wave
-        const uint16_t* W = v.router + (size_t)r * p.d;
+        const uint16_t* W = layer_at(p, l)->router + (size_t)r * p.d;
         float acc = 0.f;
 #pragma unroll
         for (int sg = 0; sg < NSH; ++sg) {
@@ -486,87 +506,101 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           acc = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), acc, false);
         }
         acc = wave_sum(acc) * scale;
-        ll_put(ws, p, p.ll_logits + r, lead, __float_as_uint(acc), c.tag(3 * l));
+        ll_put(ws, p, p.ll_logits, r, lead, __float_as_uint(acc), c.tag(3 * l));
       }
       lds_barrier();  // B2
-      issue_A<BITS, PG, NSH, GU, NH>(p, v, sm.route_e + l * K, c.prev_i ? sm.prev_e + l * K : nullptr, wg, cw, lane, A);
-      issue_B<BITS, NSF, PD>(p, v, sm.route_e + l * K, wg, cw, lane, B);
+      issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l, sm.route_e + l * K, c.prev_i ? sm.prev_e + l * K : nullptr, fc2_now,
+                                          wg, cw, lane, A);
+      issue_B<BITS, NSF, PD>(p, l, sm.route_e + l * K, wg, cw, lane, B);
     }
 
-    // ---- A_l: gate/up + SwiGLU, head fc1 (+GELU) and linear rows ----
+    // ---- A_l: gate/up + SwiGLU, then linear and fc1 rows of head l, then fc2 rows of head l-1 ----
+    // In order of urgency: the SwiGLU outputs gate the act exchange, g_l is needed a phase later,
+    // and the head logits only at the end of the token, so they are computed while the exchange
+    // is in flight.  Partials of one stage are reduced together (interleaved DPP chains).
     {
       const uint32_t tA = c.tag(3 * l + 1);
-      uint32_t xp[PG][GS::PAIRS];
-      float sx[PG][2], sq = 0.f;
+      {
+        float red[2 * GU];
+        uint32_t xp[PG][GS::PAIRS];
+        float sx[PG][2], sq = 0.f;
 #pragma unroll
-      for (int q = 0; q < PG; ++q) load_xpairs<BITS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
+        for (int q = 0; q < PG; ++q) load_xpairs<BITS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
 #pragma unroll
-      for (int u = 0; u < GU; ++u) {
-        float pg = 0.f, pu = 0.f;
+        for (int u = 0; u < GU; ++u) {
+          float pg = 0.f, pu = 0.f;
 #pragma unroll
-        for (int q = 0; q < PG; ++q) {
-          float d0 = 0.f, d1 = 0.f;
-          dot_segment<BITS>(A.qg[u][q], xp[q], d0, d1);
-          pg += h2f(A.sg[u][q]) * (d0 + d1) + h2f(A.bg[u][q]) * (sx[q][0] + sx[q][1]);
-          d0 = d1 = 0.f;
-          dot_segment<BITS>(A.qu[u][q], xp[q], d0, d1);
-          pu += h2f(A.su[u][q]) * (d0 + d1) + h2f(A.bu[u][q]) * (sx[q][0] + sx[q][1]);
+          for (int q = 0; q < PG; ++q) {
+            float d0 = 0.f, d1 = 0.f;
+            dot_segment<BITS>(A.qg[u][q], xp[q], d0, d1);
+            pg += h2f(A.sg[u][q]) * (d0 + d1) + h2f(A.bg[u][q]) * (sx[q][0] + sx[q][1]);
+            d0 = d1 = 0.f;
+            dot_segment<BITS>(A.qu[u][q], xp[q], d0, d1);
+            pu += h2f(A.su[u][q]) * (d0 + d1) + h2f(A.bu[u][q]) * (sx[q][0] + sx[q][1]);
+          }
+          red[2 * u] = pg;
+          red[2 * u + 1] = pu;
         }
-        pg = wave_sum(pg) * scale;
-        pu = wave_sum(pu) * scale;
-        const float a = pg / (1.f + expf(-pg)) * pu;
-        ll_put(ws, p, p.ll_act + A.item[u], lead && A.ok[u], __float_as_uint(A.bad[u] ? quiet_nan() : a), tA);
+        wave_sum_n(red);
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+          const float pg = red[2 * u] * scale, pu = red[2 * u + 1] * scale;
+          const float a = pg / (1.f + expf(-pg)) * pu;
+          if (lead) sm.aout[cw * GU + u] = A.bad[u] ? quiet_nan() : a;
+        }
+        // the workgroup's MW*GU consecutive outputs leave as one store of whole lines (partial
+        // lines written by many waves were measured slower to reach the readers)
+        lds_barrier();  // BA
+        if (cw == 0) {
+          const int j = min(lane, MW * GU - 1);
+          const int item = wg * MW * GU + j;
+          ll_put(ws, p, p.ll_act, min(item, p.K * p.I - 1), lane < MW * GU && item < p.K * p.I,
+                 __float_as_uint(sm.aout[j]), tA);
+        }
       }
-      if (v.head) {
+      // first half of this layer's head: fc1 rows (+GELU, sent) and the linear row (kept)
+      if (head && head_row(p, 0, wg, cw) < p.H + p.E) {  // uniform over the wave
+        float red[2 * NH];
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          red[2 * r] = 0.f;
+          red[2 * r + 1] = 0.f;
+          if (head_row(p, r, wg, cw) < p.H + p.E) {  // uniform over the wave
+            float acc = 0.f;
+#pragma unroll
+            for (int sg = 0; sg < NSH; ++sg) {
+              const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)(lane + sg * WAVE) * 8);
+              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
+              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
+              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
+              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
+            }
+            red[2 * r] = acc;
+            red[2 * r + 1] = A.khm == 1 ? h2f(A.kh[r]) : (A.khm == 2 ? quiet_nan() : 0.f);
+          }
+        }
+        wave_sum_n(red);
 #pragma unroll
         for (int r = 0; r < NH; ++r) {
           const int row = head_row(p, r, wg, cw);
-          if (row >= p.H + p.E) break;  // uniform over the wave
-          float acc = 0.f;
-#pragma unroll
-          for (int sg = 0; sg < NSH; ++sg) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)(lane + sg * WAVE) * 8);
-            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
-            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
-            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
-            acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
+          if (row < p.H + p.E) {  // uniform over the wave
+            const float val = red[2 * r] * scale + red[2 * r + 1] + h2f(A.hb[r]);
+            if (row >= p.H)
+              lin_keep_next = val;  // linear row: this wave adds it to its fc2 row in the next layer
+            else
+              ll_put(ws, p, p.ll_g, row, lead, __float_as_uint(gelu_erf(val)), tA);
           }
-          const float kh = A.khm == 1 ? h2f(A.kh[r]) : (A.khm == 2 ? quiet_nan() : 0.f);
-          const float val = wave_sum(acc) * scale + wave_sum(kh) + h2f(A.hb[r]);
-          const bool fc1 = row < p.H;
-          ll_put(ws, p, fc1 ? p.ll_g + row : p.ll_lin + (row - p.H), lead, __float_as_uint(fc1 ? gelu_erf(val) : val), tA);
         }
       }
-    }
-    if (prefetch)  // weights of A_{l+1}, one phase early
-      issue_A<BITS, PG, NSH, GU, NH>(p, vn, sm.route_e + (l + 1) * K, c.prev_i ? sm.prev_e + (l + 1) * K : nullptr,
-                                     wg, cw, lane, A);
-    lds_barrier();  // B3
-
-    // ---- B_l: down partials of this workgroup's rows, head fc2 rows ----
-    {
-      const int S = p.I * BITS / 128;
-      const int ls = lane % p.Ldn;
-      const int lsc = min(ls, S - 1);
-#pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        uint32_t xh[GS::PAIRS], xl[GS::PAIRS];
-        float sx[2];
-        load_xpairs_f32<BITS>(sm.act + (size_t)B.k[u] * p.I + (size_t)lsc * GS::COLS, xh, xl, sx);
-        float d0 = 0.f, d1 = 0.f;
-        dot_segment_split<BITS>(B.q[u], xh, xl, d0, d1);
-        float po = ls < S ? h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * (sx[0] + sx[1]) : 0.f;
-        po = group_sum_last(po, p.Ldn);
-        if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
-      }
-      const int row = e_row(p, wg, cw);
-      if (v.head && row < p.E) {  // uniform over the wave
+      // second half of the previous layer's head: fc2 row `er` of this wave
+      const int er = lin_row<NH>(p, wg, cw);
+      if (fc2_now && er >= 0) {  // uniform over the wave
         float acc = 0.f;
 #pragma unroll
         for (int sg = 0; sg < NSF; ++sg) {
           const float* gp = sm.g + (size_t)(lane + sg * WAVE) * 8;
-          const half2_t w0 = as_h2(B.fr[sg].x), w1 = as_h2(B.fr[sg].y), w2 = as_h2(B.fr[sg].z),
-                        w3 = as_h2(B.fr[sg].w);
+          const half2_t w0 = as_h2(A.fr[sg].x), w1 = as_h2(A.fr[sg].y), w2 = as_h2(A.fr[sg].z),
+                        w3 = as_h2(A.fr[sg].w);
           acc = fmaf((float)w0.x, gp[0], acc);
           acc = fmaf((float)w0.y, gp[1], acc);
           acc = fmaf((float)w1.x, gp[2], acc);
@@ -576,12 +610,32 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           acc = fmaf((float)w3.x, gp[6], acc);
           acc = fmaf((float)w3.y, gp[7], acc);
         }
-        const float val = wave_sum(acc) + sm.lin[row] + h2f(B.fb);
-        ll_put(ws, p, p.ll_hlog + (size_t)l * p.E + row, lead, __float_as_uint(val), c.tag(3 * l + 2));
+        ll_put(ws, p, p.ll_hlog, (size_t)(l - 1) * p.E + er, lead, __float_as_uint(wave_sum(acc) + lin_keep + h2f(A.fb)),
+               c.tag(3 * (l - 1) + 2));
+      }
+      lin_keep = lin_keep_next;
+    }
+    if (prefetch)  // weights of A_{l+1}, one phase early
+      issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K,
+                                          c.prev_i ? sm.prev_e + (l + 1) * K : nullptr, head, wg, cw, lane, A);
+    lds_barrier();  // B3
+
+    // ---- B_l: down partials of this workgroup's rows ----
+    {
+      const int S = p.I * BITS / 128;
+      const int ls = lane % p.Ldn;
+      const int lsc = min(ls, S - 1);
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        float d = 0.f, sx = 0.f;
+        dot_segment_f32<BITS>(B.q[u], sm.act + (size_t)B.k[u] * p.I + (size_t)lsc * GS::COLS, d, sx);
+        float po = ls < S ? h2f(B.s[u]) * d + h2f(B.b[u]) * sx : 0.f;
+        po = group_sum_last(po, p.Ldn);
+        if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
       }
     }
     if (prefetch)  // weights of B_{l+1}, one phase early
-      issue_B<BITS, NSF, PD>(p, vn, sm.route_e + (l + 1) * K, wg, cw, lane, B);
+      issue_B<BITS, NSF, PD>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, B);
     lds_barrier();  // B4
     // ---- combine + residual of this workgroup's rows -> h_{l+1} (wave 1; lane = row) ----
     if (cw == 0) {
@@ -598,14 +652,14 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         // lane m sends word m (rows 2m, 2m+1)
         const int m = min(lane, nrows / 2 - 1);
         const uint32_t lo = __shfl(yb, 2 * m, WAVE), hi = __shfl(yb, 2 * m + 1, WAVE);
-        ll_put(ws, p, p.ll_h + (size_t)(l + 1) * dh + wg * (p.DR / 2) + m, lane < nrows / 2, lo | (hi << 16),
+        ll_put(ws, p, p.ll_h, (size_t)(l + 1) * dh + wg * (p.DR / 2) + m, lane < nrows / 2, lo | (hi << 16),
                c.tag(3 * l + 2));
       }
     }
   }
 }
 
-template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
 __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   __shared__ __attribute__((aligned(16))) StepShared sm;
   StepCtx c;
@@ -633,7 +687,7 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   } else {
     // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
     __builtin_amdgcn_s_setprio(2);
-    compute_role<BITS, PG, NSH, NSF, GU, PD>(p, c, sm);
+    compute_role<BITS, PG, NSH, NSF, GU, PD, NH>(p, c, sm);
   }
   if (c.wg == 0 && threadIdx.x == 0) *p.epoch = c.epoch + 1;
 }
@@ -646,7 +700,7 @@ struct StepPlan {
   int G, GU, NH, NR, NO, DR, DI, PD, Ldn, PG, NSH, NSF;
 };
 
-static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD);
+static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD, int NH);
 
 static StepPlan plan_step(const moe_decode_stack& st, int cus) {
   StepPlan pl{};
@@ -684,26 +738,25 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
     pl.NSF = 1;
     pl.NH = 0;
   }
-  pl.ok = has_variant(bits, pl.PG, pl.NSH, pl.NSF, pl.GU, pl.PD);
+  pl.NH = pl.NH < 1 ? 1 : pl.NH;  // a variant holds at least one head-row slot (unused without heads)
+  pl.ok = has_variant(bits, pl.PG, pl.NSH, pl.NSF, pl.GU, pl.PD, pl.NH);
   return pl;
 }
 
 struct StepWs {
-  size_t epoch, err, zero, logits, act, g, lin, hlog, h, total;
+  size_t epoch, err, zero, logits, act, g, hlog, h, total;
 };
 static StepWs step_ws(const moe_decode_stack& st) {
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   StepWs w{};
   w.epoch = 0;
   w.err = 4;
   w.zero = 8;  // 8 bytes that stay zero
   w.logits = 256;
-  w.act = w.logits + al((size_t)st.E * 8);
-  w.g = w.act + al((size_t)st.K * st.d_ff * 8);
-  w.lin = w.g + al((size_t)(st.d_hidden > 0 ? st.d_hidden : 1) * 8);
-  w.hlog = w.lin + al((size_t)st.E * 8);
-  w.h = w.hlog + al((size_t)st.L * st.E * 8);
-  w.total = w.h + al((size_t)(st.L + 1) * (st.d_model / 2) * 8);
+  w.act = w.logits + ll_bytes(st.E);
+  w.g = w.act + ll_bytes((size_t)st.K * st.d_ff);
+  w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? st.d_hidden : 1);
+  w.h = w.hlog + ll_bytes((size_t)st.L * st.E);
+  w.total = w.h + ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
   return w;
 }
 
@@ -714,10 +767,10 @@ static int device_cus() {
   return cus;
 }
 
-template <int BITS, int PG, int NSH, int NSF, int GU, int PD>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
 static hipError_t go(hipStream_t s, const StepParams& p) {
   int occ = 0;
-  auto k = k_decode_step<BITS, PG, NSH, NSF, GU, PD>;
+  auto k = k_decode_step<BITS, PG, NSH, NSF, GU, PD, NH>;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, NTHREADS, 0);
   if (e != hipSuccess) return e;
   if (occ < 1) return hipErrorInvalidConfiguration;  // every workgroup must be resident at once
@@ -725,25 +778,26 @@ static hipError_t go(hipStream_t s, const StepParams& p) {
 }
 
 // Instantiated shapes: (bits, gate/up segments per lane, fp16 segments per lane of a d-row and of
-// an H-row, gate/up pairs per wave, down items per wave).  The counts are exact, so every compute
-// wave issues the same loads.
+// an H-row, gate/up pairs per wave, down items per wave, head-row slots per wave).  The counts
+// are exact, so every compute wave issues the same loads.
 #define MOE_STEP_VARIANTS(X)                                                                       \
-  X(4, 1, 4, 2, 2, 2) /* d 2048, I 512, K 4, E 256, head hidden 1024 */                            \
-  X(4, 1, 4, 1, 4, 4) /* d 2048, I 512, K 8, E 256, no heads */                                    \
-  X(4, 2, 8, 1, 4, 8) /* d 4096, I 1024, K 4, E 512, int4, no heads */                             \
-  X(2, 1, 8, 1, 4, 4) /* d 4096, I 1024, K 4, E 512, int2, no heads */
+  X(4, 1, 4, 2, 1, 1, 1) /* d 2048, I 512, K 4, E 256, head hidden 1024 */                         \
+  X(4, 1, 4, 1, 2, 2, 1) /* d 2048, I 512, K 8, E 256, no heads */                                 \
+  X(4, 2, 8, 1, 2, 4, 1) /* d 4096, I 1024, K 4, E 512, int4, no heads */                          \
+  X(2, 1, 8, 1, 2, 2, 1) /* d 4096, I 1024, K 4, E 512, int2, no heads */
 
-static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD) {
-#define MOE_STEP_HAS(B_, PG_, NSH_, NSF_, GU_, PD_) \
-  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && GU == GU_ && PD == PD_) return true;
+static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD, int NH) {
+#define MOE_STEP_HAS(B_, PG_, NSH_, NSF_, GU_, PD_, NH_) \
+  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && GU == GU_ && PD == PD_ && NH == NH_) return true;
   MOE_STEP_VARIANTS(MOE_STEP_HAS)
 #undef MOE_STEP_HAS
   return false;
 }
 
 static hipError_t dispatch(hipStream_t s, const StepParams& p, int bits, int PG, int NSH, int NSF) {
-#define MOE_STEP_GO(B_, PG_, NSH_, NSF_, GU_, PD_) \
-  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && p.GU == GU_ && p.PD == PD_) return go<B_, PG_, NSH_, NSF_, GU_, PD_>(s, p);
+#define MOE_STEP_GO(B_, PG_, NSH_, NSF_, GU_, PD_, NH_)                                          \
+  if (bits == B_ && PG == PG_ && NSH == NSH_ && NSF == NSF_ && p.GU == GU_ && p.PD == PD_ && p.NH == NH_) \
+    return go<B_, PG_, NSH_, NSF_, GU_, PD_, NH_>(s, p);
   MOE_STEP_VARIANTS(MOE_STEP_GO)
 #undef MOE_STEP_GO
   return hipErrorInvalidValue;
@@ -791,7 +845,6 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.ll_logits = (uint64_t*)(b + w.logits);
   p.ll_act = (uint64_t*)(b + w.act);
   p.ll_g = (uint64_t*)(b + w.g);
-  p.ll_lin = (uint64_t*)(b + w.lin);
   p.ll_hlog = (uint64_t*)(b + w.hlog);
   p.ll_h = (uint64_t*)(b + w.h);
   p.epoch = (uint32_t*)(b + w.epoch);
