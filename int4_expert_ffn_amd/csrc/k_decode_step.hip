@@ -86,6 +86,14 @@ constexpr int CPOL_SC1 = 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+__device__ __forceinline__ void ll_put64(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* vec, size_t i,
+                                         bool on, uint64_t word) {
+  u32x2 v;
+  v.x = (uint32_t)word;
+  v.y = (uint32_t)(word >> 32);
+  const uint32_t off = (uint32_t)((const char*)ll_at(vec, i) - (const char*)p.ws);
+  __builtin_amdgcn_raw_buffer_store_b64(v, ws, on ? off : OFF_NONE, 0, CPOL_SC1);
+}
 __device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* vec, size_t i,
                                        bool on, uint32_t payload, uint32_t tag) {
   u32x2 v;
@@ -94,6 +102,17 @@ __device__ __forceinline__ void ll_put(__amdgpu_buffer_rsrc_t ws, const StepPara
   const uint32_t off = (uint32_t)((const char*)ll_at(vec, i) - (const char*)p.ws);
   __builtin_amdgcn_raw_buffer_store_b64(v, ws, on ? off : OFF_NONE, 0, CPOL_SC1);
 }
+
+// The SwiGLU outputs travel two to a word: each float32 rounded to its top 24 bits (sign,
+// exponent, 15 mantissa bits; round to nearest even, NaN and Inf kept) beside a 16-bit tag.  A
+// 16-bit significand keeps the chained decode well inside its tolerance (float16's 11 bits did
+// not), and half the words make the exchange one polling pass.
+__device__ __forceinline__ uint32_t f32_to_f24(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return u >> 8;  // Inf / NaN: truncate (a NaN stays a NaN)
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ float f24_to_f32(uint32_t v) { return __uint_as_float(v << 8); }
 __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -104,9 +123,11 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 // time: past WAIT_TICKS it raises the error word, sets `failed`, and every later wait of this
 // wave returns at once, so a grid that cannot make progress still finishes quickly (with
 // invalid results).
-template <class Sink>
+// TAGB: tag bits in the top of each word (32: a 32-bit payload; 16: a 48-bit payload).
+template <int TAGB = 32, class Sink>
 __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n, uint32_t tag, int* err, bool& failed,
                                         Sink sink) {
+  constexpr uint64_t PAY = (1ull << (64 - TAGB)) - 1;
   if (failed) return;
   const int lane = threadIdx.x % WAVE;
   constexpr uint64_t ALL = POLL_MAX == 64 ? ~0ull : (1ull << POLL_MAX) - 1;  // one bit per word slot of a lane
@@ -124,8 +145,8 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n
         if (!((done >> j) & 1u)) v[j] = ll_load(ll_at(src, q + j * WAVE));
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
-        if (!((done >> j) & 1u) && (uint32_t)(v[j] >> 32) == tag) {
-          sink(base + lane + j * WAVE, (uint32_t)v[j]);
+        if (!((done >> j) & 1u) && (uint32_t)(v[j] >> (64 - TAGB)) == tag) {
+          sink(base + lane + j * WAVE, v[j] & PAY);
           done |= 1ull << j;
         }
       if (__all(done == ALL)) break;
@@ -402,6 +423,9 @@ struct StepCtx {
   float *cur_w, *nxt_w;
   const int32_t* prev_i;
   __device__ uint32_t tag(int ph) const { return ((epoch << 10) | (uint32_t)ph) ^ TAG_SALT; }
+  // 16-bit tag of the packed act words: 9 bits of phase, 7 of the token counter.  Every act word
+  // is rewritten in every layer of every token, so a word 128 tokens old cannot still be there.
+  __device__ uint32_t tag16(int ph) const { return (((epoch & 0x7Fu) << 9) | (uint32_t)ph) ^ (TAG_SALT & 0xFFFFu); }
 };
 
 __device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
@@ -445,7 +469,10 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     }
     const uint32_t tA = c.tag(3 * l + 1);
     lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
-    ll_wait(p.ll_act, 0, p.K * p.I, tA, p.err, failed, [&](int i, uint32_t v) { sm.act[i] = __uint_as_float(v); });
+    ll_wait<16>(p.ll_act, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed, [&](int i, uint64_t v) {
+      sm.act[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
+      sm.act[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
+    });
     lds_barrier();  // B3: act ready
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
     // The head's hidden vector g_l feeds its fc2 rows in phase A of layer l+1; fetching it here
@@ -551,11 +578,12 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         // the workgroup's MW*GU consecutive outputs leave as one store of whole lines (partial
         // lines written by many waves were measured slower to reach the readers)
         lds_barrier();  // BA
-        if (cw == 0) {
-          const int j = min(lane, MW * GU - 1);
-          const int item = wg * MW * GU + j;
-          ll_put(ws, p, p.ll_act, min(item, p.K * p.I - 1), lane < MW * GU && item < p.K * p.I,
-                 __float_as_uint(sm.aout[j]), tA);
+        if (cw == 0) {  // lane j sends outputs 2j, 2j+1 of the workgroup as one packed word
+          const int j = min(lane, MW * GU / 2 - 1);
+          const int word = wg * MW * GU / 2 + j;
+          const uint64_t w = (uint64_t)f32_to_f24(sm.aout[2 * j]) | ((uint64_t)f32_to_f24(sm.aout[2 * j + 1]) << 24) |
+                             ((uint64_t)c.tag16(3 * l + 1) << 48);
+          ll_put64(ws, p, p.ll_act, min(word, p.K * p.I / 2 - 1), lane < MW * GU / 2 && 2 * word < p.K * p.I, w);
         }
       }
       // first half of this layer's head: fc1 rows (+GELU, sent) and the linear row (kept)
@@ -712,6 +740,7 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
   if (SI < 1 || SI > WAVE || (I * bits) % 128) return pl;
   if (bits == 2 && st.group < 64) return pl;  // a 2-bit segment must sit inside one group
   if (K > 8 || K * I > LDS_ACT || E > LDS_E || st.L * K > LDS_LK) return pl;
+  if (3 * st.L > 512) return pl;  // phases must fit the 9 phase bits of the packed act tags
   pl.Ldn = 1;
   while (pl.Ldn < SI) pl.Ldn <<= 1;
   const int RPI = WAVE / pl.Ldn;
