@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+STEP_KERNEL_SOURCES = ("int4_expert_ffn_amd/csrc/k_decode_step.hip", "int4_expert_ffn_amd/csrc/moe_device.h",
+                       "int4_expert_ffn_amd/csrc/moe_launch.h", "include/moe.h")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_decode_step_decode35b_traffic.json")
 
 
 def log(msg):
@@ -57,6 +60,43 @@ def algorithmic_bytes(cfg):
     ffn_call = expert + 3 * d * 2 + K * 8          # x, r in; y out; idx, w
     total = cfg.L * expert + (cfg.L - 1) * head + E * d * 2 + cfg.L * vec
     return total, ffn_call
+
+
+def kernel_source_hash():
+    """sha256 over the sources the persistent kernel is built from (to tell whether a stored
+    counter record still describes the kernel that runs)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in STEP_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib):
+    """A plain device copy of `mib` MiB (reads and writes that many bytes), three times: the
+    reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def cpu_baseline(cfg, layers, syn, tokens=2):
@@ -99,7 +139,15 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each timed token directly instead of replaying a HIP graph (for counter profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -149,7 +197,10 @@ def main():
             if t % 3 == 1:                       # refill the inputs of tokens t, t+1, t+2
                 p = (t // 3 * 3) % n_pool
                 ring.copy_(pool[p:p + 3])
-            graphs[(t - 1) % 3].replay()
+            if callable(graphs):
+                graphs(t)
+            else:
+                graphs[(t - 1) % 3].replay()
 
     def timed(graphs, steps, warmup):
         warmup = -(-warmup // 3) * 3             # whole slot rotations keep tokens consecutive
@@ -170,6 +221,8 @@ def main():
     # the timed step: one persistent-kernel launch (moe_decode_step) per token
     stack = DecodeStack(layers, cfg.K, dev)
     graphs = capture(stack, True)
+    if args.eager:                               # same tokens, direct launches (graphs captured but unused)
+        graphs = lambda t: stack.step(t, ring[t % 3])
     wall, ev_ms, args.warmup = timed(graphs, args.steps, args.warmup)
     assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
     h_out = stack.h[cfg.L].float()
@@ -181,12 +234,15 @@ def main():
 
     # context: the same schedule as per-layer C-ABI calls (5 launches per layer)
     del graphs
-    stack2 = DecodeStack(layers, cfg.K, dev)
-    graphs2 = capture(stack2, False)
-    n2 = max(30, args.steps // 4)
-    wall2, ev2, _ = timed(graphs2, n2, 30)
-    per_layer_tok_s = n2 / wall2
-    del graphs2
+    per_layer_tok_s = None
+    if not args.no_per_layer:
+        stack2 = DecodeStack(layers, cfg.K, dev)
+        graphs2 = capture(stack2, False)
+        n2 = max(30, args.steps // 4)
+        wall2, ev2, _ = timed(graphs2, n2, 30)
+        per_layer_tok_s = round(n2 / wall2, 2)
+        del graphs2
+    traffic = stored_traffic()
 
     rec = {
         "metric": "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)",
@@ -219,11 +275,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": total_bytes,
             "avg_us": round(step_us, 2),
         },
-        "per_layer_calls": {"tokens_per_s": round(per_layer_tok_s, 2), "launches_per_token": 5 * cfg.L - 2,
+        "per_layer_calls": {"tokens_per_s": per_layer_tok_s, "launches_per_token": 5 * cfg.L - 2,
                             "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"},
     }
     if not args.no_cpu_baseline:
