@@ -203,9 +203,12 @@ typedef struct {
 size_t moe_decode_workspace_size(const moe_decode_stack* st);
 
 /* h_in[d] float16 (device): the token's input hidden state; h_out[d] float16 (device): the output
-   of layer L-1.  flags: MOE_TOPK_RENORM or 0 (applies to every top-K). */
+   of layer L-1.  h_layers: NULL, or [L+1][d] float16 (device) receiving every layer's input (row l,
+   row 0 = h_in) and the final output (row L), for inspection and layer-by-layer checking; 4-byte
+   aligned.  flags: MOE_TOPK_RENORM or 0 (applies to every top-K). */
 moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
-                           const uint16_t* h_in, uint16_t* h_out, void* workspace, size_t workspace_bytes);
+                           const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
+                           size_t workspace_bytes);
 
 const char* moe_status_string(moe_status s);
 

@@ -85,7 +85,7 @@ def _load():
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_decode_workspace_size": (sz, [ctypes.POINTER(moe_decode_stack)]),
-        "moe_decode_step": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, sz]),
+        "moe_decode_step": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, vp, sz]),
         "moe_version": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -237,10 +237,11 @@ def moe_decode_workspace_size(stack: "moe_decode_stack") -> int:
 
 
 def moe_decode_step(stack: "moe_decode_stack", token, flags, h_in, h_out, workspace, workspace_bytes=None,
-                    stream=None):
+                    stream=None, h_layers=None):
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     st = _lib.moe_decode_step(_stream(stream, h_in, h_out), ctypes.byref(stack), token, flags, _ptr(h_in, _f16(), "h_in"),
-                              _ptr(h_out, _f16(), "h_out"), _ptr(workspace, None, "workspace"), nbytes)
+                              _ptr(h_out, _f16(), "h_out"), _ptr(h_layers, _f16(), "h_layers"),
+                              _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_decode_step")
 
 

@@ -81,12 +81,14 @@ class DecodeStack:
             self._step = (desc, st, ws)
         return self._step
 
-    def step(self, t: int, h_in: torch.Tensor, h_out: Optional[torch.Tensor] = None):
+    def step(self, t: int, h_in: torch.Tensor, h_out: Optional[torch.Tensor] = None,
+             h_layers: Optional[torch.Tensor] = None):
         """Enqueue token t as one persistent-kernel launch reading h_in [d] and writing h_out
-        (default: self.h[L]).  Returns h_out."""
+        (default: self.h[L]); h_layers [L+1][d] float16, if given, receives every layer's input and
+        the output.  Returns h_out."""
         desc, st, ws = self._step_state()
         out = self.h[self.L] if h_out is None else h_out
-        L.moe_decode_step(st, t, self.topk_flags, h_in, out, ws)
+        L.moe_decode_step(st, t, self.topk_flags, h_in, out, ws, h_layers=h_layers)
         return out
 
     def step_error_word(self) -> int:

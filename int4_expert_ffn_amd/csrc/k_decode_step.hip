@@ -51,6 +51,7 @@ struct StepParams {
   const moe_decode_layer* layers;
   const uint16_t* h_in;
   uint16_t* h_out;
+  uint16_t* h_layers;  // NULL or [L+1][d]: every layer's input and the final output
   int32_t* ridx;
   float* rw;
   int slot, bootstrap;
@@ -441,6 +442,8 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     uint32_t* hw = reinterpret_cast<uint32_t*>(sm.h[hb]);
     if (l == 0) {
       for (int m = lane; m < dh; m += WAVE) hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
+      if (p.h_layers != nullptr && c.wg == 0)  // row 0 of the per-layer copies: the token's input
+        for (int m = lane; m < dh; m += WAVE) reinterpret_cast<uint32_t*>(p.h_layers)[m] = hw[m];
     } else {
       ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) { hw[i] = v; });
     }
@@ -503,6 +506,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
   const int lane = c.lane, cw = c.cw, wg = c.wg, dh = p.d / 2, K = p.K;
   const __amdgpu_buffer_rsrc_t ws = buffer_of(p.ws, p.ws_bytes);
   const __amdgpu_buffer_rsrc_t hout = buffer_of(p.h_out, (uint32_t)p.d * 2);
+  // per-layer copies of h: a zero-sized buffer when not asked for, so every store is dropped
+  const __amdgpu_buffer_rsrc_t hall = buffer_of(p.h_layers, p.h_layers ? (uint32_t)(p.L + 1) * p.d * 2 : 0u);
   const bool lead = lane == 0;
   ABuf<BITS, PG, NSH, NSF, GU, NH> A;
   BBuf<BITS, NSF, PD> B;
@@ -674,6 +679,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       float acc = 0.f;
       for (int k = 0; k < K; ++k) acc = fmaf(sm.route_w[l * K + k], sm.part[k * p.DR + jr], acc);
       const uint32_t yb = f2h(h2f(hl[j]) + acc);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)yb, hall, mine ? (uint32_t)((l + 1) * p.d + j) * 2 : OFF_NONE,
+                                            0, 0);
       if (l + 1 == p.L) {
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)yb, hout, mine ? (uint32_t)j * 2 : OFF_NONE, 0, 0);
       } else {
@@ -837,7 +844,7 @@ bool decode_step_supported(const moe_decode_stack& st) { return plan_step(st, 25
 size_t decode_step_workspace(const moe_decode_stack& st) { return step_ws(st).total; }
 
 hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
-                              const uint16_t* h_in, uint16_t* h_out, void* ws) {
+                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws) {
   const int G = device_cus();
   const StepPlan pl = plan_step(st, G);
   if (!pl.ok) return hipErrorInvalidValue;
@@ -866,6 +873,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.layers = st.layers;
   p.h_in = h_in;
   p.h_out = h_out;
+  p.h_layers = h_layers;
   p.ridx = st.route_idx;
   p.rw = st.route_w;
   p.slot = token % 3;

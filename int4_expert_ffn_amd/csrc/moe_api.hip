@@ -193,7 +193,8 @@ size_t moe_decode_workspace_size(const moe_decode_stack* st) {
 }
 
 moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
-                           const uint16_t* h_in, uint16_t* h_out, void* workspace, size_t workspace_bytes) {
+                           const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
+                           size_t workspace_bytes) {
   if (!st || !h_in || !h_out || !workspace || token < 0) return MOE_ERR_INVALID_ARG;
   if (flags & ~MOE_TOPK_RENORM) return MOE_ERR_INVALID_ARG;
   if (st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return MOE_ERR_INVALID_ARG;
@@ -203,10 +204,11 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
   if (st->d_model < 1 || st->d_model > MOE_MAX_D || st->d_ff < 1 || st->d_ff > MOE_MAX_D || st->d_hidden < 0)
     return MOE_ERR_INVALID_ARG;
   if (st->d_model % st->group || st->d_ff % st->group) return MOE_ERR_INVALID_ARG;
-  if (((uintptr_t)h_in & 3u) || ((uintptr_t)h_out & 3u) || ((uintptr_t)workspace & 255u)) return MOE_ERR_INVALID_ARG;
+  if (((uintptr_t)h_in & 3u) || ((uintptr_t)h_out & 3u) || ((uintptr_t)h_layers & 3u) || ((uintptr_t)workspace & 255u))
+    return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < decode_step_workspace(*st)) return MOE_ERR_INVALID_ARG;
   if (!decode_step_supported(*st)) return MOE_ERR_UNSUPPORTED;
-  return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, workspace));
+  return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace));
 }
 
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,

@@ -62,7 +62,7 @@ size_t grouped_workspace_extra(int T, int K, int E, int d);
 bool decode_step_supported(const moe_decode_stack& st);
 size_t decode_step_workspace(const moe_decode_stack& st);
 hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
-                              const uint16_t* h_in, uint16_t* h_out, void* ws);
+                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws);
 
 // combine -------------------------------------------------------------------------------------
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,

@@ -101,12 +101,13 @@ def test_prerouter_and_combine_reject():
     assert so(1 << 22, 16, 256, FAKE, FAKE, FAKE, FAKE) == INVALID
     assert so(4, 4, 256, FAKE, None, FAKE, FAKE) == INVALID
     st = lib_mod.moe_decode_stack(40, 256, 4, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
-    ds = lambda stk, tok=1, flags=1, ws=FAKE, wsb=1 << 40: L.moe_decode_step(None, ctypes.byref(stk), tok, flags, FAKE,
-                                                                           FAKE, ws, wsb)
+    ds = lambda stk, tok=1, flags=1, ws=FAKE, wsb=1 << 40, hl=None: L.moe_decode_step(
+        None, ctypes.byref(stk), tok, flags, FAKE, FAKE, hl, ws, wsb)
     assert ds(st, tok=-1) == INVALID
     assert ds(st, flags=2) == INVALID
     assert ds(st, wsb=64) == INVALID
     assert ds(st, ws=FAKE + 16) == INVALID
+    assert ds(st, hl=FAKE + 2) == INVALID      # per-layer copies must be 4-byte aligned
     bad = lib_mod.moe_decode_stack(40, 256, 9, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
     assert ds(bad) == UNSUP                     # K > 8 is not a persistent-kernel shape
     tiny = lib_mod.moe_decode_stack(1, 16, 2, 256, 128, 4, 32, 0, FAKE, FAKE, FAKE)

@@ -1,0 +1,115 @@
+"""GPU parity at full depth: the persistent whole-token kernel (moe_decode_step) over every layer of
+each decode configuration, in the launch configuration the benchmark times (and the per-layer C-ABI
+calls over the 40-layer stack), checked layer by layer against the fp64 oracle.
+
+Over 40 chained layers the float16 rounding of each layer's output is amplified like any
+perturbation of the chain, so two correct implementations drift apart end to end. The check is
+therefore teacher-forced, along the GPU's own trajectory: the kernel hands out every layer's input
+(h_layers), and per token and layer
+  * the routing the kernel used must equal the oracle's top-K of the same input (its own router on
+    self-routed layers; the previous token's head prediction otherwise), unless the oracle's logits
+    come closer than 1e-4 to a tie;
+  * the layer output must equal the oracle layer applied to the same input with that routing,
+    within max|y - y_ref| <= 2e-3 max|y_ref|;
+  * every head's prediction for the next token must equal the oracle head's top-K.
+The oracle regenerates on the CPU only the experts the tokens select, so the full stacks (10-54 GB
+on the GPU) stay checkable."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle as O
+from parity_util import GAP, TOL, ExpertCache, assert_rows_close, log
+from test_decode_step_gpu import build
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+FULL = {
+    "decode35b-L40": (S.CONFIGS["decode35b"], True),
+    "widek8-L24": (S.CONFIGS["widek8"], False),
+    "large-int4-L15": (S.CONFIGS["large-int4"], False),
+    "large-int2-L15": (S.CONFIGS["large-int2"], False),
+}
+
+
+@pytest.fixture(scope="module")
+def M():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_expert_ffn_amd as m
+    return m
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_topk(logits, idx_gpu, w_gpu, K, what):
+    """Index equality (unless near a tie) and weights close; returns 1 if compared, 0 if skipped."""
+    idx_ref, w_ref = O.route_topk(logits[None], K)
+    if O.topk_gaps(logits, K).min() < GAP:
+        return 0
+    assert np.array_equal(np.asarray(idx_gpu), idx_ref[0]), f"{what}: routing {idx_gpu} vs oracle {idx_ref[0]}"
+    np.testing.assert_allclose(np.asarray(w_gpu, dtype=np.float64), w_ref[0], atol=2e-5, err_msg=what)
+    return 1
+
+
+CASES = [(n, "step") for n in FULL] + [("decode35b-L40", "calls")]
+
+
+@pytest.mark.parametrize("name,path", CASES)
+def test_full_depth_layer_by_layer(M, name, path):
+    """path "step": one moe_decode_step launch per token (inputs of every layer via h_layers);
+    path "calls": the per-layer C-ABI calls (every layer's input kept in the stack)."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = FULL[name]
+    L, K, E = cfg.L, cfg.K, cfg.E
+    log(f"{name} ({path}): building {L} layers on the GPU")
+    syn, layers, heads_cpu, routers_cpu = build(M, cfg, heads)
+    stack = DecodeStack(layers, K, DEV)
+    hl = torch.empty((L + 1, cfg.d), dtype=torch.float16, device=DEV)
+    caches = [ExpertCache(syn, l) for l in range(L)]
+    routed = predicted = 0
+    prev_idx = None
+    for t in range(3):
+        h0 = syn.hidden(9000 + t, 1)[0]
+        if path == "step":
+            out = stack.step(t, h0.to(DEV), h_layers=hl)
+        else:
+            out = stack.token(t, h0.to(DEV))
+            hl = stack.h
+        torch.cuda.synchronize()
+        if path == "step":
+            assert stack.step_error_word() == 0
+        H = hl.cpu().numpy()
+        idx = stack.route_idx[t % 3].cpu().numpy()
+        w = stack.route_w[t % 3].cpu().numpy()
+        nxt_idx = stack.route_idx[(t + 1) % 3].cpu().numpy()
+        nxt_w = stack.route_w[(t + 1) % 3].cpu().numpy()
+        assert np.array_equal(H[0], h0.numpy()), "row 0 must be the token's input"
+        assert np.array_equal(H[L], out.cpu().numpy()), "row L must be the output"
+        for l in range(L):
+            x = O.rmsnorm(H[l])
+            self_routed = t == 0 or l == 0 or not heads
+            if self_routed:   # the layer's own router + top-K on this input
+                routed += _check_topk(O.router_logits(routers_cpu[l], x), idx[l], w[l], K, f"{name} t{t} l{l} router")
+            y_ref = O.f64(H[l]).copy()
+            for k in range(K):
+                y_ref += float(w[l][k]) * O.expert_ffn_packed(x, *caches[l](idx[l][k]), bits=cfg.bits, group=cfg.group)
+            assert_rows_close(H[l + 1][None], y_ref[None], tol=TOL, what=f"{name} t{t} layer {l} output")
+            if heads and l + 1 < L:   # head l: prediction of layer l+1 for token t+1
+                lg = O.prerouter_logits(x, idx[l], None if t == 0 else prev_idx[l], heads_cpu[l], E)
+                predicted += _check_topk(lg, nxt_idx[l + 1], nxt_w[l + 1], K, f"{name} t{t} head {l}")
+        prev_idx = idx
+        log(f"{name} ({path}): token {t} checked at all {L} layers")
+    log(f"{name} ({path}): {routed} router top-Ks and {predicted} head predictions compared (others near ties)")
+    assert routed >= L // 2
+    if heads:
+        assert predicted >= L
+    del stack, layers
+    _free()
