@@ -119,11 +119,14 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 }
 
 // Poll n tagged words until all carry `tag`; sink(i, payload) receives each word once.
-// Whole wave, POLL_MAX words per lane per pass, chunk after chunk: wider passes were measured
-// slower, as more readers hammer the same lines at once.  A wait is bounded in wall-clock
-// time: past WAIT_TICKS it raises the error word, sets `failed`, and every later wait of this
-// wave returns at once, so a grid that cannot make progress still finishes quickly (with
-// invalid results).
+// Whole wave, POLL_MAX words per lane per pass, chunk after chunk (wider passes were measured
+// slower: more readers hammer the same lines at once).  Two passes are in flight: the next one
+// is issued before the previous one is checked, so a word is seen about one memory round trip
+// after it lands rather than one and a half.  Every pass loads all POLL_MAX slots (slots past
+// the end re-read the last word and are ignored), which keeps the count of outstanding loads
+// exact for the compiler's waits.  A wait is bounded in wall-clock time: past WAIT_TICKS it raises
+// the error word, sets `failed`, and every later wait of this wave returns at once, so a grid
+// that cannot make progress still finishes quickly (with invalid results).
 // TAGB: tag bits in the top of each word (32: a 32-bit payload; 16: a 48-bit payload).
 template <int TAGB = 32, class Sink>
 __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n, uint32_t tag, int* err, bool& failed,
@@ -138,18 +141,26 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n
 #pragma unroll
     for (int j = 0; j < POLL_MAX; ++j)
       if (base + lane + j * WAVE >= n) done |= 1ull << j;
-    while (true) {
-      const size_t q = start + base + lane;
-      uint64_t v[POLL_MAX];
+    uint64_t a[POLL_MAX], b[POLL_MAX];
+    auto issue = [&](uint64_t (&v)[POLL_MAX]) {
 #pragma unroll
-      for (int j = 0; j < POLL_MAX; ++j)
-        if (!((done >> j) & 1u)) v[j] = ll_load(ll_at(src, q + j * WAVE));
+      for (int j = 0; j < POLL_MAX; ++j) v[j] = ll_load(ll_at(src, start + min(base + lane + j * WAVE, n - 1)));
+    };
+    auto check = [&](const uint64_t (&v)[POLL_MAX]) {
 #pragma unroll
       for (int j = 0; j < POLL_MAX; ++j)
         if (!((done >> j) & 1u) && (uint32_t)(v[j] >> (64 - TAGB)) == tag) {
           sink(base + lane + j * WAVE, v[j] & PAY);
           done |= 1ull << j;
         }
+    };
+    issue(a);
+    while (true) {
+      issue(b);
+      check(a);
+      if (__all(done == ALL)) break;
+      issue(a);
+      check(b);
       if (__all(done == ALL)) break;
       if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
         if (lane == 0) atomicAdd(err, 1);
@@ -406,7 +417,10 @@ __device__ __forceinline__ void issue_B(const StepParams& p, int l, const int* r
 
 struct StepShared {
   uint16_t h[2][LDS_D];
-  float act[LDS_ACT];
+  float act_f[LDS_ACT];  // the SwiGLU outputs of all K experts, as received
+  // the same as float16 hi + lo parts (act ~ hi + lo), in the permuted pair order of the down
+  // projection's code words (see act_pos); made by all compute waves together
+  uint16_t act_hi[LDS_ACT], act_lo[LDS_ACT];
   float g[LDS_H];
   float logit[LDS_E];
   float part[LDS_PART];
@@ -433,24 +447,44 @@ __device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
   return p.bootstrap || l == 0 || !has_head(p, l - 1);
 }
 
+// Position of SwiGLU output n (n = k*I + column) in the LDS hi/lo arrays: the down projection's
+// 16-byte segment of 32/BITS-column words pairs column j of a word with column j + PAIRS_PER_WORD
+// (the two halves of one decoded code pair), so the activations are stored pair by pair.
+template <int BITS>
+__device__ __forceinline__ int act_pos(int n) {
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD, CPW = 2 * PPW;
+  return (n & ~(CPW - 1)) + 2 * (n & (PPW - 1)) + ((n / PPW) & 1);
+}
+template <int BITS>
+__device__ __forceinline__ void put_act(StepShared& sm, int n, float f) {
+  const _Float16 hi = (_Float16)f;
+  const _Float16 lo = (_Float16)(f - (float)hi);
+  const int q = act_pos<BITS>(n);
+  sm.act_hi[q] = __builtin_bit_cast(uint16_t, hi);
+  sm.act_lo[q] = __builtin_bit_cast(uint16_t, lo);
+}
+
 // Wave 0 of every workgroup: waits for the vectors each phase needs and unpacks them into LDS.
+template <int BITS>
 __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   const int lane = c.lane, dh = p.d / 2;
   bool failed = false;
   for (int l = 0; l < p.L; ++l) {
     const int hb = l & 1;
     uint32_t* hw = reinterpret_cast<uint32_t*>(sm.h[hb]);
+    float sq = 0.f;  // sum of squares of h_l, accumulated as the words arrive
     if (l == 0) {
-      for (int m = lane; m < dh; m += WAVE) hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
+      for (int m = lane; m < dh; m += WAVE) {
+        hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
+        sq = __builtin_amdgcn_fdot2(as_h2(hw[m]), as_h2(hw[m]), sq, false);
+      }
       if (p.h_layers != nullptr && c.wg == 0)  // row 0 of the per-layer copies: the token's input
         for (int m = lane; m < dh; m += WAVE) reinterpret_cast<uint32_t*>(p.h_layers)[m] = hw[m];
     } else {
-      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) { hw[i] = v; });
-    }
-    float sq = 0.f;
-    for (int m = lane; m < dh; m += WAVE) {
-      const half2_t v = as_h2(hw[m]);
-      sq = __builtin_amdgcn_fdot2(v, v, sq, false);
+      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) {
+        hw[i] = v;
+        sq = __builtin_amdgcn_fdot2(as_h2(v), as_h2(v), sq, false);
+      });
     }
     sq = wave_sum(sq);
     if (lane == 0) sm.scale[hb] = 1.f / sqrtf(sq / (float)p.d + RMS_EPS);
@@ -473,10 +507,11 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     const uint32_t tA = c.tag(3 * l + 1);
     lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
     ll_wait<16>(p.ll_act, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed, [&](int i, uint64_t v) {
-      sm.act[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
-      sm.act[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
+      sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
+      sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
     });
     lds_barrier();  // B3: act ready
+    lds_barrier();  // B3b: act split into hi/lo pairs (by the compute waves)
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
     // The head's hidden vector g_l feeds its fc2 rows in phase A of layer l+1; fetching it here
     // overlaps the wait for h_{l+1} instead of lengthening the act exchange.
@@ -652,6 +687,9 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K,
                                           c.prev_i ? sm.prev_e + (l + 1) * K : nullptr, head, wg, cw, lane, A);
     lds_barrier();  // B3
+    // split act into float16 hi/lo pairs once per workgroup, every compute lane a few values
+    for (int n = cw * WAVE + lane; n < K * p.I; n += MW * WAVE) put_act<BITS>(sm, n, sm.act_f[n]);
+    lds_barrier();  // B3b
 
     // ---- B_l: down partials of this workgroup's rows ----
     {
@@ -660,9 +698,24 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       const int lsc = min(ls, S - 1);
 #pragma unroll
       for (int u = 0; u < PD; ++u) {
-        float d = 0.f, sx = 0.f;
-        dot_segment_f32<BITS>(B.q[u], sm.act + (size_t)B.k[u] * p.I + (size_t)lsc * GS::COLS, d, sx);
-        float po = ls < S ? h2f(B.s[u]) * d + h2f(B.b[u]) * sx : 0.f;
+        const size_t so = (size_t)B.k[u] * p.I + (size_t)lsc * GS::COLS;  // segment start (halves)
+        uint32_t hp[GS::PAIRS], lp[GS::PAIRS];
+#pragma unroll
+        for (int w = 0; w < GS::PAIRS / 4; ++w) {
+          const uint4 a = reinterpret_cast<const uint4*>(sm.act_hi + so)[w];
+          const uint4 b = reinterpret_cast<const uint4*>(sm.act_lo + so)[w];
+          hp[4 * w] = a.x, hp[4 * w + 1] = a.y, hp[4 * w + 2] = a.z, hp[4 * w + 3] = a.w;
+          lp[4 * w] = b.x, lp[4 * w + 1] = b.y, lp[4 * w + 2] = b.z, lp[4 * w + 3] = b.w;
+        }
+        float d0 = 0.f, d1 = 0.f, sx = 0.f;
+        dot_segment_split<BITS>(B.q[u], hp, lp, d0, d1);
+        const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int j = 0; j < GS::PAIRS; ++j) {
+          sx = __builtin_amdgcn_fdot2(as_h2(hp[j]), one, sx, false);
+          sx = __builtin_amdgcn_fdot2(as_h2(lp[j]), one, sx, false);
+        }
+        float po = ls < S ? h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * sx : 0.f;
         po = group_sum_last(po, p.Ldn);
         if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
       }
@@ -718,7 +771,7 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
     }
   }
   if (wave == 0) {
-    sync_role(p, c, sm);
+    sync_role<BITS>(p, c, sm);
   } else {
     // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
     __builtin_amdgcn_s_setprio(2);

@@ -216,39 +216,4 @@ __device__ __forceinline__ void dot_segment_split(uint4 q, const uint32_t* hp, c
   }
 }
 
-// One 16-byte segment against float32 activations, word by word (one word's columns live at a
-// time): d += sum_j c_j x_j with x split into float16 hi + lo as above, sx += sum_j x_j.  For a
-// segment that lies inside one quantisation group.
-template <int BITS>
-__device__ __forceinline__ void dot_segment_f32(uint4 q, const float* __restrict__ xs, float& d, float& sx) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
-  constexpr int CPW = 32 / BITS;
-  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v[CPW];
-#pragma unroll
-    for (int c = 0; c < CPW; c += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(xs + i * CPW + c);
-      v[c] = f.x;
-      v[c + 1] = f.y;
-      v[c + 2] = f.z;
-      v[c + 3] = f.w;
-    }
-#pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const float a = v[j], b = v[j + PPW];
-      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-      const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
-      const half2_t hi = {ha, hb}, lo = {la, lb};
-      const half2_t c = as_h2(((w[i] >> (BITS * j)) & MASK) | 0x64006400u) - k1024;
-      d = __builtin_amdgcn_fdot2(c, hi, d, false);
-      d = __builtin_amdgcn_fdot2(c, lo, d, false);
-      sx += a + b;
-    }
-  }
-}
-
 }  // namespace moe
