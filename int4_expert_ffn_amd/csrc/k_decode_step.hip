@@ -599,11 +599,13 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
 #pragma unroll
           for (int q = 0; q < PG; ++q) {
             float d0 = 0.f, d1 = 0.f;
-            dot_segment<BITS>(A.qg[u][q], xp[q], d0, d1);
-            pg += h2f(A.sg[u][q]) * (d0 + d1) + h2f(A.bg[u][q]) * (sx[q][0] + sx[q][1]);
+            const float sxq = sx[q][0] + sx[q][1];
+            dot_segment_biased<BITS>(A.qg[u][q], xp[q], d0, d1);
+            const float s_g = h2f(A.sg[u][q]), s_u = h2f(A.su[u][q]);
+            pg += s_g * (d0 + d1) + (h2f(A.bg[u][q]) - 1024.f * s_g) * sxq;
             d0 = d1 = 0.f;
-            dot_segment<BITS>(A.qu[u][q], xp[q], d0, d1);
-            pu += h2f(A.su[u][q]) * (d0 + d1) + h2f(A.bu[u][q]) * (sx[q][0] + sx[q][1]);
+            dot_segment_biased<BITS>(A.qu[u][q], xp[q], d0, d1);
+            pu += s_u * (d0 + d1) + (h2f(A.bu[u][q]) - 1024.f * s_u) * sxq;
           }
           red[2 * u] = pg;
           red[2 * u + 1] = pu;
@@ -708,14 +710,15 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           lp[4 * w] = b.x, lp[4 * w + 1] = b.y, lp[4 * w + 2] = b.z, lp[4 * w + 3] = b.w;
         }
         float d0 = 0.f, d1 = 0.f, sx = 0.f;
-        dot_segment_split<BITS>(B.q[u], hp, lp, d0, d1);
+        dot_segment_split_biased<BITS>(B.q[u], hp, lp, d0, d1);
         const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int j = 0; j < GS::PAIRS; ++j) {
           sx = __builtin_amdgcn_fdot2(as_h2(hp[j]), one, sx, false);
           sx = __builtin_amdgcn_fdot2(as_h2(lp[j]), one, sx, false);
         }
-        float po = ls < S ? h2f(B.s[u]) * (d0 + d1) + h2f(B.b[u]) * sx : 0.f;
+        const float s_d = h2f(B.s[u]);
+        float po = ls < S ? s_d * (d0 + d1) + (h2f(B.b[u]) - 1024.f * s_d) * sx : 0.f;
         po = group_sum_last(po, p.Ldn);
         if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
       }

@@ -216,4 +216,41 @@ __device__ __forceinline__ void dot_segment_split(uint4 q, const uint32_t* hp, c
   }
 }
 
+// The same dot products with the codes left biased: the exponent trick decodes a code pair to
+// 1024 + q exactly, and dotting that directly gives sum (1024 + q) x = sum q x + 1024 sum x.  The
+// caller folds the 1024 into the group bias, s * d' + (b - 1024 s) * sum x, which saves the float16
+// subtract of every pair.
+template <int BITS>
+__device__ __forceinline__ void dot_segment_biased(uint4 q, const uint32_t* xp, float& d0, float& d1) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const half2_t c = as_h2(((w[i] >> (BITS * j)) & MASK) | 0x64006400u);
+      float& d = i < 2 ? d0 : d1;
+      d = __builtin_amdgcn_fdot2(c, as_h2(xp[i * PPW + j]), d, false);
+    }
+  }
+}
+template <int BITS>
+__device__ __forceinline__ void dot_segment_split_biased(uint4 q, const uint32_t* hp, const uint32_t* lp, float& d0,
+                                                         float& d1) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const half2_t c = as_h2(((w[i] >> (BITS * j)) & MASK) | 0x64006400u);
+      float& d = i < 2 ? d0 : d1;
+      d = __builtin_amdgcn_fdot2(c, as_h2(hp[i * PPW + j]), d, false);
+      d = __builtin_amdgcn_fdot2(c, as_h2(lp[i * PPW + j]), d, false);
+    }
+  }
+}
+
 }  // namespace moe

@@ -115,20 +115,28 @@ def test_decode_step_equals_per_layer_path(M):
 
 
 def test_decode_step_deterministic_and_mixable(M):
-    """Two fresh stacks fed the same tokens give bit-identical outputs; a stack can switch from
-    the per-layer path (first token) to the persistent kernel (later tokens)."""
+    """Two fresh stacks fed the same tokens through the persistent kernel give bit-identical outputs
+    and routing.  A third stack that runs the first token through the per-layer calls and the
+    rest through the persistent kernel (the routing state carries over between the two paths) picks
+    the same experts and agrees within the tolerance.  The two paths differ in rounding (the
+    persistent kernel exchanges the SwiGLU outputs with a 16-bit significand), so they are not
+    compared bit for bit."""
     from int4_expert_ffn_amd.chain import DecodeStack
     cfg, heads = CASES["decode35b"]
     syn, layers, _, _ = build(M, cfg, heads)
     a = DecodeStack(layers, cfg.K, DEV)
+    a2 = DecodeStack(layers, cfg.K, DEV)
     b = DecodeStack(layers, cfg.K, DEV)
     for t in range(5):
         h0 = syn.hidden(8200 + t, 1)[0].to(DEV)
         ya = a.step(t, h0).clone()
+        ya2 = a2.step(t, h0).clone()
         yb = (b.token(t, h0) if t == 0 else b.step(t, h0)).clone()
         torch.cuda.synchronize()
+        assert torch.equal(ya, ya2), f"token {t}: persistent kernel not deterministic"
+        assert torch.equal(a.route_idx[t % 3], a2.route_idx[t % 3])
         if t >= 1:
-            assert torch.equal(a.route_idx[t % 3], b.route_idx[t % 3])
-        if t >= 2:
-            assert torch.equal(ya, yb)
-    assert a.step_error_word() == 0 and b.step_error_word() == 0
+            assert torch.equal(a.route_idx[t % 3], b.route_idx[t % 3]), f"token {t}: routing after the switch"
+        assert_rows_close(yb.float().cpu().numpy()[None], ya.float().cpu().numpy()[None],
+                          what=f"token {t} mixed vs persistent")
+    assert a.step_error_word() == 0 and a2.step_error_word() == 0 and b.step_error_word() == 0
