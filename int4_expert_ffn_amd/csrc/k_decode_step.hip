@@ -319,11 +319,13 @@ __device__ __forceinline__ int lin_row(const StepParams& p, int wg, int cw) {
   return -1;
 }
 
-// Loads of phase A of layer l, and the fc2 row of the head of layer l-1 when fc2_of_prev (the
-// second half of that head runs in this phase).  Descriptor fields are scalar loads.
+// Loads of phase A of layer l, in two parts: the gate/up rows (needed first), and the head rows of
+// layer l plus the fc2 row of the head of layer l-1 when fc2_of_prev (the second half of that head
+// runs in this phase; both are needed only after the SwiGLU outputs).  Descriptor fields are
+// scalar loads.
 template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
-__device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* re, const int* prev, bool fc2_of_prev,
-                                        int wg, int cw, int lane, ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
+__device__ __forceinline__ void issue_A_gu(const StepParams& p, int l, const int* re, int wg, int cw, int lane,
+                                           ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
   const layer_cptr D = layer_at(p, l);
   const int gw = wg * MW + cw;
   const int wpr = p.d * BITS / 32, ngr = p.d >> p.lg2g;
@@ -351,6 +353,12 @@ __device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* r
       a.bu[u][q] = D->experts.up.biases[go];
     }
   }
+}
+template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
+__device__ __forceinline__ void issue_A_head(const StepParams& p, int l, const int* re, const int* prev,
+                                             bool fc2_of_prev, int wg, int cw, int lane,
+                                             ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
+  const layer_cptr D = layer_at(p, l);
   if (has_head(p, l)) {
     // K-hot gather: lane j < K reads row cur[j] of the routing table, lane K <= j < 2K row
     // E + prev[j - K] (none at the first token); other lanes re-read row cur[0] and add 0.
@@ -386,6 +394,12 @@ __device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* r
       a.fr[sg] = *reinterpret_cast<const uint4*>(fc2 + (size_t)row * p.H + (size_t)(lane + sg * WAVE) * 8);
     a.fb = fc2_b ? fc2_b[row] : *p.zero16;
   }
+}
+template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
+__device__ __forceinline__ void issue_A(const StepParams& p, int l, const int* re, const int* prev, bool fc2_of_prev,
+                                        int wg, int cw, int lane, ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
+  issue_A_gu(p, l, re, wg, cw, lane, a);
+  issue_A_head(p, l, re, prev, fc2_of_prev, wg, cw, lane, a);
 }
 
 template <int BITS, int NSF, int PD>
@@ -425,7 +439,6 @@ struct StepShared {
   float logit[LDS_E];
   float part[LDS_PART];
   float aout[MW * 4];   // this workgroup's SwiGLU outputs of the phase, gathered for one store
-  float scale[2];
   int route_e[LDS_LK];  // this token's routing of every layer: [l * K + k]
   float route_w[LDS_LK];
   int prev_e[LDS_LK];   // the previous token's routing (K-hot "previous" input of the heads)
@@ -472,22 +485,16 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
   for (int l = 0; l < p.L; ++l) {
     const int hb = l & 1;
     uint32_t* hw = reinterpret_cast<uint32_t*>(sm.h[hb]);
-    float sq = 0.f;  // sum of squares of h_l, accumulated as the words arrive
+    // (the RMS norm of h_l is taken by the compute waves from their own reads of it, in a fixed
+    // order; summed here, as the words arrive, it would depend on their arrival order)
     if (l == 0) {
-      for (int m = lane; m < dh; m += WAVE) {
-        hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
-        sq = __builtin_amdgcn_fdot2(as_h2(hw[m]), as_h2(hw[m]), sq, false);
-      }
+      for (int m = lane; m < dh; m += WAVE) hw[m] = reinterpret_cast<const uint32_t*>(p.h_in)[m];
       if (p.h_layers != nullptr && c.wg == 0)  // row 0 of the per-layer copies: the token's input
         for (int m = lane; m < dh; m += WAVE) reinterpret_cast<uint32_t*>(p.h_layers)[m] = hw[m];
     } else {
-      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, [&](int i, uint32_t v) {
-        hw[i] = v;
-        sq = __builtin_amdgcn_fdot2(as_h2(v), as_h2(v), sq, false);
-      });
+      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed,
+              [&](int i, uint32_t v) { hw[i] = v; });
     }
-    sq = wave_sum(sq);
-    if (lane == 0) sm.scale[hb] = 1.f / sqrtf(sq / (float)p.d + RMS_EPS);
     lds_barrier();  // B1: h_l ready
     if (self_routed(p, l)) {
       ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
@@ -554,25 +561,30 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     const bool prefetch = l + 1 < p.L && !self_routed(p, l + 1);
     const int hb = l & 1;
     lds_barrier();  // B1
-    const float scale = sm.scale[hb];
+    float scale;  // 1 / rms(h_l), from this wave's own reads of h_l (a fixed summation order)
     const uint16_t* hl = sm.h[hb];
     if (self) {
       // R_l: at most one router row per wave -> tagged logit
       const int r = e_row(p, wg, cw);
       if (r < p.E) {  // uniform over the wave
         const uint16_t* W = layer_at(p, l)->router + (size_t)r * p.d;
-        float acc = 0.f;
+        float red[2] = {0.f, 0.f};  // router dot, sum of squares of h_l
 #pragma unroll
         for (int sg = 0; sg < NSH; ++sg) {
           const int g = lane + sg * WAVE;
           const uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
           const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)g * 8);
-          acc = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), acc, false);
-          acc = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), acc, false);
-          acc = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), acc, false);
-          acc = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), acc, false);
+          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), red[0], false);
+          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), red[0], false);
+          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), red[0], false);
+          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), red[0], false);
+          red[1] = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(xv.x), red[1], false);
+          red[1] = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(xv.y), red[1], false);
+          red[1] = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(xv.z), red[1], false);
+          red[1] = __builtin_amdgcn_fdot2(as_h2(xv.w), as_h2(xv.w), red[1], false);
         }
-        acc = wave_sum(acc) * scale;
+        wave_sum_n(red);
+        const float acc = red[0] / sqrtf(red[1] / (float)p.d + RMS_EPS);
         ll_put(ws, p, p.ll_logits, r, lead, __float_as_uint(acc), c.tag(3 * l));
       }
       lds_barrier();  // B2
@@ -588,7 +600,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     {
       const uint32_t tA = c.tag(3 * l + 1);
       {
-        float red[2 * GU];
+        float red[2 * GU + 1];  // gate, up per pair | sum of squares of h_l
         uint32_t xp[PG][GS::PAIRS];
         float sx[PG][2], sq = 0.f;
 #pragma unroll
@@ -610,7 +622,9 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           red[2 * u] = pg;
           red[2 * u + 1] = pu;
         }
+        red[2 * GU] = sq;  // the segments of the 64 lanes cover all of h_l
         wave_sum_n(red);
+        scale = 1.f / sqrtf(red[2 * GU] / (float)p.d + RMS_EPS);
 #pragma unroll
         for (int u = 0; u < GU; ++u) {
           const float pg = red[2 * u] * scale, pu = red[2 * u + 1] * scale;
@@ -685,9 +699,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       }
       lin_keep = lin_keep_next;
     }
-    if (prefetch)  // weights of A_{l+1}, one phase early
-      issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K,
-                                          c.prev_i ? sm.prev_e + (l + 1) * K : nullptr, head, wg, cw, lane, A);
+    if (prefetch)  // gate/up weights of A_{l+1}, one phase early
+      issue_A_gu<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, A);
     lds_barrier();  // B3
     // split act into float16 hi/lo pairs once per workgroup, every compute lane a few values
     for (int n = cw * WAVE + lane; n < K * p.I; n += MW * WAVE) put_act<BITS>(sm, n, sm.act_f[n]);
@@ -747,6 +760,11 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
                c.tag(3 * l + 2));
       }
     }
+    // The head half of A_{l+1}'s weights (needed only after its SwiGLU outputs) goes out after the
+    // combine: issued together with the gate/up half it slowed the act exchange that follows.
+    if (prefetch)
+      issue_A_head<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K,
+                                               c.prev_i ? sm.prev_e + (l + 1) * K : nullptr, head, wg, cw, lane, A);
   }
 }
 
