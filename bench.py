@@ -17,6 +17,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -62,14 +63,20 @@ def algorithmic_bytes(cfg):
     return total, ffn_call
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
 def kernel_source_hash():
-    """sha256 over the sources the persistent kernel is built from (to tell whether a stored
-    counter record still describes the kernel that runs)."""
+    """sha256 over the code of the sources the persistent kernel is built from, with comments
+    dropped and whitespace runs collapsed (to tell whether a stored counter record still
+    describes the kernel that runs; an edit of a comment does not change the kernel)."""
     import hashlib
     h = hashlib.sha256()
     for rel in STEP_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            src = f.read()
+        code = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()
 
 

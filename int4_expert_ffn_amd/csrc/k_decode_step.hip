@@ -10,14 +10,18 @@
 //   * Work is split statically: every workgroup owns a slice of the gate/up row pairs, of the
 //     head's fc1 / linear rows, of the down rows (all K experts of a row live in one workgroup,
 //     so the weighted combine stays local and in fixed order) and of the fc2 rows.
-//   * The SwiGLU output travels in float32 and meets the down weights as a float16 hi + lo pair.
-//   * Data moves between workgroups as tagged 8-byte words (32-bit payload, 32-bit tag naming
-//     the token epoch and the phase), written by one lane with device-coherent stores and read
-//     with agent-scope relaxed atomic loads; a reader polls until every tag matches, so no
-//     flag/data ordering is needed.
+//   * The SwiGLU output travels as floats with a 16-bit significand (two per word) and meets the
+//     down weights as a float16 hi + lo pair.
+//   * Data moves between workgroups as tagged 8-byte words (32-bit payload and 32-bit tag naming
+//     the token epoch and the phase; for the SwiGLU output 48 bits of payload and a 16-bit tag),
+//     written by one lane with device-coherent stores and read with agent-scope relaxed atomic
+//     loads; a reader polls until every tag matches, so no flag/data ordering is needed.
 //   * Per workgroup, wave 0 only waits for and unpacks the vector the next phase needs (into
-//     LDS); waves 1..4 compute.  Their weight loads for a phase are issued one phase early, and
-//     workgroup barriers fence LDS only, so those loads stay in flight while the phase waits.
+//     LDS); waves 1..8 compute (two per SIMD).  Their weight loads for a phase are issued one
+//     phase early, and workgroup barriers fence LDS only, so those loads stay in flight while
+//     the phase waits.
+//   * Every reduction runs in a fixed order (the RMS norm of h_l too: each compute wave takes it
+//     from its own reads of h_l), so equal inputs give bit-identical outputs from run to run.
 //   * The heads are off the critical path (their output routes the next token).  The linear and
 //     fc1 rows of head l run in phase A of layer l; the wave that computes linear row e keeps it
 //     and adds it to fc2 row e, which runs in phase A of layer l+1, after the head's hidden vector
