@@ -43,7 +43,7 @@ def build_stack(cfg, syn, dev, M):
         mats = S.fill_experts(syn, l, dev)
         ex = M.Experts(mats["gate"], mats["up"], mats["down"], cfg.bits, cfg.group)
         head = None
-        if l < cfg.L - 1:
+        if cfg.head_hidden and l < cfg.L - 1:
             hw = syn.head(l, dev)
             hw["lin_x"] = routers[l + 1]          # the head's linear path is the next router
             head = M.PrerouterWeights(hw)
@@ -52,15 +52,21 @@ def build_stack(cfg, syn, dev, M):
 
 
 def algorithmic_bytes(cfg):
-    """Bytes a token must move: K selected experts per layer, each head (dense rows + the 2K
-    gathered K-hot rows), the layer-0 router, and the float16 in/out vectors."""
+    """Bytes a token must move through the whole stack, and through its expert FFN steps alone.
+    With prerouter heads: K selected experts per layer, each head (dense rows + the 2K gathered
+    K-hot rows), the layer-0 router and the float16 in/out vectors of every layer.  Without: K
+    experts, the layer's router and the in/out vectors of every layer.  Expert FFN alone: the
+    experts and the vectors."""
     E, d, K, H = cfg.E, cfg.d, cfg.K, cfg.head_hidden
     expert = K * cfg.expert_bytes()
-    head = (H * d + 2 * K * H + H + E * H + E + E * d + 2 * K * E + E) * 2
     vec = 2 * d * 2
-    ffn_call = expert + 3 * d * 2 + K * 8          # x, r in; y out; idx, w
-    total = cfg.L * expert + (cfg.L - 1) * head + E * d * 2 + cfg.L * vec
-    return total, ffn_call
+    router = E * d * 2
+    if H:
+        head = (H * d + 2 * K * H + H + E * H + E + E * d + 2 * K * E + E) * 2
+        total = cfg.L * expert + (cfg.L - 1) * head + router + cfg.L * vec
+    else:
+        total = cfg.L * (expert + router + vec)
+    return total, cfg.L * (expert + vec)
 
 
 _CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
@@ -106,7 +112,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def cpu_baseline(cfg, layers, syn, tokens=2):
+def cpu_baseline(cfg, layers, syn, tokens):
     """Time the fp64 oracle (single thread) on `tokens` steady-state tokens of the same stack."""
     import numpy as np
     import oracle as O
@@ -140,13 +146,359 @@ def cpu_baseline(cfg, layers, syn, tokens=2):
                       f"1 BLAS thread; includes copying each selected expert's packed bytes from HBM once)"}
 
 
+STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
+WORKLOADS = STACK_WORKLOADS + ("tiny", "batched")
+METRIC = "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)"
+
+
+def describe(cfg):
+    w = (f"{cfg.name}: d_model {cfg.d}, {cfg.E} experts, top-{cfg.K}, expert I {cfg.I}, "
+         f"int{cfg.bits} affine g{cfg.group}, {cfg.L} layer{'s' if cfg.L > 1 else ''} resident")
+    if cfg.head_hidden:
+        w += (f", prerouter heads {cfg.d + 2 * cfg.E}->{cfg.head_hidden}->{cfg.E} "
+              f"(+linear {cfg.d + 2 * cfg.E}->{cfg.E})")
+    elif cfg.T == 1:
+        w += ", every layer routed by its own router"
+    if cfg.shared_expert:
+        w += f", shared expert + LoRA r{cfg.lora_rank} alpha {cfg.lora_alpha:g}"
+    return w + (f", batch {cfg.T}" if cfg.T > 1 else ", batch 1")
+
+
+def base_record(args, cfg, value, wall, steps):
+    return {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": describe(cfg),
+            "global_batch": cfg.T, "layers": cfg.L, "accumulate": "f32",
+            "weights": f"int{cfg.bits} affine g{cfg.group} (fp16 scale/bias)",
+            "parallelism": "none (1 GPU)",
+        },
+    }
+
+
+def roofline(kernel, nbytes, avg_us, traffic):
+    achieved = nbytes / (avg_us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "bytes_per_launch": nbytes,
+            "avg_us": round(avg_us, 2)}
+
+
+class Timer:
+    """Token loops on one stream: graph replays (or direct launches), HIP events around the timed
+    region, fresh inputs from a resident pool written into a 3-slot ring every three tokens."""
+
+    def __init__(self, torch, dev, pool):
+        self.torch, self.pool = torch, pool
+        self.n_pool = pool.shape[0]
+        self.ring = torch.empty((3,) + tuple(pool.shape[1:]), dtype=pool.dtype, device=dev)
+        self.stream = torch.cuda.Stream(device=dev)
+
+    def capture(self, enqueue):
+        """Three graphs, one per routing slot (tokens 1, 2, 3), each reading its ring slot;
+        enqueue(t, h) issues token t (token 0 runs eagerly first)."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            enqueue(0, self.pool[0])
+            self.ring.copy_(self.pool[0:3])
+        self.stream.synchronize()
+        graphs = []
+        for j in range(3):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                enqueue(j + 1, self.ring[(j + 1) % 3])
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def run(self, graphs, n, start, refill=None):
+        for i in range(n):
+            t = start + i
+            if t % 3 == 1:                       # refill the inputs of tokens t, t+1, t+2
+                p = (t // 3 * 3) % self.n_pool
+                self.ring.copy_(self.pool[p:p + 3])
+                if refill is not None:
+                    refill(p)
+            if callable(graphs):
+                graphs(t)
+            else:
+                graphs[(t - 1) % 3].replay()
+
+    def timed(self, graphs, steps, warmup, refill=None):
+        """(wall seconds, HIP-event milliseconds, warm-up tokens actually run)"""
+        torch = self.torch
+        warmup = -(-warmup // 3) * 3             # whole slot rotations keep tokens consecutive
+        with torch.cuda.stream(self.stream):
+            self.run(graphs, warmup, 1, refill)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            e0.record(self.stream)
+            self.run(graphs, steps, 1 + warmup, refill)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            w1 = time.perf_counter()
+        return w1 - w0, e0.elapsed_time(e1), warmup
+
+
+def bench_stack(args, cfg, torch, M, S, dev):
+    """A resident L-layer stack at batch 1: the timed step is one moe_decode_step launch per token
+    (the persistent kernel running every layer); the expert FFN steps alone and the per-layer
+    C-ABI calls are timed beside it."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    syn = S.Synth(cfg)
+    t0 = time.time()
+    layers = build_stack(cfg, syn, dev, M)
+    torch.cuda.synchronize()
+    log(f"stack resident: {cfg.L} layers, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.1f} s")
+    tm = Timer(torch, dev, syn.hidden(7, 3 * 64, dev))
+
+    stack = DecodeStack(layers, cfg.K, dev)
+    graphs = tm.capture(lambda t, h: stack.step(t, h))
+    if args.eager:                               # same tokens, direct launches (graphs captured but unused)
+        graphs = lambda t: stack.step(t, tm.ring[t % 3])
+    wall, ev_ms, args.warmup = tm.timed(graphs, args.steps, args.warmup)
+    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
+    h_out = stack.h[cfg.L].float()
+    assert torch.isfinite(h_out).all(), "non-finite decode output"
+    del graphs
+    total_bytes, eo_bytes = algorithmic_bytes(cfg)
+    step_us = ev_ms * 1e3 / args.steps               # HIP-event time per token on the stream
+
+    # the expert FFN steps alone (gate/up + SwiGLU, down + combine + residual through all layers, the
+    # RMS-norm chain included) on the routing the full path chose for the same tokens, recorded
+    # per token and written into the routing slots between tokens
+    expert_only = None
+    if not args.no_expert_only:
+        n_pool = tm.n_pool
+        rec_i = torch.empty((n_pool, cfg.L, cfg.K), dtype=torch.int32, device=dev)
+        rec_w = torch.empty((n_pool, cfg.L, cfg.K), dtype=torch.float32, device=dev)
+        src = DecodeStack(layers, cfg.K, dev)
+        with torch.cuda.stream(tm.stream):
+            for t in range(n_pool):
+                src.step(t, tm.pool[t])
+                rec_i[t].copy_(src.route_idx[t % 3])
+                rec_w[t].copy_(src.route_w[t % 3])
+        torch.cuda.synchronize()
+        assert src.step_error_word() == 0, "a wait inside the decode kernel ran out of time (recording)"
+        del src
+        stack3 = DecodeStack(layers, cfg.K, dev)
+        stack3.route_idx.copy_(rec_i[0:3])
+        stack3.route_w.copy_(rec_w[0:3])
+
+        def refill(p):
+            stack3.route_idx.copy_(rec_i[p:p + 3])
+            stack3.route_w.copy_(rec_w[p:p + 3])
+
+        graphs3 = tm.capture(lambda t, h: stack3.step(t, h, given_routing=True))
+        wall3, ev3, _ = tm.timed(graphs3, args.steps, args.warmup, refill)
+        assert stack3.step_error_word() == 0, "a wait inside the decode kernel ran out of time (expert only)"
+        del graphs3
+        eo_us = ev3 * 1e3 / args.steps
+        expert_only = {
+            "tokens_per_s": round(args.steps / wall3, 2), "avg_us": round(eo_us, 2),
+            "algorithmic_bytes_per_token": eo_bytes,
+            "achieved_GBps": round(eo_bytes / (eo_us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(eo_bytes / (eo_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "S3-S6 alone (moe_decode_step with MOE_DECODE_GIVEN_ROUTING) on the routing the full "
+                    "path chose for the same tokens; HIP-event time per token includes the routing refill copies",
+        }
+
+    # context: the same schedule as per-layer C-ABI calls
+    per_layer_tok_s = None
+    if not args.no_per_layer:
+        stack2 = DecodeStack(layers, cfg.K, dev)
+        graphs2 = tm.capture(lambda t, h: stack2.token(t, h))
+        n2 = max(30, args.steps // 4)
+        wall2, _, _ = tm.timed(graphs2, n2, 30)
+        per_layer_tok_s = round(n2 / wall2, 2)
+        del graphs2
+    launches = (5 * cfg.L - 2) if cfg.head_hidden else 4 * cfg.L
+
+    tok_s = args.steps / wall
+    rec = base_record(args, cfg, tok_s, wall, args.steps)
+    rec["hbm"] = {"algorithmic_bytes_per_token": total_bytes,
+                  "achieved_GBps": round(total_bytes * tok_s / 1e9, 1),
+                  "frac_of_peak": round(total_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4)}
+    rec["roofline"] = roofline(f"k_decode_step (moe_decode_step: all {cfg.L} layers of one token in one launch)",
+                               total_bytes, step_us, stored_traffic() if cfg.name == "decode35b" else None)
+    rec["expert_only"] = expert_only
+    rec["per_layer_calls"] = {"tokens_per_s": per_layer_tok_s, "launches_per_token": launches,
+                              "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn, tokens=2 if cfg.d <= 2048 else 1)
+    return rec
+
+
+def bench_tiny(args, cfg, torch, M, S, dev):
+    """The small single-layer case (d 256, 16 experts): router + top-K, then the expert FFN with
+    the fused weighted combine, four kernel launches per token, replayed as a graph.  Everything fits in
+    cache, so this is a latency figure, not a bandwidth one."""
+    from int4_expert_ffn_amd.chain import DecodeStack, LayerWeights
+    syn = S.Synth(cfg)
+    mats = S.fill_experts(syn, 0, dev)
+    ex = M.Experts(mats["gate"], mats["up"], mats["down"], cfg.bits, cfg.group)
+    stack = DecodeStack([LayerWeights(ex, syn.router(0, dev), None)], cfg.K, dev)
+    tm = Timer(torch, dev, syn.hidden(7, 3 * 64, dev))
+    graphs = tm.capture(lambda t, h: stack.token(t, h))
+    wall, ev_ms, args.warmup = tm.timed(graphs, args.steps, args.warmup)
+    total, _ = algorithmic_bytes(cfg)
+    us = ev_ms * 1e3 / args.steps
+    rec = base_record(args, cfg, args.steps / wall, wall, args.steps)
+    rec["roofline"] = roofline("router + top-K + expert FFN with fused combine (4 launches per token)", total, us, None)
+    rec["roofline"]["note"] = "the whole layer (132 KB) stays in cache: latency-bound, the fraction is not meaningful"
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(cfg, stack.layers, syn, tokens=64)
+    return rec
+
+
+def bench_batched(args, cfg, torch, M, S, dev):
+    """The batched layer (T tokens per call): router GEMM + top-K, routed experts as MFMA grouped
+    GEMMs over the tokens sorted by expert, the shared expert with its unmerged LoRA, and the
+    combine with the residual.  Four weight copies are rotated so that consecutive batches do
+    not find the previous batch's weights in the memory-side cache."""
+    T, K, d, E = cfg.T, cfg.K, cfg.d, cfg.E
+    copies = []
+    for c in range(4):
+        syn = S.Synth(cfg, seed=c)
+        mats = S.fill_experts(syn, 0, dev)
+        se = syn.shared_expert_id()
+        sh = M.Experts(*[syn.expert_mat(0, [se], m, dev) for m in S.MATS], cfg.bits, cfg.group)
+        lw = syn.lora(0, dev)
+        copies.append({"ex": M.Experts(mats["gate"], mats["up"], mats["down"], cfg.bits, cfg.group),
+                       "sh": sh, "lora": M.Lora3([lw[m] for m in S.MATS], cfg.lora_alpha),
+                       "router": syn.router(0, dev)})
+    torch.cuda.synchronize()
+    syn = S.Synth(cfg)
+    n_in = 8
+    hs = syn.hidden(11, n_in * T, dev).view(n_in, T, d)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    o = torch.empty((T, K, d), dtype=torch.float32, device=dev)
+    sho = torch.empty((T, 1, d), dtype=torch.float32, device=dev)
+    zeros = torch.zeros((T, 1), dtype=torch.int32, device=dev)
+    y = torch.empty((T, d), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(M.moe_expert_ffn_workspace_size(T, K, copies[0]["ex"]),
+                         M.moe_expert_ffn_workspace_size(T, 1, copies[0]["sh"])), dtype=torch.uint8, device=dev)
+
+    def layer(cp, h):
+        M.moe_route_topk(T, d, E, K, M.MOE_TOPK_RENORM, h, cp["router"], logits, idx, w)
+        M.moe_expert_ffn_q4(T, K, 0, h, idx, cp["ex"], None, o, None, None, None, ws)
+        M.moe_expert_ffn_q4(T, 1, 0, h, zeros, cp["sh"], cp["lora"], sho, None, None, None, ws)
+        M.moe_combine(T, K, d, o, w, h, sho.view(T, d), y)
+
+    # experts each (copy, input) pair touches, for the algorithmic bytes
+    used = []
+    for c, cp in enumerate(copies):
+        for i in range(n_in):
+            layer(cp, hs[i])
+            used.append(int(torch.unique(idx).numel()))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(device=dev)
+    graphs = []
+    with torch.cuda.stream(stream):
+        for c, cp in enumerate(copies):
+            for i in range(2):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    layer(cp, hs[(2 * c + i) % n_in])
+                graphs.append(g)
+    torch.cuda.synchronize()
+    steps = args.steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        w1 = time.perf_counter()
+    wall = w1 - w0
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    assert torch.isfinite(y.float()).all(), "non-finite batched output"
+    mean_used = sum(used) / len(used)
+    eb = cfg.expert_bytes()
+    lora_b = sum(2 * (r.numel() + b.numel()) for r, b in [syn.lora(0, "cpu")[m] for m in S.MATS])
+    nbytes = int(round(mean_used * eb + eb + E * d * 2 + lora_b + 2 * T * d * 2))
+    rec = base_record(args, cfg, steps * T / wall, wall, steps)
+    rec["roofline"] = roofline("the batched layer: router GEMM + top-K, sort, grouped MFMA gate/up and down, "
+                               "shared expert + LoRA, combine (one graph per batch)", nbytes, us, None)
+    rec["roofline"]["used_experts_mean"] = round(mean_used, 2)
+    rec["batch_us"] = round(us, 2)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline_batched(cfg, S, tokens=32)
+    return rec
+
+
+def cpu_baseline_batched(cfg, S, tokens):
+    """Time the fp64 oracle (single thread) on the first `tokens` tokens of a batch: router, top-K,
+    the routed experts each token selects, the shared expert with its LoRA, combine.  The packed
+    weights are drawn beforehand (untimed)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    syn = S.Synth(cfg)
+    h = O.f64(syn.hidden(11, tokens).numpy())
+    wr = syn.router(0).numpy()
+    idx0, _ = O.route_topk(O.router_logits(wr, h), cfg.K)
+    packed = {int(e): tuple(tuple(a[0].numpy() for a in syn.expert_mat(0, [int(e)], m)) for m in S.MATS)
+              for e in np.unique(idx0)}
+    se = syn.shared_expert_id()
+    shared = tuple(tuple(a[0].numpy() for a in syn.expert_mat(0, [se], m)) for m in S.MATS)
+    lw = syn.lora(0, "cpu")
+    lora = {m: (lw[m][0].numpy(), lw[m][1].numpy()) for m in S.MATS}
+    lora["alpha"] = cfg.lora_alpha
+    t0 = time.perf_counter()
+    idx, w = O.route_topk(O.router_logits(wr, h), cfg.K)
+    o = np.zeros((tokens, cfg.K, cfg.d))
+    for t in range(tokens):
+        for k in range(cfg.K):
+            o[t, k] = O.expert_ffn_packed(h[t], *packed[int(idx[t, k])], bits=cfg.bits, group=cfg.group)
+    sh = O.expert_ffn_packed(h, *shared, cfg.bits, cfg.group, lora)
+    O.combine(o, w, h, sh)
+    elapsed = time.perf_counter() - t0
+    del limiter
+    return {"value": round(tokens / elapsed, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {tokens} tokens of a {cfg.T}-token batch (fp64, explicit dequant per expert "
+                      f"and token, 1 BLAS thread; weights drawn beforehand)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", choices=WORKLOADS, default="decode35b",
+                    help="decode35b (default, the headline line), widek8, large-int4, large-int2 (resident stacks "
+                         "through the persistent kernel), tiny (d 256, one layer), batched (256 tokens per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
+    ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed token directly instead of replaying a HIP graph (for counter profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -164,134 +516,13 @@ def main():
     import moe_synth as S
 
     dev = torch.device("cuda:0")
-    cfg = S.CONFIGS["decode35b"]
-    syn = S.Synth(cfg)
-    t0 = time.time()
-    layers = build_stack(cfg, syn, dev, M)
-    torch.cuda.synchronize()
-    log(f"stack resident: {cfg.L} layers, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.1f} s")
-
-    from int4_expert_ffn_amd.chain import DecodeStack
-    n_pool = 3 * 64
-    pool = syn.hidden(7, n_pool, dev)
-    ring = torch.empty((3, cfg.d), dtype=torch.float16, device=dev)
-    stream = torch.cuda.Stream(device=dev)
-
-    def capture(stack, use_step):
-        """Three graphs, one per routing slot (tokens 1, 2, 3), each reading its ring slot."""
-        with torch.cuda.stream(stream):
-            if use_step:
-                stack.step(0, pool[0])          # token 0: every layer routes itself
-            else:
-                stack.token(0, pool[0])
-            ring.copy_(pool[0:3])
-        stream.synchronize()
-        graphs = []
-        for j in range(3):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                if use_step:
-                    stack.step(j + 1, ring[(j + 1) % 3])
-                else:
-                    stack.token(j + 1, ring[(j + 1) % 3])
-            graphs.append(g)
-        torch.cuda.synchronize()
-        return graphs
-
-    def run(graphs, n, start):
-        for i in range(n):
-            t = start + i
-            if t % 3 == 1:                       # refill the inputs of tokens t, t+1, t+2
-                p = (t // 3 * 3) % n_pool
-                ring.copy_(pool[p:p + 3])
-            if callable(graphs):
-                graphs(t)
-            else:
-                graphs[(t - 1) % 3].replay()
-
-    def timed(graphs, steps, warmup):
-        warmup = -(-warmup // 3) * 3             # whole slot rotations keep tokens consecutive
-        with torch.cuda.stream(stream):
-            run(graphs, warmup, 1)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            w0 = time.perf_counter()
-            e0.record(stream)
-            run(graphs, steps, 1 + warmup)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            w1 = time.perf_counter()
-        return w1 - w0, e0.elapsed_time(e1), warmup
-
-    # the timed step: one persistent-kernel launch (moe_decode_step) per token
-    stack = DecodeStack(layers, cfg.K, dev)
-    graphs = capture(stack, True)
-    if args.eager:                               # same tokens, direct launches (graphs captured but unused)
-        graphs = lambda t: stack.step(t, ring[t % 3])
-    wall, ev_ms, args.warmup = timed(graphs, args.steps, args.warmup)
-    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
-    h_out = stack.h[cfg.L].float()
-    assert torch.isfinite(h_out).all(), "non-finite decode output"
-    tok_s = args.steps / wall
-    total_bytes, ffn_bytes = algorithmic_bytes(cfg)
-    step_us = ev_ms * 1e3 / args.steps                 # HIP-event time per token on the stream
-    achieved = total_bytes / (step_us * 1e-6) / 1e9
-
-    # context: the same schedule as per-layer C-ABI calls (5 launches per layer)
-    del graphs
-    per_layer_tok_s = None
-    if not args.no_per_layer:
-        stack2 = DecodeStack(layers, cfg.K, dev)
-        graphs2 = capture(stack2, False)
-        n2 = max(30, args.steps // 4)
-        wall2, ev2, _ = timed(graphs2, n2, 30)
-        per_layer_tok_s = round(n2 / wall2, 2)
-        del graphs2
-    traffic = stored_traffic()
-
-    rec = {
-        "metric": "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)",
-        "value": round(tok_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {
-            "workload": "decode35b: d_model 2048, 256 experts, top-4, expert I 512, int4 affine g64, 40 layers "
-                        "resident, prerouter heads 2560->1024->256 (+linear 2560->256), batch 1",
-            "global_batch": 1, "layers": cfg.L, "accumulate": "f32", "weights": "int4 affine g64 (fp16 scale/bias)",
-            "parallelism": "none (1 GPU)",
-        },
-        "hbm": {
-            "algorithmic_bytes_per_token": total_bytes,
-            "achieved_GBps": round(total_bytes * tok_s / 1e9, 1),
-            "frac_of_peak": round(total_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
-        },
-        "roofline": {
-            "kernel": "k_decode_step (moe_decode_step: all 40 layers of one token in one launch)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "bytes_per_launch": total_bytes,
-            "avg_us": round(step_us, 2),
-        },
-        "per_layer_calls": {"tokens_per_s": per_layer_tok_s, "launches_per_token": 5 * cfg.L - 2,
-                            "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"},
-    }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle ...")
-        rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn)
+    cfg = S.CONFIGS[args.workload]
+    if args.workload in STACK_WORKLOADS:
+        rec = bench_stack(args, cfg, torch, M, S, dev)
+    elif args.workload == "tiny":
+        rec = bench_tiny(args, cfg, torch, M, S, dev)
+    else:
+        rec = bench_batched(args, cfg, torch, M, S, dev)
     print(json.dumps(rec), flush=True)
 
 

@@ -62,6 +62,9 @@ typedef enum {
                                   it, the full softmax over all E logits read at the K experts */
 #define MOE_INPUT_RMSNORM 0x2u /* consume x := x / sqrt(mean(x^2) + 1e-6) (weightless RMS norm,
                                   the glue between chained layers), computed in float32       */
+#define MOE_DECODE_GIVEN_ROUTING 0x4u /* moe_decode_step only: every layer takes its experts and
+                                  weights from route_idx / route_w slot token % 3 as the caller
+                                  wrote them; no router or head runs, nothing else is written */
 
 /* Limits checked by every call. */
 #define MOE_MAX_E 1024
@@ -205,7 +208,10 @@ size_t moe_decode_workspace_size(const moe_decode_stack* st);
 /* h_in[d] float16 (device): the token's input hidden state; h_out[d] float16 (device): the output
    of layer L-1.  h_layers: NULL, or [L+1][d] float16 (device) receiving every layer's input (row l,
    row 0 = h_in) and the final output (row L), for inspection and layer-by-layer checking; 4-byte
-   aligned.  flags: MOE_TOPK_RENORM or 0 (applies to every top-K). */
+   aligned.  flags: MOE_TOPK_RENORM (applies to every top-K) and/or MOE_DECODE_GIVEN_ROUTING (the
+   expert FFN steps alone on routing the caller supplies for every layer; token 0 is then no
+   bootstrap, the heads and routers of the descriptors are not read, and route_idx values must lie
+   in [0, E), K distinct per layer). */
 moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
                            const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
                            size_t workspace_bytes);

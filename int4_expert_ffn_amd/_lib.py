@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
 MOE_TOPK_RENORM = 0x1
 MOE_INPUT_RMSNORM = 0x2
+MOE_DECODE_GIVEN_ROUTING = 0x4
 MOE_MAX_E, MOE_MAX_K, MOE_MAX_D = 1024, 16, 8192
 
 # every symbol include/moe.h declares

@@ -82,14 +82,27 @@ class DecodeStack:
         return self._step
 
     def step(self, t: int, h_in: torch.Tensor, h_out: Optional[torch.Tensor] = None,
-             h_layers: Optional[torch.Tensor] = None):
+             h_layers: Optional[torch.Tensor] = None, given_routing: bool = False):
         """Enqueue token t as one persistent-kernel launch reading h_in [d] and writing h_out
         (default: self.h[L]); h_layers [L+1][d] float16, if given, receives every layer's input and
-        the output.  Returns h_out."""
+        the output.  given_routing: the expert FFN steps alone, every layer routed by what the
+        caller wrote into route_idx / route_w slot t % 3 (see set_routing).  Returns h_out."""
         desc, st, ws = self._step_state()
         out = self.h[self.L] if h_out is None else h_out
-        L.moe_decode_step(st, t, self.topk_flags, h_in, out, ws, h_layers=h_layers)
+        flags = self.topk_flags | (L.MOE_DECODE_GIVEN_ROUTING if given_routing else 0)
+        L.moe_decode_step(st, t, flags, h_in, out, ws, h_layers=h_layers)
         return out
+
+    def set_routing(self, t: int, idx: torch.Tensor, w: torch.Tensor):
+        """Write every layer's experts idx [L][K] (int32, distinct per layer, in [0, E)) and weights
+        w [L][K] (float32) into the routing slot of token t (asynchronous, on the current stream)."""
+        if tuple(idx.shape) != (self.L, self.K) or tuple(w.shape) != (self.L, self.K):
+            raise ValueError(f"routing must be [{self.L}][{self.K}]")
+        i64 = idx.to(torch.int64)
+        if bool(((i64 < 0) | (i64 >= self.E)).any()):
+            raise ValueError("expert index outside [0, E)")
+        self.route_idx[t % 3].copy_(idx.to(torch.int32))
+        self.route_w[t % 3].copy_(w.to(torch.float32))
 
     def step_error_word(self) -> int:
         """Nonzero if a wait inside a persistent-kernel step exceeded its bound (read after sync)."""

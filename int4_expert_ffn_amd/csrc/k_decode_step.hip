@@ -47,7 +47,8 @@ constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART
 constexpr int POLL_MAX = 16;                 // words per lane per polling pass (1024 per wave), <= 64
 static_assert(POLL_MAX >= 1 && POLL_MAX <= 64, "one done bit per polled word");
 constexpr uint32_t TAG_SALT = 0x5A5A5A5Au;
-constexpr uint64_t WAIT_TICKS = 20000000;       // 0.2 s of the 100 MHz real-time counter
+constexpr uint64_t WAIT_TICKS = 20000000;       // 0.2 s of polling, in ticks of the 100 MHz real-time counter
+constexpr uint64_t WAIT_STEP_MAX = 2000;        // at most 20 us charged per polling pass (see ll_wait)
 
 struct StepParams {
   int L, E, K, d, I, H, lg2g;
@@ -58,7 +59,7 @@ struct StepParams {
   uint16_t* h_layers;  // NULL or [L+1][d]: every layer's input and the final output
   int32_t* ridx;
   float* rw;
-  int slot, bootstrap;
+  int slot, bootstrap, given;  // given: every layer's routing supplied by the caller
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
   uint32_t* epoch;
@@ -128,9 +129,12 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 // is issued before the previous one is checked, so a word is seen about one memory round trip
 // after it lands rather than one and a half.  Every pass loads all POLL_MAX slots (slots past
 // the end re-read the last word and are ignored), which keeps the count of outstanding loads
-// exact for the compiler's waits.  A wait is bounded in wall-clock time: past WAIT_TICKS it raises
+// exact for the compiler's waits.  A wait is bounded in polling time: past WAIT_TICKS it raises
 // the error word, sets `failed`, and every later wait of this wave returns at once, so a grid
-// that cannot make progress still finishes quickly (with invalid results).
+// that cannot make progress still finishes quickly (with invalid results).  Each pass is charged
+// the real time since the previous one, capped at WAIT_STEP_MAX: a pass takes a few us, so the
+// cap only matters when the whole grid was paused (the queue preempted and later resumed), and
+// such a pause, during which no producer could run either, does not count against the bound.
 // TAGB: tag bits in the top of each word (32: a 32-bit payload; 16: a 48-bit payload).
 template <int TAGB = 32, class Sink>
 __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n, uint32_t tag, int* err, bool& failed,
@@ -139,7 +143,7 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n
   if (failed) return;
   const int lane = threadIdx.x % WAVE;
   constexpr uint64_t ALL = POLL_MAX == 64 ? ~0ull : (1ull << POLL_MAX) - 1;  // one bit per word slot of a lane
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t last = __builtin_amdgcn_s_memrealtime(), waited = 0;
   for (int base = 0; base < n; base += POLL_MAX * WAVE) {
     uint64_t done = 0;
 #pragma unroll
@@ -166,7 +170,10 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n
       issue(a);
       check(b);
       if (__all(done == ALL)) break;
-      if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      waited += min(now - last, WAIT_STEP_MAX);
+      last = now;
+      if (waited > WAIT_TICKS) {
         if (lane == 0) atomicAdd(err, 1);
         failed = true;
         return;
@@ -282,7 +289,7 @@ __device__ __forceinline__ layer_cptr layer_at(const StepParams& p, int l) { ret
 
 // Whether layer l carries a head that predicts layer l+1.
 __device__ __forceinline__ bool has_head(const StepParams& p, int l) {
-  return l + 1 < p.L && layer_at(p, l)->head.fc1_x != nullptr;
+  return !p.given && l + 1 < p.L && layer_at(p, l)->head.fc1_x != nullptr;
 }
 
 template <int BITS, int PG, int NSH, int NSF, int GU, int NH>
@@ -461,7 +468,7 @@ struct StepCtx {
 };
 
 __device__ __forceinline__ bool self_routed(const StepParams& p, int l) {
-  return p.bootstrap || l == 0 || !has_head(p, l - 1);
+  return !p.given && (p.bootstrap || l == 0 || !has_head(p, l - 1));
 }
 
 // Position of SwiGLU output n (n = k*I + column) in the LDS hi/lo arrays: the down projection's
@@ -525,9 +532,14 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     lds_barrier();  // B3b: act split into hi/lo pairs (by the compute waves)
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
     // The head's hidden vector g_l feeds its fc2 rows in phase A of layer l+1; fetching it here
-    // overlaps the wait for h_{l+1} instead of lengthening the act exchange.
+    // overlaps the wait for h_{l+1} instead of lengthening the act exchange.  This workgroup's
+    // part of h_{l+1} has already left, so another workgroup may be writing g_{l+1} meanwhile:
+    // g alternates between two buffers by layer parity (g_{l+2}, the next write into this
+    // buffer, needs h_{l+2}, which needs this workgroup's combine of layer l+1, which comes after
+    // this read).
     if (has_head(p, l))
-      ll_wait(p.ll_g, 0, p.H, tA, p.err, failed, [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
+      ll_wait(p.ll_g, (size_t)(l & 1) * p.H, p.H, tA, p.err, failed,
+              [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
   }
   // Top-K of every head, off the token's critical path: head l predicts layer l+1's routing for
   // the next token; workgroup l % G handles head l.
@@ -592,6 +604,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         ll_put(ws, p, p.ll_logits, r, lead, __float_as_uint(acc), c.tag(3 * l));
       }
       lds_barrier();  // B2
+    }
+    if (self || l == 0) {  // no earlier phase has loaded this layer's weights
       issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l, sm.route_e + l * K, c.prev_i ? sm.prev_e + l * K : nullptr, fc2_now,
                                           wg, cw, lane, A);
       issue_B<BITS, NSF, PD>(p, l, sm.route_e + l * K, wg, cw, lane, B);
@@ -676,7 +690,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
             if (row >= p.H)
               lin_keep_next = val;  // linear row: this wave adds it to its fc2 row in the next layer
             else
-              ll_put(ws, p, p.ll_g, row, lead, __float_as_uint(gelu_erf(val)), tA);
+              ll_put(ws, p, p.ll_g, (size_t)(l & 1) * p.H + row, lead, __float_as_uint(gelu_erf(val)), tA);
           }
         }
       }
@@ -868,7 +882,7 @@ static StepWs step_ws(const moe_decode_stack& st) {
   w.logits = 256;
   w.act = w.logits + ll_bytes(st.E);
   w.g = w.act + ll_bytes((size_t)st.K * st.d_ff);
-  w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? st.d_hidden : 1);
+  w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? 2 * (size_t)st.d_hidden : 1);  // two buffers, by layer parity
   w.h = w.hlog + ll_bytes((size_t)st.L * st.E);
   w.total = w.h + ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
   return w;
@@ -955,7 +969,8 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.ridx = st.route_idx;
   p.rw = st.route_w;
   p.slot = token % 3;
-  p.bootstrap = token == 0;
+  p.given = (flags & MOE_DECODE_GIVEN_ROUTING) != 0;
+  p.bootstrap = token == 0 && !p.given;
   p.topk_flags = flags & MOE_TOPK_RENORM;
   p.ll_logits = (uint64_t*)(b + w.logits);
   p.ll_act = (uint64_t*)(b + w.act);

@@ -196,7 +196,7 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
                            const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
                            size_t workspace_bytes) {
   if (!st || !h_in || !h_out || !workspace || token < 0) return MOE_ERR_INVALID_ARG;
-  if (flags & ~MOE_TOPK_RENORM) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_TOPK_RENORM | MOE_DECODE_GIVEN_ROUTING)) return MOE_ERR_INVALID_ARG;
   if (st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return MOE_ERR_INVALID_ARG;
   if (!st->layers || !st->route_idx || !st->route_w) return MOE_ERR_INVALID_ARG;
   if (st->bits != 4 && st->bits != 2) return MOE_ERR_UNSUPPORTED;

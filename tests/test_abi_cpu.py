@@ -105,6 +105,8 @@ def test_prerouter_and_combine_reject():
         None, ctypes.byref(stk), tok, flags, FAKE, FAKE, hl, ws, wsb)
     assert ds(st, tok=-1) == INVALID
     assert ds(st, flags=2) == INVALID
+    assert ds(st, flags=8) == INVALID           # unknown flag bit
+    assert ds(st, flags=5, wsb=64) == INVALID   # given routing passes the flag check, the size check still applies
     assert ds(st, wsb=64) == INVALID
     assert ds(st, ws=FAKE + 16) == INVALID
     assert ds(st, hl=FAKE + 2) == INVALID      # per-layer copies must be 4-byte aligned

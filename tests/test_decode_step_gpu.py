@@ -140,3 +140,46 @@ def test_decode_step_deterministic_and_mixable(M):
         assert_rows_close(yb.float().cpu().numpy()[None], ya.float().cpu().numpy()[None],
                           what=f"token {t} mixed vs persistent")
     assert a.step_error_word() == 0 and a2.step_error_word() == 0 and b.step_error_word() == 0
+
+
+def given_routing(syn, cfg, t):
+    """Seeded routing for every layer of token t: the oracle's top-K (renormalised softmax) of N(0,1)
+    logits, i.e. K distinct experts drawn uniformly per layer."""
+    lg = syn.logits(7000 + t, cfg.L).numpy()
+    idx, w = O.route_topk(lg, cfg.K)
+    return idx.astype(np.int32), w.astype(np.float32)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_step_given_routing(M, name):
+    """MOE_DECODE_GIVEN_ROUTING: the expert FFN steps alone on caller-supplied routing.  Every layer
+    output equals the oracle layer applied to the kernel's own input of that layer with the given
+    experts and weights; the routing slots are left as the caller wrote them, whatever heads and
+    routers the descriptors carry."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = CASES[name]
+    syn, layers, _, _ = build(M, cfg, heads)
+    stack = DecodeStack(layers, cfg.K, DEV)
+    caches = [ExpertCache(syn, l) for l in range(cfg.L)]
+    hl = torch.empty((cfg.L + 1, cfg.d), dtype=torch.float16, device=DEV)
+    stack.route_idx.fill_(-7)
+    stack.route_w.fill_(-7.0)
+    for t in range(3):
+        idx, w = given_routing(syn, cfg, t)
+        stack.set_routing(t, torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV))
+        before_i, before_w = stack.route_idx.clone(), stack.route_w.clone()
+        h0 = syn.hidden(9100 + t, 1)[0]
+        out = stack.step(t, h0.to(DEV), h_layers=hl, given_routing=True)
+        torch.cuda.synchronize()
+        assert stack.step_error_word() == 0
+        assert torch.equal(stack.route_idx, before_i) and torch.equal(stack.route_w, before_w), \
+            "the kernel wrote routing state"
+        H = hl.cpu().numpy()
+        assert np.array_equal(H[0], h0.numpy()) and np.array_equal(H[cfg.L], out.cpu().numpy())
+        for l in range(cfg.L):
+            x = O.rmsnorm(H[l])
+            y_ref = O.f64(H[l]).copy()
+            for k in range(cfg.K):
+                y_ref += float(w[l][k]) * O.expert_ffn_packed(x, *caches[l](idx[l][k]), bits=cfg.bits, group=cfg.group)
+            assert_rows_close(H[l + 1][None], y_ref[None], what=f"{name} t{t} layer {l} (given routing)")
+    log(f"{name}: given routing checked at all {cfg.L} layers of 3 tokens")

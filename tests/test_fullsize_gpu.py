@@ -23,7 +23,7 @@ import torch
 import moe_synth as S
 import oracle as O
 from parity_util import GAP, TOL, ExpertCache, assert_rows_close, log
-from test_decode_step_gpu import build
+from test_decode_step_gpu import build, given_routing
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -59,13 +59,15 @@ def _check_topk(logits, idx_gpu, w_gpu, K, what):
     return 1
 
 
-CASES = [(n, "step") for n in FULL] + [("decode35b-L40", "calls")]
+CASES = [(n, "step") for n in FULL] + [("decode35b-L40", "calls"), ("decode35b-L40", "given")]
 
 
 @pytest.mark.parametrize("name,path", CASES)
 def test_full_depth_layer_by_layer(M, name, path):
     """path "step": one moe_decode_step launch per token (inputs of every layer via h_layers);
-    path "calls": the per-layer C-ABI calls (every layer's input kept in the stack)."""
+    path "calls": the per-layer C-ABI calls (every layer's input kept in the stack); path "given":
+    moe_decode_step on caller-supplied routing for every layer (the expert FFN steps alone, as the
+    expert-only benchmark times them)."""
     from int4_expert_ffn_amd.chain import DecodeStack
     cfg, heads = FULL[name]
     L, K, E = cfg.L, cfg.K, cfg.E
@@ -78,13 +80,17 @@ def test_full_depth_layer_by_layer(M, name, path):
     prev_idx = None
     for t in range(3):
         h0 = syn.hidden(9000 + t, 1)[0]
-        if path == "step":
+        if path == "given":
+            gi, gw = given_routing(syn, cfg, t)
+            stack.set_routing(t, torch.from_numpy(gi).to(DEV), torch.from_numpy(gw).to(DEV))
+            out = stack.step(t, h0.to(DEV), h_layers=hl, given_routing=True)
+        elif path == "step":
             out = stack.step(t, h0.to(DEV), h_layers=hl)
         else:
             out = stack.token(t, h0.to(DEV))
             hl = stack.h
         torch.cuda.synchronize()
-        if path == "step":
+        if path != "calls":
             assert stack.step_error_word() == 0
         H = hl.cpu().numpy()
         idx = stack.route_idx[t % 3].cpu().numpy()
@@ -96,20 +102,23 @@ def test_full_depth_layer_by_layer(M, name, path):
         for l in range(L):
             x = O.rmsnorm(H[l])
             self_routed = t == 0 or l == 0 or not heads
-            if self_routed:   # the layer's own router + top-K on this input
+            if path == "given":
+                assert np.array_equal(idx[l], gi[l]) and np.array_equal(w[l], gw[l])
+            elif self_routed:   # the layer's own router + top-K on this input
                 routed += _check_topk(O.router_logits(routers_cpu[l], x), idx[l], w[l], K, f"{name} t{t} l{l} router")
             y_ref = O.f64(H[l]).copy()
             for k in range(K):
                 y_ref += float(w[l][k]) * O.expert_ffn_packed(x, *caches[l](idx[l][k]), bits=cfg.bits, group=cfg.group)
             assert_rows_close(H[l + 1][None], y_ref[None], tol=TOL, what=f"{name} t{t} layer {l} output")
-            if heads and l + 1 < L:   # head l: prediction of layer l+1 for token t+1
+            if heads and path != "given" and l + 1 < L:   # head l: prediction of layer l+1 for token t+1
                 lg = O.prerouter_logits(x, idx[l], None if t == 0 else prev_idx[l], heads_cpu[l], E)
                 predicted += _check_topk(lg, nxt_idx[l + 1], nxt_w[l + 1], K, f"{name} t{t} head {l}")
         prev_idx = idx
         log(f"{name} ({path}): token {t} checked at all {L} layers")
     log(f"{name} ({path}): {routed} router top-Ks and {predicted} head predictions compared (others near ties)")
-    assert routed >= L // 2
-    if heads:
-        assert predicted >= L
+    if path != "given":
+        assert routed >= L // 2
+        if heads:
+            assert predicted >= L
     del stack, layers
     _free()
