@@ -69,11 +69,6 @@ struct StepParams {
   uint32_t ws_bytes;
 };
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Tagged-word vectors are plain arrays of 8-byte words; each lives in its own 256-byte-aligned
 // region of the workspace.  (Spreading their 64-byte lines over memory pages was measured slower.)

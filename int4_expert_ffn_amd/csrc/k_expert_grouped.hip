@@ -23,21 +23,25 @@
 namespace moe {
 namespace {
 
-constexpr int GT_WAVES = 4;          // waves per block: 4 x 16 weight rows
-constexpr int KCH = 512;             // columns of token rows staged per LDS pass
-constexpr int XS_STRIDE = KCH + 8;   // halves per staged row (padding spreads LDS banks)
 
 // ------------------------------------------------------------------------------------- sort
-// One block.  counts[E+1], offsets[E+2] (bucket E collects indices outside [0, E)),
-// perm[T*K]: pair indices grouped by expert, ascending inside each expert.
+constexpr int MT = 16;  // token rows per MFMA tile
+
+// One block of 1024 threads.  counts[E+1], offsets[E+2] (bucket E collects indices outside
+// [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles (may
+// be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one (bucket, first
+// sorted position inside the bucket) pair per MT-row tile, buckets in order.
 __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __restrict__ idx,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                               int32_t* __restrict__ perm) {
+                                               int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
+                                               int max_tiles) {
   extern __shared__ int sh[];
   int* run = sh;              // [E+1]
   int* offs = sh + E + 1;     // [E+2]
-  int* ids = offs + E + 2;    // [blockDim]
-  const int tid = threadIdx.x, bs = blockDim.x;
+  int* toff = offs + E + 2;   // [E+2] first tile of each bucket
+  int* ids = toff + E + 2;    // [blockDim]
+  __shared__ int wsum[2][16];
+  const int tid = threadIdx.x, bs = blockDim.x, lane = tid % WAVE, w = tid / WAVE;
   for (int i = tid; i <= E; i += bs) run[i] = 0;
   __syncthreads();
   for (int p = tid; p < TK; p += bs) {
@@ -46,19 +50,58 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
     atomicAdd(&run[e], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e <= E; ++e) {
-      offs[e] = acc;
-      acc += run[e];
+  // exclusive scans of the pair counts and of the tile counts over buckets 0..E (E + 1 <= 2 bs),
+  // two buckets per thread
+  const int b0 = 2 * tid, b1 = b0 + 1;
+  const int c0 = b0 <= E ? run[b0] : 0, c1 = b1 <= E ? run[b1] : 0;
+  const int t0 = (c0 + MT - 1) / MT, t1 = (c1 + MT - 1) / MT;
+  int v = c0 + c1, u = t0 + t1;
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int pv = __shfl_up(v, o), pu = __shfl_up(u, o);
+    if (lane >= o) {
+      v += pv;
+      u += pu;
     }
-    offs[E + 1] = acc;
+  }
+  if (lane == WAVE - 1) {
+    wsum[0][w] = v;
+    wsum[1][w] = u;
+  }
+  __syncthreads();
+  for (int j = 0; j < w; ++j) {
+    v += wsum[0][j];
+    u += wsum[1][j];
+  }
+  const int ev = v - c0 - c1, eu = u - t0 - t1;  // exclusive through bucket b0
+  if (b0 <= E) {
+    offs[b0] = ev;
+    toff[b0] = eu;
+  }
+  if (b1 <= E) {
+    offs[b1] = ev + c0;
+    toff[b1] = eu + t0;
+  }
+  if (b0 == E || b1 == E) {
+    offs[E + 1] = v;
+    toff[E + 1] = u;
   }
   __syncthreads();
   for (int i = tid; i <= E + 1; i += bs) {
     offsets[i] = offs[i];
     if (i <= E) counts[i] = run[i];
   }
+  if (tiles != nullptr) {
+    if (tid == 0) tiles[0] = min(toff[E + 1], max_tiles);
+    for (int e = tid; e <= E; e += bs)
+      for (int j = 0, n = (run[e] + MT - 1) / MT; j < n; ++j) {
+        const int k = toff[e] + j;
+        if (k < max_tiles) {
+          tiles[1 + 2 * k] = e;
+          tiles[2 + 2 * k] = j * MT;
+        }
+      }
+  }
+  __syncthreads();
   for (int i = tid; i <= E; i += bs) run[i] = 0;
   __syncthreads();
   for (int base = 0; base < TK; base += bs) {
@@ -98,6 +141,16 @@ __global__ void __launch_bounds__(256) k_rowscale(int T, int d, const uint16_t* 
 }
 
 // ------------------------------------------------------------------------------------- MFMA core
+constexpr int GW = 8;            // waves per block: GW x 16 weight rows
+constexpr int XCH = 2048;        // columns of the token tile staged per LDS pass (d <= XCH: one pass)
+// Staged rows are read 8 bytes per lane with the 16 lanes of a quad reading 16 different token
+// rows: a row stride of 1 (mod 16) 8-byte bank slots, i.e. 4 (mod 64) halves, puts them in 16
+// different slots, so a half-wave's read takes the minimum two passes (a stride of 10 slots put
+// four lanes on each slot).
+__host__ __device__ constexpr int lds_row_stride(int halves) { return halves + ((4 - halves) % 64 + 64) % 64; }
+constexpr int XS = lds_row_stride(XCH);  // halves per staged row
+constexpr int PF = 4;            // macro steps of weight segments in flight per wave
+
 template <int BITS>
 struct GSeg {
   static constexpr int COLS = SegT<BITS>::COLS;     // columns per lane segment
@@ -106,16 +159,16 @@ struct GSeg {
   static constexpr int PB = BITS == 4 ? 8 : 16;     // columns per permutation block
 };
 
-// Stage 16 rows x KCH columns [c0, c0 + KCH) of the float16 matrix rows listed by `rows`
-// (row < 0 = zero padding) into LDS, permuted per block so that each code pair's two
-// activation columns are adjacent.
+// Stage MT rows x `width` columns [c0, c0 + width) of the float16 matrix rows listed by `rows`
+// (row < 0 = zero padding; columns at or past ncols are zero) into LDS, permuted per block so
+// that each code pair's two activation columns are adjacent.
 template <int BITS>
 __device__ __forceinline__ void stage_rows(uint16_t* xs, const uint16_t* __restrict__ src, int ncols, int c0,
-                                           const int* rows) {
+                                           int width, const int* rows) {
   constexpr int PB = GSeg<BITS>::PB;
-  constexpr int UNITS = 16 * KCH / PB;
-  for (int u = threadIdx.x; u < UNITS; u += blockDim.x) {
-    const int m = u / (KCH / PB), cb = u % (KCH / PB);
+  const int per_row = width / PB, units = MT * per_row;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int m = u / per_row, cb = u % per_row;
     const int col = c0 + cb * PB;
     const int r = rows[m];
     uint32_t outw[PB / 2];
@@ -141,64 +194,111 @@ __device__ __forceinline__ void stage_rows(uint16_t* xs, const uint16_t* __restr
 #pragma unroll
       for (int j = 0; j < PB / 2; ++j) outw[j] = 0;
     }
-    uint4* dst = reinterpret_cast<uint4*>(xs + m * XS_STRIDE + cb * PB);
+    uint4* dst = reinterpret_cast<uint4*>(xs + m * XS + cb * PB);
     dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
     if constexpr (PB == 16) dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
   }
 }
 
-// Dequantise one 16-byte segment to float16 pairs w = fma(code, scale, bias) (pairs in the
-// order the activation pairs use).  Segments at or past `ncols` give zeros.
-template <int BITS, bool SPLIT>
-__device__ __forceinline__ void dequant_segment(const moe_qmat& m, size_t row, int wpr, int ngr, int lg2g,
-                                                int col, int ncols, uint32_t* w) {
-  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
-  constexpr uint32_t MASK = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-  if (col >= ncols) {
-#pragma unroll
-    for (int i = 0; i < 4 * PPW; ++i) w[i] = 0;
-    return;
-  }
-  const uint4 q = *reinterpret_cast<const uint4*>(m.q + row * wpr + (size_t)col * BITS / 32);
+// One lane's weight segment of one macro step, for NMAT matrices: the 16 code bytes and the
+// group scale/bias (two groups when a group is narrower than the segment).
+template <int NMAT, bool SPLIT>
+struct WStage {
+  uint4 q[NMAT];
+  uint16_t sa[NMAT], ba[NMAT], sb[NMAT], bb[NMAT];
+};
+
+// Load the segment starting at column `col` of weight row `row` (col is clamped into the row, so
+// every issue is a valid load and the number of loads in flight never depends on the data).
+template <int BITS, bool SPLIT, int NMAT>
+__device__ __forceinline__ void issue_w(WStage<NMAT, SPLIT>& S, const moe_qmat* mats, size_t row, int wpr, int ngr,
+                                        int lg2g, int ncols, int col) {
+  constexpr int COLS = GSeg<BITS>::COLS;
+  col = min(col, ncols - COLS);
   const size_t ga = row * ngr + (col >> lg2g);
-  const size_t gb = SPLIT ? row * ngr + ((col + SegT<BITS>::COLS / 2) >> lg2g) : ga;
-  const _Float16 sa = __builtin_bit_cast(_Float16, m.scales[ga]), ba = __builtin_bit_cast(_Float16, m.biases[ga]);
-  const _Float16 sb = __builtin_bit_cast(_Float16, m.scales[gb]), bb = __builtin_bit_cast(_Float16, m.biases[gb]);
+#pragma unroll
+  for (int mi = 0; mi < NMAT; ++mi) {
+    S.q[mi] = *reinterpret_cast<const uint4*>(mats[mi].q + row * wpr + (size_t)col * BITS / 32);
+    S.sa[mi] = mats[mi].scales[ga];
+    S.ba[mi] = mats[mi].biases[ga];
+    if constexpr (SPLIT) {
+      const size_t gb = row * ngr + ((col + COLS / 2) >> lg2g);
+      S.sb[mi] = mats[mi].scales[gb];
+      S.bb[mi] = mats[mi].biases[gb];
+    }
+  }
+}
+
+// Dequantise a staged segment to float16 pairs w = fma(code, scale, bias), in the pair order
+// the staged activations use (pair j of a word: codes j and j + PPW, one from each half); a
+// segment past the row end (valid == false) gives zeros.  A code placed in the mantissa under
+// the right exponent reads as (2^e + code) exactly: bits 0..1 / 0..3 under 1024, bits 2..3 under
+// 256, bits 4..5 / 4..7 under 64, bits 6..7 under 16, so one mask-or and one subtract give the
+// code as float16 with no shift for the lower byte of each half (and one shift per word for
+// the upper byte).  mg[] holds the four magic words in registers, so the mask-or is one
+// v_and_or_b32.
+template <int BITS, bool SPLIT>
+__device__ __forceinline__ void dequant_stage(uint4 q, uint16_t sa16, uint16_t ba16, uint16_t sb16, uint16_t bb16,
+                                              bool valid, const uint32_t* mg, uint32_t* w) {
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  if (!SPLIT) {
+    sb16 = sa16;
+    bb16 = ba16;
+  }
+  const _Float16 sa = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sa16 : 0)),
+                 ba = __builtin_bit_cast(_Float16, (uint16_t)(valid ? ba16 : 0));
+  const _Float16 sb = __builtin_bit_cast(_Float16, (uint16_t)(valid ? sb16 : 0)),
+                 bb = __builtin_bit_cast(_Float16, (uint16_t)(valid ? bb16 : 0));
   const half2_t s0 = {sa, sa}, b0 = {ba, ba}, s1 = {sb, sb}, b1 = {bb, bb};
-  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = wd[i], hi = wd[i] >> 8;
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
-      const half2_t c = as_h2(((wd[i] >> (BITS * j)) & MASK) | 0x64006400u) - k1024;
-      const half2_t v = i < 2 ? __builtin_elementwise_fma(c, s0, b0) : __builtin_elementwise_fma(c, s1, b1);
+      // pair j sits at bit BITS*j of each half: in the lower byte for j < PPW / 2
+      const uint32_t src = j < PPW / 2 ? lo : hi;
+      const int jb = j % (PPW / 2);  // position inside the byte, in codes
+      const uint32_t mask = (BITS == 4 ? 0x000F000Fu : 0x00030003u) << (BITS * jb);
+      const int m = BITS == 4 ? 2 * jb : jb;  // magic: 1024, 256, 64, 16 for shifts 0, 2, 4, 6 bits
+      const half2_t c = as_h2((src & mask) | mg[m]);
+      const _Float16 base = (_Float16)(1024 >> (2 * m));
+      const half2_t k = {base, base};
+      const half2_t v = i < 2 ? __builtin_elementwise_fma(c - k, s0, b0) : __builtin_elementwise_fma(c - k, s1, b1);
       w[i * PPW + j] = __builtin_bit_cast(uint32_t, v);
     }
+  }
+}
+
+// The magic words of dequant_stage, kept in vector registers (an opaque copy stops the compiler
+// from folding them back into literals, which v_and_or_b32 cannot take two of).
+__device__ __forceinline__ void magic_words(uint32_t* mg) {
+  mg[0] = 0x64006400u;  // 1024.0
+  mg[1] = 0x5C005C00u;  // 256.0
+  mg[2] = 0x54005400u;  // 64.0
+  mg[3] = 0x4C004C00u;  // 16.0
+  asm volatile("" : "+v"(mg[0]), "+v"(mg[1]), "+v"(mg[2]), "+v"(mg[3]));
 }
 
 __device__ __forceinline__ half4_t pair2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(half4_t, make_uint2(a, b));
 }
 
-// acc += X[16 tokens][c0 .. c0 + KCH) * W[16 rows][same]^T for the wave's 16 rows.
+// acc[mi] += X[MT tokens][one macro step] * W_mi[16 rows][same]^T.
 template <int BITS, bool SPLIT, int NMAT>
-__device__ __forceinline__ void mfma_chunk(const uint16_t* xs, const moe_qmat* mats, size_t row, int wpr, int ngr,
-                                           int lg2g, int ncols, int c0, int ln, int lq, float4_t* acc) {
+__device__ __forceinline__ void consume_w(const WStage<NMAT, SPLIT>& S, bool valid, const uint16_t* xa,
+                                          const uint32_t* mg, float4_t* acc) {
   using GS = GSeg<BITS>;
-  for (int ms = 0; ms < KCH; ms += GS::MACRO) {
-    const int col = c0 + ms + lq * GS::COLS;
-    uint32_t w[NMAT][GS::STEPS * 2];
+  uint32_t w[NMAT][GS::STEPS * 2];
 #pragma unroll
-    for (int mi = 0; mi < NMAT; ++mi) dequant_segment<BITS, SPLIT>(mats[mi], row, wpr, ngr, lg2g, col, ncols, w[mi]);
-    const uint16_t* xa = xs + ln * XS_STRIDE + ms + lq * GS::COLS;
+  for (int mi = 0; mi < NMAT; ++mi)
+    dequant_stage<BITS, SPLIT>(S.q[mi], S.sa[mi], S.ba[mi], S.sb[mi], S.bb[mi], valid, mg, w[mi]);
 #pragma unroll
-    for (int s = 0; s < GS::STEPS; ++s) {
-      const half4_t a = *reinterpret_cast<const half4_t*>(xa + 4 * s);
+  for (int s = 0; s < GS::STEPS; ++s) {
+    const half4_t a = *reinterpret_cast<const half4_t*>(xa + 4 * s);
 #pragma unroll
-      for (int mi = 0; mi < NMAT; ++mi)
-        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[mi], 0, 0, 0);
-    }
+    for (int mi = 0; mi < NMAT; ++mi)
+      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[mi], 0, 0, 0);
   }
 }
 
@@ -216,107 +316,285 @@ __device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) 
   return lr.scale * acc;
 }
 
-// gate/up + SwiGLU for expert blockIdx.x, weight rows blockIdx.y * 64 .. +64.
-// act_sorted[pos][i] (float16) for the expert's sorted pair positions.
-template <int BITS, bool SPLIT>
-__global__ void __launch_bounds__(256) k_grouped_gateup(int K, int E, int d, int I, int lg2g,
-                                                        const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ perm,
-                                                        const float* __restrict__ rowscale, moe_qmat gate,
-                                                        moe_qmat up, uint16_t* __restrict__ act_sorted,
-                                                        LoraRefG lg, LoraRefG lu) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XS_STRIDE];
-  __shared__ int rows[16];
-  const int e = blockIdx.x;
-  if (e >= E) return;
+// One tile of the work list (MT sorted pairs of one expert) against weight rows
+// blockIdx.y * 16 GW .. + 16 GW of NMAT matrices, the input columns in chunks of NST macro steps
+// (columns past ncols are zero).
+//   NMAT == 2: gate/up of the tile's tokens (rows of x), SwiGLU, act_sorted[pos][row] float16;
+//   NMAT == 1: down of the tile's activations (rows of act_sorted), out[pair][row] float32;
+//              tiles of bucket E (indices outside [0, E)) write NaN.
+// The token tile is staged in LDS once per XCH columns; each wave streams its 16 rows with PF
+// macro steps of weight loads in flight, and the barriers order LDS only, so the loads issued
+// before a barrier stay in flight across it.
+template <int BITS, bool SPLIT, int NMAT, int NST>
+__global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncols, int nrows, int lg2g,
+                                                          const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ tiles,
+                                                          const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1,
+                                                          uint16_t* __restrict__ act_sorted, float* __restrict__ out,
+                                                          LoraRefG l0, LoraRefG l1) {
+  using GS = GSeg<BITS>;
+  static_assert(NST % PF == 0 && NST * GS::MACRO <= XCH, "whole stages, one LDS pass per chunk");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XS];
+  __shared__ int rows[MT];
+  if ((int)blockIdx.x >= tiles[0]) return;
+  const int e = tiles[1 + 2 * blockIdx.x], mt = tiles[2 + 2 * blockIdx.x];
   const int beg = offsets[e], n_e = offsets[e + 1] - beg;
-  if (n_e == 0) return;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
-  const int n0 = blockIdx.y * (16 * GT_WAVES) + wave * 16;
-  const bool active = n0 < I;
-  const int wpr = d * BITS / 32, ngr = d >> lg2g;
-  const size_t row = (size_t)e * I + (active ? n0 + ln : 0);
-  const moe_qmat mats[2] = {gate, up};
-  for (int mt = 0; mt < n_e; mt += 16) {
-    float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int c0 = 0; c0 < d; c0 += KCH) {
-      __syncthreads();
-      if (threadIdx.x < 16) {
-        const int pos = mt + threadIdx.x;
-        rows[threadIdx.x] = pos < n_e ? perm[beg + pos] / K : -1;
-      }
-      __syncthreads();
-      stage_rows<BITS>(xs, x, d, c0, rows);
-      __syncthreads();
-      if (active) mfma_chunk<BITS, SPLIT, 2>(xs, mats, row, wpr, ngr, lg2g, d, c0, ln, lq, acc);
-    }
+  const int n0 = blockIdx.y * (16 * GW) + wave * 16;
+  if (e >= E) {
+    if constexpr (NMAT == 1)  // pairs whose expert index is out of range
+      for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
+        if (n0 + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0 + ln] = quiet_nan();
+    return;
+  }
+  if (threadIdx.x < MT) {
+    const int pos = mt + threadIdx.x;
+    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? perm[beg + pos] / K : beg + pos) : -1;
+  }
+  lds_barrier();
+  const bool active = n0 < nrows;  // uniform over the wave
+  const int wpr = ncols * BITS / 32, ngr = ncols >> lg2g;
+  const size_t row = (size_t)e * nrows + (active ? n0 + ln : 0);
+  const moe_qmat mats[2] = {m0, m1};
+  float4_t acc[NMAT];
+#pragma unroll
+  for (int mi = 0; mi < NMAT; ++mi) acc[mi] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t mg[4];
+  magic_words(mg);
+  WStage<NMAT, SPLIT> st[PF];
+  for (int c0 = 0; c0 < ncols; c0 += NST * GS::MACRO) {
+    if (c0 > 0) lds_barrier();  // every wave is done with the previous pass
+    stage_rows<BITS>(xs, src, ncols, c0, NST * GS::MACRO, rows);
+    const int lcol = c0 + lq * GS::COLS;  // this lane's column at macro step 0
     if (active) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = mt + 4 * lq + i;
-        if (pos >= n_e) continue;
-        const int n = n0 + ln;
-        const int t = perm[beg + pos] / K;
-        const float sc = rowscale ? rowscale[t] : 1.f;
-        float g = acc[0][i] * sc, u = acc[1][i] * sc;
-        if (lg.B) g += lora_row_g(lg, t, n);
-        if (lu.B) u += lora_row_g(lu, t, n);
-        act_sorted[(size_t)(beg + pos) * I + n] = f2h(g / (1.f + expf(-g)) * u);
+      for (int u = 0; u < PF; ++u) {
+        issue_w<BITS, SPLIT, NMAT>(st[u], mats, row, wpr, ngr, lg2g, ncols, lcol + u * GS::MACRO);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    lds_barrier();
+    if (!active) continue;
+    const uint16_t* xa = xs + ln * XS + lq * GS::COLS;
+    // The chunk is straight-line code (NST compile-time steps): consume stage step % PF, refill
+    // it PF steps ahead.  In a loop the compiler merges the outstanding loads of the loop's entry
+    // and back edge and its waits turn conservative; unrolled, every wait is exact.  The
+    // scheduling barriers keep each stage's loads together and in program order.
+#pragma unroll
+    for (int step = 0; step < NST; ++step) {
+      consume_w<BITS, SPLIT, NMAT>(st[step % PF], lcol + step * GS::MACRO < ncols, xa + step * GS::MACRO, mg, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + PF < NST) {
+        issue_w<BITS, SPLIT, NMAT>(st[step % PF], mats, row, wpr, ngr, lg2g, ncols, lcol + (step + PF) * GS::MACRO);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = mt + 4 * lq + i;
+    if (pos >= n_e || pos >= mt + MT) continue;
+    const int n = n0 + ln;
+    if constexpr (NMAT == 2) {
+      const int t = perm[beg + pos] / K;
+      const float sc = rowscale ? rowscale[t] : 1.f;
+      float g = acc[0][i] * sc, u = acc[1][i] * sc;
+      if (l0.B) g += lora_row_g(l0, t, n);
+      if (l1.B) u += lora_row_g(l1, t, n);
+      act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
+    } else {
+      const int pr = perm[beg + pos];
+      float o = acc[0][i];
+      if (l0.B) o += lora_row_g(l0, pr / K, n);
+      out[(size_t)pr * nrows + n] = o;
     }
   }
 }
 
-// down projection for expert blockIdx.x, output rows blockIdx.y * 64 .. +64; rows scattered
-// to out[pair][j] (float32, pair = t*K + k).  Bucket E (indices outside [0, E)) writes NaN.
-template <int BITS, bool SPLIT>
-__global__ void __launch_bounds__(256) k_grouped_down(int K, int E, int d, int I, int lg2g,
-                                                      const uint16_t* __restrict__ act_sorted,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ perm, moe_qmat down,
-                                                      float* __restrict__ out, LoraRefG ldn) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XS_STRIDE];
-  __shared__ int rows[16];
-  const int e = blockIdx.x;
+// The same product for 64-column groups, lane-contiguous: in each chunk of W = 4 R columns
+// (R = NST segments), lane (n, q) of a wave streams columns [q R, (q + 1) R) of its weight row, so
+// the scales and biases of the whole chunk are one vector load per array (per-step two-byte
+// loads of them cost as much issue bandwidth as the weight bytes).  Needs the input width a
+// multiple of W and 16-byte aligned rows of scales and biases (the host checks); the token tile
+// is staged with unconditional loads (zero rows selected afterwards) so that every wait stays
+// exact.
+template <int BITS, int NMAT, int NST>
+__global__ void __launch_bounds__(GW * WAVE) k_grouped_mm64(int K, int E, int ncols, int nrows,
+                                                            const uint16_t* __restrict__ src,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ tiles,
+                                                            const float* __restrict__ rowscale, moe_qmat m0,
+                                                            moe_qmat m1, uint16_t* __restrict__ act_sorted,
+                                                            float* __restrict__ out, LoraRefG l0, LoraRefG l1) {
+  using GS = GSeg<BITS>;
+  constexpr int COLS = GS::COLS, R = NST * COLS, W = 4 * R, NG = R / 64, PB = GS::PB;
+  constexpr int PFN = NST < PF ? NST : PF;
+  constexpr int PADR = 8;                  // halves after each lane range
+  constexpr int XSW = lds_row_stride(W + 4 * PADR);  // staged row stride, halves
+  constexpr int UNITS = MT * W / PB, PER_T = UNITS / (GW * WAVE);
+  static_assert(NST % PFN == 0 && NG >= 1 && NG <= 8 && (NG & (NG - 1)) == 0, "whole stages, 1..8 groups per lane");
+  static_assert(UNITS % (GW * WAVE) == 0 && MT * XSW * 2 <= 70 * 1024, "staging layout");
+  static_assert(XSW % 64 == 4 && (R + PADR) % 4 == 0, "conflict-free 8-byte reads");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
+  __shared__ int rows[MT];
+  if ((int)blockIdx.x >= tiles[0]) return;
+  const int e = tiles[1 + 2 * blockIdx.x], mt = tiles[2 + 2 * blockIdx.x];
   const int beg = offsets[e], n_e = offsets[e + 1] - beg;
-  if (n_e == 0) return;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
-  const int n0 = blockIdx.y * (16 * GT_WAVES) + wave * 16;
-  if (e == E) {  // pairs whose expert index is out of range
-    for (int pos = lq; pos < n_e; pos += 4)
-      if (n0 + ln < d) out[(size_t)perm[beg + pos] * d + n0 + ln] = quiet_nan();
+  const int n0 = blockIdx.y * (16 * GW) + wave * 16;
+  if (e >= E) {
+    if constexpr (NMAT == 1)  // pairs whose expert index is out of range
+      for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
+        if (n0 + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0 + ln] = quiet_nan();
     return;
   }
-  const bool active = n0 < d;
-  const int wpr = I * BITS / 32, ngr = I >> lg2g;
-  const size_t row = (size_t)e * d + (active ? n0 + ln : 0);
-  for (int mt = 0; mt < n_e; mt += 16) {
-    float4_t acc[1] = {{0.f, 0.f, 0.f, 0.f}};
-    for (int c0 = 0; c0 < I; c0 += KCH) {
-      __syncthreads();
-      if (threadIdx.x < 16) {
-        const int pos = mt + threadIdx.x;
-        rows[threadIdx.x] = pos < n_e ? beg + pos : -1;
-      }
-      __syncthreads();
-      stage_rows<BITS>(xs, act_sorted, I, c0, rows);
-      __syncthreads();
-      if (active) mfma_chunk<BITS, SPLIT, 1>(xs, &down, row, wpr, ngr, lg2g, I, c0, ln, lq, acc);
-    }
-    if (active) {
+  if (threadIdx.x < MT) {
+    const int pos = mt + threadIdx.x;
+    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? perm[beg + pos] / K : beg + pos) : -1;
+  }
+  lds_barrier();
+  const bool active = n0 < nrows;  // uniform over the wave
+  const int wpr = ncols * BITS / 32, ngr = ncols / 64;
+  const size_t row = (size_t)e * nrows + (active ? n0 + ln : 0);
+  const moe_qmat mats[2] = {m0, m1};
+  const int row0 = rows[0];  // always a real row (the tile holds at least one pair)
+  // the pairs of this lane's four outputs, read now rather than after the last step
+  int pr_out[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = mt + 4 * lq + i;
-        if (pos >= n_e) continue;
-        const int j = n0 + ln;
-        const int pr = perm[beg + pos];
-        float o = acc[0][i];
-        if (ldn.B) o += lora_row_g(ldn, pr / K, j);
-        out[(size_t)pr * d + j] = o;
+  for (int i = 0; i < 4; ++i) pr_out[i] = perm[beg + min(mt + 4 * lq + i, n_e - 1)];
+  float4_t acc[NMAT];
+#pragma unroll
+  for (int mi = 0; mi < NMAT; ++mi) acc[mi] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t mg[4];
+  magic_words(mg);
+  for (int c0 = 0; c0 < ncols; c0 += W) {
+    if (c0 > 0) lds_barrier();  // every wave is done with the previous chunk
+    const int lcol = c0 + lq * R;
+    // this lane's scales and biases for the chunk: NG consecutive groups of its row
+    uint32_t sw[NMAT][NG > 1 ? NG / 2 : 1], bw[NMAT][NG > 1 ? NG / 2 : 1];
+    uint4 q[PFN][NMAT];
+    if (active) {
+      const size_t g0 = row * ngr + (size_t)(lcol / 64);
+#pragma unroll
+      for (int mi = 0; mi < NMAT; ++mi) {
+        if constexpr (NG == 8) {
+          const uint4 s = *reinterpret_cast<const uint4*>(mats[mi].scales + g0);
+          const uint4 b = *reinterpret_cast<const uint4*>(mats[mi].biases + g0);
+          sw[mi][0] = s.x; sw[mi][1] = s.y; sw[mi][2] = s.z; sw[mi][3] = s.w;
+          bw[mi][0] = b.x; bw[mi][1] = b.y; bw[mi][2] = b.z; bw[mi][3] = b.w;
+        } else if constexpr (NG == 4) {
+          const uint2 s = *reinterpret_cast<const uint2*>(mats[mi].scales + g0);
+          const uint2 b = *reinterpret_cast<const uint2*>(mats[mi].biases + g0);
+          sw[mi][0] = s.x; sw[mi][1] = s.y;
+          bw[mi][0] = b.x; bw[mi][1] = b.y;
+        } else if constexpr (NG == 2) {
+          sw[mi][0] = *reinterpret_cast<const uint32_t*>(mats[mi].scales + g0);
+          bw[mi][0] = *reinterpret_cast<const uint32_t*>(mats[mi].biases + g0);
+        } else {
+          sw[mi][0] = mats[mi].scales[g0];
+          bw[mi][0] = mats[mi].biases[g0];
+        }
       }
+#pragma unroll
+      for (int u = 0; u < PFN; ++u)
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi)
+          q[u][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + row * wpr + (size_t)(lcol + u * COLS) * BITS / 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage the token tile: every load unconditional (padding rows read row0, then zeroed)
+    {
+      uint4 xv[PER_T][PB / 8];
+#pragma unroll
+      for (int k = 0; k < PER_T; ++k) {
+        const int u = threadIdx.x + k * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
+        const int r = rows[m];
+        const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)(r >= 0 ? r : row0) * ncols + c0 + cb * PB);
+#pragma unroll
+        for (int h = 0; h < PB / 8; ++h) xv[k][h] = p[h];
+      }
+#pragma unroll
+      for (int k = 0; k < PER_T; ++k) {
+        const int u = threadIdx.x + k * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
+        const bool real = rows[m] >= 0;
+        uint32_t outw[PB / 2];
+        if constexpr (BITS == 4) {
+          const uint4 v = xv[k][0];
+          outw[0] = (v.x & 0xFFFFu) | (v.z << 16);
+          outw[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+          outw[2] = (v.y & 0xFFFFu) | (v.w << 16);
+          outw[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        } else {
+          const uint4 a = xv[k][0], b = xv[k][1];
+          const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = (j & 1) ? (av[j >> 1] >> 16) : (av[j >> 1] & 0xFFFFu);
+            const uint32_t hi = (j & 1) ? (bv[j >> 1] & 0xFFFF0000u) : (bv[j >> 1] << 16);
+            outw[j] = lo | hi;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < PB / 2; ++j) outw[j] = real ? outw[j] : 0u;
+        const int c = cb * PB;
+        uint4* dst = reinterpret_cast<uint4*>(xs + m * XSW + c + (c / R) * PADR);
+        dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+        if constexpr (PB == 16) dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
+      }
+    }
+    lds_barrier();
+    if (!active) continue;
+    const uint16_t* xa = xs + ln * XSW + lq * (R + PADR);
+#pragma unroll
+    for (int step = 0; step < NST; ++step) {
+      const int gi = step * COLS / 64;  // group of this step inside the lane's range (compile time)
+      uint32_t w[NMAT][GS::STEPS * 2];
+#pragma unroll
+      for (int mi = 0; mi < NMAT; ++mi) {
+        const uint32_t sv = sw[mi][gi / 2] >> (16 * (gi % 2)), bv = bw[mi][gi / 2] >> (16 * (gi % 2));
+        dequant_stage<BITS, false>(q[step % PFN][mi], (uint16_t)sv, (uint16_t)bv, 0, 0, true, mg, w[mi]);
+      }
+#pragma unroll
+      for (int s = 0; s < GS::STEPS; ++s) {
+        const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * COLS + 4 * s);
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi)
+          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[mi], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + PFN < NST) {
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi)
+          q[step % PFN][mi] =
+              *reinterpret_cast<const uint4*>(mats[mi].q + row * wpr + (size_t)(lcol + (step + PFN) * COLS) * BITS / 32);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = mt + 4 * lq + i;
+    if (pos >= n_e || pos >= mt + MT) continue;
+    const int n = n0 + ln;
+    if constexpr (NMAT == 2) {
+      const int t = pr_out[i] / K;
+      const float sc = rowscale ? rowscale[t] : 1.f;
+      float g = acc[0][i] * sc, u = acc[1][i] * sc;
+      if (l0.B) g += lora_row_g(l0, t, n);
+      if (l1.B) u += lora_row_g(l1, t, n);
+      act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
+    } else {
+      const int pr = pr_out[i];
+      float o = acc[0][i];
+      if (l0.B) o += lora_row_g(l0, pr / K, n);
+      out[(size_t)pr * nrows + n] = o;
     }
   }
 }
@@ -329,14 +607,56 @@ int ilog2g(int v) {
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Upper bound of the work list's length: every nonempty bucket (at most E + 1 of them, and at
+// most TK) rounds up to whole tiles.
+int max_tiles(int TK, int E) { return (TK + MT - 1) / MT + min(E + 1, TK); }
+
+// Steps per chunk: a short chunk (PF macro steps) when the input row fits in it, else the
+// longest one LDS holds.
+template <int BITS, int NMAT>
+auto grouped_kernel(bool split, int ncols) {
+  constexpr int SHORT = PF, LONG = XCH / GSeg<BITS>::MACRO;
+  const bool shrt = ncols <= SHORT * GSeg<BITS>::MACRO;
+  if constexpr (BITS == 4)
+    return shrt ? k_grouped_mm<4, false, NMAT, SHORT> : k_grouped_mm<4, false, NMAT, LONG>;
+  else
+    return split ? (shrt ? k_grouped_mm<2, true, NMAT, SHORT> : k_grouped_mm<2, true, NMAT, LONG>)
+                 : (shrt ? k_grouped_mm<2, false, NMAT, SHORT> : k_grouped_mm<2, false, NMAT, LONG>);
+}
+
+// The lane-contiguous kernel for 64-column groups: the longest chunk (in segments per lane) that
+// divides the input width, or nullptr when none does or the scale rows are not 16-byte aligned.
+template <int BITS, int NMAT>
+auto grouped_kernel64(int group, int ncols, const moe_qmat* mats) {
+  using KT = decltype(&k_grouped_mm64<BITS, NMAT, 4>);
+  if (group != 64 || (ncols / 64) % 8 != 0) return (KT) nullptr;
+  for (int mi = 0; mi < NMAT; ++mi)
+    if (((uintptr_t)mats[mi].scales | (uintptr_t)mats[mi].biases) & 15) return (KT) nullptr;
+  constexpr int COLS = GSeg<BITS>::COLS;
+  constexpr int LONG = BITS == 4 ? 16 : 8;  // 2048 columns per chunk
+  if (ncols % (4 * LONG * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, LONG>;
+  if (ncols % (4 * 4 * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, 4>;
+  if (ncols % (4 * 2 * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, 2>;
+  return (KT) nullptr;
+}
+
 template <int BITS, bool SPLIT>
 hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowscale, float* o_tk, LoraRefG lg,
                         LoraRefG lu, LoraRefG ldn, const DecodeArgs& a) {
   const int lg2g = ilog2g(a.group);
-  const int rows_per_block = 16 * GT_WAVES;
-  hipError_t err = launch(k_grouped_gateup<BITS, SPLIT>, dim3(a.E, (a.I + rows_per_block - 1) / rows_per_block),
-                          dim3(WAVE * GT_WAVES), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x, (const int32_t*)g.offsets,
-                          (const int32_t*)g.perm, rowscale, a.ex.gate, a.ex.up, (uint16_t*)a.act, lg, lu);
+  const int rows_per_block = 16 * GW;
+  const int nt = max_tiles(a.T * a.K, a.E);
+  const moe_qmat gu[2] = {a.ex.gate, a.ex.up};
+  hipError_t err;
+  if (auto k64 = grouped_kernel64<BITS, 2>(a.group, a.d, gu))
+    err = launch(k64, dim3(nt, (a.I + rows_per_block - 1) / rows_per_block), dim3(WAVE * GW), 0, s, a.K, a.E, a.d,
+                 a.I, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
+                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu);
+  else
+    err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), dim3(nt, (a.I + rows_per_block - 1) / rows_per_block),
+                 dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x, (const int32_t*)g.offsets,
+                 (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up,
+                 (uint16_t*)a.act, (float*)nullptr, lg, lu);
   if (err != hipSuccess) return err;
   if (a.lora3) {
     const int wd = a.T * a.lora3[2].rank;
@@ -344,27 +664,35 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
                         a.lora3[2].A, a.u_down);
     if (err != hipSuccess) return err;
   }
-  return launch(k_grouped_down<BITS, SPLIT>, dim3(a.E + 1, (a.d + rows_per_block - 1) / rows_per_block),
-                dim3(WAVE * GT_WAVES), 0, s, a.K, a.E, a.d, a.I, lg2g, (const uint16_t*)a.act,
-                (const int32_t*)g.offsets, (const int32_t*)g.perm, a.ex.down, o_tk, ldn);
+  if (auto k64 = grouped_kernel64<BITS, 1>(a.group, a.I, &a.ex.down))
+    return launch(k64, dim3(nt, (a.d + rows_per_block - 1) / rows_per_block), dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
+                  a.d, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
+                  (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
+                  LoraRefG{});
+  return launch(grouped_kernel<BITS, 1>(SPLIT, a.I), dim3(nt, (a.d + rows_per_block - 1) / rows_per_block),
+                dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d, lg2g, (const uint16_t*)a.act, (const int32_t*)g.offsets,
+                (const int32_t*)g.perm, (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down,
+                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{});
 }
 
 }  // namespace
 
+size_t grouped_tiles_bytes(int T, int K, int E) { return al256((1 + 2 * (size_t)max_tiles(T * K, E)) * 4); }
+
 size_t grouped_workspace_extra(int T, int K, int E, int d) {
   return al256((size_t)(E + 1) * 4) + al256((size_t)(E + 2) * 4) + al256((size_t)T * K * 4) + al256((size_t)T * 4) +
-         al256((size_t)T * K * d * 4);
+         al256((size_t)T * K * d * 4) + grouped_tiles_bytes(T, K, E);
 }
 
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm) {
-  const size_t lds = (size_t)(E + 1 + E + 2 + 1024) * sizeof(int);
-  return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm);
+                       int32_t* perm, int32_t* tiles) {
+  const size_t lds = (size_t)(E + 1 + 2 * (E + 2) + 1024) * sizeof(int);
+  return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK, E));
 }
 
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   const DecodeArgs& a = g.base;
-  hipError_t err = launch_sort(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm);
+  hipError_t err = launch_sort(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm, g.tiles);
   if (err != hipSuccess) return err;
   float* rowscale = nullptr;
   if (a.flags & MOE_INPUT_RMSNORM) {

@@ -170,7 +170,9 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
     const size_t o_perm = o_offsets + align_up((size_t)(ex->n_experts + 2) * sizeof(int32_t));
     const size_t o_rowscale = o_perm + align_up((size_t)T * K * sizeof(int32_t));
     const size_t o_osorted = o_rowscale + align_up((size_t)T * sizeof(float));
+    const size_t o_tiles = o_osorted + align_up((size_t)T * K * ex->d_model * sizeof(float));
     g.counts = (int32_t*)(gb + o_counts);
+    g.tiles = (int32_t*)(gb + o_tiles);
     g.offsets = (int32_t*)(gb + o_offsets);
     g.perm = (int32_t*)(gb + o_perm);
     g.rowscale = (float*)(gb + o_rowscale);
@@ -184,7 +186,7 @@ moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, con
                               int32_t* offsets, int32_t* perm) {
   if (T < 1 || K < 1 || E < 1 || E > MOE_MAX_E || (int64_t)T * K > (1 << 24)) return MOE_ERR_INVALID_ARG;
   if (!idx || !counts || !offsets || !perm) return MOE_ERR_INVALID_ARG;
-  return from_hip(launch_sort((hipStream_t)stream, T * K, E, idx, counts, offsets, perm));
+  return from_hip(launch_sort((hipStream_t)stream, T * K, E, idx, counts, offsets, perm, nullptr));
 }
 
 size_t moe_decode_workspace_size(const moe_decode_stack* st) {

@@ -80,6 +80,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // ---------------------------------------------------------------------------------------------
 // Segment geometry per code width.
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it
+// (a plain __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int BITS>
 struct SegT;
 template <>

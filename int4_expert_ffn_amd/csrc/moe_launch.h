@@ -52,11 +52,13 @@ struct GroupedArgs {
   int32_t* perm;      // workspace [T*K]
   float* rowscale;    // workspace [T]
   float* o_sorted;    // workspace [T*K][d] float32 (used when out == nullptr)
+  int32_t* tiles;     // workspace: the grouped GEMMs' work list (count, then (bucket, position) pairs)
 };
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& a);
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm);
+                       int32_t* perm, int32_t* tiles);
 size_t grouped_workspace_extra(int T, int K, int E, int d);
+size_t grouped_tiles_bytes(int T, int K, int E);
 
 // whole-token persistent decode -----------------------------------------------------------------
 bool decode_step_supported(const moe_decode_stack& st);

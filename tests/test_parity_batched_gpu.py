@@ -111,6 +111,12 @@ def test_grouped_rmsnorm(M):
     (4, 32, 96, 160, 5, 3),      # ragged rows and columns: partial MFMA tiles, zero-padded chunks
     (4, 64, 1088, 576, 6, 2),    # d and I not multiples of the 512-column LDS chunk
     (4, 32, 256, 128, 16, 16),   # K = E
+    # 64-column groups with 16-byte aligned scale rows: the lane-contiguous kernel, with one and
+    # several chunks and each chunk length
+    (4, 64, 1024, 512, 8, 2),
+    (4, 64, 4096, 1536, 8, 2),
+    (2, 64, 2048, 512, 8, 3),
+    (2, 64, 512, 1024, 6, 2),
 ])
 def test_grouped_shapes(M, bits, group, d, I, E, K):
     cfg = replace(S.CONFIGS["tiny"], name=f"g{bits}-{group}-{d}-{I}", bits=bits, group=group, d=d, I=I, E=E, K=K)
