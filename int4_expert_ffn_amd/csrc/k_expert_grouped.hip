@@ -39,7 +39,8 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
   int* run = sh;              // [E+1]
   int* offs = sh + E + 1;     // [E+2]
   int* toff = offs + E + 2;   // [E+2] first tile of each bucket
-  int* ids = toff + E + 2;    // [blockDim]
+  int* ctot = toff + E + 2;   // [E+1] pairs of each bucket in the current chunk
+  int* hist = ctot + E + 1;   // [bs / WAVE][E+1] per-wave bucket counts of a chunk, then their prefixes
   __shared__ int wsum[2][16];
   const int tid = threadIdx.x, bs = blockDim.x, lane = tid % WAVE, w = tid / WAVE;
   for (int i = tid; i <= E; i += bs) run[i] = 0;
@@ -103,23 +104,36 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
   }
   __syncthreads();
   for (int i = tid; i <= E; i += bs) run[i] = 0;
-  __syncthreads();
+  // Stable placement, one chunk of bs pairs at a time: a pair's position in its bucket is the
+  // bucket's start + the pairs of earlier chunks + those of earlier waves of this chunk (per-wave
+  // histograms, prefixed over waves) + those of earlier lanes of its own wave.
+  const int nwv = bs / WAVE;
   for (int base = 0; base < TK; base += bs) {
+    for (int i = tid; i < nwv * (E + 1); i += bs) hist[i] = 0;
+    __syncthreads();
     const int p = base + tid;
     int e = -1;
     if (p < TK) {
       e = idx[p];
       if ((unsigned)e >= (unsigned)E) e = E;
+      atomicAdd(&hist[w * (E + 1) + e], 1);
     }
-    ids[tid] = e;
+    int rank = 0;  // earlier lanes of this wave with the same bucket
+    for (int j = 0; j < WAVE; ++j) rank += (j < lane && __builtin_amdgcn_readlane(e, j) == e) ? 1 : 0;
     __syncthreads();
-    if (p < TK) {
-      int rank = 0;
-      for (int j = 0; j < tid; ++j) rank += ids[j] == e;
-      perm[offs[e] + run[e] + rank] = p;
+    for (int b2 = tid; b2 <= E; b2 += bs) {  // prefix over waves, per bucket
+      int acc = 0;
+      for (int v = 0; v < nwv; ++v) {
+        const int c = hist[v * (E + 1) + b2];
+        hist[v * (E + 1) + b2] = acc;
+        acc += c;
+      }
+      ctot[b2] = acc;
     }
     __syncthreads();
-    if (p < TK) atomicAdd(&run[e], 1);
+    if (p < TK) perm[offs[e] + run[e] + hist[w * (E + 1) + e] + rank] = p;
+    __syncthreads();
+    for (int b2 = tid; b2 <= E; b2 += bs) run[b2] += ctot[b2];
     __syncthreads();
   }
 }
@@ -308,11 +322,23 @@ struct LoraRefG {
   int rank;
   float scale;
 };
+// (alpha / rank) * B[row] . u[t]: rank 16 (the common case) as two 16-byte reads of B and four of
+// u issued together; other ranks element by element.
 __device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) {
   const uint16_t* b = lr.B + (size_t)row * lr.rank;
   const float* u = lr.u + (size_t)t * lr.rank;
   float acc = 0.f;
-  for (int r = 0; r < lr.rank; ++r) acc = fmaf(h2f(b[r]), u[r], acc);
+  if (lr.rank == 16 && (((uintptr_t)lr.B | (uintptr_t)lr.u) & 15) == 0) {
+    const uint4 b0 = reinterpret_cast<const uint4*>(b)[0], b1 = reinterpret_cast<const uint4*>(b)[1];
+    const float4 u0 = reinterpret_cast<const float4*>(u)[0], u1 = reinterpret_cast<const float4*>(u)[1];
+    const float4 u2 = reinterpret_cast<const float4*>(u)[2], u3 = reinterpret_cast<const float4*>(u)[3];
+    const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    const float uv[16] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w, u2.x, u2.y, u2.z, u2.w, u3.x, u3.y, u3.z, u3.w};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc = fmaf(h2f((uint16_t)(bw[r / 2] >> (16 * (r % 2)))), uv[r], acc);
+  } else {
+    for (int r = 0; r < lr.rank; ++r) acc = fmaf(h2f(b[r]), u[r], acc);
+  }
   return lr.scale * acc;
 }
 
@@ -686,7 +712,7 @@ size_t grouped_workspace_extra(int T, int K, int E, int d) {
 
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* tiles) {
-  const size_t lds = (size_t)(E + 1 + 2 * (E + 2) + 1024) * sizeof(int);
+  const size_t lds = (size_t)(2 * (E + 1) + 2 * (E + 2) + 16 * (E + 1)) * sizeof(int);  // 1024 threads = 16 waves
   return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK, E));
 }
 

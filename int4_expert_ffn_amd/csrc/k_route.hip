@@ -76,6 +76,72 @@ __global__ void __launch_bounds__(64) k_router(int T, int d, int E, uint32_t fla
   }
 }
 
+// The same logits for many tokens at once, on the matrix cores: logits = X W^T with X [T][d] and
+// W [E][d] both K-contiguous.  A block computes one 16-token x 16-expert tile; its waves split the
+// d columns (at most RK each) and each wave issues all of its loads at once, straight from memory
+// (both operands stay in L2), before its MFMAs (v_mfma_f32_16x16x16_f16; D lane (n, q) holds rows
+// 4q..4q+3 of column n).  A lane reads 8 consecutive halves of its row per load and feeds them to
+// two MFMA steps; X and W use the same column order, which is all a dot product needs.  With
+// MOE_INPUT_RMSNORM each token's sum of squares comes from the same X reads.  The partial tiles
+// meet in LDS.  Needs T and E multiples of 16, d of 32 and 16-byte aligned rows (the host checks).
+constexpr int RK = 512;                      // columns per wave
+constexpr int RK_LOADS = RK / 32;            // 16-byte loads per lane and operand
+constexpr int R_MAXW = MOE_MAX_D / RK;       // waves per block at most
+
+__global__ void __launch_bounds__(R_MAXW * WAVE) k_router_mfma(int T, int d, int E, uint32_t flags,
+                                                               const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ W,
+                                                               float* __restrict__ logits) {
+  __shared__ float part[R_MAXW][WAVE][5];
+  const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+  const int m = lane % 16, q = lane / 16;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int c0 = wave * RK;
+  const uint16_t* xr = x + (size_t)(t0 + m) * d + 8 * q;
+  const uint16_t* wr = W + (size_t)(e0 + m) * d + 8 * q;
+  uint4 a[RK_LOADS], b[RK_LOADS];
+#pragma unroll
+  for (int i = 0; i < RK_LOADS; ++i) {
+    const int c = min(c0 + 32 * i, d - 32);  // clamped: every load valid, extra ones ignored below
+    a[i] = *reinterpret_cast<const uint4*>(xr + c);
+    b[i] = *reinterpret_cast<const uint4*>(wr + c);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic: one memory latency in all
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < RK_LOADS; ++i) {
+    if (c0 + 32 * i >= d) break;  // uniform
+    const half4_t a0 = __builtin_bit_cast(half4_t, make_uint2(a[i].x, a[i].y));
+    const half4_t a1 = __builtin_bit_cast(half4_t, make_uint2(a[i].z, a[i].w));
+    const half4_t b0 = __builtin_bit_cast(half4_t, make_uint2(b[i].x, b[i].y));
+    const half4_t b1 = __builtin_bit_cast(half4_t, make_uint2(b[i].z, b[i].w));
+    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, b1, acc, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sq = fmaf((float)a0[j], (float)a0[j], fmaf((float)a1[j], (float)a1[j], sq));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][lane][i] = acc[i];
+  part[wave][lane][4] = sq;
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < nw; ++w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += part[w][lane][i];
+    sq += part[w][lane][4];
+  }
+  float s[4] = {1.f, 1.f, 1.f, 1.f};
+  if (flags & MOE_INPUT_RMSNORM) {
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);  // every lane of row m now holds the row's sum of squares
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = 1.f / sqrtf(__shfl(sq, 4 * q + i) / (float)d + RMS_EPS);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) logits[(size_t)(t0 + 4 * q + i) * E + e0 + m] = acc[i] * s[i];
+}
+
 __device__ __forceinline__ uint32_t order_bits(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0;  // -0 ranks as +0 (equal logits tie to the lower index)
@@ -261,6 +327,9 @@ constexpr int TPW = 16;  // tokens per wave in the matvecs
 
 hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags, const uint16_t* x,
                               const uint16_t* w, float* logits) {
+  if (T >= 32 && T % 16 == 0 && E % 16 == 0 && d % 32 == 0 && d <= MOE_MAX_D && (((uintptr_t)x | (uintptr_t)w) & 15) == 0)
+    return launch(k_router_mfma, dim3(T / 16, E / 16), dim3((d + RK - 1) / RK * WAVE), 0, s, T, d, E, flags, x, w,
+                  logits);
   const dim3 grid(E, (T + TPW - 1) / TPW);
   switch (nseg_for(d)) {
     case 1: return launch(k_router<1>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);

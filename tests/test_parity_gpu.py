@@ -72,7 +72,7 @@ def test_topk_from_logits(M, E, K, renorm):
 def test_router_topk(M, name, rms):
     cfg = S.CONFIGS[name]
     syn = S.Synth(cfg)
-    T = {"batched": 256, "tiny": 64}.get(name, 8)
+    T = {"batched": 256, "tiny": 64, "large-int4": 48}.get(name, 8)  # T >= 32: the MFMA router
     wr = syn.router(0)
     h, redraws = gap_tokens(syn, O.f64(wr.numpy()), T, cfg.K, rmsnorm=rms)
     log(f"{name}: {T} tokens, {redraws} redraws for the logit gap")
