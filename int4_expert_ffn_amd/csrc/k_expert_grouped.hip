@@ -164,6 +164,8 @@ constexpr int XCH = 2048;        // columns of the token tile staged per LDS pas
 __host__ __device__ constexpr int lds_row_stride(int halves) { return halves + ((4 - halves) % 64 + 64) % 64; }
 constexpr int XS = lds_row_stride(XCH);  // halves per staged row
 constexpr int PF = 4;            // macro steps of weight segments in flight per wave
+constexpr int PF64 = 3;          // the same for the lane-contiguous kernel (4 would need more than
+                                 // 128 registers and leave one block per compute unit)
 
 template <int BITS>
 struct GSeg {
@@ -441,31 +443,34 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
   }
 }
 
-// The same product for 64-column groups, lane-contiguous: in each chunk of W = 4 R columns
-// (R = NST segments), lane (n, q) of a wave streams columns [q R, (q + 1) R) of its weight row, so
-// the scales and biases of the whole chunk are one vector load per array (per-step two-byte
-// loads of them cost as much issue bandwidth as the weight bytes).  Needs the input width a
-// multiple of W and 16-byte aligned rows of scales and biases (the host checks); the token tile
-// is staged with unconditional loads (zero rows selected afterwards) so that every wait stays
-// exact.
-template <int BITS, int NMAT, int NST>
-__global__ void __launch_bounds__(GW * WAVE) k_grouped_mm64(int K, int E, int ncols, int nrows,
-                                                            const uint16_t* __restrict__ src,
-                                                            const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ perm,
-                                                            const int32_t* __restrict__ tiles,
-                                                            const float* __restrict__ rowscale, moe_qmat m0,
-                                                            moe_qmat m1, uint16_t* __restrict__ act_sorted,
-                                                            float* __restrict__ out, LoraRefG l0, LoraRefG l1) {
+// The same product for 64-column groups without per-step scale loads.  The columns are walked as
+// in k_grouped_mm (at each macro step the four lanes of a row read 64 contiguous bytes, so every
+// line is used whole within two steps), but the chunk's scales and biases of a row are loaded
+// once: each of the row's four lanes reads a quarter of them (NG groups, one vector load per
+// array) and packs scale | bias << 16 per group; at each step a lane takes the word of its
+// group from the lane that holds it with ds_bpermute, which spends no vector-memory issue slot
+// (per-step two-byte loads of them cost as much issue bandwidth as the weight bytes).  Needs the
+// input width a multiple of the chunk and 16-byte aligned rows of scales and biases (the host
+// checks); the token tile is staged with unconditional loads (zero rows selected afterwards) so
+// that every wait stays exact.
+template <int BITS, int NMAT, int NST, int RG>
+__global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(BITS == 4 || NMAT == 1 ? 4 : 3)))
+k_grouped_mm64(
+    int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
+    moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1) {
   using GS = GSeg<BITS>;
-  constexpr int COLS = GS::COLS, R = NST * COLS, W = 4 * R, NG = R / 64, PB = GS::PB;
-  constexpr int PFN = NST < PF ? NST : PF;
-  constexpr int PADR = 8;                  // halves after each lane range
-  constexpr int XSW = lds_row_stride(W + 4 * PADR);  // staged row stride, halves
+  constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
+  constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
+  constexpr int GPS = MACRO / 64;         // groups per macro step (2 for int4, 4 for int2)
+  constexpr int LPG = 4 / GPS;            // lanes of a row per group at one step (2, 1)
+  constexpr int PFD = BITS == 4 ? PF64 : 2;  // 2-bit: one stage fewer keeps it within 128 registers
+  constexpr int PFN = NST < PFD ? NST : PFD;
+  constexpr int XSW = lds_row_stride(W);
   constexpr int UNITS = MT * W / PB, PER_T = UNITS / (GW * WAVE);
-  static_assert(NST % PFN == 0 && NG >= 1 && NG <= 8 && (NG & (NG - 1)) == 0, "whole stages, 1..8 groups per lane");
-  static_assert(UNITS % (GW * WAVE) == 0 && MT * XSW * 2 <= 70 * 1024, "staging layout");
-  static_assert(XSW % 64 == 4 && (R + PADR) % 4 == 0, "conflict-free 8-byte reads");
+  constexpr int NHALF = PER_T >= 2 ? 2 : 1;
+  static_assert(NG >= 1 && NG <= 8 && (NG & (NG - 1)) == 0, "1..8 groups per lane");
+  static_assert(UNITS % (NHALF * GW * WAVE) == 0 && MT * XSW * 2 <= 70 * 1024, "staging layout");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
   __shared__ int rows[MT];
   if ((int)blockIdx.x >= tiles[0]) return;
@@ -473,11 +478,13 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm64(int K, int E, int nc
   const int beg = offsets[e], n_e = offsets[e + 1] - beg;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
-  const int n0 = blockIdx.y * (16 * GW) + wave * 16;
+  // row group rg of this wave: weight rows n0(rg) .. + 16
+  auto n0 = [&](int rg) { return (int)blockIdx.y * (16 * GW * RG) + rg * 16 * GW + wave * 16; };
   if (e >= E) {
     if constexpr (NMAT == 1)  // pairs whose expert index is out of range
-      for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
-        if (n0 + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0 + ln] = quiet_nan();
+      for (int rg = 0; rg < RG; ++rg)
+        for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
+          if (n0(rg) + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0(rg) + ln] = quiet_nan();
     return;
   }
   if (threadIdx.x < MT) {
@@ -485,79 +492,101 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm64(int K, int E, int nc
     rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? perm[beg + pos] / K : beg + pos) : -1;
   }
   lds_barrier();
-  const bool active = n0 < nrows;  // uniform over the wave
+  const bool active = n0(0) < nrows;  // uniform over the wave (later row groups checked at the stores)
   const int wpr = ncols * BITS / 32, ngr = ncols / 64;
-  const size_t row = (size_t)e * nrows + (active ? n0 + ln : 0);
+  // weight row of row group rg, clamped into the expert so that every load is valid
+  auto wrow = [&](int rg) { return (size_t)e * nrows + min(n0(rg) + ln, nrows - 1); };
   const moe_qmat mats[2] = {m0, m1};
   const int row0 = rows[0];  // always a real row (the tile holds at least one pair)
   // the pairs of this lane's four outputs, read now rather than after the last step
   int pr_out[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr_out[i] = perm[beg + min(mt + 4 * lq + i, n_e - 1)];
-  float4_t acc[NMAT];
+  float4_t acc[RG][NMAT];
 #pragma unroll
-  for (int mi = 0; mi < NMAT; ++mi) acc[mi] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int mi = 0; mi < NMAT; ++mi) acc[rg][mi] = float4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t mg[4];
   magic_words(mg);
   for (int c0 = 0; c0 < ncols; c0 += W) {
     if (c0 > 0) lds_barrier();  // every wave is done with the previous chunk
-    const int lcol = c0 + lq * R;
-    // this lane's scales and biases for the chunk: NG consecutive groups of its row
-    uint32_t sw[NMAT][NG > 1 ? NG / 2 : 1], bw[NMAT][NG > 1 ? NG / 2 : 1];
+    const int lcol = c0 + lq * COLS;  // this lane's column at macro step 0
+    uint32_t sbw[RG][NMAT][NG];       // scale | bias << 16 of groups [c0 / 64 + lq NG, + NG) of each row
     uint4 q[PFN][NMAT];
     if (active) {
-      const size_t g0 = row * ngr + (size_t)(lcol / 64);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+      const size_t g0 = wrow(rg) * ngr + (size_t)(c0 / 64 + lq * NG);
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi) {
+        uint16_t sv[NG], bv[NG];
         if constexpr (NG == 8) {
-          const uint4 s = *reinterpret_cast<const uint4*>(mats[mi].scales + g0);
-          const uint4 b = *reinterpret_cast<const uint4*>(mats[mi].biases + g0);
-          sw[mi][0] = s.x; sw[mi][1] = s.y; sw[mi][2] = s.z; sw[mi][3] = s.w;
-          bw[mi][0] = b.x; bw[mi][1] = b.y; bw[mi][2] = b.z; bw[mi][3] = b.w;
+          const uint4 s4 = *reinterpret_cast<const uint4*>(mats[mi].scales + g0);
+          const uint4 b4 = *reinterpret_cast<const uint4*>(mats[mi].biases + g0);
+          const uint32_t sa[4] = {s4.x, s4.y, s4.z, s4.w}, ba[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            sv[j] = (uint16_t)(sa[j / 2] >> (16 * (j % 2)));
+            bv[j] = (uint16_t)(ba[j / 2] >> (16 * (j % 2)));
+          }
         } else if constexpr (NG == 4) {
-          const uint2 s = *reinterpret_cast<const uint2*>(mats[mi].scales + g0);
-          const uint2 b = *reinterpret_cast<const uint2*>(mats[mi].biases + g0);
-          sw[mi][0] = s.x; sw[mi][1] = s.y;
-          bw[mi][0] = b.x; bw[mi][1] = b.y;
+          const uint2 s2 = *reinterpret_cast<const uint2*>(mats[mi].scales + g0);
+          const uint2 b2 = *reinterpret_cast<const uint2*>(mats[mi].biases + g0);
+          const uint32_t sa[2] = {s2.x, s2.y}, ba[2] = {b2.x, b2.y};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sv[j] = (uint16_t)(sa[j / 2] >> (16 * (j % 2)));
+            bv[j] = (uint16_t)(ba[j / 2] >> (16 * (j % 2)));
+          }
         } else if constexpr (NG == 2) {
-          sw[mi][0] = *reinterpret_cast<const uint32_t*>(mats[mi].scales + g0);
-          bw[mi][0] = *reinterpret_cast<const uint32_t*>(mats[mi].biases + g0);
+          const uint32_t s1 = *reinterpret_cast<const uint32_t*>(mats[mi].scales + g0);
+          const uint32_t b1 = *reinterpret_cast<const uint32_t*>(mats[mi].biases + g0);
+          sv[0] = (uint16_t)s1; sv[1] = (uint16_t)(s1 >> 16);
+          bv[0] = (uint16_t)b1; bv[1] = (uint16_t)(b1 >> 16);
         } else {
-          sw[mi][0] = mats[mi].scales[g0];
-          bw[mi][0] = mats[mi].biases[g0];
+          sv[0] = mats[mi].scales[g0];
+          bv[0] = mats[mi].biases[g0];
         }
+#pragma unroll
+        for (int j = 0; j < NG; ++j) sbw[rg][mi][j] = (uint32_t)sv[j] | ((uint32_t)bv[j] << 16);
+      }
       }
 #pragma unroll
       for (int u = 0; u < PFN; ++u)
 #pragma unroll
         for (int mi = 0; mi < NMAT; ++mi)
-          q[u][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + row * wpr + (size_t)(lcol + u * COLS) * BITS / 32);
+          q[u][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + wrow(u / NST) * wpr +
+                                                     (size_t)(lcol + (u % NST) * MACRO) * BITS / 32);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // stage the token tile: every load unconditional (padding rows read row0, then zeroed)
-    {
-      uint4 xv[PER_T][PB / 8];
+    // stage the token tile: every load unconditional (padding rows read row0, then zeroed), in
+    // two halves to bound the registers it holds
 #pragma unroll
-      for (int k = 0; k < PER_T; ++k) {
-        const int u = threadIdx.x + k * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
+    for (int half = 0; half < NHALF; ++half) {
+      constexpr int HT = PER_T / NHALF;
+      uint4 xv[HT][PB / 8];
+#pragma unroll
+      for (int kk = 0; kk < HT; ++kk) {
+        const int u = threadIdx.x + (half * HT + kk) * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
         const int r = rows[m];
         const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)(r >= 0 ? r : row0) * ncols + c0 + cb * PB);
 #pragma unroll
-        for (int h = 0; h < PB / 8; ++h) xv[k][h] = p[h];
+        for (int h = 0; h < PB / 8; ++h) xv[kk][h] = p[h];
       }
 #pragma unroll
-      for (int k = 0; k < PER_T; ++k) {
-        const int u = threadIdx.x + k * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
+      for (int kk = 0; kk < HT; ++kk) {
+        const int u = threadIdx.x + (half * HT + kk) * GW * WAVE, m = u / (W / PB), cb = u % (W / PB);
         const bool real = rows[m] >= 0;
         uint32_t outw[PB / 2];
         if constexpr (BITS == 4) {
-          const uint4 v = xv[k][0];
+          const uint4 v = xv[kk][0];
           outw[0] = (v.x & 0xFFFFu) | (v.z << 16);
           outw[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
           outw[2] = (v.y & 0xFFFFu) | (v.w << 16);
           outw[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
         } else {
-          const uint4 a = xv[k][0], b = xv[k][1];
+          const uint4 a = xv[kk][0], b = xv[kk][1];
           const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -568,57 +597,67 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm64(int K, int E, int nc
         }
 #pragma unroll
         for (int j = 0; j < PB / 2; ++j) outw[j] = real ? outw[j] : 0u;
-        const int c = cb * PB;
-        uint4* dst = reinterpret_cast<uint4*>(xs + m * XSW + c + (c / R) * PADR);
+        uint4* dst = reinterpret_cast<uint4*>(xs + m * XSW + cb * PB);
         dst[0] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
         if constexpr (PB == 16) dst[1] = make_uint4(outw[4], outw[5], outw[6], outw[7]);
       }
     }
     lds_barrier();
     if (!active) continue;
-    const uint16_t* xa = xs + ln * XSW + lq * (R + PADR);
+    const uint16_t* xa = xs + ln * XSW + lq * COLS;
+    const int sub = lq / LPG;  // which of the step's groups this lane's segment lies in
 #pragma unroll
-    for (int step = 0; step < NST; ++step) {
-      const int gi = step * COLS / 64;  // group of this step inside the lane's range (compile time)
+    for (int f = 0; f < RG * NST; ++f) {  // row group f / NST, macro step f % NST
+      const int rg = f / NST, step = f % NST;
       uint32_t w[NMAT][GS::STEPS * 2];
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi) {
-        const uint32_t sv = sw[mi][gi / 2] >> (16 * (gi % 2)), bv = bw[mi][gi / 2] >> (16 * (gi % 2));
-        dequant_stage<BITS, false>(q[step % PFN][mi], (uint16_t)sv, (uint16_t)bv, 0, 0, true, mg, w[mi]);
+        // group step * GPS + g of the chunk lives in lane (ln, (step GPS + g) / NG), element (...) % NG
+        uint32_t pick = 0;
+#pragma unroll
+        for (int g = 0; g < GPS; ++g) {
+          const int G = step * GPS + g;
+          const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((ln + 16 * (G / NG)) * 4, (int)sbw[rg][mi][G % NG]);
+          pick = sub == g ? v : pick;
+        }
+        dequant_stage<BITS, false>(q[f % PFN][mi], (uint16_t)pick, (uint16_t)(pick >> 16), 0, 0, true, mg, w[mi]);
       }
 #pragma unroll
       for (int s = 0; s < GS::STEPS; ++s) {
-        const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * COLS + 4 * s);
+        const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * MACRO + 4 * s);
 #pragma unroll
         for (int mi = 0; mi < NMAT; ++mi)
-          acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[mi], 0, 0, 0);
+          acc[rg][mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[rg][mi], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (step + PFN < NST) {
+      if (f + PFN < RG * NST) {
+        const int fn = f + PFN;
 #pragma unroll
         for (int mi = 0; mi < NMAT; ++mi)
-          q[step % PFN][mi] =
-              *reinterpret_cast<const uint4*>(mats[mi].q + row * wpr + (size_t)(lcol + (step + PFN) * COLS) * BITS / 32);
+          q[f % PFN][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + wrow(fn / NST) * wpr +
+                                                           (size_t)(lcol + (fn % NST) * MACRO) * BITS / 32);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
   if (!active) return;
 #pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pos = mt + 4 * lq + i;
-    if (pos >= n_e || pos >= mt + MT) continue;
-    const int n = n0 + ln;
+    const int n = n0(rg) + ln;
+    if (pos >= n_e || pos >= mt + MT || n >= nrows) continue;
     if constexpr (NMAT == 2) {
       const int t = pr_out[i] / K;
       const float sc = rowscale ? rowscale[t] : 1.f;
-      float g = acc[0][i] * sc, u = acc[1][i] * sc;
+      float g = acc[rg][0][i] * sc, u = acc[rg][1][i] * sc;
       if (l0.B) g += lora_row_g(l0, t, n);
       if (l1.B) u += lora_row_g(l1, t, n);
       act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
     } else {
       const int pr = pr_out[i];
-      float o = acc[0][i];
+      float o = acc[rg][0][i];
       if (l0.B) o += lora_row_g(l0, pr / K, n);
       out[(size_t)pr * nrows + n] = o;
     }
@@ -653,18 +692,30 @@ auto grouped_kernel(bool split, int ncols) {
 // The lane-contiguous kernel for 64-column groups: the longest chunk (in segments per lane) that
 // divides the input width, or nullptr when none does or the scale rows are not 16-byte aligned.
 template <int BITS, int NMAT>
-auto grouped_kernel64(int group, int ncols, const moe_qmat* mats) {
-  using KT = decltype(&k_grouped_mm64<BITS, NMAT, 4>);
+auto grouped_kernel64(int group, int ncols, const moe_qmat* mats, bool many_tiles) {
+  using KT = decltype(&k_grouped_mm64<BITS, NMAT, 4, 1>);
   if (group != 64 || (ncols / 64) % 8 != 0) return (KT) nullptr;
   for (int mi = 0; mi < NMAT; ++mi)
     if (((uintptr_t)mats[mi].scales | (uintptr_t)mats[mi].biases) & 15) return (KT) nullptr;
-  constexpr int COLS = GSeg<BITS>::COLS;
-  constexpr int LONG = BITS == 4 ? 16 : 8;  // 2048 columns per chunk
-  if (ncols % (4 * LONG * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, LONG>;
-  if (ncols % (4 * 4 * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, 4>;
-  if (ncols % (4 * 2 * COLS) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, 2>;
+  constexpr int MACRO = GSeg<BITS>::MACRO;
+  constexpr int LONG = XCH / MACRO;  // 2048 columns per chunk
+  // short chunks take several row groups per wave (one staged tile and prologue serve more rows)
+  // Short chunks take four row groups per wave when the work list is long (one staged tile and
+  // prologue then serve four times the rows); a short list keeps one so that it still spreads
+  // over the chip.  (Two matrices' accumulators for four groups would spill.)
+  constexpr int RGS = NMAT == 1 ? 4 : 1;
+  if (ncols % (LONG * MACRO) == 0) return (KT)&k_grouped_mm64<BITS, NMAT, LONG, 1>;
+  if (ncols % (4 * MACRO) == 0)
+    return many_tiles ? (KT)&k_grouped_mm64<BITS, NMAT, 4, RGS> : (KT)&k_grouped_mm64<BITS, NMAT, 4, 1>;
+  if (ncols % (2 * MACRO) == 0)
+    return many_tiles ? (KT)&k_grouped_mm64<BITS, NMAT, 2, RGS> : (KT)&k_grouped_mm64<BITS, NMAT, 2, 1>;
   return (KT) nullptr;
 }
+
+// Row groups per wave of the kernel grouped_kernel64 picks for an input width.
+template <int NMAT>
+int rg64(int ncols, bool many_tiles) { return ncols % XCH == 0 || NMAT == 2 || !many_tiles ? 1 : 4; }
+constexpr int MANY_TILES = 128;  // work lists at least this long take four row groups
 
 template <int BITS, bool SPLIT>
 hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowscale, float* o_tk, LoraRefG lg,
@@ -674,8 +725,9 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   const int nt = max_tiles(a.T * a.K, a.E);
   const moe_qmat gu[2] = {a.ex.gate, a.ex.up};
   hipError_t err;
-  if (auto k64 = grouped_kernel64<BITS, 2>(a.group, a.d, gu))
-    err = launch(k64, dim3(nt, (a.I + rows_per_block - 1) / rows_per_block), dim3(WAVE * GW), 0, s, a.K, a.E, a.d,
+  if (auto k64 = grouped_kernel64<BITS, 2>(a.group, a.d, gu, nt >= MANY_TILES))
+    err = launch(k64, dim3(nt, (a.I + rows_per_block * rg64<2>(a.d, nt >= MANY_TILES) - 1) / (rows_per_block * rg64<2>(a.d, nt >= MANY_TILES))),
+                 dim3(WAVE * GW), 0, s, a.K, a.E, a.d,
                  a.I, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
                  a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu);
   else
@@ -690,8 +742,9 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
                         a.lora3[2].A, a.u_down);
     if (err != hipSuccess) return err;
   }
-  if (auto k64 = grouped_kernel64<BITS, 1>(a.group, a.I, &a.ex.down))
-    return launch(k64, dim3(nt, (a.d + rows_per_block - 1) / rows_per_block), dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
+  if (auto k64 = grouped_kernel64<BITS, 1>(a.group, a.I, &a.ex.down, nt >= MANY_TILES))
+    return launch(k64, dim3(nt, (a.d + rows_per_block * rg64<1>(a.I, nt >= MANY_TILES) - 1) / (rows_per_block * rg64<1>(a.I, nt >= MANY_TILES))),
+                  dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
                   a.d, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
                   (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
                   LoraRefG{});
