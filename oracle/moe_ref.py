@@ -76,10 +76,14 @@ def dequant(qwords, scales, biases, bits: int, group: int) -> np.ndarray:
 # ----------------------------------------------------------------------------------------
 # elementwise pieces
 # ----------------------------------------------------------------------------------------
-def rmsnorm(h, eps: float = RMS_EPS) -> np.ndarray:
-    """Weightless RMS normalisation h / sqrt(mean(h^2) + eps) (glue between chained layers)."""
+def rmsnorm(h, gain=None, eps: float = RMS_EPS) -> np.ndarray:
+    """RMS normalisation g * h / sqrt(mean(h^2) + eps) over the last axis  [METAL, "Arquitectura del
+    Sistema": RMS normalisation is one of the GPU kernels; EDGE0, "Arquitectura del cabezal
+    Prerouter": the head reads the normalised hidden state].  gain None: the weightless form
+    (g = 1), the glue between chained layers."""
     h = f64(h)
-    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    x = h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    return x if gain is None else x * f64(gain)
 
 
 def silu(v) -> np.ndarray:
@@ -296,7 +300,7 @@ class LayerTrace:
 
 def chain_token(h0, state: ChainState, *, E: int, K: int, bits: int, group: int,
                 router_get: Callable, head_get: Callable, expert_get: Callable,
-                renorm: bool = True):
+                renorm: bool = True, gain_get: Optional[Callable] = None):
     """One decode token through the L layers of a prerouted stack.
 
     Layer l: x = rmsnorm(h).  Routing: layer 0 (and any layer with no prediction yet, i.e.
@@ -308,13 +312,14 @@ def chain_token(h0, state: ChainState, *, E: int, K: int, bits: int, group: int,
     y = h + sum_k w_k FFN_k(x), rounded to float16, is the next layer's h.
 
     router_get(l) -> W_r [E][d]; head_get(l) -> split head dict; expert_get(l, e) -> packed
-    (gate, up, down).  Returns (h_L, new_state, traces)."""
+    (gate, up, down); gain_get(l) -> the layer's RMS-norm gain [d] or None (weightless).
+    Returns (h_L, new_state, traces)."""
     L = state.L
     new = ChainState(L)
     h = f64(h0)
     traces = []
     for l in range(L):
-        x = rmsnorm(h)
+        x = rmsnorm(h, None if gain_get is None else gain_get(l))
         rl = None
         if l == 0 or state.pred[l] is None:
             rl = router_logits(router_get(l), x)

@@ -100,6 +100,24 @@ def test_rmsnorm_closed_form():
     assert O.rmsnorm(h).tolist() == pytest.approx([3 / math.sqrt(12.5 + 1e-6), -4 / math.sqrt(12.5 + 1e-6)])
 
 
+def test_rmsnorm_gain():
+    """The gain multiplies each normalised element; the sum of squares is of h alone."""
+    h = np.array([3.0, -4.0])
+    r = math.sqrt(12.5 + 1e-6)
+    assert O.rmsnorm(h, np.array([2.0, 0.5])).tolist() == pytest.approx([6 / r, -2 / r], rel=1e-15)
+    rng = np.random.default_rng(3)
+    hh = rng.standard_normal((5, 64))
+    assert np.array_equal(O.rmsnorm(hh, np.ones(64)), O.rmsnorm(hh))          # unit gain = weightless
+    g = rng.uniform(0.5, 1.5, 64)
+    np.testing.assert_allclose(O.rmsnorm(hh, g), O.rmsnorm(hh) * g, rtol=1e-15)  # per column, every row
+    np.testing.assert_allclose(O.rmsnorm(7.0 * hh, g), O.rmsnorm(hh, g), rtol=1e-6)  # scale-free (up to eps)
+    # the mean square is of h, not of g * h: a gain that zeroes a column leaves the others unchanged
+    g0 = np.ones(64)
+    g0[5] = 0.0
+    x0 = O.rmsnorm(hh, g0)
+    assert np.all(x0[:, 5] == 0) and np.array_equal(np.delete(x0, 5, 1), np.delete(O.rmsnorm(hh), 5, 1))
+
+
 # ------------------------------------------------------------------------------- top-K
 def test_topk_crafted_ties():
     assert O.topk_indices(np.zeros(16), 4) == [0, 1, 2, 3]
