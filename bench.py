@@ -34,7 +34,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def build_stack(cfg, syn, dev, M):
+def build_stack(cfg, syn, dev, M, norm_gain=False):
     from int4_expert_ffn_amd.chain import DecodeStack, LayerWeights
     import moe_synth as S
     layers = []
@@ -47,7 +47,7 @@ def build_stack(cfg, syn, dev, M):
             hw = syn.head(l, dev)
             hw["lin_x"] = routers[l + 1]          # the head's linear path is the next router
             head = M.PrerouterWeights(hw)
-        layers.append(LayerWeights(ex, routers[l], head))
+        layers.append(LayerWeights(ex, routers[l], head, syn.norm_gain(l, dev) if norm_gain else None))
     return layers
 
 
@@ -260,7 +260,7 @@ def bench_stack(args, cfg, torch, M, S, dev):
     from int4_expert_ffn_amd.chain import DecodeStack
     syn = S.Synth(cfg)
     t0 = time.time()
-    layers = build_stack(cfg, syn, dev, M)
+    layers = build_stack(cfg, syn, dev, M, norm_gain=args.norm_gain)
     torch.cuda.synchronize()
     log(f"stack resident: {cfg.L} layers, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.1f} s")
     tm = Timer(torch, dev, syn.hidden(7, 3 * 64, dev))
@@ -329,11 +329,15 @@ def bench_stack(args, cfg, torch, M, S, dev):
 
     tok_s = args.steps / wall
     rec = base_record(args, cfg, tok_s, wall, args.steps)
+    if args.norm_gain:
+        rec["config"]["workload"] += ", layer inputs RMS-normalised with a per-layer float16 gain"
+        total_bytes += cfg.L * cfg.d * 2          # the gains
     rec["hbm"] = {"algorithmic_bytes_per_token": total_bytes,
                   "achieved_GBps": round(total_bytes * tok_s / 1e9, 1),
                   "frac_of_peak": round(total_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4)}
     rec["roofline"] = roofline(f"k_decode_step (moe_decode_step: all {cfg.L} layers of one token in one launch)",
-                               total_bytes, step_us, stored_traffic() if cfg.name == "decode35b" else None)
+                               total_bytes, step_us,
+                               stored_traffic() if cfg.name == "decode35b" and not args.norm_gain else None)
     rec["expert_only"] = expert_only
     rec["per_layer_calls"] = {"tokens_per_s": per_layer_tok_s, "launches_per_token": launches,
                               "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"}
@@ -499,6 +503,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
+    ap.add_argument("--norm-gain", action="store_true",
+                    help="stack workloads: every layer input normalised with a per-layer gain (x = g * h / rms(h))")
     ap.add_argument("--eager", action="store_true",
                     help="launch each timed token directly instead of replaying a HIP graph (for counter profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -158,6 +158,16 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx,
                               int32_t* counts, int32_t* offsets, int32_t* perm);
 
+/* RMS normalisation of a layer input with an optional gain ("Inferencia de LLM MoE en MacBook Pro
+   ...", section "Arquitectura del Sistema", lists RMS normalisation among the GPU kernels; the
+   prerouter head reads the normalised state, "La otra mitad del muro ...", section "Arquitectura
+   del cabezal Prerouter"):  x[t][i] = float16(g[i] * h[t][i] / sqrt(mean_i(h[t][i]^2) + 1e-6)),
+   the sum of squares and the product in float32, rounded to nearest even.  h, x: [T][d] float16
+   (device, 16-byte aligned; x may be h); gain: [d] float16 (16-byte aligned) or NULL for g = 1.
+   The result feeds the routing and expert calls without MOE_INPUT_RMSNORM (the residual is h).
+   Limits: T >= 1, d a multiple of 8, d <= MOE_MAX_D. */
+moe_status moe_rmsnorm(void* stream, int32_t T, int32_t d, const uint16_t* h, const uint16_t* gain, uint16_t* x);
+
 /* S6: y[T][d] float16 = r + sum_k w[t][k] o[t][k] (+ shared[t], weight 1), accumulated in
    float32 in ascending k, rounded to nearest even. */
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,
@@ -194,6 +204,9 @@ typedef struct {
   moe_experts experts;   /* this layer's routed experts (E, d_model, d_ff, bits, group as in the stack) */
   const uint16_t* router; /* [E][d]: needed by self-routed layers (layer 0, token 0, no predecessor head) */
   moe_prerouter_w head;  /* head predicting layer l+1 (d_hidden == stack d_hidden); fc1_x == NULL: none */
+  const uint16_t* norm_gain; /* [d] float16 gain of this layer's input normalisation (x = g * h /
+                                rms(h)), applied inside the kernel; read only when the stack's
+                                norm_gains is 1 (then 16-byte aligned in every layer) */
 } moe_decode_layer;
 
 typedef struct {
@@ -201,6 +214,7 @@ typedef struct {
   const moe_decode_layer* layers; /* DEVICE array of L descriptors */
   int32_t* route_idx;             /* DEVICE [3][L][K] */
   float* route_w;                 /* DEVICE [3][L][K] */
+  int32_t norm_gains;             /* 1: every layer descriptor's norm_gain is set; 0: none is */
 } moe_decode_stack;
 
 size_t moe_decode_workspace_size(const moe_decode_stack* st);

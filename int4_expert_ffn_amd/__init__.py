@@ -7,5 +7,6 @@ from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, MOE_INPUT_RMSNORM, MOE_MAX_D, MOE_MAX_E, MOE_MAX_K, MOE_TOPK_RENORM, Experts, Lora3,
     MoEError, PrerouterWeights, moe_combine, moe_expert_ffn_q4, moe_expert_ffn_workspace_size, moe_prerouter,
     moe_prerouter_workspace_size, moe_route_topk, moe_sort_by_expert, moe_status_string, moe_version,
-    moe_decode_step, moe_decode_workspace_size, moe_decode_layer, moe_decode_stack,
+    moe_decode_step, moe_decode_workspace_size, moe_decode_layer, moe_decode_stack, moe_rmsnorm,
+    MOE_DECODE_GIVEN_ROUTING,
 )

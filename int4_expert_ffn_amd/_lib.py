@@ -23,7 +23,7 @@ MOE_MAX_E, MOE_MAX_K, MOE_MAX_D = 1024, 16, 8192
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_sort_by_expert",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
 )
 
@@ -56,14 +56,15 @@ class moe_prerouter_w(ctypes.Structure):
 
 
 class moe_decode_layer(ctypes.Structure):
-    _fields_ = [("experts", moe_experts), ("router", ctypes.c_void_p), ("head", moe_prerouter_w)]
+    _fields_ = [("experts", moe_experts), ("router", ctypes.c_void_p), ("head", moe_prerouter_w),
+                ("norm_gain", ctypes.c_void_p)]
 
 
 class moe_decode_stack(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("d_hidden", ctypes.c_int32), ("layers", ctypes.c_void_p), ("route_idx", ctypes.c_void_p),
-                ("route_w", ctypes.c_void_p)]
+                ("route_w", ctypes.c_void_p), ("norm_gains", ctypes.c_int32)]
 
 
 def _load():
@@ -83,6 +84,7 @@ def _load():
         "moe_expert_ffn_q4": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora),
                                    vp, vp, vp, vp, vp, sz]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_decode_workspace_size": (sz, [ctypes.POINTER(moe_decode_stack)]),
@@ -225,6 +227,12 @@ def moe_combine(T, K, d, o, w, r, shared, y, stream=None):
     st = _lib.moe_combine(_stream(stream, o, y), T, K, d, _ptr(o, _f32(), "o"), _ptr(w, _f32(), "w"),
                           _ptr(r, _f16(), "r"), _ptr(shared, _f32(), "shared"), _ptr(y, _f16(), "y"))
     _check(st, "moe_combine")
+
+
+def moe_rmsnorm(T, d, h, gain, x, stream=None):
+    st = _lib.moe_rmsnorm(_stream(stream, h, x), T, d, _ptr(h, _f16(), "h"), _ptr(gain, _f16(), "gain"),
+                          _ptr(x, _f16(), "x"))
+    _check(st, "moe_rmsnorm")
 
 
 def moe_sort_by_expert(T, K, E, idx, counts, offsets, perm, stream=None):

@@ -9,8 +9,10 @@ Per token t and layer l (all calls asynchronous on one stream, routing never lea
     tokens t and t-1 and predicts layer l+1's routing for token t+1 (section "Arquitectura del
     cabezal Prerouter");
   * the expert FFN with the fused weighted combine + residual produces the next layer's input.
-Layer inputs are consumed through the weightless RMS norm (MOE_INPUT_RMSNORM); the residual is
-the un-normalised float16 hidden state.
+Layer inputs are consumed through an RMS norm: the weightless one fused into every call
+(MOE_INPUT_RMSNORM), or, for a stack whose layers carry norm gains, moe_rmsnorm before the
+layer's calls (the persistent kernel applies the gain inside); the residual is the un-normalised
+float16 hidden state.
 
 Routing buffers rotate over three token slots, so the head writing token t+1's routing never
 overwrites what token t still reads (slot t%3) or the previous-token vector (slot (t-1)%3).
@@ -34,11 +36,16 @@ class LayerWeights:
     experts: L.Experts
     router: torch.Tensor                      # [E][d] float16
     head: Optional[L.PrerouterWeights] = None  # predicts the next layer; None on the last layer
+    norm_gain: Optional[torch.Tensor] = None   # [d] float16 gain of the input norm (all layers or none)
 
 
 class DecodeStack:
     def __init__(self, layers: List[LayerWeights], K: int, device, renorm: bool = True):
         ex0 = layers[0].experts
+        gained = [lw.norm_gain is not None for lw in layers]
+        if any(gained) and not all(gained):
+            raise ValueError("norm gains must be given for every layer or for none")
+        self.gained = all(gained)
         self.layers = layers
         self.L = len(layers)
         self.E, self.d, self.K = ex0.E, ex0.d, K
@@ -51,6 +58,7 @@ class DecodeStack:
         self.logits = torch.zeros((self.L, E), dtype=torch.float32, device=dev)
         self.head_logits = torch.zeros((self.L, E), dtype=torch.float32, device=dev)
         self.h = torch.zeros((self.L + 1, d), dtype=torch.float16, device=dev)   # per-layer inputs/outputs
+        self.xn = torch.zeros(d, dtype=torch.float16, device=dev)                # gained normalised input
         ffn_ws = max(L.moe_expert_ffn_workspace_size(1, K, lw.experts) for lw in layers)
         H = max([lw.head.H for lw in layers if lw.head is not None] or [8])
         head_ws = L.moe_prerouter_workspace_size(1, E, H)
@@ -72,11 +80,13 @@ class DecodeStack:
                 if lw.head is not None and l + 1 < L_:
                     arr[l].head = lw.head.desc
                     H = lw.head.H
+                if lw.norm_gain is not None:
+                    arr[l].norm_gain = lw.norm_gain.data_ptr()
             raw = bytes(arr)
             desc = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
             ex0 = self.layers[0].experts
             st = L.moe_decode_stack(L_, self.E, self.K, self.d, ex0.I, ex0.bits, ex0.group, H, desc.data_ptr(),
-                                    self.route_idx.data_ptr(), self.route_w.data_ptr())
+                                    self.route_idx.data_ptr(), self.route_w.data_ptr(), 1 if self.gained else 0)
             ws = torch.zeros(L.moe_decode_workspace_size(st), dtype=torch.uint8, device=self.device)
             self._step = (desc, st, ws)
         return self._step
@@ -115,11 +125,16 @@ class DecodeStack:
         if h_in is not None:
             self.h[0].copy_(h_in)
         s, sp, sn = t % 3, (t - 1) % 3, (t + 1) % 3
-        RMS = L.MOE_INPUT_RMSNORM
         for l, lw in enumerate(self.layers):
-            x = self.h[l]
+            h = self.h[l]
+            if lw.norm_gain is not None:      # x = g * h / rms(h), then the calls take x as it is
+                L.moe_rmsnorm(1, self.d, h, lw.norm_gain, self.xn)
+                x, RMS = self.xn, 0
+            else:                             # the calls normalise h themselves
+                x, RMS = h, L.MOE_INPUT_RMSNORM
             idx, w = self.route_idx[s, l], self.route_w[s, l]
-            if l == 0 or t == 0:
+            # a layer routes itself unless the head of the layer before predicted it one token ago
+            if l == 0 or t == 0 or self.layers[l - 1].head is None:
                 L.moe_route_topk(1, self.d, self.E, self.K, self.topk_flags | RMS, x, lw.router,
                                  self.logits[l], idx, w)
             if lw.head is not None and l + 1 < self.L:
@@ -127,6 +142,6 @@ class DecodeStack:
                                 lw.head, self.head_logits[l], self.head_ws)
                 L.moe_route_topk(1, self.d, self.E, self.K, self.topk_flags, None, None, self.head_logits[l],
                                  self.route_idx[sn, l + 1], self.route_w[sn, l + 1])
-            L.moe_expert_ffn_q4(1, self.K, RMS, x, idx, lw.experts, None, None, w, x, self.h[l + 1],
+            L.moe_expert_ffn_q4(1, self.K, RMS, x, idx, lw.experts, None, None, w, h, self.h[l + 1],
                                 self.ffn_ws)
         return self.h[self.L]

@@ -60,6 +60,7 @@ struct StepParams {
   int32_t* ridx;
   float* rw;
   int slot, bootstrap, given;  // given: every layer's routing supplied by the caller
+  int gained;                  // every layer's input norm has a gain (else none has)
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
   uint32_t* epoch;
@@ -448,6 +449,10 @@ struct StepShared {
   int route_e[LDS_LK];  // this token's routing of every layer: [l * K + k]
   float route_w[LDS_LK];
   int prev_e[LDS_LK];   // the previous token's routing (K-hot "previous" input of the heads)
+  // Last, so that the arrays above keep LDS offsets below 64 KiB (the immediate offset of a ds
+  // instruction is 16 bits; past it every access needs an address register):
+  uint16_t gain[2][LDS_D];  // input-norm gains of layers l and l+1 (by layer parity), staged by the compute waves
+  uint16_t xg[LDS_D];       // gain * h_l, formed by the compute waves once h_l is in (gained layers only)
 };
 
 struct StepCtx {
@@ -484,7 +489,8 @@ __device__ __forceinline__ void put_act(StepShared& sm, int n, float f) {
 }
 
 // Wave 0 of every workgroup: waits for the vectors each phase needs and unpacks them into LDS.
-template <int BITS>
+// GW0: 32-bit words of a d-row per lane (d = NSH 64 lanes x 8 halves).
+template <int BITS, int GW0>
 __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   const int lane = c.lane, dh = p.d / 2;
   bool failed = false;
@@ -502,6 +508,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
               [&](int i, uint32_t v) { hw[i] = v; });
     }
     lds_barrier();  // B1: h_l ready
+    if (p.gained) lds_barrier();  // B1g: gain * h_l formed
     if (self_routed(p, l)) {
       ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
       int e;
@@ -565,6 +572,24 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
   ABuf<BITS, PG, NSH, NSF, GU, NH> A;
   BBuf<BITS, NSF, PD> B;
   float lin_keep = 0.f, lin_keep_next = 0.f;  // this wave's linear-row output of heads l-1 and l
+  // Layer l's input-norm gain into LDS buffer l & 1, split over the compute waves (a few words per
+  // lane, all loads first): layer 0's before the first barrier, layer l+1's while waiting for the
+  // act exchange of layer l (buffer (l+1) & 1 was last read at layer l-1).
+  const auto stage_gain = [&](int l) {
+    if (!p.gained) return;
+    const uint32_t* gs = reinterpret_cast<const uint32_t*>(layer_at(p, l)->norm_gain);
+    constexpr int NWL = (NSH * 4 + MW - 1) / MW;  // words per lane: d/2 words over MW waves
+    uint32_t gv[NWL];
+#pragma unroll
+    for (int j = 0; j < NWL; ++j) gv[j] = gs[min(cw * WAVE + lane + j * MW * WAVE, dh - 1)];
+    uint32_t* gw = reinterpret_cast<uint32_t*>(sm.gain[l & 1]);
+#pragma unroll
+    for (int j = 0; j < NWL; ++j) {
+      const int m = cw * WAVE + lane + j * MW * WAVE;
+      if (m < dh) gw[m] = gv[j];
+    }
+  };
+  stage_gain(0);
   for (int l = 0; l < p.L; ++l) {
     const bool self = self_routed(p, l);
     const bool head = has_head(p, l);
@@ -574,6 +599,19 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     lds_barrier();  // B1
     float scale;  // 1 / rms(h_l), from this wave's own reads of h_l (a fixed summation order)
     const uint16_t* hl = sm.h[hb];
+    // a layer with a norm gain: the gate/up dot products take g * h as float16 pairs, formed here
+    // by all compute waves together (the router and head rows form the products in float32
+    // themselves); the sum of squares stays that of h
+    const bool gn = p.gained != 0;
+    if (gn) {
+      const uint32_t* hw = reinterpret_cast<const uint32_t*>(hl);
+      const uint32_t* gw = reinterpret_cast<const uint32_t*>(sm.gain[l & 1]);
+      uint32_t* xw = reinterpret_cast<uint32_t*>(sm.xg);
+      for (int m = cw * WAVE + lane; m < dh; m += MW * WAVE)
+        xw[m] = __builtin_bit_cast(uint32_t, as_h2(hw[m]) * as_h2(gw[m]));
+      lds_barrier();  // B1g
+    }
+    const uint16_t* xl = gn ? sm.xg : hl;
     if (self) {
       // R_l: at most one router row per wave -> tagged logit
       const int r = e_row(p, wg, cw);
@@ -585,10 +623,14 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           const int g = lane + sg * WAVE;
           const uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
           const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)g * 8);
-          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), red[0], false);
-          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), red[0], false);
-          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), red[0], false);
-          red[0] = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), red[0], false);
+          if (gn) {  // the routing decides indices: the gained product in float32, not rounded
+            red[0] = dot8_gained(wv, xv, *reinterpret_cast<const uint4*>(sm.gain[l & 1] + (size_t)g * 8), red[0]);
+          } else {
+            red[0] = __builtin_amdgcn_fdot2(as_h2(wv.x), as_h2(xv.x), red[0], false);
+            red[0] = __builtin_amdgcn_fdot2(as_h2(wv.y), as_h2(xv.y), red[0], false);
+            red[0] = __builtin_amdgcn_fdot2(as_h2(wv.z), as_h2(xv.z), red[0], false);
+            red[0] = __builtin_amdgcn_fdot2(as_h2(wv.w), as_h2(xv.w), red[0], false);
+          }
           red[1] = __builtin_amdgcn_fdot2(as_h2(xv.x), as_h2(xv.x), red[1], false);
           red[1] = __builtin_amdgcn_fdot2(as_h2(xv.y), as_h2(xv.y), red[1], false);
           red[1] = __builtin_amdgcn_fdot2(as_h2(xv.z), as_h2(xv.z), red[1], false);
@@ -617,7 +659,12 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         uint32_t xp[PG][GS::PAIRS];
         float sx[PG][2], sq = 0.f;
 #pragma unroll
-        for (int q = 0; q < PG; ++q) load_xpairs<BITS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
+        for (int q = 0; q < PG; ++q) load_xpairs<BITS>(xl + (size_t)(lane + q * WAVE) * GS::COLS, xp[q], sx[q], sq);
+        if (gn) {  // the pairs above are of g * h: take the sum of squares from h itself
+          sq = 0.f;
+#pragma unroll
+          for (int q = 0; q < PG; ++q) sq = sum_sq<GS::COLS>(hl + (size_t)(lane + q * WAVE) * GS::COLS, sq);
+        }
 #pragma unroll
         for (int u = 0; u < GU; ++u) {
           float pg = 0.f, pu = 0.f;
@@ -667,10 +714,15 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
 #pragma unroll
             for (int sg = 0; sg < NSH; ++sg) {
               const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)(lane + sg * WAVE) * 8);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
-              acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
+              if (gn) {  // the head's logits decide the next token's experts: float32 gained products
+                acc = dot8_gained(A.hr[r][sg], xv,
+                                  *reinterpret_cast<const uint4*>(sm.gain[l & 1] + (size_t)(lane + sg * WAVE) * 8), acc);
+              } else {
+                acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].x), as_h2(xv.x), acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].y), as_h2(xv.y), acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].z), as_h2(xv.z), acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(A.hr[r][sg].w), as_h2(xv.w), acc, false);
+              }
             }
             red[2 * r] = acc;
             red[2 * r + 1] = A.khm == 1 ? h2f(A.kh[r]) : (A.khm == 2 ? quiet_nan() : 0.f);
@@ -712,6 +764,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       }
       lin_keep = lin_keep_next;
     }
+    if (l + 1 < p.L) stage_gain(l + 1);  // while the act exchange runs; its loads go before the prefetch's
     if (prefetch)  // gate/up weights of A_{l+1}, one phase early
       issue_A_gu<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, A);
     lds_barrier();  // B3
@@ -805,7 +858,7 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
     }
   }
   if (wave == 0) {
-    sync_role<BITS>(p, c, sm);
+    sync_role<BITS, NSH * 4>(p, c, sm);
   } else {
     // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
     __builtin_amdgcn_s_setprio(2);
@@ -965,6 +1018,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.rw = st.route_w;
   p.slot = token % 3;
   p.given = (flags & MOE_DECODE_GIVEN_ROUTING) != 0;
+  p.gained = st.norm_gains != 0;
   p.bootstrap = token == 0 && !p.given;
   p.topk_flags = flags & MOE_TOPK_RENORM;
   p.ll_logits = (uint64_t*)(b + w.logits);

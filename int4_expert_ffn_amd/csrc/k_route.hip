@@ -325,6 +325,40 @@ constexpr int TPW = 16;  // tokens per wave in the matvecs
 
 }  // namespace
 
+// x[t] = float16(g * h[t] / sqrt(mean(h[t]^2) + eps)); one wave per token, the sum of squares in a
+// fixed order (each lane's 8-column slices, then a DPP reduction), so equal rows give equal x.
+__global__ void __launch_bounds__(256) k_rmsnorm(int T, int d, const uint16_t* __restrict__ h,
+                                                 const uint16_t* __restrict__ gain, uint16_t* __restrict__ x) {
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE), lane = threadIdx.x % WAVE;
+  if (t >= T) return;  // uniform over the wave
+  const uint16_t* hr = h + (size_t)t * d;
+  float sq = 0.f;
+  for (int c = lane * 8; c < d; c += WAVE * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hr + c);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq = __builtin_amdgcn_fdot2(as_h2(a[i]), as_h2(a[i]), sq, false);
+  }
+  const float s = 1.f / sqrtf(group_sum(sq, WAVE) / (float)d + RMS_EPS);
+  for (int c = lane * 8; c < d; c += WAVE * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hr + c);
+    const uint4 g = gain ? *reinterpret_cast<const uint4*>(gain + c) : make_uint4(0x3C003C00u, 0x3C003C00u,
+                                                                                   0x3C003C00u, 0x3C003C00u);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w}, b[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2_t hv = as_h2(a[i]), gv = as_h2(b[i]);
+      o[i] = f2h((float)hv[0] * (float)gv[0] * s) | ((uint32_t)f2h((float)hv[1] * (float)gv[1] * s) << 16);
+    }
+    *reinterpret_cast<uint4*>(x + (size_t)t * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const uint16_t* gain, uint16_t* x) {
+  return launch(k_rmsnorm, dim3((T + 3) / 4), dim3(256), 0, s, T, d, h, gain, x);
+}
+
 hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags, const uint16_t* x,
                               const uint16_t* w, float* logits) {
   if (T >= 32 && T % 16 == 0 && E % 16 == 0 && d % 32 == 0 && d <= MOE_MAX_D && (((uintptr_t)x | (uintptr_t)w) & 15) == 0)

@@ -199,6 +199,7 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
                            size_t workspace_bytes) {
   if (!st || !h_in || !h_out || !workspace || token < 0) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_TOPK_RENORM | MOE_DECODE_GIVEN_ROUTING)) return MOE_ERR_INVALID_ARG;
+  if (st->norm_gains != 0 && st->norm_gains != 1) return MOE_ERR_INVALID_ARG;
   if (st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return MOE_ERR_INVALID_ARG;
   if (!st->layers || !st->route_idx || !st->route_w) return MOE_ERR_INVALID_ARG;
   if (st->bits != 4 && st->bits != 2) return MOE_ERR_UNSUPPORTED;
@@ -211,6 +212,12 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
   if (workspace_bytes < decode_step_workspace(*st)) return MOE_ERR_INVALID_ARG;
   if (!decode_step_supported(*st)) return MOE_ERR_UNSUPPORTED;
   return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace));
+}
+
+moe_status moe_rmsnorm(void* stream, int32_t T, int32_t d, const uint16_t* h, const uint16_t* gain, uint16_t* x) {
+  if (T < 1 || d < 8 || d % 8 || d > MOE_MAX_D || !h || !x) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(x) || (gain && !aligned16(gain))) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_rmsnorm((hipStream_t)stream, T, d, h, gain, x));
 }
 
 moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const float* o, const float* w,

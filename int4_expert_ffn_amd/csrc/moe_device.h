@@ -148,6 +148,33 @@ __device__ __forceinline__ void load_xpairs(const uint16_t* __restrict__ xs, uin
   sq += q;
 }
 
+// acc + sum_j w_j (g_j x_j) over eight float16 columns, in float32: the product g_j x_j of two
+// float16 values is exact in float32, so a gained input loses nothing before the weight.
+__device__ __forceinline__ float dot8_gained(uint4 w, uint4 x, uint4 g, float acc) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w}, xv[4] = {x.x, x.y, x.z, x.w}, gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t a = as_h2(wv[i]), b = as_h2(xv[i]), c = as_h2(gv[i]);
+    acc = fmaf((float)a[0], (float)b[0] * (float)c[0], acc);
+    acc = fmaf((float)a[1], (float)b[1] * (float)c[1], acc);
+  }
+  return acc;
+}
+
+// sq + sum of x^2 over N float16 values (16-byte aligned, N a multiple of 8), in a fixed order.
+template <int N>
+__device__ __forceinline__ float sum_sq(const uint16_t* __restrict__ xs, float sq) {
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(xs)[i];
+    sq = __builtin_amdgcn_fdot2(as_h2(v.x), as_h2(v.x), sq, false);
+    sq = __builtin_amdgcn_fdot2(as_h2(v.y), as_h2(v.y), sq, false);
+    sq = __builtin_amdgcn_fdot2(as_h2(v.z), as_h2(v.z), sq, false);
+    sq = __builtin_amdgcn_fdot2(as_h2(v.w), as_h2(v.w), sq, false);
+  }
+  return sq;
+}
+
 // sum_j c_j x_j over the two half segments (words 0-1 and words 2-3) of one 16-byte segment.
 template <int BITS>
 __device__ __forceinline__ void dot_segment(uint4 q, const uint32_t* xp, float& d0, float& d1) {

@@ -67,6 +67,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
                               const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws);
 
 // combine -------------------------------------------------------------------------------------
+hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const uint16_t* gain, uint16_t* x);
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,
                           const uint16_t* r, const float* shared, uint16_t* y);
 

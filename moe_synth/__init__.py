@@ -66,6 +66,7 @@ T_LOGITS = 3
 T_Q, T_SCALE, T_BIASNOISE = 10, 11, 12          # + 4 * matrix (gate 0, up 1, down 2)
 T_FC1X, T_FC1R, T_FC1B, T_FC2, T_FC2B, T_LINR, T_LINB = 20, 21, 22, 23, 24, 26, 27
 T_LORA_A, T_LORA_B = 30, 31                    # + 2 * matrix
+T_NORM = 40                                     # RMS-norm gain of a layer input
 MATS = ("gate", "up", "down")
 
 
@@ -251,6 +252,13 @@ class Synth:
             "lin_r": normal_f16(k(T_LINR), 2 * E * E, 1 / math.sqrt(fan1), device).view(2 * E, E),
             "lin_b": normal_f16(k(T_LINB), E, 0.02, device).view(E),
         }
+
+    # ---- RMS-norm gain of a layer input -------------------------------------------------
+    def norm_gain(self, layer: int, device="cpu") -> torch.Tensor:
+        """[d] float16 gain of layer `layer`'s input normalisation, U[0.5, 1.5) (a trained gain sits
+        around 1; the spread makes a dropped or misplaced gain visible)."""
+        c = self.cfg
+        return to_f16(uniform_f64([self.key(layer, 0, T_NORM)], c.d, 0.5, 1.5)).view(c.d).to(device)
 
     # ---- shared-path LoRA -----------------------------------------------------------
     def lora(self, layer: int, device="cpu") -> dict:

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -117,6 +117,15 @@ def test_prerouter_and_combine_reject():
     nolayers = lib_mod.moe_decode_stack(40, 256, 4, 2048, 512, 4, 64, 1024, None, FAKE, FAKE)
     assert ds(nolayers) == INVALID
     assert L.moe_decode_workspace_size(ctypes.byref(st)) > 40 * 1024 * 8
+    g2 = lib_mod.moe_decode_stack(40, 256, 4, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE, 2)
+    assert ds(g2) == INVALID                    # norm_gains is 0 or 1
+    n = lambda *a: L.moe_rmsnorm(None, *a)
+    assert n(0, 2048, FAKE, None, FAKE) == INVALID          # T < 1
+    assert n(1, 2044, FAKE, None, FAKE) == INVALID          # d % 8
+    assert n(1, 16384, FAKE, None, FAKE) == INVALID         # d > MOE_MAX_D
+    assert n(1, 2048, None, None, FAKE) == INVALID          # h NULL
+    assert n(1, 2048, FAKE + 8, None, FAKE) == INVALID      # h not 16-byte aligned
+    assert n(1, 2048, FAKE, FAKE + 2, FAKE) == INVALID      # gain not 16-byte aligned
     c = lambda *a: L.moe_combine(None, *a)
     assert c(0, 4, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
     assert c(1, 17, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID

@@ -93,11 +93,13 @@ def test_decode_step_matches_oracle_chain(M, name):
     assert n >= 2, "too few tokens compared"
 
 
-def test_decode_step_equals_per_layer_path(M):
+@pytest.mark.parametrize("name", ["decode35b", "widek8"])
+def test_decode_step_equals_per_layer_path(M, name):
     """Same weights, same tokens: the persistent kernel and the per-layer calls pick the same
-    experts and agree on every output within the tolerance, token after token."""
+    experts and agree on every output within the tolerance, token after token (without heads,
+    every layer of the per-layer path routes itself at every token)."""
     from int4_expert_ffn_amd.chain import DecodeStack
-    cfg, heads = CASES["decode35b"]
+    cfg, heads = CASES[name]
     syn, layers, _, _ = build(M, cfg, heads)
     a = DecodeStack(layers, cfg.K, DEV)
     b = DecodeStack(layers, cfg.K, DEV)
@@ -183,3 +185,95 @@ def test_decode_step_given_routing(M, name):
                 y_ref += float(w[l][k]) * O.expert_ffn_packed(x, *caches[l](idx[l][k]), bits=cfg.bits, group=cfg.group)
             assert_rows_close(H[l + 1][None], y_ref[None], what=f"{name} t{t} layer {l} (given routing)")
     log(f"{name}: given routing checked at all {cfg.L} layers of 3 tokens")
+
+
+# ------------------------------------------------------------------------- RMS norm with a gain
+@pytest.mark.parametrize("d", [2048, 4096, 264])
+@pytest.mark.parametrize("gained", [True, False])
+def test_rmsnorm_matches_oracle(M, d, gained):
+    """moe_rmsnorm against the oracle, rows within the tolerance; in place as well."""
+    cfg = replace(S.CONFIGS["decode35b"], d=d)
+    syn = S.Synth(cfg)
+    T = 7
+    h = syn.hidden(4242, T)
+    g = syn.norm_gain(3) if gained else None
+    x = torch.empty((T, d), dtype=torch.float16, device=DEV)
+    hd = h.to(DEV)
+    M.moe_rmsnorm(T, d, hd, None if g is None else g.to(DEV), x)
+    ref = O.rmsnorm(h.numpy(), None if g is None else g.numpy())
+    assert_rows_close(x.float().cpu().numpy(), ref, what=f"rmsnorm d {d}")
+    M.moe_rmsnorm(T, d, hd, None if g is None else g.to(DEV), hd)     # x may be h
+    torch.cuda.synchronize()
+    assert torch.equal(hd, x)
+
+
+def gained_stack(M, cfg, heads):
+    from int4_expert_ffn_amd.chain import LayerWeights
+    syn, layers, heads_cpu, routers_cpu = build(M, cfg, heads)
+    gains = [syn.norm_gain(l) for l in range(cfg.L)]
+    layers = [LayerWeights(lw.experts, lw.router, lw.head, gains[l].to(DEV)) for l, lw in enumerate(layers)]
+    return syn, layers, heads_cpu, routers_cpu, [g.numpy() for g in gains]
+
+
+@pytest.mark.parametrize("name", ["decode35b", "widek8", "large-int4"])
+def test_decode_step_norm_gain_layer_by_layer(M, name):
+    """Layers with an input-norm gain (x = g * h / rms(h)) through the persistent kernel: per
+    token and layer, the routing a self-routed layer chose equals the oracle's top-K of the gained
+    input, the layer output equals the oracle layer on the kernel's own input, and every head
+    predicts the oracle head's top-K (near ties excepted)."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    from test_fullsize_gpu import _check_topk
+    cfg, heads = CASES[name]
+    syn, layers, heads_cpu, routers_cpu, gains = gained_stack(M, cfg, heads)
+    stack = DecodeStack(layers, cfg.K, DEV)
+    caches = [ExpertCache(syn, l) for l in range(cfg.L)]
+    hl = torch.empty((cfg.L + 1, cfg.d), dtype=torch.float16, device=DEV)
+    prev_idx, routed, predicted = None, 0, 0
+    for t in range(3):
+        h0 = syn.hidden(9300 + t, 1)[0]
+        out = stack.step(t, h0.to(DEV), h_layers=hl)
+        torch.cuda.synchronize()
+        assert stack.step_error_word() == 0
+        H = hl.cpu().numpy()
+        assert np.array_equal(H[0], h0.numpy()) and np.array_equal(H[cfg.L], out.cpu().numpy())
+        idx = stack.route_idx[t % 3].cpu().numpy()
+        w = stack.route_w[t % 3].cpu().numpy()
+        nxt_idx = stack.route_idx[(t + 1) % 3].cpu().numpy()
+        nxt_w = stack.route_w[(t + 1) % 3].cpu().numpy()
+        for l in range(cfg.L):
+            x = O.rmsnorm(H[l], gains[l])
+            if t == 0 or l == 0 or not heads:
+                routed += _check_topk(O.router_logits(routers_cpu[l], x), idx[l], w[l], cfg.K, f"{name} t{t} l{l}")
+            y_ref = O.f64(H[l]).copy()
+            for k in range(cfg.K):
+                y_ref += float(w[l][k]) * O.expert_ffn_packed(x, *caches[l](idx[l][k]), bits=cfg.bits, group=cfg.group)
+            assert_rows_close(H[l + 1][None], y_ref[None], what=f"{name} t{t} layer {l} (gained)")
+            if heads and l + 1 < cfg.L:
+                lg = O.prerouter_logits(x, idx[l], None if t == 0 else prev_idx[l], heads_cpu[l], cfg.E)
+                predicted += _check_topk(lg, nxt_idx[l + 1], nxt_w[l + 1], cfg.K, f"{name} t{t} head {l}")
+        prev_idx = idx
+    log(f"{name} gained: {routed} router top-Ks, {predicted} head predictions compared")
+    assert routed >= 1
+
+
+@pytest.mark.parametrize("name", ["decode35b", "widek8"])
+def test_norm_gain_step_matches_per_layer_path(M, name):
+    """The per-layer calls (moe_rmsnorm, then the calls on x) and the persistent kernel (the gain
+    applied inside) pick the same experts and agree within the tolerance, token by token; for the
+    stack without heads this also exercises the per-layer path's own routing at every layer."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = CASES[name]
+    syn, layers, _, _, _ = gained_stack(M, cfg, heads)
+    a = DecodeStack(layers, cfg.K, DEV)
+    b = DecodeStack(layers, cfg.K, DEV)
+    for t in range(4):
+        h0 = syn.hidden(9400 + t, 1)[0].to(DEV)
+        ya = a.step(t, h0).clone()
+        yb = b.token(t, h0).clone()
+        torch.cuda.synchronize()
+        ra, rb = a.route_idx[t % 3].cpu().numpy(), b.route_idx[t % 3].cpu().numpy()
+        if not np.array_equal(ra, rb):
+            log(f"{name} token {t}: paths diverge at a routing tie ({ra.tolist()} vs {rb.tolist()})")
+            break
+        assert_rows_close(ya.float().cpu().numpy()[None], yb.float().cpu().numpy()[None], what=f"{name} token {t}")
+    assert a.step_error_word() == 0

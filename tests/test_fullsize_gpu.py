@@ -59,7 +59,8 @@ def _check_topk(logits, idx_gpu, w_gpu, K, what):
     return 1
 
 
-CASES = [(n, "step") for n in FULL] + [("decode35b-L40", "calls"), ("decode35b-L40", "given")]
+CASES = [(n, "step") for n in FULL] + [("decode35b-L40", "calls"), ("decode35b-L40", "given"),
+                                       ("decode35b-L40", "gained")]
 
 
 @pytest.mark.parametrize("name,path", CASES)
@@ -67,12 +68,19 @@ def test_full_depth_layer_by_layer(M, name, path):
     """path "step": one moe_decode_step launch per token (inputs of every layer via h_layers);
     path "calls": the per-layer C-ABI calls (every layer's input kept in the stack); path "given":
     moe_decode_step on caller-supplied routing for every layer (the expert FFN steps alone, as the
-    expert-only benchmark times them)."""
+    expert-only benchmark times them); path "gained": moe_decode_step on a stack whose layer inputs
+    are normalised with a per-layer gain."""
     from int4_expert_ffn_amd.chain import DecodeStack
     cfg, heads = FULL[name]
     L, K, E = cfg.L, cfg.K, cfg.E
     log(f"{name} ({path}): building {L} layers on the GPU")
     syn, layers, heads_cpu, routers_cpu = build(M, cfg, heads)
+    gains = [None] * L
+    if path == "gained":
+        from int4_expert_ffn_amd.chain import LayerWeights
+        gains = [syn.norm_gain(l) for l in range(L)]
+        layers = [LayerWeights(lw.experts, lw.router, lw.head, gains[l].to(DEV)) for l, lw in enumerate(layers)]
+        gains = [g.numpy() for g in gains]
     stack = DecodeStack(layers, K, DEV)
     hl = torch.empty((L + 1, cfg.d), dtype=torch.float16, device=DEV)
     caches = [ExpertCache(syn, l) for l in range(L)]
@@ -84,7 +92,7 @@ def test_full_depth_layer_by_layer(M, name, path):
             gi, gw = given_routing(syn, cfg, t)
             stack.set_routing(t, torch.from_numpy(gi).to(DEV), torch.from_numpy(gw).to(DEV))
             out = stack.step(t, h0.to(DEV), h_layers=hl, given_routing=True)
-        elif path == "step":
+        elif path in ("step", "gained"):
             out = stack.step(t, h0.to(DEV), h_layers=hl)
         else:
             out = stack.token(t, h0.to(DEV))
@@ -100,7 +108,7 @@ def test_full_depth_layer_by_layer(M, name, path):
         assert np.array_equal(H[0], h0.numpy()), "row 0 must be the token's input"
         assert np.array_equal(H[L], out.cpu().numpy()), "row L must be the output"
         for l in range(L):
-            x = O.rmsnorm(H[l])
+            x = O.rmsnorm(H[l], gains[l])
             self_routed = t == 0 or l == 0 or not heads
             if path == "given":
                 assert np.array_equal(idx[l], gi[l]) and np.array_equal(w[l], gw[l])
