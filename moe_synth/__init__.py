@@ -67,6 +67,7 @@ T_Q, T_SCALE, T_BIASNOISE = 10, 11, 12          # + 4 * matrix (gate 0, up 1, do
 T_FC1X, T_FC1R, T_FC1B, T_FC2, T_FC2B, T_LINR, T_LINB = 20, 21, 22, 23, 24, 26, 27
 T_LORA_A, T_LORA_B = 30, 31                    # + 2 * matrix
 T_NORM = 40                                     # RMS-norm gain of a layer input
+T_DOWN_NM = 50                                  # neuron-major down projection: + 0 codes, 1 scales, 2 bias noise
 MATS = ("gate", "up", "down")
 
 
@@ -155,7 +156,8 @@ class MoEConfig:
         return cols * self.bits // 32
 
     def mat_shape(self, mat: str):
-        return (self.I, self.d) if mat in ("gate", "up") else (self.d, self.I)
+        """[rows][cols] of a matrix; "down_nm" is the down projection stored neuron-major."""
+        return (self.I, self.d) if mat in ("gate", "up", "down_nm") else (self.d, self.I)
 
     def qmat_bytes(self, mat: str) -> int:
         rows, cols = self.mat_shape(mat)
@@ -202,16 +204,19 @@ class Synth:
         bias = -2^(bits-1) * scale + N(0, bias_noise^2), all float16.
         """
         c = self.cfg
-        m = MATS.index(mat)
+        if mat == "down_nm":
+            tq, ts, tb = T_DOWN_NM, T_DOWN_NM + 1, T_DOWN_NM + 2
+        else:
+            m = MATS.index(mat)
+            tq, ts, tb = T_Q + 4 * m, T_SCALE + 4 * m, T_BIASNOISE + 4 * m
         rows, cols = c.mat_shape(mat)
         nw = rows * c.words_per_row(cols)
         ng = rows * (cols // c.group)
         n = len(experts)
-        q = words_u32([self.key(layer, e, T_Q + 4 * m) for e in experts], nw, device)
-        s64 = uniform_f64([self.key(layer, e, T_SCALE + 4 * m) for e in experts], ng,
-                          c.scale_lo, c.scale_hi, device)
+        q = words_u32([self.key(layer, e, tq) for e in experts], nw, device)
+        s64 = uniform_f64([self.key(layer, e, ts) for e in experts], ng, c.scale_lo, c.scale_hi, device)
         s16 = to_f16(s64)
-        hn = hash_block([self.key(layer, e, T_BIASNOISE + 4 * m) for e in experts], 0, 3 * ng, device)
+        hn = hash_block([self.key(layer, e, tb) for e in experts], 0, 3 * ng, device)
         noise = _irwin_hall12(hn.view(n, ng, 3)) * c.bias_noise
         b16 = to_f16(s16.to(torch.float64) * -float(1 << (c.bits - 1)) + noise)
         return (q.view(n, rows, -1), s16.view(n, rows, -1), b16.view(n, rows, -1))
@@ -287,18 +292,21 @@ class Synth:
         return (_irwin_hall12(h)).to(torch.float32).view(T, c.E)
 
 
-def fill_experts(syn: Synth, layer: int, device, chunk: int = 32):
-    """All E routed experts of one layer on `device`: dict mat -> (q, s, b) stacked [E][...]."""
+def fill_experts(syn: Synth, layer: int, device, chunk: int = 32, relu: bool = False):
+    """All E routed experts of one layer on `device`: dict mat -> (q, s, b) stacked [E][...].
+    relu: the down projection is drawn neuron-major ([E][I][d], groups along d), the layout of
+    the ReLU activation-sparse expert; gate and up are the same draws either way."""
     c = syn.cfg
     out = {}
     for mat in MATS:
-        rows, cols = c.mat_shape(mat)
+        src = "down_nm" if (relu and mat == "down") else mat
+        rows, cols = c.mat_shape(src)
         q = torch.empty((c.E, rows, c.words_per_row(cols)), dtype=torch.int32, device=device)
         s = torch.empty((c.E, rows, cols // c.group), dtype=torch.float16, device=device)
         b = torch.empty_like(s)
         for e0 in range(0, c.E, chunk):
             ids = list(range(e0, min(c.E, e0 + chunk)))
-            qq, ss, bb = syn.expert_mat(layer, ids, mat, device)
+            qq, ss, bb = syn.expert_mat(layer, ids, src, device)
             q[e0:e0 + len(ids)] = qq
             s[e0:e0 + len(ids)] = ss
             b[e0:e0 + len(ids)] = bb

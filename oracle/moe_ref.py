@@ -213,6 +213,40 @@ def expert_ffn_packed(x, gate, up, down, bits: int, group: int, lora=None) -> np
 
 
 # ----------------------------------------------------------------------------------------
+# ReLU activation-sparse expert  [DEVICE, "Dos niveles de sparsity", level 2 (sparse FFN):
+# under a ReLU-type nonlinearity many intermediate neurons are exactly zero for a token, and a
+# zero neuron's weights need not be read or multiplied.  Reading taken: the gated unit keeps its
+# gate / up / down matrices and ReLU replaces SiLU on the gate branch; the down projection is
+# stored neuron-major ([I][d], row i = the weights neuron i feeds, groups along d) so that a
+# skipped neuron is a skipped contiguous row.  Skipping is exact, so the definition below is the
+# dense product.]
+# ----------------------------------------------------------------------------------------
+def relu(v) -> np.ndarray:
+    return np.maximum(f64(v), 0.0)
+
+
+def expert_ffn_relu(x, Wg, Wu, WdT):
+    """(o, a): a = relu(Wg x) * (Wu x) and o = sum_i a_i WdT[i] = WdT^T a, float64.  WdT is the
+    down projection neuron-major, [I][d]; x [d] or [T][d]."""
+    xv = f64(x)
+    a = relu(xv @ Wg.T) * (xv @ Wu.T)
+    return a @ WdT, a
+
+
+def expert_ffn_relu_packed(x, gate, up, down_nm, bits: int, group: int):
+    """Same as expert_ffn_relu from packed triples; down_nm is [I][d*bits/32] words with
+    [I][d/group] scales and biases (its groups run along d, the stored row)."""
+    return expert_ffn_relu(x, dequant(*gate, bits, group), dequant(*up, bits, group),
+                           dequant(*down_nm, bits, group))
+
+
+def active_neurons(a) -> np.ndarray:
+    """Number of intermediate neurons with a nonzero output (the rows the down projection
+    reads), over the last axis."""
+    return np.count_nonzero(f64(a) != 0.0, axis=-1)
+
+
+# ----------------------------------------------------------------------------------------
 # S6 combine  [METAL, "Arquitectura del Sistema": expert combination and residual in one step]
 # ----------------------------------------------------------------------------------------
 def combine(o, w, r, shared=None) -> np.ndarray:

@@ -320,3 +320,60 @@ def test_chain_single_layer_is_routed_layer():
     y = O.moe_layer(x, h, idx, w, get, cfg.bits, cfg.group)
     np.testing.assert_array_equal(hL, O.to_f16_f64(y[0]))
     assert st2.prev[0].tolist() == idx[0].tolist()
+
+
+# ------------------------------------------------------------------ ReLU activation-sparse expert
+def _hand_relu_mats():
+    fx = read_fixture("relu_sparse_hand.txt")
+    bits, group = int(fx["bits"][0][0]), int(fx["group"][0][0])
+
+    def mat(name):
+        q = np.array([[int(w, 16) for w in row] for row in fx[name + "_words"]], dtype=np.uint32)
+        sb = np.array([[float(v) for v in row] for row in fx[name + "_sb"]])
+        return q, sb[:, 0::2].astype(np.float16), sb[:, 1::2].astype(np.float16)
+
+    return fx, bits, group, mat("gate"), mat("up"), mat("down")
+
+
+def test_relu_sparse_expert_by_hand():
+    """Hand-worked example: neuron 0's gate is negative (its ReLU output is exactly zero, so its
+    down row never contributes), neuron 1 is on; the output pins the neuron-major orientation of
+    the down projection and its groups along d."""
+    fx, bits, group, gate, up, down = _hand_relu_mats()
+    x = np.ones(int(fx["d"][0][0]))
+    o, a = O.expert_ffn_relu_packed(x, gate, up, down, bits, group)
+    assert a.tolist() == [float(v) for v in fx["act"][0]]
+    assert int(O.active_neurons(a)) == int(fx["n_active"][0][0])
+    assert o.tolist() == [float(v) for v in fx["out"][0]]
+
+
+def test_relu_expert_matches_explicit_loops():
+    """Small random expert with every product as a Python loop and ReLU as a branch; the down
+    matrix is indexed [neuron][output] (catches a transposed down or ReLU on the up branch)."""
+    d, I = 8, 6
+    Wg, Wu, WdT = RNG.normal(size=(I, d)), RNG.normal(size=(I, d)), RNG.normal(size=(I, d))
+    x = RNG.normal(size=d)
+    a = []
+    for i in range(I):
+        g = sum(Wg[i, c] * x[c] for c in range(d))
+        u = sum(Wu[i, c] * x[c] for c in range(d))
+        a.append(g * u if g > 0 else 0.0)
+    ref = [sum(a[i] * WdT[i, j] for i in range(I)) for j in range(d)]
+    o, av = O.expert_ffn_relu(x, Wg, Wu, WdT)
+    np.testing.assert_allclose(o, ref, rtol=1e-12)
+    assert int(O.active_neurons(av)) == sum(1 for v in a if v != 0.0)
+    assert 0 < sum(1 for v in a if v != 0.0) < I      # the draw has neurons on and off
+
+
+def test_relu_expert_all_off_and_all_on():
+    """Every gate negative: the output is exactly zero and no neuron is active.  Every gate
+    positive: ReLU is the identity and the unit is the bilinear product WdT^T((Wg x)(Wu x))."""
+    d, I = 16, 8
+    x = np.abs(RNG.normal(size=d)) + 0.1
+    Wpos = np.abs(RNG.normal(size=(I, d)))
+    Wu, WdT = RNG.normal(size=(I, d)), RNG.normal(size=(I, d))
+    o, a = O.expert_ffn_relu(x, -Wpos, Wu, WdT)
+    assert (o == 0).all() and int(O.active_neurons(a)) == 0
+    o, a = O.expert_ffn_relu(x, Wpos, Wu, WdT)
+    np.testing.assert_allclose(o, np.einsum("i,id->d", (Wpos @ x) * (Wu @ x), WdT), rtol=1e-12)
+    assert int(O.active_neurons(a)) == I
