@@ -150,6 +150,31 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
                              float* out, const float* w_fuse, const uint16_t* r_fuse,
                              uint16_t* y_fuse, void* workspace, size_t workspace_bytes);
 
+/* Bytes of device workspace moe_expert_ffn_sparse needs for T tokens with K experts each. */
+size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex);
+
+/* ReLU activation-sparse variant of S3-S6 ("Arquitecturas nativas para device: MoE de grano fino
+   y pre-attention router", section "Dos niveles de sparsity", level 2: under a ReLU-type
+   activation many intermediate neurons are exactly zero for a token, and the weights of a zero
+   neuron are neither read nor multiplied).  For each token t and slot k, expert e = idx[t][k]:
+     a = relu(gate_e x_t) * (up_e x_t)          (ReLU on the gate branch of the gated unit)
+     o_tk = sum over the neurons i with a_i != 0 of a_i * down_e[i]
+   ex->down is stored NEURON-MAJOR: row i holds the d_model weights neuron i feeds, groups of
+   ex->group run along d_model (q [E][d_ff][d_model*bits/32] words, scales / biases
+   [E][d_ff][d_model/group] float16), so a zero neuron's row is skipped whole.  gate and up are as
+   in moe_expert_ffn_q4.  Float32 accumulation; the fused combine is moe_combine's arithmetic.
+   Outputs: out[T][K][d] float32 (may be NULL) and/or the fused y (w_fuse, r_fuse, y_fuse all set
+   or all NULL), as moe_expert_ffn_q4; n_active[T][K] int32 (may be NULL) = the number of neurons
+   with a != 0, i.e. the down rows read (-1 where idx lies outside [0, E)).  flags:
+   MOE_INPUT_RMSNORM only.  No LoRA.  workspace: moe_expert_ffn_sparse_workspace_size bytes,
+   256-byte aligned.  Limits: those of moe_expert_ffn_q4, and d_model a multiple of 64 (int4) or
+   128 (int2), d_ff at most 4096 (MOE_ERR_UNSUPPORTED otherwise).  Every T runs the per-token
+   kernels (the weights are read once per token). */
+moe_status moe_expert_ffn_sparse(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                 const int32_t* idx, const moe_experts* ex, float* out, const float* w_fuse,
+                                 const uint16_t* r_fuse, uint16_t* y_fuse, int32_t* n_active, void* workspace,
+                                 size_t workspace_bytes);
+
 /* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
    (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose
    index lies outside [0, E); perm[T*K] (int32, out) lists flat pair indices t*K + k grouped by

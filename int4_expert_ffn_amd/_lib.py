@@ -25,6 +25,7 @@ EXPORTS = (
     "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
+    "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse",
 )
 
 
@@ -83,6 +84,9 @@ def _load():
         "moe_expert_ffn_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
         "moe_expert_ffn_q4": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora),
                                    vp, vp, vp, vp, vp, sz]),
+        "moe_expert_ffn_sparse_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
+        "moe_expert_ffn_sparse": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), vp, vp, vp, vp, vp,
+                                       vp, sz]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -156,11 +160,17 @@ def _qw():
 class Experts:
     """A stack of E quantised experts (tensors kept alive here) and its C descriptor."""
 
-    def __init__(self, gate, up, down, bits: int, group: int):
+    def __init__(self, gate, up, down, bits: int, group: int, neuron_major_down: bool = False):
+        """neuron_major_down: down is [E][d_ff][d_model] (the layout of moe_expert_ffn_sparse), else
+        [E][d_model][d_ff]."""
         self.tensors = (gate, up, down)
         q = gate[0]
-        E, I, _ = q.shape
-        d = down[0].shape[1]
+        E, I, words = q.shape
+        d = words * 32 // bits
+        want = (E, I, d * bits // 32) if neuron_major_down else (E, d, I * bits // 32)
+        if tuple(down[0].shape) != want:
+            raise ValueError(f"down codes have shape {tuple(down[0].shape)}, expected {want}")
+        self.neuron_major_down = neuron_major_down
         mats = [moe_qmat(_ptr(m[0], _qw(), "q"), _ptr(m[1], _f16(), "scales"), _ptr(m[2], _f16(), "biases"))
                 for m in (gate, up, down)]
         self.desc = moe_experts(E, d, I, bits, group, *mats)
@@ -221,6 +231,22 @@ def moe_expert_ffn_q4(T, K, flags, x, idx, ex: Experts, lora3: Optional[Lora3], 
                                 _ptr(out, _f32(), "out"), _ptr(w_fuse, _f32(), "w_fuse"), _ptr(r_fuse, _f16(), "r_fuse"),
                                 _ptr(y_fuse, _f16(), "y_fuse"), _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_expert_ffn_q4")
+
+
+def moe_expert_ffn_sparse_workspace_size(T, K, ex: Experts) -> int:
+    return _lib.moe_expert_ffn_sparse_workspace_size(T, K, ctypes.byref(ex.desc))
+
+
+def moe_expert_ffn_sparse(T, K, flags, x, idx, ex: Experts, out, w_fuse, r_fuse, y_fuse, n_active, workspace,
+                          workspace_bytes=None, stream=None):
+    """ReLU activation-sparse expert FFN; ex.down is neuron-major ([E][d_ff][d_model] packed)."""
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_expert_ffn_sparse(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"),
+                                    _ptr(idx, _i32(), "idx"), ctypes.byref(ex.desc), _ptr(out, _f32(), "out"),
+                                    _ptr(w_fuse, _f32(), "w_fuse"), _ptr(r_fuse, _f16(), "r_fuse"),
+                                    _ptr(y_fuse, _f16(), "y_fuse"), _ptr(n_active, _i32(), "n_active"),
+                                    _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_expert_ffn_sparse")
 
 
 def moe_combine(T, K, d, o, w, r, shared, y, stream=None):

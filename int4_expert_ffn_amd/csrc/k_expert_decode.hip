@@ -113,10 +113,13 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
                                                uint32_t flags, const uint16_t* __restrict__ x,
                                                const int32_t* __restrict__ idx, moe_qmat gate,
                                                moe_qmat up, float* __restrict__ act, LoraRef lg,
-                                               LoraRef lu) {
+                                               LoraRef lu, int relu, int32_t* __restrict__ zero, int nzero) {
   using G = SegT<BITS>;
   const int lane = threadIdx.x;
   const int t = blockIdx.y;
+  // counters of the kernel that follows on the stream, cleared here so that it needs no launch of its own
+  if (zero && blockIdx.x == 0)
+    for (int i = lane; i < nzero; i += WAVE) zero[(size_t)t * nzero + i] = 0;
   const int RPI = WAVE / L;
   const int slot = lane / L, ls = lane % L;
   const int wpr = d * BITS / 32;
@@ -190,7 +193,8 @@ __global__ void __launch_bounds__(64) k_gateup(int T, int K, int E, int d, int I
     if (ls == 0 && valid[nb]) {
       if (lg.B) pg += lora_row(lg, t, ii[nb]);
       if (lu.B) pu += lora_row(lu, t, ii[nb]);
-      float a = pg / (1.f + expf(-pg)) * pu;
+      // SwiGLU: silu(gate) * up; the ReLU variant: relu(gate) * up, exactly zero for gate <= 0
+      float a = relu ? (pg > 0.f ? pg * pu : 0.f) : pg / (1.f + expf(-pg)) * pu;
       if (bad[nb]) a = quiet_nan();
       act[((size_t)t * K + kk[nb]) * I + ii[nb]] = a;
     }
@@ -340,7 +344,8 @@ hipError_t launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, con
     const int rpw = (WAVE / gu.L) * NB_GATEUP;
     dim3 grid((a.K * a.I + rpw - 1) / rpw, a.T);
     return launch(k_gateup<BITS, P, SPLIT, NB_GATEUP>, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g,
-                  gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, (float*)a.act, lg, lu);
+                  gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, (float*)a.act, lg, lu, a.relu ? 1 : 0, a.zero,
+                  a.nzero);
   }
   const int rpw = (WAVE / gd.L) * NB_DOWN;
   dim3 grid((a.d + rpw - 1) / rpw, a.T);
@@ -406,6 +411,14 @@ hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a) {
       err = first_error(err, launch_p<2, false>(s, a, gu, gd, lg, lu, ldn, which));
   }
   return err;
+}
+
+hipError_t launch_gateup_decode(hipStream_t s, const DecodeArgs& a) {
+  const RowGeo gu = row_geo(a.bits, a.d);
+  const bool split = a.bits == 2 && a.group < SegT<2>::COLS;
+  if (a.bits == 4) return launch_p<4, false>(s, a, gu, gu, LoraRef{}, LoraRef{}, LoraRef{}, 0);
+  if (split) return launch_p<2, true>(s, a, gu, gu, LoraRef{}, LoraRef{}, LoraRef{}, 0);
+  return launch_p<2, false>(s, a, gu, gu, LoraRef{}, LoraRef{}, LoraRef{}, 0);
 }
 
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,

@@ -37,6 +37,20 @@ FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex) {
   return w;
 }
 
+// workspace layout of moe_expert_ffn_sparse
+struct SparseWs {
+  size_t act, o, cnt, total;
+};
+SparseWs sparse_ws(int32_t T, int32_t K, const moe_experts* ex) {
+  SparseWs w{};
+  const int ns = sparse_slabs(ex->bits, ex->d_model);
+  w.act = 0;
+  w.o = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(float));
+  w.cnt = w.o + align_up((size_t)T * K * ex->d_model * sizeof(float));
+  w.total = w.cnt + align_up((size_t)T * (ns > 0 ? ns : 1) * sizeof(int32_t));
+  return w;
+}
+
 moe_status check_qmat(const moe_qmat& m) {
   if (!m.q || !m.scales || !m.biases) return MOE_ERR_INVALID_ARG;
   if (!aligned16(m.q)) return MOE_ERR_INVALID_ARG;
@@ -180,6 +194,57 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
     return from_hip(launch_expert_grouped(s, g));
   }
   return from_hip(launch_expert_decode(s, a));
+}
+
+size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex) {
+  if (!ex || T < 1 || K < 1 || ex->d_ff < 1 || ex->d_model < 1) return 0;
+  return sparse_ws(T, K, ex).total;
+}
+
+moe_status moe_expert_ffn_sparse(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                 const int32_t* idx, const moe_experts* ex, float* out, const float* w_fuse,
+                                 const uint16_t* r_fuse, uint16_t* y_fuse, int32_t* n_active, void* workspace,
+                                 size_t workspace_bytes) {
+  moe_status st = check_experts(ex);
+  if (st != MOE_OK) return st;
+  if (!routing_dims_ok(T, ex->n_experts, K) || (flags & ~MOE_INPUT_RMSNORM)) return MOE_ERR_INVALID_ARG;
+  if (!x || !idx || !workspace || !aligned16(x) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  const bool fuse = w_fuse || r_fuse || y_fuse;
+  if (fuse && !(w_fuse && r_fuse && y_fuse)) return MOE_ERR_INVALID_ARG;
+  if (!out && !fuse) return MOE_ERR_INVALID_ARG;
+  const int nslab = sparse_slabs(ex->bits, ex->d_model);
+  if (nslab < 1 || ex->d_ff > 4096 || sparse_lds(ex->bits, ex->d_ff) > 65536) return MOE_ERR_UNSUPPORTED;
+  const SparseWs ws = sparse_ws(T, K, ex);
+  if (workspace_bytes < ws.total) return MOE_ERR_INVALID_ARG;
+  char* base = (char*)workspace;
+  SparseArgs sp{};
+  DecodeArgs& a = sp.base;
+  a.T = T;
+  a.K = K;
+  a.E = ex->n_experts;
+  a.d = ex->d_model;
+  a.I = ex->d_ff;
+  a.bits = ex->bits;
+  a.group = ex->group;
+  a.flags = flags;
+  a.x = x;
+  a.idx = idx;
+  a.ex = *ex;
+  a.out = out;
+  a.w_fuse = w_fuse;
+  a.r_fuse = r_fuse;
+  a.y_fuse = y_fuse;
+  a.act = base + ws.act;
+  a.relu = true;
+  sp.o = out ? out : (float*)(base + ws.o);
+  sp.cnt = (int32_t*)(base + ws.cnt);
+  sp.n_active = n_active;
+  a.zero = sp.cnt;
+  a.nzero = nslab;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_gateup_decode(s, a);
+  if (err == hipSuccess) err = launch_down_sparse(s, sp);
+  return from_hip(err);
 }
 
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,

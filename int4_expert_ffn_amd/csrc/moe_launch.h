@@ -37,8 +37,24 @@ struct DecodeArgs {
   float* u_gate;           // workspace [T][rank] (LoRA)
   float* u_up;
   float* u_down;
+  bool relu;               // ReLU on the gate branch instead of SiLU (activation-sparse variant)
+  int32_t* zero;           // [T][nzero] int32 cleared by the gate/up kernel, or nullptr
+  int nzero;
 };
 hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a);
+// gate/up + activation only (act[T][K][I] float32), for the activation-sparse variant
+hipError_t launch_gateup_decode(hipStream_t s, const DecodeArgs& a);
+
+// ReLU activation-sparse down projection over neuron-major rows, then the combine
+struct SparseArgs {
+  DecodeArgs base;         // base.act: act[T][K][I] from launch_gateup_decode; base.ex.down neuron-major
+  float* o;                // [T][K][d] float32: base.out, or workspace when only the fused output is wanted
+  int32_t* cnt;            // workspace [T][nslab]: blocks done per (token, slab), cleared by the gate/up kernel
+  int32_t* n_active;       // [T][K] or nullptr
+};
+int sparse_slabs(int bits, int d);  // column slabs of the down kernel (0: unsupported shape)
+size_t sparse_lds(int bits, int I); // dynamic LDS bytes of the down kernel
+hipError_t launch_down_sparse(hipStream_t s, const SparseArgs& a);
 bool decode_shape_supported(int bits, int group, int d, int I);
 // u[t][r] = s_t * A[r] . v_t for `waves` = T * rank waves (s_t = RMS-norm factor when rmsnorm)
 hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,

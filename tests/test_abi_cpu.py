@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -84,6 +84,30 @@ def test_expert_ffn_rejects():
     assert _ffn(_ex(E=16), lora=lora) == INVALID              # LoRA only on a single shared expert
     bad_rank = (lib_mod.moe_lora * 3)(*[lib_mod.moe_lora(FAKE, FAKE, 65, 32.0)] * 3)
     assert _ffn(_ex(E=1), K=1, lora=bad_rank) == INVALID
+
+
+def test_sparse_ffn_rejects():
+    def sp(ex, T=1, K=2, flags=0, x=FAKE, out=FAKE, wf=None, rf=None, yf=None, n=None, ws=FAKE, wsb=1 << 40):
+        st = L.moe_expert_ffn_sparse(None, T, K, flags, x, FAKE, ctypes.byref(ex), out, wf, rf, yf, n, ws, wsb)
+        assert st in (INVALID, UNSUP), "a call with fake pointers must never pass validation"
+        return st
+
+    assert sp(_ex(bits=3)) == UNSUP
+    assert sp(_ex(d=288, group=32)) == UNSUP                 # d not a multiple of the 64-column slab
+    assert sp(_ex(bits=2, d=320, I=128, group=64)) == UNSUP    # d not a multiple of the 128-column 2-bit slab
+    assert sp(_ex(d=240, group=32)) == INVALID                # d not a multiple of the group
+    assert sp(_ex(d=256, I=8192, group=64)) == UNSUP          # d_ff above 4096
+    assert sp(_ex(), flags=1) == INVALID                      # only MOE_INPUT_RMSNORM
+    assert sp(_ex(), T=0) == INVALID
+    assert sp(_ex(), x=None) == INVALID
+    assert sp(_ex(), out=None) == INVALID                     # no output at all
+    assert sp(_ex(), wf=FAKE) == INVALID                      # partial fuse triple
+    assert sp(_ex(), wsb=16) == INVALID                       # workspace too small
+    assert sp(_ex(), ws=FAKE + 8) == INVALID
+    ex = _ex(E=256, d=2048, I=512, group=64)
+    al = lambda v: (v + 255) // 256 * 256
+    want = al(4 * 512 * 4) + al(4 * 2048 * 4) + al(32 * 4)
+    assert L.moe_expert_ffn_sparse_workspace_size(1, 4, ctypes.byref(ex)) == want
 
 
 def test_prerouter_and_combine_reject():
