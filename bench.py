@@ -147,7 +147,7 @@ def cpu_baseline(cfg, layers, syn, tokens):
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
-WORKLOADS = STACK_WORKLOADS + ("tiny", "batched")
+WORKLOADS = STACK_WORKLOADS + ("tiny", "batched", "relu-sparse")
 METRIC = "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)"
 
 
@@ -455,6 +455,143 @@ def bench_batched(args, cfg, torch, M, S, dev):
     return rec
 
 
+def bench_relu_sparse(args, cfg, torch, M, S, dev):
+    """The ReLU activation-sparse expert FFN through a resident 40-layer stack at batch 1: per layer
+    one moe_expert_ffn_sparse call (gate/up with ReLU on the gate branch, then the down projection
+    over the active neurons' neuron-major rows with the fused combine + residual), RMS-normalised
+    layer inputs, routing given (top-K of seeded logits, drawn before the timed region).  The same
+    schedule with the dense SwiGLU expert FFN (moe_expert_ffn_q4, row-major down) is timed beside it."""
+    L, K, d, E, I = cfg.L, cfg.K, cfg.d, cfg.E, cfg.I
+    syn = S.Synth(cfg)
+    t0 = time.time()
+    sparse, dense = [], []
+    for l in range(L):
+        mats = S.fill_experts(syn, l, dev, relu=True)
+        sparse.append(M.Experts(mats["gate"], mats["up"], mats["down"], cfg.bits, cfg.group, neuron_major_down=True))
+        dn = S.fill_experts(syn, l, dev)["down"]
+        dense.append(M.Experts(mats["gate"], mats["up"], dn, cfg.bits, cfg.group))
+    torch.cuda.synchronize()
+    log(f"stacks resident: 2 x {L} layers, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.1f} s")
+    tm = Timer(torch, dev, syn.hidden(7, 3 * 64, dev))
+    n_pool = tm.n_pool
+    lg = syn.logits(9, n_pool * L, dev)
+    idx_pool = torch.empty((n_pool, L, K), dtype=torch.int32, device=dev)
+    w_pool = torch.empty((n_pool, L, K), dtype=torch.float32, device=dev)
+    M.moe_route_topk(n_pool * L, d, E, K, M.MOE_TOPK_RENORM, None, None, lg, idx_pool.view(-1, K), w_pool.view(-1, K))
+    ring_i = idx_pool[0:3].clone()
+    ring_w = w_pool[0:3].clone()
+    hs = torch.empty((L + 1, d), dtype=torch.float16, device=dev)
+    n_act = torch.zeros((3, L, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(M.moe_expert_ffn_sparse_workspace_size(1, K, sparse[0]),
+                         M.moe_expert_ffn_workspace_size(1, K, dense[0])), dtype=torch.uint8, device=dev)
+
+    def token(t, h, layers, relu):
+        s = t % 3
+        hs[0].copy_(h.view(d))
+        for l in range(L):
+            x, y = hs[l].view(1, d), hs[l + 1].view(1, d)
+            if relu:
+                M.moe_expert_ffn_sparse(1, K, M.MOE_INPUT_RMSNORM, x, ring_i[s, l].view(1, K), layers[l], None,
+                                        ring_w[s, l].view(1, K), x, y, n_act[s, l].view(1, K), ws)
+            else:
+                M.moe_expert_ffn_q4(1, K, M.MOE_INPUT_RMSNORM, x, ring_i[s, l].view(1, K), layers[l], None, None,
+                                    ring_w[s, l].view(1, K), x, y, ws)
+
+    def refill(p):
+        ring_i.copy_(idx_pool[p:p + 3])
+        ring_w.copy_(w_pool[p:p + 3])
+
+    # active neurons of every pool token (inputs and routing fixed per token, so the timed pass reads the same rows)
+    counts = []
+    with torch.cuda.stream(tm.stream):
+        for p in range(0, n_pool, 3):
+            refill(p)
+            for j in range(3):
+                token(p + j + 3, tm.pool[p + j], sparse, True)     # slot (p + j) % 3 = j
+                counts.append(n_act[(p + j) % 3].clone())
+    torch.cuda.synchronize()
+    cnt = torch.stack(counts).double()
+    assert (cnt >= 0).all(), "an index outside [0, E) reached the sparse path"
+    mean_active = float(cnt.mean())
+    refill(0)
+
+    res = {}
+    for name, layers, relu in (("sparse", sparse, True), ("dense", dense, False)):
+        graphs = tm.capture(lambda t, h: token(t, h, layers, relu))
+        if args.eager:                           # same tokens, direct launches (graphs captured but unused)
+            graphs = lambda t, layers=layers, relu=relu: token(t, tm.ring[t % 3], layers, relu)
+        wall, ev_ms, warm = tm.timed(graphs, args.steps, args.warmup, refill)
+        del graphs
+        res[name] = (wall, ev_ms)
+        assert torch.isfinite(hs[L].float()).all(), f"non-finite {name} output"
+    args.warmup = warm
+    row = d * cfg.bits // 8 + (d // cfg.group) * 4                  # one neuron-major down row
+    gu = 2 * cfg.qmat_bytes("gate")
+    vec = 3 * d * 2                                                 # x read, residual read, y written
+    sparse_call = int(round(K * gu + K * mean_active * row + vec))
+    dense_call = K * cfg.expert_bytes() + vec
+    wall, ev_ms = res["sparse"]
+    call_us = ev_ms * 1e3 / (args.steps * L)
+    cfg_name = f"{cfg.name} shapes, ReLU activation-sparse experts (neuron-major down)"
+    rec = base_record(args, cfg, args.steps / wall, wall, args.steps)
+    rec["metric"] = "ReLU activation-sparse expert FFN decode tokens/s at batch 1 (40 layers) + achieved HBM GB/s"
+    rec["config"]["workload"] = (f"{cfg_name}: d_model {d}, {E} experts, top-{K}, expert I {I}, int{cfg.bits} "
+                                 f"affine g{cfg.group}, {L} layers resident, one moe_expert_ffn_sparse call per "
+                                 f"layer, routing given, batch 1")
+    rec["roofline"] = roofline("moe_expert_ffn_sparse per layer: k_gateup (ReLU) + k_down_sparse (+ fused combine)",
+                               sparse_call, call_us, None)
+    rec["roofline"]["bytes_note"] = (f"K dense gate/up matrices + the active neurons' down rows "
+                                     f"({mean_active:.1f} of {I} per expert on average, measured) + the vectors")
+    wall_d, ev_d = res["dense"]
+    dense_us = ev_d * 1e3 / (args.steps * L)
+    rec["active_fraction"] = round(mean_active / I, 4)
+    rec["dense_swiglu_same_schedule"] = {
+        "tokens_per_s": round(args.steps / wall_d, 2), "call_us": round(dense_us, 2),
+        "bytes_per_call": dense_call, "achieved_GBps": round(dense_call / (dense_us * 1e-6) / 1e9, 1),
+        "note": "moe_expert_ffn_q4 (SwiGLU, row-major down) on the same gate/up weights, inputs and routing"}
+    rec["down_bytes_saved"] = round(1 - mean_active / I, 4)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline_relu(cfg, S, syn, tokens=1)
+    return rec
+
+
+def cpu_baseline_relu(cfg, S, syn, tokens):
+    """The fp64 oracle of the ReLU sparse expert FFN through all layers for `tokens` tokens (1 BLAS
+    thread), with the same routing recipe; weights of the selected experts drawn beforehand."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    L, K = cfg.L, cfg.K
+    lg = syn.logits(9, tokens * L).numpy().reshape(tokens, L, cfg.E)
+    route = [[O.route_topk(lg[t, l][None], K) for l in range(L)] for t in range(tokens)]
+    packed = {}
+    for t in range(tokens):
+        for l in range(L):
+            for e in route[t][l][0][0]:
+                key = (l, int(e))
+                if key not in packed:
+                    packed[key] = [tuple(a[0].numpy() for a in syn.expert_mat(l, [int(e)], m))
+                                   for m in ("gate", "up", "down_nm")]
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        h = O.f64(syn.hidden(7, 1)[0].numpy())
+        for l in range(L):
+            idx, w = route[t][l]
+            x = O.rmsnorm(h)
+            o = np.stack([O.expert_ffn_relu_packed(x, *packed[(l, int(e))], cfg.bits, cfg.group)[0] for e in idx[0]])
+            h = O.to_f16_f64(O.combine(o, w[0], h))
+    elapsed = time.perf_counter() - t0
+    del limiter
+    return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{tokens} token(s) through all {L} layers of the ReLU sparse expert FFN (fp64, explicit "
+                      f"dequant, 1 BLAS thread; weights drawn beforehand)"}
+
+
 def cpu_baseline_batched(cfg, S, tokens):
     """Time the fp64 oracle (single thread) on the first `tokens` tokens of a batch: router, top-K,
     the routed experts each token selects, the shared expert with its LoRA, combine.  The packed
@@ -499,7 +636,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", choices=WORKLOADS, default="decode35b",
                     help="decode35b (default, the headline line), widek8, large-int4, large-int2 (resident stacks "
-                         "through the persistent kernel), tiny (d 256, one layer), batched (256 tokens per call)")
+                         "through the persistent kernel), tiny (d 256, one layer), batched (256 tokens per call), "
+                         "relu-sparse (decode35b shapes, ReLU activation-sparse experts, per-layer calls)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
@@ -522,8 +660,10 @@ def main():
     import moe_synth as S
 
     dev = torch.device("cuda:0")
-    cfg = S.CONFIGS[args.workload]
-    if args.workload in STACK_WORKLOADS:
+    cfg = S.CONFIGS["decode35b" if args.workload == "relu-sparse" else args.workload]
+    if args.workload == "relu-sparse":
+        rec = bench_relu_sparse(args, cfg, torch, M, S, dev)
+    elif args.workload in STACK_WORKLOADS:
         rec = bench_stack(args, cfg, torch, M, S, dev)
     elif args.workload == "tiny":
         rec = bench_tiny(args, cfg, torch, M, S, dev)

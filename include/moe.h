@@ -36,7 +36,8 @@
  *            word j/(32/bits) at bit offset bits*(j%(32/bits)), lowest bits = lowest column.
  *   scales : float16 [E][rows][cols/group]; biases: float16 [E][rows][cols/group].
  *   weight[e][o][j] = code * scales[e][o][j/group] + biases[e][o][j/group].
- *   gate and up have rows = d_ff, cols = d_model; down has rows = d_model, cols = d_ff.
+ *   gate and up have rows = d_ff, cols = d_model; down has rows = d_model, cols = d_ff
+ *   (moe_expert_ffn_sparse alone takes its down projection neuron-major: see there).
  *   q must be 16-byte aligned; rows must be a whole number of 16-byte segments
  *   (cols*bits % 128 == 0).
  */
@@ -160,9 +161,9 @@ size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_expe
      a = relu(gate_e x_t) * (up_e x_t)          (ReLU on the gate branch of the gated unit)
      o_tk = sum over the neurons i with a_i != 0 of a_i * down_e[i]
    ex->down is stored NEURON-MAJOR: row i holds the d_model weights neuron i feeds, groups of
-   ex->group run along d_model (q [E][d_ff][d_model*bits/32] words, scales / biases
-   [E][d_ff][d_model/group] float16), so a zero neuron's row is skipped whole.  gate and up are as
-   in moe_expert_ffn_q4.  Float32 accumulation; the fused combine is moe_combine's arithmetic.
+   ex->group run along d_model, so a zero neuron's row is skipped whole: q [E][d_ff][d_model*bits/32]
+   words; scales and biases float16 GROUP-MAJOR, [E][d_model/group][d_ff] (entry [e][g][i] belongs
+   to neuron i, columns g*group .. g*group+group-1).  gate and up are as in moe_expert_ffn_q4.  Float32 accumulation; the fused combine is moe_combine's arithmetic.
    Outputs: out[T][K][d] float32 (may be NULL) and/or the fused y (w_fuse, r_fuse, y_fuse all set
    or all NULL), as moe_expert_ffn_q4; n_active[T][K] int32 (may be NULL) = the number of neurons
    with a != 0, i.e. the down rows read (-1 where idx lies outside [0, E)).  flags:

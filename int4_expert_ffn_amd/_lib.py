@@ -161,8 +161,9 @@ class Experts:
     """A stack of E quantised experts (tensors kept alive here) and its C descriptor."""
 
     def __init__(self, gate, up, down, bits: int, group: int, neuron_major_down: bool = False):
-        """neuron_major_down: down is [E][d_ff][d_model] (the layout of moe_expert_ffn_sparse), else
-        [E][d_model][d_ff]."""
+        """neuron_major_down: down codes [E][d_ff][d_model] with group-major scales / biases
+        [E][d_model/group][d_ff] (the layout of moe_expert_ffn_sparse), else codes [E][d_model][d_ff]
+        with scales / biases [E][d_model][d_ff/group]."""
         self.tensors = (gate, up, down)
         q = gate[0]
         E, I, words = q.shape
@@ -170,6 +171,9 @@ class Experts:
         want = (E, I, d * bits // 32) if neuron_major_down else (E, d, I * bits // 32)
         if tuple(down[0].shape) != want:
             raise ValueError(f"down codes have shape {tuple(down[0].shape)}, expected {want}")
+        want = (E, d // group, I) if neuron_major_down else (E, d, I // group)
+        if tuple(down[1].shape) != want or tuple(down[2].shape) != want:
+            raise ValueError(f"down scales/biases have shape {tuple(down[1].shape)}, expected {want}")
         self.neuron_major_down = neuron_major_down
         mats = [moe_qmat(_ptr(m[0], _qw(), "q"), _ptr(m[1], _f16(), "scales"), _ptr(m[2], _f16(), "biases"))
                 for m in (gate, up, down)]

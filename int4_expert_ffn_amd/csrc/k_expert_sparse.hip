@@ -6,7 +6,10 @@
 // nor multiplied.  The gate/up kernel of the dense path computes a = relu(gate) * up; here the
 // down projection reads only the rows of neurons with a != 0.  The down matrix is stored
 // neuron-major ([E][I][d], quantisation groups along d), so one neuron is one contiguous packed
-// row and a skipped neuron is a skipped row of bytes.
+// row and a skipped neuron is a skipped row of bytes.  Its scales and biases are stored
+// group-major ([E][d/group][I]): a block's column slab lies in one or two groups, so the scales
+// it reads sit in a short run of lines that no block of another XCD touches (row-major scales put
+// every XCD's few bytes of a row in the same line, and each XCD fetched that line).
 //
 // Mapping.  Block (slab, k, t) owns SLAB output columns of o_tk.  It lists the active neurons of
 // expert e = idx[t][k] (a != 0, ascending) in LDS from act[t][k][:] with wave ballots, then its
@@ -48,7 +51,7 @@ struct SpK {
   int K, E, d, I, lg2g, nslab;
   const float* act;      // [T][K][I]
   const int32_t* idx;    // [T][K]
-  moe_qmat down;         // neuron-major: q [E][I][d*BITS/32], scales / biases [E][I][d/group]
+  moe_qmat down;         // neuron-major: q [E][I][d*BITS/32]; scales / biases group-major, [E][d/group][I]
   float* o;              // [T][K][d]
   const float* wf;       // [T][K] or nullptr (no fused output)
   const uint16_t* rf;    // [T][d]
@@ -127,8 +130,8 @@ __global__ void __launch_bounds__(SP_THREADS) k_down_sparse(SpK p) {
   const int wpr = p.d * BITS / 32, ngr = p.d >> p.lg2g;
   const int c0 = slab * G::SLAB + ls * G::COLS;
   const uint32_t* qe = p.down.q + (size_t)e * p.I * wpr + (size_t)c0 * BITS / 32;
-  const size_t sbe = (size_t)e * p.I * ngr;
   const int ga = c0 >> p.lg2g, gb = (c0 + G::COLS / 2) >> p.lg2g;
+  const size_t sga = ((size_t)e * ngr + ga) * p.I, sgb = ((size_t)e * ngr + gb) * p.I;
   float acc[G::COLS];
 #pragma unroll
   for (int c = 0; c < G::COLS; ++c) acc[c] = 0.f;
@@ -144,11 +147,11 @@ __global__ void __launch_bounds__(SP_THREADS) k_down_sparse(SpK p) {
       al[nb] = j < n ? list_a[jj] : 0.f;
       const size_t row = list_i[jj];
       q[nb] = *reinterpret_cast<const uint4*>(qe + row * wpr);
-      sa[nb] = p.down.scales[sbe + row * ngr + ga];
-      ba[nb] = p.down.biases[sbe + row * ngr + ga];
+      sa[nb] = p.down.scales[sga + row];
+      ba[nb] = p.down.biases[sga + row];
       if (SPLIT) {
-        sb[nb] = p.down.scales[sbe + row * ngr + gb];
-        bb[nb] = p.down.biases[sbe + row * ngr + gb];
+        sb[nb] = p.down.scales[sgb + row];
+        bb[nb] = p.down.biases[sgb + row];
       }
     }
 #pragma unroll
@@ -220,14 +223,16 @@ __global__ void __launch_bounds__(SP_THREADS) k_down_sparse(SpK p) {
   }
   if (p.n_active && slab == 0 && tid == 0) p.n_active[(size_t)t * p.K + k] = bad ? -1 : n;
 
-  // 4. fused combine by the last of the token's K blocks on this slab
+  // 4. fused combine by the last of the token's K blocks on this slab.  The o stores above and the
+  //    loads below are agent-scope atomic accesses, coherent across the XCDs' L2s by themselves;
+  //    waiting for the stores' completion before the counter's atomic add orders them.  (A full
+  //    device fence would write back and invalidate the whole L2 instead, several microseconds.)
   if (p.wf) {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores have completed
     __syncthreads();
     if (tid == 0) misc[SP_WAVES] = atomicAdd(&p.cnt[(size_t)t * p.nslab + slab], 1) == p.K - 1;
     __syncthreads();
     if (misc[SP_WAVES] && tid < G::SLAB) {
-      __threadfence();
       float y = 0.f;
       for (int kk = 0; kk < p.K; ++kk)
         y = fmaf(p.wf[(size_t)t * p.K + kk], ld_coherent(p.o + ((size_t)t * p.K + kk) * p.d + col), y);

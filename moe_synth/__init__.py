@@ -295,7 +295,8 @@ class Synth:
 def fill_experts(syn: Synth, layer: int, device, chunk: int = 32, relu: bool = False):
     """All E routed experts of one layer on `device`: dict mat -> (q, s, b) stacked [E][...].
     relu: the down projection is drawn neuron-major ([E][I][d], groups along d), the layout of
-    the ReLU activation-sparse expert; gate and up are the same draws either way."""
+    the ReLU activation-sparse expert, with its scales and biases stored group-major ([E][d/group][I],
+    a transposed copy of the drawn [E][I][d/group] values); gate and up are the same draws either way."""
     c = syn.cfg
     out = {}
     for mat in MATS:
@@ -310,5 +311,7 @@ def fill_experts(syn: Synth, layer: int, device, chunk: int = 32, relu: bool = F
             q[e0:e0 + len(ids)] = qq
             s[e0:e0 + len(ids)] = ss
             b[e0:e0 + len(ids)] = bb
+        if src == "down_nm":
+            s, b = s.transpose(1, 2).contiguous(), b.transpose(1, 2).contiguous()
         out[mat] = (q, s, b)
     return out

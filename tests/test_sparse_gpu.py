@@ -191,7 +191,7 @@ def test_sparse_inactive_rows_are_not_read(M):
         e = int(idx[0, k])
         g = cache(e)[0] @ x[0]
         off = np.nonzero(g < -1e-3 * np.max(np.abs(g)))[0]
-        mats["down"][1][e, torch.as_tensor(off, device=DEV)] = float("nan")
+        mats["down"][1][e, :, torch.as_tensor(off, device=DEV)] = float("nan")   # scales [E][d/group][I]
         poisoned += len(off)
     log(f"poisoned {poisoned} down rows")
     assert poisoned > cfg.K * cfg.I // 4
@@ -233,3 +233,28 @@ def test_sparse_deterministic_and_fused_only(M):
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
     assert torch.equal(a[1], c[1]) and torch.equal(a[2], c[2])
+
+
+def test_sparse_fused_combine_repeated(M):
+    """The fused combine is formed by whichever of a slab's K blocks finishes last, from the o_k the
+    other blocks stored: over many calls with fresh inputs, the fused-only output must equal, bit
+    for bit, the one of the call that also returns o_k, and that one the combine of its o_k."""
+    cfg = S.CONFIGS["decode35b"]
+    syn = S.Synth(cfg)
+    ex, _ = sparse_layer(M, syn, 2)
+    T, K = 4, cfg.K
+    hs = syn.hidden(40, 48 * T).to(DEV).view(48, T, cfg.d)
+    lg = syn.logits(41, 48 * T).to(DEV)
+    idx = torch.empty((48 * T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((48 * T, K), dtype=torch.float32, device=DEV)
+    M.moe_route_topk(48 * T, cfg.d, cfg.E, K, M.MOE_TOPK_RENORM, None, None, lg, idx, w)
+    idx, w = idx.view(48, T, K), w.view(48, T, K)
+    y_ref = torch.empty((T, cfg.d), dtype=torch.float16, device=DEV)
+    for i in range(48):
+        h = hs[i]
+        out, y, _ = run_sparse(M, ex, T, K, 0, h, idx[i], w[i], h)
+        _, y2, _ = run_sparse(M, ex, T, K, 0, h, idx[i], w[i], h, with_out=False)
+        M.moe_combine(T, K, cfg.d, out, w[i], h, None, y_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), f"call {i}: fused-only output differs"
+        assert torch.equal(y, y_ref), f"call {i}: fused output differs from the combine of o_k"
