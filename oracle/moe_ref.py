@@ -374,3 +374,69 @@ def chain_token(h0, state: ChainState, *, E: int, K: int, bits: int, group: int,
         traces.append(LayerTrace(np.array(idx), np.array(w), rl, hl, y))
         h = y
     return h, new, traces
+
+
+# ----------------------------------------------------------------------------------------
+# Expert streaming from a slower memory tier  [DEVICE, "Las matemáticas que importan": the
+# resident set is the active experts plus a cache of recent / likely ones, and the number of
+# experts one window of compute can bring in; DEVICE, "El pre-attention router": the load is
+# hidden when the compute window is at least the load time; EDGE0, "Ideas clave": experts are
+# streamed into a compact pool and the one-token-ahead prediction is the routing, so the
+# prepared set is the routed set]
+# ----------------------------------------------------------------------------------------
+def experts_per_window(window_s: float, bandwidth_Bps: float, expert_bytes: float) -> int:
+    """How many whole experts a load of `bandwidth_Bps` brings in during `window_s`:
+    floor(window / t_one) with t_one = expert_bytes / bandwidth."""
+    t_one = expert_bytes / bandwidth_Bps
+    return int(math.floor(window_s / t_one * (1 + 1e-12)))
+
+
+def stall_time(n_needed: int, window_s: float, bandwidth_Bps: float, expert_bytes: float) -> float:
+    """Wait exposed in one window: the experts past what the window covers load after it, each
+    costing t_one; zero when every needed expert fits under the window."""
+    t_one = expert_bytes / bandwidth_Bps
+    n_free = experts_per_window(window_s, bandwidth_Bps, expert_bytes)
+    return max(0, n_needed - n_free) * t_one
+
+
+@dataclass
+class PoolState:
+    """One layer's pool of `n_slots` expert slots: the expert each slot holds (-1 = empty) and the
+    last token that used it (-1 = never)."""
+    n_slots: int
+    expert: List[int] = field(default_factory=list)
+    stamp: List[int] = field(default_factory=list)
+
+    def __post_init__(self):
+        if not self.expert:
+            self.expert = [-1] * self.n_slots
+        if not self.stamp:
+            self.stamp = [-1] * self.n_slots
+
+
+def pool_plan(state: PoolState, idx: Sequence[int], token: int):
+    """Place a token's selected experts in the pool, least recently used slot first.
+
+    Reading taken (the pages keep "recent / likely" experts and say no more): every selected
+    expert already in a slot is a hit and its slot is stamped with the token; then, in slot-k
+    order, each missing expert takes the slot with the oldest stamp among those this token has
+    not stamped (empty slots first, then ties to the lowest slot index), and must be copied in.
+    Returns (slot of each k, list of (k, slot, expert) copies) and updates `state`."""
+    idx = [int(e) for e in idx]
+    slot = [-1] * len(idx)
+    for k, e in enumerate(idx):
+        if e in state.expert:
+            s = state.expert.index(e)
+            slot[k] = s
+            state.stamp[s] = token
+    copies = []
+    for k, e in enumerate(idx):
+        if slot[k] >= 0:
+            continue
+        free = [(state.stamp[s], s) for s in range(state.n_slots) if state.stamp[s] < token]
+        _, s = min(free)
+        state.expert[s] = e
+        state.stamp[s] = token
+        slot[k] = s
+        copies.append((k, s, e))
+    return slot, copies

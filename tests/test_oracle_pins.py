@@ -377,3 +377,49 @@ def test_relu_expert_all_off_and_all_on():
     o, a = O.expert_ffn_relu(x, Wpos, Wu, WdT)
     np.testing.assert_allclose(o, np.einsum("i,id->d", (Wpos @ x) * (Wu @ x), WdT), rtol=1e-12)
     assert int(O.active_neurons(a)) == I
+
+
+# ------------------------------------------------------------------ expert streaming
+def test_prefetch_window_worked_example():
+    """The pages' own numbers: 5 GB/s, 2 MB experts, a 2 ms window -> 5 experts, 1.2 ms wait for 8."""
+    fx = read_fixture("prefetch_window.txt")
+    g = lambda k: float(fx[k][0][0])
+    bw, X, Y = g("bandwidth_Bps"), g("expert_bytes"), g("window_s")
+    assert X / bw == pytest.approx(g("t_one_s"), rel=1e-12)
+    assert O.experts_per_window(Y, bw, X) == int(g("n_prefetch"))
+    assert O.stall_time(int(g("needed")), Y, bw, X) == pytest.approx(g("stall_s"), rel=1e-12)
+    assert O.stall_time(int(g("needed_small")), Y, bw, X) == g("stall_small_s")
+    # one byte of bandwidth less and the fifth expert no longer fits
+    assert O.experts_per_window(Y, bw * (1 - 1e-6), X) == 4
+
+
+def test_pool_plan_hand_sequence():
+    fx = read_fixture("pool_lru_hand.txt")
+    st = O.PoolState(3)
+    ints = lambda s: [int(v) for v in s.split(",")]
+    for row in fx["step"]:
+        tok, sel, slots, pool, stamps, cp = row
+        slot, copies = O.pool_plan(st, ints(sel), int(tok))
+        assert slot == ints(slots)
+        assert st.expert == ints(pool) and st.stamp == ints(stamps)
+        want = [] if cp == "-" else [tuple(int(v) for v in c.split(":")) for c in cp.split(",")]
+        assert copies == want
+
+
+def test_pool_plan_invariants_random():
+    """Over a long random sequence with reuse: every selected expert sits in exactly the slot
+    returned, no expert is in two slots, and copies happen exactly for the selected experts that
+    were not pooled before."""
+    rng = np.random.default_rng(7)
+    E, K, S = 40, 4, 9
+    st = O.PoolState(S)
+    for t in range(300):
+        sel = list(rng.choice(E if t % 3 else 12, size=K, replace=False))
+        before = set(e for e in st.expert if e >= 0)
+        slot, copies = O.pool_plan(st, sel, t)
+        for k, e in enumerate(sel):
+            assert st.expert[slot[k]] == e and st.stamp[slot[k]] == t
+        pooled = [e for e in st.expert if e >= 0]
+        assert len(pooled) == len(set(pooled))
+        assert sorted(e for _, _, e in copies) == sorted(e for e in sel if e not in before)
+        assert len(set(slot)) == K
