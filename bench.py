@@ -147,7 +147,7 @@ def cpu_baseline(cfg, layers, syn, tokens):
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
-WORKLOADS = STACK_WORKLOADS + ("tiny", "batched", "relu-sparse")
+WORKLOADS = STACK_WORKLOADS + ("tiny", "batched", "relu-sparse", "stream")
 METRIC = "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)"
 
 
@@ -234,19 +234,20 @@ class Timer:
             else:
                 graphs[(t - 1) % 3].replay()
 
-    def timed(self, graphs, steps, warmup, refill=None):
-        """(wall seconds, HIP-event milliseconds, warm-up tokens actually run)"""
+    def timed(self, graphs, steps, warmup, refill=None, start=1):
+        """(wall seconds, HIP-event milliseconds, warm-up tokens actually run); tokens are numbered
+        from `start` (1 more than a multiple of 3)."""
         torch = self.torch
         warmup = -(-warmup // 3) * 3             # whole slot rotations keep tokens consecutive
         with torch.cuda.stream(self.stream):
-            self.run(graphs, warmup, 1, refill)
+            self.run(graphs, warmup, start, refill)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(self.stream):
             torch.cuda.synchronize()
             w0 = time.perf_counter()
             e0.record(self.stream)
-            self.run(graphs, steps, 1 + warmup, refill)
+            self.run(graphs, steps, start + warmup, refill)
             e1.record(self.stream)
             torch.cuda.synchronize()
             w1 = time.perf_counter()
@@ -556,6 +557,116 @@ def bench_relu_sparse(args, cfg, torch, M, S, dev):
     return rec
 
 
+def bench_stream(args, cfg, torch, M, S, dev):
+    """Expert streaming (the pages' storage tier, here pinned host memory read over the host link):
+    the 40-layer prerouted decode35b stack with every expert in host memory and an HBM pool of
+    `--pool-slots` experts per layer.  Prefetch mode streams each layer's predicted experts for the
+    next token on a copy stream as soon as the head of the layer before has predicted them; reactive
+    mode streams each layer's experts in just before its expert FFN.  Each token is one HIP-graph
+    replay; the resident stack's per-layer calls, replayed the same way, are timed for context."""
+    from int4_expert_ffn_amd.chain import DecodeStack, LayerWeights
+    from int4_expert_ffn_amd.stream import StreamedStack
+    syn = S.Synth(cfg)
+    t0 = time.time()
+    routers = [syn.router(l, dev) for l in range(cfg.L + 1)]
+    host_layers, dev_layers = [], []
+    for l in range(cfg.L):
+        mats = S.fill_experts(syn, l, dev)
+        hmats = {m: tuple(torch.empty(a.shape, dtype=a.dtype, pin_memory=True).copy_(a) for a in arrs)
+                 for m, arrs in mats.items()}
+        head = None
+        if l < cfg.L - 1:
+            hw = syn.head(l, dev)
+            hw["lin_x"] = routers[l + 1]
+            head = M.PrerouterWeights(hw)
+        dev_layers.append(LayerWeights(M.Experts(mats["gate"], mats["up"], mats["down"], cfg.bits, cfg.group),
+                                       routers[l], head))
+        host_layers.append(LayerWeights(M.Experts(hmats["gate"], hmats["up"], hmats["down"], cfg.bits, cfg.group,
+                                                  host=True), routers[l], head))
+    torch.cuda.synchronize()
+    log(f"stack in pinned host memory and resident: {cfg.L} layers, {time.time() - t0:.1f} s")
+    X = cfg.expert_bytes()
+    tm = Timer(torch, dev, syn.hidden(7, 3 * 64, dev))
+
+    # host link bandwidth of the pool copy: misses forced by resetting a pool before each call
+    n_cal = 24
+    pool = M.Pool(host_layers[1].experts, args.pool_slots, dev)
+    cal_idx = (torch.arange((n_cal + 2) * cfg.K, dtype=torch.int32, device=dev) % cfg.E).view(n_cal + 2, cfg.K)
+    cal_slot = torch.empty(cfg.K, dtype=torch.int32, device=dev)
+    cal_ws = torch.empty(M.moe_stream_workspace_size(cfg.K), dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(tm.stream):
+        for i in range(n_cal + 2):
+            pool.reset()                     # every call copies all K experts
+            if i == 2:
+                e0.record(tm.stream)
+            M.moe_stream_in(cfg.K, cal_idx[i], host_layers[1].experts, pool, cal_slot, None, cal_ws)
+        e1.record(tm.stream)
+    torch.cuda.synchronize()
+    del pool
+    cal_us = e0.elapsed_time(e1) * 1e3 / n_cal
+    link_gbps = cfg.K * X / (cal_us * 1e-6) / 1e9
+    log(f"pool copy: {cfg.K} experts in {cal_us:.1f} us = {link_gbps:.1f} GB/s")
+
+    res = {}
+    for mode in ("prefetch", "reactive"):
+        stm = StreamedStack(host_layers, cfg.K, dev, n_slots=args.pool_slots, prefetch=(mode == "prefetch"))
+        run = tm.capture(lambda t, h, stm=stm: stm.token(t, h))
+        # fill the pools first (about n_slots / misses-per-layer tokens), then count over the timed tokens
+        n_fill = -(-max(args.warmup, 2 * args.pool_slots) // 3) * 3
+        with torch.cuda.stream(tm.stream):
+            tm.run(run, n_fill, 1)
+        torch.cuda.synchronize()
+        h_a, m_a = stm.hits_misses()
+        wall, ev_ms, _ = tm.timed(run, args.steps, 0, start=1 + n_fill)
+        del run
+        h_b, m_b = stm.hits_misses()
+        assert torch.isfinite(stm.h[cfg.L].float()).all(), f"non-finite {mode} output"
+        res[mode] = dict(wall=wall, us=ev_ms * 1e3 / args.steps, hits=h_b - h_a, misses=m_b - m_a, tokens=args.steps)
+    args.warmup = n_fill
+    stack = DecodeStack(dev_layers, cfg.K, dev)
+    graphs = tm.capture(lambda t, h: stack.token(t, h))
+    n2 = max(30, args.steps // 4)
+    wall_r, ev_r, _ = tm.timed(graphs, n2, 30)
+    del graphs
+    res_us = ev_r * 1e3 / n2
+
+    p = res["prefetch"]
+    miss_tok = p["misses"] / p["tokens"]
+    hit_rate = p["hits"] / max(1, p["hits"] + p["misses"])
+    bytes_tok = miss_tok * X
+    # the pages' window model: in a window of w seconds the link brings floor(w * BW / X) experts;
+    # the rest load after it ("Las matemáticas que importan")
+    window_s = res_us * 1e-6
+    n_window = math.floor(window_s * link_gbps * 1e9 / X)
+    predicted_us = res_us + max(0.0, miss_tok - n_window) * X / (link_gbps * 1e9) * 1e6
+    rec = base_record(args, cfg, args.steps / p["wall"], p["wall"], args.steps)
+    rec["metric"] = "Streamed-expert decode tokens/s at batch 1 (experts in pinned host memory, HBM pool per layer)"
+    rec["config"]["workload"] = (describe(cfg) + f"; every expert in pinned host memory, an HBM pool of "
+                                 f"{args.pool_slots} experts per layer ({args.pool_slots * X * cfg.L / 2**30:.2f} GiB), "
+                                 f"prerouter prefetch one token ahead on a copy stream")
+    rec["roofline"] = {"kernel": "k_pool_copy (host memory -> HBM pool)", "bound": "host link",
+                       "achieved": round(link_gbps, 1), "peak": 64.0, "unit": "GB/s",
+                       "frac": round(link_gbps / 64.0, 4), "traffic": None, "bytes_per_launch": cfg.K * X,
+                       "avg_us": round(cal_us, 2),
+                       "note": "peak = PCIe 5.0 x16, one direction; the copy reads host memory over the host link"}
+    rec["streaming"] = {
+        "experts_streamed_per_token": round(miss_tok, 2), "hit_rate": round(hit_rate, 4),
+        "bytes_streamed_per_token": int(round(bytes_tok)), "expert_bytes": X,
+        "prefetch_us_per_token": round(p["us"], 1),
+        "reactive_tokens_per_s": round(args.steps / res["reactive"]["wall"], 2),
+        "reactive_us_per_token": round(res["reactive"]["us"], 1),
+        "resident_per_layer_tokens_per_s": round(n2 / wall_r, 2), "resident_us_per_token": round(res_us, 1),
+        "window_model": {"window_us": round(res_us, 1), "link_GBps": round(link_gbps, 1),
+                         "experts_per_window": n_window, "experts_needed": round(miss_tok, 2),
+                         "predicted_us_per_token": round(predicted_us, 1),
+                         "hidden": bool(miss_tok <= n_window)},
+        "note": "every path replays one HIP graph per token (the streamed ones on two streams, joined at the "
+                "token's end); the resident per-layer path runs the same schedule with every expert in HBM",
+    }
+    return rec
+
+
 def cpu_baseline_relu(cfg, S, syn, tokens):
     """The fp64 oracle of the ReLU sparse expert FFN through all layers for `tokens` tokens (1 BLAS
     thread), with the same routing recipe; weights of the selected experts drawn beforehand."""
@@ -637,7 +748,9 @@ def main():
     ap.add_argument("--workload", choices=WORKLOADS, default="decode35b",
                     help="decode35b (default, the headline line), widek8, large-int4, large-int2 (resident stacks "
                          "through the persistent kernel), tiny (d 256, one layer), batched (256 tokens per call), "
-                         "relu-sparse (decode35b shapes, ReLU activation-sparse experts, per-layer calls)")
+                         "relu-sparse (decode35b shapes, ReLU activation-sparse experts, per-layer calls), "
+                         "stream (decode35b with every expert in pinned host memory, HBM pools)")
+    ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
@@ -660,8 +773,10 @@ def main():
     import moe_synth as S
 
     dev = torch.device("cuda:0")
-    cfg = S.CONFIGS["decode35b" if args.workload == "relu-sparse" else args.workload]
-    if args.workload == "relu-sparse":
+    cfg = S.CONFIGS["decode35b" if args.workload in ("relu-sparse", "stream") else args.workload]
+    if args.workload == "stream":
+        rec = bench_stream(args, cfg, torch, M, S, dev)
+    elif args.workload == "relu-sparse":
         rec = bench_relu_sparse(args, cfg, torch, M, S, dev)
     elif args.workload in STACK_WORKLOADS:
         rec = bench_stack(args, cfg, torch, M, S, dev)

@@ -71,6 +71,7 @@ typedef enum {
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 16
 #define MOE_MAX_D 8192
+#define MOE_POOL_MAX_SLOTS 4096
 
 typedef struct {
   const uint32_t* q;
@@ -175,6 +176,47 @@ moe_status moe_expert_ffn_sparse(void* stream, int32_t T, int32_t K, uint32_t fl
                                  const int32_t* idx, const moe_experts* ex, float* out, const float* w_fuse,
                                  const uint16_t* r_fuse, uint16_t* y_fuse, int32_t* n_active, void* workspace,
                                  size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------------------------
+   Expert streaming from a slower memory tier into an HBM pool ("Arquitecturas nativas para device:
+   MoE de grano fino y pre-attention router", section "Las matemáticas que importan": only the
+   active experts and a cache of recent ones are resident, the rest is fetched when needed; "La otra
+   mitad del muro de la memoria ...", section "Ideas clave": experts stream into a compact pool and
+   the one-token-ahead prediction is the routing).
+
+   A pool is n_slots experts in HBM, described by an moe_experts with n_experts = n_slots and the
+   same d_model, d_ff, bits, group and layouts as the source.  Its state is device memory the caller
+   owns: slot_expert[n_slots] (int32, the expert a slot holds, -1 = empty), slot_stamp[n_slots]
+   (int32, the call that last used it, -1 = never) and clock[1] (int32, the number of calls so far,
+   which is the stamp of the next call); fill slot_expert and slot_stamp with -1 and clock with 0
+   before the first call.  One call per token makes a stamp a token number. */
+typedef struct {
+  int32_t n_slots;
+  int32_t* slot_expert;
+  int32_t* slot_stamp;
+  int32_t* clock;
+} moe_pool;
+
+/* Bytes of device workspace moe_stream_in needs for K selected experts. */
+size_t moe_stream_workspace_size(int32_t K);
+
+/* Place a token's K selected experts idx[K] (int32, device) in the pool and copy the missing ones
+   from src (E experts whose arrays may be pinned host memory the GPU can read, or device memory).
+   Placement: an expert already in a slot is a hit and keeps its slot; then, in k order, each
+   missing expert takes the least recently used slot among those this call has not claimed (empty
+   slots first, then the oldest stamp, ties to the lowest slot); every slot used gets the call's
+   stamp, *clock, and *clock then advances by one.  The stamp lives on the device, so a captured
+   HIP graph replays correctly.  Writes idx_slot[K] (int32, device): the slot of each selected expert, for
+   moe_expert_ffn_q4 / moe_expert_ffn_sparse on the pool (an index outside [0, E) gets -1, which
+   those calls turn into NaN).  counters[2] (int32, device, may be NULL): the call's hits and copies
+   (misses) are added; an index outside [0, E) is neither.
+   Calls on one pool must not overlap.  With one call per token and n_slots >= 2K, a slot used by
+   token t is not reused before token t+2, so the copy for token t+1 may run beside token t's
+   expert FFN.
+   Limits: 1 <= K <= 16, K <= n_slots <= MOE_POOL_MAX_SLOTS; src and pool of equal shape. */
+moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_experts* src,
+                         const moe_experts* pool_experts, const moe_pool* pool, int32_t* idx_slot,
+                         int32_t* counters, void* workspace, size_t workspace_bytes);
 
 /* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
    (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose

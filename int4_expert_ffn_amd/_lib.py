@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_route_topk", "moe_prerouter_workspace_size", "moe_prerouter",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
-    "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse",
+    "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
 )
 
 
@@ -61,6 +61,11 @@ class moe_decode_layer(ctypes.Structure):
                 ("norm_gain", ctypes.c_void_p)]
 
 
+class moe_pool(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("slot_expert", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("clock", ctypes.c_void_p)]
+
+
 class moe_decode_stack(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
@@ -87,6 +92,9 @@ def _load():
         "moe_expert_ffn_sparse_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
         "moe_expert_ffn_sparse": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), vp, vp, vp, vp, vp,
                                        vp, sz]),
+        "moe_stream_workspace_size": (sz, [i32]),
+        "moe_stream_in": (st, [vp, i32, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_experts),
+                               ctypes.POINTER(moe_pool), vp, vp, vp, sz]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -106,20 +114,50 @@ _lib = _load()
 
 
 # ----------------------------------------------------------------------------------------------
-def _ptr(t, dtype=None, name="tensor") -> Optional[int]:
-    """Device address of a tensor (checked), a raw int address, or None."""
+def _ptr(t, dtype=None, name="tensor", pinned_ok=False) -> Optional[int]:
+    """Device address of a tensor (checked), a raw int address, or None.  pinned_ok: a pinned host
+    tensor is accepted too (its address is valid on the device)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
     import torch
+    if not t.is_cuda and not (pinned_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor" + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return _host_device_ptr(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     return t.data_ptr()
+
+
+_hip = None
+
+
+def _host_device_ptr(t, name) -> int:
+    """The device address of pinned host memory, as the HIP runtime maps it (refused, before any
+    launch, when the runtime reports the memory is not mapped for the device)."""
+    global _hip
+    if _hip is None:
+        for cand in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                _hip = ctypes.CDLL(cand)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise ValueError("the HIP runtime library is not loadable")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    dptr = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dptr.value:
+        raise ValueError(f"{name}: pinned host memory has no device mapping (hipHostGetDevicePointer error {err})")
+    return dptr.value
 
 
 def _stream(stream, *tensors) -> Optional[int]:
@@ -160,10 +198,12 @@ def _qw():
 class Experts:
     """A stack of E quantised experts (tensors kept alive here) and its C descriptor."""
 
-    def __init__(self, gate, up, down, bits: int, group: int, neuron_major_down: bool = False):
+    def __init__(self, gate, up, down, bits: int, group: int, neuron_major_down: bool = False,
+                 host: bool = False):
         """neuron_major_down: down codes [E][d_ff][d_model] with group-major scales / biases
         [E][d_model/group][d_ff] (the layout of moe_expert_ffn_sparse), else codes [E][d_model][d_ff]
-        with scales / biases [E][d_model][d_ff/group]."""
+        with scales / biases [E][d_model][d_ff/group].  host: the tensors may be pinned host memory
+        (a streaming source for moe_stream_in)."""
         self.tensors = (gate, up, down)
         q = gate[0]
         E, I, words = q.shape
@@ -175,8 +215,8 @@ class Experts:
         if tuple(down[1].shape) != want or tuple(down[2].shape) != want:
             raise ValueError(f"down scales/biases have shape {tuple(down[1].shape)}, expected {want}")
         self.neuron_major_down = neuron_major_down
-        mats = [moe_qmat(_ptr(m[0], _qw(), "q"), _ptr(m[1], _f16(), "scales"), _ptr(m[2], _f16(), "biases"))
-                for m in (gate, up, down)]
+        mats = [moe_qmat(_ptr(m[0], _qw(), "q", host), _ptr(m[1], _f16(), "scales", host),
+                         _ptr(m[2], _f16(), "biases", host)) for m in (gate, up, down)]
         self.desc = moe_experts(E, d, I, bits, group, *mats)
         self.E, self.d, self.I, self.bits, self.group = E, d, I, bits, group
 
@@ -251,6 +291,42 @@ def moe_expert_ffn_sparse(T, K, flags, x, idx, ex: Experts, out, w_fuse, r_fuse,
                                     _ptr(y_fuse, _f16(), "y_fuse"), _ptr(n_active, _i32(), "n_active"),
                                     _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_expert_ffn_sparse")
+
+
+class Pool:
+    """An HBM pool of n_slots experts shaped like `like` (an Experts), its slot state, and its
+    descriptors for moe_stream_in and the expert FFN calls."""
+
+    def __init__(self, like: Experts, n_slots: int, device):
+        import torch
+        dev = torch.device(device)
+        mats = []
+        for m in like.tensors:
+            mats.append(tuple(torch.empty((n_slots,) + tuple(a.shape[1:]), dtype=a.dtype, device=dev) for a in m))
+        self.experts = Experts(*mats, like.bits, like.group, neuron_major_down=like.neuron_major_down)
+        self.slot_expert = torch.full((n_slots,), -1, dtype=torch.int32, device=dev)
+        self.slot_stamp = torch.full((n_slots,), -1, dtype=torch.int32, device=dev)
+        self.clock = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.desc = moe_pool(n_slots, self.slot_expert.data_ptr(), self.slot_stamp.data_ptr(), self.clock.data_ptr())
+        self.n_slots = n_slots
+
+    def reset(self):
+        self.slot_expert.fill_(-1)
+        self.slot_stamp.fill_(-1)
+        self.clock.zero_()
+
+
+def moe_stream_workspace_size(K) -> int:
+    return _lib.moe_stream_workspace_size(K)
+
+
+def moe_stream_in(K, idx, src: Experts, pool: Pool, idx_slot, counters, workspace, workspace_bytes=None,
+                  stream=None):
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_stream_in(_stream(stream, idx, idx_slot), K, _ptr(idx, _i32(), "idx"), ctypes.byref(src.desc),
+                            ctypes.byref(pool.experts.desc), ctypes.byref(pool.desc), _ptr(idx_slot, _i32(), "idx_slot"),
+                            _ptr(counters, _i32(), "counters"), _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_stream_in")
 
 
 def moe_combine(T, K, d, o, w, r, shared, y, stream=None):

@@ -247,6 +247,47 @@ moe_status moe_expert_ffn_sparse(void* stream, int32_t T, int32_t K, uint32_t fl
   return from_hip(err);
 }
 
+size_t moe_stream_workspace_size(int32_t K) {
+  if (K < 1 || K > MOE_MAX_K) return 0;
+  return align_up(pool_plan_bytes(K));
+}
+
+moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_experts* src,
+                         const moe_experts* pool_experts, const moe_pool* pool, int32_t* idx_slot, int32_t* counters,
+                         void* workspace, size_t workspace_bytes) {
+  if (!src || !pool_experts || !pool || !idx || !idx_slot || !workspace) return MOE_ERR_INVALID_ARG;
+  if (K < 1 || K > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  if (!pool->slot_expert || !pool->slot_stamp || !pool->clock) return MOE_ERR_INVALID_ARG;
+  if (pool->n_slots < K || pool->n_slots > MOE_POOL_MAX_SLOTS || pool_experts->n_experts != pool->n_slots)
+    return MOE_ERR_INVALID_ARG;
+  if (src->n_experts < 1 || src->n_experts > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (src->d_model != pool_experts->d_model || src->d_ff != pool_experts->d_ff || src->bits != pool_experts->bits ||
+      src->group != pool_experts->group)
+    return MOE_ERR_INVALID_ARG;
+  if (src->bits != 4 && src->bits != 2) return MOE_ERR_UNSUPPORTED;
+  if (src->group != 32 && src->group != 64 && src->group != 128) return MOE_ERR_UNSUPPORTED;
+  const int d = src->d_model, I = src->d_ff;
+  if (d < 1 || I < 1 || d > MOE_MAX_D || I > MOE_MAX_D || d % src->group || I % src->group) return MOE_ERR_INVALID_ARG;
+  if ((d * src->bits) % 128 || (I * src->bits) % 128) return MOE_ERR_INVALID_ARG;
+  for (const moe_qmat* m : {&src->gate, &src->up, &src->down, &pool_experts->gate, &pool_experts->up, &pool_experts->down}) {
+    moe_status st = check_qmat(*m);
+    if (st != MOE_OK) return st;
+  }
+  if (!aligned16(workspace) || workspace_bytes < moe_stream_workspace_size(K)) return MOE_ERR_INVALID_ARG;
+  PoolArgs a{};
+  a.K = K;
+  a.E = src->n_experts;
+  a.n_slots = pool->n_slots;
+  a.clock = pool->clock;
+  a.idx = idx;
+  a.slot_expert = pool->slot_expert;
+  a.slot_stamp = pool->slot_stamp;
+  a.idx_slot = idx_slot;
+  a.counters = counters;
+  a.plan = (int32_t*)workspace;
+  return from_hip(launch_pool_stream_in((hipStream_t)stream, a, *src, *pool_experts));
+}
+
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,
                               int32_t* offsets, int32_t* perm) {
   if (T < 1 || K < 1 || E < 1 || E > MOE_MAX_E || (int64_t)T * K > (1 << 24)) return MOE_ERR_INVALID_ARG;

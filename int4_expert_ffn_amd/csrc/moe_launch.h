@@ -82,6 +82,20 @@ size_t decode_step_workspace(const moe_decode_stack& st);
 hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
                               const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws);
 
+// expert streaming into an HBM pool --------------------------------------------------------------
+struct PoolArgs {
+  int K, E, n_slots;
+  const int32_t* idx;      // [K] selected experts
+  int32_t* slot_expert;    // [n_slots] pool state
+  int32_t* slot_stamp;     // [n_slots]
+  int32_t* clock;          // [1] calls so far (the stamp of this call)
+  int32_t* idx_slot;       // [K] out
+  int32_t* counters;       // [2] hits, misses (accumulated) or nullptr
+  int32_t* plan;           // workspace: copy count, then (slot, expert) pairs
+};
+hipError_t launch_pool_stream_in(hipStream_t s, const PoolArgs& a, const moe_experts& src, const moe_experts& pool);
+size_t pool_plan_bytes(int K);
+
 // combine -------------------------------------------------------------------------------------
 hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const uint16_t* gain, uint16_t* x);
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -108,6 +108,36 @@ def test_sparse_ffn_rejects():
     al = lambda v: (v + 255) // 256 * 256
     want = al(4 * 512 * 4) + al(4 * 2048 * 4) + al(32 * 4)
     assert L.moe_expert_ffn_sparse_workspace_size(1, 4, ctypes.byref(ex)) == want
+
+
+def test_stream_in_rejects():
+    src = _ex(E=256, d=2048, I=512, group=64)
+    pool_ex = _ex(E=8, d=2048, I=512, group=64)
+    pool = lib_mod.moe_pool(8, FAKE, FAKE, FAKE)
+    ws = L.moe_stream_workspace_size(4)
+    assert ws == 256 and L.moe_stream_workspace_size(0) == 0 and L.moe_stream_workspace_size(17) == 0
+
+    def si(K=4, src=src, pex=pool_ex, pool=pool, idx=FAKE, out=FAKE, w=FAKE, wsb=ws):
+        st = L.moe_stream_in(None, K, idx, ctypes.byref(src), ctypes.byref(pex), ctypes.byref(pool), out,
+                             None, w, wsb)
+        assert st in (INVALID, UNSUP), "a call with fake pointers must never pass validation"
+        return st
+
+    assert si(K=0) == INVALID
+    assert si(K=17) == INVALID
+    assert si(pool=lib_mod.moe_pool(8, FAKE, FAKE, None)) == INVALID    # no clock
+    assert si(idx=None) == INVALID
+    assert si(out=None) == INVALID
+    assert si(w=None) == INVALID
+    assert si(wsb=8) == INVALID                                     # workspace too small
+    assert si(w=FAKE + 8) == INVALID                                # misaligned workspace
+    assert si(K=9) == INVALID                                       # K above n_slots
+    assert si(pool=lib_mod.moe_pool(4097, FAKE, FAKE, FAKE)) == INVALID   # above MOE_POOL_MAX_SLOTS
+    assert si(pool=lib_mod.moe_pool(8, None, FAKE, FAKE)) == INVALID
+    assert si(pex=_ex(E=9, d=2048, I=512, group=64)) == INVALID     # pool descriptor of another size
+    assert si(pex=_ex(E=8, d=2048, I=512, group=32)) == INVALID     # shapes differ
+    assert si(src=_ex(E=256, d=2048, I=512, group=64, q=FAKE + 4), pex=pool_ex) == INVALID  # misaligned codes
+    assert si(src=_ex(E=256, d=2048, I=512, bits=3, group=64), pex=_ex(E=8, d=2048, I=512, bits=3, group=64)) == UNSUP
 
 
 def test_prerouter_and_combine_reject():
