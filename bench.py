@@ -388,31 +388,24 @@ def bench_batched(args, cfg, torch, M, S, dev):
                        "sh": sh, "lora": M.Lora3([lw[m] for m in S.MATS], cfg.lora_alpha),
                        "router": syn.router(0, dev)})
     torch.cuda.synchronize()
+    from int4_expert_ffn_amd.batched import BatchedLayer
     syn = S.Synth(cfg)
     n_in = 8
     hs = syn.hidden(11, n_in * T, dev).view(n_in, T, d)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K), dtype=torch.float32, device=dev)
-    o = torch.empty((T, K, d), dtype=torch.float32, device=dev)
-    sho = torch.empty((T, 1, d), dtype=torch.float32, device=dev)
-    zeros = torch.zeros((T, 1), dtype=torch.int32, device=dev)
     y = torch.empty((T, d), dtype=torch.float16, device=dev)
-    ws = torch.empty(max(M.moe_expert_ffn_workspace_size(T, K, copies[0]["ex"]),
-                         M.moe_expert_ffn_workspace_size(T, 1, copies[0]["sh"])), dtype=torch.uint8, device=dev)
+    for cp in copies:      # the shared expert runs on a second stream beside the routed ones
+        cp["layer"] = BatchedLayer(cp["ex"], cp["router"], T, K, dev, shared=cp["sh"], lora3=cp["lora"],
+                                   two_streams=not args.one_stream)
 
     def layer(cp, h):
-        M.moe_route_topk(T, d, E, K, M.MOE_TOPK_RENORM, h, cp["router"], logits, idx, w)
-        M.moe_expert_ffn_q4(T, K, 0, h, idx, cp["ex"], None, o, None, None, None, ws)
-        M.moe_expert_ffn_q4(T, 1, 0, h, zeros, cp["sh"], cp["lora"], sho, None, None, None, ws)
-        M.moe_combine(T, K, d, o, w, h, sho.view(T, d), y)
+        cp["layer"](h, y)
 
     # experts each (copy, input) pair touches, for the algorithmic bytes
     used = []
     for c, cp in enumerate(copies):
         for i in range(n_in):
             layer(cp, hs[i])
-            used.append(int(torch.unique(idx).numel()))
+            used.append(int(torch.unique(cp["layer"].idx).numel()))
     torch.cuda.synchronize()
     stream = torch.cuda.Stream(device=dev)
     graphs = []
@@ -447,7 +440,8 @@ def bench_batched(args, cfg, torch, M, S, dev):
     nbytes = int(round(mean_used * eb + eb + E * d * 2 + lora_b + 2 * T * d * 2))
     rec = base_record(args, cfg, steps * T / wall, wall, steps)
     rec["roofline"] = roofline("the batched layer: router GEMM + top-K, sort, grouped MFMA gate/up and down, "
-                               "shared expert + LoRA, combine (one graph per batch)", nbytes, us, None)
+                               "shared expert + LoRA (on a second stream), combine (one graph per batch)", nbytes, us,
+                               None)
     rec["roofline"]["used_experts_mean"] = round(mean_used, 2)
     rec["batch_us"] = round(us, 2)
     if not args.no_cpu_baseline:
@@ -751,6 +745,7 @@ def main():
                          "relu-sparse (decode35b shapes, ReLU activation-sparse experts, per-layer calls), "
                          "stream (decode35b with every expert in pinned host memory, HBM pools)")
     ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
+    ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")

@@ -233,3 +233,41 @@ def test_batched_layer_end_to_end(M):
     y_ref = O.combine(o_ref, rw, x, sh_ref)
     assert_rows_close(o.cpu().numpy().reshape(T * K, d), o_ref.reshape(T * K, d), what="routed o")
     assert_rows_close(y.cpu().numpy(), y_ref, what="layer y")
+
+
+def test_batched_layer_two_streams(M):
+    """The packaged batched layer (shared expert on a second stream) equals the same calls issued on
+    one stream, bit for bit, eagerly and as graph replays with eager work in between."""
+    from int4_expert_ffn_amd.batched import BatchedLayer
+    cfg = S.CONFIGS["batched"]
+    syn = S.Synth(cfg)
+    T, K, d = cfg.T, cfg.K, cfg.d
+    ex = device_layer(syn, 0, DEV)
+    sh_ex, _, lora, _, _ = _shared(M, cfg, syn)
+    router = syn.router(0, DEV)
+    two = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=True)
+    one = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=False)
+    hs = syn.hidden(77, 4 * T).to(DEV).view(4, T, d)
+    y1 = torch.empty((T, d), dtype=torch.float16, device=DEV)
+    y2 = torch.empty_like(y1)
+    cs = torch.cuda.Stream()
+    h_in = hs[0].clone()
+    with torch.cuda.stream(cs):
+        two(h_in, y2)
+    cs.synchronize()
+    one(hs[0], y1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        two(h_in, y2)
+    torch.cuda.synchronize()
+    for i in range(4):
+        h_in.copy_(hs[i])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cs):
+            g.replay()
+        cs.synchronize()
+        one(hs[i], y1)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"replay {i}"
