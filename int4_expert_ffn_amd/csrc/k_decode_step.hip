@@ -295,8 +295,9 @@ struct ABuf {  // gate/up row pairs, head linear/fc1 rows (+ K-hot terms, biases
   int item[GU];
   bool bad[GU];
   bool ok[GU];               // false: a repeat of the last item, not stored
-  uint4 hr[NH][NSH];
-  uint16_t kh[NH], hb[NH];  // raw float16: converted where used, so the loads stay in flight
+  // head rows (none in a variant for stacks without heads, NH = 0: the head code folds away)
+  uint4 hr[NH > 0 ? NH : 1][NSH];
+  uint16_t kh[NH > 0 ? NH : 1], hb[NH > 0 ? NH : 1];  // raw float16: converted where used, so the loads stay in flight
   int khm;                  // K-hot term of this lane: 0 none, 1 the table value, 2 NaN (bad index)
   uint4 fr[NSF];            // fc2 row of the previous layer's head
   uint16_t fb;
@@ -366,7 +367,7 @@ __device__ __forceinline__ void issue_A_head(const StepParams& p, int l, const i
                                              bool fc2_of_prev, int wg, int cw, int lane,
                                              ABuf<BITS, PG, NSH, NSF, GU, NH>& a) {
   const layer_cptr D = layer_at(p, l);
-  if (has_head(p, l)) {
+  if (NH > 0 && has_head(p, l)) {
     // K-hot gather: lane j < K reads row cur[j] of the routing table, lane K <= j < 2K row
     // E + prev[j - K] (none at the first token); other lanes re-read row cur[0] and add 0.
     const int j = lane < 2 * p.K ? lane : 0;
@@ -703,8 +704,8 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         }
       }
       // first half of this layer's head: fc1 rows (+GELU, sent) and the linear row (kept)
-      if (head && head_row(p, 0, wg, cw) < p.H + p.E) {  // uniform over the wave
-        float red[2 * NH];
+      if (NH > 0 && head && head_row(p, 0, wg, cw) < p.H + p.E) {  // uniform over the wave
+        float red[2 * (NH > 0 ? NH : 1)];
 #pragma unroll
         for (int r = 0; r < NH; ++r) {
           red[2 * r] = 0.f;
@@ -914,7 +915,6 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
     pl.NSF = 1;
     pl.NH = 0;
   }
-  pl.NH = pl.NH < 1 ? 1 : pl.NH;  // a variant holds at least one head-row slot (unused without heads)
   pl.ok = has_variant(bits, pl.PG, pl.NSH, pl.NSF, pl.GU, pl.PD, pl.NH);
   return pl;
 }
@@ -958,9 +958,9 @@ static hipError_t go(hipStream_t s, const StepParams& p) {
 // are exact, so every compute wave issues the same loads.
 #define MOE_STEP_VARIANTS(X)                                                                       \
   X(4, 1, 4, 2, 1, 1, 1) /* d 2048, I 512, K 4, E 256, head hidden 1024 */                         \
-  X(4, 1, 4, 1, 2, 2, 1) /* d 2048, I 512, K 8, E 256, no heads */                                 \
-  X(4, 2, 8, 1, 2, 4, 1) /* d 4096, I 1024, K 4, E 512, int4, no heads */                          \
-  X(2, 1, 8, 1, 2, 2, 1) /* d 4096, I 1024, K 4, E 512, int2, no heads */
+  X(4, 1, 4, 1, 2, 2, 0) /* d 2048, I 512, K 8, E 256, no heads */                                 \
+  X(4, 2, 8, 1, 2, 4, 0) /* d 4096, I 1024, K 4, E 512, int4, no heads */                          \
+  X(2, 1, 8, 1, 2, 2, 0) /* d 4096, I 1024, K 4, E 512, int2, no heads */
 
 static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD, int NH) {
 #define MOE_STEP_HAS(B_, PG_, NSH_, NSF_, GU_, PD_, NH_) \
