@@ -72,6 +72,7 @@ typedef enum {
 #define MOE_MAX_K 16
 #define MOE_MAX_D 8192
 #define MOE_POOL_MAX_SLOTS 4096
+#define MOE_POOL_MAX_JOBS 8
 
 typedef struct {
   const uint32_t* q;
@@ -217,6 +218,22 @@ size_t moe_stream_workspace_size(int32_t K);
 moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_experts* src,
                          const moe_experts* pool_experts, const moe_pool* pool, int32_t* idx_slot,
                          int32_t* counters, void* workspace, size_t workspace_bytes);
+
+/* Several moe_stream_in calls in two launches: up to MOE_POOL_MAX_JOBS pools (one layer's each, say)
+   of one shape (equal d_model, d_ff, bits, group), placed one wave per pool and copied by one grid.
+   Each job is checked as moe_stream_in checks its arguments; the pools of one call must be distinct.
+   workspace: n * moe_stream_workspace_size(K) bytes, 256-byte aligned.  Results equal n separate
+   moe_stream_in calls. */
+typedef struct {
+  const int32_t* idx;               /* [K] selected experts (device) */
+  const moe_experts* src;           /* E experts: pinned host or device memory */
+  const moe_experts* pool_experts;  /* the pool's n_slots experts (HBM) */
+  const moe_pool* pool;             /* the pool's state */
+  int32_t* idx_slot;                /* [K] out: slot of each selected expert */
+  int32_t* counters;                /* [2] hits, copies (added) or NULL */
+} moe_stream_job;
+moe_status moe_stream_in_many(void* stream, int32_t n, int32_t K, const moe_stream_job* jobs, void* workspace,
+                              size_t workspace_bytes);
 
 /* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
    (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose

@@ -26,6 +26,7 @@ EXPORTS = (
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
+    "moe_stream_in_many",
 )
 
 
@@ -66,6 +67,11 @@ class moe_pool(ctypes.Structure):
                 ("clock", ctypes.c_void_p)]
 
 
+class moe_stream_job(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("src", ctypes.POINTER(moe_experts)), ("pool_experts", ctypes.POINTER(moe_experts)),
+                ("pool", ctypes.POINTER(moe_pool)), ("idx_slot", ctypes.c_void_p), ("counters", ctypes.c_void_p)]
+
+
 class moe_decode_stack(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
@@ -95,6 +101,7 @@ def _load():
         "moe_stream_workspace_size": (sz, [i32]),
         "moe_stream_in": (st, [vp, i32, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_experts),
                                ctypes.POINTER(moe_pool), vp, vp, vp, sz]),
+        "moe_stream_in_many": (st, [vp, i32, i32, ctypes.POINTER(moe_stream_job), vp, sz]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -327,6 +334,25 @@ def moe_stream_in(K, idx, src: Experts, pool: Pool, idx_slot, counters, workspac
                             ctypes.byref(pool.experts.desc), ctypes.byref(pool.desc), _ptr(idx_slot, _i32(), "idx_slot"),
                             _ptr(counters, _i32(), "counters"), _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_stream_in")
+
+
+MOE_POOL_MAX_JOBS = 8
+
+
+def moe_stream_in_many(K, jobs, workspace, workspace_bytes=None, stream=None):
+    """jobs: sequence of (idx, src Experts, Pool, idx_slot, counters or None), at most MOE_POOL_MAX_JOBS,
+    distinct pools of one shape; workspace of len(jobs) * moe_stream_workspace_size(K) bytes."""
+    n = len(jobs)
+    arr = (moe_stream_job * max(1, n))()
+    for i, (idx, src, pool, idx_slot, counters) in enumerate(jobs):
+        arr[i] = moe_stream_job(_ptr(idx, _i32(), "idx"), ctypes.pointer(src.desc), ctypes.pointer(pool.experts.desc),
+                                ctypes.pointer(pool.desc), _ptr(idx_slot, _i32(), "idx_slot"),
+                                _ptr(counters, _i32(), "counters"))
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    first = jobs[0] if n else (None,) * 5
+    st = _lib.moe_stream_in_many(_stream(stream, first[0], first[3]), n, K, arr, _ptr(workspace, None, "workspace"),
+                                 nbytes)
+    _check(st, "moe_stream_in_many")
 
 
 def moe_combine(T, K, d, o, w, r, shared, y, stream=None):

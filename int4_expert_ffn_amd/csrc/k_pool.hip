@@ -38,7 +38,11 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
   return v;
 }
 
-__global__ void __launch_bounds__(WAVE) k_pool_plan(PoolArgs a) {
+__device__ __forceinline__ void pool_plan(const PoolArgs& a);
+
+__global__ void __launch_bounds__(WAVE) k_pool_plan(PoolJobs jobs) { pool_plan(jobs.job[blockIdx.x]); }
+
+__device__ __forceinline__ void pool_plan(const PoolArgs& a) {
   __shared__ int s_exp[MOE_POOL_MAX_SLOTS];
   __shared__ int s_stamp[MOE_POOL_MAX_SLOTS];
   __shared__ int s_slot[MOE_MAX_K];
@@ -109,47 +113,57 @@ __global__ void __launch_bounds__(WAVE) k_pool_plan(PoolArgs a) {
   }
 }
 
-// one of the nine per-expert arrays: bytes per expert, source and pool bases, and the first work
-// unit (chunk) of the array in the per-expert chunk list
+// one of the nine per-expert arrays of a job: bytes per expert, source and pool bases, and the first
+// work unit (chunk) of the array in the per-expert chunk list
 struct CopyArr {
   const unsigned char* src;
   unsigned char* dst;
-  size_t bytes;   // per expert
-  int chunk0;     // chunks of the arrays before this one
 };
-struct CopyArgs {
-  CopyArr arr[9];
-  int chunks;     // chunks per expert, all nine arrays
-  const int32_t* plan;
+struct CopyJobs {
+  CopyArr arr[MOE_POOL_MAX_JOBS][9];
+  const int32_t* plan[MOE_POOL_MAX_JOBS];
+  size_t bytes[9];   // per expert, the same for every job
+  int chunk0[9];     // chunks of the arrays before this one
+  int chunks;        // chunks per expert, all nine arrays
+  int n;             // jobs
 };
 
-// A small grid that walks (copy, array, chunk) units: the copy reads host memory at the host link's
-// pace whatever the grid size, and a few resident blocks leave the other CUs to the kernels that
-// run beside it (a grid of thousands of short blocks kept them waiting for the dispatcher).
-__global__ void __launch_bounds__(COPY_THREADS) k_pool_copy(CopyArgs c) {
-  const int n_units = c.plan[0] * c.chunks;
+// A small grid that walks (job, copy, array, chunk) units: the copy reads host memory at the host
+// link's pace whatever the grid size, and a few resident blocks leave the other CUs to the kernels
+// that run beside it (a grid of thousands of short blocks kept them waiting for the dispatcher).
+__global__ void __launch_bounds__(COPY_THREADS) k_pool_copy(CopyJobs c) {
+  int first[MOE_POOL_MAX_JOBS + 1];   // first unit of each job
+  first[0] = 0;
+#pragma unroll
+  for (int j = 0; j < MOE_POOL_MAX_JOBS; ++j) first[j + 1] = first[j] + (j < c.n ? c.plan[j][0] * c.chunks : 0);
+  const int n_units = first[MOE_POOL_MAX_JOBS];
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int m = u / c.chunks, cu = u - m * c.chunks;
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < MOE_POOL_MAX_JOBS; ++i) j += u >= first[i];
+    const int v = u - first[j];
+    const int m = v / c.chunks, cu = v - m * c.chunks;
     int a = 0;
 #pragma unroll
-    for (int j = 1; j < 9; ++j) a += cu >= c.arr[j].chunk0;
-    const CopyArr& A = c.arr[a];
-    const size_t begin = (size_t)(cu - A.chunk0) * COPY_CHUNK;
-    const int slot = c.plan[1 + 2 * m], e = c.plan[2 + 2 * m];
-    const unsigned char* src = A.src + (size_t)e * A.bytes;
-    unsigned char* dst = A.dst + (size_t)slot * A.bytes;
-    const size_t end = min(A.bytes, begin + (size_t)COPY_CHUNK);
-    if ((A.bytes & 15) == 0 && (((uintptr_t)A.src | (uintptr_t)A.dst) & 15) == 0) {
-      uint4 v[COPY_UNITS];
+    for (int i = 1; i < 9; ++i) a += cu >= c.chunk0[i];
+    const CopyArr& A = c.arr[j][a];
+    const size_t bytes = c.bytes[a];
+    const size_t begin = (size_t)(cu - c.chunk0[a]) * COPY_CHUNK;
+    const int slot = c.plan[j][1 + 2 * m], e = c.plan[j][2 + 2 * m];
+    const unsigned char* src = A.src + (size_t)e * bytes;
+    unsigned char* dst = A.dst + (size_t)slot * bytes;
+    const size_t end = min(bytes, begin + (size_t)COPY_CHUNK);
+    if ((bytes & 15) == 0 && (((uintptr_t)A.src | (uintptr_t)A.dst) & 15) == 0) {
+      uint4 v4[COPY_UNITS];
 #pragma unroll
       for (int i = 0; i < COPY_UNITS; ++i) {
         const size_t o = begin + ((size_t)i * COPY_THREADS + threadIdx.x) * 16;
-        if (o < end) v[i] = *reinterpret_cast<const uint4*>(src + o);
+        if (o < end) v4[i] = *reinterpret_cast<const uint4*>(src + o);
       }
 #pragma unroll
       for (int i = 0; i < COPY_UNITS; ++i) {
         const size_t o = begin + ((size_t)i * COPY_THREADS + threadIdx.x) * 16;
-        if (o < end) *reinterpret_cast<uint4*>(dst + o) = v[i];
+        if (o < end) *reinterpret_cast<uint4*>(dst + o) = v4[i];
       }
     } else {   // 2-byte units (every array holds whole float16 or uint32 elements)
       for (size_t o = begin + (size_t)threadIdx.x * 2; o < end; o += (size_t)COPY_THREADS * 2)
@@ -160,29 +174,40 @@ __global__ void __launch_bounds__(COPY_THREADS) k_pool_copy(CopyArgs c) {
 
 }  // namespace
 
-hipError_t launch_pool_stream_in(hipStream_t s, const PoolArgs& a, const moe_experts& src, const moe_experts& pool) {
-  hipError_t err = launch(k_pool_plan, dim3(1), dim3(WAVE), 0, s, a);
+hipError_t launch_pool_stream_in(hipStream_t s, int n, const PoolArgs* jobs, const moe_experts* const* src,
+                                 const moe_experts* const* pool) {
+  PoolJobs pj{};
+  for (int j = 0; j < n; ++j) pj.job[j] = jobs[j];
+  hipError_t err = launch(k_pool_plan, dim3(n), dim3(WAVE), 0, s, pj);
   if (err != hipSuccess) return err;
-  const size_t d = src.d_model, I = src.d_ff, bits = src.bits, g = src.group;
+  const moe_experts& s0 = *src[0];
+  const size_t d = s0.d_model, I = s0.d_ff, bits = s0.bits, g = s0.group;
   const size_t qb = I * d * bits / 8;                  // codes of one matrix of one expert
   const size_t gu_sb = I * (d / g) * 2;                // gate / up scales (or biases) of one expert
   const size_t dn_sb = d * I / g * 2;                  // down scales (or biases): the same count either layout
-  CopyArgs c{};
-  const moe_qmat* sm[3] = {&src.gate, &src.up, &src.down};
-  const moe_qmat* pm[3] = {&pool.gate, &pool.up, &pool.down};
+  CopyJobs c{};
   int chunk0 = 0;
   for (int m = 0; m < 3; ++m) {
     const size_t sb = m < 2 ? gu_sb : dn_sb;
-    const void* s3[3] = {sm[m]->q, sm[m]->scales, sm[m]->biases};
-    void* d3[3] = {(void*)pm[m]->q, (void*)pm[m]->scales, (void*)pm[m]->biases};
     const size_t b3[3] = {qb, sb, sb};
-    for (int j = 0; j < 3; ++j) {
-      c.arr[3 * m + j] = CopyArr{(const unsigned char*)s3[j], (unsigned char*)d3[j], b3[j], chunk0};
-      chunk0 += (int)((b3[j] + COPY_CHUNK - 1) / COPY_CHUNK);
+    for (int i = 0; i < 3; ++i) {
+      c.bytes[3 * m + i] = b3[i];
+      c.chunk0[3 * m + i] = chunk0;
+      chunk0 += (int)((b3[i] + COPY_CHUNK - 1) / COPY_CHUNK);
     }
   }
   c.chunks = chunk0;
-  c.plan = a.plan;
+  c.n = n;
+  for (int j = 0; j < n; ++j) {
+    const moe_qmat* sm[3] = {&src[j]->gate, &src[j]->up, &src[j]->down};
+    const moe_qmat* pm[3] = {&pool[j]->gate, &pool[j]->up, &pool[j]->down};
+    for (int m = 0; m < 3; ++m) {
+      c.arr[j][3 * m] = CopyArr{(const unsigned char*)sm[m]->q, (unsigned char*)pm[m]->q};
+      c.arr[j][3 * m + 1] = CopyArr{(const unsigned char*)sm[m]->scales, (unsigned char*)pm[m]->scales};
+      c.arr[j][3 * m + 2] = CopyArr{(const unsigned char*)sm[m]->biases, (unsigned char*)pm[m]->biases};
+    }
+    c.plan[j] = jobs[j].plan;
+  }
   return launch(k_pool_copy, dim3(COPY_BLOCKS), dim3(COPY_THREADS), 0, s, c);
 }
 

@@ -252,17 +252,20 @@ size_t moe_stream_workspace_size(int32_t K) {
   return align_up(pool_plan_bytes(K));
 }
 
-moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_experts* src,
-                         const moe_experts* pool_experts, const moe_pool* pool, int32_t* idx_slot, int32_t* counters,
-                         void* workspace, size_t workspace_bytes) {
-  if (!src || !pool_experts || !pool || !idx || !idx_slot || !workspace) return MOE_ERR_INVALID_ARG;
-  if (K < 1 || K > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+static moe_status check_stream_job(int32_t K, const moe_stream_job& j, const moe_experts* shape) {
+  const moe_experts* src = j.src;
+  const moe_experts* pool_experts = j.pool_experts;
+  const moe_pool* pool = j.pool;
+  if (!src || !pool_experts || !pool || !j.idx || !j.idx_slot) return MOE_ERR_INVALID_ARG;
   if (!pool->slot_expert || !pool->slot_stamp || !pool->clock) return MOE_ERR_INVALID_ARG;
   if (pool->n_slots < K || pool->n_slots > MOE_POOL_MAX_SLOTS || pool_experts->n_experts != pool->n_slots)
     return MOE_ERR_INVALID_ARG;
   if (src->n_experts < 1 || src->n_experts > (1 << 20)) return MOE_ERR_INVALID_ARG;
   if (src->d_model != pool_experts->d_model || src->d_ff != pool_experts->d_ff || src->bits != pool_experts->bits ||
       src->group != pool_experts->group)
+    return MOE_ERR_INVALID_ARG;
+  if (src->d_model != shape->d_model || src->d_ff != shape->d_ff || src->bits != shape->bits ||
+      src->group != shape->group)
     return MOE_ERR_INVALID_ARG;
   if (src->bits != 4 && src->bits != 2) return MOE_ERR_UNSUPPORTED;
   if (src->group != 32 && src->group != 64 && src->group != 128) return MOE_ERR_UNSUPPORTED;
@@ -273,19 +276,47 @@ moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_
     moe_status st = check_qmat(*m);
     if (st != MOE_OK) return st;
   }
-  if (!aligned16(workspace) || workspace_bytes < moe_stream_workspace_size(K)) return MOE_ERR_INVALID_ARG;
-  PoolArgs a{};
-  a.K = K;
-  a.E = src->n_experts;
-  a.n_slots = pool->n_slots;
-  a.clock = pool->clock;
-  a.idx = idx;
-  a.slot_expert = pool->slot_expert;
-  a.slot_stamp = pool->slot_stamp;
-  a.idx_slot = idx_slot;
-  a.counters = counters;
-  a.plan = (int32_t*)workspace;
-  return from_hip(launch_pool_stream_in((hipStream_t)stream, a, *src, *pool_experts));
+  return MOE_OK;
+}
+
+moe_status moe_stream_in_many(void* stream, int32_t n, int32_t K, const moe_stream_job* jobs, void* workspace,
+                              size_t workspace_bytes) {
+  if (n < 1 || n > MOE_POOL_MAX_JOBS || !jobs || !workspace) return MOE_ERR_INVALID_ARG;
+  if (K < 1 || K > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  if (!jobs[0].src) return MOE_ERR_INVALID_ARG;
+  const size_t per = moe_stream_workspace_size(K);
+  if (!aligned16(workspace) || workspace_bytes < per * (size_t)n) return MOE_ERR_INVALID_ARG;
+  PoolArgs a[MOE_POOL_MAX_JOBS];
+  const moe_experts* src[MOE_POOL_MAX_JOBS];
+  const moe_experts* pex[MOE_POOL_MAX_JOBS];
+  for (int j = 0; j < n; ++j) {
+    moe_status st = check_stream_job(K, jobs[j], jobs[0].src);
+    if (st != MOE_OK) return st;
+    for (int i = 0; i < j; ++i)
+      if (jobs[i].pool->slot_expert == jobs[j].pool->slot_expert) return MOE_ERR_INVALID_ARG;  // one pool twice
+    a[j] = PoolArgs{};
+    a[j].K = K;
+    a[j].E = jobs[j].src->n_experts;
+    a[j].n_slots = jobs[j].pool->n_slots;
+    a[j].idx = jobs[j].idx;
+    a[j].slot_expert = jobs[j].pool->slot_expert;
+    a[j].slot_stamp = jobs[j].pool->slot_stamp;
+    a[j].clock = jobs[j].pool->clock;
+    a[j].idx_slot = jobs[j].idx_slot;
+    a[j].counters = jobs[j].counters;
+    a[j].plan = (int32_t*)((char*)workspace + per * j);
+    src[j] = jobs[j].src;
+    pex[j] = jobs[j].pool_experts;
+  }
+  return from_hip(launch_pool_stream_in((hipStream_t)stream, n, a, src, pex));
+}
+
+moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_experts* src,
+                         const moe_experts* pool_experts, const moe_pool* pool, int32_t* idx_slot, int32_t* counters,
+                         void* workspace, size_t workspace_bytes) {
+  if (!src) return MOE_ERR_INVALID_ARG;
+  const moe_stream_job j{idx, src, pool_experts, pool, idx_slot, counters};
+  return moe_stream_in_many(stream, 1, K, &j, workspace, workspace_bytes);
 }
 
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,

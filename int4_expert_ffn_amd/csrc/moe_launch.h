@@ -93,7 +93,12 @@ struct PoolArgs {
   int32_t* counters;       // [2] hits, misses (accumulated) or nullptr
   int32_t* plan;           // workspace: copy count, then (slot, expert) pairs
 };
-hipError_t launch_pool_stream_in(hipStream_t s, const PoolArgs& a, const moe_experts& src, const moe_experts& pool);
+struct PoolJobs {
+  PoolArgs job[MOE_POOL_MAX_JOBS];
+};
+// n <= MOE_POOL_MAX_JOBS pools of one shape: placement (one wave per pool), then one copy grid for all
+hipError_t launch_pool_stream_in(hipStream_t s, int n, const PoolArgs* jobs, const moe_experts* const* src,
+                                 const moe_experts* const* pool);
 size_t pool_plan_bytes(int K);
 
 // combine -------------------------------------------------------------------------------------

@@ -49,13 +49,13 @@ class StreamedStack(DecodeStack):
         self.pools = [L.Pool(lw.experts, n_slots, dev) for lw in layers]
         self.idx_slot = torch.full((3, self.L, K), -1, dtype=torch.int32, device=dev)
         self.counters = torch.zeros((self.L, 2), dtype=torch.int32, device=dev)      # hits, misses
-        nb = L.moe_stream_workspace_size(K)
-        self.plan_ws = torch.empty((self.L, (nb + 255) // 256 * 256), dtype=torch.uint8, device=dev)
+        self._nb = (L.moe_stream_workspace_size(K) + 255) // 256 * 256
+        self.plan_ws = torch.empty((self.L, self._nb), dtype=torch.uint8, device=dev)   # one plan per layer
         # layers take turns on a few copy streams, so one layer's placement and launch overlap another
         # layer's copy and the host link stays busy
         self.copy_streams = [torch.cuda.Stream(device=dev) for _ in range(max(1, copy_streams))]
         self.kick = [torch.cuda.Event() for _ in range(self.L)]      # predictions so far ready
-        self.fork_every = max(1, fork_every)
+        self.fork_every = max(1, min(fork_every, L.MOE_POOL_MAX_JOBS))
         self._ffn_ws = torch.empty(max(L.moe_expert_ffn_workspace_size(1, K, p.experts) for p in self.pools),
                                    dtype=torch.uint8, device=dev)
 
@@ -73,14 +73,22 @@ class StreamedStack(DecodeStack):
     def _prefetch(self, ls: List[int], t: int, n: int):
         """Stream the predicted experts of layers `ls` for token t in on copy stream n % count, after
         the compute stream's work so far (the predictions, and any stream-in of those layers already
-        enqueued).  One fork serves several layers: each cross-stream dependency costs more than a
-        launch."""
+        enqueued).  One fork and one moe_stream_in_many call serve several layers: each cross-stream
+        dependency, and each launch, costs more than the placement of a few experts."""
         cs = torch.cuda.current_stream(self.device)
         st = self.copy_streams[n % len(self.copy_streams)]
         self.kick[n].record(cs)
         st.wait_event(self.kick[n])
-        for l in ls:
-            self._stream_in(l, t, stream=st)
+        s = t % 3
+        for i in range(0, len(ls), L.MOE_POOL_MAX_JOBS):   # the layers' plans are consecutive in plan_ws
+            part = ls[i:i + L.MOE_POOL_MAX_JOBS]
+            if part == list(range(part[0], part[0] + len(part))):
+                jobs = [(self.route_idx[s, l], self.layers[l].experts, self.pools[l], self.idx_slot[s, l],
+                         self.counters[l]) for l in part]
+                L.moe_stream_in_many(self.K, jobs, self.plan_ws[part[0]:part[0] + len(part)], stream=st)
+            else:
+                for l in part:
+                    self._stream_in(l, t, stream=st)
 
     def token(self, t: int, h_in=None, record_routing: bool = False):
         if h_in is not None:

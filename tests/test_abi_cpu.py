@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -138,6 +138,34 @@ def test_stream_in_rejects():
     assert si(pex=_ex(E=8, d=2048, I=512, group=32)) == INVALID     # shapes differ
     assert si(src=_ex(E=256, d=2048, I=512, group=64, q=FAKE + 4), pex=pool_ex) == INVALID  # misaligned codes
     assert si(src=_ex(E=256, d=2048, I=512, bits=3, group=64), pex=_ex(E=8, d=2048, I=512, bits=3, group=64)) == UNSUP
+
+
+def test_stream_in_many_rejects():
+    src = _ex(E=256, d=2048, I=512, group=64)
+    pex = _ex(E=8, d=2048, I=512, group=64)
+    pools = [lib_mod.moe_pool(8, FAKE + 256 * i, FAKE, FAKE) for i in range(10)]
+    J = lib_mod.moe_stream_job
+
+    def jobs(n, same_pool=False, other=None):
+        arr = (J * max(1, n))()
+        for i in range(n):
+            s = other if (other is not None and i == n - 1) else src
+            arr[i] = J(FAKE, ctypes.pointer(s), ctypes.pointer(pex), ctypes.pointer(pools[0 if same_pool else i]),
+                       FAKE, None)
+        return arr
+
+    def many(n, arr, wsb=1 << 20, ws=FAKE):
+        st = L.moe_stream_in_many(None, n, 4, arr, ws, wsb)
+        assert st in (INVALID, UNSUP), "a call with fake pointers must never pass validation"
+        return st
+
+    assert many(0, jobs(1)) == INVALID
+    assert many(9, jobs(9)) == INVALID                          # above MOE_POOL_MAX_JOBS
+    assert many(3, jobs(3), wsb=512) == INVALID                 # workspace for 2 jobs only
+    assert many(2, jobs(2, same_pool=True)) == INVALID          # one pool twice
+    other = _ex(E=256, d=2048, I=1024, group=64)
+    assert many(2, jobs(2, other=other)) == INVALID             # jobs of different shapes
+    assert L.moe_stream_in_many(None, 1, 4, None, FAKE, 1 << 20) == INVALID
 
 
 def test_prerouter_and_combine_reject():

@@ -233,3 +233,33 @@ def test_streamed_stack_graph_replays(M):
         assert stm.pools[l].slot_stamp.cpu().tolist() == st.stamp, f"layer {l}"
         assert int(stm.pools[l].clock.item()) == len(calls)
     del graphs
+
+
+def test_stream_in_many_equals_separate_calls(M):
+    """moe_stream_in_many over several pools gives the pools, slots and counts of separate calls."""
+    cfg = S.CONFIGS["tiny"]
+    syn = S.Synth(cfg)
+    srcs = [experts_of(M, cfg, S.fill_experts(syn, l, DEV)) for l in range(3)]
+    K = 2
+    a = [M.Pool(s_, 5, DEV) for s_ in srcs]
+    b = [M.Pool(s_, 5, DEV) for s_ in srcs]
+    ca, cb = torch.zeros((3, 2), dtype=torch.int32, device=DEV), torch.zeros((3, 2), dtype=torch.int32, device=DEV)
+    sa, sb = torch.empty((3, K), dtype=torch.int32, device=DEV), torch.empty((3, K), dtype=torch.int32, device=DEV)
+    ws1 = torch.empty(M.moe_stream_workspace_size(K), dtype=torch.uint8, device=DEV)
+    wsn = torch.empty(3 * M.moe_stream_workspace_size(K), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(5)
+    for t in range(40):
+        sel = torch.tensor(np.stack([rng.choice(8, size=K, replace=False) for _ in range(3)]), dtype=torch.int32,
+                           device=DEV)
+        for l in range(3):
+            M.moe_stream_in(K, sel[l], srcs[l], a[l], sa[l], ca[l], ws1)
+        M.moe_stream_in_many(K, [(sel[l], srcs[l], b[l], sb[l], cb[l]) for l in range(3)], wsn)
+        torch.cuda.synchronize()
+        assert torch.equal(sa, sb), f"token {t}"
+    assert torch.equal(ca, cb)
+    for l in range(3):
+        assert torch.equal(a[l].slot_expert, b[l].slot_expert) and torch.equal(a[l].slot_stamp, b[l].slot_stamp)
+        for ma, mb in zip(a[l].experts.tensors, b[l].experts.tensors):
+            for xa, xb in zip(ma, mb):
+                occupied = a[l].slot_expert >= 0
+                assert torch.equal(xa[occupied], xb[occupied])
