@@ -604,7 +604,8 @@ def bench_stream(args, cfg, torch, M, S, dev):
 
     res = {}
     for mode in ("prefetch", "reactive"):
-        stm = StreamedStack(host_layers, cfg.K, dev, n_slots=args.pool_slots, prefetch=(mode == "prefetch"))
+        stm = StreamedStack(host_layers, cfg.K, dev, n_slots=args.pool_slots, prefetch=(mode == "prefetch"),
+                            fork_every=args.fork_every)
         run = tm.capture(lambda t, h, stm=stm: stm.token(t, h))
         # fill the pools first (about n_slots / misses-per-layer tokens), then count over the timed tokens
         n_fill = -(-max(args.warmup, 2 * args.pool_slots) // 3) * 3
@@ -746,6 +747,7 @@ def main():
                          "stream (decode35b with every expert in pinned host memory, HBM pools)")
     ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
     ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
+    ap.add_argument("--fork-every", type=int, default=8, help="stream workload: layers per prefetch fork")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")

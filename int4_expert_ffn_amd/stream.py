@@ -55,7 +55,7 @@ class StreamedStack(DecodeStack):
         # layer's copy and the host link stays busy
         self.copy_streams = [torch.cuda.Stream(device=dev) for _ in range(max(1, copy_streams))]
         self.kick = [torch.cuda.Event() for _ in range(self.L)]      # predictions so far ready
-        self.fork_every = max(1, min(fork_every, L.MOE_POOL_MAX_JOBS))
+        self.fork_every = max(1, fork_every)
         self._ffn_ws = torch.empty(max(L.moe_expert_ffn_workspace_size(1, K, p.experts) for p in self.pools),
                                    dtype=torch.uint8, device=dev)
 
