@@ -344,7 +344,7 @@ def bench_stack(args, cfg, torch, M, S, dev):
                               "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn, tokens=2 if cfg.d <= 2048 else 1)
+        rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn, tokens=5 if cfg.d <= 2048 else 2)
     return rec
 
 
@@ -547,7 +547,7 @@ def bench_relu_sparse(args, cfg, torch, M, S, dev):
     rec["down_bytes_saved"] = round(1 - mean_active / I, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        rec["cpu_baseline"] = cpu_baseline_relu(cfg, S, syn, tokens=1)
+        rec["cpu_baseline"] = cpu_baseline_relu(cfg, S, syn, tokens=5)
     return rec
 
 
@@ -659,6 +659,9 @@ def bench_stream(args, cfg, torch, M, S, dev):
         "note": "every path replays one HIP graph per token (the streamed ones on two streams, joined at the "
                 "token's end); the resident per-layer path runs the same schedule with every expert in HBM",
     }
+    if not args.no_cpu_baseline:   # streaming moves bytes and changes no result: the oracle is the resident chain's
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(cfg, dev_layers, syn, tokens=5)
     return rec
 
 
