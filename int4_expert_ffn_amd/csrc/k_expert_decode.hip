@@ -295,6 +295,120 @@ __global__ void __launch_bounds__(64) k_down(int T, int K, int E, int d, int I, 
   }
 }
 
+// Waves per block of the LDS-staged down kernel, and its segment layout in LDS.
+constexpr int DN_WAVES = 4;
+template <int BITS>
+struct DnLds {
+  static constexpr int PAIRS = SegT<BITS>::PAIRS;
+  static constexpr int STRIDE = PAIRS + 4;   // words per segment: 16 lanes of a row slot hit distinct banks
+};
+
+// The down projection with the token's activations staged once per block.  The plain k_down has
+// every row slot of every wave load and split the float32 activations of all K experts itself
+// (4 row slots per wave x every wave: the 8 KB of a decode35b token was read from L2 some 2,000
+// times); here DN_WAVES waves share one copy in LDS, held as the permuted float16 hi / lo pairs the
+// dot products take.  One segment per lane (P = 1), K <= KMAX, all K experts' weights issued before
+// the staging so that its latency hides under theirs.
+template <int BITS>
+size_t down_lds_bytes(int K, int I) {
+  const int segs = K * (I * BITS / 128);
+  return (size_t)segs * (2 * DnLds<BITS>::STRIDE * 4 + 8);
+}
+
+template <int BITS, bool SPLIT, int KMAX>
+__global__ void __launch_bounds__(DN_WAVES * WAVE) k_down_lds(int T, int K, int E, int d, int I, int lg2g, int L,
+                                                          const float* __restrict__ act,
+                                                          const int32_t* __restrict__ idx, moe_qmat down,
+                                                          float* __restrict__ out, const float* __restrict__ wf,
+                                                          const uint16_t* __restrict__ rf,
+                                                          uint16_t* __restrict__ yf, LoraRef ldn) {
+  using G = SegT<BITS>;
+  using D = DnLds<BITS>;
+  extern __shared__ __align__(16) uint32_t dsm[];
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int t = blockIdx.y;
+  const int RPI = WAVE / L;
+  const int slot = lane / L, ls = lane % L;
+  const int wpr = I * BITS / 32;
+  const int ngr = I >> lg2g;
+  const int S = I * BITS / 128;
+  const int j = (blockIdx.x * DN_WAVES + wv) * RPI + slot;
+  const bool jok = j < d;
+  const bool seg = ls < S;
+  const int lsc = seg ? ls : 0;
+  uint32_t* hpL = dsm;                                   // [K * S][STRIDE]
+  uint32_t* lpL = dsm + (size_t)K * S * D::STRIDE;       // [K * S][STRIDE]
+  float* sxL = reinterpret_cast<float*>(lpL + (size_t)K * S * D::STRIDE);  // [K * S][2]
+
+  // 1. this lane's weights of all K experts
+  uint4 q[KMAX];
+  SegSB<BITS, SPLIT> sb[KMAX];
+  bool bad[KMAX];
+  float wk[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    bad[k] = true;
+    wk[k] = 0.f;
+    if (k < K) {
+      int e = idx[(size_t)t * K + k];
+      bad[k] = (unsigned)e >= (unsigned)E;
+      if (bad[k]) e = 0;
+      wk[k] = wf ? wf[(size_t)t * K + k] : 0.f;
+      const size_t rw = (size_t)e * d + (jok ? j : 0);
+      q[k] = *reinterpret_cast<const uint4*>(down.q + rw * wpr + (size_t)lsc * 4);
+      sb[k].load(down, rw, ngr, lg2g, lsc);
+    }
+  }
+  // 2. the token's activations, split and permuted once per block (one segment per thread step)
+  for (int u = tid; u < K * S; u += DN_WAVES * WAVE) {
+    const int k = u / S, sg = u - k * S;
+    uint32_t hp[G::PAIRS], lp[G::PAIRS];
+    float sx[2];
+    load_xpairs_f32<BITS>(act + ((size_t)t * K + k) * I + (size_t)sg * G::COLS, hp, lp, sx);
+    uint4* hd = reinterpret_cast<uint4*>(hpL + (size_t)u * D::STRIDE);
+    uint4* ld = reinterpret_cast<uint4*>(lpL + (size_t)u * D::STRIDE);
+#pragma unroll
+    for (int w = 0; w < G::PAIRS / 4; ++w) {
+      hd[w] = make_uint4(hp[4 * w], hp[4 * w + 1], hp[4 * w + 2], hp[4 * w + 3]);
+      ld[w] = make_uint4(lp[4 * w], lp[4 * w + 1], lp[4 * w + 2], lp[4 * w + 3]);
+    }
+    sxL[2 * u] = sx[0];
+    sxL[2 * u + 1] = sx[1];
+  }
+  __syncthreads();
+  // 3. dot products, expert by expert, and the weighted combine in ascending k
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k >= K) break;
+    float po = 0.f;
+    if (seg) {
+      const int u = k * S + ls;
+      uint32_t hp[G::PAIRS], lp[G::PAIRS];
+      const uint4* hs = reinterpret_cast<const uint4*>(hpL + (size_t)u * D::STRIDE);
+      const uint4* lsrc = reinterpret_cast<const uint4*>(lpL + (size_t)u * D::STRIDE);
+#pragma unroll
+      for (int w = 0; w < G::PAIRS / 4; ++w) {
+        const uint4 a = hs[w], b = lsrc[w];
+        hp[4 * w] = a.x, hp[4 * w + 1] = a.y, hp[4 * w + 2] = a.z, hp[4 * w + 3] = a.w;
+        lp[4 * w] = b.x, lp[4 * w + 1] = b.y, lp[4 * w + 2] = b.z, lp[4 * w + 3] = b.w;
+      }
+      const float sx[2] = {sxL[2 * u], sxL[2 * u + 1]};
+      float d0 = 0.f, d1 = 0.f;
+      dot_segment_split<BITS>(q[k], hp, lp, d0, d1);
+      po = sb[k].apply(d0, d1, sx);
+    }
+    po = group_sum(po, L);
+    if (ls == 0 && jok) {
+      if (ldn.B) po += lora_row(ldn, t, j);
+      if (bad[k]) po = quiet_nan();
+      if (out) out[((size_t)t * K + k) * d + j] = po;
+      acc = fmaf(wk[k], po, acc);
+    }
+  }
+  if (yf && ls == 0 && jok) yf[(size_t)t * d + j] = f2h(h2f(rf[(size_t)t * d + j]) + acc);
+}
+
 __global__ void __launch_bounds__(256) k_combine(int T, int K, int d, const float* __restrict__ o,
                                                  const float* __restrict__ w,
                                                  const uint16_t* __restrict__ r,
@@ -346,6 +460,16 @@ hipError_t launch_pair(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, con
     return launch(k_gateup<BITS, P, SPLIT, NB_GATEUP>, grid, dim3(WAVE), 0, s, a.T, a.K, a.E, a.d, a.I, lg2g,
                   gu.L, a.flags, a.x, a.idx, a.ex.gate, a.ex.up, (float*)a.act, lg, lu, a.relu ? 1 : 0, a.zero,
                   a.nzero);
+  }
+  if (P == 1 && a.K <= 8 && down_lds_bytes<BITS>(a.K, a.I) <= 48 * 1024) {
+    const int rpb = (WAVE / gd.L) * DN_WAVES;
+    dim3 grid((a.d + rpb - 1) / rpb, a.T);
+    auto go_lds = [&](auto kern) {
+      return launch(kern, grid, dim3(DN_WAVES * WAVE), down_lds_bytes<BITS>(a.K, a.I), s, a.T, a.K, a.E, a.d, a.I,
+                    lg2g, gd.L, (const float*)a.act, a.idx, a.ex.down, a.out, a.w_fuse, a.r_fuse, a.y_fuse, ldn);
+    };
+    if (a.K <= 4) return go_lds(k_down_lds<BITS, SPLIT, 4>);
+    return go_lds(k_down_lds<BITS, SPLIT, 8>);
   }
   const int rpw = (WAVE / gd.L) * NB_DOWN;
   dim3 grid((a.d + rpw - 1) / rpw, a.T);
