@@ -70,7 +70,6 @@ class DecodeStack:
     def _step_state(self):
         """Device array of layer descriptors, the stack descriptor and the zeroed step workspace."""
         if self._step is None:
-            import ctypes
             L_ = self.L
             arr = (L.moe_decode_layer * L_)()
             H = 0

@@ -2,7 +2,6 @@
 
 Bar: expert indices bit-exact (tokens drawn with top-(K+1) logit gaps >= 1e-4); float outputs per
 token row within max|y - y_ref| <= 2e-3 * max|y_ref| (float16 in, float32 accumulation)."""
-import math
 from dataclasses import replace
 
 import numpy as np
@@ -11,7 +10,7 @@ import torch
 
 import moe_synth as S
 import oracle as O
-from parity_util import (TOL, ExpertCache, assert_rows_close, device_layer, gap_tokens, log)
+from parity_util import (ExpertCache, assert_rows_close, device_layer, gap_tokens, log)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

@@ -3,7 +3,6 @@ independence, and the value distributions of the workloads."""
 import math
 
 import numpy as np
-import pytest
 import torch
 
 import moe_synth as S
