@@ -112,15 +112,18 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def cpu_baseline(cfg, layers, syn, tokens):
-    """Time the fp64 oracle (single thread) on `tokens` steady-state tokens of the same stack."""
+def cpu_baseline(cfg, layers, syn, tokens, threads=1):
+    """Time the fp64 oracle on `tokens` steady-state tokens of the same stack, with `threads` BLAS
+    threads (None: the library's default, every core)."""
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        limiter = None
+    limiter = None
+    if threads is not None:
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(threads)
+        except Exception:  # pragma: no cover
+            limiter = None
     routers = [lw.router.cpu().numpy() for lw in layers]
     heads = [None if lw.head is None else {k: (None if v is None else v.cpu().numpy())
                                            for k, v in lw.head.tensors.items()} for lw in layers]
@@ -141,9 +144,13 @@ def cpu_baseline(cfg, layers, syn, tokens):
     for i in range(tokens):
         _, st, _ = O.chain_token(syn.hidden(10**6 + 1 + i, 1)[0].numpy(), st, **kw)
     elapsed = time.perf_counter() - t0
-    return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    cores = threads if threads is not None else (os.cpu_count() or 1)
+    return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{tokens} steady-state decode tokens through all {cfg.L} layers (fp64, explicit dequant, "
-                      f"1 BLAS thread; includes copying each selected expert's packed bytes from HBM once)"}
+                      f"{cores} BLAS thread{'s' if cores > 1 else ''}; includes copying each selected expert's packed "
+                      f"bytes from HBM once)"}
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
@@ -328,6 +335,49 @@ def bench_stack(args, cfg, torch, M, S, dev):
         del graphs2
     launches = (5 * cfg.L - 2) if cfg.head_hidden else 4 * cfg.L
 
+    # cold tokens: a 1 GiB streaming read before each token evicts L2 and the memory-side cache, and
+    # HIP events time the token's launch alone
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fold = torch.empty(M.MOE_READ_PROBE_BLOCKS, dtype=torch.int32, device=dev)
+        stack_c = DecodeStack(layers, cfg.K, dev)
+        graphs_c = tm.capture(lambda t, h: stack_c.step(t, h))
+        n_cold = max(30, args.steps // 4) // 3 * 3
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+        with torch.cuda.stream(tm.stream):
+            tm.run(graphs_c, 30, 1)
+            for i in range(n_cold):
+                t = 31 + i
+                if t % 3 == 1:
+                    p = (t // 3 * 3) % tm.n_pool
+                    tm.ring.copy_(tm.pool[p:p + 3])
+                M.moe_read_probe(flush, fold)
+                evs[i][0].record(tm.stream)
+                graphs_c[(t - 1) % 3].replay()
+                evs[i][1].record(tm.stream)
+        torch.cuda.synchronize()
+        assert stack_c.step_error_word() == 0, "a wait inside the decode kernel ran out of time (cold)"
+        cold_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / n_cold
+        cold = {"tokens": n_cold, "avg_us": round(cold_us, 2), "tokens_per_s": round(1e6 / cold_us, 2),
+                "achieved_GBps": round(total_bytes / (cold_us * 1e-6) / 1e9, 1),
+                "frac_of_peak": round(total_bytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "note": "a 1 GiB streaming read before each token; the token's launch timed alone"}
+        del graphs_c, stack_c, flush
+    # measured HBM read ceiling: a plain 16-byte streaming read over 8 GiB
+    buf = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
+    fold = torch.empty(M.MOE_READ_PROBE_BLOCKS, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        M.moe_read_probe(buf, fold)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        M.moe_read_probe(buf, fold)
+    e1.record()
+    torch.cuda.synchronize()
+    read_ceiling = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+
     tok_s = args.steps / wall
     rec = base_record(args, cfg, tok_s, wall, args.steps)
     if args.norm_gain:
@@ -336,15 +386,22 @@ def bench_stack(args, cfg, torch, M, S, dev):
     rec["hbm"] = {"algorithmic_bytes_per_token": total_bytes,
                   "achieved_GBps": round(total_bytes * tok_s / 1e9, 1),
                   "frac_of_peak": round(total_bytes * tok_s / 1e9 / HBM_PEAK_GBPS, 4)}
+    rec["hbm"]["measured_read_ceiling_GBps"] = round(read_ceiling, 1)
+    rec["hbm"]["frac_of_measured_ceiling"] = round(total_bytes * tok_s / 1e9 / read_ceiling, 4)
     rec["roofline"] = roofline(f"k_decode_step (moe_decode_step: all {cfg.L} layers of one token in one launch)",
                                total_bytes, step_us,
                                stored_traffic() if cfg.name == "decode35b" and not args.norm_gain else None)
+    rec["roofline"]["measured_read_ceiling_GBps"] = round(read_ceiling, 1)
+    rec["roofline"]["frac_of_measured_ceiling"] = round(rec["roofline"]["achieved"] / read_ceiling, 4)
+    rec["cold"] = cold
     rec["expert_only"] = expert_only
     rec["per_layer_calls"] = {"tokens_per_s": per_layer_tok_s, "launches_per_token": launches,
                               "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn, tokens=5 if cfg.d <= 2048 else 2)
+        log("timing the CPU oracle on every core ...")
+        rec["cpu_baseline_all_cores"] = cpu_baseline(cfg, layers, syn, tokens=5 if cfg.d <= 2048 else 2, threads=None)
     return rec
 
 
@@ -695,7 +752,8 @@ def cpu_baseline_relu(cfg, S, syn, tokens):
             o = np.stack([O.expert_ffn_relu_packed(x, *packed[(l, int(e))], cfg.bits, cfg.group)[0] for e in idx[0]])
             h = O.to_f16_f64(O.combine(o, w[0], h))
     elapsed = time.perf_counter() - t0
-    del limiter
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{tokens} token(s) through all {L} layers of the ReLU sparse expert FFN (fp64, explicit "
                       f"dequant, 1 BLAS thread; weights drawn beforehand)"}
@@ -732,7 +790,8 @@ def cpu_baseline_batched(cfg, S, tokens):
     sh = O.expert_ffn_packed(h, *shared, cfg.bits, cfg.group, lora)
     O.combine(o, w, h, sh)
     elapsed = time.perf_counter() - t0
-    del limiter
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": round(tokens / elapsed, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the first {tokens} tokens of a {cfg.T}-token batch (fp64, explicit dequant per expert "
                       f"and token, 1 BLAS thread; weights drawn beforehand)"}
@@ -751,6 +810,7 @@ def main():
     ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
     ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
     ap.add_argument("--fork-every", type=int, default=8, help="stream workload: layers per prefetch fork")
+    ap.add_argument("--no-cold", action="store_true", help="stack workloads: skip the cold-token timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")

@@ -235,6 +235,13 @@ typedef struct {
 moe_status moe_stream_in_many(void* stream, int32_t n, int32_t K, const moe_stream_job* jobs, void* workspace,
                               size_t workspace_bytes);
 
+/* Measurement aid, not a step of the method: a plain streaming read of `bytes` bytes of device
+   memory at buf (16-byte aligned, bytes a multiple of 16) with 16-byte loads, the measured read
+   ceiling of HBM the layer kernels are compared with.  out[MOE_READ_PROBE_BLOCKS] (uint32, device)
+   receives one fold of the data per block, so that no load can be dropped. */
+#define MOE_READ_PROBE_BLOCKS 4096
+moe_status moe_read_probe(void* stream, const void* buf, size_t bytes, uint32_t* out);
+
 /* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
    (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose
    index lies outside [0, E); perm[T*K] (int32, out) lists flat pair indices t*K + k grouped by

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
-    "moe_stream_in_many",
+    "moe_stream_in_many", "moe_read_probe",
 )
 
 
@@ -102,6 +102,7 @@ def _load():
         "moe_stream_in": (st, [vp, i32, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_experts),
                                ctypes.POINTER(moe_pool), vp, vp, vp, sz]),
         "moe_stream_in_many": (st, [vp, i32, i32, ctypes.POINTER(moe_stream_job), vp, sz]),
+        "moe_read_probe": (st, [vp, vp, sz, vp]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -337,6 +338,14 @@ def moe_stream_in(K, idx, src: Experts, pool: Pool, idx_slot, counters, workspac
 
 
 MOE_POOL_MAX_JOBS = 8
+MOE_READ_PROBE_BLOCKS = 4096
+
+
+def moe_read_probe(buf, out, stream=None):
+    """Streaming read of the device tensor `buf` (measurement aid); out: int32 [MOE_READ_PROBE_BLOCKS]."""
+    nbytes = buf.numel() * buf.element_size()
+    st = _lib.moe_read_probe(_stream(stream, buf, out), _ptr(buf, None, "buf"), nbytes, _ptr(out, _i32(), "out"))
+    _check(st, "moe_read_probe")
 
 
 def moe_stream_in_many(K, jobs, workspace, workspace_bytes=None, stream=None):

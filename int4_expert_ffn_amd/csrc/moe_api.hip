@@ -319,6 +319,11 @@ moe_status moe_stream_in(void* stream, int32_t K, const int32_t* idx, const moe_
   return moe_stream_in_many(stream, 1, K, &j, workspace, workspace_bytes);
 }
 
+moe_status moe_read_probe(void* stream, const void* buf, size_t bytes, uint32_t* out) {
+  if (!buf || !out || bytes < 16 || (bytes & 15) || !aligned16(buf)) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_read_probe((hipStream_t)stream, buf, bytes, out));
+}
+
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,
                               int32_t* offsets, int32_t* perm) {
   if (T < 1 || K < 1 || E < 1 || E > MOE_MAX_E || (int64_t)T * K > (1 << 24)) return MOE_ERR_INVALID_ARG;

@@ -101,6 +101,9 @@ hipError_t launch_pool_stream_in(hipStream_t s, int n, const PoolArgs* jobs, con
                                  const moe_experts* const* pool);
 size_t pool_plan_bytes(int K);
 
+// measurement aid: streaming read of a buffer (MOE_READ_PROBE_BLOCKS words out)
+hipError_t launch_read_probe(hipStream_t s, const void* buf, size_t bytes, uint32_t* out);
+
 // combine -------------------------------------------------------------------------------------
 hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const uint16_t* gain, uint16_t* x);
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,

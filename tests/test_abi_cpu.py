@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -166,6 +166,13 @@ def test_stream_in_many_rejects():
     other = _ex(E=256, d=2048, I=1024, group=64)
     assert many(2, jobs(2, other=other)) == INVALID             # jobs of different shapes
     assert L.moe_stream_in_many(None, 1, 4, None, FAKE, 1 << 20) == INVALID
+
+
+def test_read_probe_rejects():
+    assert L.moe_read_probe(None, None, 1024, FAKE) == INVALID
+    assert L.moe_read_probe(None, FAKE, 1024, None) == INVALID
+    assert L.moe_read_probe(None, FAKE, 1000, FAKE) == INVALID     # not whole 16-byte units
+    assert L.moe_read_probe(None, FAKE + 8, 1024, FAKE) == INVALID  # misaligned
 
 
 def test_prerouter_and_combine_reject():
