@@ -344,6 +344,8 @@ MOE_READ_PROBE_BLOCKS = 4096
 def moe_read_probe(buf, out, stream=None):
     """Streaming read of the device tensor `buf` (measurement aid); out: int32 [MOE_READ_PROBE_BLOCKS]."""
     nbytes = buf.numel() * buf.element_size()
+    if out.numel() < MOE_READ_PROBE_BLOCKS:
+        raise ValueError(f"moe_read_probe: out needs {MOE_READ_PROBE_BLOCKS} int32 words")
     st = _lib.moe_read_probe(_stream(stream, buf, out), _ptr(buf, None, "buf"), nbytes, _ptr(out, _i32(), "out"))
     _check(st, "moe_read_probe")
 
