@@ -148,9 +148,21 @@ def cpu_baseline(cfg, layers, syn, tokens, threads=1):
         limiter.restore_original_limits()
     cores = threads if threads is not None else (os.cpu_count() or 1)
     return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{tokens} steady-state decode tokens through all {cfg.L} layers (fp64, explicit dequant, "
                       f"{cores} BLAS thread{'s' if cores > 1 else ''}; includes copying each selected expert's packed "
                       f"bytes from HBM once)"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
@@ -261,6 +273,34 @@ class Timer:
         return w1 - w0, e0.elapsed_time(e1), warmup
 
 
+def routing_histogram(cfg, layers, syn, torch, dev, tokens=1024):
+    """Experts chosen per layer over `tokens` decode tokens of the chain (a fresh hidden state per
+    token): min and max count per expert against the uniform expectation tokens*K/E, and Pearson's
+    chi-square over the E experts (E - 1 degrees of freedom)."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    stack = DecodeStack(layers, cfg.K, dev)
+    hs = syn.hidden(11, tokens, dev)
+    rec = torch.empty((tokens, cfg.L, cfg.K), dtype=torch.int32, device=dev)
+    for t in range(tokens):
+        stack.step(t, hs[t])
+        rec[t].copy_(stack.route_idx[t % 3])
+    torch.cuda.synchronize()
+    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time (histogram)"
+    idx = rec.cpu().long()
+    expect = tokens * cfg.K / cfg.E
+    mins, maxs, chi2 = [], [], []
+    for l in range(cfg.L):
+        n = torch.bincount(idx[:, l].reshape(-1), minlength=cfg.E).double()
+        mins.append(int(n.min()))
+        maxs.append(int(n.max()))
+        chi2.append(round(float(((n - expect) ** 2).sum() / expect), 1))
+    srt = sorted(chi2)
+    return {"tokens": tokens, "expected_per_expert": expect, "dof": cfg.E - 1,
+            "min_count": min(mins), "max_count": max(maxs), "chi2_median": srt[len(srt) // 2], "chi2_max": srt[-1],
+            "chi2_per_layer": chi2,
+            "note": "routing the full path chose (layer 0 and the first token self-routed, the rest as the stack routes)"}
+
+
 def bench_stack(args, cfg, torch, M, S, dev):
     """A resident L-layer stack at batch 1: the timed step is one moe_decode_step launch per token
     (the persistent kernel running every layer); the expert FFN steps alone and the per-layer
@@ -281,6 +321,9 @@ def bench_stack(args, cfg, torch, M, S, dev):
     assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
     h_out = stack.h[cfg.L].float()
     assert torch.isfinite(h_out).all(), "non-finite decode output"
+    # the same timed loop again (no further warm-up): the spread of the figure over repeats
+    reps = [args.steps / wall] + [args.steps / tm.timed(graphs, args.steps, 0)[0] for _ in range(args.repeats - 1)]
+    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time (repeats)"
     del graphs
     total_bytes, eo_bytes = algorithmic_bytes(cfg)
     step_us = ev_ms * 1e3 / args.steps               # HIP-event time per token on the stream
@@ -293,15 +336,26 @@ def bench_stack(args, cfg, torch, M, S, dev):
         n_pool = tm.n_pool
         rec_i = torch.empty((n_pool, cfg.L, cfg.K), dtype=torch.int32, device=dev)
         rec_w = torch.empty((n_pool, cfg.L, cfg.K), dtype=torch.float32, device=dev)
-        src = DecodeStack(layers, cfg.K, dev)
-        with torch.cuda.stream(tm.stream):
-            for t in range(n_pool):
-                src.step(t, tm.pool[t])
-                rec_i[t].copy_(src.route_idx[t % 3])
-                rec_w[t].copy_(src.route_w[t % 3])
-        torch.cuda.synchronize()
-        assert src.step_error_word() == 0, "a wait inside the decode kernel ran out of time (recording)"
-        del src
+        if cfg.head_hidden:
+            # prerouted: the routing the full path chose for the same tokens
+            routing_note = "the routing the full path chose for the same tokens"
+            src = DecodeStack(layers, cfg.K, dev)
+            with torch.cuda.stream(tm.stream):
+                for t in range(n_pool):
+                    src.step(t, tm.pool[t])
+                    rec_i[t].copy_(src.route_idx[t % 3])
+                    rec_w[t].copy_(src.route_w[t % 3])
+            torch.cuda.synchronize()
+            assert src.step_error_word() == 0, "a wait inside the decode kernel ran out of time (recording)"
+            del src
+        else:
+            # self-routed: per (token, layer) K distinct experts drawn uniformly, as the top-K of
+            # seeded N(0, 1) logits, with their renormalised softmax weights
+            routing_note = "seeded routing drawn uniformly per (token, layer): top-K of N(0,1) logits, renormalised"
+            lg = syn.logits(13, n_pool * cfg.L, dev)
+            M.moe_route_topk(n_pool * cfg.L, cfg.d, cfg.E, cfg.K, M.MOE_TOPK_RENORM, None, None, lg,
+                             rec_i.view(-1, cfg.K), rec_w.view(-1, cfg.K))
+            torch.cuda.synchronize()
         stack3 = DecodeStack(layers, cfg.K, dev)
         stack3.route_idx.copy_(rec_i[0:3])
         stack3.route_w.copy_(rec_w[0:3])
@@ -320,8 +374,8 @@ def bench_stack(args, cfg, torch, M, S, dev):
             "algorithmic_bytes_per_token": eo_bytes,
             "achieved_GBps": round(eo_bytes / (eo_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(eo_bytes / (eo_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "note": "S3-S6 alone (moe_decode_step with MOE_DECODE_GIVEN_ROUTING) on the routing the full "
-                    "path chose for the same tokens; HIP-event time per token includes the routing refill copies",
+            "note": "S3-S6 alone (moe_decode_step with MOE_DECODE_GIVEN_ROUTING) on " + routing_note +
+                    "; HIP-event time per token includes the routing refill copies",
         }
 
     # context: the same schedule as per-layer C-ABI calls
@@ -378,6 +432,8 @@ def bench_stack(args, cfg, torch, M, S, dev):
     read_ceiling = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del buf
 
+    hist = routing_histogram(cfg, layers, syn, torch, dev) if not args.no_histogram else None
+
     tok_s = args.steps / wall
     rec = base_record(args, cfg, tok_s, wall, args.steps)
     if args.norm_gain:
@@ -394,6 +450,9 @@ def bench_stack(args, cfg, torch, M, S, dev):
     rec["roofline"]["measured_read_ceiling_GBps"] = round(read_ceiling, 1)
     rec["roofline"]["frac_of_measured_ceiling"] = round(rec["roofline"]["achieved"] / read_ceiling, 4)
     rec["cold"] = cold
+    rec["repeats"] = {"tokens_per_s": [round(v, 2) for v in reps], "median": round(sorted(reps)[len(reps) // 2], 2),
+                      "note": f"{len(reps)} runs of the same {args.steps} timed tokens, the first being `value`"}
+    rec["routing_histogram"] = hist
     rec["expert_only"] = expert_only
     rec["per_layer_calls"] = {"tokens_per_s": per_layer_tok_s, "launches_per_token": launches,
                               "note": "same schedule issued as per-layer C-ABI calls in a HIP graph"}
@@ -811,6 +870,8 @@ def main():
     ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
     ap.add_argument("--fork-every", type=int, default=8, help="stream workload: layers per prefetch fork")
     ap.add_argument("--no-cold", action="store_true", help="stack workloads: skip the cold-token timing")
+    ap.add_argument("--no-histogram", action="store_true", help="stack workloads: skip the routing histogram")
+    ap.add_argument("--repeats", type=int, default=5, help="stack workloads: runs of the timed loop (the first is value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
