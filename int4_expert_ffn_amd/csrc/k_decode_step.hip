@@ -44,6 +44,8 @@ constexpr int MW = 8;                        // compute waves per workgroup (two
 constexpr int NTHREADS = (MW + 1) * WAVE;
 constexpr int NH_MAX = 2;                    // head fc1/linear rows per compute wave
 constexpr int LDS_D = 4096, LDS_ACT = 4096, LDS_H = 2048, LDS_E = 1024, LDS_PART = 512, LDS_LK = 512;
+constexpr int RWG = 2;                       // router rows per workgroup that LDS can stage
+constexpr int LDS_RR = 8192;                 // halves of staged router rows (RWG rows of d <= 4096)
 constexpr int POLL_MAX = 16;                 // words per lane per polling pass (1024 per wave), <= 64
 static_assert(POLL_MAX >= 1 && POLL_MAX <= 64, "one done bit per polled word");
 constexpr uint32_t TAG_SALT = 0x5A5A5A5Au;
@@ -61,6 +63,7 @@ struct StepParams {
   float* rw;
   int slot, bootstrap, given;  // given: every layer's routing supplied by the caller
   int gained;                  // every layer's input norm has a gain (else none has)
+  int rstage;                  // the compute waves stage each self-routed layer's router rows in LDS
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
   uint32_t* epoch;
@@ -454,6 +457,7 @@ struct StepShared {
   // instruction is 16 bits; past it every access needs an address register):
   uint16_t gain[2][LDS_D];  // input-norm gains of layers l and l+1 (by layer parity), staged by the compute waves
   uint16_t xg[LDS_D];       // gain * h_l, formed by the compute waves once h_l is in (gained layers only)
+  uint16_t rrow[LDS_RR];    // router rows of a self-routed layer, staged by the compute waves: slot cw holds row cw * G + wg
 };
 
 struct StepCtx {
@@ -590,7 +594,21 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       if (m < dh) gw[m] = gv[j];
     }
   };
+  // A self-routed layer's router row of this wave goes straight from memory into LDS slot cw
+  // (16-byte global-to-LDS loads: no registers held), issued a layer early; the router phase then
+  // waits for it with the wave's other loads long done.  Slot cw holds row cw * G + wg.
+  const auto stage_router = [&](int l) {
+    const int r = e_row(p, wg, cw);
+    if (!p.rstage || r >= p.E) return;  // uniform over the wave
+    // the row as a buffer: one lane offset serves every piece, the piece's offset goes in soffset
+    const __amdgpu_buffer_rsrc_t rb = buffer_of(layer_at(p, l)->router + (size_t)r * p.d, (uint32_t)p.d * 2);
+#pragma unroll
+    for (int sg = 0; sg < NSH; ++sg)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(sm.rrow + (size_t)cw * p.d + sg * WAVE * 8),
+                                               16, (uint32_t)lane * 16, (uint32_t)sg * WAVE * 16, 0, 0);
+  };
   stage_gain(0);
+  if (self_routed(p, 0)) stage_router(0);
   for (int l = 0; l < p.L; ++l) {
     const bool self = self_routed(p, l);
     const bool head = has_head(p, l);
@@ -617,12 +635,22 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       // R_l: at most one router row per wave -> tagged logit
       const int r = e_row(p, wg, cw);
       if (r < p.E) {  // uniform over the wave
-        const uint16_t* W = layer_at(p, l)->router + (size_t)r * p.d;
+        uint4 wr[NSH];  // this wave's router row: slot cw of the staged rows, else from memory
+        if (p.rstage) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the row's global-to-LDS loads have landed
+          const uint4* W = reinterpret_cast<const uint4*>(sm.rrow + (size_t)cw * p.d);
+#pragma unroll
+          for (int sg = 0; sg < NSH; ++sg) wr[sg] = W[lane + sg * WAVE];
+        } else {
+          const uint4* W = reinterpret_cast<const uint4*>(layer_at(p, l)->router + (size_t)r * p.d);
+#pragma unroll
+          for (int sg = 0; sg < NSH; ++sg) wr[sg] = W[lane + sg * WAVE];
+        }
         float red[2] = {0.f, 0.f};  // router dot, sum of squares of h_l
 #pragma unroll
         for (int sg = 0; sg < NSH; ++sg) {
           const int g = lane + sg * WAVE;
-          const uint4 wv = *reinterpret_cast<const uint4*>(W + (size_t)g * 8);
+          const uint4 wv = wr[sg];
           const uint4 xv = *reinterpret_cast<const uint4*>(hl + (size_t)g * 8);
           if (gn) {  // the routing decides indices: the gained product in float32, not rounded
             red[0] = dot8_gained(wv, xv, *reinterpret_cast<const uint4*>(sm.gain[l & 1] + (size_t)g * 8), red[0]);
@@ -832,6 +860,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     if (prefetch)
       issue_A_head<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K,
                                                c.prev_i ? sm.prev_e + (l + 1) * K : nullptr, head, wg, cw, lane, A);
+    if (l + 1 < p.L && self_routed(p, l + 1)) stage_router(l + 1);
   }
 }
 
@@ -1019,6 +1048,10 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.slot = token % 3;
   p.given = (flags & MOE_DECODE_GIVEN_ROUTING) != 0;
   p.gained = st.norm_gains != 0;
+  {
+    const int rows = (st.E + pl.G - 1) / pl.G;  // router rows of the busiest workgroup (row r: wave r / G)
+    p.rstage = rows <= RWG && rows * st.d_model <= LDS_RR;
+  }
   p.bootstrap = token == 0 && !p.given;
   p.topk_flags = flags & MOE_TOPK_RENORM;
   p.ll_logits = (uint64_t*)(b + w.logits);
