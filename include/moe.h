@@ -238,7 +238,9 @@ moe_status moe_stream_in_many(void* stream, int32_t n, int32_t K, const moe_stre
 /* Measurement aid, not a step of the method: a plain streaming read of `bytes` bytes of device
    memory at buf (16-byte aligned, bytes a multiple of 16) with 16-byte loads, the measured read
    ceiling of HBM the layer kernels are compared with.  out[MOE_READ_PROBE_BLOCKS] (uint32, device)
-   receives one fold of the data per block, so that no load can be dropped. */
+   receives one fold of the data per block, so that no load can be dropped.  The caller owns both
+   buffers.  MOE_ERR_INVALID_ARG (nothing enqueued) for a null pointer, bytes below 16 or not a
+   multiple of 16, or buf not 16-byte aligned; MOE_ERR_HIP if the launch fails. */
 #define MOE_READ_PROBE_BLOCKS 4096
 moe_status moe_read_probe(void* stream, const void* buf, size_t bytes, uint32_t* out);
 
