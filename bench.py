@@ -146,7 +146,14 @@ def cpu_baseline(cfg, layers, syn, tokens, threads=1):
     elapsed = time.perf_counter() - t0
     if limiter is not None:
         limiter.restore_original_limits()
-    cores = threads if threads is not None else (os.cpu_count() or 1)
+    cores = threads
+    if cores is None:  # the BLAS pools' own thread count (what the oracle's products used)
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"),
+                        default=1)
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
     return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "cpu": cpu_model(),
             "sample": f"{tokens} steady-state decode tokens through all {cfg.L} layers (fp64, explicit dequant, "
