@@ -151,8 +151,9 @@ __device__ __forceinline__ float from_order_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-constexpr int TOPK_VPL = MOE_MAX_E / WAVE;  // logits per lane
-
+// TOPK_VPL logits per lane: the smallest power of two with 64 * TOPK_VPL >= E (up to MOE_MAX_E / 64),
+// so a small E does not pay for the largest one's registers and compare rounds.
+template <int TOPK_VPL>
 __global__ void __launch_bounds__(64) k_topk(int T, int E, int K, uint32_t flags,
                                              const float* __restrict__ logits, int32_t* __restrict__ idx,
                                              float* __restrict__ w) {
@@ -376,7 +377,12 @@ hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags
 
 hipError_t launch_topk(hipStream_t s, int T, int E, int K, uint32_t flags, const float* logits, int32_t* idx,
                        float* w) {
-  return launch(k_topk, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  static_assert(MOE_MAX_E <= 16 * WAVE, "k_topk holds at most 16 logits per lane");
+  if (E <= WAVE) return launch(k_topk<1>, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  if (E <= 2 * WAVE) return launch(k_topk<2>, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  if (E <= 4 * WAVE) return launch(k_topk<4>, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  if (E <= 8 * WAVE) return launch(k_topk<8>, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
+  return launch(k_topk<16>, dim3(T), dim3(WAVE), 0, s, T, E, K, flags, logits, idx, w);
 }
 
 hipError_t launch_prerouter(hipStream_t s, int T, int d, int E, int K, uint32_t flags, const uint16_t* x,
