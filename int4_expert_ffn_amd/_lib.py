@@ -143,6 +143,15 @@ def _ptr(t, dtype=None, name="tensor", pinned_ok=False) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need(t, n, name):
+    """A tensor argument must hold at least n elements (the kernels index it by the call's sizes;
+    raw addresses and None pass through unchecked)."""
+    if t is None or isinstance(t, int):
+        return
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
 _hip = None
 
 
@@ -251,6 +260,12 @@ class PrerouterWeights:
 
 # ---------------------------------------------------------------------------------------------- calls
 def moe_route_topk(T, d, E, K, flags, x, w_router, logits, idx, w, stream=None):
+    if w_router is not None:
+        _need(x, T * d, "x")
+        _need(w_router, E * d, "w_router")
+    _need(logits, T * E, "logits")
+    _need(idx, T * K, "idx")
+    _need(w, T * K, "w")
     st = _lib.moe_route_topk(_stream(stream, logits, idx), T, d, E, K, flags,
                              _ptr(x, _f16(), "x"), _ptr(w_router, _f16(), "w_router"),
                              _ptr(logits, _f32(), "logits"), _ptr(idx, _i32(), "idx"), _ptr(w, _f32(), "w"))
@@ -263,6 +278,10 @@ def moe_prerouter_workspace_size(T, E, d_hidden) -> int:
 
 def moe_prerouter(T, d, E, K, flags, x, idx_cur, idx_prev, pw: PrerouterWeights, logits, workspace,
                   workspace_bytes=None, stream=None):
+    _need(x, T * d, "x")
+    _need(idx_cur, T * K, "idx_cur")
+    _need(idx_prev, T * K, "idx_prev")
+    _need(logits, T * E, "logits")
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     st = _lib.moe_prerouter(_stream(stream, logits), T, d, E, K, flags, _ptr(x, _f16(), "x"),
                             _ptr(idx_cur, _i32(), "idx_cur"), _ptr(idx_prev, _i32(), "idx_prev"),
@@ -277,6 +296,13 @@ def moe_expert_ffn_workspace_size(T, K, ex: Experts) -> int:
 
 def moe_expert_ffn_q4(T, K, flags, x, idx, ex: Experts, lora3: Optional[Lora3], out, w_fuse, r_fuse, y_fuse,
                       workspace, workspace_bytes=None, stream=None):
+    d = ex.d
+    _need(x, T * d, "x")
+    _need(idx, T * K, "idx")
+    _need(out, T * K * d, "out")
+    _need(w_fuse, T * K, "w_fuse")
+    _need(r_fuse, T * d, "r_fuse")
+    _need(y_fuse, T * d, "y_fuse")
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     st = _lib.moe_expert_ffn_q4(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"), _ptr(idx, _i32(), "idx"),
                                 ctypes.byref(ex.desc), ctypes.cast(lora3.desc, ctypes.POINTER(moe_lora)) if lora3 is not None else None,
@@ -292,6 +318,14 @@ def moe_expert_ffn_sparse_workspace_size(T, K, ex: Experts) -> int:
 def moe_expert_ffn_sparse(T, K, flags, x, idx, ex: Experts, out, w_fuse, r_fuse, y_fuse, n_active, workspace,
                           workspace_bytes=None, stream=None):
     """ReLU activation-sparse expert FFN; ex.down is neuron-major ([E][d_ff][d_model] packed)."""
+    d = ex.d
+    _need(x, T * d, "x")
+    _need(idx, T * K, "idx")
+    _need(out, T * K * d, "out")
+    _need(w_fuse, T * K, "w_fuse")
+    _need(r_fuse, T * d, "r_fuse")
+    _need(y_fuse, T * d, "y_fuse")
+    _need(n_active, T * K, "n_active")
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     st = _lib.moe_expert_ffn_sparse(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"),
                                     _ptr(idx, _i32(), "idx"), ctypes.byref(ex.desc), _ptr(out, _f32(), "out"),
@@ -367,18 +401,30 @@ def moe_stream_in_many(K, jobs, workspace, workspace_bytes=None, stream=None):
 
 
 def moe_combine(T, K, d, o, w, r, shared, y, stream=None):
+    _need(o, T * K * d, "o")
+    _need(w, T * K, "w")
+    _need(r, T * d, "r")
+    _need(shared, T * d, "shared")
+    _need(y, T * d, "y")
     st = _lib.moe_combine(_stream(stream, o, y), T, K, d, _ptr(o, _f32(), "o"), _ptr(w, _f32(), "w"),
                           _ptr(r, _f16(), "r"), _ptr(shared, _f32(), "shared"), _ptr(y, _f16(), "y"))
     _check(st, "moe_combine")
 
 
 def moe_rmsnorm(T, d, h, gain, x, stream=None):
+    _need(h, T * d, "h")
+    _need(gain, d, "gain")
+    _need(x, T * d, "x")
     st = _lib.moe_rmsnorm(_stream(stream, h, x), T, d, _ptr(h, _f16(), "h"), _ptr(gain, _f16(), "gain"),
                           _ptr(x, _f16(), "x"))
     _check(st, "moe_rmsnorm")
 
 
 def moe_sort_by_expert(T, K, E, idx, counts, offsets, perm, stream=None):
+    _need(idx, T * K, "idx")
+    _need(counts, E + 1, "counts")
+    _need(offsets, E + 2, "offsets")
+    _need(perm, T * K, "perm")
     st = _lib.moe_sort_by_expert(_stream(stream, idx), T, K, E, _ptr(idx, _i32(), "idx"), _ptr(counts, _i32(), "counts"),
                                  _ptr(offsets, _i32(), "offsets"), _ptr(perm, _i32(), "perm"))
     _check(st, "moe_sort_by_expert")

@@ -235,3 +235,24 @@ def test_workspace_sizes_closed_form():
 def test_binding_checks_tensors_on_host():
     with pytest.raises(ValueError):
         lib_mod._ptr(torch.zeros(4), None, "x")      # a host tensor is refused before any call
+
+
+def test_binding_rejects_short_tensors():
+    """The Python binding checks every tensor against the call's sizes before the library sees it."""
+    f16, f32, i32 = torch.float16, torch.float32, torch.int32
+    T, K, d, E = 2, 4, 8, 16
+    with pytest.raises(ValueError, match="o holds"):
+        lib_mod.moe_combine(T, K, d, torch.zeros(T * K * d - 1, dtype=f32), torch.zeros(T * K, dtype=f32),
+                            torch.zeros(T * d, dtype=f16), None, torch.zeros(T * d, dtype=f16))
+    with pytest.raises(ValueError, match="y holds"):
+        lib_mod.moe_combine(T, K, d, torch.zeros(T * K * d, dtype=f32), torch.zeros(T * K, dtype=f32),
+                            torch.zeros(T * d, dtype=f16), None, torch.zeros(T * d - 2, dtype=f16))
+    with pytest.raises(ValueError, match="idx holds"):
+        lib_mod.moe_route_topk(T, d, E, K, 0, None, None, torch.zeros(T * E, dtype=f32),
+                               torch.zeros(T * K - 1, dtype=i32), torch.zeros(T * K, dtype=f32))
+    with pytest.raises(ValueError, match="offsets holds"):
+        lib_mod.moe_sort_by_expert(T, K, E, torch.zeros(T * K, dtype=i32), torch.zeros(E + 1, dtype=i32),
+                                   torch.zeros(E + 1, dtype=i32), torch.zeros(T * K, dtype=i32))
+    with pytest.raises(ValueError, match="gain holds"):
+        lib_mod.moe_rmsnorm(T, d, torch.zeros(T * d, dtype=f16), torch.zeros(d - 1, dtype=f16),
+                            torch.zeros(T * d, dtype=f16))
