@@ -51,3 +51,30 @@ def test_stored_traffic_follows_the_sources(tmp_path, monkeypatch):
     assert b.stored_traffic() is None
     monkeypatch.setattr(b, "TRAFFIC_RECORD", str(tmp_path / "missing.json"))
     assert b.stored_traffic() is None
+
+
+def test_record_carries_the_contract_keys():
+    import argparse
+    import moe_synth as S
+    b = _bench()
+    cfg = S.CONFIGS["decode35b"]
+    rec = b.base_record(argparse.Namespace(warmup=60), cfg, 2750.0, 600 / 2750.0, 600)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+              "vs_baseline", "dtype", "data", "config"):
+        assert k in rec
+    assert rec["n_gpus"] == 1 and rec["higher_is_better"] is True and rec["vs_baseline"] is None
+    assert rec["config"]["workload"].startswith("decode35b")
+    assert abs(rec["ms_per_step"] - 1e3 / 2750.0) < 1e-3
+
+
+def test_roofline_and_algorithmic_bytes():
+    import moe_synth as S
+    b = _bench()
+    total, expert_only = b.algorithmic_bytes(S.CONFIGS["decode35b"])
+    # 40 layers of 4 experts, 39 heads, the layer-0 router and the float16 in/out vectors of every layer
+    assert total == 40 * 4 * 1_769_472 + 39 * 5_790_720 + 256 * 2048 * 2 + 40 * 2 * 2048 * 2 == 510_329_856
+    assert expert_only == 40 * (4 * 1_769_472 + 2 * 2048 * 2)
+    r = b.roofline("k", total, 362.0, None)
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - total / 362e-6 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
