@@ -21,9 +21,11 @@ full-softmax probabilities of the selected experts); the two routing vectors of
 the prerouter are binary K-hot vectors of the head's own layer at tokens t and
 t-1 (zero at t = 0), concatenated after the hidden state.
 
-Parity pins: see tests/test_oracle_pins.py.  Chain semantics (which routing
-vectors feed the head, bootstrap at the first token) are parity unpinned: no
-worked example exists on the pages.
+Parity pins: see tests/test_oracle_pins.py.  The pages print no worked example of
+the prerouted chain; its semantics (which routing vectors feed the head, where
+the prediction lands, the first-token bootstrap, self-routing after a layer
+without a head) are pinned by a stack worked by hand from the readings above
+(tests/golden/prerouted_chain_hand.txt).
 """
 from __future__ import annotations
 

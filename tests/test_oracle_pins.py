@@ -10,6 +10,7 @@ import pytest
 import scipy.special
 
 import oracle as O
+import golden_io
 from golden_io import read_fixture
 from moe_synth import CONFIGS, Synth
 
@@ -248,6 +249,18 @@ def _rand_head(d, E, H):
             "lin_x": RNG.normal(size=(E, d)), "lin_r": RNG.normal(size=(2 * E, E)), "lin_b": RNG.normal(size=E)}
 
 
+def test_router_on_basis_vectors_returns_columns():
+    """logits = W_r x with x = e_j is column j of W_r, exactly (catches a transposed router)."""
+    E, d = 16, 32
+    W = RNG.normal(size=(E, d)).astype(np.float16)
+    for j in (0, 7, 31):
+        x = np.zeros(d)
+        x[j] = 1.0
+        assert O.router_logits(W, x).tolist() == W[:, j].astype(np.float64).tolist()
+    X = np.eye(d)[[3, 9]]
+    np.testing.assert_array_equal(O.router_logits(W, X), W[:, [3, 9]].T.astype(np.float64))
+
+
 def test_prerouter_reduces_to_router():
     d, E, H, K = 32, 16, 8, 2
     pw = _rand_head(d, E, H)
@@ -320,6 +333,83 @@ def test_chain_single_layer_is_routed_layer():
     y = O.moe_layer(x, h, idx, w, get, cfg.bits, cfg.group)
     np.testing.assert_array_equal(hL, O.to_f16_f64(y[0]))
     assert st2.prev[0].tolist() == idx[0].tolist()
+
+
+def _hand_chain_stack(fx):
+    """The hand-worked stack of prerouted_chain_hand.txt: zero experts, permutation routers,
+    heads that read only the two K-hot vectors."""
+    d, E, I, H, bits = fx["d"], fx["E"], fx["d_ff"], fx["H"], fx["bits"]
+    zero_up = (np.zeros((I, d * bits // 32), np.uint32), np.zeros((I, d // fx["group"]), np.float16),
+               np.zeros((I, d // fx["group"]), np.float16))
+    zero_dn = (np.zeros((d, I * bits // 32), np.uint32), np.zeros((d, I // fx["group"]), np.float16),
+               np.zeros((d, I // fx["group"]), np.float16))
+
+    def head_get(l):
+        if l not in fx["heads"]:
+            return None
+        return {"fc1_x": np.zeros((H, d), np.float16), "fc1_r": np.zeros((2 * E, H), np.float16), "fc1_b": None,
+                "fc2": np.zeros((E, H), np.float16), "fc2_b": None, "lin_x": np.zeros((E, d), np.float16),
+                "lin_r": fx["lin_r"][l], "lin_b": None}
+
+    return dict(E=E, K=fx["K"], bits=bits, group=fx["group"], router_get=lambda l: fx["router"][l],
+                head_get=head_get, expert_get=lambda l, e: (zero_up, zero_up, zero_dn))
+
+
+def test_prerouted_chain_hand_worked():
+    """Three tokens through the hand-worked 4-layer stack: which routing each layer uses (own
+    router at t = 0, after a head-less layer and at layer 0; else the head of layer l-1 at t-1),
+    the head's current / previous K-hot inputs, and where its prediction lands (layer l+1, token
+    t+1).  Each of these slips changes an expected line: a prediction stored for layer l instead
+    of l+1, the two K-hot vectors swapped, the previous-token vector filled at t = 0, the next
+    layer's routing fed to the head, a layer after a head-less layer not routing itself."""
+    fx = golden_io.hand_chain()
+    kw = _hand_chain_stack(fx)
+    r = math.sqrt(np.mean(fx["h"][0].astype(np.float64) ** 2) + O.RMS_EPS)
+    st = O.ChainState(fx["L"])
+    prev_idx = [None] * fx["L"]
+    for t in range(fx["h"].shape[0]):
+        h = fx["h"][t]
+        hL, new, tr = O.chain_token(h, st, **kw)
+        for l in range(fx["L"]):
+            src, idx, w = fx["route"][(t, l)]
+            assert tr[l].idx.tolist() == idx, (t, l)
+            np.testing.assert_allclose(tr[l].w, w, rtol=0, atol=1e-15)
+            assert (tr[l].route_logits is not None) == (src == "router"), (t, l)
+            if src == "router":
+                np.testing.assert_allclose(tr[l].route_logits, np.array(fx["router_num"][(t, l)]) / r, rtol=1e-15)
+            np.testing.assert_array_equal(tr[l].y, h.astype(np.float64))  # zero experts: y = h
+            if l in fx["heads"]:
+                cur, prev = fx["head_in"][(t, l)]
+                assert sorted(cur) == sorted(idx) and prev == prev_idx[l], (t, l)
+                np.testing.assert_array_equal(tr[l].head_logits, fx["head_logits"][(t, l)])
+                pidx, pw = fx["pred"][(t, l + 1)]
+                assert new.pred[l + 1][0].tolist() == pidx, (t, l)
+                np.testing.assert_allclose(new.pred[l + 1][1], pw, rtol=0, atol=1e-15)
+            else:
+                assert tr[l].head_logits is None and (l + 1 >= fx["L"] or new.pred[l + 1] is None)
+            prev_idx[l] = idx
+        assert new.pred[0] is None
+        np.testing.assert_array_equal(hL, h.astype(np.float64))
+        st = new
+
+
+def test_chain_threads_layer_outputs():
+    """Three head-less layers: the chain equals three routed layers applied in turn, each on
+    rmsnorm of the float16-rounded output of the one before (every layer routes itself)."""
+    cfg, syn, get = _tiny_layer()
+    h = syn.hidden(5, 1)[0].numpy()
+    routers = [syn.router(0).numpy(), syn.router(0).numpy()[::-1].copy(), -syn.router(0).numpy()]
+    hL, _, tr = O.chain_token(h, O.ChainState(3), E=cfg.E, K=cfg.K, bits=cfg.bits, group=cfg.group,
+                              router_get=lambda l: routers[l], head_get=lambda l: None,
+                              expert_get=lambda l, e: get(e))
+    cur = O.f64(h)
+    for l in range(3):
+        x = O.rmsnorm(cur)
+        idx, w = O.route_topk(O.router_logits(routers[l], x)[None], cfg.K)
+        assert tr[l].idx.tolist() == idx[0].tolist()
+        cur = O.to_f16_f64(O.moe_layer(x, cur, idx, w, get, cfg.bits, cfg.group)[0])
+        np.testing.assert_array_equal(tr[l].y, cur)
+    np.testing.assert_array_equal(hL, cur)
 
 
 # ------------------------------------------------------------------ ReLU activation-sparse expert
