@@ -308,6 +308,78 @@ def routing_histogram(cfg, layers, syn, torch, dev, tokens=1024):
             "note": "routing the full path chose (layer 0 and the first token self-routed, the rest as the stack routes)"}
 
 
+def exchange_probe(M, torch, dev, words):
+    """The committed exchange-latency probe (moe_exchange_probe): one workgroup per compute unit.
+    ring: one tagged word passed workgroup to workgroup (consecutive workgroups sit on different
+    XCDs), the latency of one dependent hand-off; all: every workgroup publishes its slice of a
+    `words`-word vector and polls it whole, phase after phase (the shape of the decode kernel's
+    exchanges), the period of such an exchange loop."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(1 + 3 * cus, dtype=torch.int32, device=dev)
+    res = {}
+    for name, pat, gs, w, it in (("ring_hop_us", M.MOE_XCHG_RING, 8, 0, 200),
+                                 ("all_exchange_us", M.MOE_XCHG_ALL, cus, words, 200)):
+        cfg = M.moe_xchg_cfg(pat, cus, gs, 0, w, it, M.MOE_XCHG_SCOPE_DEVICE, M.MOE_XCHG_SCOPE_DEVICE, 1, 1, 0)
+        ws = torch.zeros(M.moe_exchange_probe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+        vals = []
+        for rep in range(3):
+            cfg.epoch = rep + 1
+            out.zero_()
+            M.moe_exchange_probe(cfg, ws, out)
+            torch.cuda.synchronize()
+            o = out.cpu().numpy().view("uint32").astype("int64")
+            assert o[0] == 0, "a wait of the exchange probe ran out of time"
+            ticks = o[1::3] | (o[2::3] << 32)
+            if pat == M.MOE_XCHG_RING:
+                vals.append(float(ticks[0::gs].max()) / 100.0 / (it * gs))   # member 0 of each ring
+            else:
+                vals.append(float(ticks.max()) / 100.0 / it)
+        res[name] = round(sorted(vals)[1], 3)
+    res["workgroups"] = cus
+    res["words"] = words
+    return res
+
+
+def phase_breakdown(layers, cfg, syn, torch, dev, M, tokens=12, warm=20):
+    """Per-layer time split of the persistent kernel from its phase stamps (moe_decode_step_stamped,
+    the global 100 MHz counter): medians over workgroups and over the inner layers of the last
+    `tokens` tokens.  h_exchange / act_exchange: from the last workgroup's store of the vector to
+    the median workgroup having all of it; gate_up: h seen -> SwiGLU outputs stored (median);
+    store_spread: median -> last workgroup storing; act_to_down: all SwiGLU outputs in -> down
+    phase starts; down: down phase -> layer output stored."""
+    import numpy as np
+    from int4_expert_ffn_amd.chain import DecodeStack
+    stack = DecodeStack(layers, cfg.K, dev)
+    G = stack.grid()
+    st = torch.zeros((G, cfg.L, 8), dtype=torch.int64, device=dev)
+    hs = syn.hidden(17, warm + tokens, dev)
+    rows, tok_us = [], []
+    for t in range(warm + tokens):
+        stack.step(t, hs[t], stamps=st if t >= warm else None)
+        if t >= warm:
+            torch.cuda.synchronize()
+            a = st.cpu().numpy().astype(np.float64) / 100.0
+            tok_us.append(float(a[:, -1, 6].max() - a[:, 0, 0].min()))
+            for l in range(1, cfg.L - 1):
+                s, pv, nx = a[:, l, :], a[:, l - 1, :], a[:, l + 1, :]
+                med = lambda v: float(np.median(v))
+                rows.append({
+                    "h_exchange": med(s[:, 1]) - pv[:, 6].max(),
+                    "gate_up": med(s[:, 4]) - med(s[:, 3]),
+                    "act_store_spread": s[:, 4].max() - med(s[:, 4]),
+                    "act_exchange": med(s[:, 2]) - s[:, 4].max(),
+                    "act_to_down": med(s[:, 5]) - med(s[:, 2]),
+                    "down": med(s[:, 6]) - med(s[:, 5]),
+                    "h_store_spread": s[:, 6].max() - med(s[:, 6]),
+                    "layer": med(nx[:, 1]) - med(s[:, 1]),
+                })
+    assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time (stamped)"
+    out = {k: round(float(np.median([r[k] for r in rows])), 3) for k in rows[0]}
+    out["token_us"] = round(float(np.median(tok_us)), 1)
+    out["layers_used"] = f"1..{cfg.L - 2} (inner layers), {tokens} tokens"
+    return out
+
+
 def bench_stack(args, cfg, torch, M, S, dev):
     """A resident L-layer stack at batch 1: the timed step is one moe_decode_step launch per token
     (the persistent kernel running every layer); the expert FFN steps alone and the per-layer
@@ -440,6 +512,10 @@ def bench_stack(args, cfg, torch, M, S, dev):
     del buf
 
     hist = routing_histogram(cfg, layers, syn, torch, dev) if not args.no_histogram else None
+    phases = xprobe = None
+    if not args.no_phases:
+        phases = phase_breakdown(layers, cfg, syn, torch, dev, M)
+        xprobe = exchange_probe(M, torch, dev, cfg.d // 2)
 
     tok_s = args.steps / wall
     rec = base_record(args, cfg, tok_s, wall, args.steps)
@@ -457,6 +533,18 @@ def bench_stack(args, cfg, torch, M, S, dev):
     rec["roofline"]["measured_read_ceiling_GBps"] = round(read_ceiling, 1)
     rec["roofline"]["frac_of_measured_ceiling"] = round(rec["roofline"]["achieved"] / read_ceiling, 4)
     rec["cold"] = cold
+    if phases is not None:
+        floor = xprobe["ring_hop_us"]
+        rec["roofline"]["exchange_floor_us"] = floor
+        rec["roofline"]["latency_roof_us"] = round(cfg.L * 2 * floor, 1)
+        rec["roofline"]["exchange_bound_us"] = round(cfg.L * (phases["h_exchange"] + phases["act_exchange"]), 1)
+        rec["latency"] = {
+            "phases_per_layer_us": phases, "exchange_probe": xprobe,
+            "note": "exchange_floor_us: one dependent hand-off of a tagged word across XCDs (the probe's ring); "
+                    "latency_roof_us = layers x 2 exchanges x that floor; exchange_bound_us = layers x (h + act "
+                    "exchange as measured inside the kernel), the token time the two exchanges per layer take at "
+                    "zero compute",
+        }
     rec["repeats"] = {"tokens_per_s": [round(v, 2) for v in reps], "median": round(sorted(reps)[len(reps) // 2], 2),
                       "note": f"{len(reps)} runs of the same {args.steps} timed tokens, the first being `value`"}
     rec["routing_histogram"] = hist
@@ -882,6 +970,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true", help="skip the per-layer-calls context timing")
     ap.add_argument("--no-expert-only", action="store_true", help="skip the expert-FFN-only timing")
+    ap.add_argument("--no-phases", action="store_true",
+                    help="stack workloads: skip the stamped phase breakdown and the exchange probe")
     ap.add_argument("--norm-gain", action="store_true",
                     help="stack workloads: every layer input normalised with a per-layer gain (x = g * h / rms(h))")
     ap.add_argument("--eager", action="store_true",

@@ -244,6 +244,41 @@ moe_status moe_stream_in_many(void* stream, int32_t n, int32_t K, const moe_stre
 #define MOE_READ_PROBE_BLOCKS 4096
 moe_status moe_read_probe(void* stream, const void* buf, size_t bytes, uint32_t* out);
 
+/* Measurement aid, not a step of the method: the latency of handing tagged 8-byte words between
+   resident workgroups, the unit of every grid-wide exchange inside moe_decode_step.  n_wg
+   workgroups of one wave each, one per compute unit, run `iters` phases of `pattern`:
+     MOE_XCHG_ALL  : in every phase each member of a group stores words/group_size words of a
+                     vector and then polls all `words` of it until each carries the phase's tag;
+     MOE_XCHG_RING : one word is passed member to member, `iters` laps of the group.
+   Groups: group_size consecutive workgroup numbers (xcd_local 0), or the workgroups b with equal
+   b % (n_wg / group_size) (xcd_local 1; the dispatcher deals workgroups round robin over the 8
+   XCDs, so each such group runs on one XCD when n_wg / group_size is a multiple of 8).
+   load_scope / store_scope: MOE_XCHG_SCOPE_DEVICE (device-coherent: what crossing XCDs needs) or
+   MOE_XCHG_SCOPE_XCD (loads bypass only the L1 and stores end in the XCD's L2: enough inside one
+   XCD).  Every wait is bounded (0.1 s); one that runs out adds 1 to out[0] and the grid finishes.
+   out (uint32, device, 1 + 3 n_wg words): out[0] += waits that ran out (zero it first); for
+   workgroup b, out[1+3b] / out[2+3b] = low / high word of the real-time-counter ticks (100 MHz)
+   from the common start to its end, out[3+3b] = the XCD it ran on.  workspace:
+   moe_exchange_probe_workspace_size bytes, 256-byte aligned, zeroed once before the first call;
+   `epoch` must differ between consecutive calls on one workspace (it tags the words).
+   Limits: 1 <= n_wg <= compute units; group_size divides n_wg; ALL: words a multiple of
+   group_size, words / group_size <= 64, words <= 16384; 1 <= iters <= 32767 (ALL) or
+   iters * group_size <= 65535 (RING).  MOE_ERR_INVALID_ARG otherwise (nothing enqueued). */
+#define MOE_XCHG_ALL 0
+#define MOE_XCHG_RING 1
+#define MOE_XCHG_SCOPE_DEVICE 0
+#define MOE_XCHG_SCOPE_XCD 1
+typedef struct {
+  int32_t pattern, n_wg, group_size, xcd_local, words, iters, load_scope, store_scope;
+  uint32_t epoch;
+  int32_t replicas; /* ALL: each word is stored in `replicas` copies (1..8) and workgroup b reads copy
+                       b % replicas (with 8, the copy of its XCD), which spreads the readers' traffic */
+  int32_t wide_loads; /* ALL: 1 = poll with 16-byte loads (two words per lane per load), 0 = 8-byte */
+} moe_xchg_cfg;
+size_t moe_exchange_probe_workspace_size(const moe_xchg_cfg* cfg);
+moe_status moe_exchange_probe(void* stream, const moe_xchg_cfg* cfg, void* workspace, size_t workspace_bytes,
+                              uint32_t* out);
+
 /* Grouping used by the batched path (tokens sorted by expert): a stable counting sort of the T*K
    (token, slot) pairs.  counts[E+1] and offsets[E+2] (int32, out): bucket E collects pairs whose
    index lies outside [0, E); perm[T*K] (int32, out) lists flat pair indices t*K + k grouped by
@@ -323,6 +358,24 @@ size_t moe_decode_workspace_size(const moe_decode_stack* st);
 moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
                            const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
                            size_t workspace_bytes);
+
+/* Workgroups one moe_decode_step launch of this stack runs on the current device (one per compute
+   unit that holds a slice of the rows), or 0 if the stack is not supported by it. */
+int32_t moe_decode_step_grid(const moe_decode_stack* st);
+
+/* Measurement aid, not a step of the method: moe_decode_step that also writes phase stamps of the
+   device's 100 MHz real-time counter (one clock for every compute unit, so stamps of different
+   workgroups compare).  stamps: uint64 [G][L][8] (device, 8-byte aligned, stamp_bytes >=
+   G * L * 64, G = moe_decode_step_grid(st)); slot s of (workgroup g, layer l):
+     0 the layer starts in g's polling wave, 1 g has unpacked the layer's input h_l,
+     2 g has unpacked all SwiGLU outputs of the layer, 3 g's first compute wave sees h_l,
+     4 g's SwiGLU outputs are stored, 5 g's down phase starts, 6 g's rows of the layer's output
+     are stored, 7 g's first compute wave has finished its head rows of the layer.
+   Results and every other argument as moe_decode_step.  This call runs a variant of the kernel with
+   the stamp stores compiled in (a little slower); moe_decode_step runs the variant without them. */
+moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
+                                   const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, uint64_t* stamps,
+                                   size_t stamp_bytes, void* workspace, size_t workspace_bytes);
 
 const char* moe_status_string(moe_status s);
 

@@ -26,7 +26,8 @@ EXPORTS = (
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_q4", "moe_combine", "moe_rmsnorm", "moe_sort_by_expert",
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
-    "moe_stream_in_many", "moe_read_probe",
+    "moe_stream_in_many", "moe_read_probe", "moe_exchange_probe_workspace_size", "moe_exchange_probe",
+    "moe_decode_step_grid", "moe_decode_step_stamped",
 )
 
 
@@ -72,6 +73,13 @@ class moe_stream_job(ctypes.Structure):
                 ("pool", ctypes.POINTER(moe_pool)), ("idx_slot", ctypes.c_void_p), ("counters", ctypes.c_void_p)]
 
 
+class moe_xchg_cfg(ctypes.Structure):
+    _fields_ = [("pattern", ctypes.c_int32), ("n_wg", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("xcd_local", ctypes.c_int32), ("words", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("load_scope", ctypes.c_int32), ("store_scope", ctypes.c_int32), ("epoch", ctypes.c_uint32),
+                ("replicas", ctypes.c_int32), ("wide_loads", ctypes.c_int32)]
+
+
 class moe_decode_stack(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
@@ -103,12 +111,16 @@ def _load():
                                ctypes.POINTER(moe_pool), vp, vp, vp, sz]),
         "moe_stream_in_many": (st, [vp, i32, i32, ctypes.POINTER(moe_stream_job), vp, sz]),
         "moe_read_probe": (st, [vp, vp, sz, vp]),
+        "moe_exchange_probe_workspace_size": (sz, [ctypes.POINTER(moe_xchg_cfg)]),
+        "moe_exchange_probe": (st, [vp, ctypes.POINTER(moe_xchg_cfg), vp, sz, vp]),
         "moe_combine": (st, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_rmsnorm": (st, [vp, i32, i32, vp, vp, vp]),
         "moe_sort_by_expert": (st, [vp, i32, i32, i32, vp, vp, vp, vp]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_decode_workspace_size": (sz, [ctypes.POINTER(moe_decode_stack)]),
         "moe_decode_step": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, vp, sz]),
+        "moe_decode_step_grid": (i32, [ctypes.POINTER(moe_decode_stack)]),
+        "moe_decode_step_stamped": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, vp, sz, vp, sz]),
         "moe_version": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -384,6 +396,26 @@ def moe_read_probe(buf, out, stream=None):
     _check(st, "moe_read_probe")
 
 
+MOE_XCHG_ALL, MOE_XCHG_RING = 0, 1
+MOE_XCHG_SCOPE_DEVICE, MOE_XCHG_SCOPE_XCD = 0, 1
+
+
+def moe_exchange_probe_workspace_size(cfg: moe_xchg_cfg) -> int:
+    return _lib.moe_exchange_probe_workspace_size(ctypes.byref(cfg))
+
+
+def moe_exchange_probe(cfg: moe_xchg_cfg, workspace, out, stream=None):
+    """Tagged-word hand-off probe (measurement aid).  workspace: uint8 device tensor of
+    moe_exchange_probe_workspace_size(cfg) bytes, zeroed once; out: int32 [1 + 3 n_wg] device tensor
+    with out[0] zeroed (waits that ran out are added there)."""
+    if out.numel() < 1 + 3 * cfg.n_wg:
+        raise ValueError(f"moe_exchange_probe: out needs {1 + 3 * cfg.n_wg} int32 words")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.moe_exchange_probe(_stream(stream, workspace, out), ctypes.byref(cfg), _ptr(workspace, None, "workspace"),
+                                 nbytes, _ptr(out, _i32(), "out"))
+    _check(st, "moe_exchange_probe")
+
+
 def moe_stream_in_many(K, jobs, workspace, workspace_bytes=None, stream=None):
     """jobs: sequence of (idx, src Experts, Pool, idx_slot, counters or None), at most MOE_POOL_MAX_JOBS,
     distinct pools of one shape; workspace of len(jobs) * moe_stream_workspace_size(K) bytes."""
@@ -441,6 +473,21 @@ def moe_decode_step(stack: "moe_decode_stack", token, flags, h_in, h_out, worksp
                               _ptr(h_out, _f16(), "h_out"), _ptr(h_layers, _f16(), "h_layers"),
                               _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_decode_step")
+
+
+def moe_decode_step_grid(stack: "moe_decode_stack") -> int:
+    return _lib.moe_decode_step_grid(ctypes.byref(stack))
+
+
+def moe_decode_step_stamped(stack: "moe_decode_stack", token, flags, h_in, h_out, stamps, workspace,
+                            workspace_bytes=None, stream=None, h_layers=None):
+    """moe_decode_step writing phase stamps into `stamps` (int64 device tensor, [G][L][8])."""
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_decode_step_stamped(_stream(stream, h_in, h_out), ctypes.byref(stack), token, flags,
+                                      _ptr(h_in, _f16(), "h_in"), _ptr(h_out, _f16(), "h_out"),
+                                      _ptr(h_layers, _f16(), "h_layers"), _ptr(stamps, None, "stamps"),
+                                      stamps.numel() * stamps.element_size(), _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_decode_step_stamped")
 
 
 def moe_version() -> int:

@@ -27,10 +27,7 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,6 +36,26 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source to an object in _build/ (in parallel), then link libmoe.so."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs, cmds = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *compile_flags, *inc, "-c", src, "-o", obj])
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as pool:
+        list(pool.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -91,16 +91,25 @@ class DecodeStack:
         return self._step
 
     def step(self, t: int, h_in: torch.Tensor, h_out: Optional[torch.Tensor] = None,
-             h_layers: Optional[torch.Tensor] = None, given_routing: bool = False):
+             h_layers: Optional[torch.Tensor] = None, given_routing: bool = False,
+             stamps: Optional[torch.Tensor] = None):
         """Enqueue token t as one persistent-kernel launch reading h_in [d] and writing h_out
         (default: self.h[L]); h_layers [L+1][d] float16, if given, receives every layer's input and
         the output.  given_routing: the expert FFN steps alone, every layer routed by what the
-        caller wrote into route_idx / route_w slot t % 3 (see set_routing).  Returns h_out."""
+        caller wrote into route_idx / route_w slot t % 3 (see set_routing).  stamps: an int64
+        tensor [G][L][8] (G = grid()) that receives the kernel's phase stamps.  Returns h_out."""
         desc, st, ws = self._step_state()
         out = self.h[self.L] if h_out is None else h_out
         flags = self.topk_flags | (L.MOE_DECODE_GIVEN_ROUTING if given_routing else 0)
-        L.moe_decode_step(st, t, flags, h_in, out, ws, h_layers=h_layers)
+        if stamps is None:
+            L.moe_decode_step(st, t, flags, h_in, out, ws, h_layers=h_layers)
+        else:
+            L.moe_decode_step_stamped(st, t, flags, h_in, out, stamps, ws, h_layers=h_layers)
         return out
+
+    def grid(self) -> int:
+        """Workgroups of one persistent-kernel launch of this stack (0: not supported)."""
+        return L.moe_decode_step_grid(self._step_state()[1])
 
     def set_routing(self, t: int, idx: torch.Tensor, w: torch.Tensor):
         """Write every layer's experts idx [L][K] (int32, distinct per layer, in [0, E)) and weights

@@ -71,6 +71,7 @@ struct StepParams {
   const uint16_t* zero16;  // a float16 zero (stands in for an absent bias)
   const void* ws;          // the workspace (base of the tagged-word buffers)
   uint32_t ws_bytes;
+  uint64_t* stamps;        // NULL or [G][L][NSTAMP] real-time-counter stamps (measurement aid)
 };
 
 
@@ -90,6 +91,20 @@ constexpr int CPOL_SC1 = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Phase stamps (measurement aid, the kernel variant with STAMP set): slot `slot` of (workgroup,
+// layer) receives the 100 MHz real-time counter, stored by lane 0 of the calling wave when `on`.
+//   poll wave:      0 layer start, 1 h_l unpacked, 2 SwiGLU outputs of the layer unpacked
+//   compute wave 1: 3 h_l seen (after the barrier), 4 this workgroup's SwiGLU outputs stored,
+//                   5 down phase starts, 6 this workgroup's rows of h_{l+1} stored, 7 head rows done
+// The plain variant compiles every stamp away.
+constexpr int NSTAMP = 8;
+template <bool STAMP>
+__device__ __forceinline__ void stamp(const StepParams& p, int wg, int l, int slot, bool on = true) {
+  if constexpr (STAMP) {
+    const uint64_t t = __builtin_amdgcn_s_memrealtime();
+    if (on && threadIdx.x % WAVE == 0) p.stamps[((size_t)wg * p.L + l) * NSTAMP + slot] = t;
+  }
 }
 __device__ __forceinline__ void ll_put64(__amdgpu_buffer_rsrc_t ws, const StepParams& p, const uint64_t* vec, size_t i,
                                          bool on, uint64_t word) {
@@ -495,13 +510,14 @@ __device__ __forceinline__ void put_act(StepShared& sm, int n, float f) {
 
 // Wave 0 of every workgroup: waits for the vectors each phase needs and unpacks them into LDS.
 // GW0: 32-bit words of a d-row per lane (d = NSH 64 lanes x 8 halves).
-template <int BITS, int GW0>
+template <int BITS, int GW0, bool STAMP>
 __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   const int lane = c.lane, dh = p.d / 2;
   bool failed = false;
   for (int l = 0; l < p.L; ++l) {
     const int hb = l & 1;
     uint32_t* hw = reinterpret_cast<uint32_t*>(sm.h[hb]);
+    stamp<STAMP>(p, c.wg, l, 0);
     // (the RMS norm of h_l is taken by the compute waves from their own reads of it, in a fixed
     // order; summed here, as the words arrive, it would depend on their arrival order)
     if (l == 0) {
@@ -512,6 +528,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed,
               [&](int i, uint32_t v) { hw[i] = v; });
     }
+    stamp<STAMP>(p, c.wg, l, 1);
     lds_barrier();  // B1: h_l ready
     if (p.gained) lds_barrier();  // B1g: gain * h_l formed
     if (self_routed(p, l)) {
@@ -535,6 +552,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
       sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
     });
+    stamp<STAMP>(p, c.wg, l, 2);
     lds_barrier();  // B3: act ready
     lds_barrier();  // B3b: act split into hi/lo pairs (by the compute waves)
     lds_barrier();  // B4: partial down sums ready (the combine runs in wave 1)
@@ -565,7 +583,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
 }
 
 // Waves 1..MW: the arithmetic, with each phase's weight loads issued one phase early.
-template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH, bool STAMP>
 __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   using GS = SegT<BITS>;
   const int lane = c.lane, cw = c.cw, wg = c.wg, dh = p.d / 2, K = p.K;
@@ -616,6 +634,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     const bool prefetch = l + 1 < p.L && !self_routed(p, l + 1);
     const int hb = l & 1;
     lds_barrier();  // B1
+    stamp<STAMP>(p, wg, l, 3, cw == 0);
     float scale;  // 1 / rms(h_l), from this wave's own reads of h_l (a fixed summation order)
     const uint16_t* hl = sm.h[hb];
     // a layer with a norm gain: the gate/up dot products take g * h as float16 pairs, formed here
@@ -729,6 +748,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           const uint64_t w = (uint64_t)f32_to_f24(sm.aout[2 * j]) | ((uint64_t)f32_to_f24(sm.aout[2 * j + 1]) << 24) |
                              ((uint64_t)c.tag16(3 * l + 1) << 48);
           ll_put64(ws, p, p.ll_act, min(word, p.K * p.I / 2 - 1), lane < MW * GU / 2 && 2 * word < p.K * p.I, w);
+          stamp<STAMP>(p, wg, l, 4);
         }
       }
       // first half of this layer's head: fc1 rows (+GELU, sent) and the linear row (kept)
@@ -792,6 +812,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
                c.tag(3 * (l - 1) + 2));
       }
       lin_keep = lin_keep_next;
+      stamp<STAMP>(p, wg, l, 7, cw == 0);
     }
     if (l + 1 < p.L) stage_gain(l + 1);  // while the act exchange runs; its loads go before the prefetch's
     if (prefetch)  // gate/up weights of A_{l+1}, one phase early
@@ -800,6 +821,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
     // split act into float16 hi/lo pairs once per workgroup, every compute lane a few values
     for (int n = cw * WAVE + lane; n < K * p.I; n += MW * WAVE) put_act<BITS>(sm, n, sm.act_f[n]);
     lds_barrier();  // B3b
+    stamp<STAMP>(p, wg, l, 5, cw == 0);
 
     // ---- B_l: down partials of this workgroup's rows ----
     {
@@ -854,6 +876,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         ll_put(ws, p, p.ll_h, (size_t)(l + 1) * dh + wg * (p.DR / 2) + m, lane < nrows / 2, lo | (hi << 16),
                c.tag(3 * l + 2));
       }
+      stamp<STAMP>(p, wg, l, 6);
     }
     // The head half of A_{l+1}'s weights (needed only after its SwiGLU outputs) goes out after the
     // combine: issued together with the gate/up half it slowed the act exchange that follows.
@@ -864,7 +887,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
   }
 }
 
-template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
+template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH, bool STAMP>
 __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   __shared__ __attribute__((aligned(16))) StepShared sm;
   StepCtx c;
@@ -888,11 +911,11 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
     }
   }
   if (wave == 0) {
-    sync_role<BITS, NSH * 4>(p, c, sm);
+    sync_role<BITS, NSH * 4, STAMP>(p, c, sm);
   } else {
     // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
     __builtin_amdgcn_s_setprio(2);
-    compute_role<BITS, PG, NSH, NSF, GU, PD, NH>(p, c, sm);
+    compute_role<BITS, PG, NSH, NSF, GU, PD, NH, STAMP>(p, c, sm);
   }
   if (c.wg == 0 && threadIdx.x == 0) *p.epoch = c.epoch + 1;
 }
@@ -975,7 +998,7 @@ static int device_cus() {
 template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH>
 static hipError_t go(hipStream_t s, const StepParams& p) {
   int occ = 0;
-  auto k = k_decode_step<BITS, PG, NSH, NSF, GU, PD, NH>;
+  auto k = p.stamps ? k_decode_step<BITS, PG, NSH, NSF, GU, PD, NH, true> : k_decode_step<BITS, PG, NSH, NSF, GU, PD, NH, false>;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, NTHREADS, 0);
   if (e != hipSuccess) return e;
   if (occ < 1) return hipErrorInvalidConfiguration;  // every workgroup must be resident at once
@@ -1008,12 +1031,17 @@ static hipError_t dispatch(hipStream_t s, const StepParams& p, int bits, int PG,
   return hipErrorInvalidValue;
 }
 
-bool decode_step_supported(const moe_decode_stack& st) { return plan_step(st, 256).ok; }
+bool decode_step_supported(const moe_decode_stack& st) { return plan_step(st, device_cus()).ok; }
 
 size_t decode_step_workspace(const moe_decode_stack& st) { return step_ws(st).total; }
 
+int decode_step_grid(const moe_decode_stack& st) {
+  const StepPlan pl = plan_step(st, device_cus());
+  return pl.ok ? pl.G : 0;
+}
+
 hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
-                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws) {
+                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws, uint64_t* stamps) {
   const int G = device_cus();
   const StepPlan pl = plan_step(st, G);
   if (!pl.ok) return hipErrorInvalidValue;
@@ -1064,6 +1092,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.zero16 = (const uint16_t*)(b + w.zero);
   p.ws = ws;
   p.ws_bytes = (uint32_t)w.total;
+  p.stamps = stamps;
   return dispatch(s, p, st.bits, pl.PG, pl.NSH, pl.NSF);
 }
 

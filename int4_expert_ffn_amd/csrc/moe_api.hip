@@ -324,6 +324,41 @@ moe_status moe_read_probe(void* stream, const void* buf, size_t bytes, uint32_t*
   return from_hip(launch_read_probe((hipStream_t)stream, buf, bytes, out));
 }
 
+static bool xchg_cfg_ok(const moe_xchg_cfg* c) {
+  if (!c) return false;
+  if (c->pattern != MOE_XCHG_ALL && c->pattern != MOE_XCHG_RING) return false;
+  if (c->load_scope != MOE_XCHG_SCOPE_DEVICE && c->load_scope != MOE_XCHG_SCOPE_XCD) return false;
+  if (c->store_scope != MOE_XCHG_SCOPE_DEVICE && c->store_scope != MOE_XCHG_SCOPE_XCD) return false;
+  if (c->xcd_local != 0 && c->xcd_local != 1) return false;
+  if (c->n_wg < 1 || c->group_size < 1 || c->n_wg % c->group_size) return false;
+  if (c->iters < 1) return false;
+  if (c->replicas < 1 || c->replicas > 8) return false;
+  if (c->wide_loads != 0 && c->wide_loads != 1) return false;
+  if (c->pattern == MOE_XCHG_ALL) {
+    if (c->words < c->group_size || c->words % c->group_size || c->words / c->group_size > 64 || c->words > 16384)
+      return false;
+    if (c->iters > 32767) return false;
+  } else if ((int64_t)c->iters * c->group_size > 65535) {
+    return false;
+  }
+  return true;
+}
+
+size_t moe_exchange_probe_workspace_size(const moe_xchg_cfg* cfg) {
+  return xchg_cfg_ok(cfg) ? xchg_probe_workspace(*cfg) : 0;
+}
+
+moe_status moe_exchange_probe(void* stream, const moe_xchg_cfg* cfg, void* workspace, size_t workspace_bytes,
+                              uint32_t* out) {
+  if (!xchg_cfg_ok(cfg) || !workspace || !out || ((uintptr_t)workspace & 255)) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < xchg_probe_workspace(*cfg)) return MOE_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (cfg->n_wg > cus) return MOE_ERR_INVALID_ARG;  // every workgroup must be resident at once
+  return from_hip(launch_xchg_probe((hipStream_t)stream, *cfg, workspace, out));
+}
+
 moe_status moe_sort_by_expert(void* stream, int32_t T, int32_t K, int32_t E, const int32_t* idx, int32_t* counts,
                               int32_t* offsets, int32_t* perm) {
   if (T < 1 || K < 1 || E < 1 || E > MOE_MAX_E || (int64_t)T * K > (1 << 24)) return MOE_ERR_INVALID_ARG;
@@ -336,9 +371,8 @@ size_t moe_decode_workspace_size(const moe_decode_stack* st) {
   return decode_step_workspace(*st);
 }
 
-moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
-                           const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
-                           size_t workspace_bytes) {
+static moe_status check_decode_step(const moe_decode_stack* st, int32_t token, uint32_t flags, const uint16_t* h_in,
+                                    uint16_t* h_out, uint16_t* h_layers, void* workspace, size_t workspace_bytes) {
   if (!st || !h_in || !h_out || !workspace || token < 0) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_TOPK_RENORM | MOE_DECODE_GIVEN_ROUTING)) return MOE_ERR_INVALID_ARG;
   if (st->norm_gains != 0 && st->norm_gains != 1) return MOE_ERR_INVALID_ARG;
@@ -353,7 +387,32 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
     return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < decode_step_workspace(*st)) return MOE_ERR_INVALID_ARG;
   if (!decode_step_supported(*st)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
+                           const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* workspace,
+                           size_t workspace_bytes) {
+  const moe_status c = check_decode_step(st, token, flags, h_in, h_out, h_layers, workspace, workspace_bytes);
+  if (c != MOE_OK) return c;
   return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace));
+}
+
+int32_t moe_decode_step_grid(const moe_decode_stack* st) {
+  if (!st || st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return 0;
+  if ((st->bits != 4 && st->bits != 2) || st->d_model < 1 || st->d_ff < 1 || st->d_hidden < 0) return 0;
+  return decode_step_grid(*st);
+}
+
+moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,
+                                   const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, uint64_t* stamps,
+                                   size_t stamp_bytes, void* workspace, size_t workspace_bytes) {
+  const moe_status c = check_decode_step(st, token, flags, h_in, h_out, h_layers, workspace, workspace_bytes);
+  if (c != MOE_OK) return c;
+  const int G = decode_step_grid(*st);
+  if (!stamps || ((uintptr_t)stamps & 7u) || G < 1 || stamp_bytes < (size_t)G * st->L * 8 * sizeof(uint64_t))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace, stamps));
 }
 
 moe_status moe_rmsnorm(void* stream, int32_t T, int32_t d, const uint16_t* h, const uint16_t* gain, uint16_t* x) {

@@ -80,7 +80,9 @@ size_t grouped_tiles_bytes(int T, int K, int E);
 bool decode_step_supported(const moe_decode_stack& st);
 size_t decode_step_workspace(const moe_decode_stack& st);
 hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int token, uint32_t flags,
-                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws);
+                              const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws,
+                              uint64_t* stamps = nullptr);
+int decode_step_grid(const moe_decode_stack& st);  // workgroups of one launch (0: unsupported)
 
 // expert streaming into an HBM pool --------------------------------------------------------------
 struct PoolArgs {
@@ -103,6 +105,9 @@ size_t pool_plan_bytes(int K);
 
 // measurement aid: streaming read of a buffer (MOE_READ_PROBE_BLOCKS words out)
 hipError_t launch_read_probe(hipStream_t s, const void* buf, size_t bytes, uint32_t* out);
+// measurement aid: tagged-word hand-off latency between resident workgroups
+size_t xchg_probe_workspace(const moe_xchg_cfg& c);
+hipError_t launch_xchg_probe(hipStream_t s, const moe_xchg_cfg& c, void* ws, uint32_t* out);
 
 // combine -------------------------------------------------------------------------------------
 hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const uint16_t* gain, uint16_t* x);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 22
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -256,3 +256,23 @@ def test_binding_rejects_short_tensors():
     with pytest.raises(ValueError, match="gain holds"):
         lib_mod.moe_rmsnorm(T, d, torch.zeros(T * d, dtype=f16), torch.zeros(d - 1, dtype=f16),
                             torch.zeros(T * d, dtype=f16))
+
+
+def test_exchange_probe_rejects():
+    """Every configuration outside the header's limits is refused before anything is enqueued."""
+    good = dict(pattern=0, n_wg=256, group_size=256, xcd_local=0, words=1024, iters=100, load_scope=0,
+                store_scope=0, epoch=1, replicas=1, wide_loads=0)
+    cfg = lambda **k: lib_mod.moe_xchg_cfg(**{**good, **k})
+    assert L.moe_exchange_probe_workspace_size(ctypes.byref(cfg())) > 0
+    bad = [dict(pattern=2), dict(n_wg=0), dict(group_size=3), dict(words=1000), dict(words=256 * 65),
+           dict(iters=0), dict(iters=40000), dict(load_scope=2), dict(store_scope=-1), dict(xcd_local=2),
+           dict(pattern=1, group_size=8, iters=9000), dict(replicas=0), dict(replicas=9), dict(wide_loads=2)]
+    for b in bad:
+        c = cfg(**b)
+        assert L.moe_exchange_probe_workspace_size(ctypes.byref(c)) == 0, b
+        assert L.moe_exchange_probe(None, ctypes.byref(c), FAKE, 1 << 30, FAKE) == INVALID, b
+    c = cfg()
+    assert L.moe_exchange_probe(None, ctypes.byref(c), None, 1 << 30, FAKE) == INVALID
+    assert L.moe_exchange_probe(None, ctypes.byref(c), FAKE, 16, FAKE) == INVALID       # workspace too small
+    assert L.moe_exchange_probe(None, ctypes.byref(c), FAKE + 8, 1 << 30, FAKE) == INVALID  # not 256-aligned
+    assert L.moe_exchange_probe(None, None, FAKE, 1 << 30, FAKE) == INVALID

@@ -167,6 +167,36 @@ def test_decode_step_deterministic_and_mixable(M):
     assert a.step_error_word() == 0 and a2.step_error_word() == 0 and b.step_error_word() == 0
 
 
+@pytest.mark.parametrize("name", ["decode35b", "widek8"])
+def test_decode_step_stamped(M, name):
+    """moe_decode_step_stamped gives bit-identical outputs and routing to the plain launch, and its
+    phase stamps are ordered: inside a workgroup, layer start <= h_l unpacked <= h_l seen by the
+    compute waves <= SwiGLU outputs stored <= down phase <= layer output stored; across the grid,
+    no workgroup has h_{l+1} before the last workgroup stored its rows of it (a real exchange), and
+    none has all SwiGLU outputs before the last one stored its own."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = CASES[name]
+    syn, layers, _, _ = build(M, cfg, heads)
+    a, b = DecodeStack(layers, cfg.K, DEV), DecodeStack(layers, cfg.K, DEV)
+    G = a.grid()
+    assert G > 0
+    st = torch.zeros((G, cfg.L, 8), dtype=torch.int64, device=DEV)
+    for t in range(3):
+        h0 = syn.hidden(8300 + t, 1)[0].to(DEV)
+        ya = a.step(t, h0).clone()
+        yb = b.step(t, h0, stamps=st).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb) and torch.equal(a.route_idx[t % 3], b.route_idx[t % 3])
+        s = st.cpu().numpy()
+        assert (s > 0).all()
+        for x, y in ((0, 1), (1, 3), (3, 4), (4, 5), (2, 5), (5, 6)):
+            assert (s[:, :, y] >= s[:, :, x]).all(), (x, y)
+        for l in range(cfg.L - 1):
+            assert s[:, l + 1, 1].min() >= s[:, l, 6].max(), l
+        assert (s[:, :, 2].min(axis=0) >= s[:, :, 4].max(axis=0)).all()
+    assert a.step_error_word() == 0 and b.step_error_word() == 0
+
+
 def given_routing(syn, cfg, t):
     """Seeded routing for every layer of token t: the oracle's top-K (renormalised softmax) of N(0,1)
     logits, i.e. K distinct experts drawn uniformly per layer."""
