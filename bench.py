@@ -351,7 +351,7 @@ def phase_breakdown(layers, cfg, syn, torch, dev, M, tokens=12, warm=20):
     from int4_expert_ffn_amd.chain import DecodeStack
     stack = DecodeStack(layers, cfg.K, dev)
     G = stack.grid()
-    st = torch.zeros((G, cfg.L, 8), dtype=torch.int64, device=dev)
+    st = torch.zeros((G, cfg.L, 16), dtype=torch.int64, device=dev)
     hs = syn.hidden(17, warm + tokens, dev)
     rows, tok_us = [], []
     for t in range(warm + tokens):

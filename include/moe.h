@@ -365,12 +365,15 @@ int32_t moe_decode_step_grid(const moe_decode_stack* st);
 
 /* Measurement aid, not a step of the method: moe_decode_step that also writes phase stamps of the
    device's 100 MHz real-time counter (one clock for every compute unit, so stamps of different
-   workgroups compare).  stamps: uint64 [G][L][8] (device, 8-byte aligned, stamp_bytes >=
-   G * L * 64, G = moe_decode_step_grid(st)); slot s of (workgroup g, layer l):
+   workgroups compare).  stamps: uint64 [G][L][16] (device, 8-byte aligned, stamp_bytes >=
+   G * L * 128, G = moe_decode_step_grid(st)); slot s of (workgroup g, layer l):
      0 the layer starts in g's polling wave, 1 g has unpacked the layer's input h_l,
      2 g has unpacked all SwiGLU outputs of the layer, 3 g's first compute wave sees h_l,
      4 g's SwiGLU outputs are stored, 5 g's down phase starts, 6 g's rows of the layer's output
-     are stored, 7 g's first compute wave has finished its head rows of the layer.
+     are stored, 7 g's first compute wave has finished its head rows of the layer; finer marks of
+     the compute waves: 8 first wave's gate/up dot products done, 9 / 10 / 11 the SwiGLU output of
+     compute wave 1 / 4 / 2 ready, 12 the combine starts, 13 first wave's down dot products done,
+     14 / 15 down partials of compute wave 1 / 4 stored.
    Results and every other argument as moe_decode_step.  This call runs a variant of the kernel with
    the stamp stores compiled in (a little slower); moe_decode_step runs the variant without them. */
 moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,

@@ -481,7 +481,7 @@ def moe_decode_step_grid(stack: "moe_decode_stack") -> int:
 
 def moe_decode_step_stamped(stack: "moe_decode_stack", token, flags, h_in, h_out, stamps, workspace,
                             workspace_bytes=None, stream=None, h_layers=None):
-    """moe_decode_step writing phase stamps into `stamps` (int64 device tensor, [G][L][8])."""
+    """moe_decode_step writing phase stamps into `stamps` (int64 device tensor, [G][L][16])."""
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     st = _lib.moe_decode_step_stamped(_stream(stream, h_in, h_out), ctypes.byref(stack), token, flags,
                                       _ptr(h_in, _f16(), "h_in"), _ptr(h_out, _f16(), "h_out"),

@@ -97,7 +97,7 @@ class DecodeStack:
         (default: self.h[L]); h_layers [L+1][d] float16, if given, receives every layer's input and
         the output.  given_routing: the expert FFN steps alone, every layer routed by what the
         caller wrote into route_idx / route_w slot t % 3 (see set_routing).  stamps: an int64
-        tensor [G][L][8] (G = grid()) that receives the kernel's phase stamps.  Returns h_out."""
+        tensor [G][L][16] (G = grid()) that receives the kernel's phase stamps.  Returns h_out."""
         desc, st, ws = self._step_state()
         out = self.h[self.L] if h_out is None else h_out
         flags = self.topk_flags | (L.MOE_DECODE_GIVEN_ROUTING if given_routing else 0)

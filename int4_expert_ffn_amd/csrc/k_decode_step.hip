@@ -96,9 +96,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
 // layer) receives the 100 MHz real-time counter, stored by lane 0 of the calling wave when `on`.
 //   poll wave:      0 layer start, 1 h_l unpacked, 2 SwiGLU outputs of the layer unpacked
 //   compute wave 1: 3 h_l seen (after the barrier), 4 this workgroup's SwiGLU outputs stored,
-//                   5 down phase starts, 6 this workgroup's rows of h_{l+1} stored, 7 head rows done
+//                   5 down phase starts, 6 this workgroup's rows of h_{l+1} stored, 7 head rows done,
+//                   8 gate/up dot products done, 9 its SwiGLU output ready (before the gathering
+//                   barrier), 12 the combine starts, 13 down dot products done, 14 down partials stored
+//   compute waves 4 and 2: 10 and 11, their SwiGLU output ready (wave 4 shares a SIMD with the poll
+//                   wave, wave 2 does not); compute wave 4: 15 its down partials stored
 // The plain variant compiles every stamp away.
-constexpr int NSTAMP = 8;
+constexpr int NSTAMP = 16;
 template <bool STAMP>
 __device__ __forceinline__ void stamp(const StepParams& p, int wg, int l, int slot, bool on = true) {
   if constexpr (STAMP) {
@@ -731,6 +735,7 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           red[2 * u + 1] = pu;
         }
         red[2 * GU] = sq;  // the segments of the 64 lanes cover all of h_l
+        stamp<STAMP>(p, wg, l, 8, cw == 0);
         wave_sum_n(red);
         scale = 1.f / sqrtf(red[2 * GU] / (float)p.d + RMS_EPS);
 #pragma unroll
@@ -739,6 +744,9 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           const float a = pg / (1.f + expf(-pg)) * pu;
           if (lead) sm.aout[cw * GU + u] = A.bad[u] ? quiet_nan() : a;
         }
+        stamp<STAMP>(p, wg, l, 9, cw == 0);
+        stamp<STAMP>(p, wg, l, 10, cw == 3);
+        stamp<STAMP>(p, wg, l, 11, cw == 1);
         // the workgroup's MW*GU consecutive outputs leave as one store of whole lines (partial
         // lines written by many waves were measured slower to reach the readers)
         lds_barrier();  // BA
@@ -849,13 +857,17 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         }
         const float s_d = h2f(B.s[u]);
         float po = ls < S ? s_d * (d0 + d1) + (h2f(B.b[u]) - 1024.f * s_d) * sx : 0.f;
+        stamp<STAMP>(p, wg, l, 13, cw == 0);
         po = group_sum_last(po, p.Ldn);
         if (ls == p.Ldn - 1 && B.ok[u]) sm.part[B.k[u] * p.DR + B.jr[u]] = B.bad[u] ? quiet_nan() : po;
       }
     }
+    stamp<STAMP>(p, wg, l, 14, cw == 0);
+    stamp<STAMP>(p, wg, l, 15, cw == 3);
     if (prefetch)  // weights of B_{l+1}, one phase early
       issue_B<BITS, NSF, PD>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, B);
     lds_barrier();  // B4
+    stamp<STAMP>(p, wg, l, 12, cw == 0);
     // ---- combine + residual of this workgroup's rows -> h_{l+1} (wave 1; lane = row) ----
     if (cw == 0) {
       const int nrows = min(p.DR, p.d - wg * p.DR);  // >= 2 and even: the last workgroup may hold fewer

@@ -410,7 +410,7 @@ moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int
   const moe_status c = check_decode_step(st, token, flags, h_in, h_out, h_layers, workspace, workspace_bytes);
   if (c != MOE_OK) return c;
   const int G = decode_step_grid(*st);
-  if (!stamps || ((uintptr_t)stamps & 7u) || G < 1 || stamp_bytes < (size_t)G * st->L * 8 * sizeof(uint64_t))
+  if (!stamps || ((uintptr_t)stamps & 7u) || G < 1 || stamp_bytes < (size_t)G * st->L * 16 * sizeof(uint64_t))
     return MOE_ERR_INVALID_ARG;
   return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace, stamps));
 }

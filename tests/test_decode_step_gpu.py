@@ -180,7 +180,7 @@ def test_decode_step_stamped(M, name):
     a, b = DecodeStack(layers, cfg.K, DEV), DecodeStack(layers, cfg.K, DEV)
     G = a.grid()
     assert G > 0
-    st = torch.zeros((G, cfg.L, 8), dtype=torch.int64, device=DEV)
+    st = torch.zeros((G, cfg.L, 16), dtype=torch.int64, device=DEV)
     for t in range(3):
         h0 = syn.hidden(8300 + t, 1)[0].to(DEV)
         ya = a.step(t, h0).clone()
