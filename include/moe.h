@@ -55,7 +55,8 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad size, K > E, misalignment ...     */
   MOE_ERR_UNSUPPORTED = 2, /* bits not in {2,4}, group not in {32,64,128}, shape off-grid   */
-  MOE_ERR_HIP = 3          /* the HIP runtime rejected a launch                              */
+  MOE_ERR_HIP = 3,         /* the HIP runtime rejected a launch                              */
+  MOE_ERR_TOO_LARGE = 4    /* moe_expert_ffn_q4_noalloc: the call needs more than its scratch */
 } moe_status;
 
 /* flags */
@@ -152,6 +153,20 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
                              const int32_t* idx, const moe_experts* ex, const moe_lora* lora3,
                              float* out, const float* w_fuse, const uint16_t* r_fuse,
                              uint16_t* y_fuse, void* workspace, size_t workspace_bytes);
+
+/* moe_expert_ffn_q4 without the workspace argument, for callers that cannot allocate device memory:
+   code under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Arguments,
+   results and errors as moe_expert_ffn_q4.  The scratch it needs (moe_expert_ffn_workspace_size
+   bytes) is a device array inside the library, MOE_NOALLOC_SCRATCH_BYTES per GPU, allocated once
+   with the library's code on each GPU it runs on and held until the process ends; the call
+   allocates nothing.  A call that needs more returns MOE_ERR_TOO_LARGE with nothing enqueued
+   (e.g. T >= 32 large batches: use moe_expert_ffn_q4 with a workspace).  Every call on one GPU
+   uses the same array: calls that may overlap on one GPU (other streams, other threads) race and
+   must be ordered by the caller.  MOE_ERR_HIP if the array's device address cannot be found. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_expert_ffn_q4_noalloc(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                     const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
+                                     const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse);
 
 /* Bytes of device workspace moe_expert_ffn_sparse needs for T tokens with K experts each. */
 size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex);

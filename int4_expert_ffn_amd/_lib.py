@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_TOPK_RENORM = 0x1
 MOE_INPUT_RMSNORM = 0x2
 MOE_DECODE_GIVEN_ROUTING = 0x4
@@ -27,7 +28,7 @@ EXPORTS = (
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
     "moe_stream_in_many", "moe_read_probe", "moe_exchange_probe_workspace_size", "moe_exchange_probe",
-    "moe_decode_step_grid", "moe_decode_step_stamped",
+    "moe_decode_step_grid", "moe_decode_step_stamped", "moe_expert_ffn_q4_noalloc",
 )
 
 
@@ -103,6 +104,8 @@ def _load():
         "moe_expert_ffn_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
         "moe_expert_ffn_q4": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora),
                                    vp, vp, vp, vp, vp, sz]),
+        "moe_expert_ffn_q4_noalloc": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts),
+                                           ctypes.POINTER(moe_lora), vp, vp, vp, vp]),
         "moe_expert_ffn_sparse_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
         "moe_expert_ffn_sparse": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), vp, vp, vp, vp, vp,
                                        vp, sz]),
@@ -321,6 +324,24 @@ def moe_expert_ffn_q4(T, K, flags, x, idx, ex: Experts, lora3: Optional[Lora3], 
                                 _ptr(out, _f32(), "out"), _ptr(w_fuse, _f32(), "w_fuse"), _ptr(r_fuse, _f16(), "r_fuse"),
                                 _ptr(y_fuse, _f16(), "y_fuse"), _ptr(workspace, None, "workspace"), nbytes)
     _check(st, "moe_expert_ffn_q4")
+
+
+def moe_expert_ffn_q4_noalloc(T, K, flags, x, idx, ex: Experts, lora3: Optional[Lora3], out, w_fuse, r_fuse, y_fuse,
+                              stream=None):
+    """moe_expert_ffn_q4 on the library's own scratch (no workspace argument, nothing allocated)."""
+    d = ex.d
+    _need(x, T * d, "x")
+    _need(idx, T * K, "idx")
+    _need(out, T * K * d, "out")
+    _need(w_fuse, T * K, "w_fuse")
+    _need(r_fuse, T * d, "r_fuse")
+    _need(y_fuse, T * d, "y_fuse")
+    st = _lib.moe_expert_ffn_q4_noalloc(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"),
+                                        _ptr(idx, _i32(), "idx"), ctypes.byref(ex.desc),
+                                        ctypes.cast(lora3.desc, ctypes.POINTER(moe_lora)) if lora3 is not None else None,
+                                        _ptr(out, _f32(), "out"), _ptr(w_fuse, _f32(), "w_fuse"),
+                                        _ptr(r_fuse, _f16(), "r_fuse"), _ptr(y_fuse, _f16(), "y_fuse"))
+    _check(st, "moe_expert_ffn_q4_noalloc")
 
 
 def moe_expert_ffn_sparse_workspace_size(T, K, ex: Experts) -> int:

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_launch.h"
 
 using namespace moe;
@@ -75,6 +77,29 @@ moe_status check_experts(const moe_experts* ex) {
   return MOE_OK;
 }
 
+// Scratch of moe_expert_ffn_q4_noalloc: a file-scope device array, one copy on every GPU the library
+// runs on, held until the process ends.  In host code its name is only a host-side stand-in: the
+// device address of each GPU's copy is looked up once per device (with that device current) and
+// kept; kernels only ever receive that address.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];  // device address of `scratch` per device, once looked up
+
+moe_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +110,8 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported bits, group or shape";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime rejected a launch";
+    case MOE_ERR_TOO_LARGE:
+      return "MOE_ERR_TOO_LARGE: the call needs more scratch than the allocation-free entry point holds";
   }
   return "unknown moe_status";
 }
@@ -132,14 +159,14 @@ size_t moe_expert_ffn_workspace_size(int32_t T, int32_t K, const moe_experts* ex
   return ffn_ws(T, K, ex).total;
 }
 
-moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
-                             const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
-                             const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace,
-                             size_t workspace_bytes) {
+// Argument checks of moe_expert_ffn_q4 other than the workspace.
+static moe_status check_expert_ffn(int32_t T, int32_t K, uint32_t flags, const uint16_t* x, const int32_t* idx,
+                                   const moe_experts* ex, const moe_lora* lora3, float* out, const float* w_fuse,
+                                   const uint16_t* r_fuse, uint16_t* y_fuse) {
   moe_status st = check_experts(ex);
   if (st != MOE_OK) return st;
   if (!routing_dims_ok(T, ex->n_experts, K) || !known_flags(flags)) return MOE_ERR_INVALID_ARG;
-  if (!x || !idx || !workspace || !aligned16(x) || !aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+  if (!x || !idx || !aligned16(x)) return MOE_ERR_INVALID_ARG;
   const bool fuse = w_fuse || r_fuse || y_fuse;
   if (fuse && !(w_fuse && r_fuse && y_fuse)) return MOE_ERR_INVALID_ARG;
   if (!out && !fuse) return MOE_ERR_INVALID_ARG;
@@ -150,8 +177,14 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
       if (!aligned16(lora3[m].A)) return MOE_ERR_INVALID_ARG;
     }
   }
+  return MOE_OK;
+}
+
+// Enqueue the expert FFN on checked arguments with `workspace` (ffn_ws(T, K, ex).total bytes).
+static moe_status run_expert_ffn(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                 const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
+                                 const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace) {
   const FfnWs ws = ffn_ws(T, K, ex);
-  if (workspace_bytes < ws.total) return MOE_ERR_INVALID_ARG;
   char* base = (char*)workspace;
   DecodeArgs a{};
   a.T = T;
@@ -194,6 +227,28 @@ moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags,
     return from_hip(launch_expert_grouped(s, g));
   }
   return from_hip(launch_expert_decode(s, a));
+}
+
+moe_status moe_expert_ffn_q4(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                             const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
+                             const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace,
+                             size_t workspace_bytes) {
+  const moe_status st = check_expert_ffn(T, K, flags, x, idx, ex, lora3, out, w_fuse, r_fuse, y_fuse);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < ffn_ws(T, K, ex).total) return MOE_ERR_INVALID_ARG;
+  return run_expert_ffn(stream, T, K, flags, x, idx, ex, lora3, out, w_fuse, r_fuse, y_fuse, workspace);
+}
+
+moe_status moe_expert_ffn_q4_noalloc(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                     const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
+                                     const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse) {
+  const moe_status st = check_expert_ffn(T, K, flags, x, idx, ex, lora3, out, w_fuse, r_fuse, y_fuse);
+  if (st != MOE_OK) return st;
+  if (ffn_ws(T, K, ex).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ptr = nullptr;
+  const moe_status sp = scratch_on_current_device(&ptr);
+  if (sp != MOE_OK) return sp;
+  return run_expert_ffn(stream, T, K, flags, x, idx, ex, lora3, out, w_fuse, r_fuse, y_fuse, ptr);
 }
 
 size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex) {

@@ -28,12 +28,12 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
     assert L.moe_version() == 100
-    for s in (0, 1, 2, 3):
+    for s in (0, 1, 2, 3, 4):
         assert L.moe_status_string(s).startswith(b"MOE_")
 
 
@@ -276,3 +276,20 @@ def test_exchange_probe_rejects():
     assert L.moe_exchange_probe(None, ctypes.byref(c), FAKE, 16, FAKE) == INVALID       # workspace too small
     assert L.moe_exchange_probe(None, ctypes.byref(c), FAKE + 8, 1 << 30, FAKE) == INVALID  # not 256-aligned
     assert L.moe_exchange_probe(None, None, FAKE, 1 << 30, FAKE) == INVALID
+
+
+def test_expert_ffn_noalloc_rejects():
+    """The allocation-free entry point checks its arguments as moe_expert_ffn_q4 does (nothing is
+    enqueued), and refuses a call whose scratch would exceed MOE_NOALLOC_SCRATCH_BYTES."""
+    ex = _ex()
+    f = lambda *a: L.moe_expert_ffn_q4_noalloc(None, *a)
+    assert f(0, 2, 0, FAKE, FAKE, ctypes.byref(ex), None, FAKE, None, None, None) == INVALID   # T < 1
+    assert f(1, 2, 0, None, FAKE, ctypes.byref(ex), None, FAKE, None, None, None) == INVALID   # no x
+    assert f(1, 2, 0, FAKE, FAKE, ctypes.byref(ex), None, None, None, None, None) == INVALID   # no output
+    assert f(1, 2, 0, FAKE, FAKE, ctypes.byref(ex), None, FAKE, FAKE, None, None) == INVALID   # half a fuse
+    bad = _ex(bits=3)
+    assert f(1, 2, 0, FAKE, FAKE, ctypes.byref(bad), None, FAKE, None, None, None) == UNSUP
+    big = _ex(E=16, d=8192, I=8192)
+    need = L.moe_expert_ffn_workspace_size(40, 16, ctypes.byref(big))
+    assert need > lib_mod.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(40, 16, 0, FAKE, FAKE, ctypes.byref(big), None, FAKE, None, None, None) == lib_mod.MOE_ERR_TOO_LARGE
