@@ -288,7 +288,8 @@ typedef struct {
   uint32_t epoch;
   int32_t replicas; /* ALL: each word is stored in `replicas` copies (1..8) and workgroup b reads copy
                        b % replicas (with 8, the copy of its XCD), which spreads the readers' traffic */
-  int32_t wide_loads; /* ALL: 1 = poll with 16-byte loads (two words per lane per load), 0 = 8-byte */
+  int32_t wide_loads; /* ALL: 0 = 8-byte buffer loads, 1 = 16-byte buffer loads (two words per lane per
+                         load), 2 = 8-byte agent-scope atomic loads through the global path (words <= 1024) */
 } moe_xchg_cfg;
 size_t moe_exchange_probe_workspace_size(const moe_xchg_cfg* cfg);
 moe_status moe_exchange_probe(void* stream, const moe_xchg_cfg* cfg, void* workspace, size_t workspace_bytes,

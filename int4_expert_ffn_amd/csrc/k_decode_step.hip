@@ -34,6 +34,8 @@
 // the first token] -> A_l: gate/up + SwiGLU, fc2 rows of head l-1, linear and fc1 (+GELU) rows of
 // head l -> B_l: down + combine + residual.  Every wait is bounded in time: one that runs out
 // sets the error word and lets the kernel finish (its results are then invalid).
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -66,6 +68,9 @@ struct StepParams {
   int rstage;                  // the compute waves stage each self-routed layer's router rows in LDS
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
+  // h and the SwiGLU outputs are written in xr_h / xr_a copies (strides in words); workgroup b
+  // reads copy b % xr, so the 256 readers of one exchange spread over several sets of lines
+  int xr_h, xr_a, h_stride, act_stride;
   uint32_t* epoch;
   int* err;
   const uint16_t* zero16;  // a float16 zero (stands in for an absent bias)
@@ -529,7 +534,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       if (p.h_layers != nullptr && c.wg == 0)  // row 0 of the per-layer copies: the token's input
         for (int m = lane; m < dh; m += WAVE) reinterpret_cast<uint32_t*>(p.h_layers)[m] = hw[m];
     } else {
-      ll_wait(p.ll_h, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed,
+      ll_wait(p.ll_h + (size_t)(c.wg % p.xr_h) * p.h_stride, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed,
               [&](int i, uint32_t v) { hw[i] = v; });
     }
     stamp<STAMP>(p, c.wg, l, 1);
@@ -552,7 +557,8 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     }
     const uint32_t tA = c.tag(3 * l + 1);
     lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
-    ll_wait<16>(p.ll_act, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed, [&](int i, uint64_t v) {
+    ll_wait<16>(p.ll_act + (size_t)(c.wg % p.xr_a) * p.act_stride, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed,
+                [&](int i, uint64_t v) {
       sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
       sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
     });
@@ -750,12 +756,14 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         // the workgroup's MW*GU consecutive outputs leave as one store of whole lines (partial
         // lines written by many waves were measured slower to reach the readers)
         lds_barrier();  // BA
-        if (cw == 0) {  // lane j sends outputs 2j, 2j+1 of the workgroup as one packed word
-          const int j = min(lane, MW * GU / 2 - 1);
-          const int word = wg * MW * GU / 2 + j;
+        if (cw == 0) {  // lane j + n*copy sends outputs 2j, 2j+1 of the workgroup as one packed word of that copy
+          constexpr int NW = MW * GU / 2;
+          const int j = lane % NW, cpy = lane / NW;
+          const int word = wg * NW + j;
           const uint64_t w = (uint64_t)f32_to_f24(sm.aout[2 * j]) | ((uint64_t)f32_to_f24(sm.aout[2 * j + 1]) << 24) |
                              ((uint64_t)c.tag16(3 * l + 1) << 48);
-          ll_put64(ws, p, p.ll_act, min(word, p.K * p.I / 2 - 1), lane < MW * GU / 2 && 2 * word < p.K * p.I, w);
+          ll_put64(ws, p, p.ll_act, (size_t)min(cpy, p.xr_a - 1) * p.act_stride + min(word, p.K * p.I / 2 - 1),
+                   cpy < p.xr_a && 2 * word < p.K * p.I, w);
           stamp<STAMP>(p, wg, l, 4);
         }
       }
@@ -882,11 +890,11 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       if (l + 1 == p.L) {
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)yb, hout, mine ? (uint32_t)j * 2 : OFF_NONE, 0, 0);
       } else {
-        // lane m sends word m (rows 2m, 2m+1)
-        const int m = min(lane, nrows / 2 - 1);
+        // lane m + n*copy sends word m (rows 2m, 2m+1) of that copy
+        const int nw = nrows / 2, m = lane % nw, cpy = lane / nw;
         const uint32_t lo = __shfl(yb, 2 * m, WAVE), hi = __shfl(yb, 2 * m + 1, WAVE);
-        ll_put(ws, p, p.ll_h, (size_t)(l + 1) * dh + wg * (p.DR / 2) + m, lane < nrows / 2, lo | (hi << 16),
-               c.tag(3 * l + 2));
+        ll_put(ws, p, p.ll_h, (size_t)min(cpy, p.xr_h - 1) * p.h_stride + (size_t)(l + 1) * dh + wg * (p.DR / 2) + m,
+               cpy < p.xr_h, lo | (hi << 16), c.tag(3 * l + 2));
       }
       stamp<STAMP>(p, wg, l, 6);
     }
@@ -925,8 +933,8 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   if (wave == 0) {
     sync_role<BITS, NSH * 4, STAMP>(p, c, sm);
   } else {
-    // the polling wave shares a SIMD with one compute wave: let the arithmetic issue first
-    __builtin_amdgcn_s_setprio(2);
+    // (all waves at the same issue priority: raising the compute waves' above the polling wave's,
+    // which shares SIMD 0 with two of them, was measured 2 % slower per token)
     compute_role<BITS, PG, NSH, NSF, GU, PD, NH, STAMP>(p, c, sm);
   }
   if (c.wg == 0 && threadIdx.x == 0) *p.epoch = c.epoch + 1;
@@ -986,6 +994,7 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
 struct StepWs {
   size_t epoch, err, zero, logits, act, g, hlog, h, total;
 };
+constexpr int XR_MAX = 8;  // copies of h and of the SwiGLU outputs (one per XCD)
 static StepWs step_ws(const moe_decode_stack& st) {
   StepWs w{};
   w.epoch = 0;
@@ -993,10 +1002,10 @@ static StepWs step_ws(const moe_decode_stack& st) {
   w.zero = 8;  // 8 bytes that stay zero
   w.logits = 256;
   w.act = w.logits + ll_bytes(st.E);
-  w.g = w.act + ll_bytes((size_t)st.K * st.d_ff);
+  w.g = w.act + XR_MAX * ll_bytes((size_t)st.K * st.d_ff);
   w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? 2 * (size_t)st.d_hidden : 1);  // two buffers, by layer parity
   w.h = w.hlog + ll_bytes((size_t)st.L * st.E);
-  w.total = w.h + ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
+  w.total = w.h + XR_MAX * ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
   return w;
 }
 
@@ -1099,6 +1108,10 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.ll_g = (uint64_t*)(b + w.g);
   p.ll_hlog = (uint64_t*)(b + w.hlog);
   p.ll_h = (uint64_t*)(b + w.h);
+  p.h_stride = (int)(ll_bytes((size_t)(st.L + 1) * (st.d_model / 2)) / 8);
+  p.act_stride = (int)(ll_bytes((size_t)st.K * st.d_ff) / 8);
+  p.xr_h = std::min(XR_MAX, WAVE / (pl.DR / 2));
+  p.xr_a = std::min(XR_MAX, WAVE / (MW * pl.GU / 2));
   p.epoch = (uint32_t*)(b + w.epoch);
   p.err = (int*)(b + w.err);
   p.zero16 = (const uint16_t*)(b + w.zero);

@@ -137,9 +137,55 @@ __device__ void xp_wait_wide(__amdgpu_buffer_rsrc_t rs, uint32_t base, int n, ui
   }
 }
 
+// The same with agent-scope atomic 8-byte loads through the global (flat) path instead of buffer
+// loads (NP words per lane per pass; the decode kernel's polling loads).
+template <int NP>
+__device__ void xp_wait_global(const uint64_t* src, int n, uint32_t tag, uint32_t* err, bool& failed) {
+  const int lane = threadIdx.x % WAVE;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int b0 = 0; b0 < n; b0 += NP * WAVE) {
+    uint32_t done = 0;
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      if (b0 + lane + j * WAVE >= n) done |= 1u << j;
+    uint64_t a[NP], b[NP];
+    auto issue = [&](uint64_t (&v)[NP]) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        v[j] = __hip_atomic_load(src + min(b0 + lane + j * WAVE, n - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto check = [&](const uint64_t (&v)[NP]) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+        if ((uint32_t)(v[j] >> 32) == tag) done |= 1u << j;
+    };
+    issue(a);
+    while (true) {
+      issue(b);
+      check(a);
+      if (__all(done == (1u << NP) - 1)) break;
+      issue(a);
+      check(b);
+      if (__all(done == (1u << NP) - 1)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > XP_WAIT_TICKS) {
+        if (lane == 0) atomicAdd(err, 1u);
+        failed = true;
+        return;
+      }
+    }
+  }
+}
+
 __device__ void xp_wait_all(__amdgpu_buffer_rsrc_t rs, uint32_t base, int n, uint32_t tag, int aux, uint32_t* err,
-                            bool& failed, bool wide = false) {
+                            bool& failed, int wide = 0, const void* ws = nullptr) {
   if (failed) return;
+  if (wide == 2) {  // global atomic loads, sixteen per lane per pass (n <= 1024)
+    const uint64_t* src = (const uint64_t*)((const char*)ws + base);
+    if (n <= 4 * WAVE) xp_wait_global<4>(src, n, tag, err, failed);
+    else if (n <= 8 * WAVE) xp_wait_global<8>(src, n, tag, err, failed);
+    else xp_wait_global<16>(src, n, tag, err, failed);
+    return;
+  }
   if (wide) {
     if (n <= 2 * WAVE) xp_wait_wide<1>(rs, base, n, tag, aux, err, failed);
     else if (n <= 4 * WAVE) xp_wait_wide<2>(rs, base, n, tag, aux, err, failed);
@@ -204,7 +250,7 @@ __global__ void __launch_bounds__(WAVE) k_xchg_probe(XchgParams p) {
         xp_store(rs, buf + (uint32_t)c * p.copy_stride + 8u * (uint32_t)(r * per + min(lane, per - 1)), lane < per,
                  (uint32_t)ph, tag, p.store_aux);
       xp_wait_all(rs, buf + (uint32_t)(b % p.replicas) * p.copy_stride, p.words, tag, p.load_aux, err, failed,
-                  p.wide != 0);
+                  p.wide, p.ws);
     }
   } else {  // RING: slot s of the group at gbase + 256 s; hop v lands in slot v % gs
     const uint32_t mine = gbase + 256u * (uint32_t)r, next = gbase + 256u * (uint32_t)((r + 1) % p.gs);

@@ -388,7 +388,8 @@ static bool xchg_cfg_ok(const moe_xchg_cfg* c) {
   if (c->n_wg < 1 || c->group_size < 1 || c->n_wg % c->group_size) return false;
   if (c->iters < 1) return false;
   if (c->replicas < 1 || c->replicas > 8) return false;
-  if (c->wide_loads != 0 && c->wide_loads != 1) return false;
+  if (c->wide_loads < 0 || c->wide_loads > 2) return false;
+  if (c->wide_loads == 2 && c->words > 1024) return false;
   if (c->pattern == MOE_XCHG_ALL) {
     if (c->words < c->group_size || c->words % c->group_size || c->words / c->group_size > 64 || c->words > 16384)
       return false;

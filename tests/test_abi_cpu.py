@@ -266,7 +266,7 @@ def test_exchange_probe_rejects():
     assert L.moe_exchange_probe_workspace_size(ctypes.byref(cfg())) > 0
     bad = [dict(pattern=2), dict(n_wg=0), dict(group_size=3), dict(words=1000), dict(words=256 * 65),
            dict(iters=0), dict(iters=40000), dict(load_scope=2), dict(store_scope=-1), dict(xcd_local=2),
-           dict(pattern=1, group_size=8, iters=9000), dict(replicas=0), dict(replicas=9), dict(wide_loads=2)]
+           dict(pattern=1, group_size=8, iters=9000), dict(replicas=0), dict(replicas=9), dict(wide_loads=3), dict(wide_loads=2, words=2048, group_size=256)]
     for b in bad:
         c = cfg(**b)
         assert L.moe_exchange_probe_workspace_size(ctypes.byref(c)) == 0, b
