@@ -112,64 +112,97 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def cpu_baseline(cfg, layers, syn, tokens, threads=1):
-    """Time the fp64 oracle on `tokens` steady-state tokens of the same stack, with `threads` BLAS
-    threads (None: the library's default, every core)."""
-    import numpy as np
+def host_cores():
+    """Cores this process may run on (the box's share of the host)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, layers, syn, tokens, streams=1):
+    """Time the fp64 oracle (oracle.chain_token, as it stands) on steady-state tokens of the same
+    stack, one BLAS thread per stream.  streams == 1: `tokens` tokens of one token stream.
+    streams > 1: that many independent token streams (each its own hidden states and routing
+    state, all starting from one bootstrap token) run `tokens` tokens each in as many Python
+    threads, one per core; numpy releases the interpreter lock inside its array operations, so
+    the streams run in parallel, and the figure is their aggregate tokens/s (the oracle on every
+    core, for independent decode streams, since one stream's tokens depend on each other)."""
+    import copy
+    import threading
+
     import oracle as O
     limiter = None
-    if threads is not None:
-        try:
-            from threadpoolctl import threadpool_limits
-            limiter = threadpool_limits(threads)
-        except Exception:  # pragma: no cover
-            limiter = None
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
     routers = [lw.router.cpu().numpy() for lw in layers]
     heads = [None if lw.head is None else {k: (None if v is None else v.cpu().numpy())
                                            for k, v in lw.head.tensors.items()} for lw in layers]
     packed = {}
+    lock = threading.Lock()
 
     def expert_get(l, e):
         key = (l, int(e))
-        if key not in packed:
+        with lock:
+            got = packed.get(key)
+        if got is None:
             mats = layers[l].experts.tensors
-            packed[key] = tuple(tuple(a[int(e)].cpu().numpy() for a in m) for m in mats)
-        return packed[key]
+            got = tuple(tuple(a[int(e)].cpu().numpy() for a in m) for m in mats)
+            with lock:
+                packed[key] = got
+        return got
 
-    st = O.ChainState(cfg.L)
     kw = dict(E=cfg.E, K=cfg.K, bits=cfg.bits, group=cfg.group, router_get=lambda l: routers[l],
               head_get=lambda l: heads[l], expert_get=expert_get)
-    _, st, _ = O.chain_token(syn.hidden(10**6, 1)[0].numpy(), st, **kw)      # bootstrap token, untimed
+    _, st0, _ = O.chain_token(syn.hidden(10**6, 1)[0].numpy(), O.ChainState(cfg.L), **kw)  # bootstrap, untimed
+    hs = syn.hidden(10**6 + 1, streams * tokens).numpy()
+
+    def stream(i):
+        st = copy.deepcopy(st0)
+        for j in range(tokens):
+            _, st, _ = O.chain_token(hs[i * tokens + j], st, **kw)
+
     t0 = time.perf_counter()
-    for i in range(tokens):
-        _, st, _ = O.chain_token(syn.hidden(10**6 + 1 + i, 1)[0].numpy(), st, **kw)
+    if streams == 1:
+        stream(0)
+    else:
+        ths = [threading.Thread(target=stream, args=(i,)) for i in range(streams)]
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
     elapsed = time.perf_counter() - t0
     if limiter is not None:
         limiter.restore_original_limits()
-    cores = threads
-    if cores is None:  # the BLAS pools' own thread count (what the oracle's products used)
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max((int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"),
-                        default=1)
-        except Exception:  # pragma: no cover
-            cores = os.cpu_count() or 1
-    return {"value": round(tokens / elapsed, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "cpu": cpu_model(),
-            "sample": f"{tokens} steady-state decode tokens through all {cfg.L} layers (fp64, explicit dequant, "
-                      f"{cores} BLAS thread{'s' if cores > 1 else ''}; includes copying each selected expert's packed "
-                      f"bytes from HBM once)"}
+    n = streams * tokens
+    what = (f"{tokens} steady-state decode tokens through all {cfg.L} layers" if streams == 1 else
+            f"{streams} independent token streams x {tokens} steady-state tokens through all {cfg.L} layers, one "
+            f"Python thread per stream")
+    return {"value": round(n / elapsed, 5), "unit": "tokens/s", "cores": streams, "host_cores": host_cores(),
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": what + " (fp64, explicit dequant, 1 BLAS thread per stream; includes copying each selected "
+                             "expert's packed bytes from HBM once)"}
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model name, family, model, stepping)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    if name is None:
+        return None
+    extra = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({extra})" if extra else name
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
@@ -396,16 +429,19 @@ def bench_stack(args, cfg, torch, M, S, dev):
     graphs = tm.capture(lambda t, h: stack.step(t, h))
     if args.eager:                               # same tokens, direct launches (graphs captured but unused)
         graphs = lambda t: stack.step(t, tm.ring[t % 3])
-    wall, ev_ms, args.warmup = tm.timed(graphs, args.steps, args.warmup)
+    runs = [tm.timed(graphs, args.steps, args.warmup)]
+    args.warmup = runs[0][2]
     assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time"
     h_out = stack.h[cfg.L].float()
     assert torch.isfinite(h_out).all(), "non-finite decode output"
-    # the same timed loop again (no further warm-up): the spread of the figure over repeats
-    reps = [args.steps / wall] + [args.steps / tm.timed(graphs, args.steps, 0)[0] for _ in range(args.repeats - 1)]
+    # the same timed loop again (no further warm-up): `value` is the median run of the repeats
+    runs += [tm.timed(graphs, args.steps, 0) for _ in range(args.repeats - 1)]
     assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time (repeats)"
     del graphs
+    reps = [args.steps / r[0] for r in runs]
+    wall, ev_ms, _ = sorted(runs, key=lambda r: r[0])[len(runs) // 2]
     total_bytes, eo_bytes = algorithmic_bytes(cfg)
-    step_us = ev_ms * 1e3 / args.steps               # HIP-event time per token on the stream
+    step_us = ev_ms * 1e3 / args.steps               # HIP-event time per token on the stream (median run)
 
     # the expert FFN steps alone (gate/up + SwiGLU, down + combine + residual through all layers, the
     # RMS-norm chain included) on the routing the full path chose for the same tokens, recorded
@@ -546,7 +582,8 @@ def bench_stack(args, cfg, torch, M, S, dev):
                     "zero compute",
         }
     rec["repeats"] = {"tokens_per_s": [round(v, 2) for v in reps], "median": round(sorted(reps)[len(reps) // 2], 2),
-                      "note": f"{len(reps)} runs of the same {args.steps} timed tokens, the first being `value`"}
+                      "note": f"{len(reps)} runs of the same {args.steps} timed tokens; `value`, `ms_per_step` and the "
+                              f"roofline's avg_us are those of the median run"}
     rec["routing_histogram"] = hist
     rec["expert_only"] = expert_only
     rec["per_layer_calls"] = {"tokens_per_s": per_layer_tok_s, "launches_per_token": launches,
@@ -555,7 +592,7 @@ def bench_stack(args, cfg, torch, M, S, dev):
         log("timing the CPU oracle ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, layers, syn, tokens=5 if cfg.d <= 2048 else 2)
         log("timing the CPU oracle on every core ...")
-        rec["cpu_baseline_all_cores"] = cpu_baseline(cfg, layers, syn, tokens=5 if cfg.d <= 2048 else 2, threads=None)
+        rec["cpu_baseline_all_cores"] = cpu_baseline(cfg, layers, syn, tokens=1, streams=host_cores())
     return rec
 
 

@@ -336,7 +336,11 @@ moe_status moe_combine(void* stream, int32_t T, int32_t K, int32_t d, const floa
    with t' % 3 == t % 3.
 
    One workgroup per compute unit stays resident for the whole token; workgroups hand vectors to
-   each other through tagged words in the workspace.  The workspace must be zeroed once before
+   each other through tagged words in the workspace.  Precondition: the launch has the device's
+   compute units to itself (every workgroup must be resident at once).  A kernel running at the
+   same time on another stream that holds compute units can keep workgroups from starting; the
+   resident ones then wait, each wait is bounded (0.2 s of polling), and the call ends with the
+   error word set and its outputs invalid (no hang).  The workspace must be zeroed once before
    the first call and then passed unchanged to every later call of the same stack; calls on one
    workspace must not overlap.  Its first 4 bytes hold a token counter, the next 4 an error
    word: nonzero means a wait inside the kernel exceeded its bound and that call's outputs are

@@ -228,13 +228,19 @@ class Synth:
     def router(self, layer: int, device="cpu") -> torch.Tensor:
         """[E][d] float16.  "gauss": N(0, 1/d) (variance 1/d, so logits ~ N(0, 1) for
         unit-RMS input); "orthonormal": rows of an orthonormal basis of a seeded
-        Gaussian (QR in float64 on the CPU), so logits of isotropic input are iid N(0,1)."""
+        Gaussian whose rows were first made orthogonal to the all-ones vector (each row
+        minus its mean; QR in float64 on the CPU), so logits of isotropic input are iid
+        N(0,1) and a component shared by every column of the input moves no logit.  (The
+        affine 4-bit weights of the recipe have mean -scale/2, so every expert adds such a
+        component to the residual stream and, left in the routers, it steers every token of
+        a deep chain to the same few experts.)"""
         c = self.cfg
         if c.router == "gauss":
             return normal_f16([self.key(layer, 0, T_ROUTER)], c.E * c.d, 1.0 / math.sqrt(c.d),
                               device).view(c.E, c.d)
-        g = normal_f16([self.key(layer, 0, T_ROUTER)], c.E * c.d, 1.0, "cpu").view(c.E, c.d)
-        qm, _ = torch.linalg.qr(g.to(torch.float64).t())      # [d][E], orthonormal columns
+        g = normal_f16([self.key(layer, 0, T_ROUTER)], c.E * c.d, 1.0, "cpu").view(c.E, c.d).to(torch.float64)
+        g = g - g.mean(dim=1, keepdim=True)
+        qm, _ = torch.linalg.qr(g.t())                        # [d][E], orthonormal columns
         return to_f16(qm.t().contiguous()).to(device)
 
     # ---- prerouter head of layer `layer` (predicts layer+1) --------------------------

@@ -130,3 +130,34 @@ def test_full_depth_layer_by_layer(M, name, path):
             assert predicted >= L
     del stack, layers
     _free()
+
+
+def test_widek8_routing_spread_over_1024_tokens(M):
+    """The K = 8 stack's routing is spread over the experts at every layer of the chain: over 1024
+    seeded tokens, Pearson's chi-square of each layer's expert counts against the uniform count
+    stays within a few times its E - 1 degrees of freedom (with routers that do not ignore the
+    residual stream's shared component, the chain collapses onto a few experts from the third layer
+    on: chi-square 10^4 to 10^5), and no expert takes more than a few times its share."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = FULL["widek8-L24"]
+    _free()
+    syn, layers, _, _ = build(M, cfg, heads)
+    stack = DecodeStack(layers, cfg.K, DEV)
+    T = 1024
+    hs = syn.hidden(11, T, DEV)
+    rec = torch.empty((T, cfg.L, cfg.K), dtype=torch.int32, device=DEV)
+    for t in range(T):
+        stack.step(t, hs[t])
+        rec[t].copy_(stack.route_idx[t % 3])
+    torch.cuda.synchronize()
+    assert stack.step_error_word() == 0
+    expect = T * cfg.K / cfg.E
+    chi2 = []
+    for l in range(cfg.L):
+        n = torch.bincount(rec[:, l].reshape(-1).long().cpu(), minlength=cfg.E).double()
+        chi2.append(float(((n - expect) ** 2).sum() / expect))
+        assert n.max().item() <= 4 * expect, (l, n.max().item())
+    log(f"widek8 chi-square per layer (dof {cfg.E - 1}): {[round(c) for c in chi2]}")
+    assert max(chi2) < 4 * (cfg.E - 1), chi2
+    del stack, layers
+    _free()

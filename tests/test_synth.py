@@ -55,6 +55,8 @@ def test_router_scale_and_orthonormal_rows():
     w2 = S.Synth(S.CONFIGS["widek8"]).router(3).double()
     gram = w2 @ w2.t()
     assert torch.allclose(gram, torch.eye(gram.shape[0], dtype=torch.float64), atol=5e-3)
+    # and orthogonal to the all-ones direction (up to the float16 rounding of the rows)
+    assert (w2.sum(dim=1).abs() / math.sqrt(w2.shape[1])).max().item() < 2e-3
 
 
 def test_head_uses_next_router_for_linear_path():
