@@ -9,13 +9,13 @@
 // section "Ejecucion del adaptador no fusionado"); the dequantised projections, SwiGLU and
 // combine follow "Inferencia de LLM MoE en MacBook Pro ...", section "Arquitectura del Sistema".
 //
-// MFMA mapping (v_mfma_f32_16x16x16_f16): A = 16 token rows x 16 columns, B = 16 columns x 16
-// weight rows, D = 16 tokens x 16 weight rows in float32.  A wave owns 16 weight rows; lane
+// MFMA mapping (gfx950's v_mfma_f32_16x16x32_f16): A = 16 token rows x 32 columns, B = 32 columns
+// x 16 weight rows, D = 16 tokens x 16 weight rows in float32.  A wave owns 16 weight rows; lane
 // (n = lane % 16, q = lane / 16) loads one 16-byte segment of row n (32 int4 / 64 int2 columns,
 // segment q of a 4-segment macro step) and dequantises it once to float16 pairs
-// w = fma(code, scale, bias).  MFMA step s takes the lane's pairs 2s and 2s+1; the token rows
+// w = fma(code, scale, bias).  MFMA step s takes the lane's pairs 4s .. 4s+3; the token rows
 // are staged in LDS with columns permuted inside each 8 (int4) or 16 (int2) column block so the
-// same four columns sit next to each other, so A is one 8-byte LDS read.  Which physical column
+// same four columns sit next to each other, so A is two 8-byte LDS reads.  Which physical column
 // feeds which k slot does not matter to the dot product as long as A and B agree.
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -296,8 +296,15 @@ __device__ __forceinline__ void magic_words(uint32_t* mg) {
   asm volatile("" : "+v"(mg[0]), "+v"(mg[1]), "+v"(mg[2]), "+v"(mg[3]));
 }
 
-__device__ __forceinline__ half4_t pair2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(half4_t, make_uint2(a, b));
+// B operand of one v_mfma_f32_16x16x32_f16: four dequantised code pairs (eight columns).
+__device__ __forceinline__ half8_t pair4(const uint32_t* w) {
+  return __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+// A operand: the eight staged activation columns the same four pairs cover, as two 8-byte LDS
+// reads (a staged row is 8-byte aligned: its stride keeps the 16 rows a quad reads in distinct banks).
+__device__ __forceinline__ half8_t lds_a8(const uint16_t* xa) {
+  const half4_t lo = *reinterpret_cast<const half4_t*>(xa), hi = *reinterpret_cast<const half4_t*>(xa + 4);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // acc[mi] += X[MT tokens][one macro step] * W_mi[16 rows][same]^T.
@@ -310,11 +317,11 @@ __device__ __forceinline__ void consume_w(const WStage<NMAT, SPLIT>& S, bool val
   for (int mi = 0; mi < NMAT; ++mi)
     dequant_stage<BITS, SPLIT>(S.q[mi], S.sa[mi], S.ba[mi], S.sb[mi], S.bb[mi], valid, mg, w[mi]);
 #pragma unroll
-  for (int s = 0; s < GS::STEPS; ++s) {
-    const half4_t a = *reinterpret_cast<const half4_t*>(xa + 4 * s);
+  for (int s = 0; s < GS::STEPS / 2; ++s) {
+    const half8_t a = lds_a8(xa + 8 * s);
 #pragma unroll
     for (int mi = 0; mi < NMAT; ++mi)
-      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[mi], 0, 0, 0);
+      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pair4(&w[mi][4 * s]), acc[mi], 0, 0, 0);
   }
 }
 
@@ -622,12 +629,25 @@ k_grouped_mm64(
         }
         dequant_stage<BITS, false>(q[f % PFN][mi], (uint16_t)pick, (uint16_t)(pick >> 16), 0, 0, true, mg, w[mi]);
       }
+      if constexpr (BITS == 4 || RG == 1) {
 #pragma unroll
-      for (int s = 0; s < GS::STEPS; ++s) {
-        const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * MACRO + 4 * s);
+        for (int s = 0; s < GS::STEPS / 2; ++s) {
+          const half8_t a = lds_a8(xa + step * MACRO + 8 * s);
 #pragma unroll
-        for (int mi = 0; mi < NMAT; ++mi)
-          acc[rg][mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pair2(w[mi][2 * s], w[mi][2 * s + 1]), acc[rg][mi], 0, 0, 0);
+          for (int mi = 0; mi < NMAT; ++mi)
+            acc[rg][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pair4(&w[mi][4 * s]), acc[rg][mi], 0, 0, 0);
+        }
+      } else {
+        // 2-bit codes with four row groups: the 16-column form holds fewer activation registers
+        // live and keeps this variant within its 128 registers without spilling
+#pragma unroll
+        for (int s = 0; s < GS::STEPS; ++s) {
+          const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * MACRO + 4 * s);
+#pragma unroll
+          for (int mi = 0; mi < NMAT; ++mi)
+            acc[rg][mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                a, __builtin_bit_cast(half4_t, make_uint2(w[mi][2 * s], w[mi][2 * s + 1])), acc[rg][mi], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (f + PFN < RG * NST) {

@@ -79,9 +79,9 @@ __global__ void __launch_bounds__(64) k_router(int T, int d, int E, uint32_t fla
 // The same logits for many tokens at once, on the matrix cores: logits = X W^T with X [T][d] and
 // W [E][d] both K-contiguous.  A block computes one 16-token x 16-expert tile; its waves split the
 // d columns (at most RK each) and each wave issues all of its loads at once, straight from memory
-// (both operands stay in L2), before its MFMAs (v_mfma_f32_16x16x16_f16; D lane (n, q) holds rows
-// 4q..4q+3 of column n).  A lane reads 8 consecutive halves of its row per load and feeds them to
-// two MFMA steps; X and W use the same column order, which is all a dot product needs.  With
+// (both operands stay in L2), before its MFMAs (gfx950's v_mfma_f32_16x16x32_f16; D lane (n, q)
+// holds rows 4q..4q+3 of column n).  A lane reads 8 consecutive halves of its row per load and
+// feeds them to one MFMA step; X and W use the same column order, which is all a dot product needs.  With
 // MOE_INPUT_RMSNORM each token's sum of squares comes from the same X reads.  The partial tiles
 // meet in LDS.  Needs T and E multiples of 16, d of 32 and 16-byte aligned rows (the host checks).
 constexpr int RK = 512;                      // columns per wave
@@ -112,14 +112,10 @@ __global__ void __launch_bounds__(R_MAXW * WAVE) k_router_mfma(int T, int d, int
 #pragma unroll
   for (int i = 0; i < RK_LOADS; ++i) {
     if (c0 + 32 * i >= d) break;  // uniform
-    const half4_t a0 = __builtin_bit_cast(half4_t, make_uint2(a[i].x, a[i].y));
-    const half4_t a1 = __builtin_bit_cast(half4_t, make_uint2(a[i].z, a[i].w));
-    const half4_t b0 = __builtin_bit_cast(half4_t, make_uint2(b[i].x, b[i].y));
-    const half4_t b1 = __builtin_bit_cast(half4_t, make_uint2(b[i].z, b[i].w));
-    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, b0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, b1, acc, 0, 0, 0);
+    const half8_t a8 = __builtin_bit_cast(half8_t, a[i]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, __builtin_bit_cast(half8_t, b[i]), acc, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sq = fmaf((float)a0[j], (float)a0[j], fmaf((float)a1[j], (float)a1[j], sq));
+    for (int j = 0; j < 4; ++j) sq = fmaf((float)a8[j], (float)a8[j], fmaf((float)a8[4 + j], (float)a8[4 + j], sq));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) part[wave][lane][i] = acc[i];

@@ -41,6 +41,7 @@ inline hipError_t first_error(hipError_t a, hipError_t b) { return a != hipSucce
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
