@@ -68,6 +68,7 @@ struct StepParams {
   int rstage;                  // the compute waves stage each self-routed layer's router rows in LDS
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
+  const uint64_t* spare;  // one 64-byte line per workgroup, never written
   // h and the SwiGLU outputs are written in xr_h / xr_a copies (strides in words); workgroup b
   // reads copy b % xr, so the 256 readers of one exchange spread over several sets of lines
   int xr_h, xr_a, h_stride, act_stride;
@@ -151,8 +152,10 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 // slower: more readers hammer the same lines at once).  Two passes are in flight: the next one
 // is issued before the previous one is checked, so a word is seen about one memory round trip
 // after it lands rather than one and a half.  Every pass loads all POLL_MAX slots (slots past
-// the end re-read the last word and are ignored), which keeps the count of outstanding loads
-// exact for the compiler's waits.  A wait is bounded in polling time: past WAIT_TICKS it raises
+// the end read this workgroup's own spare line and are ignored), which keeps the count of
+// outstanding loads exact for the compiler's waits.  (Pointing those slots at the vector's last
+// word made every workgroup hit one line with twelve loads per lane and pass when polling the 256
+// router logits: that exchange took 4.1 us against 2.4 us for the 1,024-word h.)  A wait is bounded in polling time: past WAIT_TICKS it raises
 // the error word, sets `failed`, and every later wait of this wave returns at once, so a grid
 // that cannot make progress still finishes quickly (with invalid results).  Each pass is charged
 // the real time since the previous one, capped at WAIT_STEP_MAX: a pass takes a few us, so the
@@ -161,7 +164,7 @@ __device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
 // TAGB: tag bits in the top of each word (32: a 32-bit payload; 16: a 48-bit payload).
 template <int TAGB = 32, class Sink>
 __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n, uint32_t tag, int* err, bool& failed,
-                                        Sink sink) {
+                                        const uint64_t* spare, Sink sink) {
   constexpr uint64_t PAY = (1ull << (64 - TAGB)) - 1;
   if (failed) return;
   const int lane = threadIdx.x % WAVE;
@@ -175,7 +178,10 @@ __device__ __forceinline__ void ll_wait(const uint64_t* src, size_t start, int n
     uint64_t a[POLL_MAX], b[POLL_MAX];
     auto issue = [&](uint64_t (&v)[POLL_MAX]) {
 #pragma unroll
-      for (int j = 0; j < POLL_MAX; ++j) v[j] = ll_load(ll_at(src, start + min(base + lane + j * WAVE, n - 1)));
+      for (int j = 0; j < POLL_MAX; ++j) {
+        const int i = base + lane + j * WAVE;
+        v[j] = ll_load(i < n ? ll_at(src, start + i) : spare);
+      }
     };
     auto check = [&](const uint64_t (&v)[POLL_MAX]) {
 #pragma unroll
@@ -249,10 +255,11 @@ __device__ __forceinline__ uint32_t order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Softmax top-K of E logits held in LDS (one wave); idx/w land in lanes 0..K-1.
-__device__ __forceinline__ void wave_topk(const float* lt, int E, int K, uint32_t flags, int& out_e, float& out_w) {
+// Softmax top-K of E logits held in LDS (one wave, VPL >= E / 64 logits per lane); idx/w land in
+// lanes 0..K-1.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_v(const float* lt, int E, int K, uint32_t flags, int& out_e, float& out_w) {
   const int lane = threadIdx.x % WAVE;
-  constexpr int VPL = MOE_MAX_E / WAVE;
   uint64_t key[VPL];
   float val[VPL];
 #pragma unroll
@@ -290,6 +297,17 @@ __device__ __forceinline__ void wave_topk(const float* lt, int E, int K, uint32_
   }
   out_e = mine_e;
   out_w = expf(mine_v - top) / den;
+}
+// K rounds of a wave-wide maximum over VPL keys per lane: holding only the E / 64 keys a lane
+// needs (rather than the 16 of the largest E) cuts each round's work four-fold at E = 256, where
+// the selection of the K = 8 routing took 4.3 us on a SIMD shared with two compute waves.
+__device__ __forceinline__ void wave_topk(const float* lt, int E, int K, uint32_t flags, int& out_e, float& out_w) {
+  if (E <= 4 * WAVE)
+    wave_topk_v<4>(lt, E, K, flags, out_e, out_w);
+  else if (E <= 8 * WAVE)
+    wave_topk_v<8>(lt, E, K, flags, out_e, out_w);
+  else
+    wave_topk_v<MOE_MAX_E / WAVE>(lt, E, K, flags, out_e, out_w);
 }
 
 __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
@@ -486,6 +504,7 @@ struct StepShared {
 
 struct StepCtx {
   int wg, lane, cw, gw;
+  const uint64_t* spare;  // this workgroup's own line in the workspace (the target of spare polling slots)
   uint32_t epoch;
   int32_t *cur_i, *nxt_i;
   float *cur_w, *nxt_w;
@@ -534,14 +553,14 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       if (p.h_layers != nullptr && c.wg == 0)  // row 0 of the per-layer copies: the token's input
         for (int m = lane; m < dh; m += WAVE) reinterpret_cast<uint32_t*>(p.h_layers)[m] = hw[m];
     } else {
-      ll_wait(p.ll_h + (size_t)(c.wg % p.xr_h) * p.h_stride, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed,
+      ll_wait(p.ll_h + (size_t)(c.wg % p.xr_h) * p.h_stride, (size_t)l * dh, dh, c.tag(3 * (l - 1) + 2), p.err, failed, c.spare,
               [&](int i, uint32_t v) { hw[i] = v; });
     }
     stamp<STAMP>(p, c.wg, l, 1);
     lds_barrier();  // B1: h_l ready
     if (p.gained) lds_barrier();  // B1g: gain * h_l formed
     if (self_routed(p, l)) {
-      ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
+      ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, c.spare, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
       int e;
       float w;
       wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
@@ -557,7 +576,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     }
     const uint32_t tA = c.tag(3 * l + 1);
     lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
-    ll_wait<16>(p.ll_act + (size_t)(c.wg % p.xr_a) * p.act_stride, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed,
+    ll_wait<16>(p.ll_act + (size_t)(c.wg % p.xr_a) * p.act_stride, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed, c.spare,
                 [&](int i, uint64_t v) {
       sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
       sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
@@ -573,14 +592,14 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     // buffer, needs h_{l+2}, which needs this workgroup's combine of layer l+1, which comes after
     // this read).
     if (has_head(p, l))
-      ll_wait(p.ll_g, (size_t)(l & 1) * p.H, p.H, tA, p.err, failed,
+      ll_wait(p.ll_g, (size_t)(l & 1) * p.H, p.H, tA, p.err, failed, c.spare,
               [&](int i, uint32_t v) { sm.g[i] = __uint_as_float(v); });
   }
   // Top-K of every head, off the token's critical path: head l predicts layer l+1's routing for
   // the next token; workgroup l % G handles head l.
   for (int l = c.wg; l + 1 < p.L; l += p.G) {
     if (!has_head(p, l)) continue;
-    ll_wait(p.ll_hlog, (size_t)l * p.E, p.E, c.tag(3 * l + 2), p.err, failed,
+    ll_wait(p.ll_hlog, (size_t)l * p.E, p.E, c.tag(3 * l + 2), p.err, failed, c.spare,
             [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
     int e;
     float w;
@@ -916,6 +935,7 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   c.cw = wave - 1;
   c.gw = c.wg * MW + c.cw;
+  c.spare = p.spare + (size_t)c.wg * 8;
   c.epoch = *p.epoch;
   const int LK = p.L * p.K;
   c.cur_i = p.ridx + (size_t)p.slot * LK;
@@ -992,8 +1012,9 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
 }
 
 struct StepWs {
-  size_t epoch, err, zero, logits, act, g, hlog, h, total;
+  size_t epoch, err, zero, logits, act, g, hlog, h, spare, total;
 };
+constexpr int SPARE_WGS = 1024;  // spare polling lines: one per workgroup
 constexpr int XR_MAX = 8;  // copies of h and of the SwiGLU outputs (one per XCD)
 static StepWs step_ws(const moe_decode_stack& st) {
   StepWs w{};
@@ -1005,7 +1026,8 @@ static StepWs step_ws(const moe_decode_stack& st) {
   w.g = w.act + XR_MAX * ll_bytes((size_t)st.K * st.d_ff);
   w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? 2 * (size_t)st.d_hidden : 1);  // two buffers, by layer parity
   w.h = w.hlog + ll_bytes((size_t)st.L * st.E);
-  w.total = w.h + XR_MAX * ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
+  w.spare = w.h + XR_MAX * ll_bytes((size_t)(st.L + 1) * (st.d_model / 2));
+  w.total = w.spare + (size_t)SPARE_WGS * 64;
   return w;
 }
 
@@ -1067,7 +1089,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   const StepPlan pl = plan_step(st, G);
   if (!pl.ok) return hipErrorInvalidValue;
   const StepWs w = step_ws(st);
-  if (w.total >= OFF_NONE) return hipErrorInvalidValue;
+  if (w.total >= OFF_NONE || pl.G > SPARE_WGS) return hipErrorInvalidValue;
   char* b = (char*)ws;
   StepParams p{};
   p.L = st.L;
@@ -1108,6 +1130,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
   p.ll_g = (uint64_t*)(b + w.g);
   p.ll_hlog = (uint64_t*)(b + w.hlog);
   p.ll_h = (uint64_t*)(b + w.h);
+  p.spare = (const uint64_t*)(b + w.spare);
   p.h_stride = (int)(ll_bytes((size_t)(st.L + 1) * (st.d_model / 2)) / 8);
   p.act_stride = (int)(ll_bytes((size_t)st.K * st.d_ff) / 8);
   p.xr_h = std::min(XR_MAX, WAVE / (pl.DR / 2));
