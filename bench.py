@@ -206,7 +206,7 @@ def cpu_model():
 
 
 STACK_WORKLOADS = ("decode35b", "widek8", "large-int4", "large-int2")
-WORKLOADS = STACK_WORKLOADS + ("tiny", "batched", "relu-sparse", "stream")
+WORKLOADS = STACK_WORKLOADS + ("tiny", "batched", "relu-sparse", "stream", "exchange")
 METRIC = "MoE-layer decode tokens/s at batch 1 + achieved HBM GB/s (% of peak)"
 
 
@@ -373,6 +373,66 @@ def exchange_probe(M, torch, dev, words):
     return res
 
 
+def bench_exchange(args, torch, M, dev):
+    """The exchange-latency probe over the shapes the decode kernel's design rests on (one
+    workgroup per compute unit): single hand-offs (rings across XCDs and inside one), and
+    all-to-all exchanges of 256..2,048 tagged words with the three polling-load forms, grouped
+    across the chip or inside one XCD, with and without eight copies."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Dv, Xv = M.MOE_XCHG_SCOPE_DEVICE, M.MOE_XCHG_SCOPE_XCD
+    forms = {0: "8-byte buffer loads", 1: "16-byte buffer loads", 2: "8-byte agent-scope atomic loads (global)"}
+    rows = []
+    epoch = [1]
+
+    def run(pattern, n, gs, xl, words, iters, ls, ss, reps_=1, wide=0):
+        cfg = M.moe_xchg_cfg(pattern, n, gs, xl, words, iters, ls, ss, 0, reps_, wide)
+        ws = torch.zeros(M.moe_exchange_probe_workspace_size(cfg), dtype=torch.uint8, device=dev)
+        out = torch.zeros(1 + 3 * n, dtype=torch.int32, device=dev)
+        vals, errs = [], 0
+        for _ in range(3):
+            epoch[0] += 1
+            cfg.epoch = epoch[0]
+            out.zero_()
+            M.moe_exchange_probe(cfg, ws, out)
+            torch.cuda.synchronize()
+            o = out.cpu().numpy().view("uint32").astype("int64")
+            errs += int(o[0])
+            ticks = o[1::3] | (o[2::3] << 32)
+            if pattern == M.MOE_XCHG_RING:
+                first = [b for b in range(n) if (b // (n // gs) if xl else b % gs) == 0]
+                vals.append(float(ticks[first].max()) / 100.0 / (iters * gs))
+            else:
+                vals.append(float(ticks.max()) / 100.0 / iters)
+        return round(sorted(vals)[1], 3), errs
+
+    R, A = M.MOE_XCHG_RING, M.MOE_XCHG_ALL
+    for label, gs, xl, ss in (("ring, hops across XCDs, device-coherent stores", 8, 0, Dv),
+                              ("ring, hops inside one XCD, device-coherent stores", 32, 1, Dv),
+                              ("ring, hops inside one XCD, stores to the XCD's L2", 32, 1, Xv)):
+        us, err = run(R, cus, gs, xl, 0, 100, Dv, ss)
+        rows.append({"pattern": "ring", "what": label, "us_per_hop": us, "timeouts": err})
+    for words in (256, 512, 1024, 2048):
+        for wide in (0, 1, 2):
+            if wide == 2 and words > 1024:
+                continue
+            us, err = run(A, cus, cus, 0, words, 200, Dv, Dv, 1, wide)
+            rows.append({"pattern": "all", "workgroups": cus, "group": cus, "words": words, "loads": forms[wide],
+                         "us_per_exchange": us, "timeouts": err})
+    for words, wide, reps_ in ((1024, 2, 8), (1024, 1, 8)):
+        us, err = run(A, cus, cus, 0, words, 200, Dv, Dv, reps_, wide)
+        rows.append({"pattern": "all", "workgroups": cus, "group": cus, "words": words, "loads": forms[wide],
+                     "copies": reps_, "us_per_exchange": us, "timeouts": err})
+    for words, wide, ss in ((1024, 2, Dv), (1024, 1, Dv), (512, 0, Xv)):
+        us, err = run(A, cus, 32, 1, words, 200, Dv, ss, 1, wide)
+        rows.append({"pattern": "all", "workgroups": cus, "group": "32 on one XCD (8 groups)", "words": words,
+                     "loads": forms[wide], "stores": "device" if ss == Dv else "XCD L2",
+                     "us_per_exchange": us, "timeouts": err})
+    return {"metric": "tagged-word exchange latency between resident workgroups (measurement aid)",
+            "unit": "us", "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "rows": rows,
+            "note": "one workgroup of one wave per compute unit; all: per phase, every workgroup publishes its "
+                    "slice and polls the whole vector (the period of such a loop); ring: one word passed on"}
+
+
 def phase_breakdown(layers, cfg, syn, torch, dev, M, tokens=12, warm=20):
     """Per-layer time split of the persistent kernel from its phase stamps (moe_decode_step_stamped,
     the global 100 MHz counter): medians over workgroups and over the inner layers of the last
@@ -533,6 +593,45 @@ def bench_stack(args, cfg, torch, M, S, dev):
                 "frac_of_peak": round(total_bytes / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 "note": "a 1 GiB streaming read before each token; the token's launch timed alone"}
         del graphs_c, stack_c, flush
+    # warm experts (the bound on prefetching a token's experts into the memory-side cache at token
+    # start): before each token, every expert the token will use in layers 1..L-1 (their routing
+    # is known then: the previous token's heads wrote it) is read once with the streaming probe,
+    # deepest layer first so that the first layers are the most recently touched; HIP events then
+    # time the token's launch alone.  Prerouted stacks only (a self-routed layer's experts are not
+    # known before the layer runs).
+    warm = None
+    if cfg.head_hidden and not args.no_cold:
+        fold = torch.empty(M.MOE_READ_PROBE_BLOCKS, dtype=torch.int32, device=dev)
+        stack_w = DecodeStack(layers, cfg.K, dev)
+        graphs_w = tm.capture(lambda t, h: stack_w.step(t, h))
+        n_warm = max(30, args.steps // 10) // 3 * 3
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_warm)]
+        touched = 0
+        with torch.cuda.stream(tm.stream):
+            tm.run(graphs_w, 30, 1)
+            for i in range(n_warm):
+                t = 31 + i
+                if t % 3 == 1:
+                    p = (t // 3 * 3) % tm.n_pool
+                    tm.ring.copy_(tm.pool[p:p + 3])
+                idx = stack_w.route_idx[t % 3].cpu()          # this token's routing (written by token t-1)
+                for l in range(cfg.L - 1, 0, -1):
+                    for e in idx[l].tolist():
+                        for mat in layers[l].experts.tensors:
+                            for arr in mat:
+                                M.moe_read_probe(arr[e], fold)
+                                touched += arr[e].numel() * arr[e].element_size()
+                evs[i][0].record(tm.stream)
+                graphs_w[(t - 1) % 3].replay()
+                evs[i][1].record(tm.stream)
+        torch.cuda.synchronize()
+        assert stack_w.step_error_word() == 0, "a wait inside the decode kernel ran out of time (warm)"
+        warm_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / n_warm
+        warm = {"tokens": n_warm, "avg_us": round(warm_us, 2), "tokens_per_s": round(1e6 / warm_us, 2),
+                "expert_bytes_touched_per_token": touched // n_warm,
+                "note": "each token's experts of layers 1..L-1 read into the caches just before the token "
+                        "(deepest layer first); the token's launch timed alone"}
+        del graphs_w, stack_w
     # measured HBM read ceiling: a plain 16-byte streaming read over 8 GiB
     buf = torch.empty(8 << 30, dtype=torch.uint8, device=dev)
     fold = torch.empty(M.MOE_READ_PROBE_BLOCKS, dtype=torch.int32, device=dev)
@@ -569,6 +668,7 @@ def bench_stack(args, cfg, torch, M, S, dev):
     rec["roofline"]["measured_read_ceiling_GBps"] = round(read_ceiling, 1)
     rec["roofline"]["frac_of_measured_ceiling"] = round(rec["roofline"]["achieved"] / read_ceiling, 4)
     rec["cold"] = cold
+    rec["warm_experts"] = warm
     if phases is not None:
         floor = xprobe["ring_hop_us"]
         rec["roofline"]["exchange_floor_us"] = floor
@@ -997,7 +1097,8 @@ def main():
                     help="decode35b (default, the headline line), widek8, large-int4, large-int2 (resident stacks "
                          "through the persistent kernel), tiny (d 256, one layer), batched (256 tokens per call), "
                          "relu-sparse (decode35b shapes, ReLU activation-sparse experts, per-layer calls), "
-                         "stream (decode35b with every expert in pinned host memory, HBM pools)")
+                         "stream (decode35b with every expert in pinned host memory, HBM pools), exchange (the "
+                         "exchange-latency probe's table)")
     ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
     ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
     ap.add_argument("--fork-every", type=int, default=8, help="stream workload: layers per prefetch fork")
@@ -1028,6 +1129,9 @@ def main():
     import moe_synth as S
 
     dev = torch.device("cuda:0")
+    if args.workload == "exchange":
+        print(json.dumps(bench_exchange(args, torch, M, dev)), flush=True)
+        return
     cfg = S.CONFIGS["decode35b" if args.workload in ("relu-sparse", "stream") else args.workload]
     if args.workload == "stream":
         rec = bench_stream(args, cfg, torch, M, S, dev)
