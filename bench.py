@@ -346,13 +346,16 @@ def exchange_probe(M, torch, dev, words):
     ring: one tagged word passed workgroup to workgroup (consecutive workgroups sit on different
     XCDs), the latency of one dependent hand-off; all: every workgroup publishes its slice of a
     `words`-word vector and polls it whole, phase after phase (the shape of the decode kernel's
-    exchanges), the period of such an exchange loop."""
+    exchanges: polled with 8-byte agent-scope atomic loads from one of eight copies, as the kernel
+    does, up to 1,024 words; 16-byte buffer loads beyond, a form the probe offers there), the
+    period of such an exchange loop."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.zeros(1 + 3 * cus, dtype=torch.int32, device=dev)
     res = {}
-    for name, pat, gs, w, it in (("ring_hop_us", M.MOE_XCHG_RING, 8, 0, 200),
-                                 ("all_exchange_us", M.MOE_XCHG_ALL, cus, words, 200)):
-        cfg = M.moe_xchg_cfg(pat, cus, gs, 0, w, it, M.MOE_XCHG_SCOPE_DEVICE, M.MOE_XCHG_SCOPE_DEVICE, 1, 1, 0)
+    wide = 2 if words <= 1024 else 1
+    for name, pat, gs, w, it, reps_, wd in (("ring_hop_us", M.MOE_XCHG_RING, 8, 0, 200, 1, 0),
+                                           ("all_exchange_us", M.MOE_XCHG_ALL, cus, words, 200, 8, wide)):
+        cfg = M.moe_xchg_cfg(pat, cus, gs, 0, w, it, M.MOE_XCHG_SCOPE_DEVICE, M.MOE_XCHG_SCOPE_DEVICE, 1, reps_, wd)
         ws = torch.zeros(M.moe_exchange_probe_workspace_size(cfg), dtype=torch.uint8, device=dev)
         vals = []
         for rep in range(3):
@@ -370,6 +373,7 @@ def exchange_probe(M, torch, dev, words):
         res[name] = round(sorted(vals)[1], 3)
     res["workgroups"] = cus
     res["words"] = words
+    res["all_exchange_loads"] = ("8-byte agent-scope atomic loads" if wide == 2 else "16-byte buffer loads") + ", 8 copies"
     return res
 
 
@@ -439,13 +443,17 @@ def phase_breakdown(layers, cfg, syn, torch, dev, M, tokens=12, warm=20):
     `tokens` tokens.  h_exchange / act_exchange: from the last workgroup's store of the vector to
     the median workgroup having all of it; gate_up: h seen -> SwiGLU outputs stored (median);
     store_spread: median -> last workgroup storing; act_to_down: all SwiGLU outputs in -> down
-    phase starts; down: down phase -> layer output stored."""
+    phase starts; down: down phase -> layer output stored.  On a stack whose layers route
+    themselves, the router phase too: router_dot (h seen -> the workgroup's logit stored),
+    logit_exchange (last logit stored -> the median polling wave has all E), topk (-> the compute
+    waves know the routing), to_gate_up_dots (routing known -> gate/up dot products done)."""
     import numpy as np
     from int4_expert_ffn_amd.chain import DecodeStack
     stack = DecodeStack(layers, cfg.K, dev)
     G = stack.grid()
     st = torch.zeros((G, cfg.L, 16), dtype=torch.int64, device=dev)
     hs = syn.hidden(17, warm + tokens, dev)
+    self_routed = not cfg.head_hidden
     rows, tok_us = [], []
     for t in range(warm + tokens):
         stack.step(t, hs[t], stamps=st if t >= warm else None)
@@ -466,6 +474,13 @@ def phase_breakdown(layers, cfg, syn, torch, dev, M, tokens=12, warm=20):
                     "h_store_spread": s[:, 6].max() - med(s[:, 6]),
                     "layer": med(nx[:, 1]) - med(s[:, 1]),
                 })
+                if self_routed:
+                    rows[-1].update({
+                        "router_dot": med(s[:, 10]) - med(s[:, 3]),
+                        "logit_exchange": med(s[:, 15]) - s[:, 10].max(),
+                        "topk": med(s[:, 11]) - med(s[:, 15]),
+                        "to_gate_up_dots": med(s[:, 8]) - med(s[:, 11]),
+                    })
     assert stack.step_error_word() == 0, "a wait inside the decode kernel ran out of time (stamped)"
     out = {k: round(float(np.median([r[k] for r in rows])), 3) for k in rows[0]}
     out["token_us"] = round(float(np.median(tok_us)), 1)

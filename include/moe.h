@@ -391,9 +391,10 @@ int32_t moe_decode_step_grid(const moe_decode_stack* st);
      2 g has unpacked all SwiGLU outputs of the layer, 3 g's first compute wave sees h_l,
      4 g's SwiGLU outputs are stored, 5 g's down phase starts, 6 g's rows of the layer's output
      are stored, 7 g's first compute wave has finished its head rows of the layer; finer marks of
-     the compute waves: 8 first wave's gate/up dot products done, 9 / 10 / 11 the SwiGLU output of
-     compute wave 1 / 4 / 2 ready, 12 the combine starts, 13 first wave's down dot products done,
-     14 / 15 down partials of compute wave 1 / 4 stored.
+     the first compute wave: 8 gate/up dot products done, 9 its SwiGLU output ready, 12 the combine
+     starts, 13 down dot products done, 14 down partials stored; on a layer that routes itself:
+     10 the first compute wave's router logit stored, 11 that wave knows the routing, 15 the polling
+     wave has all the router logits (slots 10, 11, 15 are left as they were on other layers).
    Results and every other argument as moe_decode_step.  This call runs a variant of the kernel with
    the stamp stores compiled in (a little slower); moe_decode_step runs the variant without them. */
 moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,

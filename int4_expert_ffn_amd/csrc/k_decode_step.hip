@@ -104,9 +104,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
 //   compute wave 1: 3 h_l seen (after the barrier), 4 this workgroup's SwiGLU outputs stored,
 //                   5 down phase starts, 6 this workgroup's rows of h_{l+1} stored, 7 head rows done,
 //                   8 gate/up dot products done, 9 its SwiGLU output ready (before the gathering
-//                   barrier), 12 the combine starts, 13 down dot products done, 14 down partials stored
-//   compute waves 4 and 2: 10 and 11, their SwiGLU output ready (wave 4 shares a SIMD with the poll
-//                   wave, wave 2 does not); compute wave 4: 15 its down partials stored
+//                   barrier), 12 the combine starts, 13 down dot products done, 14 down partials
+//                   stored; on a self-routed layer, 10 its router logit stored, 11 the routing known
+//   poll wave (self-routed layer): 15 all router logits unpacked (the top-K starts)
 // The plain variant compiles every stamp away.
 constexpr int NSTAMP = 16;
 template <bool STAMP>
@@ -563,6 +563,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
       ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, c.spare, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
       int e;
       float w;
+      stamp<STAMP>(p, c.wg, l, 15);
       wave_topk(sm.logit, p.E, p.K, p.topk_flags, e, w);
       if (lane < p.K) {
         sm.route_e[l * p.K + lane] = e;
@@ -716,8 +717,10 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         wave_sum_n(red);
         const float acc = red[0] / sqrtf(red[1] / (float)p.d + RMS_EPS);
         ll_put(ws, p, p.ll_logits, r, lead, __float_as_uint(acc), c.tag(3 * l));
+        stamp<STAMP>(p, wg, l, 10, cw == 0);
       }
       lds_barrier();  // B2
+      stamp<STAMP>(p, wg, l, 11, cw == 0);
     }
     if (self || l == 0) {  // no earlier phase has loaded this layer's weights
       issue_A<BITS, PG, NSH, NSF, GU, NH>(p, l, sm.route_e + l * K, c.prev_i ? sm.prev_e + l * K : nullptr, fc2_now,
@@ -770,8 +773,6 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
           if (lead) sm.aout[cw * GU + u] = A.bad[u] ? quiet_nan() : a;
         }
         stamp<STAMP>(p, wg, l, 9, cw == 0);
-        stamp<STAMP>(p, wg, l, 10, cw == 3);
-        stamp<STAMP>(p, wg, l, 11, cw == 1);
         // the workgroup's MW*GU consecutive outputs leave as one store of whole lines (partial
         // lines written by many waves were measured slower to reach the readers)
         lds_barrier();  // BA
@@ -890,7 +891,6 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       }
     }
     stamp<STAMP>(p, wg, l, 14, cw == 0);
-    stamp<STAMP>(p, wg, l, 15, cw == 3);
     if (prefetch)  // weights of B_{l+1}, one phase early
       issue_B<BITS, NSF, PD>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, B);
     lds_barrier();  // B4

@@ -167,6 +167,60 @@ def test_decode_step_deterministic_and_mixable(M):
     assert a.step_error_word() == 0 and a2.step_error_word() == 0 and b.step_error_word() == 0
 
 
+TIE_CASES = {
+    "widek8": replace(S.CONFIGS["widek8"], L=2),            # E 256, K 8: 4 logits per lane
+    "large-int4": replace(S.CONFIGS["large-int4"], L=2),    # E 512, K 4: 8 per lane
+    "widek8-E1024": replace(S.CONFIGS["widek8"], L=2, E=1024),  # 16 per lane
+}
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_decode_step_topk_exact_ties(M, name, renorm):
+    """Router rows repeated in runs of three, so every logit occurs three times (bit-identical
+    dot products, in the kernel as in float64): the top-K takes whole runs and then the
+    lower-indexed members of the run cut at K, in the oracle's order (larger logit first, equal
+    logits by lower expert index).  renorm False: weights from the softmax over all E logits.
+    Tokens are screened for gaps between distinct logits only."""
+    from int4_expert_ffn_amd.chain import DecodeStack, LayerWeights
+    cfg = TIE_CASES[name]
+    syn = S.Synth(cfg)
+    rep = (np.arange(cfg.E) // 3) * 3
+    routers_cpu = [syn.router(l, "cpu").numpy()[rep] for l in range(cfg.L)]
+    layers = [LayerWeights(device_layer(syn, l, DEV), torch.from_numpy(routers_cpu[l]).to(DEV), None)
+              for l in range(cfg.L)]
+    stack = DecodeStack(layers, cfg.K, DEV, renorm=renorm)
+    caches = [ExpertCache(syn, l) for l in range(cfg.L)]
+
+    def oracle(h0):
+        return O.chain_token(h0.numpy(), O.ChainState(cfg.L), E=cfg.E, K=cfg.K, bits=cfg.bits, group=cfg.group,
+                             router_get=lambda l: routers_cpu[l], head_get=lambda l: None,
+                             expert_get=lambda l, e: caches[l](e), renorm=renorm)
+
+    compared, seed = 0, 9100
+    while compared < 2:
+        assert seed < 9140, "no token with distinct logits well apart"
+        h0 = syn.hidden(seed, 1)[0]
+        seed += 1
+        hL, _, tr = oracle(h0)
+        distinct = [np.unique(t.route_logits)[::-1][: cfg.K + 1] for t in tr]
+        if min(np.min(u[:-1] - u[1:]) for u in distinct) < 1e-4:
+            continue
+        assert any(len(set(t.route_logits[t.idx].tolist())) < cfg.K for t in tr), "no tie inside the top-K"
+        stack.step(compared, h0.to(DEV))
+        torch.cuda.synchronize()
+        assert stack.step_error_word() == 0
+        slot = compared % 3
+        for l, t in enumerate(tr):
+            got_i = stack.route_idx[slot, l].cpu().numpy()
+            got_w = stack.route_w[slot, l].cpu().numpy().astype(np.float64)
+            assert np.array_equal(got_i, t.idx), f"layer {l}: {got_i.tolist()} vs oracle {t.idx.tolist()}"
+            assert np.allclose(got_w, t.w, rtol=1e-3, atol=1e-6), f"layer {l}: weights {got_w} vs {t.w}"
+        assert_rows_close(stack.h[cfg.L].float().cpu().numpy()[None], hL[None], what=f"{name} output")
+        log(f"{name} renorm={renorm} token {compared}: routing {[t.idx.tolist() for t in tr]}")
+        compared += 1
+
+
 @pytest.mark.parametrize("name", ["decode35b", "widek8"])
 def test_decode_step_stamped(M, name):
     """moe_decode_step_stamped gives bit-identical outputs and routing to the plain launch, and its
