@@ -66,6 +66,7 @@ struct StepParams {
   int slot, bootstrap, given;  // given: every layer's routing supplied by the caller
   int gained;                  // every layer's input norm has a gain (else none has)
   int rstage;                  // the compute waves stage each self-routed layer's router rows in LDS
+  int lshift;                  // router logit r fills words [r << lshift, (r + 1) << lshift), every one tagged
   uint32_t topk_flags;
   uint64_t *ll_logits, *ll_act, *ll_g, *ll_hlog, *ll_h;
   const uint64_t* spare;  // one 64-byte line per workgroup, never written
@@ -255,8 +256,30 @@ __device__ __forceinline__ uint32_t order_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Sorts N keys of one lane into descending order (Batcher's odd-even merge network; N a power of 2).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+    for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+      for (int j = q % p; j + q < N; j += 2 * q)
+#pragma unroll
+        for (int i = 0; i < q && i + j + q < N; ++i)
+          if ((i + j) / (2 * p) == (i + j + q) / (2 * p)) {
+            const uint64_t a = k[i + j], b = k[i + j + q];
+            k[i + j] = a > b ? a : b;
+            k[i + j + q] = a > b ? b : a;
+          }
+}
+
 // Softmax top-K of E logits held in LDS (one wave, VPL >= E / 64 logits per lane); idx/w land in
-// lanes 0..K-1.
+// lanes 0..K-1 (larger logit first; equal logits by lower expert index).  Each lane first sorts its
+// own VPL keys, so a round needs the wave maximum of one 32-bit word, the lanes' heads: the winner
+// is the lane holding it (found by a ballot), which then drops its head.  Only when several heads
+// share that word (equal logits) does a second maximum, over the index word, decide.  The weights
+// follow the same arithmetic in the same order as a plain K-round selection would.
 template <int VPL>
 __device__ __forceinline__ void wave_topk_v(const float* lt, int E, int K, uint32_t flags, int& out_e, float& out_w) {
   const int lane = threadIdx.x % WAVE;
@@ -268,27 +291,37 @@ __device__ __forceinline__ void wave_topk_v(const float* lt, int E, int K, uint3
     val[j] = e < E ? lt[e] : 0.f;
     key[j] = e < E ? ((uint64_t)order_bits(val[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
   }
-  float top = 0.f, den = 0.f, mine_v = 0.f;
+  sort_desc<VPL>(key);
+  float top = 0.f, mine_v = 0.f;
   int mine_e = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
+    const uint32_t hh = (uint32_t)(key[0] >> 32);
+    const uint32_t hi = wave_max_u32(hh);
+    uint64_t m = __ballot(hh == hi);
+    uint32_t lo;
+    if (__popcll(m) == 1) {
+      lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], (int)__builtin_ctzll(m));
+    } else {
+      lo = wave_max_u32(hh == hi ? (uint32_t)key[0] : 0u);
+      m = __ballot(key[0] == (((uint64_t)hi << 32) | lo));
+    }
+    if (lane == (int)__builtin_ctzll(m)) {
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) best = key[j] > best ? key[j] : best;
-    const uint32_t hi = wave_max_u32((uint32_t)(best >> 32));
-    const uint32_t lo = wave_max_u32((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
-    const uint64_t t = ((uint64_t)hi << 32) | lo;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j)
-      if (key[j] == t) key[j] = 0;
+      for (int j = 0; j + 1 < VPL; ++j) key[j] = key[j + 1];
+      key[VPL - 1] = 0;
+    }
     const float v = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
     if (k == 0) top = v;
-    if (flags & MOE_TOPK_RENORM) den += expf(v - top);
     if (lane == k) {
       mine_e = (int)(0xFFFFFFFFu - lo);
       mine_v = v;
     }
   }
-  if (!(flags & MOE_TOPK_RENORM)) {
+  const float x = expf(mine_v - top);
+  float den = 0.f;
+  if (flags & MOE_TOPK_RENORM) {
+    for (int k = 0; k < K; ++k) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+  } else {
     float part = 0.f;
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
@@ -296,11 +329,12 @@ __device__ __forceinline__ void wave_topk_v(const float* lt, int E, int K, uint3
     den = wave_sum(part);
   }
   out_e = mine_e;
-  out_w = expf(mine_v - top) / den;
+  out_w = x / den;
 }
-// K rounds of a wave-wide maximum over VPL keys per lane: holding only the E / 64 keys a lane
-// needs (rather than the 16 of the largest E) cuts each round's work four-fold at E = 256, where
-// the selection of the K = 8 routing took 4.3 us on a SIMD shared with two compute waves.
+// VPL from E: each lane holds only the E / 64 keys it needs (rather than the 16 of the largest E),
+// which keeps its sort and its per-round shift short.  A single wave issues at a quarter of the
+// SIMD's rate, so the selection is a chain of dependent instructions: K = 8 of 256 took 2.5 us as
+// K rounds of two wave maxima over unsorted keys, 2.0 us with sorted heads.
 __device__ __forceinline__ void wave_topk(const float* lt, int E, int K, uint32_t flags, int& out_e, float& out_w) {
   if (E <= 4 * WAVE)
     wave_topk_v<4>(lt, E, K, flags, out_e, out_w);
@@ -560,7 +594,7 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     lds_barrier();  // B1: h_l ready
     if (p.gained) lds_barrier();  // B1g: gain * h_l formed
     if (self_routed(p, l)) {
-      ll_wait(p.ll_logits, 0, p.E, c.tag(3 * l), p.err, failed, c.spare, [&](int i, uint32_t v) { sm.logit[i] = __uint_as_float(v); });
+      ll_wait(p.ll_logits, 0, p.E << p.lshift, c.tag(3 * l), p.err, failed, c.spare, [&](int i, uint32_t v) { sm.logit[i >> p.lshift] = __uint_as_float(v); });
       int e;
       float w;
       stamp<STAMP>(p, c.wg, l, 15);
@@ -716,7 +750,10 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
         }
         wave_sum_n(red);
         const float acc = red[0] / sqrtf(red[1] / (float)p.d + RMS_EPS);
-        ll_put(ws, p, p.ll_logits, r, lead, __float_as_uint(acc), c.tag(3 * l));
+        // the logit in 1 << lshift consecutive words (one store from as many lanes): at E <= 256 four
+        // writers share a 128-byte line instead of sixteen, and the exchange took 2.5 us against
+        // 3.5 us; the pollers read the same count of lines as for the 1,024-word h
+        ll_put(ws, p, p.ll_logits, ((size_t)r << p.lshift) + lane, lane < (1 << p.lshift), __float_as_uint(acc), c.tag(3 * l));
         stamp<STAMP>(p, wg, l, 10, cw == 0);
       }
       lds_barrier();  // B2
@@ -1022,7 +1059,7 @@ static StepWs step_ws(const moe_decode_stack& st) {
   w.err = 4;
   w.zero = 8;  // 8 bytes that stay zero
   w.logits = 256;
-  w.act = w.logits + ll_bytes(st.E);
+  w.act = w.logits + ll_bytes(4 * (size_t)st.E);  // E logits, each in up to 4 words
   w.g = w.act + XR_MAX * ll_bytes((size_t)st.K * st.d_ff);
   w.hlog = w.g + ll_bytes(st.d_hidden > 0 ? 2 * (size_t)st.d_hidden : 1);  // two buffers, by layer parity
   w.h = w.hlog + ll_bytes((size_t)st.L * st.E);
@@ -1123,6 +1160,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
     const int rows = (st.E + pl.G - 1) / pl.G;  // router rows of the busiest workgroup (row r: wave r / G)
     p.rstage = rows <= RWG && rows * st.d_model <= LDS_RR;
   }
+  p.lshift = st.E <= 256 ? 2 : st.E <= 512 ? 1 : 0;  // up to 1,024 polled words (one pass of 16 per lane)
   p.bootstrap = token == 0 && !p.given;
   p.topk_flags = flags & MOE_TOPK_RENORM;
   p.ll_logits = (uint64_t*)(b + w.logits);
