@@ -383,6 +383,12 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
    unit that holds a slice of the rows), or 0 if the stack is not supported by it. */
 int32_t moe_decode_step_grid(const moe_decode_stack* st);
 
+/* The same for a device with `compute_units` compute units: the workgroups a launch there would
+   use, or 0 if that device could not run the stack (moe_decode_step returns MOE_ERR_UNSUPPORTED
+   there).  Host-only: reads only the shape fields of `st` (not its device arrays) and touches no
+   device.  compute_units < 1 or a NULL or malformed stack gives 0. */
+int32_t moe_decode_step_grid_for(const moe_decode_stack* st, int32_t compute_units);
+
 /* Measurement aid, not a step of the method: moe_decode_step that also writes phase stamps of the
    device's 100 MHz real-time counter (one clock for every compute unit, so stamps of different
    workgroups compare).  stamps: uint64 [G][L][16] (device, 8-byte aligned, stamp_bytes >=

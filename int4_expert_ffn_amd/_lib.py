@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_status_string", "moe_version", "moe_decode_workspace_size", "moe_decode_step",
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
     "moe_stream_in_many", "moe_read_probe", "moe_exchange_probe_workspace_size", "moe_exchange_probe",
-    "moe_decode_step_grid", "moe_decode_step_stamped", "moe_expert_ffn_q4_noalloc",
+    "moe_decode_step_grid", "moe_decode_step_stamped", "moe_expert_ffn_q4_noalloc", "moe_decode_step_grid_for",
 )
 
 
@@ -123,6 +123,7 @@ def _load():
         "moe_decode_workspace_size": (sz, [ctypes.POINTER(moe_decode_stack)]),
         "moe_decode_step": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, vp, sz]),
         "moe_decode_step_grid": (i32, [ctypes.POINTER(moe_decode_stack)]),
+        "moe_decode_step_grid_for": (i32, [ctypes.POINTER(moe_decode_stack), i32]),
         "moe_decode_step_stamped": (st, [vp, ctypes.POINTER(moe_decode_stack), i32, u32, vp, vp, vp, vp, sz, vp, sz]),
         "moe_version": (i32, []),
     }
@@ -498,6 +499,10 @@ def moe_decode_step(stack: "moe_decode_stack", token, flags, h_in, h_out, worksp
 
 def moe_decode_step_grid(stack: "moe_decode_stack") -> int:
     return _lib.moe_decode_step_grid(ctypes.byref(stack))
+
+
+def moe_decode_step_grid_for(stack: "moe_decode_stack", compute_units: int) -> int:
+    return _lib.moe_decode_step_grid_for(ctypes.byref(stack), int(compute_units))
 
 
 def moe_decode_step_stamped(stack: "moe_decode_stack", token, flags, h_in, h_out, stamps, workspace,

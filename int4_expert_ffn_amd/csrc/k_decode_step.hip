@@ -1007,6 +1007,8 @@ struct StepPlan {
 
 static bool has_variant(int bits, int PG, int NSH, int NSF, int GU, int PD, int NH);
 
+constexpr int SPARE_WGS = 1024;  // spare polling lines: one per workgroup
+
 static StepPlan plan_step(const moe_decode_stack& st, int cus) {
   StepPlan pl{};
   const int d = st.d_model, I = st.d_ff, E = st.E, K = st.K, H = st.d_hidden, bits = st.bits;
@@ -1028,6 +1030,7 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
   pl.DR += pl.DR & 1;
   if (pl.DR > WAVE || K * pl.DR > LDS_PART) return pl;
   pl.G = (d + pl.DR - 1) / pl.DR;
+  if (pl.G > SPARE_WGS) return pl;  // one spare polling line per workgroup
   const int GW = pl.G * MW;
   pl.DI = (pl.DR + RPI - 1) / RPI;
   pl.PD = (K * pl.DI + MW - 1) / MW;
@@ -1051,7 +1054,6 @@ static StepPlan plan_step(const moe_decode_stack& st, int cus) {
 struct StepWs {
   size_t epoch, err, zero, logits, act, g, hlog, h, spare, total;
 };
-constexpr int SPARE_WGS = 1024;  // spare polling lines: one per workgroup
 constexpr int XR_MAX = 8;  // copies of h and of the SwiGLU outputs (one per XCD)
 static StepWs step_ws(const moe_decode_stack& st) {
   StepWs w{};
@@ -1115,8 +1117,10 @@ bool decode_step_supported(const moe_decode_stack& st) { return plan_step(st, de
 
 size_t decode_step_workspace(const moe_decode_stack& st) { return step_ws(st).total; }
 
-int decode_step_grid(const moe_decode_stack& st) {
-  const StepPlan pl = plan_step(st, device_cus());
+int decode_step_grid(const moe_decode_stack& st) { return decode_step_grid_for(st, device_cus()); }
+
+int decode_step_grid_for(const moe_decode_stack& st, int cus) {
+  const StepPlan pl = plan_step(st, cus);
   return pl.ok ? pl.G : 0;
 }
 

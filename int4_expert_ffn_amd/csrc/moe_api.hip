@@ -454,10 +454,17 @@ moe_status moe_decode_step(void* stream, const moe_decode_stack* st, int32_t tok
   return from_hip(launch_decode_step((hipStream_t)stream, *st, token, flags, h_in, h_out, h_layers, workspace));
 }
 
+static bool decode_stack_shape_ok(const moe_decode_stack* st) {
+  if (!st || st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return false;
+  return (st->bits == 4 || st->bits == 2) && st->d_model >= 1 && st->d_ff >= 1 && st->d_hidden >= 0;
+}
+
 int32_t moe_decode_step_grid(const moe_decode_stack* st) {
-  if (!st || st->L < 1 || st->L > 256 || !routing_dims_ok(1, st->E, st->K)) return 0;
-  if ((st->bits != 4 && st->bits != 2) || st->d_model < 1 || st->d_ff < 1 || st->d_hidden < 0) return 0;
-  return decode_step_grid(*st);
+  return decode_stack_shape_ok(st) ? decode_step_grid(*st) : 0;
+}
+
+int32_t moe_decode_step_grid_for(const moe_decode_stack* st, int32_t compute_units) {
+  return decode_stack_shape_ok(st) && compute_units >= 1 ? decode_step_grid_for(*st, compute_units) : 0;
 }
 
 moe_status moe_decode_step_stamped(void* stream, const moe_decode_stack* st, int32_t token, uint32_t flags,

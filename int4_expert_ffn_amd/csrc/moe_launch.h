@@ -83,6 +83,7 @@ hipError_t launch_decode_step(hipStream_t s, const moe_decode_stack& st, int tok
                               const uint16_t* h_in, uint16_t* h_out, uint16_t* h_layers, void* ws,
                               uint64_t* stamps = nullptr);
 int decode_step_grid(const moe_decode_stack& st);  // workgroups of one launch (0: unsupported)
+int decode_step_grid_for(const moe_decode_stack& st, int cus);  // the same on a device with `cus` CUs
 
 // expert streaming into an HBM pool --------------------------------------------------------------
 struct PoolArgs {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -220,6 +220,35 @@ def test_prerouter_and_combine_reject():
     assert c(1, 17, 2048, FAKE, FAKE, FAKE, None, FAKE) == INVALID
     assert c(1, 4, 2048, None, FAKE, FAKE, None, FAKE) == INVALID
     assert c(1, 4, 2048, FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_decode_step_grid_for_other_cu_counts():
+    """The persistent kernel's plan on devices with other compute-unit counts (host-only): the four
+    stacks it is built for take one workgroup per compute unit on a 256-CU device; elsewhere a plan
+    is either refused (0: the call returns MOE_ERR_UNSUPPORTED there) or uses at most one workgroup
+    per compute unit, so a plan that passes never needs more workgroups than can be resident."""
+    gf = lambda stk, n: L.moe_decode_step_grid_for(ctypes.byref(stk), n)
+    shapes = {  # L, E, K, d_model, d_ff, bits, group, d_hidden
+        "decode35b": (40, 256, 4, 2048, 512, 4, 64, 1024),
+        "widek8": (24, 256, 8, 2048, 512, 4, 64, 0),
+        "large-int4": (15, 512, 4, 4096, 1024, 4, 64, 0),
+        "large-int2": (15, 512, 4, 4096, 1024, 2, 64, 0),
+    }
+    for name, shp in shapes.items():
+        st = lib_mod.moe_decode_stack(*shp, FAKE, FAKE, FAKE)
+        assert gf(st, 256) == 256, name
+        assert gf(st, 0) == 0 and gf(st, -8) == 0
+        for n in (1, 8, 64, 80, 104, 120, 128, 160, 200, 228, 240, 255, 257, 304, 512, 1024, 4096, 1 << 20):
+            g = gf(st, n)
+            assert g == 0 or 1 <= g <= min(n, 1024), (name, n, g)
+        # no device here: the current-device query and the call itself both refuse the stack
+        assert L.moe_decode_step_grid(ctypes.byref(st)) == 0
+        assert L.moe_decode_step(None, ctypes.byref(st), 1, 1, FAKE, FAKE, None, FAKE, 1 << 40) == UNSUP
+    assert L.moe_decode_step_grid_for(None, 256) == 0
+    tiny = lib_mod.moe_decode_stack(1, 16, 2, 256, 128, 4, 32, 0, FAKE, FAKE, FAKE)
+    assert gf(tiny, 256) == 0                   # d_model 256: per-layer calls only
+    bad = lib_mod.moe_decode_stack(40, 256, 9, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
+    assert gf(bad, 256) == 0                    # K > 8
 
 
 def test_workspace_sizes_closed_form():
