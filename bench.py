@@ -756,9 +756,9 @@ def bench_batched(args, cfg, torch, M, S, dev):
     n_in = 8
     hs = syn.hidden(11, n_in * T, dev).view(n_in, T, d)
     y = torch.empty((T, d), dtype=torch.float16, device=dev)
-    for cp in copies:      # the shared expert runs on a second stream beside the routed ones
+    for cp in copies:
         cp["layer"] = BatchedLayer(cp["ex"], cp["router"], T, K, dev, shared=cp["sh"], lora3=cp["lora"],
-                                   two_streams=not args.one_stream)
+                                   two_streams=not args.one_stream, separate=args.separate_shared)
 
     def layer(cp, h):
         cp["layer"](h, y)
@@ -802,9 +802,10 @@ def bench_batched(args, cfg, torch, M, S, dev):
     lora_b = sum(2 * (r.numel() + b.numel()) for r, b in [syn.lora(0, "cpu")[m] for m in S.MATS])
     nbytes = int(round(mean_used * eb + eb + E * d * 2 + lora_b + 2 * T * d * 2))
     rec = base_record(args, cfg, steps * T / wall, wall, steps)
+    sched = ("shared expert + LoRA as its own call, " + ("after the routed experts" if args.one_stream else
+             "on a second stream")) if args.separate_shared else "shared expert + LoRA sorted in with the routed pairs"
     rec["roofline"] = roofline("the batched layer: router GEMM + top-K, sort, grouped MFMA gate/up and down, "
-                               "shared expert + LoRA (on a second stream), combine (one graph per batch)", nbytes, us,
-                               None)
+                               f"{sched}, combine (one graph per batch)", nbytes, us, None)
     rec["roofline"]["used_experts_mean"] = round(mean_used, 2)
     rec["batch_us"] = round(us, 2)
     if not args.no_cpu_baseline:
@@ -1115,7 +1116,10 @@ def main():
                          "stream (decode35b with every expert in pinned host memory, HBM pools), exchange (the "
                          "exchange-latency probe's table)")
     ap.add_argument("--pool-slots", type=int, default=32, help="stream workload: HBM pool slots per layer")
-    ap.add_argument("--one-stream", action="store_true", help="batched workload: the shared expert on the main stream")
+    ap.add_argument("--separate-shared", action="store_true",
+                    help="batched workload: the shared expert as its own call (on a second stream unless --one-stream)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="batched workload with --separate-shared: the shared expert on the main stream")
     ap.add_argument("--fork-every", type=int, default=8, help="stream workload: layers per prefetch fork")
     ap.add_argument("--no-cold", action="store_true", help="stack workloads: skip the cold-token timing")
     ap.add_argument("--no-histogram", action="store_true", help="stack workloads: skip the routing histogram")

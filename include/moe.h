@@ -168,6 +168,27 @@ moe_status moe_expert_ffn_q4_noalloc(void* stream, int32_t T, int32_t K, uint32_
                                      const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
                                      const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse);
 
+/* Bytes of device workspace moe_expert_ffn_q4_shared needs (0 when T < 32). */
+size_t moe_expert_ffn_shared_workspace_size(int32_t T, int32_t K, const moe_experts* ex);
+
+/* S3-S7 of a batched layer with a shared expert ("La otra mitad del muro de la memoria ...",
+   section "Ejecución del adaptador no fusionado": an always-on shared path whose LoRA runs
+   unmerged, W v + (alpha / r) B (A v)) in one call:
+     y[t] = r[t] + sum_k w[t][k] FFN_{idx[t][k]}(x_t) + FFN_shared(x_t)        (float16 out)
+   FFN as in moe_expert_ffn_q4; the LoRA (lora3, may be NULL) is the shared expert's.  The shared
+   expert's T (token) rows join the routed (token, slot) pairs as one more expert of the sort, so
+   one grouped GEMM launch per projection covers both; the result equals moe_expert_ffn_q4 on the
+   routed experts, moe_expert_ffn_q4 on the shared expert (K = 1, lora3) and moe_combine with its
+   output as `shared`, to the bit.  shared: one expert (n_experts == 1) of the same d_model, d_ff,
+   bits and group as ex.  w [T][K] float32, r [T][d] float16 and y all required.  T >= 32 (the
+   batched path; MOE_ERR_UNSUPPORTED below it: use the two calls and moe_combine).  workspace:
+   moe_expert_ffn_shared_workspace_size bytes, 256-byte aligned.  Other limits and errors as
+   moe_expert_ffn_q4. */
+moe_status moe_expert_ffn_q4_shared(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                    const int32_t* idx, const moe_experts* ex, const moe_experts* shared,
+                                    const moe_lora* lora3, const float* w, const uint16_t* r, uint16_t* y,
+                                    void* workspace, size_t workspace_bytes);
+
 /* Bytes of device workspace moe_expert_ffn_sparse needs for T tokens with K experts each. */
 size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex);
 

@@ -13,5 +13,5 @@ from ._lib import (  # noqa: F401
     moe_read_probe, MOE_READ_PROBE_BLOCKS, moe_exchange_probe, moe_exchange_probe_workspace_size, moe_xchg_cfg,
     MOE_XCHG_ALL, MOE_XCHG_RING, MOE_XCHG_SCOPE_DEVICE, MOE_XCHG_SCOPE_XCD, moe_decode_step_grid,
     moe_decode_step_stamped, moe_expert_ffn_q4_noalloc, MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_TOO_LARGE,
-    moe_decode_step_grid_for,
+    moe_decode_step_grid_for, moe_expert_ffn_q4_shared, moe_expert_ffn_shared_workspace_size,
 )

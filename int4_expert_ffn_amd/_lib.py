@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_expert_ffn_sparse_workspace_size", "moe_expert_ffn_sparse", "moe_stream_workspace_size", "moe_stream_in",
     "moe_stream_in_many", "moe_read_probe", "moe_exchange_probe_workspace_size", "moe_exchange_probe",
     "moe_decode_step_grid", "moe_decode_step_stamped", "moe_expert_ffn_q4_noalloc", "moe_decode_step_grid_for",
+    "moe_expert_ffn_shared_workspace_size", "moe_expert_ffn_q4_shared",
 )
 
 
@@ -106,6 +107,9 @@ def _load():
                                    vp, vp, vp, vp, vp, sz]),
         "moe_expert_ffn_q4_noalloc": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts),
                                            ctypes.POINTER(moe_lora), vp, vp, vp, vp]),
+        "moe_expert_ffn_shared_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
+        "moe_expert_ffn_q4_shared": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts),
+                                          ctypes.POINTER(moe_experts), ctypes.POINTER(moe_lora), vp, vp, vp, vp, sz]),
         "moe_expert_ffn_sparse_workspace_size": (sz, [i32, i32, ctypes.POINTER(moe_experts)]),
         "moe_expert_ffn_sparse": (st, [vp, i32, i32, u32, vp, vp, ctypes.POINTER(moe_experts), vp, vp, vp, vp, vp,
                                        vp, sz]),
@@ -343,6 +347,29 @@ def moe_expert_ffn_q4_noalloc(T, K, flags, x, idx, ex: Experts, lora3: Optional[
                                         _ptr(out, _f32(), "out"), _ptr(w_fuse, _f32(), "w_fuse"),
                                         _ptr(r_fuse, _f16(), "r_fuse"), _ptr(y_fuse, _f16(), "y_fuse"))
     _check(st, "moe_expert_ffn_q4_noalloc")
+
+
+def moe_expert_ffn_shared_workspace_size(T, K, ex: Experts) -> int:
+    return _lib.moe_expert_ffn_shared_workspace_size(T, K, ctypes.byref(ex.desc))
+
+
+def moe_expert_ffn_q4_shared(T, K, flags, x, idx, ex: Experts, shared: Experts, lora3: Optional[Lora3], w, r, y,
+                             workspace, workspace_bytes=None, stream=None):
+    """Routed experts + a shared expert (with its LoRA) + the combine in one call: y = r + sum_k w_k o_k
+    + shared."""
+    d = ex.d
+    _need(x, T * d, "x")
+    _need(idx, T * K, "idx")
+    _need(w, T * K, "w")
+    _need(r, T * d, "r")
+    _need(y, T * d, "y")
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    st = _lib.moe_expert_ffn_q4_shared(_stream(stream, x, idx), T, K, flags, _ptr(x, _f16(), "x"),
+                                       _ptr(idx, _i32(), "idx"), ctypes.byref(ex.desc), ctypes.byref(shared.desc),
+                                       ctypes.cast(lora3.desc, ctypes.POINTER(moe_lora)) if lora3 is not None else None,
+                                       _ptr(w, _f32(), "w"), _ptr(r, _f16(), "r"), _ptr(y, _f16(), "y"),
+                                       _ptr(workspace, None, "workspace"), nbytes)
+    _check(st, "moe_expert_ffn_q4_shared")
 
 
 def moe_expert_ffn_sparse_workspace_size(T, K, ex: Experts) -> int:

@@ -41,12 +41,19 @@ __device__ __forceinline__ float lora_row(const LoraRef& lr, int t, int row) {
 
 // u[t][r] = s_t * sum_i A[r][i] v_t[i]; one wave per (t, r).  s_t is the RMS-norm factor of v_t
 // when `rmsnorm`, else 1.
+// One wave per (token, rank row) of each of the n_mat (1 or 2) matrices A / A2 on the same v.
 __global__ void __launch_bounds__(256) k_lora_a(int T, int n_in, int rank, int rmsnorm,
                                                 const uint16_t* __restrict__ v, size_t v_stride,
-                                                const uint16_t* __restrict__ A, float* __restrict__ u) {
-  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
+                                                const uint16_t* __restrict__ A, float* __restrict__ u,
+                                                const uint16_t* __restrict__ A2, float* __restrict__ u2) {
+  int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
   const int lane = threadIdx.x % WAVE;
-  if (wave >= T * rank) return;
+  if (wave >= T * rank) {  // the second matrix's waves (uniform over the wave)
+    if (A2 == nullptr || wave >= 2 * T * rank) return;
+    wave -= T * rank;
+    A = A2;
+    u = u2;
+  }
   const int t = wave / rank, r = wave % rank;
   const uint16_t* vr = v + (size_t)t * v_stride;
   const uint16_t* ar = A + (size_t)r * n_in;
@@ -496,8 +503,9 @@ hipError_t launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const 
 }  // namespace
 
 hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,
-                         size_t v_stride, const uint16_t* A, float* u) {
-  return launch(k_lora_a, dim3((waves + 3) / 4), dim3(256), 0, s, T, n_in, rank, rmsnorm, v, v_stride, A, u);
+                         size_t v_stride, const uint16_t* A, float* u, const uint16_t* A2, float* u2) {
+  const int all = A2 ? 2 * waves : waves;
+  return launch(k_lora_a, dim3((all + 3) / 4), dim3(256), 0, s, T, n_in, rank, rmsnorm, v, v_stride, A, u, A2, u2);
 }
 
 bool decode_shape_supported(int bits, int group, int d, int I) {
@@ -512,10 +520,13 @@ hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a) {
   if (a.lora3) {
     const moe_lora* L3 = a.lora3;
     const int wg = a.T * L3[0].rank, wu = a.T * L3[1].rank;
-    err = first_error(err, launch(k_lora_a, dim3((wg + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[0].rank, rms, a.x,
-                                  (size_t)a.d, L3[0].A, a.u_gate));
-    err = first_error(err, launch(k_lora_a, dim3((wu + 3) / 4), dim3(256), 0, s, a.T, a.d, L3[1].rank, rms, a.x,
-                                  (size_t)a.d, L3[1].A, a.u_up));
+    if (wg == wu) {  // gate's and up's A . x in one launch
+      err = first_error(err, launch_lora_a(s, wg, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate,
+                                           L3[1].A, a.u_up));
+    } else {
+      err = first_error(err, launch_lora_a(s, wg, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate));
+      err = first_error(err, launch_lora_a(s, wu, a.T, a.d, L3[1].rank, rms, a.x, (size_t)a.d, L3[1].A, a.u_up));
+    }
     lg = LoraRef{L3[0].B, a.u_gate, L3[0].rank, L3[0].alpha / (float)L3[0].rank};
     lu = LoraRef{L3[1].B, a.u_up, L3[1].rank, L3[1].alpha / (float)L3[1].rank};
     ldn = LoraRef{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank};

@@ -26,35 +26,43 @@ namespace {
 
 // ------------------------------------------------------------------------------------- sort
 constexpr int MT = 16;  // token rows per MFMA tile
+// Work-list record of one tile: bucket, first sorted position inside the bucket, the bucket's
+// start in perm and its pair count, then the tile's MT pair indices (-1 past the bucket's end).
+// A GEMM block reads everything it needs before its first weight and activation loads from this
+// one record, instead of a chain of dependent loads (bucket -> offsets -> perm -> activations).
+constexpr int TREC = 4 + MT;
 
 // One block of 1024 threads.  counts[E+1], offsets[E+2] (bucket E collects indices outside
 // [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles (may
-// be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one (bucket, first
-// sorted position inside the bucket) pair per MT-row tile, buckets in order.
+// be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one TREC-int record per
+// MT-row tile, buckets in order.
 __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __restrict__ idx,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
-                                               int max_tiles) {
+                                               int max_tiles, int TS) {
+  // TS > 0: pairs TK .. TK + TS - 1 form one more bucket, E + 1 (a shared expert's, one per token)
+  const int NB = E + 1 + (TS > 0 ? 1 : 0), LB = NB - 1, NP = TK + TS;  // buckets, the last, pairs
   extern __shared__ int sh[];
-  int* run = sh;              // [E+1]
-  int* offs = sh + E + 1;     // [E+2]
-  int* toff = offs + E + 2;   // [E+2] first tile of each bucket
-  int* ctot = toff + E + 2;   // [E+1] pairs of each bucket in the current chunk
-  int* hist = ctot + E + 1;   // [bs / WAVE][E+1] per-wave bucket counts of a chunk, then their prefixes
+  int* run = sh;               // [NB]
+  int* offs = sh + NB;         // [NB+1]
+  int* toff = offs + NB + 1;   // [NB+1] first tile of each bucket
+  int* ctot = toff + NB + 1;   // [NB] pairs of each bucket in the current chunk
+  int* hist = ctot + NB;       // [bs / WAVE][NB] per-wave bucket counts of a chunk, then their prefixes
   __shared__ int wsum[2][16];
   const int tid = threadIdx.x, bs = blockDim.x, lane = tid % WAVE, w = tid / WAVE;
-  for (int i = tid; i <= E; i += bs) run[i] = 0;
+  const auto bucket = [&](int p) {
+    if (p >= TK) return E + 1;
+    const int e = idx[p];
+    return (unsigned)e >= (unsigned)E ? E : e;
+  };
+  for (int i = tid; i <= LB; i += bs) run[i] = 0;
   __syncthreads();
-  for (int p = tid; p < TK; p += bs) {
-    int e = idx[p];
-    if ((unsigned)e >= (unsigned)E) e = E;
-    atomicAdd(&run[e], 1);
-  }
+  for (int p = tid; p < NP; p += bs) atomicAdd(&run[bucket(p)], 1);
   __syncthreads();
-  // exclusive scans of the pair counts and of the tile counts over buckets 0..E (E + 1 <= 2 bs),
+  // exclusive scans of the pair counts and of the tile counts over buckets 0..LB (NB <= 2 bs),
   // two buckets per thread
   const int b0 = 2 * tid, b1 = b0 + 1;
-  const int c0 = b0 <= E ? run[b0] : 0, c1 = b1 <= E ? run[b1] : 0;
+  const int c0 = b0 <= LB ? run[b0] : 0, c1 = b1 <= LB ? run[b1] : 0;
   const int t0 = (c0 + MT - 1) / MT, t1 = (c1 + MT - 1) / MT;
   int v = c0 + c1, u = t0 + t1;
   for (int o = 1; o < WAVE; o <<= 1) {
@@ -74,66 +82,82 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
     u += wsum[1][j];
   }
   const int ev = v - c0 - c1, eu = u - t0 - t1;  // exclusive through bucket b0
-  if (b0 <= E) {
+  if (b0 <= LB) {
     offs[b0] = ev;
     toff[b0] = eu;
   }
-  if (b1 <= E) {
+  if (b1 <= LB) {
     offs[b1] = ev + c0;
     toff[b1] = eu + t0;
   }
-  if (b0 == E || b1 == E) {
-    offs[E + 1] = v;
-    toff[E + 1] = u;
+  if (b0 == LB || b1 == LB) {
+    offs[NB] = v;
+    toff[NB] = u;
   }
   __syncthreads();
-  for (int i = tid; i <= E + 1; i += bs) {
+  if (TS > 0) {  // the shared bucket's tiles go first in the work list (its weights are the same for
+                 // every tile, so they come from the caches, and the list's tail is left to HBM tiles)
+    const int ts = toff[NB] - toff[LB];
+    __syncthreads();
+    for (int b = tid; b < LB; b += bs) toff[b] += ts;
+    if (tid == 0) toff[LB] = 0;
+    __syncthreads();
+  }
+  for (int i = tid; i <= NB; i += bs) {
     offsets[i] = offs[i];
-    if (i <= E) counts[i] = run[i];
+    if (i <= LB) counts[i] = run[i];
   }
   if (tiles != nullptr) {
-    if (tid == 0) tiles[0] = min(toff[E + 1], max_tiles);
-    for (int e = tid; e <= E; e += bs)
+    if (tid == 0) tiles[0] = min(toff[NB], max_tiles);
+    for (int e = tid; e <= LB; e += bs)
       for (int j = 0, n = (run[e] + MT - 1) / MT; j < n; ++j) {
         const int k = toff[e] + j;
         if (k < max_tiles) {
-          tiles[1 + 2 * k] = e;
-          tiles[2 + 2 * k] = j * MT;
+          int32_t* rec = tiles + 1 + (size_t)TREC * k;
+          rec[0] = e;
+          rec[1] = j * MT;
+          rec[2] = offs[e];
+          rec[3] = run[e];
+          for (int i = run[e] - j * MT; i < MT; ++i) rec[4 + i] = -1;  // the tile's padding rows
         }
       }
   }
   __syncthreads();
-  for (int i = tid; i <= E; i += bs) run[i] = 0;
+  for (int i = tid; i <= LB; i += bs) run[i] = 0;
   // Stable placement, one chunk of bs pairs at a time: a pair's position in its bucket is the
   // bucket's start + the pairs of earlier chunks + those of earlier waves of this chunk (per-wave
   // histograms, prefixed over waves) + those of earlier lanes of its own wave.
   const int nwv = bs / WAVE;
-  for (int base = 0; base < TK; base += bs) {
-    for (int i = tid; i < nwv * (E + 1); i += bs) hist[i] = 0;
+  for (int base = 0; base < NP; base += bs) {
+    for (int i = tid; i < nwv * NB; i += bs) hist[i] = 0;
     __syncthreads();
     const int p = base + tid;
     int e = -1;
-    if (p < TK) {
-      e = idx[p];
-      if ((unsigned)e >= (unsigned)E) e = E;
-      atomicAdd(&hist[w * (E + 1) + e], 1);
+    if (p < NP) {
+      e = bucket(p);
+      atomicAdd(&hist[w * NB + e], 1);
     }
     int rank = 0;  // earlier lanes of this wave with the same bucket
     for (int j = 0; j < WAVE; ++j) rank += (j < lane && __builtin_amdgcn_readlane(e, j) == e) ? 1 : 0;
     __syncthreads();
-    for (int b2 = tid; b2 <= E; b2 += bs) {  // prefix over waves, per bucket
+    for (int b2 = tid; b2 <= LB; b2 += bs) {  // prefix over waves, per bucket
       int acc = 0;
       for (int v = 0; v < nwv; ++v) {
-        const int c = hist[v * (E + 1) + b2];
-        hist[v * (E + 1) + b2] = acc;
+        const int c = hist[v * NB + b2];
+        hist[v * NB + b2] = acc;
         acc += c;
       }
       ctot[b2] = acc;
     }
     __syncthreads();
-    if (p < TK) perm[offs[e] + run[e] + hist[w * (E + 1) + e] + rank] = p;
+    if (p < NP) {
+      const int q = run[e] + hist[w * NB + e] + rank;  // position inside the bucket
+      perm[offs[e] + q] = p;
+      const int k = toff[e] + q / MT;
+      if (tiles != nullptr && k < max_tiles) tiles[1 + (size_t)TREC * k + 4 + q % MT] = p;
+    }
     __syncthreads();
-    for (int b2 = tid; b2 <= E; b2 += bs) run[b2] += ctot[b2];
+    for (int b2 = tid; b2 <= LB; b2 += bs) run[b2] += ctot[b2];
     __syncthreads();
   }
 }
@@ -368,32 +392,39 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
                                                           const int32_t* __restrict__ tiles,
                                                           const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1,
                                                           uint16_t* __restrict__ act_sorted, float* __restrict__ out,
-                                                          LoraRefG l0, LoraRefG l1) {
+                                                          LoraRefG l0, LoraRefG l1, moe_qmat s0, moe_qmat s1, int SB,
+                                                          int TK) {
   using GS = GSeg<BITS>;
   static_assert(NST % PF == 0 && NST * GS::MACRO <= XCH, "whole stages, one LDS pass per chunk");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XS];
   __shared__ int rows[MT];
   if ((int)blockIdx.x >= tiles[0]) return;
-  const int e = tiles[1 + 2 * blockIdx.x], mt = tiles[2 + 2 * blockIdx.x];
-  const int beg = offsets[e], n_e = offsets[e + 1] - beg;
+  const int32_t* rec = tiles + 1 + (size_t)TREC * blockIdx.x;
+  const int e = rec[0], mt = rec[1], beg = rec[2], n_e = rec[3];
+  // bucket SB (when >= 0) holds the shared expert's pairs TK + t, one per token t: its tiles read
+  // the shared weights (expert 0 of s0 / s1) and carry the LoRA terms; routed pair p is token p / K
+  const bool shb = e == SB;
+  const int ee = shb ? 0 : e;
+  const bool lora_on = SB < 0 || shb;
+  const auto tok = [&](int pr) { return pr < TK ? pr / K : pr - TK; };
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
   const int n0 = blockIdx.y * (16 * GW) + wave * 16;
-  if (e >= E) {
+  if (e >= E && !shb) {
     if constexpr (NMAT == 1)  // pairs whose expert index is out of range
       for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
-        if (n0 + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0 + ln] = quiet_nan();
+        if (n0 + ln < nrows) out[(size_t)rec[4 + pos - mt] * nrows + n0 + ln] = quiet_nan();
     return;
   }
   if (threadIdx.x < MT) {
     const int pos = mt + threadIdx.x;
-    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? perm[beg + pos] / K : beg + pos) : -1;
+    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? tok(rec[4 + threadIdx.x]) : beg + pos) : -1;
   }
   lds_barrier();
   const bool active = n0 < nrows;  // uniform over the wave
   const int wpr = ncols * BITS / 32, ngr = ncols >> lg2g;
-  const size_t row = (size_t)e * nrows + (active ? n0 + ln : 0);
-  const moe_qmat mats[2] = {m0, m1};
+  const size_t row = (size_t)ee * nrows + (active ? n0 + ln : 0);
+  const moe_qmat mats[2] = {shb ? s0 : m0, shb ? s1 : m1};
   float4_t acc[NMAT];
 #pragma unroll
   for (int mi = 0; mi < NMAT; ++mi) acc[mi] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -435,16 +466,16 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
     if (pos >= n_e || pos >= mt + MT) continue;
     const int n = n0 + ln;
     if constexpr (NMAT == 2) {
-      const int t = perm[beg + pos] / K;
+      const int t = tok(rec[4 + pos - mt]);
       const float sc = rowscale ? rowscale[t] : 1.f;
       float g = acc[0][i] * sc, u = acc[1][i] * sc;
-      if (l0.B) g += lora_row_g(l0, t, n);
-      if (l1.B) u += lora_row_g(l1, t, n);
+      if (lora_on && l0.B) g += lora_row_g(l0, t, n);
+      if (lora_on && l1.B) u += lora_row_g(l1, t, n);
       act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
     } else {
-      const int pr = perm[beg + pos];
+      const int pr = rec[4 + pos - mt];
       float o = acc[0][i];
-      if (l0.B) o += lora_row_g(l0, pr / K, n);
+      if (lora_on && l0.B) o += lora_row_g(l0, tok(pr), n);
       out[(size_t)pr * nrows + n] = o;
     }
   }
@@ -465,7 +496,8 @@ __global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(
 k_grouped_mm64(
     int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
-    moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1) {
+    moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1,
+    moe_qmat s0, moe_qmat s1, int SB, int TK) {
   using GS = GSeg<BITS>;
   constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
   constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
@@ -481,34 +513,40 @@ k_grouped_mm64(
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
   __shared__ int rows[MT];
   if ((int)blockIdx.x >= tiles[0]) return;
-  const int e = tiles[1 + 2 * blockIdx.x], mt = tiles[2 + 2 * blockIdx.x];
-  const int beg = offsets[e], n_e = offsets[e + 1] - beg;
+  const int32_t* rec = tiles + 1 + (size_t)TREC * blockIdx.x;
+  const int e = rec[0], mt = rec[1], beg = rec[2], n_e = rec[3];
+  // bucket SB (when >= 0) holds the shared expert's pairs TK + t, one per token t: its tiles read
+  // the shared weights (expert 0 of s0 / s1) and carry the LoRA terms; routed pair p is token p / K
+  const bool shb = e == SB;
+  const int ee = shb ? 0 : e;
+  const bool lora_on = SB < 0 || shb;
+  const auto tok = [&](int pr) { return pr < TK ? pr / K : pr - TK; };
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
   // row group rg of this wave: weight rows n0(rg) .. + 16
   auto n0 = [&](int rg) { return (int)blockIdx.y * (16 * GW * RG) + rg * 16 * GW + wave * 16; };
-  if (e >= E) {
+  if (e >= E && !shb) {
     if constexpr (NMAT == 1)  // pairs whose expert index is out of range
       for (int rg = 0; rg < RG; ++rg)
         for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
-          if (n0(rg) + ln < nrows) out[(size_t)perm[beg + pos] * nrows + n0(rg) + ln] = quiet_nan();
+          if (n0(rg) + ln < nrows) out[(size_t)rec[4 + pos - mt] * nrows + n0(rg) + ln] = quiet_nan();
     return;
   }
   if (threadIdx.x < MT) {
     const int pos = mt + threadIdx.x;
-    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? perm[beg + pos] / K : beg + pos) : -1;
+    rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? tok(rec[4 + threadIdx.x]) : beg + pos) : -1;
   }
   lds_barrier();
   const bool active = n0(0) < nrows;  // uniform over the wave (later row groups checked at the stores)
   const int wpr = ncols * BITS / 32, ngr = ncols / 64;
   // weight row of row group rg, clamped into the expert so that every load is valid
-  auto wrow = [&](int rg) { return (size_t)e * nrows + min(n0(rg) + ln, nrows - 1); };
-  const moe_qmat mats[2] = {m0, m1};
+  auto wrow = [&](int rg) { return (size_t)ee * nrows + min(n0(rg) + ln, nrows - 1); };
+  const moe_qmat mats[2] = {shb ? s0 : m0, shb ? s1 : m1};
   const int row0 = rows[0];  // always a real row (the tile holds at least one pair)
   // the pairs of this lane's four outputs, read now rather than after the last step
   int pr_out[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr_out[i] = perm[beg + min(mt + 4 * lq + i, n_e - 1)];
+  for (int i = 0; i < 4; ++i) pr_out[i] = rec[4 + min(4 * lq + i, n_e - mt - 1)];
   float4_t acc[RG][NMAT];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -669,16 +707,16 @@ k_grouped_mm64(
     const int n = n0(rg) + ln;
     if (pos >= n_e || pos >= mt + MT || n >= nrows) continue;
     if constexpr (NMAT == 2) {
-      const int t = pr_out[i] / K;
+      const int t = tok(pr_out[i]);
       const float sc = rowscale ? rowscale[t] : 1.f;
       float g = acc[rg][0][i] * sc, u = acc[rg][1][i] * sc;
-      if (l0.B) g += lora_row_g(l0, t, n);
-      if (l1.B) u += lora_row_g(l1, t, n);
+      if (lora_on && l0.B) g += lora_row_g(l0, t, n);
+      if (lora_on && l1.B) u += lora_row_g(l1, t, n);
       act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
     } else {
       const int pr = pr_out[i];
       float o = acc[rg][0][i];
-      if (l0.B) o += lora_row_g(l0, pr / K, n);
+      if (lora_on && l0.B) o += lora_row_g(l0, tok(pr), n);
       out[(size_t)pr * nrows + n] = o;
     }
   }
@@ -692,9 +730,9 @@ int ilog2g(int v) {
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Upper bound of the work list's length: every nonempty bucket (at most E + 1 of them, and at
-// most TK) rounds up to whole tiles.
-int max_tiles(int TK, int E) { return (TK + MT - 1) / MT + min(E + 1, TK); }
+// Upper bound of the work list's length: every nonempty bucket (at most NB of them, and at most
+// N, the pairs) rounds up to whole tiles.
+int max_tiles(int N, int NB) { return (N + MT - 1) / MT + min(NB, N); }
 
 // Steps per chunk: a short chunk (PF macro steps) when the input row fits in it, else the
 // longest one LDS holds.
@@ -737,61 +775,80 @@ template <int NMAT>
 int rg64(int ncols, bool many_tiles) { return ncols % XCH == 0 || NMAT == 2 || !many_tiles ? 1 : 4; }
 constexpr int MANY_TILES = 128;  // work lists at least this long take four row groups
 
+// The two GEMMs over the work list.  With a shared expert (a.shared), its T pairs form bucket E + 1
+// of the same list, so one launch per projection covers routed and shared tiles alike.
 template <int BITS, bool SPLIT>
 hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowscale, float* o_tk, LoraRefG lg,
                         LoraRefG lu, LoraRefG ldn, const DecodeArgs& a) {
   const int lg2g = ilog2g(a.group);
   const int rows_per_block = 16 * GW;
-  const int nt = max_tiles(a.T * a.K, a.E);
-  const moe_qmat gu[2] = {a.ex.gate, a.ex.up};
+  const int TK = a.T * a.K, TS = a.shared ? a.T : 0, SB = a.shared ? a.E + 1 : -1;
+  const int nt = max_tiles(TK + TS, a.E + 1 + (TS > 0));
+  const moe_experts& sx = a.shared ? *a.shared : a.ex;  // the shared weights (unused without a shared expert)
+  const moe_qmat gu[4] = {a.ex.gate, a.ex.up, sx.gate, sx.up};
+  const moe_qmat dn[2] = {a.ex.down, sx.down};
+  const bool many = nt >= MANY_TILES;
+  const auto k64_gu = grouped_kernel64<BITS, 2>(a.group, a.d, gu, many);
+  const auto k64_gu_s = grouped_kernel64<BITS, 2>(a.group, a.d, gu + 2, many);
   hipError_t err;
-  if (auto k64 = grouped_kernel64<BITS, 2>(a.group, a.d, gu, nt >= MANY_TILES))
-    err = launch(k64, dim3(nt, (a.I + rows_per_block * rg64<2>(a.d, nt >= MANY_TILES) - 1) / (rows_per_block * rg64<2>(a.d, nt >= MANY_TILES))),
+  if (k64_gu && k64_gu_s)
+    err = launch(k64_gu, dim3(nt, (a.I + rows_per_block * rg64<2>(a.d, many) - 1) / (rows_per_block * rg64<2>(a.d, many))),
                  dim3(WAVE * GW), 0, s, a.K, a.E, a.d,
                  a.I, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
-                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu);
+                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK);
   else
     err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), dim3(nt, (a.I + rows_per_block - 1) / rows_per_block),
                  dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x, (const int32_t*)g.offsets,
                  (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up,
-                 (uint16_t*)a.act, (float*)nullptr, lg, lu);
+                 (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK);
   if (err != hipSuccess) return err;
-  if (a.lora3) {
+  if (a.lora3) {  // A . act of the LoRA's expert: the shared bucket's rows (after the routed ones), else all
     const int wd = a.T * a.lora3[2].rank;
-    err = launch_lora_a(s, wd, a.T, a.I, a.lora3[2].rank, 0, (const uint16_t*)a.act, (size_t)a.K * a.I,
+    const uint16_t* act_l = (const uint16_t*)a.act + (size_t)(TS > 0 ? TK : 0) * a.I;
+    err = launch_lora_a(s, wd, a.T, a.I, a.lora3[2].rank, 0, act_l, TS > 0 ? (size_t)a.I : (size_t)a.K * a.I,
                         a.lora3[2].A, a.u_down);
     if (err != hipSuccess) return err;
   }
-  if (auto k64 = grouped_kernel64<BITS, 1>(a.group, a.I, &a.ex.down, nt >= MANY_TILES))
-    return launch(k64, dim3(nt, (a.d + rows_per_block * rg64<1>(a.I, nt >= MANY_TILES) - 1) / (rows_per_block * rg64<1>(a.I, nt >= MANY_TILES))),
+  const auto k64_dn = grouped_kernel64<BITS, 1>(a.group, a.I, dn, many);
+  const auto k64_dn_s = grouped_kernel64<BITS, 1>(a.group, a.I, dn + 1, many);
+  if (k64_dn && k64_dn_s)
+    return launch(k64_dn, dim3(nt, (a.d + rows_per_block * rg64<1>(a.I, many) - 1) / (rows_per_block * rg64<1>(a.I, many))),
                   dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
                   a.d, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
                   (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
-                  LoraRefG{});
+                  LoraRefG{}, sx.down, sx.down, SB, TK);
   return launch(grouped_kernel<BITS, 1>(SPLIT, a.I), dim3(nt, (a.d + rows_per_block - 1) / rows_per_block),
                 dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d, lg2g, (const uint16_t*)a.act, (const int32_t*)g.offsets,
                 (const int32_t*)g.perm, (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down,
-                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{});
+                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down, sx.down, SB, TK);
 }
 
 }  // namespace
 
-size_t grouped_tiles_bytes(int T, int K, int E) { return al256((1 + 2 * (size_t)max_tiles(T * K, E)) * 4); }
-
-size_t grouped_workspace_extra(int T, int K, int E, int d) {
-  return al256((size_t)(E + 1) * 4) + al256((size_t)(E + 2) * 4) + al256((size_t)T * K * 4) + al256((size_t)T * 4) +
-         al256((size_t)T * K * d * 4) + grouped_tiles_bytes(T, K, E);
+GroupedLayout grouped_layout(int T, int K, int E, int d, int TS) {
+  const int NB = E + 1 + (TS > 0), NP = T * K + TS;
+  GroupedLayout l{};
+  l.counts = 0;
+  l.offsets = l.counts + al256((size_t)NB * 4);
+  l.perm = l.offsets + al256((size_t)(NB + 1) * 4);
+  l.rowscale = l.perm + al256((size_t)NP * 4);
+  l.o_sorted = l.rowscale + al256((size_t)T * 4);
+  l.tiles = l.o_sorted + al256((size_t)NP * d * 4);
+  l.total = l.tiles + al256((1 + TREC * (size_t)max_tiles(NP, NB)) * 4);
+  return l;
 }
 
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, int32_t* tiles) {
-  const size_t lds = (size_t)(2 * (E + 1) + 2 * (E + 2) + 16 * (E + 1)) * sizeof(int);  // 1024 threads = 16 waves
-  return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK, E));
+                       int32_t* perm, int32_t* tiles, int TS) {
+  const int NB = E + 1 + (TS > 0);
+  const size_t lds = (size_t)(2 * NB + 2 * (NB + 1) + 16 * NB) * sizeof(int);  // 1024 threads = 16 waves
+  return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK + TS, NB),
+                TS);
 }
 
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   const DecodeArgs& a = g.base;
-  hipError_t err = launch_sort(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm, g.tiles);
+  hipError_t err = launch_sort(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm, g.tiles, a.shared ? a.T : 0);
   if (err != hipSuccess) return err;
   float* rowscale = nullptr;
   if (a.flags & MOE_INPUT_RMSNORM) {
@@ -803,15 +860,20 @@ hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   if (a.lora3) {
     const moe_lora* L3 = a.lora3;
     const int rms = (a.flags & MOE_INPUT_RMSNORM) != 0;
-    err = launch_lora_a(s, a.T * L3[0].rank, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate);
-    if (err == hipSuccess)
-      err = launch_lora_a(s, a.T * L3[1].rank, a.T, a.d, L3[1].rank, rms, a.x, (size_t)a.d, L3[1].A, a.u_up);
+    if (L3[0].rank == L3[1].rank)  // gate's and up's A . x in one launch
+      err = launch_lora_a(s, a.T * L3[0].rank, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate,
+                          L3[1].A, a.u_up);
+    else {
+      err = launch_lora_a(s, a.T * L3[0].rank, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate);
+      if (err == hipSuccess)
+        err = launch_lora_a(s, a.T * L3[1].rank, a.T, a.d, L3[1].rank, rms, a.x, (size_t)a.d, L3[1].A, a.u_up);
+    }
     if (err != hipSuccess) return err;
     lg = LoraRefG{L3[0].B, a.u_gate, L3[0].rank, L3[0].alpha / (float)L3[0].rank};
     lu = LoraRefG{L3[1].B, a.u_up, L3[1].rank, L3[1].alpha / (float)L3[1].rank};
     ldn = LoraRefG{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank};
   }
-  float* o_tk = a.out ? a.out : g.o_sorted;
+  float* o_tk = a.out && !a.shared ? a.out : g.o_sorted;  // with a shared expert: [T*K + T][d]
   if (a.bits == 4)
     err = launch_gemms<4, false>(s, g, rowscale, o_tk, lg, lu, ldn, a);
   else if (a.group < SegT<2>::COLS)
@@ -819,7 +881,9 @@ hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   else
     err = launch_gemms<2, false>(s, g, rowscale, o_tk, lg, lu, ldn, a);
   if (err != hipSuccess) return err;
-  if (a.y_fuse) err = launch_combine(s, a.T, a.K, a.d, o_tk, a.w_fuse, a.r_fuse, nullptr, a.y_fuse);
+  if (a.y_fuse)
+    err = launch_combine(s, a.T, a.K, a.d, o_tk, a.w_fuse, a.r_fuse,
+                         a.shared ? o_tk + (size_t)a.T * a.K * a.d : nullptr, a.y_fuse);
   return err;
 }
 

@@ -28,14 +28,16 @@ bool routing_dims_ok(int32_t T, int32_t E, int32_t K) {
 struct FfnWs {
   size_t act, u_gate, u_up, u_down, grouped, total;
 };
-FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex) {
+// TS: pairs of a shared expert run with the routed ones (T, or 0); its expert-sorted activations
+// [T*K + T][I] float16 fit the T*K*I float32 of the decode path's act for any K >= 1.
+FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex, int32_t TS = 0) {
   FfnWs w{};
   w.act = 0;
   w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(float));
   w.u_up = w.u_gate + align_up((size_t)T * MAX_RANK * sizeof(float));
   w.u_down = w.u_up + align_up((size_t)T * MAX_RANK * sizeof(float));
   w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * sizeof(float));
-  w.total = w.grouped + (T >= GROUPED_MIN_T ? grouped_workspace_extra(T, K, ex->n_experts, ex->d_model) : 0);
+  w.total = w.grouped + (T >= GROUPED_MIN_T ? grouped_layout(T, K, ex->n_experts, ex->d_model, TS).total : 0);
   return w;
 }
 
@@ -183,8 +185,10 @@ static moe_status check_expert_ffn(int32_t T, int32_t K, uint32_t flags, const u
 // Enqueue the expert FFN on checked arguments with `workspace` (ffn_ws(T, K, ex).total bytes).
 static moe_status run_expert_ffn(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
                                  const int32_t* idx, const moe_experts* ex, const moe_lora* lora3, float* out,
-                                 const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace) {
-  const FfnWs ws = ffn_ws(T, K, ex);
+                                 const float* w_fuse, const uint16_t* r_fuse, uint16_t* y_fuse, void* workspace,
+                                 const moe_experts* shared = nullptr) {
+  const int32_t TS = shared ? T : 0;
+  const FfnWs ws = ffn_ws(T, K, ex, TS);
   char* base = (char*)workspace;
   DecodeArgs a{};
   a.T = T;
@@ -207,23 +211,19 @@ static moe_status run_expert_ffn(void* stream, int32_t T, int32_t K, uint32_t fl
   a.u_gate = (float*)(base + ws.u_gate);
   a.u_up = (float*)(base + ws.u_up);
   a.u_down = (float*)(base + ws.u_down);
+  a.shared = shared;
   hipStream_t s = (hipStream_t)stream;
   if (T >= GROUPED_MIN_T) {
     GroupedArgs g{};
     g.base = a;
     char* gb = base + ws.grouped;
-    const size_t o_counts = 0;
-    const size_t o_offsets = o_counts + align_up((size_t)(ex->n_experts + 1) * sizeof(int32_t));
-    const size_t o_perm = o_offsets + align_up((size_t)(ex->n_experts + 2) * sizeof(int32_t));
-    const size_t o_rowscale = o_perm + align_up((size_t)T * K * sizeof(int32_t));
-    const size_t o_osorted = o_rowscale + align_up((size_t)T * sizeof(float));
-    const size_t o_tiles = o_osorted + align_up((size_t)T * K * ex->d_model * sizeof(float));
-    g.counts = (int32_t*)(gb + o_counts);
-    g.tiles = (int32_t*)(gb + o_tiles);
-    g.offsets = (int32_t*)(gb + o_offsets);
-    g.perm = (int32_t*)(gb + o_perm);
-    g.rowscale = (float*)(gb + o_rowscale);
-    g.o_sorted = (float*)(gb + o_osorted);
+    const GroupedLayout gl = grouped_layout(T, K, ex->n_experts, ex->d_model, TS);
+    g.counts = (int32_t*)(gb + gl.counts);
+    g.tiles = (int32_t*)(gb + gl.tiles);
+    g.offsets = (int32_t*)(gb + gl.offsets);
+    g.perm = (int32_t*)(gb + gl.perm);
+    g.rowscale = (float*)(gb + gl.rowscale);
+    g.o_sorted = (float*)(gb + gl.o_sorted);
     return from_hip(launch_expert_grouped(s, g));
   }
   return from_hip(launch_expert_decode(s, a));
@@ -249,6 +249,30 @@ moe_status moe_expert_ffn_q4_noalloc(void* stream, int32_t T, int32_t K, uint32_
   const moe_status sp = scratch_on_current_device(&ptr);
   if (sp != MOE_OK) return sp;
   return run_expert_ffn(stream, T, K, flags, x, idx, ex, lora3, out, w_fuse, r_fuse, y_fuse, ptr);
+}
+
+size_t moe_expert_ffn_shared_workspace_size(int32_t T, int32_t K, const moe_experts* ex) {
+  if (!ex || T < GROUPED_MIN_T || K < 1 || ex->d_ff < 1 || ex->d_model < 1) return 0;
+  return ffn_ws(T, K, ex, T).total;
+}
+
+moe_status moe_expert_ffn_q4_shared(void* stream, int32_t T, int32_t K, uint32_t flags, const uint16_t* x,
+                                    const int32_t* idx, const moe_experts* ex, const moe_experts* shared,
+                                    const moe_lora* lora3, const float* w, const uint16_t* r, uint16_t* y,
+                                    void* workspace, size_t workspace_bytes) {
+  // the routed experts' checks (the LoRA is the shared expert's, checked against it below)
+  moe_status st = check_expert_ffn(T, K, flags, x, idx, ex, nullptr, nullptr, w, r, y);
+  if (st != MOE_OK) return st;
+  if (!w || !r || !y) return MOE_ERR_INVALID_ARG;
+  if (!shared) return MOE_ERR_INVALID_ARG;
+  st = check_expert_ffn(T, 1, flags, x, idx, shared, lora3, nullptr, w, r, y);
+  if (st != MOE_OK) return st;
+  if (shared->n_experts != 1 || shared->d_model != ex->d_model || shared->d_ff != ex->d_ff ||
+      shared->bits != ex->bits || shared->group != ex->group)
+    return MOE_ERR_INVALID_ARG;
+  if (T < GROUPED_MIN_T) return MOE_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < ffn_ws(T, K, ex, T).total) return MOE_ERR_INVALID_ARG;
+  return run_expert_ffn(stream, T, K, flags, x, idx, ex, lora3, nullptr, w, r, y, workspace, shared);
 }
 
 size_t moe_expert_ffn_sparse_workspace_size(int32_t T, int32_t K, const moe_experts* ex) {

@@ -40,6 +40,8 @@ struct DecodeArgs {
   bool relu;               // ReLU on the gate branch instead of SiLU (activation-sparse variant)
   int32_t* zero;           // [T][nzero] int32 cleared by the gate/up kernel, or nullptr
   int nzero;
+  const moe_experts* shared;  // batched path only: a shared expert run with the routed ones (lora3 is
+                              // its LoRA), whose output joins the fused combine; nullptr: none
 };
 hipError_t launch_expert_decode(hipStream_t s, const DecodeArgs& a);
 // gate/up + activation only (act[T][K][I] float32), for the activation-sparse variant
@@ -57,24 +59,32 @@ size_t sparse_lds(int bits, int I); // dynamic LDS bytes of the down kernel
 hipError_t launch_down_sparse(hipStream_t s, const SparseArgs& a);
 bool decode_shape_supported(int bits, int group, int d, int I);
 // u[t][r] = s_t * A[r] . v_t for `waves` = T * rank waves (s_t = RMS-norm factor when rmsnorm)
+// u[t][r] = A[r] . v_t (v_t optionally RMS-normed); with A2 also u2 = A2 . v_t in the same launch
+// (the two ranks equal).  waves = T * rank.
 hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,
-                         size_t v_stride, const uint16_t* A, float* u);
+                         size_t v_stride, const uint16_t* A, float* u, const uint16_t* A2 = nullptr,
+                         float* u2 = nullptr);
 
 // batched (grouped GEMM) expert FFN ------------------------------------------------------------
+// With a shared expert (base.shared), NB = E + 2 buckets and NP = T*K + T pairs (the shared
+// expert's pair of token t is T*K + t, in bucket E + 1); else NB = E + 1 and NP = T*K.
 struct GroupedArgs {
-  DecodeArgs base;    // base.act holds the expert-sorted activations [T*K][I]
-  int32_t* counts;    // workspace [E+1] (bucket E: indices outside [0, E))
-  int32_t* offsets;   // workspace [E+2]
-  int32_t* perm;      // workspace [T*K]
+  DecodeArgs base;    // base.act holds the expert-sorted activations [NP][I]
+  int32_t* counts;    // workspace [NB] (bucket E: indices outside [0, E))
+  int32_t* offsets;   // workspace [NB+1]
+  int32_t* perm;      // workspace [NP]
   float* rowscale;    // workspace [T]
-  float* o_sorted;    // workspace [T*K][d] float32 (used when out == nullptr)
-  int32_t* tiles;     // workspace: the grouped GEMMs' work list (count, then (bucket, position) pairs)
+  float* o_sorted;    // workspace [NP][d] float32 (used when out == nullptr or with a shared expert)
+  int32_t* tiles;     // workspace: the grouped GEMMs' work list (count, then one record per tile)
 };
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& a);
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, int32_t* tiles);
-size_t grouped_workspace_extra(int T, int K, int E, int d);
-size_t grouped_tiles_bytes(int T, int K, int E);
+                       int32_t* perm, int32_t* tiles, int TS = 0);
+// byte offsets of GroupedArgs' workspace arrays (TS: the shared expert's pairs, T or 0)
+struct GroupedLayout {
+  size_t counts, offsets, perm, rowscale, o_sorted, tiles, total;
+};
+GroupedLayout grouped_layout(int T, int K, int E, int d, int TS);
 
 // whole-token persistent decode -----------------------------------------------------------------
 bool decode_step_supported(const moe_decode_stack& st);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 26
     assert sorted(lib_mod.EXPORTS) == names
     for n in names:
         assert hasattr(L, n)
@@ -249,6 +249,29 @@ def test_decode_step_grid_for_other_cu_counts():
     assert gf(tiny, 256) == 0                   # d_model 256: per-layer calls only
     bad = lib_mod.moe_decode_stack(40, 256, 9, 2048, 512, 4, 64, 1024, FAKE, FAKE, FAKE)
     assert gf(bad, 256) == 0                    # K > 8
+
+
+def test_expert_ffn_shared_rejects():
+    ex = _ex(E=256, d=2048, I=512, group=64)
+    sh = _ex(E=1, d=2048, I=512, group=64)
+    ws_need = L.moe_expert_ffn_shared_workspace_size(256, 4, ctypes.byref(ex))
+    assert ws_need > L.moe_expert_ffn_workspace_size(256, 4, ctypes.byref(ex)) > 0
+    assert L.moe_expert_ffn_shared_workspace_size(31, 4, ctypes.byref(ex)) == 0
+
+    def call(T=256, K=4, flags=0, shared=sh, lora=None, w=FAKE, r=FAKE, y=FAKE, ws=FAKE, wsb=ws_need, e=ex):
+        return L.moe_expert_ffn_q4_shared(None, T, K, flags, FAKE, FAKE, ctypes.byref(e),
+                                          ctypes.byref(shared) if shared is not None else None, lora, w, r, y, ws, wsb)
+    assert call(shared=None) == INVALID
+    assert call(shared=_ex(E=2, d=2048, I=512, group=64)) == INVALID        # one shared expert
+    assert call(shared=_ex(E=1, d=2048, I=1024, group=64)) == INVALID       # shapes must match
+    assert call(shared=_ex(E=1, d=2048, I=512, group=32)) == INVALID
+    assert call(w=None) == INVALID and call(r=None) == INVALID and call(y=None) == INVALID
+    assert call(wsb=ws_need - 1) == INVALID
+    assert call(ws=FAKE + 8) == INVALID
+    assert call(flags=0x8) == INVALID
+    assert call(T=31, wsb=1 << 40) == UNSUP                                 # the batched path only
+    bad_lora = (lib_mod.moe_lora * 3)(*[lib_mod.moe_lora(FAKE, FAKE, 0, 32.0) for _ in range(3)])
+    assert call(lora=ctypes.cast(bad_lora, ctypes.POINTER(lib_mod.moe_lora))) == INVALID  # rank 0
 
 
 def test_workspace_sizes_closed_form():

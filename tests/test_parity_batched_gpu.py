@@ -235,9 +235,81 @@ def test_batched_layer_end_to_end(M):
     assert_rows_close(y.cpu().numpy(), y_ref, what="layer y")
 
 
-def test_batched_layer_two_streams(M):
-    """The packaged batched layer (shared expert on a second stream) equals the same calls issued on
-    one stream, bit for bit, eagerly and as graph replays with eager work in between."""
+def _separate(M, T, K, flags, x, idx, w, ex, sh_ex, lora):
+    """The three-call reference of moe_expert_ffn_q4_shared: routed experts, shared expert (K = 1,
+    with its LoRA), combine."""
+    d = ex.d
+    o = torch.empty((T, K, d), dtype=torch.float32, device=DEV)
+    M.moe_expert_ffn_q4(T, K, flags, x, idx, ex, None, o, None, None, None, ws_for(M, T, K, ex))
+    sh = torch.empty((T, 1, d), dtype=torch.float32, device=DEV)
+    zeros = torch.zeros((T, 1), dtype=torch.int32, device=DEV)
+    M.moe_expert_ffn_q4(T, 1, flags, x, zeros, sh_ex, lora, sh, None, None, None, ws_for(M, T, 1, sh_ex))
+    y = torch.empty((T, d), dtype=torch.float16, device=DEV)
+    M.moe_combine(T, K, d, o, w, x, sh.view(T, d), y)
+    return y
+
+
+def _merged(M, T, K, flags, x, idx, w, ex, sh_ex, lora):
+    y = torch.full((T, ex.d), float("nan"), dtype=torch.float16, device=DEV)
+    ws = torch.empty(M.moe_expert_ffn_shared_workspace_size(T, K, ex), dtype=torch.uint8, device=DEV)
+    M.moe_expert_ffn_q4_shared(T, K, flags, x, idx, ex, sh_ex, lora, w, x, y, ws)
+    return y
+
+
+@pytest.mark.parametrize("bits,group,d,I,E,K,T,rms,lora", [
+    (4, 64, 2048, 512, 256, 4, 256, False, True),    # the batched configuration's shapes
+    (4, 64, 2048, 512, 256, 4, 256, True, False),
+    (4, 32, 96, 160, 5, 3, 37, False, True),         # ragged rows and columns (the 16-column kernel)
+    (2, 64, 2048, 512, 8, 3, 40, False, True),       # 2-bit, lane-contiguous kernel
+    (4, 64, 4096, 1536, 8, 2, 33, True, True),
+    (4, 32, 256, 128, 16, 16, 32, False, False),     # K = E
+])
+def test_shared_expert_in_the_routed_call(M, bits, group, d, I, E, K, T, rms, lora):
+    """moe_expert_ffn_q4_shared (the shared expert's rows sorted in with the routed pairs, one GEMM
+    launch per projection) equals the routed call, the shared call and moe_combine, bit for bit;
+    a token whose index is out of range gives a NaN row in both."""
+    cfg = replace(S.CONFIGS["batched"], name=f"s{bits}-{group}-{d}-{I}", bits=bits, group=group, d=d, I=I, E=E, K=K,
+                  T=T)
+    syn = S.Synth(cfg)
+    ex = device_layer(syn, 0, DEV)
+    sh_ex, _, lo, _, _ = _shared(M, cfg, syn)
+    lo = lo if lora else None
+    h = syn.hidden(4321, T).to(DEV)
+    idx_np, w_np = O.route_topk(syn.logits(98, T).numpy(), K)
+    idx_np[T // 2, 0] = E + 3                          # outside [0, E): that token's row is NaN
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    w = torch.tensor(w_np, dtype=torch.float32, device=DEV)
+    flags = M.MOE_INPUT_RMSNORM if rms else 0
+    a = _separate(M, T, K, flags, h, idx, w, ex, sh_ex, lo)
+    b = _merged(M, T, K, flags, h, idx, w, ex, sh_ex, lo)
+    torch.cuda.synchronize()
+    assert torch.isnan(a[T // 2]).all() and torch.isnan(b[T // 2]).all()
+    keep = torch.ones(T, dtype=torch.bool)
+    keep[T // 2] = False
+    assert torch.isfinite(a[keep]).all()
+    assert torch.equal(a[keep], b[keep])
+
+
+def test_shared_call_small_T_unsupported(M):
+    cfg = S.CONFIGS["batched"]
+    syn = S.Synth(cfg)
+    ex = device_layer(syn, 0, DEV)
+    sh_ex, _, lo, _, _ = _shared(M, cfg, syn)
+    assert M.moe_expert_ffn_shared_workspace_size(31, 4, ex) == 0
+    T = 31
+    x = syn.hidden(1, T).to(DEV)
+    idx = torch.zeros((T, 4), dtype=torch.int32, device=DEV) + torch.arange(4, dtype=torch.int32, device=DEV)
+    w = torch.full((T, 4), 0.25, dtype=torch.float32, device=DEV)
+    y = torch.empty((T, cfg.d), dtype=torch.float16, device=DEV)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    with pytest.raises(M.MoEError, match="UNSUPPORTED"):
+        M.moe_expert_ffn_q4_shared(T, 4, 0, x, idx, ex, sh_ex, lo, w, x, y, ws)
+
+
+def test_batched_layer_schedules(M):
+    """The packaged batched layer: the shared expert inside the routed call (default), on a second
+    stream, or on the same stream after the routed experts, all equal bit for bit, eagerly and as
+    graph replays with eager work in between."""
     from int4_expert_ffn_amd.batched import BatchedLayer
     cfg = S.CONFIGS["batched"]
     syn = S.Synth(cfg)
@@ -245,8 +317,33 @@ def test_batched_layer_two_streams(M):
     ex = device_layer(syn, 0, DEV)
     sh_ex, _, lora, _, _ = _shared(M, cfg, syn)
     router = syn.router(0, DEV)
-    two = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=True)
-    one = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=False)
+    merged = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora)
+    assert merged.merged
+    two = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=True, separate=True)
+    one = BatchedLayer(ex, router, T, K, DEV, shared=sh_ex, lora3=lora, two_streams=False, separate=True)
+    hs0 = syn.hidden(78, T).to(DEV)
+    ym = torch.empty((T, d), dtype=torch.float16, device=DEV)
+    yo = torch.empty_like(ym)
+    merged(hs0, ym)
+    one(hs0, yo)
+    torch.cuda.synchronize()
+    assert torch.equal(ym, yo)
+    gm = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    h_m = hs0.clone()
+    with torch.cuda.graph(gm, stream=cs):
+        merged(h_m, ym)
+    torch.cuda.synchronize()
+    for i in range(3):
+        hi = syn.hidden(90 + i, T).to(DEV)
+        h_m.copy_(hi)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cs):
+            gm.replay()
+        cs.synchronize()
+        one(hi, yo)
+        torch.cuda.synchronize()
+        assert torch.equal(ym, yo), f"merged replay {i}"
     hs = syn.hidden(77, 4 * T).to(DEV).view(4, T, d)
     y1 = torch.empty((T, d), dtype=torch.float16, device=DEV)
     y2 = torch.empty_like(y1)
