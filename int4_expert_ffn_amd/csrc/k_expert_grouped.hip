@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
                                                int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
                                                int max_tiles, int TS) {
   // TS > 0: pairs TK .. TK + TS - 1 form one more bucket, E + 1 (a shared expert's, one per token)
-  const int NB = E + 1 + (TS > 0 ? 1 : 0), LB = NB - 1, NP = TK + TS;  // buckets, the last, pairs
+  const int NB = E + 1 + (TS > 0 ? 1 : 0), LB = NB - 1;  // buckets, the last one
   extern __shared__ int sh[];
   int* run = sh;               // [NB]
   int* offs = sh + NB;         // [NB+1]
@@ -50,14 +50,13 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
   int* hist = ctot + NB;       // [bs / WAVE][NB] per-wave bucket counts of a chunk, then their prefixes
   __shared__ int wsum[2][16];
   const int tid = threadIdx.x, bs = blockDim.x, lane = tid % WAVE, w = tid / WAVE;
-  const auto bucket = [&](int p) {
-    if (p >= TK) return E + 1;
+  const auto bucket = [&](int p) {  // of routed pair p < TK
     const int e = idx[p];
     return (unsigned)e >= (unsigned)E ? E : e;
   };
-  for (int i = tid; i <= LB; i += bs) run[i] = 0;
+  for (int i = tid; i <= LB; i += bs) run[i] = (TS > 0 && i == LB) ? TS : 0;  // the shared bucket: TS pairs
   __syncthreads();
-  for (int p = tid; p < NP; p += bs) atomicAdd(&run[bucket(p)], 1);
+  for (int p = tid; p < TK; p += bs) atomicAdd(&run[bucket(p)], 1);
   __syncthreads();
   // exclusive scans of the pair counts and of the tile counts over buckets 0..LB (NB <= 2 bs),
   // two buckets per thread
@@ -124,16 +123,22 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
   }
   __syncthreads();
   for (int i = tid; i <= LB; i += bs) run[i] = 0;
-  // Stable placement, one chunk of bs pairs at a time: a pair's position in its bucket is the
-  // bucket's start + the pairs of earlier chunks + those of earlier waves of this chunk (per-wave
-  // histograms, prefixed over waves) + those of earlier lanes of its own wave.
+  // The shared bucket's pairs keep their order: pair TK + q is its q-th.
+  for (int q = tid; q < TS; q += bs) {
+    perm[offs[LB] + q] = TK + q;
+    const int k = toff[LB] + q / MT;
+    if (tiles != nullptr && k < max_tiles) tiles[1 + (size_t)TREC * k + 4 + q % MT] = TK + q;
+  }
+  // Stable placement of the routed pairs, one chunk of bs pairs at a time: a pair's position in its
+  // bucket is the bucket's start + the pairs of earlier chunks + those of earlier waves of this
+  // chunk (per-wave histograms, prefixed over waves) + those of earlier lanes of its own wave.
   const int nwv = bs / WAVE;
-  for (int base = 0; base < NP; base += bs) {
+  for (int base = 0; base < TK; base += bs) {
     for (int i = tid; i < nwv * NB; i += bs) hist[i] = 0;
     __syncthreads();
     const int p = base + tid;
     int e = -1;
-    if (p < NP) {
+    if (p < TK) {
       e = bucket(p);
       atomicAdd(&hist[w * NB + e], 1);
     }
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __r
       ctot[b2] = acc;
     }
     __syncthreads();
-    if (p < NP) {
+    if (p < TK) {
       const int q = run[e] + hist[w * NB + e] + rank;  // position inside the bucket
       perm[offs[e] + q] = p;
       const int k = toff[e] + q / MT;
