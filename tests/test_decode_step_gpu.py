@@ -221,6 +221,19 @@ def test_decode_step_topk_exact_ties(M, name, renorm):
         compared += 1
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_step_grid_matches_plan_for_this_device(M, name):
+    """The grid a launch uses on this device is the host-only plan for its compute-unit count."""
+    from int4_expert_ffn_amd.chain import DecodeStack
+    cfg, heads = CASES[name]
+    _, layers, _, _ = build(M, cfg, heads)
+    stack = DecodeStack(layers, cfg.K, DEV)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = stack._step_state()[1]
+    assert stack.grid() == M.moe_decode_step_grid_for(st, cus)
+    assert 1 <= stack.grid() <= cus
+
+
 @pytest.mark.parametrize("name", ["decode35b", "widek8"])
 def test_decode_step_stamped(M, name):
     """moe_decode_step_stamped gives bit-identical outputs and routing to the plain launch, and its
