@@ -32,137 +32,164 @@ constexpr int MT = 16;  // token rows per MFMA tile
 // one record, instead of a chain of dependent loads (bucket -> offsets -> perm -> activations).
 constexpr int TREC = 4 + MT;
 
-// One block of 1024 threads.  counts[E+1], offsets[E+2] (bucket E collects indices outside
+constexpr int SORT_THREADS = 1024, SORT_WAVES = SORT_THREADS / WAVE;
+
+// Inclusive prefix sum over the 64 lanes with DPP moves: row_shr 1, 2, 4, 8 inside each row of 16
+// lanes, then row_bcast15 / row_bcast31 carry the row totals into the rows after them.  A lane
+// whose DPP source is out of range, or whose row is masked off, adds the `old` operand, 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add_step(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v = dpp_add_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_add_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_add_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_add_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_add_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// The lanes of `live` whose key equals this lane's (keys below 2^nbits), one ballot per key bit.
+__device__ __forceinline__ uint64_t match_lanes(int key, int nbits, uint64_t live) {
+  uint64_t m = live;
+  for (int b = 0; b < nbits; ++b) {
+    const bool s = (key >> b) & 1;
+    const uint64_t bb = __ballot(s);
+    m &= s ? bb : ~bb;
+  }
+  return m;
+}
+
+// One block of SORT_THREADS threads.  counts[E+1], offsets[E+2] (bucket E collects indices outside
 // [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles (may
 // be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one TREC-int record per
 // MT-row tile, buckets in order.
-__global__ void __launch_bounds__(1024) k_sort(int TK, int E, const int32_t* __restrict__ idx,
-                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                               int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
-                                               int max_tiles, int TS) {
+//
+// A pair's position in its bucket is the number of earlier pairs with the same bucket: those of
+// earlier chunks of SORT_THREADS pairs, of earlier waves of its chunk (per-wave counts prefixed over
+// the waves) and of earlier lanes of its wave (the lanes with an equal bucket, found by ballots over
+// the bucket's bits).  The lowest lane of each such set of lanes writes the wave's count, so no
+// atomic ever serialises the lanes of one bucket.
+__global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int32_t* __restrict__ idx,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
+                                                      int max_tiles, int TS) {
   // TS > 0: pairs TK .. TK + TS - 1 form one more bucket, E + 1 (a shared expert's, one per token)
   const int NB = E + 1 + (TS > 0 ? 1 : 0), LB = NB - 1;  // buckets, the last one
   extern __shared__ int sh[];
-  int* run = sh;               // [NB]
-  int* offs = sh + NB;         // [NB+1]
+  int* cnt = sh;               // [NB] pairs of each bucket
+  int* run = cnt + NB;         // [NB] pairs placed by earlier chunks
+  int* offs = run + NB;        // [NB+1] first position of each bucket in perm
   int* toff = offs + NB + 1;   // [NB+1] first tile of each bucket
   int* ctot = toff + NB + 1;   // [NB] pairs of each bucket in the current chunk
-  int* hist = ctot + NB;       // [bs / WAVE][NB] per-wave bucket counts of a chunk, then their prefixes
-  __shared__ int wsum[2][16];
-  const int tid = threadIdx.x, bs = blockDim.x, lane = tid % WAVE, w = tid / WAVE;
+  int* hist = ctot + NB;       // [SORT_WAVES][NB] per-wave counts of a chunk, then their prefixes
+  const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
+  const int nbits = 32 - __clz(LB);           // every bucket number fits in nbits bits
+  const uint64_t below = (1ull << lane) - 1;  // the lanes before this one
   const auto bucket = [&](int p) {  // of routed pair p < TK
     const int e = idx[p];
     return (unsigned)e >= (unsigned)E ? E : e;
   };
-  for (int i = tid; i <= LB; i += bs) run[i] = (TS > 0 && i == LB) ? TS : 0;  // the shared bucket: TS pairs
+  for (int i = tid; i <= LB; i += SORT_THREADS) {
+    cnt[i] = (TS > 0 && i == LB) ? TS : 0;  // the shared bucket: TS pairs
+    run[i] = 0;
+  }
+  for (int i = tid; i < SORT_WAVES * NB; i += SORT_THREADS) hist[i] = 0;
   __syncthreads();
-  for (int p = tid; p < TK; p += bs) atomicAdd(&run[bucket(p)], 1);
-  __syncthreads();
-  // exclusive scans of the pair counts and of the tile counts over buckets 0..LB (NB <= 2 bs),
-  // two buckets per thread
-  const int b0 = 2 * tid, b1 = b0 + 1;
-  const int c0 = b0 <= LB ? run[b0] : 0, c1 = b1 <= LB ? run[b1] : 0;
-  const int t0 = (c0 + MT - 1) / MT, t1 = (c1 + MT - 1) / MT;
-  int v = c0 + c1, u = t0 + t1;
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int pv = __shfl_up(v, o), pu = __shfl_up(u, o);
-    if (lane >= o) {
-      v += pv;
-      u += pu;
-    }
-  }
-  if (lane == WAVE - 1) {
-    wsum[0][w] = v;
-    wsum[1][w] = u;
-  }
-  __syncthreads();
-  for (int j = 0; j < w; ++j) {
-    v += wsum[0][j];
-    u += wsum[1][j];
-  }
-  const int ev = v - c0 - c1, eu = u - t0 - t1;  // exclusive through bucket b0
-  if (b0 <= LB) {
-    offs[b0] = ev;
-    toff[b0] = eu;
-  }
-  if (b1 <= LB) {
-    offs[b1] = ev + c0;
-    toff[b1] = eu + t0;
-  }
-  if (b0 == LB || b1 == LB) {
-    offs[NB] = v;
-    toff[NB] = u;
-  }
-  __syncthreads();
-  if (TS > 0) {  // the shared bucket's tiles go first in the work list (its weights are the same for
-                 // every tile, so they come from the caches, and the list's tail is left to HBM tiles)
-    const int ts = toff[NB] - toff[LB];
-    __syncthreads();
-    for (int b = tid; b < LB; b += bs) toff[b] += ts;
-    if (tid == 0) toff[LB] = 0;
-    __syncthreads();
-  }
-  for (int i = tid; i <= NB; i += bs) {
-    offsets[i] = offs[i];
-    if (i <= LB) counts[i] = run[i];
-  }
-  if (tiles != nullptr) {
-    if (tid == 0) tiles[0] = min(toff[NB], max_tiles);
-    for (int e = tid; e <= LB; e += bs)
-      for (int j = 0, n = (run[e] + MT - 1) / MT; j < n; ++j) {
-        const int k = toff[e] + j;
-        if (k < max_tiles) {
-          int32_t* rec = tiles + 1 + (size_t)TREC * k;
-          rec[0] = e;
-          rec[1] = j * MT;
-          rec[2] = offs[e];
-          rec[3] = run[e];
-          for (int i = run[e] - j * MT; i < MT; ++i) rec[4 + i] = -1;  // the tile's padding rows
-        }
-      }
-  }
-  __syncthreads();
-  for (int i = tid; i <= LB; i += bs) run[i] = 0;
-  // The shared bucket's pairs keep their order: pair TK + q is its q-th.
-  for (int q = tid; q < TS; q += bs) {
-    perm[offs[LB] + q] = TK + q;
-    const int k = toff[LB] + q / MT;
-    if (tiles != nullptr && k < max_tiles) tiles[1 + (size_t)TREC * k + 4 + q % MT] = TK + q;
-  }
-  // Stable placement of the routed pairs, one chunk of bs pairs at a time: a pair's position in its
-  // bucket is the bucket's start + the pairs of earlier chunks + those of earlier waves of this
-  // chunk (per-wave histograms, prefixed over waves) + those of earlier lanes of its own wave.
-  const int nwv = bs / WAVE;
-  for (int base = 0; base < TK; base += bs) {
-    for (int i = tid; i < nwv * NB; i += bs) hist[i] = 0;
-    __syncthreads();
+  int e0 = 0;  // the first chunk's bucket and match mask, kept for its placement
+  uint64_t m0 = 0;
+  for (int base = 0; base < TK; base += SORT_THREADS) {
     const int p = base + tid;
-    int e = -1;
-    if (p < TK) {
-      e = bucket(p);
-      atomicAdd(&hist[w * NB + e], 1);
+    const int e = p < TK ? bucket(p) : 0;
+    const uint64_t m = match_lanes(e, nbits, __ballot(p < TK));
+    if (p < TK && (m & below) == 0) atomicAdd(&cnt[e], __popcll(m));
+    if (base == 0) {
+      e0 = e;
+      m0 = m;
     }
-    int rank = 0;  // earlier lanes of this wave with the same bucket
-    for (int j = 0; j < WAVE; ++j) rank += (j < lane && __builtin_amdgcn_readlane(e, j) == e) ? 1 : 0;
+  }
+  __syncthreads();
+  // exclusive scans of the pair and tile counts over the buckets, by wave 0: each lane sums a run
+  // of consecutive buckets, one wave scan joins the runs
+  if (w == 0) {
+    const int per = (NB + WAVE - 1) / WAVE, b_lo = min(lane * per, NB), b_hi = min(b_lo + per, NB);
+    int c = 0, t = 0;
+    for (int b = b_lo; b < b_hi; ++b) {
+      const int n = cnt[b];
+      c += n;
+      t += (n + MT - 1) / MT;
+    }
+    const int ci = wave_incl_sum(c), ti = wave_incl_sum(t);
+    // the shared bucket's tiles go first in the work list (its weights are the same for every
+    // tile, so they come from the caches, and the list's tail is left to HBM tiles)
+    const int ts = TS > 0 ? (TS + MT - 1) / MT : 0;
+    int ce = ci - c, te = ti - t;
+    for (int b = b_lo; b < b_hi; ++b) {
+      const int n = cnt[b];
+      offs[b] = ce;
+      toff[b] = TS > 0 && b == LB ? 0 : te + ts;
+      ce += n;
+      te += (n + MT - 1) / MT;
+    }
+    if (lane == WAVE - 1) {
+      offs[NB] = ci;
+      toff[NB] = ti;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i <= NB; i += SORT_THREADS) {
+    offsets[i] = offs[i];
+    if (i <= LB) counts[i] = cnt[i];
+  }
+  if (tiles != nullptr && tid == 0) tiles[0] = min(toff[NB], max_tiles);
+  // pair p at position q of bucket e: its perm entry and its row of the tile's record; a tile's
+  // first pair also writes the record's header, the bucket's last pair the padding rows after it
+  const auto place = [&](int e, int q, int p) {
+    perm[offs[e] + q] = p;
+    const int k = toff[e] + q / MT;
+    if (tiles == nullptr || k >= max_tiles) return;
+    int32_t* rec = tiles + 1 + (size_t)TREC * k;
+    rec[4 + q % MT] = p;
+    if (q % MT == 0) {
+      rec[0] = e;
+      rec[1] = q;
+      rec[2] = offs[e];
+      rec[3] = cnt[e];
+    }
+    if (q == cnt[e] - 1)
+      for (int i = q % MT + 1; i < MT; ++i) rec[4 + i] = -1;
+  };
+  // The shared bucket's pairs keep their order: pair TK + q is its q-th.
+  for (int q = tid; q < TS; q += SORT_THREADS) place(LB, q, TK + q);
+  for (int base = 0; base < TK; base += SORT_THREADS) {
+    const int p = base + tid;
+    int e = e0;
+    uint64_t m = m0;
+    if (base > 0) {
+      e = p < TK ? bucket(p) : 0;
+      m = match_lanes(e, nbits, __ballot(p < TK));
+    }
+    if (p < TK && (m & below) == 0) hist[w * NB + e] = __popcll(m);
     __syncthreads();
-    for (int b2 = tid; b2 <= LB; b2 += bs) {  // prefix over waves, per bucket
+    for (int b = tid; b <= LB; b += SORT_THREADS) {  // exclusive prefix over the waves, per bucket
+      int h[SORT_WAVES];
+#pragma unroll
+      for (int v = 0; v < SORT_WAVES; ++v) h[v] = hist[v * NB + b];
       int acc = 0;
-      for (int v = 0; v < nwv; ++v) {
-        const int c = hist[v * NB + b2];
-        hist[v * NB + b2] = acc;
-        acc += c;
+#pragma unroll
+      for (int v = 0; v < SORT_WAVES; ++v) {
+        hist[v * NB + b] = acc;
+        acc += h[v];
       }
-      ctot[b2] = acc;
+      ctot[b] = acc;
     }
     __syncthreads();
-    if (p < TK) {
-      const int q = run[e] + hist[w * NB + e] + rank;  // position inside the bucket
-      perm[offs[e] + q] = p;
-      const int k = toff[e] + q / MT;
-      if (tiles != nullptr && k < max_tiles) tiles[1 + (size_t)TREC * k + 4 + q % MT] = p;
-    }
+    if (p < TK) place(e, run[e] + hist[w * NB + e] + __popcll(m & below), p);
     __syncthreads();
-    for (int b2 = tid; b2 <= LB; b2 += bs) run[b2] += ctot[b2];
+    for (int b = tid; b <= LB; b += SORT_THREADS) run[b] += ctot[b];
+    for (int i = tid; i < SORT_WAVES * NB; i += SORT_THREADS) hist[i] = 0;
     __syncthreads();
   }
 }
@@ -846,8 +873,8 @@ GroupedLayout grouped_layout(int T, int K, int E, int d, int TS) {
 hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
                        int32_t* perm, int32_t* tiles, int TS) {
   const int NB = E + 1 + (TS > 0);
-  const size_t lds = (size_t)(2 * NB + 2 * (NB + 1) + 16 * NB) * sizeof(int);  // 1024 threads = 16 waves
-  return launch(k_sort, dim3(1), dim3(1024), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK + TS, NB),
+  const size_t lds = (size_t)(3 * NB + 2 * (NB + 1) + SORT_WAVES * NB) * sizeof(int);
+  return launch(k_sort, dim3(1), dim3(SORT_THREADS), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK + TS, NB),
                 TS);
 }
 

@@ -171,19 +171,22 @@ def _shared(M, cfg, syn, layer=0):
     return ex, cpu, lora, lora_cpu, lw
 
 
-@pytest.mark.parametrize("T", [256, 5])
-def test_shared_expert_with_lora(M, T):
-    """Grouped (T = 256) and decode (T = 5) paths of the always-on shared expert with an unmerged
-    LoRA on gate, up and down (rank 16, alpha 32)."""
+@pytest.mark.parametrize("T,rms", [(256, False), (5, False), (64, True), (48, True), (33, True)])
+def test_shared_expert_with_lora(M, T, rms):
+    """Grouped (T >= 32) and decode (T = 5) paths of the always-on shared expert with an unmerged
+    LoRA on gate, up and down (rank 16, alpha 32), on raw and on RMS-normed input.  The adapter's
+    A . x runs on the matrix cores when T is a multiple of 16 and one wave per (token, rank row)
+    otherwise (T = 33)."""
     cfg = S.CONFIGS["batched"]
     syn = S.Synth(cfg)
     ex, cpu, lora, lora_cpu, _ = _shared(M, cfg, syn)
     h = syn.hidden(77, T)
-    ref = O.expert_ffn_packed(O.f64(h.numpy()), *cpu, cfg.bits, cfg.group, lora_cpu)
-    base = O.expert_ffn_packed(O.f64(h.numpy()), *cpu, cfg.bits, cfg.group)
+    x = O.rmsnorm(h.numpy()) if rms else O.f64(h.numpy())
+    ref = O.expert_ffn_packed(x, *cpu, cfg.bits, cfg.group, lora_cpu)
+    base = O.expert_ffn_packed(x, *cpu, cfg.bits, cfg.group)
     log(f"LoRA delta relative size {np.abs(ref - base).max() / np.abs(base).max():.3f}")
     idx = torch.zeros((T, 1), dtype=torch.int32, device=DEV)
-    out, _ = run(M, ex, T, 1, 0, h.to(DEV), idx, lora=lora, fused=False)
+    out, _ = run(M, ex, T, 1, M.MOE_INPUT_RMSNORM if rms else 0, h.to(DEV), idx, lora=lora, fused=False)
     assert_rows_close(out.cpu().numpy()[:, 0], ref, what="shared + LoRA")
     assert np.abs(ref - base).max() > 50 * 2e-3 * np.abs(ref).max() / 10   # the delta is visible
 
