@@ -20,6 +20,7 @@
 // in a fixed order, so results are bit-reproducible run to run.
 #include "moe_device.h"
 #include "moe_launch.h"
+#include "moe_lora.h"
 
 namespace moe {
 namespace {
@@ -39,39 +40,9 @@ __device__ __forceinline__ float lora_row(const LoraRef& lr, int t, int row) {
   return lr.scale * acc;
 }
 
-// u[t][r] = s_t * sum_i A[r][i] v_t[i]; one wave per (t, r).  s_t is the RMS-norm factor of v_t
-// when `rmsnorm`, else 1.
-// One wave per (token, rank row) of each of the n_mat (1 or 2) matrices A / A2 on the same v.
-__global__ void __launch_bounds__(256) k_lora_a(int T, int n_in, int rank, int rmsnorm,
-                                                const uint16_t* __restrict__ v, size_t v_stride,
-                                                const uint16_t* __restrict__ A, float* __restrict__ u,
-                                                const uint16_t* __restrict__ A2, float* __restrict__ u2) {
-  int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
-  const int lane = threadIdx.x % WAVE;
-  if (wave >= T * rank) {  // the second matrix's waves (uniform over the wave)
-    if (A2 == nullptr || wave >= 2 * T * rank) return;
-    wave -= T * rank;
-    A = A2;
-    u = u2;
-  }
-  const int t = wave / rank, r = wave % rank;
-  const uint16_t* vr = v + (size_t)t * v_stride;
-  const uint16_t* ar = A + (size_t)r * n_in;
-  float acc = 0.f, sq = 0.f;
-  for (int c = lane * 8; c < n_in; c += WAVE * 8) {
-    uint4 va = *reinterpret_cast<const uint4*>(vr + c);
-    uint4 aa = *reinterpret_cast<const uint4*>(ar + c);
-    const uint32_t vv[4] = {va.x, va.y, va.z, va.w}, av[4] = {aa.x, aa.y, aa.z, aa.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = __builtin_amdgcn_fdot2(as_h2(vv[i]), as_h2(av[i]), acc, false);
-      sq = __builtin_amdgcn_fdot2(as_h2(vv[i]), as_h2(vv[i]), sq, false);
-    }
-  }
-  acc = group_sum(acc, WAVE);
-  sq = group_sum(sq, WAVE);
-  const float s = rmsnorm ? 1.f / sqrtf(sq / (float)n_in + RMS_EPS) : 1.f;
-  if (lane == 0) u[(size_t)t * rank + r] = acc * s;
+// u = A . v (and u2 = A2 . v) for the adapter, one wave per (token, rank row).
+__global__ void __launch_bounds__(256) k_lora_a(LoraAJob j) {
+  lora_a_wave(j, (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE), threadIdx.x % WAVE);
 }
 
 // scale and bias of the one or two groups a segment touches (SPLIT: a 2-bit segment spanning two
@@ -504,8 +475,9 @@ hipError_t launch_p(hipStream_t s, const DecodeArgs& a, const RowGeo& gu, const 
 
 hipError_t launch_lora_a(hipStream_t s, int waves, int T, int n_in, int rank, int rmsnorm, const uint16_t* v,
                          size_t v_stride, const uint16_t* A, float* u, const uint16_t* A2, float* u2) {
-  const int all = A2 ? 2 * waves : waves;
-  return launch(k_lora_a, dim3((all + 3) / 4), dim3(256), 0, s, T, n_in, rank, rmsnorm, v, v_stride, A, u, A2, u2);
+  const LoraAJob j{T, n_in, rmsnorm, v, v_stride, A, u, rank, A2, u2, rank};
+  if (waves != T * rank) return hipErrorInvalidValue;
+  return launch(k_lora_a, dim3((j.waves() + 3) / 4), dim3(256), 0, s, j);
 }
 
 bool decode_shape_supported(int bits, int group, int d, int I) {

@@ -19,6 +19,7 @@
 // feeds which k slot does not matter to the dot product as long as A and B agree.
 #include "moe_device.h"
 #include "moe_launch.h"
+#include "moe_lora.h"
 
 namespace moe {
 namespace {
@@ -62,10 +63,35 @@ __device__ __forceinline__ uint64_t match_lanes(int key, int nbits, uint64_t liv
   return m;
 }
 
-// One block of SORT_THREADS threads.  counts[E+1], offsets[E+2] (bucket E collects indices outside
-// [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles (may
-// be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one TREC-int record per
-// MT-row tile, buckets in order.
+// rowscale[t] = 1 / sqrt(mean(x_t^2) + eps) of token row t (row length d), by one wave.
+__device__ __forceinline__ void rowscale_wave(int t, int d, const uint16_t* __restrict__ x, float* __restrict__ rowscale,
+                                              int lane) {
+  float sq = 0.f;
+  for (int c = lane * 8; c < d; c += WAVE * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)t * d + c);
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq = __builtin_amdgcn_fdot2(as_h2(a[i]), as_h2(a[i]), sq, false);
+  }
+  sq = group_sum(sq, WAVE);
+  if (lane == 0) rowscale[t] = 1.f / sqrtf(sq / (float)d + RMS_EPS);
+}
+
+// Work that needs no sorted order, done beside the sort: the adapter's A . x and the RMS-norm
+// factors of the token rows (rowscale null: none).
+struct SortSideJobs {
+  LoraAJob lora;
+  int T, d;
+  const uint16_t* x;
+  float* rowscale;
+  __host__ __device__ int waves() const { return lora.waves() + (rowscale ? T : 0); }
+};
+
+// Block 0 (SORT_THREADS threads) sorts.  counts[E+1], offsets[E+2] (bucket E collects indices
+// outside [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles
+// (may be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one TREC-int record
+// per MT-row tile, buckets in order.  Blocks 1, 2, ... run `side` on the compute units the sort
+// leaves idle, SORT_WAVES waves each.
 //
 // A pair's position in its bucket is the number of earlier pairs with the same bucket: those of
 // earlier chunks of SORT_THREADS pairs, of earlier waves of its chunk (per-wave counts prefixed over
@@ -75,7 +101,15 @@ __device__ __forceinline__ uint64_t match_lanes(int key, int nbits, uint64_t liv
 __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int32_t* __restrict__ idx,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
-                                                      int max_tiles, int TS) {
+                                                      int max_tiles, int TS, SortSideJobs side) {
+  if (blockIdx.x > 0) {
+    const int wv = (blockIdx.x - 1) * SORT_WAVES + threadIdx.x / WAVE, nl = side.lora.waves();
+    if (wv < nl)
+      lora_a_wave(side.lora, wv, threadIdx.x % WAVE);
+    else if (side.rowscale && wv - nl < side.T)
+      rowscale_wave(wv - nl, side.d, side.x, side.rowscale, threadIdx.x % WAVE);
+    return;
+  }
   // TS > 0: pairs TK .. TK + TS - 1 form one more bucket, E + 1 (a shared expert's, one per token)
   const int NB = E + 1 + (TS > 0 ? 1 : 0), LB = NB - 1;  // buckets, the last one
   extern __shared__ int sh[];
@@ -192,22 +226,6 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
     for (int i = tid; i < SORT_WAVES * NB; i += SORT_THREADS) hist[i] = 0;
     __syncthreads();
   }
-}
-
-// rowscale[t] = 1 / sqrt(mean(x_t^2) + eps); one wave per token.
-__global__ void __launch_bounds__(256) k_rowscale(int T, int d, const uint16_t* __restrict__ x,
-                                                  float* __restrict__ rowscale) {
-  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE), lane = threadIdx.x % WAVE;
-  if (t >= T) return;
-  float sq = 0.f;
-  for (int c = lane * 8; c < d; c += WAVE * 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)t * d + c);
-    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sq = __builtin_amdgcn_fdot2(as_h2(a[i]), as_h2(a[i]), sq, false);
-  }
-  sq = group_sum(sq, WAVE);
-  if (lane == 0) rowscale[t] = 1.f / sqrtf(sq / (float)d + RMS_EPS);
 }
 
 // ------------------------------------------------------------------------------------- MFMA core
@@ -381,19 +399,22 @@ __device__ __forceinline__ void consume_w(const WStage<NMAT, SPLIT>& S, bool val
   }
 }
 
+constexpr int LORA_MAX_RANK = 64;  // the largest adapter rank the entry points accept
+
 struct LoraRefG {
   const uint16_t* B;  // [rows][rank]
-  const float* u;     // [T][rank]
+  const float* u;     // [T][rank]; with nparts > 0, nparts partial sums [nparts][T][rank]
   int rank;
   float scale;
+  int nparts;         // 0: u is the product itself
+  int T;
 };
-// (alpha / rank) * B[row] . u[t]: rank 16 (the common case) as two 16-byte reads of B and four of
-// u issued together; other ranks element by element.
-__device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) {
+// (alpha / rank) * B[row] . u: rank 16 (the common case) as two 16-byte reads of B and four of u
+// issued together; other ranks element by element.  u: [rank] floats (global memory or LDS).
+__device__ __forceinline__ float lora_dot_g(const LoraRefG& lr, const float* u, int row) {
   const uint16_t* b = lr.B + (size_t)row * lr.rank;
-  const float* u = lr.u + (size_t)t * lr.rank;
   float acc = 0.f;
-  if (lr.rank == 16 && (((uintptr_t)lr.B | (uintptr_t)lr.u) & 15) == 0) {
+  if (lr.rank == 16 && (((uintptr_t)lr.B | (uintptr_t)u) & 15) == 0) {
     const uint4 b0 = reinterpret_cast<const uint4*>(b)[0], b1 = reinterpret_cast<const uint4*>(b)[1];
     const float4 u0 = reinterpret_cast<const float4*>(u)[0], u1 = reinterpret_cast<const float4*>(u)[1];
     const float4 u2 = reinterpret_cast<const float4*>(u)[2], u3 = reinterpret_cast<const float4*>(u)[3];
@@ -405,6 +426,60 @@ __device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) 
     for (int r = 0; r < lr.rank; ++r) acc = fmaf(h2f(b[r]), u[r], acc);
   }
   return lr.scale * acc;
+}
+__device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) {
+  return lora_dot_g(lr, lr.u + (size_t)t * lr.rank, row);
+}
+
+// The down adapter's A . act, taken in the gate/up kernel: each block of RB activation rows adds
+// its rows' share, part[blockIdx.y][t][r] = sum over the block's rows i of A[r][i] act[t][i]
+// (act rounded to float16 as stored), and the down kernel sums the parts in order.
+struct LoraPartG {
+  const uint16_t* A;  // [rank][I] (null: no down adapter)
+  float* part;        // [gridDim.y][T][rank]
+  int rank, T;
+};
+
+// Gate/up epilogue of an adapter tile: the tile's activations av (lane (ln, lq): tile rows
+// 4 lq .. + 3 of activation row rbase + wave * 16 + ln, 0 where there is none) go through LDS
+// (`lds`, at least MT * RB floats, free once every wave is past the main loop), then thread
+// (m, r) sums row m's share of u_down[t][r].  rows[m]: token of tile row m, -1 for none.  Every
+// wave of the block calls this.
+template <int RB>
+__device__ __forceinline__ void lora_down_part(const LoraPartG& lp, const float (&av)[4], float* lds, const int* rows,
+                                               int rbase, int nrows) {
+  const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, ln = lane % 16, lq = lane / 16;
+  lds_barrier();  // every wave is done with the staged tokens
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lds[(4 * lq + i) * RB + wave * 16 + ln] = av[i];
+  lds_barrier();
+  const int nr = min(RB, nrows - rbase);
+  for (int o = threadIdx.x; o < MT * lp.rank; o += blockDim.x) {
+    const int m = o / lp.rank, r = o % lp.rank, t = rows[m];
+    if (t < 0) continue;
+    const uint16_t* a = lp.A + (size_t)r * nrows + rbase;
+    const float* v = lds + m * RB;
+    float acc = 0.f;
+    for (int j = 0; j < nr; ++j) acc = fmaf(h2f(a[j]), v[j], acc);
+    lp.part[((size_t)blockIdx.y * lp.T + t) * lp.rank + r] = acc;
+  }
+}
+
+// Down kernel of an adapter tile: ul[m][r] = the parts of u_down[t][r] summed in order, t the
+// token of the tile's pair rec4[m] (routed pair p < TK is token p / K, pair TK + t the shared
+// expert's of token t; rec4[m] < 0: no pair, 0).  ul: LDS, [MT][rank] floats, free once every wave
+// is past the main loop.  Every wave of the block calls this; ul is ready when it returns.
+__device__ __forceinline__ void lora_down_gather(const LoraRefG& lr, float* ul, const int32_t* rec4, int TK, int K) {
+  lds_barrier();  // every wave is done with the staged activations
+  for (int o = threadIdx.x; o < MT * lr.rank; o += blockDim.x) {
+    const int m = o / lr.rank, r = o % lr.rank, pr = rec4[m];
+    const int t = pr < 0 ? -1 : (pr < TK ? pr / K : pr - TK);
+    float acc = 0.f;
+    if (t >= 0)
+      for (int p = 0; p < lr.nparts; ++p) acc += lr.u[((size_t)p * lr.T + t) * lr.rank + r];
+    ul[o] = acc;
+  }
+  lds_barrier();
 }
 
 // One tile of the work list (MT sorted pairs of one expert) against weight rows
@@ -425,9 +500,10 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
                                                           const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1,
                                                           uint16_t* __restrict__ act_sorted, float* __restrict__ out,
                                                           LoraRefG l0, LoraRefG l1, moe_qmat s0, moe_qmat s1, int SB,
-                                                          int TK) {
+                                                          int TK, LoraPartG lp) {
   using GS = GSeg<BITS>;
   static_assert(NST % PF == 0 && NST * GS::MACRO <= XCH, "whole stages, one LDS pass per chunk");
+  static_assert(XS * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XS];
   __shared__ int rows[MT];
   if ((int)blockIdx.x >= tiles[0]) return;
@@ -491,26 +567,37 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
       }
     }
   }
-  if (!active) return;
+  // the down adapter's A . act: its parts summed here (down), or this block's part taken (gate/up)
+  float* lds_f = reinterpret_cast<float*>(xs);
+  const bool gather = NMAT == 1 && lora_on && l0.B != nullptr && l0.nparts > 0;  // uniform over the block
+  if (gather) lora_down_gather(l0, lds_f, rec + 4, TK, K);
+  float av[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = mt + 4 * lq + i;
-    if (pos >= n_e || pos >= mt + MT) continue;
-    const int n = n0 + ln;
-    if constexpr (NMAT == 2) {
-      const int t = tok(rec[4 + pos - mt]);
-      const float sc = rowscale ? rowscale[t] : 1.f;
-      float g = acc[0][i] * sc, u = acc[1][i] * sc;
-      if (lora_on && l0.B) g += lora_row_g(l0, t, n);
-      if (lora_on && l1.B) u += lora_row_g(l1, t, n);
-      act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
-    } else {
-      const int pr = rec[4 + pos - mt];
-      float o = acc[0][i];
-      if (lora_on && l0.B) o += lora_row_g(l0, tok(pr), n);
-      out[(size_t)pr * nrows + n] = o;
+    for (int i = 0; i < 4; ++i) {
+      const int pos = mt + 4 * lq + i;
+      if (pos >= n_e || pos >= mt + MT) continue;
+      const int n = n0 + ln;
+      if constexpr (NMAT == 2) {
+        const int t = tok(rec[4 + pos - mt]);
+        const float sc = rowscale ? rowscale[t] : 1.f;
+        float g = acc[0][i] * sc, u = acc[1][i] * sc;
+        if (lora_on && l0.B) g += lora_row_g(l0, t, n);
+        if (lora_on && l1.B) u += lora_row_g(l1, t, n);
+        const uint16_t a16 = f2h(g / (1.f + expf(-g)) * u);
+        act_sorted[(size_t)(beg + pos) * nrows + n] = a16;
+        av[i] = n < nrows ? h2f(a16) : 0.f;
+      } else {
+        const int pr = rec[4 + pos - mt];
+        float o = acc[0][i];
+        if (lora_on && l0.B)
+          o += gather ? lora_dot_g(l0, lds_f + (pos - mt) * l0.rank, n) : lora_row_g(l0, tok(pr), n);
+        out[(size_t)pr * nrows + n] = o;
+      }
     }
   }
+  if (NMAT == 2 && lora_on && lp.A != nullptr)
+    lora_down_part<16 * GW>(lp, av, lds_f, rows, (int)blockIdx.y * 16 * GW, nrows);
 }
 
 // The same product for 64-column groups without per-step scale loads.  The columns are walked as
@@ -529,7 +616,7 @@ k_grouped_mm64(
     int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
     moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1,
-    moe_qmat s0, moe_qmat s1, int SB, int TK) {
+    moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp) {
   using GS = GSeg<BITS>;
   constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
   constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
@@ -542,6 +629,8 @@ k_grouped_mm64(
   constexpr int NHALF = PER_T >= 2 ? 2 : 1;
   static_assert(NG >= 1 && NG <= 8 && (NG & (NG - 1)) == 0, "1..8 groups per lane");
   static_assert(UNITS % (NHALF * GW * WAVE) == 0 && MT * XSW * 2 <= 70 * 1024, "staging layout");
+  static_assert(NMAT == 1 || RG == 1, "gate/up: one row group per wave");
+  static_assert(XSW * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
   __shared__ int rows[MT];
   if ((int)blockIdx.x >= tiles[0]) return;
@@ -730,28 +819,39 @@ k_grouped_mm64(
       }
     }
   }
-  if (!active) return;
+  // the down adapter's A . act: its parts summed here (down), or this block's part taken (gate/up)
+  float* lds_f = reinterpret_cast<float*>(xs);
+  const bool gather = NMAT == 1 && lora_on && l0.B != nullptr && l0.nparts > 0;  // uniform over the block
+  if (gather) lora_down_gather(l0, lds_f, rec + 4, TK, K);
+  float av[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = mt + 4 * lq + i;
-    const int n = n0(rg) + ln;
-    if (pos >= n_e || pos >= mt + MT || n >= nrows) continue;
-    if constexpr (NMAT == 2) {
-      const int t = tok(pr_out[i]);
-      const float sc = rowscale ? rowscale[t] : 1.f;
-      float g = acc[rg][0][i] * sc, u = acc[rg][1][i] * sc;
-      if (lora_on && l0.B) g += lora_row_g(l0, t, n);
-      if (lora_on && l1.B) u += lora_row_g(l1, t, n);
-      act_sorted[(size_t)(beg + pos) * nrows + n] = f2h(g / (1.f + expf(-g)) * u);
-    } else {
-      const int pr = pr_out[i];
-      float o = acc[rg][0][i];
-      if (lora_on && l0.B) o += lora_row_g(l0, tok(pr), n);
-      out[(size_t)pr * nrows + n] = o;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int pos = mt + 4 * lq + i;
+        const int n = n0(rg) + ln;
+        if (pos >= n_e || pos >= mt + MT || n >= nrows) continue;
+        if constexpr (NMAT == 2) {
+          const int t = tok(pr_out[i]);
+          const float sc = rowscale ? rowscale[t] : 1.f;
+          float g = acc[rg][0][i] * sc, u = acc[rg][1][i] * sc;
+          if (lora_on && l0.B) g += lora_row_g(l0, t, n);
+          if (lora_on && l1.B) u += lora_row_g(l1, t, n);
+          const uint16_t a16 = f2h(g / (1.f + expf(-g)) * u);
+          act_sorted[(size_t)(beg + pos) * nrows + n] = a16;
+          av[i] = h2f(a16);
+        } else {
+          const int pr = pr_out[i];
+          float o = acc[rg][0][i];
+          if (lora_on && l0.B)
+            o += gather ? lora_dot_g(l0, lds_f + (pos - mt) * l0.rank, n) : lora_row_g(l0, tok(pr), n);
+          out[(size_t)pr * nrows + n] = o;
+        }
+      }
   }
+  if (NMAT == 2 && lora_on && lp.A != nullptr)
+    lora_down_part<16 * GW>(lp, av, lds_f, rows, (int)blockIdx.y * 16 * GW, nrows);
 }
 
 int ilog2g(int v) {
@@ -807,6 +907,7 @@ template <int NMAT>
 int rg64(int ncols, bool many_tiles) { return ncols % XCH == 0 || NMAT == 2 || !many_tiles ? 1 : 4; }
 constexpr int MANY_TILES = 128;  // work lists at least this long take four row groups
 
+
 // The two GEMMs over the work list.  With a shared expert (a.shared), its T pairs form bucket E + 1
 // of the same list, so one launch per projection covers routed and shared tiles alike.
 template <int BITS, bool SPLIT>
@@ -820,27 +921,27 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   const moe_qmat gu[4] = {a.ex.gate, a.ex.up, sx.gate, sx.up};
   const moe_qmat dn[2] = {a.ex.down, sx.down};
   const bool many = nt >= MANY_TILES;
+  // The down adapter's A . act is taken by the gate/up blocks of the adapter's tiles, one part per
+  // block row (rows_per_block activation rows); the down kernel sums the parts.
+  const int nparts = grouped_lora_parts(a.I);
+  LoraPartG lp{};
+  if (a.lora3) {
+    lp = LoraPartG{a.lora3[2].A, a.u_down, a.lora3[2].rank, a.T};
+    ldn.nparts = nparts;
+    ldn.T = a.T;
+  }
   const auto k64_gu = grouped_kernel64<BITS, 2>(a.group, a.d, gu, many);
   const auto k64_gu_s = grouped_kernel64<BITS, 2>(a.group, a.d, gu + 2, many);
   hipError_t err;
   if (k64_gu && k64_gu_s)
-    err = launch(k64_gu, dim3(nt, (a.I + rows_per_block * rg64<2>(a.d, many) - 1) / (rows_per_block * rg64<2>(a.d, many))),
-                 dim3(WAVE * GW), 0, s, a.K, a.E, a.d,
-                 a.I, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
-                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK);
+    err = launch(k64_gu, dim3(nt, nparts), dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, a.x, (const int32_t*)g.offsets,
+                 (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up, (uint16_t*)a.act,
+                 (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp);
   else
-    err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), dim3(nt, (a.I + rows_per_block - 1) / rows_per_block),
-                 dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x, (const int32_t*)g.offsets,
-                 (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up,
-                 (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK);
+    err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), dim3(nt, nparts), dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I,
+                 lg2g, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
+                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp);
   if (err != hipSuccess) return err;
-  if (a.lora3) {  // A . act of the LoRA's expert: the shared bucket's rows (after the routed ones), else all
-    const int wd = a.T * a.lora3[2].rank;
-    const uint16_t* act_l = (const uint16_t*)a.act + (size_t)(TS > 0 ? TK : 0) * a.I;
-    err = launch_lora_a(s, wd, a.T, a.I, a.lora3[2].rank, 0, act_l, TS > 0 ? (size_t)a.I : (size_t)a.K * a.I,
-                        a.lora3[2].A, a.u_down);
-    if (err != hipSuccess) return err;
-  }
   const auto k64_dn = grouped_kernel64<BITS, 1>(a.group, a.I, dn, many);
   const auto k64_dn_s = grouped_kernel64<BITS, 1>(a.group, a.I, dn + 1, many);
   if (k64_dn && k64_dn_s)
@@ -848,14 +949,16 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
                   dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
                   a.d, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
                   (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
-                  LoraRefG{}, sx.down, sx.down, SB, TK);
+                  LoraRefG{}, sx.down, sx.down, SB, TK, LoraPartG{});
   return launch(grouped_kernel<BITS, 1>(SPLIT, a.I), dim3(nt, (a.d + rows_per_block - 1) / rows_per_block),
                 dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d, lg2g, (const uint16_t*)a.act, (const int32_t*)g.offsets,
                 (const int32_t*)g.perm, (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down,
-                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down, sx.down, SB, TK);
+                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down, sx.down, SB, TK, LoraPartG{});
 }
 
 }  // namespace
+
+int grouped_lora_parts(int I) { return (I + 16 * GW - 1) / (16 * GW); }
 
 GroupedLayout grouped_layout(int T, int K, int E, int d, int TS) {
   const int NB = E + 1 + (TS > 0), NP = T * K + TS;
@@ -870,40 +973,39 @@ GroupedLayout grouped_layout(int T, int K, int E, int d, int TS) {
   return l;
 }
 
-hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, int32_t* tiles, int TS) {
+namespace {
+// The sort, with `side` in the same launch.
+hipError_t launch_sort_side(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                            int32_t* perm, int32_t* tiles, int TS, const SortSideJobs& side) {
   const int NB = E + 1 + (TS > 0);
   const size_t lds = (size_t)(3 * NB + 2 * (NB + 1) + SORT_WAVES * NB) * sizeof(int);
-  return launch(k_sort, dim3(1), dim3(SORT_THREADS), lds, s, TK, E, idx, counts, offsets, perm, tiles, max_tiles(TK + TS, NB),
-                TS);
+  const int side_blocks = (side.waves() + SORT_WAVES - 1) / SORT_WAVES;
+  return launch(k_sort, dim3(1 + side_blocks), dim3(SORT_THREADS), lds, s, TK, E, idx, counts, offsets, perm, tiles,
+                max_tiles(TK + TS, NB), TS, side);
+}
+}  // namespace
+
+hipError_t launch_sort(hipStream_t s, int TK, int E, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* tiles, int TS) {
+  return launch_sort_side(s, TK, E, idx, counts, offsets, perm, tiles, TS, SortSideJobs{});
 }
 
 hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   const DecodeArgs& a = g.base;
-  hipError_t err = launch_sort(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm, g.tiles, a.shared ? a.T : 0);
+  const int rms = (a.flags & MOE_INPUT_RMSNORM) != 0;
+  float* rowscale = rms ? g.rowscale : nullptr;
+  SortSideJobs side{LoraAJob{}, a.T, a.d, a.x, rowscale};
+  const moe_lora* L3 = a.lora3;
+  if (L3)  // gate's and up's A . x
+    side.lora = LoraAJob{a.T, a.d, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate, L3[0].rank, L3[1].A, a.u_up, L3[1].rank};
+  hipError_t err = launch_sort_side(s, a.T * a.K, a.E, a.idx, g.counts, g.offsets, g.perm, g.tiles,
+                                    a.shared ? a.T : 0, side);
   if (err != hipSuccess) return err;
-  float* rowscale = nullptr;
-  if (a.flags & MOE_INPUT_RMSNORM) {
-    rowscale = g.rowscale;
-    err = launch(k_rowscale, dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, a.d, a.x, rowscale);
-    if (err != hipSuccess) return err;
-  }
   LoraRefG lg{}, lu{}, ldn{};
-  if (a.lora3) {
-    const moe_lora* L3 = a.lora3;
-    const int rms = (a.flags & MOE_INPUT_RMSNORM) != 0;
-    if (L3[0].rank == L3[1].rank)  // gate's and up's A . x in one launch
-      err = launch_lora_a(s, a.T * L3[0].rank, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate,
-                          L3[1].A, a.u_up);
-    else {
-      err = launch_lora_a(s, a.T * L3[0].rank, a.T, a.d, L3[0].rank, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate);
-      if (err == hipSuccess)
-        err = launch_lora_a(s, a.T * L3[1].rank, a.T, a.d, L3[1].rank, rms, a.x, (size_t)a.d, L3[1].A, a.u_up);
-    }
-    if (err != hipSuccess) return err;
+  if (L3) {
     lg = LoraRefG{L3[0].B, a.u_gate, L3[0].rank, L3[0].alpha / (float)L3[0].rank};
     lu = LoraRefG{L3[1].B, a.u_up, L3[1].rank, L3[1].alpha / (float)L3[1].rank};
-    ldn = LoraRefG{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank};
+    ldn = LoraRefG{L3[2].B, a.u_down, L3[2].rank, L3[2].alpha / (float)L3[2].rank, 0, a.T};
   }
   float* o_tk = a.out && !a.shared ? a.out : g.o_sorted;  // with a shared expert: [T*K + T][d]
   if (a.bits == 4)

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "moe_launch.h"
+#include "moe_lora.h"
 
 using namespace moe;
 
@@ -36,7 +37,9 @@ FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex, int32_t TS = 0) {
   w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(float));
   w.u_up = w.u_gate + align_up((size_t)T * MAX_RANK * sizeof(float));
   w.u_down = w.u_up + align_up((size_t)T * MAX_RANK * sizeof(float));
-  w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * sizeof(float));
+  // the grouped path's down adapter keeps grouped_lora_parts(I) partial products per token
+  const size_t parts = T >= GROUPED_MIN_T ? (size_t)grouped_lora_parts(ex->d_ff) : 1;
+  w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * parts * sizeof(float));
   w.total = w.grouped + (T >= GROUPED_MIN_T ? grouped_layout(T, K, ex->n_experts, ex->d_model, TS).total : 0);
   return w;
 }

@@ -191,6 +191,26 @@ def test_shared_expert_with_lora(M, T, rms):
     assert np.abs(ref - base).max() > 50 * 2e-3 * np.abs(ref).max() / 10   # the delta is visible
 
 
+@pytest.mark.parametrize("T", [64, 5])
+def test_lora_with_out_of_range_token(M, T):
+    """A token whose index is outside [0, n_experts) gives a NaN row and leaves every other token's
+    adapter terms alone: the down adapter's A . act must use each token's own activation row, not
+    the row at the token's number in expert-sorted order (which shifts past the skipped token)."""
+    cfg = S.CONFIGS["batched"]
+    syn = S.Synth(cfg)
+    ex, cpu, lora, lora_cpu, _ = _shared(M, cfg, syn)
+    h = syn.hidden(78, T)
+    ref = O.expert_ffn_packed(O.f64(h.numpy()), *cpu, cfg.bits, cfg.group, lora_cpu)
+    idx = torch.zeros((T, 1), dtype=torch.int32)
+    bad = T // 3
+    idx[bad, 0] = 1
+    out, _ = run(M, ex, T, 1, 0, h.to(DEV), idx.to(DEV), lora=lora, fused=False)
+    o = out.cpu().numpy()[:, 0]
+    assert np.isnan(o[bad]).all()
+    keep = np.arange(T) != bad
+    assert_rows_close(o[keep], ref[keep], what="shared + LoRA, one token out of range")
+
+
 def test_lora_zero_b_is_base(M):
     cfg = S.CONFIGS["batched"]
     syn = S.Synth(cfg)
