@@ -87,6 +87,7 @@ struct SortSideJobs {
   __host__ __device__ int waves() const { return lora.waves() + (rowscale ? T : 0); }
 };
 
+
 // Block 0 (SORT_THREADS threads) sorts.  counts[E+1], offsets[E+2] (bucket E collects indices
 // outside [0, E)), perm[T*K]: pair indices grouped by expert, ascending inside each expert.  tiles
 // (may be null): the grouped GEMMs' work list, tiles[0] = number of tiles, then one TREC-int record
@@ -432,11 +433,11 @@ __device__ __forceinline__ float lora_row_g(const LoraRefG& lr, int t, int row) 
 }
 
 // The down adapter's A . act, taken in the gate/up kernel: each block of RB activation rows adds
-// its rows' share, part[blockIdx.y][t][r] = sum over the block's rows i of A[r][i] act[t][i]
+// its rows' share, part[rb][t][r] = sum over the block's rows i of A[r][i] act[t][i]
 // (act rounded to float16 as stored), and the down kernel sums the parts in order.
 struct LoraPartG {
   const uint16_t* A;  // [rank][I] (null: no down adapter)
-  float* part;        // [gridDim.y][T][rank]
+  float* part;        // [row blocks][T][rank]
   int rank, T;
 };
 
@@ -447,7 +448,8 @@ struct LoraPartG {
 // wave of the block calls this.
 template <int RB>
 __device__ __forceinline__ void lora_down_part(const LoraPartG& lp, const float (&av)[4], float* lds, const int* rows,
-                                               int rbase, int nrows) {
+                                               int rb, int nrows) {
+  const int rbase = rb * RB;
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE, ln = lane % 16, lq = lane / 16;
   lds_barrier();  // every wave is done with the staged tokens
 #pragma unroll
@@ -460,8 +462,20 @@ __device__ __forceinline__ void lora_down_part(const LoraPartG& lp, const float 
     const uint16_t* a = lp.A + (size_t)r * nrows + rbase;
     const float* v = lds + m * RB;
     float acc = 0.f;
-    for (int j = 0; j < nr; ++j) acc = fmaf(h2f(a[j]), v[j], acc);
-    lp.part[((size_t)blockIdx.y * lp.T + t) * lp.rank + r] = acc;
+    if (nr == RB && ((uintptr_t)a & 15) == 0) {  // whole block row, 16-byte aligned: all loads at once
+      uint4 a8[RB / 8];
+#pragma unroll
+      for (int k = 0; k < RB / 8; ++k) a8[k] = reinterpret_cast<const uint4*>(a)[k];
+#pragma unroll
+      for (int k = 0; k < RB / 8; ++k) {
+        const uint32_t w4[4] = {a8[k].x, a8[k].y, a8[k].z, a8[k].w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) acc = fmaf(h2f((uint16_t)(w4[h / 2] >> (16 * (h % 2)))), v[8 * k + h], acc);
+      }
+    } else {
+      for (int j = 0; j < nr; ++j) acc = fmaf(h2f(a[j]), v[j], acc);
+    }
+    lp.part[((size_t)rb * lp.T + t) * lp.rank + r] = acc;
   }
 }
 
@@ -482,9 +496,27 @@ __device__ __forceinline__ void lora_down_gather(const LoraRefG& lr, float* ul, 
   lds_barrier();
 }
 
-// One tile of the work list (MT sorted pairs of one expert) against weight rows
-// blockIdx.y * 16 GW .. + 16 GW of NMAT matrices, the input columns in chunks of NST macro steps
-// (columns past ncols are zero).
+// XCD-aware order of the GEMM blocks.  The blocks of a launch are dealt to the NXCD XCDs in turn
+// (block b runs on XCD b mod NXCD), so XCD x takes the (b / NXCD)-th item of its own list: an equal
+// share of the S shared-expert tiles (the first S of the work list), then an equal share of the
+// routed tiles, each tile's NRB row blocks one after another.  A tile's row blocks (one token tile)
+// and an expert's consecutive tiles (the same weight rows) then go through the same L2.  False:
+// this block has no item.
+constexpr int NXCD = 8;
+__device__ __forceinline__ bool xcd_item(int nt, int S, int NRB, int& tile, int& rb) {
+  const int b = blockIdx.x, x = b % NXCD, j = b / NXCD;
+  const int s0 = S * x / NXCD, ns = S * (x + 1) / NXCD - s0;
+  const int R = nt - S, r0 = S + R * x / NXCD, nr = S + R * (x + 1) / NXCD - r0;
+  const int k = j / NRB;
+  if (k >= ns + nr) return false;
+  tile = k < ns ? s0 + k : r0 + (k - ns);
+  rb = j % NRB;
+  return true;
+}
+
+// One tile of the work list (MT sorted pairs of one expert) against weight rows rb * 16 GW .. + 16 GW
+// of NMAT matrices (tile and row block rb from xcd_item), the input columns in chunks of NST macro
+// steps (columns past ncols are zero).
 //   NMAT == 2: gate/up of the tile's tokens (rows of x), SwiGLU, act_sorted[pos][row] float16;
 //   NMAT == 1: down of the tile's activations (rows of act_sorted), out[pair][row] float32;
 //              tiles of bucket E (indices outside [0, E)) write NaN.
@@ -500,14 +532,15 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
                                                           const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1,
                                                           uint16_t* __restrict__ act_sorted, float* __restrict__ out,
                                                           LoraRefG l0, LoraRefG l1, moe_qmat s0, moe_qmat s1, int SB,
-                                                          int TK, LoraPartG lp) {
+                                                          int TK, LoraPartG lp, int S, int NRB) {
   using GS = GSeg<BITS>;
   static_assert(NST % PF == 0 && NST * GS::MACRO <= XCH, "whole stages, one LDS pass per chunk");
   static_assert(XS * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XS];
   __shared__ int rows[MT];
-  if ((int)blockIdx.x >= tiles[0]) return;
-  const int32_t* rec = tiles + 1 + (size_t)TREC * blockIdx.x;
+  int tile, rb;
+  if (!xcd_item(tiles[0], S, NRB, tile, rb)) return;
+  const int32_t* rec = tiles + 1 + (size_t)TREC * tile;
   const int e = rec[0], mt = rec[1], beg = rec[2], n_e = rec[3];
   // bucket SB (when >= 0) holds the shared expert's pairs TK + t, one per token t: its tiles read
   // the shared weights (expert 0 of s0 / s1) and carry the LoRA terms; routed pair p is token p / K
@@ -517,7 +550,7 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
   const auto tok = [&](int pr) { return pr < TK ? pr / K : pr - TK; };
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
-  const int n0 = blockIdx.y * (16 * GW) + wave * 16;
+  const int n0 = rb * (16 * GW) + wave * 16;
   if (e >= E && !shb) {
     if constexpr (NMAT == 1)  // pairs whose expert index is out of range
       for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
@@ -597,7 +630,7 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
     }
   }
   if (NMAT == 2 && lora_on && lp.A != nullptr)
-    lora_down_part<16 * GW>(lp, av, lds_f, rows, (int)blockIdx.y * 16 * GW, nrows);
+    lora_down_part<16 * GW>(lp, av, lds_f, rows, rb, nrows);
 }
 
 // The same product for 64-column groups without per-step scale loads.  The columns are walked as
@@ -616,7 +649,7 @@ k_grouped_mm64(
     int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
     moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1,
-    moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp) {
+    moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp, int S, int NRB) {
   using GS = GSeg<BITS>;
   constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
   constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
@@ -633,8 +666,9 @@ k_grouped_mm64(
   static_assert(XSW * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
   __shared__ int rows[MT];
-  if ((int)blockIdx.x >= tiles[0]) return;
-  const int32_t* rec = tiles + 1 + (size_t)TREC * blockIdx.x;
+  int tile, rb;
+  if (!xcd_item(tiles[0], S, NRB, tile, rb)) return;
+  const int32_t* rec = tiles + 1 + (size_t)TREC * tile;
   const int e = rec[0], mt = rec[1], beg = rec[2], n_e = rec[3];
   // bucket SB (when >= 0) holds the shared expert's pairs TK + t, one per token t: its tiles read
   // the shared weights (expert 0 of s0 / s1) and carry the LoRA terms; routed pair p is token p / K
@@ -645,7 +679,7 @@ k_grouped_mm64(
   const int wave = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int ln = lane % 16, lq = lane / 16;
   // row group rg of this wave: weight rows n0(rg) .. + 16
-  auto n0 = [&](int rg) { return (int)blockIdx.y * (16 * GW * RG) + rg * 16 * GW + wave * 16; };
+  auto n0 = [&](int rg) { return rb * (16 * GW * RG) + rg * 16 * GW + wave * 16; };
   if (e >= E && !shb) {
     if constexpr (NMAT == 1)  // pairs whose expert index is out of range
       for (int rg = 0; rg < RG; ++rg)
@@ -851,7 +885,7 @@ k_grouped_mm64(
       }
   }
   if (NMAT == 2 && lora_on && lp.A != nullptr)
-    lora_down_part<16 * GW>(lp, av, lds_f, rows, (int)blockIdx.y * 16 * GW, nrows);
+    lora_down_part<16 * GW>(lp, av, lds_f, rows, rb, nrows);
 }
 
 int ilog2g(int v) {
@@ -910,6 +944,10 @@ constexpr int MANY_TILES = 128;  // work lists at least this long take four row 
 
 // The two GEMMs over the work list.  With a shared expert (a.shared), its T pairs form bucket E + 1
 // of the same list, so one launch per projection covers routed and shared tiles alike.
+// Blocks of a GEMM launch over at most nt tiles (the first S the shared expert's) and NRB row
+// blocks each, in xcd_item's order: every XCD's list padded to the longest one.
+int xcd_grid(int nt, int S, int NRB) { return NXCD * ((S + NXCD - 1) / NXCD + (nt - S + NXCD - 1) / NXCD) * NRB; }
+
 template <int BITS, bool SPLIT>
 hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowscale, float* o_tk, LoraRefG lg,
                         LoraRefG lu, LoraRefG ldn, const DecodeArgs& a) {
@@ -917,12 +955,13 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   const int rows_per_block = 16 * GW;
   const int TK = a.T * a.K, TS = a.shared ? a.T : 0, SB = a.shared ? a.E + 1 : -1;
   const int nt = max_tiles(TK + TS, a.E + 1 + (TS > 0));
+  const int S = (TS + MT - 1) / MT;  // the shared expert's tiles, first in the work list
   const moe_experts& sx = a.shared ? *a.shared : a.ex;  // the shared weights (unused without a shared expert)
   const moe_qmat gu[4] = {a.ex.gate, a.ex.up, sx.gate, sx.up};
   const moe_qmat dn[2] = {a.ex.down, sx.down};
   const bool many = nt >= MANY_TILES;
   // The down adapter's A . act is taken by the gate/up blocks of the adapter's tiles, one part per
-  // block row (rows_per_block activation rows); the down kernel sums the parts.
+  // row block (rows_per_block activation rows); the down kernel sums the parts.
   const int nparts = grouped_lora_parts(a.I);
   LoraPartG lp{};
   if (a.lora3) {
@@ -932,28 +971,31 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   }
   const auto k64_gu = grouped_kernel64<BITS, 2>(a.group, a.d, gu, many);
   const auto k64_gu_s = grouped_kernel64<BITS, 2>(a.group, a.d, gu + 2, many);
+  const dim3 grid_gu(xcd_grid(nt, S, nparts));
   hipError_t err;
   if (k64_gu && k64_gu_s)
-    err = launch(k64_gu, dim3(nt, nparts), dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, a.x, (const int32_t*)g.offsets,
+    err = launch(k64_gu, grid_gu, dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, a.x, (const int32_t*)g.offsets,
                  (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up, (uint16_t*)a.act,
-                 (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp);
+                 (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp, S, nparts);
   else
-    err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), dim3(nt, nparts), dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I,
-                 lg2g, a.x, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale,
-                 a.ex.gate, a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp);
+    err = launch(grouped_kernel<BITS, 2>(SPLIT, a.d), grid_gu, dim3(WAVE * GW), 0, s, a.K, a.E, a.d, a.I, lg2g, a.x,
+                 (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate,
+                 a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp, S, nparts);
   if (err != hipSuccess) return err;
   const auto k64_dn = grouped_kernel64<BITS, 1>(a.group, a.I, dn, many);
   const auto k64_dn_s = grouped_kernel64<BITS, 1>(a.group, a.I, dn + 1, many);
-  if (k64_dn && k64_dn_s)
-    return launch(k64_dn, dim3(nt, (a.d + rows_per_block * rg64<1>(a.I, many) - 1) / (rows_per_block * rg64<1>(a.I, many))),
-                  dim3(WAVE * GW), 0, s, a.K, a.E, a.I,
-                  a.d, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
-                  (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
-                  LoraRefG{}, sx.down, sx.down, SB, TK, LoraPartG{});
-  return launch(grouped_kernel<BITS, 1>(SPLIT, a.I), dim3(nt, (a.d + rows_per_block - 1) / rows_per_block),
-                dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d, lg2g, (const uint16_t*)a.act, (const int32_t*)g.offsets,
-                (const int32_t*)g.perm, (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down,
-                (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down, sx.down, SB, TK, LoraPartG{});
+  if (k64_dn && k64_dn_s) {
+    const int rb = rows_per_block * rg64<1>(a.I, many), nrb = (a.d + rb - 1) / rb;
+    return launch(k64_dn, dim3(xcd_grid(nt, S, nrb)), dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d,
+                  (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles,
+                  (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down,
+                  sx.down, SB, TK, LoraPartG{}, S, nrb);
+  }
+  const int nrb = (a.d + rows_per_block - 1) / rows_per_block;
+  return launch(grouped_kernel<BITS, 1>(SPLIT, a.I), dim3(xcd_grid(nt, S, nrb)), dim3(WAVE * GW), 0, s, a.K, a.E,
+                a.I, a.d, lg2g, (const uint16_t*)a.act, (const int32_t*)g.offsets, (const int32_t*)g.perm,
+                (const int32_t*)g.tiles, (const float*)nullptr, a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn,
+                LoraRefG{}, sx.down, sx.down, SB, TK, LoraPartG{}, S, nrb);
 }
 
 }  // namespace
