@@ -402,6 +402,41 @@ __global__ void __launch_bounds__(256) k_combine(int T, int K, int d, const floa
   }
 }
 
+// The same four columns at a time (d a multiple of 4, 16-byte aligned o and shared, 8-byte aligned r
+// and y, T d < 2^31): 16-byte loads of o and 32-bit index arithmetic.  Each element's arithmetic
+// is k_combine's, in the same order, so the two give the same bits.
+__global__ void __launch_bounds__(256) k_combine4(int T, int K, int d, const float4* __restrict__ o,
+                                                  const float* __restrict__ w, const uint2* __restrict__ r,
+                                                  const float4* __restrict__ shared, uint2* __restrict__ y) {
+  const int d4 = d / 4, n4 = T * d4;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
+    const int t = i / d4, j = i - t * d4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+      const float wk = w[t * K + k];
+      const float4 v = o[(size_t)(t * K + k) * d4 + j];
+      acc[0] = fmaf(wk, v.x, acc[0]);
+      acc[1] = fmaf(wk, v.y, acc[1]);
+      acc[2] = fmaf(wk, v.z, acc[2]);
+      acc[3] = fmaf(wk, v.w, acc[3]);
+    }
+    if (shared) {
+      const float4 v = shared[i];
+      acc[0] += v.x;
+      acc[1] += v.y;
+      acc[2] += v.z;
+      acc[3] += v.w;
+    }
+    const uint2 rv = r[i];
+    const uint32_t rw[2] = {rv.x, rv.y};
+    uint32_t yw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      yw[h] = f2h(h2f((uint16_t)rw[h]) + acc[2 * h]) | (uint32_t)f2h(h2f((uint16_t)(rw[h] >> 16)) + acc[2 * h + 1]) << 16;
+    y[i] = make_uint2(yw[0], yw[1]);
+  }
+}
+
 // geometry of a packed row with `cols` columns: S segments, row slots of L lanes (a power of two,
 // lanes at or past S idle), P segments per lane.
 struct RowGeo {
@@ -531,6 +566,13 @@ hipError_t launch_gateup_decode(hipStream_t s, const DecodeArgs& a) {
 hipError_t launch_combine(hipStream_t s, int T, int K, int d, const float* o, const float* w,
                           const uint16_t* r, const float* shared, uint16_t* y) {
   const size_t n = (size_t)T * d;
+  if (d % 4 == 0 && n < ((size_t)1 << 31) && (((uintptr_t)o | (uintptr_t)shared) & 15) == 0 &&
+      (((uintptr_t)r | (uintptr_t)y) & 7) == 0) {
+    int blocks = (int)((n / 4 + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    return launch(k_combine4, dim3(blocks), dim3(256), 0, s, T, K, d, (const float4*)o, w, (const uint2*)r,
+                  (const float4*)shared, (uint2*)y);
+  }
   int blocks = (int)((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   return launch(k_combine, dim3(blocks), dim3(256), 0, s, T, K, d, o, w, r, shared, y);

@@ -186,6 +186,29 @@ def test_combine(M):
         assert_rows_close(y.cpu().numpy(), ref, what="combine")
 
 
+def test_combine_vector_and_scalar_paths_agree(M):
+    """moe_combine takes four columns per thread when d % 4 == 0 and the buffers are aligned, one
+    otherwise; both do each element's arithmetic in the same order, so they agree to the bit."""
+    g = torch.Generator().manual_seed(6)
+    T, K, d = 37, 4, 2048
+    o = torch.randn((T * K * d + 1,), generator=g).to(DEV)
+    w = torch.softmax(torch.randn((T, K), generator=g), -1).to(DEV)
+    r = torch.randn((T * d + 1,), generator=g).half().to(DEV)
+    sh = torch.randn((T * d + 1,), generator=g).to(DEV)
+    for shared in (False, True):
+        ya = torch.empty((T, d), dtype=torch.float16, device=DEV)
+        yb = torch.empty((T * d + 1,), dtype=torch.float16, device=DEV)
+        oa, ra, sa = o[:-1].clone(), r[:-1].clone(), sh[:-1].clone()
+        M.moe_combine(T, K, d, oa, w, ra, sa if shared else None, ya)   # aligned: four columns per thread
+        ob, rb, sb = o[1:], r[1:], sh[1:]
+        ob.copy_(oa)
+        rb.copy_(ra)
+        sb.copy_(sa)
+        M.moe_combine(T, K, d, ob, w, rb, sb if shared else None, yb[1:])   # offset by one element: scalar
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(-1), yb[1:])
+
+
 # ------------------------------------------------------------------------------------ prerouter
 def test_prerouter_head(M):
     cfg = S.CONFIGS["decode35b"]
