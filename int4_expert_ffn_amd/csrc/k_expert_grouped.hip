@@ -98,7 +98,8 @@ struct SortSideJobs {
 // earlier chunks of SORT_THREADS pairs, of earlier waves of its chunk (per-wave counts prefixed over
 // the waves) and of earlier lanes of its wave (the lanes with an equal bucket, found by ballots over
 // the bucket's bits).  The lowest lane of each such set of lanes writes the wave's count, so no
-// atomic ever serialises the lanes of one bucket.
+// atomic ever serialises the lanes of one bucket.  The barriers order LDS only: no step reads what
+// another thread stored to global memory, so no barrier waits for the stores of perm and tiles.
 __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int32_t* __restrict__ idx,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ tiles,
@@ -127,25 +128,23 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
     const int e = idx[p];
     return (unsigned)e >= (unsigned)E ? E : e;
   };
+  // the first chunk's buckets, loaded before the LDS set-up so that the load's latency overlaps it
+  int e0 = tid < TK ? bucket(tid) : 0;
+  uint64_t m0 = 0;  // the first chunk's match mask, kept for its placement
   for (int i = tid; i <= LB; i += SORT_THREADS) {
     cnt[i] = (TS > 0 && i == LB) ? TS : 0;  // the shared bucket: TS pairs
     run[i] = 0;
   }
   for (int i = tid; i < SORT_WAVES * NB; i += SORT_THREADS) hist[i] = 0;
-  __syncthreads();
-  int e0 = 0;  // the first chunk's bucket and match mask, kept for its placement
-  uint64_t m0 = 0;
+  lds_barrier();
   for (int base = 0; base < TK; base += SORT_THREADS) {
     const int p = base + tid;
-    const int e = p < TK ? bucket(p) : 0;
+    const int e = base == 0 ? e0 : p < TK ? bucket(p) : 0;
     const uint64_t m = match_lanes(e, nbits, __ballot(p < TK));
     if (p < TK && (m & below) == 0) atomicAdd(&cnt[e], __popcll(m));
-    if (base == 0) {
-      e0 = e;
-      m0 = m;
-    }
+    if (base == 0) m0 = m;
   }
-  __syncthreads();
+  lds_barrier();
   // exclusive scans of the pair and tile counts over the buckets, by wave 0: each lane sums a run
   // of consecutive buckets, one wave scan joins the runs
   if (w == 0) {
@@ -173,7 +172,7 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
       toff[NB] = ti;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i <= NB; i += SORT_THREADS) {
     offsets[i] = offs[i];
     if (i <= LB) counts[i] = cnt[i];
@@ -207,7 +206,7 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
       m = match_lanes(e, nbits, __ballot(p < TK));
     }
     if (p < TK && (m & below) == 0) hist[w * NB + e] = __popcll(m);
-    __syncthreads();
+    lds_barrier();
     for (int b = tid; b <= LB; b += SORT_THREADS) {  // exclusive prefix over the waves, per bucket
       int h[SORT_WAVES];
 #pragma unroll
@@ -220,12 +219,12 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
       }
       ctot[b] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     if (p < TK) place(e, run[e] + hist[w * NB + e] + __popcll(m & below), p);
-    __syncthreads();
+    lds_barrier();
     for (int b = tid; b <= LB; b += SORT_THREADS) run[b] += ctot[b];
     for (int i = tid; i < SORT_WAVES * NB; i += SORT_THREADS) hist[i] = 0;
-    __syncthreads();
+    lds_barrier();
   }
 }
 
