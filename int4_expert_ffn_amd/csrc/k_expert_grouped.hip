@@ -238,7 +238,7 @@ constexpr int XCH = 2048;        // columns of the token tile staged per LDS pas
 __host__ __device__ constexpr int lds_row_stride(int halves) { return halves + ((4 - halves) % 64 + 64) % 64; }
 constexpr int XS = lds_row_stride(XCH);  // halves per staged row
 constexpr int PF = 4;            // macro steps of weight segments in flight per wave
-constexpr int PF64 = 3;          // the same for the lane-contiguous kernel (4 would need more than
+constexpr int PF64 = 4;          // the same for the lane-contiguous kernel (5 would need more than
                                  // 128 registers and leave one block per compute unit)
 
 template <int BITS>
@@ -665,6 +665,7 @@ k_grouped_mm64(
   static_assert(XSW * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
   __shared__ int rows[MT];
+  __shared__ int prs[MT];  // the tile's pair indices (padding rows: the last pair), for the epilogue
   int tile, rb;
   if (!xcd_item(tiles[0], S, NRB, tile, rb)) return;
   const int32_t* rec = tiles + 1 + (size_t)TREC * tile;
@@ -689,18 +690,25 @@ k_grouped_mm64(
   if (threadIdx.x < MT) {
     const int pos = mt + threadIdx.x;
     rows[threadIdx.x] = pos < n_e ? (NMAT == 2 ? tok(rec[4 + threadIdx.x]) : beg + pos) : -1;
+    prs[threadIdx.x] = rec[4 + min((int)threadIdx.x, n_e - mt - 1)];
   }
   lds_barrier();
   const bool active = n0(0) < nrows;  // uniform over the wave (later row groups checked at the stores)
   const int wpr = ncols * BITS / 32, ngr = ncols / 64;
-  // weight row of row group rg, clamped into the expert so that every load is valid
-  auto wrow = [&](int rg) { return (size_t)ee * nrows + min(n0(rg) + ln, nrows - 1); };
+  // weight row (inside the expert) of row group rg, clamped so that every load is valid; the
+  // expert's base addresses are uniform over the block, the offsets from them 32-bit
+  auto lrow = [&](int rg) { return (uint32_t)min(n0(rg) + ln, nrows - 1); };
   const moe_qmat mats[2] = {shb ? s0 : m0, shb ? s1 : m1};
-  const int row0 = rows[0];  // always a real row (the tile holds at least one pair)
-  // the pairs of this lane's four outputs, read now rather than after the last step
-  int pr_out[4];
+  const uint32_t* qe[2];
+  const uint16_t* se[2];
+  const uint16_t* be[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr_out[i] = rec[4 + min(4 * lq + i, n_e - mt - 1)];
+  for (int mi = 0; mi < 2; ++mi) {
+    qe[mi] = mats[mi].q + (size_t)ee * nrows * wpr;
+    se[mi] = mats[mi].scales + (size_t)ee * nrows * ngr;
+    be[mi] = mats[mi].biases + (size_t)ee * nrows * ngr;
+  }
+  const int row0 = rows[0];  // always a real row (the tile holds at least one pair)
   float4_t acc[RG][NMAT];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -716,13 +724,13 @@ k_grouped_mm64(
     if (active) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-      const size_t g0 = wrow(rg) * ngr + (size_t)(c0 / 64 + lq * NG);
+      const uint32_t g0 = lrow(rg) * (uint32_t)ngr + (uint32_t)(c0 / 64 + lq * NG);
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi) {
         uint16_t sv[NG], bv[NG];
         if constexpr (NG == 8) {
-          const uint4 s4 = *reinterpret_cast<const uint4*>(mats[mi].scales + g0);
-          const uint4 b4 = *reinterpret_cast<const uint4*>(mats[mi].biases + g0);
+          const uint4 s4 = *reinterpret_cast<const uint4*>(se[mi] + g0);
+          const uint4 b4 = *reinterpret_cast<const uint4*>(be[mi] + g0);
           const uint32_t sa[4] = {s4.x, s4.y, s4.z, s4.w}, ba[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -730,8 +738,8 @@ k_grouped_mm64(
             bv[j] = (uint16_t)(ba[j / 2] >> (16 * (j % 2)));
           }
         } else if constexpr (NG == 4) {
-          const uint2 s2 = *reinterpret_cast<const uint2*>(mats[mi].scales + g0);
-          const uint2 b2 = *reinterpret_cast<const uint2*>(mats[mi].biases + g0);
+          const uint2 s2 = *reinterpret_cast<const uint2*>(se[mi] + g0);
+          const uint2 b2 = *reinterpret_cast<const uint2*>(be[mi] + g0);
           const uint32_t sa[2] = {s2.x, s2.y}, ba[2] = {b2.x, b2.y};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -739,13 +747,13 @@ k_grouped_mm64(
             bv[j] = (uint16_t)(ba[j / 2] >> (16 * (j % 2)));
           }
         } else if constexpr (NG == 2) {
-          const uint32_t s1 = *reinterpret_cast<const uint32_t*>(mats[mi].scales + g0);
-          const uint32_t b1 = *reinterpret_cast<const uint32_t*>(mats[mi].biases + g0);
+          const uint32_t s1 = *reinterpret_cast<const uint32_t*>(se[mi] + g0);
+          const uint32_t b1 = *reinterpret_cast<const uint32_t*>(be[mi] + g0);
           sv[0] = (uint16_t)s1; sv[1] = (uint16_t)(s1 >> 16);
           bv[0] = (uint16_t)b1; bv[1] = (uint16_t)(b1 >> 16);
         } else {
-          sv[0] = mats[mi].scales[g0];
-          bv[0] = mats[mi].biases[g0];
+          sv[0] = se[mi][g0];
+          bv[0] = be[mi][g0];
         }
 #pragma unroll
         for (int j = 0; j < NG; ++j) sbw[rg][mi][j] = (uint32_t)sv[j] | ((uint32_t)bv[j] << 16);
@@ -755,8 +763,8 @@ k_grouped_mm64(
       for (int u = 0; u < PFN; ++u)
 #pragma unroll
         for (int mi = 0; mi < NMAT; ++mi)
-          q[u][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + wrow(u / NST) * wpr +
-                                                     (size_t)(lcol + (u % NST) * MACRO) * BITS / 32);
+          q[u][mi] = *reinterpret_cast<const uint4*>(qe[mi] + (lrow(u / NST) * (uint32_t)wpr +
+                                                                (uint32_t)(lcol + (u % NST) * MACRO) * BITS / 32));
     }
     __builtin_amdgcn_sched_barrier(0);
     // stage the token tile: every load unconditional (padding rows read row0, then zeroed), in
@@ -846,8 +854,8 @@ k_grouped_mm64(
         const int fn = f + PFN;
 #pragma unroll
         for (int mi = 0; mi < NMAT; ++mi)
-          q[f % PFN][mi] = *reinterpret_cast<const uint4*>(mats[mi].q + wrow(fn / NST) * wpr +
-                                                           (size_t)(lcol + (fn % NST) * MACRO) * BITS / 32);
+          q[f % PFN][mi] = *reinterpret_cast<const uint4*>(qe[mi] + (lrow(fn / NST) * (uint32_t)wpr +
+                                                                      (uint32_t)(lcol + (fn % NST) * MACRO) * BITS / 32));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -866,7 +874,7 @@ k_grouped_mm64(
         const int n = n0(rg) + ln;
         if (pos >= n_e || pos >= mt + MT || n >= nrows) continue;
         if constexpr (NMAT == 2) {
-          const int t = tok(pr_out[i]);
+          const int t = tok(prs[4 * lq + i]);
           const float sc = rowscale ? rowscale[t] : 1.f;
           float g = acc[rg][0][i] * sc, u = acc[rg][1][i] * sc;
           if (lora_on && l0.B) g += lora_row_g(l0, t, n);
@@ -875,7 +883,7 @@ k_grouped_mm64(
           act_sorted[(size_t)(beg + pos) * nrows + n] = a16;
           av[i] = h2f(a16);
         } else {
-          const int pr = pr_out[i];
+          const int pr = prs[4 * lq + i];
           float o = acc[rg][0][i];
           if (lora_on && l0.B)
             o += gather ? lora_dot_g(l0, lds_f + (pos - mt) * l0.rank, n) : lora_row_g(l0, tok(pr), n);
