@@ -399,8 +399,6 @@ __device__ __forceinline__ void consume_w(const WStage<NMAT, SPLIT>& S, bool val
   }
 }
 
-constexpr int LORA_MAX_RANK = 64;  // the largest adapter rank the entry points accept
-
 struct LoraRefG {
   const uint16_t* B;  // [rows][rank]
   const float* u;     // [T][rank]; with nparts > 0, nparts partial sums [nparts][T][rank]

@@ -13,7 +13,6 @@ using namespace moe;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int MAX_RANK = 64;
 constexpr int GROUPED_MIN_T = 32;  // token count from which the grouped MFMA path runs
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -35,11 +34,11 @@ FfnWs ffn_ws(int32_t T, int32_t K, const moe_experts* ex, int32_t TS = 0) {
   FfnWs w{};
   w.act = 0;
   w.u_gate = w.act + align_up((size_t)T * K * ex->d_ff * sizeof(float));
-  w.u_up = w.u_gate + align_up((size_t)T * MAX_RANK * sizeof(float));
-  w.u_down = w.u_up + align_up((size_t)T * MAX_RANK * sizeof(float));
+  w.u_up = w.u_gate + align_up((size_t)T * LORA_MAX_RANK * sizeof(float));
+  w.u_down = w.u_up + align_up((size_t)T * LORA_MAX_RANK * sizeof(float));
   // the grouped path's down adapter keeps grouped_lora_parts(I) partial products per token
   const size_t parts = T >= GROUPED_MIN_T ? (size_t)grouped_lora_parts(ex->d_ff) : 1;
-  w.grouped = w.u_down + align_up((size_t)T * MAX_RANK * parts * sizeof(float));
+  w.grouped = w.u_down + align_up((size_t)T * LORA_MAX_RANK * parts * sizeof(float));
   w.total = w.grouped + (T >= GROUPED_MIN_T ? grouped_layout(T, K, ex->n_experts, ex->d_model, TS).total : 0);
   return w;
 }
@@ -178,7 +177,7 @@ static moe_status check_expert_ffn(int32_t T, int32_t K, uint32_t flags, const u
   if (lora3) {
     if (ex->n_experts != 1) return MOE_ERR_INVALID_ARG;
     for (int m = 0; m < 3; ++m) {
-      if (!lora3[m].A || !lora3[m].B || lora3[m].rank < 1 || lora3[m].rank > MAX_RANK) return MOE_ERR_INVALID_ARG;
+      if (!lora3[m].A || !lora3[m].B || lora3[m].rank < 1 || lora3[m].rank > LORA_MAX_RANK) return MOE_ERR_INVALID_ARG;
       if (!aligned16(lora3[m].A)) return MOE_ERR_INVALID_ARG;
     }
   }

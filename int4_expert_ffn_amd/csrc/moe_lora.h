@@ -6,6 +6,8 @@
 
 namespace moe {
 
+constexpr int LORA_MAX_RANK = 64;  // the largest adapter rank the entry points accept
+
 // u[t][r] = s_t * sum_i A[r][i] v_t[i] for the T rows v_t (row stride v_stride halves) and, with
 // A2, u2[t][r] = s_t * A2[r] . v_t in the same pass; s_t is the RMS-norm factor of v_t when
 // `rmsnorm`, else 1.  One wave per (token, rank row): waves [0, T*rank) are A's, the next
