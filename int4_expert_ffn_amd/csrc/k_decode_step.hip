@@ -650,12 +650,13 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
 template <int BITS, int PG, int NSH, int NSF, int GU, int PD, int NH, bool STAMP>
 __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   using GS = SegT<BITS>;
-  const int lane = c.lane, cw = c.cw, wg = c.wg, dh = p.d / 2, K = p.K;
+  const int cw = c.cw, wg = c.wg, dh = p.d / 2, K = p.K;
+  int lane = c.lane;
   const __amdgpu_buffer_rsrc_t ws = buffer_of(p.ws, p.ws_bytes);
   const __amdgpu_buffer_rsrc_t hout = buffer_of(p.h_out, (uint32_t)p.d * 2);
   // per-layer copies of h: a zero-sized buffer when not asked for, so every store is dropped
   const __amdgpu_buffer_rsrc_t hall = buffer_of(p.h_layers, p.h_layers ? (uint32_t)(p.L + 1) * p.d * 2 : 0u);
-  const bool lead = lane == 0;
+  bool lead = lane == 0;
   ABuf<BITS, PG, NSH, NSF, GU, NH> A;
   BBuf<BITS, NSF, PD> B;
   float lin_keep = 0.f, lin_keep_next = 0.f;  // this wave's linear-row output of heads l-1 and l
@@ -692,6 +693,16 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
   stage_gain(0);
   if (self_routed(p, 0)) stage_router(0);
   for (int l = 0; l < p.L; ++l) {
+    // At d = 4096 (NSH = 8) the address arithmetic derived from the lane, hoisted out of this loop
+    // and held for the whole token, pushed the compute waves past their registers: the spilled
+    // values came back with waits on every outstanding load, prefetches included.  There the lane
+    // is made opaque in each layer, so that arithmetic is redone per layer instead (no spills;
+    // large-int4 413 -> 378 and large-int2 396 -> 374 us per token).  At d = 2048 the hoisted form
+    // fits and is faster.
+    if constexpr (NSH > 4) {
+      asm volatile("" : "+v"(lane));
+      lead = lane == 0;
+    }
     const bool self = self_routed(p, l);
     const bool head = has_head(p, l);
     const bool fc2_now = l > 0 && has_head(p, l - 1);  // fc2 of head l-1 runs in this layer
