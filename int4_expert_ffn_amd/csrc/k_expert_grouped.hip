@@ -77,14 +77,18 @@ __device__ __forceinline__ void rowscale_wave(int t, int d, const uint16_t* __re
   if (lane == 0) rowscale[t] = 1.f / sqrtf(sq / (float)d + RMS_EPS);
 }
 
-// Work that needs no sorted order, done beside the sort: the adapter's A . x and the RMS-norm
-// factors of the token rows (rowscale null: none).
+// Work that needs no sorted order, done beside the sort: the adapter's A . x, the RMS-norm factors
+// of the token rows (rowscale null: none) and clearing nzero ints at zero (the GEMMs' tile counts).
 struct SortSideJobs {
   LoraAJob lora;
   int T, d;
   const uint16_t* x;
   float* rowscale;
-  __host__ __device__ int waves() const { return lora.waves() + (rowscale ? T : 0); }
+  int32_t* zero;
+  int nzero;
+  __host__ __device__ int waves() const {
+    return lora.waves() + (rowscale ? T : 0) + (zero ? (nzero + WAVE - 1) / WAVE : 0);
+  }
 };
 
 
@@ -106,10 +110,13 @@ __global__ void __launch_bounds__(SORT_THREADS) k_sort(int TK, int E, const int3
                                                       int max_tiles, int TS, SortSideJobs side) {
   if (blockIdx.x > 0) {
     const int wv = (blockIdx.x - 1) * SORT_WAVES + threadIdx.x / WAVE, nl = side.lora.waves();
+    const int nr = side.rowscale ? side.T : 0, lane = threadIdx.x % WAVE;
     if (wv < nl)
-      lora_a_wave(side.lora, wv, threadIdx.x % WAVE);
-    else if (side.rowscale && wv - nl < side.T)
-      rowscale_wave(wv - nl, side.d, side.x, side.rowscale, threadIdx.x % WAVE);
+      lora_a_wave(side.lora, wv, lane);
+    else if (wv - nl < nr)
+      rowscale_wave(wv - nl, side.d, side.x, side.rowscale, lane);
+    else if (side.zero && (wv - nl - nr) * WAVE + lane < side.nzero)
+      side.zero[(wv - nl - nr) * WAVE + lane] = 0;
     return;
   }
   // TS > 0: pairs TK .. TK + TS - 1 form one more bucket, E + 1 (a shared expert's, one per token)
@@ -640,19 +647,26 @@ __global__ void __launch_bounds__(GW * WAVE) k_grouped_mm(int K, int E, int ncol
 // input width a multiple of the chunk and 16-byte aligned rows of scales and biases (the host
 // checks); the token tile is staged with unconditional loads (zero rows selected afterwards) so
 // that every wait stays exact.
+// Halves of LDS the token tile of one mm64 item takes (MT rows of NST macro steps' columns).
+template <int BITS, int NST>
+constexpr int mm64_xs_halves() { return MT * lds_row_stride(NST * GSeg<BITS>::MACRO); }
+
+// One (tile, row block) item of k_grouped_mm64, every thread of the block taking part; xs, rows and
+// prs are the block's LDS (mm64_xs_halves halves, MT ints, MT ints).
 template <int BITS, int NMAT, int NST, int RG>
-__global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(BITS == 4 || NMAT == 1 ? 4 : 3)))
-k_grouped_mm64(
-    int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
-    moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1,
-    moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp, int S, int NRB) {
+__device__ __forceinline__ void mm64_item(
+    int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ tiles,
+    const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted,
+    float* __restrict__ out, LoraRefG l0, LoraRefG l1, moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp,
+    int tile, int rb, uint16_t* __restrict__ xs, int* __restrict__ rows, int* __restrict__ prs) {
   using GS = GSeg<BITS>;
   constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
   constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
   constexpr int GPS = MACRO / 64;         // groups per macro step (2 for int4, 4 for int2)
   constexpr int LPG = 4 / GPS;            // lanes of a row per group at one step (2, 1)
-  constexpr int PFD = BITS == 4 ? PF64 : 2;  // 2-bit: one stage fewer keeps it within 128 registers
+  // 4-bit down: PF64 stages; 4-bit gate/up: three (its two matrices' fourth stage leaves no registers);
+  // 2-bit: two, which keeps it within its registers
+  constexpr int PFD = BITS == 4 ? (NMAT == 2 ? 3 : PF64) : 2;
   constexpr int PFN = NST < PFD ? NST : PFD;
   constexpr int XSW = lds_row_stride(W);
   constexpr int UNITS = MT * W / PB, PER_T = UNITS / (GW * WAVE);
@@ -661,11 +675,6 @@ k_grouped_mm64(
   static_assert(UNITS % (NHALF * GW * WAVE) == 0 && MT * XSW * 2 <= 70 * 1024, "staging layout");
   static_assert(NMAT == 1 || RG == 1, "gate/up: one row group per wave");
   static_assert(XSW * 2 >= (NMAT == 2 ? 16 * GW : LORA_MAX_RANK) * 4, "the adapter's tiles fit in the token tile's LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[MT * XSW];
-  __shared__ int rows[MT];
-  __shared__ int prs[MT];  // the tile's pair indices (padding rows: the last pair), for the epilogue
-  int tile, rb;
-  if (!xcd_item(tiles[0], S, NRB, tile, rb)) return;
   const int32_t* rec = tiles + 1 + (size_t)TREC * tile;
   const int e = rec[0], mt = rec[1], beg = rec[2], n_e = rec[3];
   // bucket SB (when >= 0) holds the shared expert's pairs TK + t, one per token t: its tiles read
@@ -893,6 +902,84 @@ k_grouped_mm64(
     lora_down_part<16 * GW>(lp, av, lds_f, rows, rb, nrows);
 }
 
+template <int BITS, int NMAT, int NST, int RG>
+__global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(BITS == 4 || NMAT == 1 ? 4 : 3)))
+k_grouped_mm64(
+    int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ tiles, const float* __restrict__ rowscale,
+    moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted, float* __restrict__ out, LoraRefG l0, LoraRefG l1,
+    moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp, int S, int NRB) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[mm64_xs_halves<BITS, NST>()];
+  __shared__ int rows[MT];
+  __shared__ int prs[MT];  // the tile's pair indices (padding rows: the last pair), for the epilogue
+  int tile, rb;
+  if (!xcd_item(tiles[0], S, NRB, tile, rb)) return;
+  mm64_item<BITS, NMAT, NST, RG>(K, E, ncols, nrows, src, tiles, rowscale, m0, m1, act_sorted, out, l0, l1, s0, s1,
+                                 SB, TK, lp, tile, rb, xs, rows, prs);
+}
+
+// The arguments of one projection of the fused launch below (those of k_grouped_mm64).
+struct MM64Args {
+  int K, E, ncols, nrows;
+  const uint16_t* src;
+  const int32_t* tiles;
+  const float* rowscale;
+  moe_qmat m0, m1;
+  uint16_t* act_sorted;
+  float* out;
+  LoraRefG l0, l1;
+  moe_qmat s0, s1;
+  int SB, TK;
+  LoraPartG lp;
+};
+constexpr int FUSED_SPIN_MAX = 1 << 20;  // polls of a tile count (each after a short sleep): ~0.1 s
+
+// Gate/up and down in one launch.  XCD x (blocks b with b mod NXCD = x, in xcd_item's split of the
+// tiles) first takes the gate/up items of its tiles, then their down items.  A gate/up block adds
+// one to done[tile] once its activation rows (and adapter parts) are stored; a down block first
+// waits for done[tile] == NRB_G.  The two launches' boundary made every down block wait for the
+// last gate/up block of the grid, whose final round leaves a third of the slots idle; here the down
+// items fill them.  Every gate/up block of an XCD is dealt before any of its down blocks, so the
+// ones a down block waits for are running or done (the wait is bounded regardless).  Producer and
+// consumer of a tile run on one XCD: the activations travel through that XCD's L2, and a down
+// block reads them only after the count says they are complete.  done[]: zero at the launch (the
+// sort's side blocks clear it).
+template <int BITS, int NST_G, int NST_D, int RG_D>
+__global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(4)))
+k_grouped_fused64(MM64Args g, MM64Args dn, int S, int NRB_G, int NRB_D, int32_t* __restrict__ done) {
+  constexpr int XG = mm64_xs_halves<BITS, NST_G>(), XD = mm64_xs_halves<BITS, NST_D>();
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XG > XD ? XG : XD];
+  __shared__ int rows[MT];
+  __shared__ int prs[MT];
+  const int nt = g.tiles[0];
+  const int x = blockIdx.x % NXCD, j = blockIdx.x / NXCD;
+  const int s0 = S * x / NXCD, ns = S * (x + 1) / NXCD - s0;
+  const int R = nt - S, r0 = S + R * x / NXCD, nr = S + R * (x + 1) / NXCD - r0;
+  const int ntx = ns + nr;  // this XCD's tiles
+  const auto tile_of = [&](int k) { return k < ns ? s0 + k : r0 + (k - ns); };
+  if (j < ntx * NRB_G) {
+    const int tile = tile_of(j / NRB_G), rb = j % NRB_G;
+    mm64_item<BITS, 2, NST_G, 1>(g.K, g.E, g.ncols, g.nrows, g.src, g.tiles, g.rowscale, g.m0, g.m1, g.act_sorted,
+                                 g.out, g.l0, g.l1, g.s0, g.s1, g.SB, g.TK, g.lp, tile, rb, xs, rows, prs);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores have completed
+    __syncthreads();                     // ... and every other lane's
+    if (threadIdx.x == 0) atomicAdd(done + tile, 1);
+    return;
+  }
+  const int jd = j - ntx * NRB_G;
+  if (jd >= ntx * NRB_D) return;
+  const int tile = tile_of(jd / NRB_D), rb = jd % NRB_D;
+  if (threadIdx.x == 0)
+    for (int spin = 0; spin < FUSED_SPIN_MAX; ++spin) {
+      if (__hip_atomic_load(done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NRB_G) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  __syncthreads();
+  mm64_item<BITS, 1, NST_D, RG_D>(dn.K, dn.E, dn.ncols, dn.nrows, dn.src, dn.tiles, dn.rowscale, dn.m0, dn.m1,
+                                  dn.act_sorted, dn.out, dn.l0, dn.l1, dn.s0, dn.s1, dn.SB, dn.TK, dn.lp, tile, rb, xs,
+                                  rows, prs);
+}
+
 int ilog2g(int v) {
   int r = 0;
   while ((1 << r) < v) ++r;
@@ -904,6 +991,12 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 // Upper bound of the work list's length: every nonempty bucket (at most NB of them, and at most
 // N, the pairs) rounds up to whole tiles.
 int max_tiles(int N, int NB) { return (N + MT - 1) / MT + min(NB, N); }
+// Bytes of the work list (count + records) for N pairs in NB buckets; the per-tile completion counts
+// of the fused GEMM launch follow it.
+size_t tile_list_bytes(int N, int NB) { return al256((1 + TREC * (size_t)max_tiles(N, NB)) * 4); }
+int32_t* tile_counts(int32_t* tiles, int N, int NB) {
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(tiles) + tile_list_bytes(N, NB));
+}
 
 // Steps per chunk: a short chunk (PF macro steps) when the input row fits in it, else the
 // longest one LDS holds.
@@ -976,6 +1069,29 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
   }
   const auto k64_gu = grouped_kernel64<BITS, 2>(a.group, a.d, gu, many);
   const auto k64_gu_s = grouped_kernel64<BITS, 2>(a.group, a.d, gu + 2, many);
+  const auto k64_dn = grouped_kernel64<BITS, 1>(a.group, a.I, dn, many);
+  const auto k64_dn_s = grouped_kernel64<BITS, 1>(a.group, a.I, dn + 1, many);
+  if constexpr (BITS == 4) {
+    // both projections in one launch where both take the lane-contiguous kernels of the fused one:
+    // gate/up over whole 2,048-column chunks, down over 512-column chunks
+    const bool gu_long = k64_gu && k64_gu == k64_gu_s && k64_gu == &k_grouped_mm64<4, 2, XCH / GSeg<4>::MACRO, 1>;
+    const bool dn_rg4 = k64_dn && k64_dn == k64_dn_s && k64_dn == &k_grouped_mm64<4, 1, 4, 4>;
+    const bool dn_rg1 = k64_dn && k64_dn == k64_dn_s && k64_dn == &k_grouped_mm64<4, 1, 4, 1>;
+    if (gu_long && (dn_rg4 || dn_rg1)) {
+      const int rg = dn_rg4 ? 4 : 1, nrb_d = (a.d + rows_per_block * rg - 1) / (rows_per_block * rg);
+      const MM64Args ga{a.K, a.E, a.d, a.I, a.x, (const int32_t*)g.tiles, rowscale, a.ex.gate, a.ex.up,
+                        (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp};
+      const MM64Args da{a.K, a.E, a.I, a.d, (const uint16_t*)a.act, (const int32_t*)g.tiles, (const float*)nullptr,
+                        a.ex.down, a.ex.down, (uint16_t*)nullptr, o_tk, ldn, LoraRefG{}, sx.down, sx.down, SB, TK,
+                        LoraPartG{}};
+      const dim3 grid(xcd_grid(nt, S, nparts + nrb_d));
+      int32_t* done = tile_counts(g.tiles, TK + TS, a.E + 1 + (TS > 0));
+      return dn_rg4 ? launch(k_grouped_fused64<4, XCH / GSeg<4>::MACRO, 4, 4>, grid, dim3(WAVE * GW), 0, s, ga, da, S,
+                             nparts, nrb_d, done)
+                    : launch(k_grouped_fused64<4, XCH / GSeg<4>::MACRO, 4, 1>, grid, dim3(WAVE * GW), 0, s, ga, da, S,
+                             nparts, nrb_d, done);
+    }
+  }
   const dim3 grid_gu(xcd_grid(nt, S, nparts));
   hipError_t err;
   if (k64_gu && k64_gu_s)
@@ -987,8 +1103,6 @@ hipError_t launch_gemms(hipStream_t s, const GroupedArgs& g, const float* rowsca
                  (const int32_t*)g.offsets, (const int32_t*)g.perm, (const int32_t*)g.tiles, rowscale, a.ex.gate,
                  a.ex.up, (uint16_t*)a.act, (float*)nullptr, lg, lu, sx.gate, sx.up, SB, TK, lp, S, nparts);
   if (err != hipSuccess) return err;
-  const auto k64_dn = grouped_kernel64<BITS, 1>(a.group, a.I, dn, many);
-  const auto k64_dn_s = grouped_kernel64<BITS, 1>(a.group, a.I, dn + 1, many);
   if (k64_dn && k64_dn_s) {
     const int rb = rows_per_block * rg64<1>(a.I, many), nrb = (a.d + rb - 1) / rb;
     return launch(k64_dn, dim3(xcd_grid(nt, S, nrb)), dim3(WAVE * GW), 0, s, a.K, a.E, a.I, a.d,
@@ -1016,7 +1130,8 @@ GroupedLayout grouped_layout(int T, int K, int E, int d, int TS) {
   l.rowscale = l.perm + al256((size_t)NP * 4);
   l.o_sorted = l.rowscale + al256((size_t)T * 4);
   l.tiles = l.o_sorted + al256((size_t)NP * d * 4);
-  l.total = l.tiles + al256((1 + TREC * (size_t)max_tiles(NP, NB)) * 4);
+  // the work list, then one completion count per tile (the fused GEMM launch's)
+  l.total = l.tiles + tile_list_bytes(NP, NB) + al256((size_t)max_tiles(NP, NB) * 4);
   return l;
 }
 
@@ -1041,7 +1156,9 @@ hipError_t launch_expert_grouped(hipStream_t s, const GroupedArgs& g) {
   const DecodeArgs& a = g.base;
   const int rms = (a.flags & MOE_INPUT_RMSNORM) != 0;
   float* rowscale = rms ? g.rowscale : nullptr;
-  SortSideJobs side{LoraAJob{}, a.T, a.d, a.x, rowscale};
+  const int NP = a.T * a.K + (a.shared ? a.T : 0), NB = a.E + 1 + (a.shared ? 1 : 0);
+  int32_t* done = tile_counts(g.tiles, NP, NB);
+  SortSideJobs side{LoraAJob{}, a.T, a.d, a.x, rowscale, done, max_tiles(NP, NB)};
   const moe_lora* L3 = a.lora3;
   if (L3)  // gate's and up's A . x
     side.lora = LoraAJob{a.T, a.d, rms, a.x, (size_t)a.d, L3[0].A, a.u_gate, L3[0].rank, L3[1].A, a.u_up, L3[1].rank};
