@@ -245,8 +245,8 @@ constexpr int XCH = 2048;        // columns of the token tile staged per LDS pas
 __host__ __device__ constexpr int lds_row_stride(int halves) { return halves + ((4 - halves) % 64 + 64) % 64; }
 constexpr int XS = lds_row_stride(XCH);  // halves per staged row
 constexpr int PF = 4;            // macro steps of weight segments in flight per wave
-constexpr int PF64 = 4;          // the same for the lane-contiguous kernel (5 would need more than
-                                 // 128 registers and leave one block per compute unit)
+constexpr int PF64 = 4;          // the same for the lane-contiguous kernel (5 fits in 128 registers
+                                 // but measured slower; deeper down prefetch gained nothing)
 
 template <int BITS>
 struct GSeg {
@@ -334,6 +334,25 @@ __device__ __forceinline__ void issue_w(WStage<NMAT, SPLIT>& S, const moe_qmat* 
 // code as float16 with no shift for the lower byte of each half (and one shift per word for
 // the upper byte).  mg[] holds the four magic words in registers, so the mask-or is one
 // v_and_or_b32.
+// One word of codes: its PPW pairs, with scale s and bias b (both halves of each).
+template <int BITS>
+__device__ __forceinline__ void dequant_word(uint32_t wd, half2_t s, half2_t b, const uint32_t* mg, uint32_t* w) {
+  constexpr int PPW = SegT<BITS>::PAIRS_PER_WORD;
+  const uint32_t lo = wd, hi = wd >> 8;
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    // pair j sits at bit BITS*j of each half: in the lower byte for j < PPW / 2
+    const uint32_t src = j < PPW / 2 ? lo : hi;
+    const int jb = j % (PPW / 2);  // position inside the byte, in codes
+    const uint32_t mask = (BITS == 4 ? 0x000F000Fu : 0x00030003u) << (BITS * jb);
+    const int m = BITS == 4 ? 2 * jb : jb;  // magic: 1024, 256, 64, 16 for shifts 0, 2, 4, 6 bits
+    const half2_t c = as_h2((src & mask) | mg[m]);
+    const _Float16 base = (_Float16)(1024 >> (2 * m));
+    const half2_t k = {base, base};
+    w[j] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c - k, s, b));
+  }
+}
+
 template <int BITS, bool SPLIT>
 __device__ __forceinline__ void dequant_stage(uint4 q, uint16_t sa16, uint16_t ba16, uint16_t sb16, uint16_t bb16,
                                               bool valid, const uint32_t* mg, uint32_t* w) {
@@ -349,22 +368,7 @@ __device__ __forceinline__ void dequant_stage(uint4 q, uint16_t sa16, uint16_t b
   const half2_t s0 = {sa, sa}, b0 = {ba, ba}, s1 = {sb, sb}, b1 = {bb, bb};
   const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = wd[i], hi = wd[i] >> 8;
-#pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      // pair j sits at bit BITS*j of each half: in the lower byte for j < PPW / 2
-      const uint32_t src = j < PPW / 2 ? lo : hi;
-      const int jb = j % (PPW / 2);  // position inside the byte, in codes
-      const uint32_t mask = (BITS == 4 ? 0x000F000Fu : 0x00030003u) << (BITS * jb);
-      const int m = BITS == 4 ? 2 * jb : jb;  // magic: 1024, 256, 64, 16 for shifts 0, 2, 4, 6 bits
-      const half2_t c = as_h2((src & mask) | mg[m]);
-      const _Float16 base = (_Float16)(1024 >> (2 * m));
-      const half2_t k = {base, base};
-      const half2_t v = i < 2 ? __builtin_elementwise_fma(c - k, s0, b0) : __builtin_elementwise_fma(c - k, s1, b1);
-      w[i * PPW + j] = __builtin_bit_cast(uint32_t, v);
-    }
-  }
+  for (int i = 0; i < 4; ++i) dequant_word<BITS>(wd[i], i < 2 ? s0 : s1, i < 2 ? b0 : b1, mg, w + i * PPW);
 }
 
 // The magic words of dequant_stage, kept in vector registers (an opaque copy stops the compiler
@@ -652,22 +656,28 @@ template <int BITS, int NST>
 constexpr int mm64_xs_halves() { return MT * lds_row_stride(NST * GSeg<BITS>::MACRO); }
 
 // One (tile, row block) item of k_grouped_mm64, every thread of the block taking part; xs, rows and
-// prs are the block's LDS (mm64_xs_halves halves, MT ints, MT ints).
-template <int BITS, int NMAT, int NST, int RG>
+// prs are the block's LDS (mm64_xs_halves halves, MT ints, MT ints).  ready() runs once, with every
+// thread, after the first weight loads are issued and before the token tile is read: a wait for the
+// tile's input rows there overlaps those loads.
+struct NoWait {
+  __device__ void operator()() const {}
+};
+template <int BITS, int NMAT, int NST, int RG, typename Ready = NoWait>
 __device__ __forceinline__ void mm64_item(
     int K, int E, int ncols, int nrows, const uint16_t* __restrict__ src, const int32_t* __restrict__ tiles,
     const float* __restrict__ rowscale, moe_qmat m0, moe_qmat m1, uint16_t* __restrict__ act_sorted,
     float* __restrict__ out, LoraRefG l0, LoraRefG l1, moe_qmat s0, moe_qmat s1, int SB, int TK, LoraPartG lp,
-    int tile, int rb, uint16_t* __restrict__ xs, int* __restrict__ rows, int* __restrict__ prs) {
+    int tile, int rb, uint16_t* __restrict__ xs, int* __restrict__ rows, int* __restrict__ prs,
+    Ready ready = Ready{}) {
   using GS = GSeg<BITS>;
   constexpr int COLS = GS::COLS, MACRO = GS::MACRO, W = NST * MACRO, PB = GS::PB;
   constexpr int NG = W / 64 / 4;          // groups per lane (a quarter of the chunk's)
   constexpr int GPS = MACRO / 64;         // groups per macro step (2 for int4, 4 for int2)
   constexpr int LPG = 4 / GPS;            // lanes of a row per group at one step (2, 1)
-  // 4-bit down: PF64 stages; 4-bit gate/up: three (its two matrices' fourth stage leaves no registers);
-  // 2-bit: two, which keeps it within its registers
-  constexpr int PFD = BITS == 4 ? (NMAT == 2 ? 3 : PF64) : 2;
-  constexpr int PFN = NST < PFD ? NST : PFD;
+  // 4-bit: PF64 stages (with each word dequantised just before its MFMA, gate/up holds four at 127
+  // registers); 2-bit: two, which keeps it within its registers
+  constexpr int PFD = BITS == 4 ? PF64 : 2;
+  constexpr int PFN = RG * NST < PFD ? RG * NST : PFD;
   constexpr int XSW = lds_row_stride(W);
   constexpr int UNITS = MT * W / PB, PER_T = UNITS / (GW * WAVE);
   constexpr int NHALF = PER_T >= 2 ? 2 : 1;
@@ -774,6 +784,7 @@ __device__ __forceinline__ void mm64_item(
                                                                 (uint32_t)(lcol + (u % NST) * MACRO) * BITS / 32));
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (c0 == 0) ready();
     // stage the token tile: every load unconditional (padding rows read row0, then zeroed), in
     // two halves to bound the registers it holds
 #pragma unroll
@@ -823,20 +834,42 @@ __device__ __forceinline__ void mm64_item(
 #pragma unroll
     for (int f = 0; f < RG * NST; ++f) {  // row group f / NST, macro step f % NST
       const int rg = f / NST, step = f % NST;
-      uint32_t w[NMAT][GS::STEPS * 2];
+      uint32_t pick[NMAT];
 #pragma unroll
       for (int mi = 0; mi < NMAT; ++mi) {
         // group step * GPS + g of the chunk lives in lane (ln, (step GPS + g) / NG), element (...) % NG
-        uint32_t pick = 0;
+        pick[mi] = 0;
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
           const int G = step * GPS + g;
           const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((ln + 16 * (G / NG)) * 4, (int)sbw[rg][mi][G % NG]);
-          pick = sub == g ? v : pick;
+          pick[mi] = sub == g ? v : pick[mi];
         }
-        dequant_stage<BITS, false>(q[f % PFN][mi], (uint16_t)pick, (uint16_t)(pick >> 16), 0, 0, true, mg, w[mi]);
       }
-      if constexpr (BITS == 4 || RG == 1) {
+      if constexpr (BITS == 4) {
+        // word s of a lane's segment holds the eight columns MFMA s takes: each word is
+        // dequantised just before its MFMA, so only one word's pairs are live per matrix
+        const uint32_t* qw[NMAT];
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi) qw[mi] = reinterpret_cast<const uint32_t*>(&q[f % PFN][mi]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const half8_t a = lds_a8(xa + step * MACRO + 8 * s);
+#pragma unroll
+          for (int mi = 0; mi < NMAT; ++mi) {
+            const half2_t sc = __builtin_bit_cast(half2_t, (pick[mi] & 0xFFFFu) * 0x10001u);
+            const half2_t bi = __builtin_bit_cast(half2_t, (pick[mi] >> 16) * 0x10001u);
+            uint32_t w4[4];
+            dequant_word<4>(qw[mi][s], sc, bi, mg, w4);
+            acc[rg][mi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pair4(w4), acc[rg][mi], 0, 0, 0);
+          }
+        }
+      } else if constexpr (RG == 1) {
+        uint32_t w[NMAT][GS::STEPS * 2];
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi)
+          dequant_stage<BITS, false>(q[f % PFN][mi], (uint16_t)pick[mi], (uint16_t)(pick[mi] >> 16), 0, 0, true, mg,
+                                     w[mi]);
 #pragma unroll
         for (int s = 0; s < GS::STEPS / 2; ++s) {
           const half8_t a = lds_a8(xa + step * MACRO + 8 * s);
@@ -847,6 +880,11 @@ __device__ __forceinline__ void mm64_item(
       } else {
         // 2-bit codes with four row groups: the 16-column form holds fewer activation registers
         // live and keeps this variant within its 128 registers without spilling
+        uint32_t w[NMAT][GS::STEPS * 2];
+#pragma unroll
+        for (int mi = 0; mi < NMAT; ++mi)
+          dequant_stage<BITS, false>(q[f % PFN][mi], (uint16_t)pick[mi], (uint16_t)(pick[mi] >> 16), 0, 0, true, mg,
+                                     w[mi]);
 #pragma unroll
         for (int s = 0; s < GS::STEPS; ++s) {
           const half4_t a = *reinterpret_cast<const half4_t*>(xa + step * MACRO + 4 * s);
@@ -969,15 +1007,22 @@ k_grouped_fused64(MM64Args g, MM64Args dn, int S, int NRB_G, int NRB_D, int32_t*
   const int jd = j - ntx * NRB_G;
   if (jd >= ntx * NRB_D) return;
   const int tile = tile_of(jd / NRB_D), rb = jd % NRB_D;
-  if (threadIdx.x == 0)
-    for (int spin = 0; spin < FUSED_SPIN_MAX; ++spin) {
-      if (__hip_atomic_load(done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NRB_G) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  __syncthreads();
+  // the wait for the tile's activations, once the first down weight loads are in flight; the
+  // activation loads stay behind the barrier (no reordering of memory accesses across it), and
+  // after it they find the rows in this XCD's L2
+  const auto ready = [&]() {
+    if (threadIdx.x == 0)
+      for (int spin = 0; spin < FUSED_SPIN_MAX; ++spin) {
+        if (__hip_atomic_load(done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NRB_G) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    asm volatile("" ::: "memory");
+    lds_barrier();
+    asm volatile("" ::: "memory");
+  };
   mm64_item<BITS, 1, NST_D, RG_D>(dn.K, dn.E, dn.ncols, dn.nrows, dn.src, dn.tiles, dn.rowscale, dn.m0, dn.m1,
                                   dn.act_sorted, dn.out, dn.l0, dn.l1, dn.s0, dn.s1, dn.SB, dn.TK, dn.lp, tile, rb, xs,
-                                  rows, prs);
+                                  rows, prs, ready);
 }
 
 int ilog2g(int v) {
