@@ -658,9 +658,10 @@ constexpr int mm64_xs_halves() { return MT * lds_row_stride(NST * GSeg<BITS>::MA
 // One (tile, row block) item of k_grouped_mm64, every thread of the block taking part; xs, rows and
 // prs are the block's LDS (mm64_xs_halves halves, MT ints, MT ints).  ready() runs once, with every
 // thread, after the first weight loads are issued and before the token tile is read: a wait for the
-// tile's input rows there overlaps those loads.
+// tile's input rows there overlaps those loads.  It returns the same value in every thread; false
+// (the input never became ready) makes the item store NaN in place of its outputs.
 struct NoWait {
-  __device__ void operator()() const {}
+  __device__ bool operator()() const { return true; }
 };
 template <int BITS, int NMAT, int NST, int RG, typename Ready = NoWait>
 __device__ __forceinline__ void mm64_item(
@@ -697,11 +698,16 @@ __device__ __forceinline__ void mm64_item(
   const int ln = lane % 16, lq = lane / 16;
   // row group rg of this wave: weight rows n0(rg) .. + 16
   auto n0 = [&](int rg) { return rb * (16 * GW * RG) + rg * 16 * GW + wave * 16; };
-  if (e >= E && !shb) {
-    if constexpr (NMAT == 1)  // pairs whose expert index is out of range
+  // NaN in this item's output rows (down only): pairs whose expert index is out of range, or an
+  // input that never became ready
+  const auto poison = [&]() {
+    if constexpr (NMAT == 1)
       for (int rg = 0; rg < RG; ++rg)
         for (int pos = mt + lq; pos < min(n_e, mt + MT); pos += 4)
           if (n0(rg) + ln < nrows) out[(size_t)rec[4 + pos - mt] * nrows + n0(rg) + ln] = quiet_nan();
+  };
+  if (e >= E && !shb) {
+    poison();
     return;
   }
   if (threadIdx.x < MT) {
@@ -784,7 +790,10 @@ __device__ __forceinline__ void mm64_item(
                                                                 (uint32_t)(lcol + (u % NST) * MACRO) * BITS / 32));
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (c0 == 0) ready();
+    if (c0 == 0 && !ready()) {
+      poison();
+      return;
+    }
     // stage the token tile: every load unconditional (padding rows read row0, then zeroed), in
     // two halves to bound the registers it holds
 #pragma unroll
@@ -978,10 +987,12 @@ constexpr int FUSED_SPIN_MAX = 1 << 20;  // polls of a tile count (each after a 
 // waits for done[tile] == NRB_G.  The two launches' boundary made every down block wait for the
 // last gate/up block of the grid, whose final round leaves a third of the slots idle; here the down
 // items fill them.  Every gate/up block of an XCD is dealt before any of its down blocks, so the
-// ones a down block waits for are running or done (the wait is bounded regardless).  Producer and
-// consumer of a tile run on one XCD: the activations travel through that XCD's L2, and a down
-// block reads them only after the count says they are complete.  done[]: zero at the launch (the
-// sort's side blocks clear it).
+// ones a down block waits for are running or done; the wait is bounded regardless, and a down
+// block whose wait runs out stores NaN in its outputs, so the result shows it.  The down block
+// issues its first weight loads before it waits.  Producer and consumer of a tile run on one XCD
+// (gfx950 deals workgroup b to XCD b mod 8; a partition into 4, 2 or 1 XCDs keeps each class on
+// one): the activations travel through that XCD's L2, and a down block reads them only after the
+// count says they are complete.  done[]: zero at the launch (the sort's side blocks clear it).
 template <int BITS, int NST_G, int NST_D, int RG_D>
 __global__ void __launch_bounds__(GW * WAVE) __attribute__((amdgpu_waves_per_eu(4)))
 k_grouped_fused64(MM64Args g, MM64Args dn, int S, int NRB_G, int NRB_D, int32_t* __restrict__ done) {
@@ -1010,15 +1021,20 @@ k_grouped_fused64(MM64Args g, MM64Args dn, int S, int NRB_G, int NRB_D, int32_t*
   // the wait for the tile's activations, once the first down weight loads are in flight; the
   // activation loads stay behind the barrier (no reordering of memory accesses across it), and
   // after it they find the rows in this XCD's L2
+  __shared__ int late;
   const auto ready = [&]() {
-    if (threadIdx.x == 0)
-      for (int spin = 0; spin < FUSED_SPIN_MAX; ++spin) {
-        if (__hip_atomic_load(done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NRB_G) break;
-        __builtin_amdgcn_s_sleep(2);
+    if (threadIdx.x == 0) {
+      bool ok = false;
+      for (int spin = 0; spin < FUSED_SPIN_MAX && !ok; ++spin) {
+        ok = __hip_atomic_load(done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NRB_G;
+        if (!ok) __builtin_amdgcn_s_sleep(2);
       }
+      late = !ok;
+    }
     asm volatile("" ::: "memory");
     lds_barrier();
     asm volatile("" ::: "memory");
+    return late == 0;
   };
   mm64_item<BITS, 1, NST_D, RG_D>(dn.K, dn.E, dn.ncols, dn.nrows, dn.src, dn.tiles, dn.rowscale, dn.m0, dn.m1,
                                   dn.act_sorted, dn.out, dn.l0, dn.l1, dn.s0, dn.s1, dn.SB, dn.TK, dn.lp, tile, rb, xs,
