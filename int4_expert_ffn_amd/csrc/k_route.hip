@@ -84,14 +84,15 @@ __global__ void __launch_bounds__(64) k_router(int T, int d, int E, uint32_t fla
 // feeds them to one MFMA step; X and W use the same column order, which is all a dot product needs.  With
 // MOE_INPUT_RMSNORM each token's sum of squares comes from the same X reads.  The partial tiles
 // meet in LDS.  Needs T and E multiples of 16, d of 32 and 16-byte aligned rows (the host checks).
-constexpr int RK = 512;                      // columns per wave
-constexpr int RK_LOADS = RK / 32;            // 16-byte loads per lane and operand
-constexpr int R_MAXW = MOE_MAX_D / RK;       // waves per block at most
+constexpr int R_MAXW = 16;  // waves per block at most
 
+// RK: columns per wave (RK / 32 16-byte loads per lane and operand)
+template <int RK>
 __global__ void __launch_bounds__(R_MAXW * WAVE) k_router_mfma(int T, int d, int E, uint32_t flags,
                                                                const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ W,
                                                                float* __restrict__ logits) {
+  constexpr int RK_LOADS = RK / 32;
   __shared__ float part[R_MAXW][WAVE][5];
   const int lane = threadIdx.x % WAVE, wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
   const int m = lane % 16, q = lane / 16;
@@ -356,11 +357,19 @@ hipError_t launch_rmsnorm(hipStream_t s, int T, int d, const uint16_t* h, const 
   return launch(k_rmsnorm, dim3((T + 3) / 4), dim3(256), 0, s, T, d, h, gain, x);
 }
 
+constexpr int RK_SMALL = 128;  // 16 waves at d = 2048: shorter load chains than 4 waves of 512 columns
 hipError_t launch_router_gemv(hipStream_t s, int T, int d, int E, uint32_t flags, const uint16_t* x,
                               const uint16_t* w, float* logits) {
-  if (T >= 32 && T % 16 == 0 && E % 16 == 0 && d % 32 == 0 && d <= MOE_MAX_D && (((uintptr_t)x | (uintptr_t)w) & 15) == 0)
-    return launch(k_router_mfma, dim3(T / 16, E / 16), dim3((d + RK - 1) / RK * WAVE), 0, s, T, d, E, flags, x, w,
-                  logits);
+  if (T >= 32 && T % 16 == 0 && E % 16 == 0 && d % 32 == 0 && d <= MOE_MAX_D && (((uintptr_t)x | (uintptr_t)w) & 15) == 0) {
+    // the fewest columns per wave that keep the block within R_MAXW waves
+    const dim3 grid(T / 16, E / 16);
+    if (d <= R_MAXW * RK_SMALL)
+      return launch(k_router_mfma<RK_SMALL>, grid, dim3((d + RK_SMALL - 1) / RK_SMALL * WAVE), 0, s, T, d, E, flags,
+                    x, w, logits);
+    if (d <= R_MAXW * 256)
+      return launch(k_router_mfma<256>, grid, dim3((d + 255) / 256 * WAVE), 0, s, T, d, E, flags, x, w, logits);
+    return launch(k_router_mfma<512>, grid, dim3((d + 511) / 512 * WAVE), 0, s, T, d, E, flags, x, w, logits);
+  }
   const dim3 grid(E, (T + TPW - 1) / TPW);
   switch (nseg_for(d)) {
     case 1: return launch(k_router<1>, grid, dim3(WAVE), 0, s, T, d, E, flags, TPW, x, w, logits);
