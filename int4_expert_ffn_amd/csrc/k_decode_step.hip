@@ -534,6 +534,7 @@ struct StepShared {
   uint16_t gain[2][LDS_D];  // input-norm gains of layers l and l+1 (by layer parity), staged by the compute waves
   uint16_t xg[LDS_D];       // gain * h_l, formed by the compute waves once h_l is in (gained layers only)
   uint16_t rrow[LDS_RR];    // router rows of a self-routed layer, staged by the compute waves: slot cw holds row cw * G + wg
+  uint64_t act_w[LDS_ACT / 2];  // the act words' payloads as received (two 24-bit floats each; RAW_ACT)
 };
 
 struct StepCtx {
@@ -572,7 +573,10 @@ __device__ __forceinline__ void put_act(StepShared& sm, int n, float f) {
 
 // Wave 0 of every workgroup: waits for the vectors each phase needs and unpacks them into LDS.
 // GW0: 32-bit words of a d-row per lane (d = NSH 64 lanes x 8 halves).
-template <int BITS, int GW0, bool STAMP>
+// RAW_ACT: the act words go to LDS as received and the compute waves unpack them (the stacks
+// without heads, whose layers all route themselves: there the poll wave's work per act word is on
+// the critical path, measured 1-2 % per token; with heads unpacking here measured faster).
+template <int BITS, int GW0, bool STAMP, bool RAW_ACT>
 __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c, StepShared& sm) {
   const int lane = c.lane, dh = p.d / 2;
   bool failed = false;
@@ -613,8 +617,12 @@ __device__ __forceinline__ void sync_role(const StepParams& p, const StepCtx& c,
     lds_barrier();  // BA: this workgroup's SwiGLU outputs gathered (the compute waves store them)
     ll_wait<16>(p.ll_act + (size_t)(c.wg % p.xr_a) * p.act_stride, 0, p.K * p.I / 2, c.tag16(3 * l + 1), p.err, failed, c.spare,
                 [&](int i, uint64_t v) {
-      sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
-      sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
+      if constexpr (RAW_ACT) {
+        sm.act_w[i] = v;
+      } else {
+        sm.act_f[2 * i] = f24_to_f32((uint32_t)v & 0xFFFFFFu);
+        sm.act_f[2 * i + 1] = f24_to_f32((uint32_t)(v >> 24) & 0xFFFFFFu);
+      }
     });
     stamp<STAMP>(p, c.wg, l, 2);
     lds_barrier();  // B3: act ready
@@ -903,7 +911,12 @@ __device__ __forceinline__ void compute_role(const StepParams& p, const StepCtx&
       issue_A_gu<BITS, PG, NSH, NSF, GU, NH>(p, l + 1, sm.route_e + (l + 1) * K, wg, cw, lane, A);
     lds_barrier();  // B3
     // split act into float16 hi/lo pairs once per workgroup, every compute lane a few values
-    for (int n = cw * WAVE + lane; n < K * p.I; n += MW * WAVE) put_act<BITS>(sm, n, sm.act_f[n]);
+    for (int n = cw * WAVE + lane; n < K * p.I; n += MW * WAVE) {
+      if constexpr (NH == 0)  // the poll wave stored the raw words (sync_role's RAW_ACT)
+        put_act<BITS>(sm, n, f24_to_f32((uint32_t)(sm.act_w[n >> 1] >> (24 * (n & 1))) & 0xFFFFFFu));
+      else
+        put_act<BITS>(sm, n, sm.act_f[n]);
+    }
     lds_barrier();  // B3b
     stamp<STAMP>(p, wg, l, 5, cw == 0);
 
@@ -999,7 +1012,7 @@ __global__ void __launch_bounds__(NTHREADS) k_decode_step(StepParams p) {
     }
   }
   if (wave == 0) {
-    sync_role<BITS, NSH * 4, STAMP>(p, c, sm);
+    sync_role<BITS, NSH * 4, STAMP, NH == 0>(p, c, sm);
   } else {
     // (all waves at the same issue priority: raising the compute waves' above the polling wave's,
     // which shares SIMD 0 with two of them, was measured 2 % slower per token)
