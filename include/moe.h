@@ -177,7 +177,7 @@ size_t moe_expert_ffn_shared_workspace_size(int32_t T, int32_t K, const moe_expe
      y[t] = r[t] + sum_k w[t][k] FFN_{idx[t][k]}(x_t) + FFN_shared(x_t)        (float16 out)
    FFN as in moe_expert_ffn_q4; the LoRA (lora3, may be NULL) is the shared expert's.  The shared
    expert's T (token) rows join the routed (token, slot) pairs as one more expert of the sort, so
-   one grouped GEMM launch per projection covers both; the result equals moe_expert_ffn_q4 on the
+   the grouped GEMM launches cover both; the result equals moe_expert_ffn_q4 on the
    routed experts, moe_expert_ffn_q4 on the shared expert (K = 1, lora3) and moe_combine with its
    output as `shared`, to the bit.  shared: one expert (n_experts == 1) of the same d_model, d_ff,
    bits and group as ex.  w [T][K] float32, r [T][d] float16 and y all required.  T >= 32 (the
